@@ -1,0 +1,75 @@
+"""fp64 reference of the sparse-weight product (test infrastructure only).
+
+Definition followed
+-------------------
+A statically pruned weight matrix multiplies dense activations:
+Y = (W (.) mask) X with W of shape M x K (out x in) and X of shape K x N.
+  * "Unified Static-Dynamic Pruning for Efficient LLM Inference" (SPDP),
+    abstract: unstructured static pruning removes weights permanently; the
+    product must be the exact sparse product.
+  * "Accelerating GPU inference of LLMs with moderately unstructured sparse
+    weight matrices", abstract and Sec. 2.1: prefill inputs are [BL, H], decode
+    inputs [B, H]; the pattern is computed offline and the residual layer keeps
+    the SpMM correct, i.e. the sparse kernel is exact, not an approximation.
+
+Dynamic (input-adaptive) pruning, the spMspV half of SPDP, skips input
+channels whose activation is zero.  The reduced-product form Y = W[:, I] x[I]
+over the kept channels I is the one of the "Reduced Matrix Multiplication"
+blog page, Sec. 4.2 (channel selection for FFN down projections), with I taken
+as the channels whose activation is non-zero in at least one token: dropped
+terms are then exact zeros and the result equals the full product.
+
+All arithmetic is float64 on the exact fp16 input values.  Accumulation order
+is numpy's; the pins in the tests bound it against exact integer arithmetic.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+
+def _masked_fp64(W: np.ndarray, mask: np.ndarray | None) -> np.ndarray:
+    W64 = np.asarray(W, dtype=np.float16).astype(np.float64)
+    if mask is None:
+        return W64
+    return np.where(np.asarray(mask, dtype=bool), W64, 0.0)
+
+
+def masked_matmul(W: np.ndarray, mask: np.ndarray | None, X_tok: np.ndarray) -> np.ndarray:
+    """Y = (W (.) mask) @ X in float64.
+
+    ``X_tok`` is token-major (N, K); the result is token-major (N, M), i.e.
+    ``Y_tok[n, m] = sum_k mask[m,k] W[m,k] X_tok[n,k]``.
+    """
+    Wm = _masked_fp64(W, mask)
+    X64 = np.asarray(X_tok, dtype=np.float16).astype(np.float64)
+    return (Wm @ X64.T).T
+
+
+def active_inputs(X_tok: np.ndarray) -> np.ndarray:
+    """Boolean (K,) vector: input channel k is active iff x[n, k] != 0 for some n.
+
+    +0 and -0 both count as zero (fp16 comparison).
+    """
+    X = np.asarray(X_tok, dtype=np.float16)
+    return np.any(X != 0, axis=0)
+
+
+def masked_matmul_skip(W: np.ndarray, mask: np.ndarray | None, X_tok: np.ndarray) -> np.ndarray:
+    """Zero-activation-skipping product: only active input channels take part.
+
+    Steps in the order the pages give them: (1) find the channels that carry a
+    non-zero activation, (2) multiply only the weight columns of those channels,
+    (3) the result lands in the full output (no scatter is needed for input-side
+    selection).
+    """
+    act = active_inputs(X_tok)
+    Wm = _masked_fp64(W, mask)[:, act]
+    X64 = np.asarray(X_tok, dtype=np.float16).astype(np.float64)[:, act]
+    if Wm.shape[1] == 0:
+        return np.zeros((X64.shape[0], Wm.shape[0]), dtype=np.float64)
+    return (Wm @ X64.T).T
+
+
+def to_fp16(Y: np.ndarray) -> np.ndarray:
+    """Round a float64 result to fp16, round-to-nearest-even."""
+    return np.asarray(Y, dtype=np.float64).astype(np.float16)

@@ -1,0 +1,216 @@
+"""Pins of the CPU oracle against facts that do not come from the oracle itself.
+
+* exact integer brute force (every fp16 product is an integer multiple of
+  2**-48) with a deterministic float64 error bound;
+* special cases with exact answers (identity, permutation, one-hot, all-zero
+  mask, hand-worked 3x10 example);
+* a hand-worked byte image of the format (tests/golden/tcb_hand_example.json);
+* format invariants and a round trip;
+* planted mistakes: mutated copies of the oracle must fail these pins.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle.exact import exact_masked_matmul, exact_to_float, fp64_error_bound
+import swm_workloads as wl
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _check_against_exact(fn, W, mask, X):
+    Y = fn(W, mask, X)
+    exact = exact_to_float(exact_masked_matmul(W, mask, X))
+    bound = fp64_error_bound(W, mask, X) + np.abs(exact) * 2.0 ** -52
+    return np.all(np.abs(Y - exact) <= bound), Y, exact
+
+
+def _rand_case(seed, M, K, N, density, ties=False, signed_zero=False):
+    g = np.random.default_rng(seed)
+    if ties:
+        W = g.choice(np.array([-0.5, -0.25, 0.25, 0.5, 1.0], dtype=np.float16), size=(M, K))
+    else:
+        W = (0.02 * g.standard_normal((M, K))).astype(np.float16)
+    if signed_zero:
+        z = g.random((M, K)) < 0.1
+        W[z] = np.float16(-0.0)
+    mask = g.random((M, K)) < density
+    X = g.standard_normal((N, K)).astype(np.float16)
+    return W, mask, X
+
+
+# ---------------------------------------------------------------- brute force
+def test_oracle_matches_exact_brute_force_on_tiny_workload():
+    W, mask, X = wl.tiny()
+    ok, Y, exact = _check_against_exact(oracle.masked_matmul, W, mask, X)
+    assert ok
+    assert Y.shape == (8, 256)
+
+
+@pytest.mark.parametrize("seed,M,K,N,density", [
+    (1, 1, 1, 1, 1.0), (2, 3, 7, 2, 0.5), (3, 65, 130, 3, 0.5), (4, 17, 300, 5, 0.01),
+    (5, 40, 33, 17, 0.99), (6, 129, 9, 1, 0.3),
+])
+def test_oracle_matches_exact_on_random_shapes(seed, M, K, N, density):
+    W, mask, X = _rand_case(seed, M, K, N, density, ties=seed % 2 == 0, signed_zero=True)
+    ok, _, _ = _check_against_exact(oracle.masked_matmul, W, mask, X)
+    assert ok
+    ok, _, _ = _check_against_exact(oracle.masked_matmul_skip, W, mask, X)
+    assert ok
+
+
+# ---------------------------------------------------------------- exact special cases
+def test_all_zero_mask_gives_zero():
+    W, _, X = _rand_case(7, 70, 90, 4, 0.5)
+    mask = np.zeros(W.shape, dtype=bool)
+    assert np.all(oracle.masked_matmul(W, mask, X) == 0)
+    assert np.all(oracle.masked_matmul_skip(W, mask, X) == 0)
+
+
+def test_dense_mask_is_the_plain_product_brute_force():
+    W, _, X = _rand_case(8, 20, 50, 3, 1.0)
+    ok, _, _ = _check_against_exact(oracle.masked_matmul, W, np.ones(W.shape, bool), X)
+    assert ok
+
+
+def test_identity_and_permutation_are_exact():
+    K, N = 96, 5
+    g = np.random.default_rng(9)
+    X = g.standard_normal((N, K)).astype(np.float16)
+    W = np.eye(K, dtype=np.float16)
+    assert np.array_equal(oracle.to_fp16(oracle.masked_matmul(W, np.eye(K, dtype=bool), X)).view(np.uint16),
+                          X.view(np.uint16) & np.uint16(0xFFFF))
+    perm = g.permutation(K)
+    P = np.zeros((K, K), dtype=np.float16)
+    P[np.arange(K), perm] = 1
+    Y = oracle.masked_matmul(P, P != 0, X)
+    assert np.array_equal(Y, X[:, perm].astype(np.float64))
+
+
+def test_one_hot_activations_pick_a_weight_column():
+    W, mask, _ = _rand_case(10, 33, 40, 1, 0.5)
+    for k in (0, 17, 39):
+        X = np.zeros((1, 40), dtype=np.float16)
+        X[0, k] = 1
+        Y = oracle.masked_matmul(W, mask, X)
+        assert np.array_equal(Y[0], np.where(mask[:, k], W[:, k].astype(np.float64), 0.0))
+
+
+def test_power_of_two_scaling_is_exact():
+    W, mask, X = _rand_case(11, 30, 64, 2, 0.5)
+    Y1 = oracle.masked_matmul(W, mask, X)
+    Y2 = oracle.masked_matmul(W, mask, (X.astype(np.float64) * 0.25).astype(np.float16))
+    # scaling by 2**-2 keeps every fp16 normal value exact at this magnitude
+    assert np.allclose(Y2 * 4.0, Y1, rtol=0, atol=1e-12)
+
+
+def test_hand_worked_example():
+    d = json.load(open(os.path.join(GOLDEN, "tcb_hand_example.json")))
+    W = np.array(d["W_rows_fp16"], dtype=np.float16)
+    X = np.array([d["x"]], dtype=np.float16)
+    assert list(oracle.masked_matmul(W, None, X)[0]) == d["y"]
+    assert list(oracle.masked_matmul_skip(W, None, X)[0]) == d["y"]
+
+
+def test_skip_ignores_all_zero_channels_only():
+    W, mask, X = _rand_case(12, 50, 80, 4, 0.5)
+    X[:, ::3] = 0
+    X[1, 1] = np.float16(-0.0)
+    X[0, 2] = 0
+    act = oracle.active_inputs(X)
+    assert not act[0] and act[4]
+    assert not act[1] or np.any(X[:, 1] != 0)
+    assert np.all(oracle.masked_matmul_skip(W, mask, np.zeros_like(X)) == 0)
+    ok, _, _ = _check_against_exact(oracle.masked_matmul_skip, W, mask, X)
+    assert ok
+
+
+# ---------------------------------------------------------------- format
+def test_format_hand_worked_bytes():
+    d = json.load(open(os.path.join(GOLDEN, "tcb_hand_example.json")))
+    W = np.array(d["W_rows_fp16"], dtype=np.float16)
+    f = oracle.tcb_encode(W, None, TM=d["TM"], TK=d["TK"])
+    assert (f.Mt, f.Kt, f.nnz, f.padded_len, f.max_tile) == (d["Mt"], d["Kt"], d["nnz"], d["padded_len"], d["max_tile"])
+    assert list(f.tile_ptr) == d["tile_ptr"]
+    assert [int(b) for b in f.bits] == d["bits"]
+    assert [format(int(v), "04x") for v in f.values] == d["values_hex"]
+    assert f.header() == bytes.fromhex(d["header_hex"].replace(" ", ""))
+    blob = f.blob()
+    assert len(blob) == 64 + 4 * 3 + 8 * 16 + 2 * 16
+    g = oracle.tcb_parse(blob)
+    assert np.array_equal(oracle.tcb_decode(g), W.view(np.uint16))
+
+
+@pytest.mark.parametrize("M,K,TM,TK,density", [
+    (1, 1, 64, 8, 1.0), (64, 64, 64, 64, 0.5), (100, 70, 64, 64, 0.5), (130, 300, 128, 64, 0.3),
+    (65, 257, 64, 256, 0.01), (200, 40, 256, 8, 0.99), (64, 64, 64, 64, 0.0),
+])
+def test_format_round_trip_and_invariants(M, K, TM, TK, density):
+    W, mask, _ = _rand_case(M * 1000 + K, M, K, 1, density, signed_zero=True)
+    f = oracle.tcb_encode(W, mask, TM=TM, TK=TK)
+    dec = oracle.tcb_decode(oracle.tcb_parse(f.blob()))
+    want = np.where(mask, W.view(np.uint16), np.uint16(0))
+    assert np.array_equal(dec, want)  # bit-exact, -0 kept where the mask keeps it
+    assert f.nnz == int(mask.sum())
+    pc = np.array([bin(int(b)).count("1") for b in f.bits])
+    assert pc.sum() == f.nnz
+    WPC = TM // 64
+    per_tile = pc.reshape(f.Mt * f.Kt, TK * WPC).sum(axis=1)
+    lens = np.diff(f.tile_ptr.astype(np.int64))
+    assert np.all(lens % 8 == 0) and np.all(lens >= per_tile) and np.all(lens - per_tile < 8)
+    for t in range(f.Mt * f.Kt):
+        pad = f.values[f.tile_ptr[t] + per_tile[t]:f.tile_ptr[t + 1]]
+        assert np.all(pad == 0)
+    assert f.max_tile == (lens.max() if lens.size else 0)
+
+
+def test_null_mask_keeps_nonzeros():
+    W, _, _ = _rand_case(13, 70, 70, 1, 1.0, signed_zero=True)
+    W[3, 3] = 0
+    f = oracle.tcb_encode(W, None, TM=64, TK=64)
+    keep = (W.view(np.uint16) & 0x7FFF) != 0
+    assert f.nnz == int(keep.sum())
+    dec = oracle.tcb_decode(f)
+    assert np.array_equal(dec, np.where(keep, W.view(np.uint16), 0))
+
+
+# ---------------------------------------------------------------- planted mistakes
+def _mut_dropped_last_term(W, mask, X):
+    return oracle.masked_matmul(W[:, :-1], None if mask is None else mask[:, :-1], X[:, :-1])
+
+
+def _mut_mask_ignored(W, mask, X):
+    return oracle.masked_matmul(W, None, X)
+
+
+def _mut_sign(W, mask, X):
+    Y = oracle.masked_matmul(W, mask, X)
+    Y[:, 0] = -Y[:, 0]
+    return Y
+
+
+def _mut_transposed_weight(W, mask, X):
+    Wt = np.ascontiguousarray(W.T)
+    return oracle.masked_matmul(Wt, None if mask is None else mask.T, X[:, :Wt.shape[1]])
+
+
+@pytest.mark.parametrize("mut", [_mut_dropped_last_term, _mut_mask_ignored, _mut_sign, _mut_transposed_weight])
+def test_planted_mistakes_fail_the_pins(mut):
+    W, mask, X = _rand_case(14, 24, 24, 3, 0.5)
+    try:
+        ok, _, _ = _check_against_exact(mut, W, mask, X)
+    except Exception:
+        ok = False
+    assert not ok
+
+
+def test_planted_format_mistake_fails_hand_bytes():
+    # a row-major value order instead of column-major must not reproduce the hand bytes
+    d = json.load(open(os.path.join(GOLDEN, "tcb_hand_example.json")))
+    W = np.array(d["W_rows_fp16"], dtype=np.float16)
+    Wb = W.view(np.uint16)
+    rowmajor = [format(int(v), "04x") for v in Wb[:, :8][Wb[:, :8] != 0]]
+    assert rowmajor != d["values_hex"][:len(rowmajor)]

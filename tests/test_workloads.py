@@ -1,0 +1,72 @@
+"""Pins of the seeded input generator (shared by both sides; no method arithmetic)."""
+import numpy as np
+import pytest
+from scipy import integrate, stats
+
+import swm_workloads as wl
+
+
+def test_keep_count_round_half_even():
+    assert wl.keep_count(4096, 0.5) == 2048
+    assert wl.keep_count(4096, 0.6) == 1638
+    assert wl.keep_count(4096, 0.7) == 1229
+    assert wl.keep_count(11008, 0.5) == 5504
+    assert wl.keep_count(5, 0.5) == 3  # round(2.5) = 2 (half to even)
+
+
+def test_magnitude_prune_ties_go_to_lower_column():
+    W = np.array([[0.5, -0.5, 0.25, 0.5, -0.25, 1.0]], dtype=np.float16)
+    m = wl.magnitude_prune_mask(W, 0.5)  # keep 3: 1.0 at col 5, then 0.5s at cols 0, 1
+    assert m.tolist() == [[True, True, False, False, False, True]]
+
+
+def test_magnitude_prune_against_sort_definition():
+    g = np.random.default_rng(0)
+    W = g.choice(np.array([0.0, 0.25, -0.25, 0.5, 1.0, -1.0], dtype=np.float16), size=(40, 37))
+    for s in (0.0, 0.3, 0.5, 0.7, 1.0):
+        m = wl.magnitude_prune_mask(W, s)
+        keep = wl.keep_count(37, s)
+        for r in range(40):
+            order = sorted(range(37), key=lambda c: (-abs(float(W[r, c])), c))
+            assert set(np.nonzero(m[r])[0]) == set(order[:keep])
+
+
+def test_pruned_weight_is_zero_where_pruned():
+    W, mask = wl.pruned_weight(99, 0, 64, 128, 0.5)
+    assert np.all(mask.sum(axis=1) == 64)
+    assert np.all(W.view(np.uint16)[~mask] == 0)
+
+
+def test_generators_are_deterministic():
+    a = wl.activations(2, 0, 4, 100)
+    b = wl.activations(2, 0, 4, 100)
+    assert np.array_equal(a.view(np.uint16), b.view(np.uint16))
+    c = wl.activations(2, 1, 4, 100)
+    assert not np.array_equal(a, c)
+
+
+def test_tiny_mask_is_bernoulli_half():
+    W, mask, X = wl.tiny()
+    assert W.shape == (256, 512) and X.shape == (8, 512)
+    assert abs(mask.mean() - 0.5) < 0.01
+    assert np.all(W.view(np.uint16)[~mask] == 0)
+
+
+def test_silu_threshold_zero_fraction_matches_distribution():
+    """P(|SiLU(g) u| < tau) for g, u ~ N(0,1), by 1-D quadrature over g.
+
+    For fixed g, |SiLU(g) u| < tau iff |u| < tau/|SiLU(g)|, probability
+    2 Phi(tau/|s|) - 1.  The generator's empirical zero fraction must agree.
+    """
+    tau = 0.3
+
+    def inner(gv):
+        s = abs(gv / (1 + np.exp(-gv)))
+        return stats.norm.pdf(gv) * (1.0 if s == 0 else (2 * stats.norm.cdf(tau / s) - 1))
+
+    p, _ = integrate.quad(inner, -12, 12, points=[0.0], limit=200)
+    x = wl.silu_gated_sparse(77, 0, 4, 50000, tau)
+    frac = np.mean(x == 0)
+    assert 0.69 < p < 0.72  # roughly 70% of entries fall below 0.3
+    assert abs(frac - p) < 0.01
+    assert np.all(np.abs(x[x != 0].astype(np.float64)) >= tau)
