@@ -1,0 +1,188 @@
+/*
+ * swm.h -- C ABI of the MI355X (gfx950) sparse-weight matmul library.
+ *
+ * The library multiplies a statically pruned fp16 weight matrix W (out x in,
+ * M x K, moderate unstructured sparsity, stored compressed) by dense fp16
+ * activations, in the decode regime (N = 1..16 tokens, bandwidth bound), with
+ * optional skipping of input channels whose activation is zero, and in the
+ * prefill regime (N in the hundreds to thousands, matrix-core bound).  A dense
+ * GEMM of the same shapes is exported beside it as the honest baseline.
+ *
+ * Sources of the operations (the pages this library is built from):
+ *  - "Unified Static-Dynamic Pruning for Efficient LLM Inference" (SPDP),
+ *    abstract: unstructured static pruning stored in a tiled column-wise
+ *    bitmap compressed format; a decode kernel that skips zero activations at
+ *    run time (sparse matrix x sparse vector); a prefill SpMM on the matrix
+ *    cores over the same format.
+ *  - "Accelerating GPU inference of LLMs with moderately unstructured sparse
+ *    weight matrices", Sec. 1 (Challenges 1-3) and Sec. 2.1: the pattern is
+ *    computed offline and stored in a dedicated format; prefill inputs are
+ *    [BL, H] and decode inputs [B, H]; at ~50% sparsity position metadata and
+ *    on-chip decoding decide whether a sparse kernel beats the dense one.
+ *
+ * Conventions shared by every entry point
+ *  - fp16 data is passed as raw IEEE binary16 bits (uint16_t / void*).
+ *  - W is row-major M x K with leading dimension ldw >= K (elements).
+ *  - Activations are TOKEN-MAJOR: X is N rows of K elements, row n is token
+ *    n, leading dimension ldx >= K.  The mathematical operand is X^T (K x N).
+ *  - Outputs are token-major too: Y is N rows of M elements, ldy >= M, and is
+ *    OVERWRITTEN (no accumulation into existing contents).
+ *    Y[n][m] = sum_k mask[m][k] * W[m][k] * X[n][k], accumulated in fp32 and
+ *    rounded once to fp16 (round to nearest even).
+ *  - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *    Launching entry points are asynchronous on that stream; the caller keeps
+ *    X and Y alive until the stream work completes.  Y must not alias X.
+ *  - Device pointers must belong to the device that is current when the call
+ *    is made; a format handle is bound to the device current at creation.
+ *  - Every call returns an swm_status.  Nothing aborts, throws or prints.
+ *    On a validation error no output is touched.  Kernel faults are reported
+ *    as SWM_ERR_HIP by a later checked call (swm_last_hip_error() holds the
+ *    hipError_t of the last failing runtime call).
+ *  - Calls that use the same handle share its split-K workspace and must be
+ *    ordered on one stream; handles are otherwise read-only after creation.
+ */
+#ifndef SWM_H_
+#define SWM_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum swm_status {
+  SWM_OK = 0,
+  SWM_ERR_INVALID_ARG = 1, /* null pointer, ld < dim, N <= 0, n outside [1,16] */
+  SWM_ERR_SHAPE = 2,       /* dimensions inconsistent with the format */
+  SWM_ERR_ALIGN = 3,       /* a pointer or leading dimension breaks an alignment rule */
+  SWM_ERR_OOM = 4,         /* host or device allocation failed */
+  SWM_ERR_OVERFLOW = 5,    /* padded value count would reach 2^32, or a size overflows */
+  SWM_ERR_FORMAT = 6,      /* blob or handle fails validation */
+  SWM_ERR_HIP = 7,         /* HIP runtime or launch error */
+  SWM_ERR_UNSUPPORTED = 8  /* tile shape or size this build has no kernel for */
+} swm_status;
+
+/* Opaque compressed-weight handle (owns all of its device memory). */
+typedef struct swm_format swm_format;
+
+/* Tile shape.  tm: rows per tile, a multiple of 64 (kernels: 64).  tk: columns
+ * per tile, a multiple of 8 (kernels: 64, 128 or 256).  NULL = {64, 64}. */
+typedef struct swm_tile_cfg {
+  int32_t tm;
+  int32_t tk;
+} swm_tile_cfg;
+
+/* Sizes of a format; bytes_* are the sections of the export blob. */
+typedef struct swm_format_info {
+  int64_t m, k;
+  int32_t tm, tk;
+  int64_t mt, kt;          /* tile grid */
+  uint64_t nnz;            /* kept entries (unpadded) */
+  uint64_t padded_len;     /* stored values including per-tile padding */
+  uint32_t max_tile;       /* largest padded tile run, in values */
+  uint32_t reserved;
+  uint64_t bytes_header, bytes_tile_ptr, bytes_bits, bytes_values, bytes_total;
+} swm_format_info;
+
+/* ------------------------------------------------------------------ format */
+
+/* sparse_compress: build the tiled column-bitmap format (SWM-TCB v1) from a
+ * dense fp16 W and an optional mask, and upload it to the current device.
+ * Source: SPDP abstract (Tiled-CBC format, unstructured static pruning) and
+ * the moderate-sparsity page, Sec. 2.1 (pattern precomputed offline).
+ *  W, mask: HOST pointers.  mask is uint8 M x K (ldm >= K), nonzero = keep;
+ *  NULL keeps every entry whose value is not +0/-0.  Kept entries are stored
+ *  with their exact bits (also a kept +-0); pruned entries decode to +0.
+ *  Layout: tiles of tm x tk, per tile column one tm-bit bitmap, kept values
+ *  packed column-major within the tile, each tile run padded to 8 values,
+ *  uint32 exclusive prefix of run lengths.
+ *  Synchronous: returns after the upload on `stream` has completed.
+ *  *out receives a new handle owned by the caller (swm_format_destroy). */
+swm_status swm_sparse_compress(const uint16_t* W, int64_t ldw, const uint8_t* mask, int64_t ldm,
+                               int64_t M, int64_t K, const swm_tile_cfg* cfg, void* stream,
+                               swm_format** out);
+
+/* Host-only encoder: the same bytes swm_sparse_compress uploads, written as an
+ * export blob into buf (capacity cap bytes).  buf may be NULL to query the
+ * size, which is returned in *size either way.  Touches no GPU. */
+swm_status swm_encode_blob(const uint16_t* W, int64_t ldw, const uint8_t* mask, int64_t ldm,
+                           int64_t M, int64_t K, const swm_tile_cfg* cfg, void* buf, size_t cap,
+                           size_t* size);
+
+/* Export the handle as a little-endian blob: 64-byte header ("SWMT", version
+ * 1, M, K, tm, tk, nnz, padded_len, mt, kt, max_tile, 0) || tile_ptr (uint32,
+ * mt*kt+1) || bits (uint64, mt*kt*tk*tm/64) || values (uint16, padded_len).
+ * buf NULL = size query. */
+swm_status swm_format_export(const swm_format* f, void* buf, size_t cap, size_t* size);
+
+/* Validate a blob and upload it as a new handle (synchronous on stream). */
+swm_status swm_format_import(const void* buf, size_t size, void* stream, swm_format** out);
+
+/* Check a blob without uploading: header fields, section sizes, monotone
+ * tile_ptr with runs that are multiples of 8, run length >= popcount of the
+ * tile's bitmaps and < popcount + 8, zero padding, no bits for rows >= M or
+ * columns >= K, nnz and max_tile consistent.  Returns SWM_ERR_FORMAT if not. */
+swm_status swm_format_validate_blob(const void* buf, size_t size);
+
+/* Fill *info from a handle. */
+swm_status swm_format_query(const swm_format* f, swm_format_info* info);
+
+/* Worst-case sizes for an M x K matrix with nnz kept entries (padding at most
+ * 7 values per tile); SWM_ERR_OVERFLOW if the padded length could reach 2^32
+ * or the byte count overflows.  No allocation. */
+swm_status swm_size_dry_run(int64_t M, int64_t K, uint64_t nnz, const swm_tile_cfg* cfg,
+                            swm_format_info* info);
+
+/* Release a handle and its device memory (NULL is a no-op). */
+swm_status swm_format_destroy(swm_format* f);
+
+/* Expand the handle into dense fp16 W (.) mask on the device: W_dev is M x K,
+ * ldw >= K, fully overwritten (pruned positions get +0).  Asynchronous. */
+swm_status swm_decompress(const swm_format* f, void* W_dev, int64_t ldw, void* stream);
+
+/* ------------------------------------------------------------------ products */
+
+/* spmm: Y = (W (.) mask) X for any N >= 1 (conventions above).
+ * Source: SPDP abstract (decode-phase spMspV kernel and prefill SpMM kernel over
+ * one format); moderate-sparsity page Sec. 2.1 (prefill [BL,H], decode [B,H]).
+ *  X: DEVICE fp16 token-major N x K (ldx >= K).  Y: DEVICE fp16 N x M (ldy >=
+ *  M), overwritten.  N <= 16 runs the decode kernel, larger N the prefill
+ *  kernel.  Asynchronous on stream. */
+swm_status swm_spmm(const swm_format* f, const void* X, int64_t ldx, void* Y, int64_t ldy,
+                    int64_t N, void* stream);
+
+/* spmspv: as swm_spmm for 1 <= n <= 16 tokens, skipping every input channel
+ * k with x[t][k] == 0 (+0 or -0) for all tokens t: its weight column is
+ * neither fetched nor decoded.  Same result as swm_spmm up to fp32 summation
+ * order (skipped terms are exact zeros for finite inputs).
+ * Source: SPDP abstract (input-adaptive dynamic pruning; run-time activation
+ * skipping in the spMspV kernel); "Reduced Matrix Multiplication" blog page,
+ * Sec. 4.2 (an FFN down projection multiplies only the kept channels). */
+swm_status swm_spmspv(const swm_format* f, const void* x, int64_t ldx, void* y, int64_t ldy,
+                      int32_t n, void* stream);
+
+/* dense_gemm: Y = W X with a DENSE fp16 W (row-major M x K, ldw >= K, device),
+ * the same X / Y conventions, any N >= 1.  The in-house dense baseline and the
+ * fallback to the full product.  Source: moderate-sparsity page, Sec. 1 (a
+ * sparse kernel is only useful if it beats the dense product at the same
+ * shape). */
+swm_status swm_dense_gemm(const void* W, int64_t ldw, const void* X, int64_t ldx, void* Y,
+                          int64_t ldy, int64_t M, int64_t K, int64_t N, void* stream);
+
+/* ------------------------------------------------------------------ misc */
+
+/* Static string for a status code (never NULL). */
+const char* swm_status_str(swm_status s);
+
+/* hipError_t value of the last failing HIP call in this process (0 if none). */
+int32_t swm_last_hip_error(void);
+
+/* Library version: major*10000 + minor*100 + patch. */
+int32_t swm_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SWM_H_ */

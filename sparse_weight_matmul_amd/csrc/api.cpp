@@ -1,0 +1,356 @@
+// C ABI of the sparse-weight matmul library: handle management, argument
+// checks, dispatch by token count, error mapping.  No entry point aborts,
+// throws across the boundary or prints.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstring>
+#include <mutex>
+#include <new>
+#include <vector>
+
+#include "kernels.h"
+#include "swm.h"
+#include "swm_internal.h"
+
+struct swm_format {
+  swm::Header h;
+  std::vector<uint8_t> blob;  // host copy of the export blob
+  int device = 0;
+  void* dev_mem = nullptr;     // one allocation for every device section
+  swm::DevFormat d;
+  swm::DecodePlan plan;
+};
+
+namespace {
+
+std::atomic<int32_t> g_last_hip{0};
+
+swm_status hip_fail(hipError_t e) {
+  g_last_hip.store(int32_t(e));
+  return SWM_ERR_HIP;
+}
+
+#define SWM_HIP(expr)                              \
+  do {                                             \
+    hipError_t e_ = (expr);                        \
+    if (e_ != hipSuccess) return hip_fail(e_);     \
+  } while (0)
+
+size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+int num_cus(int dev) {
+  static std::mutex mu;
+  static std::vector<int> cache;
+  std::lock_guard<std::mutex> g(mu);
+  if (dev >= int(cache.size())) cache.resize(dev + 1, 0);
+  if (cache[dev] == 0) {
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0)
+      v = 256;
+    cache[dev] = v;
+  }
+  return cache[dev];
+}
+
+// Per-device workspace of the dense small-N kernel (split-K partials, arrival
+// counters and a zero row).  Calls on one device must be stream-ordered.
+struct DenseWs {
+  float* partials = nullptr;
+  size_t partial_floats = 0;
+  uint32_t* counters = nullptr;
+  size_t n_counters = 0;
+  uint16_t* zeros = nullptr;
+  size_t n_zeros = 0;
+};
+
+swm_status dense_workspace(int dev, size_t pf, size_t nc, size_t nz, hipStream_t s, DenseWs** out) {
+  static std::mutex mu;
+  static std::vector<DenseWs> ws;
+  std::lock_guard<std::mutex> g(mu);
+  if (dev >= int(ws.size())) ws.resize(dev + 1);
+  DenseWs& w = ws[dev];
+  if (pf > w.partial_floats || nc > w.n_counters || nz > w.n_zeros) {
+    SWM_HIP(hipDeviceSynchronize());  // old buffers may still be in use by queued work
+    if (pf > w.partial_floats) {
+      if (w.partials) (void)hipFree(w.partials);
+      w.partials = nullptr;
+      w.partial_floats = 0;
+      if (hipMalloc(&w.partials, pf * sizeof(float)) != hipSuccess) return SWM_ERR_OOM;
+      w.partial_floats = pf;
+    }
+    if (nc > w.n_counters) {
+      if (w.counters) (void)hipFree(w.counters);
+      w.counters = nullptr;
+      w.n_counters = 0;
+      if (hipMalloc(&w.counters, nc * sizeof(uint32_t)) != hipSuccess) return SWM_ERR_OOM;
+      SWM_HIP(hipMemset(w.counters, 0, nc * sizeof(uint32_t)));
+      w.n_counters = nc;
+    }
+    if (nz > w.n_zeros) {
+      if (w.zeros) (void)hipFree(w.zeros);
+      w.zeros = nullptr;
+      w.n_zeros = 0;
+      if (hipMalloc(&w.zeros, nz * sizeof(uint16_t)) != hipSuccess) return SWM_ERR_OOM;
+      SWM_HIP(hipMemset(w.zeros, 0, nz * sizeof(uint16_t)));
+      w.n_zeros = nz;
+    }
+    SWM_HIP(hipDeviceSynchronize());
+  }
+  (void)s;
+  *out = &w;
+  return SWM_OK;
+}
+
+swm_status upload(std::vector<uint8_t>&& blob, const swm::Header& h, hipStream_t s, swm_format** out) {
+  swm_format* f = new (std::nothrow) swm_format;
+  if (!f) return SWM_ERR_OOM;
+  f->h = h;
+  f->blob = std::move(blob);
+  if (hipGetDevice(&f->device) != hipSuccess) {
+    delete f;
+    return hip_fail(hipErrorNoDevice);
+  }
+  f->plan = swm::plan_decode(h, 16, num_cus(f->device));
+  const size_t T = h.tiles();
+  const size_t b_tp = 4 * (T + 1), b_bits = 8 * h.n_bits(), b_vals = 2 * h.padded_len + 1024;
+  const size_t n_zero = size_t(h.kt) * h.tk + 64;
+  const size_t pf = swm::decode_partial_floats(h, f->plan);
+  size_t off = 0;
+  const size_t o_tp = off;
+  off = align_up(off + b_tp, 256);
+  const size_t o_bits = off;
+  off = align_up(off + b_bits, 256);
+  const size_t o_vals = off;
+  off = align_up(off + b_vals, 256);
+  const size_t o_zero = off;
+  off = align_up(off + 2 * n_zero, 256);
+  const size_t o_part = off;
+  off = align_up(off + 4 * pf, 256);
+  const size_t o_cnt = off;
+  off = align_up(off + 4 * size_t(h.mt) + 4, 256);
+  if (hipMalloc(&f->dev_mem, off) != hipSuccess) {
+    delete f;
+    return SWM_ERR_OOM;
+  }
+  uint8_t* base = static_cast<uint8_t*>(f->dev_mem);
+  const uint8_t* hb = f->blob.data();
+  hipError_t e = hipMemsetAsync(base, 0, off, s);
+  if (e == hipSuccess && b_tp) e = hipMemcpyAsync(base + o_tp, hb + h.off_tile_ptr(), b_tp, hipMemcpyHostToDevice, s);
+  if (e == hipSuccess && b_bits) e = hipMemcpyAsync(base + o_bits, hb + h.off_bits(), b_bits, hipMemcpyHostToDevice, s);
+  if (e == hipSuccess && h.padded_len)
+    e = hipMemcpyAsync(base + o_vals, hb + h.off_values(), 2 * h.padded_len, hipMemcpyHostToDevice, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) {
+    (void)hipFree(f->dev_mem);
+    delete f;
+    return hip_fail(e);
+  }
+  f->d.h = h;
+  f->d.tile_ptr = reinterpret_cast<const uint32_t*>(base + o_tp);
+  f->d.bits = reinterpret_cast<const uint64_t*>(base + o_bits);
+  f->d.vals = reinterpret_cast<const uint16_t*>(base + o_vals);
+  f->d.zeros = reinterpret_cast<const uint16_t*>(base + o_zero);
+  f->d.partials = reinterpret_cast<float*>(base + o_part);
+  f->d.counters = reinterpret_cast<uint32_t*>(base + o_cnt);
+  f->d.partial_floats = pf;
+  *out = f;
+  return SWM_OK;
+}
+
+swm_status check_tile_supported(const swm::Header& h) {
+  if (h.tm != 64 || h.tk != 64) return SWM_ERR_UNSUPPORTED;
+  if (h.m > (int64_t(1) << 31) - 64 || h.k > (int64_t(1) << 31) - 64) return SWM_ERR_UNSUPPORTED;
+  return SWM_OK;
+}
+
+bool on_current_device(const swm_format* f) {
+  int dev = -1;
+  return hipGetDevice(&dev) == hipSuccess && dev == f->device;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* swm_status_str(swm_status s) {
+  switch (s) {
+    case SWM_OK: return "ok";
+    case SWM_ERR_INVALID_ARG: return "invalid argument";
+    case SWM_ERR_SHAPE: return "shape mismatch";
+    case SWM_ERR_ALIGN: return "alignment";
+    case SWM_ERR_OOM: return "out of memory";
+    case SWM_ERR_OVERFLOW: return "size overflow";
+    case SWM_ERR_FORMAT: return "invalid format";
+    case SWM_ERR_HIP: return "HIP runtime error";
+    case SWM_ERR_UNSUPPORTED: return "unsupported";
+  }
+  return "unknown status";
+}
+
+int32_t swm_last_hip_error(void) { return g_last_hip.load(); }
+
+int32_t swm_version(void) { return 100; }
+
+swm_status swm_encode_blob(const uint16_t* W, int64_t ldw, const uint8_t* mask, int64_t ldm,
+                           int64_t M, int64_t K, const swm_tile_cfg* cfg, void* buf, size_t cap,
+                           size_t* size) {
+  if (!size) return SWM_ERR_INVALID_ARG;
+  std::vector<uint8_t> blob;
+  swm_status st = swm::encode_blob(W, ldw, mask, ldm, M, K, cfg, &blob);
+  if (st != SWM_OK) return st;
+  *size = blob.size();
+  if (!buf) return SWM_OK;
+  if (cap < blob.size()) return SWM_ERR_INVALID_ARG;
+  std::memcpy(buf, blob.data(), blob.size());
+  return SWM_OK;
+}
+
+swm_status swm_sparse_compress(const uint16_t* W, int64_t ldw, const uint8_t* mask, int64_t ldm,
+                               int64_t M, int64_t K, const swm_tile_cfg* cfg, void* stream,
+                               swm_format** out) {
+  if (!out) return SWM_ERR_INVALID_ARG;
+  std::vector<uint8_t> blob;
+  swm_status st = swm::encode_blob(W, ldw, mask, ldm, M, K, cfg, &blob);
+  if (st != SWM_OK) return st;
+  swm::Header h;
+  st = swm::read_header(blob.data(), blob.size(), &h);
+  if (st != SWM_OK) return st;
+  return upload(std::move(blob), h, static_cast<hipStream_t>(stream), out);
+}
+
+swm_status swm_format_export(const swm_format* f, void* buf, size_t cap, size_t* size) {
+  if (!f || !size) return SWM_ERR_INVALID_ARG;
+  *size = f->blob.size();
+  if (!buf) return SWM_OK;
+  if (cap < f->blob.size()) return SWM_ERR_INVALID_ARG;
+  std::memcpy(buf, f->blob.data(), f->blob.size());
+  return SWM_OK;
+}
+
+swm_status swm_format_validate_blob(const void* buf, size_t size) {
+  if (!buf) return SWM_ERR_INVALID_ARG;
+  return swm::validate_blob(buf, size, nullptr);
+}
+
+swm_status swm_format_import(const void* buf, size_t size, void* stream, swm_format** out) {
+  if (!buf || !out) return SWM_ERR_INVALID_ARG;
+  swm::Header h;
+  swm_status st = swm::validate_blob(buf, size, &h);
+  if (st != SWM_OK) return st;
+  std::vector<uint8_t> blob;
+  try {
+    blob.assign(static_cast<const uint8_t*>(buf), static_cast<const uint8_t*>(buf) + size);
+  } catch (...) {
+    return SWM_ERR_OOM;
+  }
+  return upload(std::move(blob), h, static_cast<hipStream_t>(stream), out);
+}
+
+swm_status swm_format_query(const swm_format* f, swm_format_info* info) {
+  if (!f || !info) return SWM_ERR_INVALID_ARG;
+  swm::fill_info(f->h, info);
+  return SWM_OK;
+}
+
+swm_status swm_size_dry_run(int64_t M, int64_t K, uint64_t nnz, const swm_tile_cfg* cfg,
+                            swm_format_info* info) {
+  if (!info) return SWM_ERR_INVALID_ARG;
+  swm::Header h;
+  swm_status st = swm::plan_grid(M, K, cfg, &h);
+  if (st != SWM_OK) return st;
+  if (nnz > uint64_t(M) * uint64_t(K)) return SWM_ERR_INVALID_ARG;
+  // Worst case: every tile pads by 7 values.
+  const unsigned __int128 worst = (unsigned __int128)nnz + (unsigned __int128)h.tiles() * 7u;
+  if (worst >= ((unsigned __int128)1 << 32)) return SWM_ERR_OVERFLOW;
+  h.nnz = nnz;
+  h.padded_len = uint64_t(worst);
+  h.max_tile = uint32_t(std::min<uint64_t>(uint64_t(h.tm) * h.tk, h.padded_len));
+  swm::fill_info(h, info);
+  return SWM_OK;
+}
+
+swm_status swm_format_destroy(swm_format* f) {
+  if (!f) return SWM_OK;
+  swm_status st = SWM_OK;
+  if (f->dev_mem) {
+    int cur = 0;
+    (void)hipGetDevice(&cur);
+    if (cur != f->device) (void)hipSetDevice(f->device);
+    hipError_t e = hipFree(f->dev_mem);
+    if (cur != f->device) (void)hipSetDevice(cur);
+    if (e != hipSuccess) st = hip_fail(e);
+  }
+  delete f;
+  return st;
+}
+
+swm_status swm_decompress(const swm_format* f, void* W_dev, int64_t ldw, void* stream) {
+  if (!f || !W_dev) return SWM_ERR_INVALID_ARG;
+  if (ldw < f->h.k) return SWM_ERR_INVALID_ARG;
+  swm_status st = check_tile_supported(f->h);
+  if (st != SWM_OK) return st;
+  if (!on_current_device(f)) return SWM_ERR_INVALID_ARG;
+  SWM_HIP(swm::launch_decompress(f->d, static_cast<uint16_t*>(W_dev), ldw, static_cast<hipStream_t>(stream)));
+  return SWM_OK;
+}
+
+static swm_status run_products(const swm_format* f, const void* X, int64_t ldx, void* Y, int64_t ldy,
+                               int64_t N, bool skip, hipStream_t s) {
+  if (!f || !X || !Y) return SWM_ERR_INVALID_ARG;
+  if (N <= 0 || ldx < f->h.k || ldy < f->h.m || ldx <= 0 || ldy <= 0) return SWM_ERR_INVALID_ARG;
+  swm_status st = check_tile_supported(f->h);
+  if (st != SWM_OK) return st;
+  if (!on_current_device(f)) return SWM_ERR_INVALID_ARG;
+  const uint16_t* x = static_cast<const uint16_t*>(X);
+  uint16_t* y = static_cast<uint16_t*>(Y);
+  if (N <= 16) {
+    SWM_HIP(swm::launch_decode(f->d, f->plan, x, ldx, y, ldy, int(N), skip, s));
+    return SWM_OK;
+  }
+  // Large N: sixteen-token slices through the decode kernel.
+  for (int64_t n0 = 0; n0 < N; n0 += 16) {
+    const int nn = int(std::min<int64_t>(16, N - n0));
+    SWM_HIP(swm::launch_decode(f->d, f->plan, x + n0 * ldx, ldx, y + n0 * ldy, ldy, nn, skip, s));
+  }
+  return SWM_OK;
+}
+
+swm_status swm_spmm(const swm_format* f, const void* X, int64_t ldx, void* Y, int64_t ldy,
+                    int64_t N, void* stream) {
+  return run_products(f, X, ldx, Y, ldy, N, false, static_cast<hipStream_t>(stream));
+}
+
+swm_status swm_spmspv(const swm_format* f, const void* x, int64_t ldx, void* y, int64_t ldy,
+                      int32_t n, void* stream) {
+  if (n < 1 || n > 16) return SWM_ERR_INVALID_ARG;
+  return run_products(f, x, ldx, y, ldy, n, true, static_cast<hipStream_t>(stream));
+}
+
+swm_status swm_dense_gemm(const void* W, int64_t ldw, const void* X, int64_t ldx, void* Y,
+                          int64_t ldy, int64_t M, int64_t K, int64_t N, void* stream) {
+  if (!W || !X || !Y) return SWM_ERR_INVALID_ARG;
+  if (M < 0 || K < 0 || N <= 0 || ldw < K || ldx < K || ldy < M || ldw <= 0 || ldx <= 0 || ldy <= 0)
+    return SWM_ERR_INVALID_ARG;
+  if (M > (int64_t(1) << 31) - 64 || K > (int64_t(1) << 31) - 64) return SWM_ERR_UNSUPPORTED;
+  if (M == 0) return SWM_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  int dev = 0;
+  SWM_HIP(hipGetDevice(&dev));
+  const auto p = swm::plan_dense_small(M, K, int(std::min<int64_t>(N, 16)), num_cus(dev));
+  DenseWs* ws = nullptr;
+  swm_status st = dense_workspace(dev, swm::dense_partial_floats(M, p), size_t((M + 63) / 64) + 1,
+                                  size_t(K) + 64, s, &ws);
+  if (st != SWM_OK) return st;
+  const uint16_t* w = static_cast<const uint16_t*>(W);
+  const uint16_t* x = static_cast<const uint16_t*>(X);
+  uint16_t* y = static_cast<uint16_t*>(Y);
+  for (int64_t n0 = 0; n0 < N; n0 += 16) {
+    const int nn = int(std::min<int64_t>(16, N - n0));
+    SWM_HIP(swm::launch_dense_small(p, w, ldw, x + n0 * ldx, ldx, y + n0 * ldy, ldy, M, K, nn,
+                                    ws->partials, ws->counters, ws->zeros, s));
+  }
+  return SWM_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,59 @@
+// Device-side view of a compressed weight and the kernel launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "swm_internal.h"
+
+namespace swm {
+
+// Device memory of one SWM-TCB v1 handle (TM = 64).
+struct DevFormat {
+  Header h;
+  const uint32_t* tile_ptr = nullptr;  // mt*kt + 1
+  const uint64_t* bits = nullptr;      // mt*kt*tk words
+  const uint16_t* vals = nullptr;      // padded_len values (+ slack for over-reads)
+  const uint16_t* zeros = nullptr;     // >= kt*tk + 64 zero halves (device)
+  float* partials = nullptr;           // split-K partial sums
+  uint32_t* counters = nullptr;        // one arrival counter per row block, kept at 0 between calls
+  size_t partial_floats = 0;
+};
+
+// Work split of the decode kernel for one call.
+struct DecodePlan {
+  int waves = 4;           // waves per workgroup (all on the same 64-row block)
+  int tiles_per_wave = 1;  // consecutive tiles of one row block per wave
+  int splits = 1;          // workgroups per row block (split-K)
+};
+
+DecodePlan plan_decode(const Header& h, int n, int num_cus);
+size_t decode_partial_floats(const Header& h, const DecodePlan& p);
+
+hipError_t launch_decode(const DevFormat& f, const DecodePlan& p, const uint16_t* X, int64_t ldx,
+                         uint16_t* Y, int64_t ldy, int n, bool skip, hipStream_t s);
+
+hipError_t launch_decompress(const DevFormat& f, uint16_t* W, int64_t ldw, hipStream_t s);
+
+// Dense W (row-major) times token-major X for n <= 16 tokens.
+struct DensePlan {
+  int waves = 4;
+  int kchunk = 512;  // columns per wave
+  int splits = 1;
+};
+DensePlan plan_dense_small(int64_t M, int64_t K, int n, int num_cus);
+size_t dense_partial_floats(int64_t M, const DensePlan& p);
+hipError_t launch_dense_small(const DensePlan& p, const uint16_t* W, int64_t ldw, const uint16_t* X,
+                              int64_t ldx, uint16_t* Y, int64_t ldy, int64_t M, int64_t K, int n,
+                              float* partials, uint32_t* counters, const uint16_t* zeros,
+                              hipStream_t s);
+
+// Tiled MFMA GEMM for larger N: dense W, or W expanded from the format tile by tile.
+hipError_t launch_prefill_dense(const uint16_t* W, int64_t ldw, const uint16_t* X, int64_t ldx,
+                                uint16_t* Y, int64_t ldy, int64_t M, int64_t K, int64_t N,
+                                hipStream_t s);
+hipError_t launch_prefill_sparse(const DevFormat& f, const uint16_t* X, int64_t ldx, uint16_t* Y,
+                                 int64_t ldy, int64_t N, hipStream_t s);
+
+}  // namespace swm

@@ -1,0 +1,48 @@
+// Internal declarations shared by the host format code and the HIP launchers.
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+#include <vector>
+
+#include "swm.h"
+
+namespace swm {
+
+constexpr uint32_t kVersion = 1;
+constexpr size_t kHeaderBytes = 64;
+constexpr int kPadValues = 8;  // each tile run is padded to a multiple of 8 values (16 B)
+
+// Parsed SWM-TCB v1 header (little-endian on disk; this build targets x86-64 hosts).
+struct Header {
+  int64_t m = 0, k = 0;
+  uint32_t tm = 0, tk = 0;
+  uint64_t nnz = 0, padded_len = 0;
+  uint32_t mt = 0, kt = 0;
+  uint32_t max_tile = 0;
+
+  uint64_t tiles() const { return uint64_t(mt) * kt; }
+  uint64_t words_per_col() const { return tm / 64; }
+  uint64_t n_bits() const { return tiles() * tk * words_per_col(); }
+  size_t off_tile_ptr() const { return kHeaderBytes; }
+  size_t off_bits() const { return off_tile_ptr() + 4 * (tiles() + 1); }
+  size_t off_values() const { return off_bits() + 8 * n_bits(); }
+  size_t total_bytes() const { return off_values() + 2 * padded_len; }
+};
+
+void write_header(const Header& h, uint8_t* dst);
+swm_status read_header(const void* buf, size_t size, Header* h);
+
+// Check tile shape and sizes; fills h.tm/tk/mt/kt/m/k.
+swm_status plan_grid(int64_t M, int64_t K, const swm_tile_cfg* cfg, Header* h);
+
+// Encode to a full export blob.
+swm_status encode_blob(const uint16_t* W, int64_t ldw, const uint8_t* mask, int64_t ldm,
+                       int64_t M, int64_t K, const swm_tile_cfg* cfg, std::vector<uint8_t>* out);
+
+// Full structural validation of a blob.
+swm_status validate_blob(const void* buf, size_t size, Header* h);
+
+void fill_info(const Header& h, swm_format_info* info);
+
+}  // namespace swm

@@ -1,0 +1,159 @@
+"""Host-side checks of the C-ABI library (no GPU needed).
+
+* the shared library loads and exports every function include/swm.h declares;
+* the C++ encoder writes the same bytes as the independent numpy encoder;
+* the validator rejects corrupted blobs;
+* size accounting and overflow detection of the dry run.
+"""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+import sparse_weight_matmul_amd as swm
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_functions():
+    text = open(os.path.join(ROOT, "include", "swm.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(swm_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = swm.load()
+    names = _declared_functions()
+    assert len(names) >= 15
+    for n in names:
+        assert hasattr(lib, n), n
+        assert n in swm.SIGNATURES, n
+    assert swm.version() >= 100
+    assert swm.status_str(0) == "ok"
+    assert swm.status_str(6) == "invalid format"
+
+
+def _case(seed, M, K, density, signed_zero=True):
+    g = np.random.default_rng(seed)
+    W = (0.02 * g.standard_normal((M, K))).astype(np.float16)
+    if signed_zero:
+        W[g.random((M, K)) < 0.05] = np.float16(-0.0)
+        W[g.random((M, K)) < 0.05] = np.float16(0.0)
+    mask = g.random((M, K)) < density
+    return W, mask
+
+
+@pytest.mark.parametrize("M,K,tile,density", [
+    (1, 1, (64, 64), 1.0), (3, 10, (64, 8), 0.5), (64, 64, (64, 64), 0.5), (100, 70, (64, 64), 0.5),
+    (130, 300, (128, 64), 0.3), (65, 257, (64, 256), 0.01), (200, 40, (256, 8), 0.99),
+    (256, 512, (64, 64), 0.0), (257, 129, (64, 128), 1.0),
+])
+def test_cpp_encoder_matches_numpy_encoder_bytes(M, K, tile, density):
+    W, mask = _case(M * 7 + K, M, K, density)
+    a = swm.encode_blob(W, mask, tile=tile)
+    b = oracle.tcb_encode(W, mask, TM=tile[0], TK=tile[1]).blob()
+    assert a == b
+    assert swm.validate_blob(a) == 0
+
+
+def test_cpp_encoder_null_mask_matches():
+    W, _ = _case(5, 90, 77, 1.0)
+    a = swm.encode_blob(W, None)
+    b = oracle.tcb_encode(W, None).blob()
+    assert a == b
+
+
+def test_cpp_encoder_tiny_workload_bytes():
+    import swm_workloads as wl
+    W, mask, _ = wl.tiny()
+    assert swm.encode_blob(W, mask) == oracle.tcb_encode(W, mask).blob()
+
+
+def _corrupt(blob: bytes, off: int, value: bytes) -> bytes:
+    b = bytearray(blob)
+    b[off:off + len(value)] = value
+    return bytes(b)
+
+
+def test_validator_rejects_corruption():
+    W, mask = _case(1, 100, 130, 0.5)
+    blob = swm.encode_blob(W, mask)
+    f = oracle.tcb_parse(blob)
+    T = f.Mt * f.Kt
+    off_tp = 64
+    off_bits = off_tp + 4 * (T + 1)
+    off_vals = off_bits + 8 * T * f.TK
+    assert swm.validate_blob(blob) == 0
+    bad = {
+        "magic": _corrupt(blob, 0, b"XXXX"),
+        "version": _corrupt(blob, 4, (2).to_bytes(4, "little")),
+        "reserved": _corrupt(blob, 60, (1).to_bytes(4, "little")),
+        "truncated": blob[:-2],
+        "extra": blob + b"\0\0",
+        "nnz": _corrupt(blob, 32, (f.nnz + 1).to_bytes(8, "little")),
+        "max_tile": _corrupt(blob, 56, (f.max_tile + 8).to_bytes(4, "little")),
+        "tile_ptr_nonmonotone": _corrupt(blob, off_tp + 4, (int(f.tile_ptr[2]) + 8).to_bytes(4, "little")),
+        "bit_beyond_M": _corrupt(blob, off_bits + 8 * ((f.Kt * 1) * f.TK + 3), (1 << 63).to_bytes(8, "little")),
+        "bit_beyond_K": _corrupt(blob, off_bits + 8 * ((f.Kt - 1) * f.TK + 63), (1).to_bytes(8, "little")),
+        "popcount_mismatch": _corrupt(blob, off_bits, (int(f.bits[0]) ^ 1).to_bytes(8, "little")),
+    }
+    # nonzero padding: find a tile whose run has padding
+    lens = np.diff(f.tile_ptr.astype(np.int64))
+    pcs = np.array([bin(int(x)).count("1") for x in f.bits]).reshape(T, f.TK).sum(1)
+    t = int(np.nonzero(lens > pcs)[0][0])
+    bad["padding"] = _corrupt(blob, off_vals + 2 * (int(f.tile_ptr[t + 1]) - 1), b"\x01\x00")
+    for name, b in bad.items():
+        assert swm.validate_blob(b) == 6, name
+
+
+def test_dry_run_sizes_and_overflow():
+    info = swm.size_dry_run(4096, 4096, 4096 * 2048)
+    assert info["mt"] == 64 and info["kt"] == 64
+    assert info["bytes_bits"] == 64 * 64 * 64 * 8
+    assert info["padded_len"] == 4096 * 2048 + 64 * 64 * 7
+    assert info["bytes_total"] == 64 + 4 * (64 * 64 + 1) + info["bytes_bits"] + 2 * info["padded_len"]
+    assert swm.size_dry_run_status(1 << 20, 1 << 20, 1 << 33) == 5  # padded length >= 2^32
+    assert swm.size_dry_run_status(10, 10, 101) == 1  # nnz > M*K
+    assert swm.size_dry_run_status(-1, 10, 0) == 1
+    assert swm.size_dry_run_status(64, 64, 0, tile=(32, 64)) == 1  # tm not a multiple of 64
+
+
+def test_dry_run_bounds_the_real_format():
+    W, mask = _case(3, 300, 200, 0.5)
+    info = swm.size_dry_run(300, 200, int(mask.sum()))
+    f = oracle.tcb_encode(W, mask)
+    assert f.padded_len <= info["padded_len"]
+    assert len(f.blob()) <= info["bytes_total"]
+
+
+def test_encoder_rejects_bad_arguments():
+    lib = swm.load()
+    size = ctypes.c_size_t(0)
+    W = np.zeros((4, 4), dtype=np.uint16)
+    # ldw < K
+    assert lib.swm_encode_blob(W.ctypes.data, 3, None, 4, 4, 4, None, None, 0, ctypes.byref(size)) == 1
+    # null W with a non-empty shape
+    assert lib.swm_encode_blob(None, 4, None, 4, 4, 4, None, None, 0, ctypes.byref(size)) == 1
+    # null size pointer
+    assert lib.swm_encode_blob(W.ctypes.data, 4, None, 4, 4, 4, None, None, 0, None) == 1
+    # bad tile shape
+    cfg = swm.TileCfg(64, 12)
+    assert lib.swm_encode_blob(W.ctypes.data, 4, None, 4, 4, 4, ctypes.byref(cfg), None, 0, ctypes.byref(size)) == 1
+    # empty matrix is fine
+    assert lib.swm_encode_blob(None, 0, None, 0, 0, 0, None, None, 0, ctypes.byref(size)) == 0
+    assert size.value == 64 + 4
+
+
+def test_null_handle_calls_are_rejected():
+    lib = swm.load()
+    inf = swm.FormatInfo()
+    assert lib.swm_format_query(None, ctypes.byref(inf)) == 1
+    assert lib.swm_spmm(None, None, 1, None, 1, 1, None) == 1
+    assert lib.swm_spmspv(None, None, 1, None, 1, 1, None) == 1
+    assert lib.swm_dense_gemm(None, 1, None, 1, None, 1, 1, 1, 1, None) == 1
+    assert lib.swm_decompress(None, None, 1, None) == 1
+    assert lib.swm_format_destroy(None) == 0
+    assert lib.swm_format_validate_blob(None, 0) == 1

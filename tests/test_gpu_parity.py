@@ -1,0 +1,235 @@
+"""GPU parity of the HIP path against the CPU oracle (MI355X only).
+
+Tolerance (floating point): max |Y_gpu - Y_ref| <= 1e-2 and
+||Y_gpu - Y_ref||_F / ||Y_ref||_F <= 1e-3, with Y_ref the float64 oracle and
+Y_gpu the fp16 output (fp32 accumulation, one rounding to fp16).
+Integer / byte work (format expansion, exact pins) is compared bitwise.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import swm_workloads as wl
+
+pytestmark = pytest.mark.gpu
+
+MAX_ABS = 1e-2
+REL_FRO = 1e-3
+
+
+def _t(a):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def _np(t):
+    import torch
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+def assert_close(Y_gpu, Y_ref, what=""):
+    Yg = np.asarray(Y_gpu, dtype=np.float64)
+    err = np.abs(Yg - Y_ref)
+    assert np.all(np.isfinite(Yg)), what
+    mx = float(err.max()) if err.size else 0.0
+    den = float(np.linalg.norm(Y_ref))
+    rel = float(np.linalg.norm(Yg - Y_ref)) / den if den > 0 else float(np.linalg.norm(Yg))
+    assert mx <= MAX_ABS, f"{what}: max abs err {mx}"
+    assert rel <= REL_FRO, f"{what}: rel Frobenius err {rel}"
+
+
+def _compress(swm, W, mask):
+    return swm.sparse_compress(W, mask)
+
+
+# ------------------------------------------------------------------ tiny workload
+@pytest.mark.parametrize("N", [1, 3, 8])
+def test_tiny_spmm(gpu_lib, N):
+    swm = gpu_lib
+    W, mask, X = wl.tiny()
+    f = _compress(swm, W, mask)
+    Y = swm.spmm(f, _t(X[:N]))
+    assert_close(_np(Y), oracle.masked_matmul(W, mask, X[:N]), f"tiny N={N}")
+
+
+def test_decompress_round_trip_bitwise(gpu_lib):
+    swm = gpu_lib
+    for (W, mask) in [wl.tiny()[:2], wl.pruned_weight(91, 0, 200, 333, 0.5)]:
+        f = _compress(swm, W, mask)
+        D = _np(swm.decompress(f)).view(np.uint16)
+        want = np.where(mask, W.view(np.uint16), np.uint16(0))
+        assert np.array_equal(D, want)
+
+
+def test_export_matches_oracle_encoder(gpu_lib):
+    swm = gpu_lib
+    W, mask, _ = wl.tiny()
+    f = _compress(swm, W, mask)
+    blob = f.export()
+    assert blob == oracle.tcb_encode(W, mask).blob()
+    g = swm.format_import(blob)
+    assert np.array_equal(_np(swm.decompress(g)).view(np.uint16), _np(swm.decompress(f)).view(np.uint16))
+
+
+# ------------------------------------------------------------------ exact pins
+def test_identity_weight_returns_x_bitwise(gpu_lib):
+    swm = gpu_lib
+    K = 200
+    W = np.eye(K, dtype=np.float16)
+    X = np.random.default_rng(1).standard_normal((16, K)).astype(np.float16)
+    f = _compress(swm, W, np.eye(K, dtype=bool))
+    Y = _np(swm.spmm(f, _t(X)))
+    assert np.array_equal(Y.view(np.uint16), X.view(np.uint16))
+
+
+def test_permutation_weight_bitwise(gpu_lib):
+    swm = gpu_lib
+    K = 130
+    g = np.random.default_rng(2)
+    perm = g.permutation(K)
+    P = np.zeros((K, K), dtype=np.float16)
+    P[np.arange(K), perm] = 1
+    X = g.standard_normal((5, K)).astype(np.float16)
+    f = _compress(swm, P, P != 0)
+    Y = _np(swm.spmm(f, _t(X)))
+    assert np.array_equal(Y.view(np.uint16), X[:, perm].view(np.uint16))
+
+
+def test_one_hot_activations_pick_columns_bitwise(gpu_lib):
+    swm = gpu_lib
+    W, mask = wl.pruned_weight(92, 0, 128, 96, 0.5)
+    f = _compress(swm, W, mask)
+    ks = [0, 1, 17, 63, 64, 95]
+    X = np.zeros((len(ks), 96), dtype=np.float16)
+    for n, k in enumerate(ks):
+        X[n, k] = 1
+    Y = _np(swm.spmm(f, _t(X))).view(np.uint16)
+    for n, k in enumerate(ks):
+        assert np.array_equal(Y[n], np.where(mask[:, k], W[:, k].view(np.uint16), 0))
+
+
+def test_all_zero_mask_gives_zero(gpu_lib):
+    swm = gpu_lib
+    W, _ = wl.pruned_weight(93, 0, 100, 300, 0.5)
+    f = _compress(swm, W, np.zeros(W.shape, dtype=bool))
+    X = np.random.default_rng(3).standard_normal((7, 300)).astype(np.float16)
+    Y = _np(swm.spmm(f, _t(X)))
+    assert np.all(Y == 0)
+
+
+# ------------------------------------------------------------------ ragged shapes and N sweep
+@pytest.mark.parametrize("M,K,N", [
+    (1, 1, 1), (65, 129, 2), (300, 1000, 16), (64, 4096, 5), (130, 72, 17), (77, 333, 9), (513, 260, 33),
+])
+def test_ragged_shapes(gpu_lib, M, K, N):
+    swm = gpu_lib
+    W, mask = wl.pruned_weight(94, M * 10 + K, M, K, 0.5)
+    X = np.random.default_rng(M + K + N).standard_normal((N, K)).astype(np.float16)
+    f = _compress(swm, W, mask)
+    Y = _np(swm.spmm(f, _t(X)))
+    assert_close(Y, oracle.masked_matmul(W, mask, X), f"{M}x{K}x{N}")
+
+
+def test_strided_activations_and_outputs(gpu_lib):
+    import torch
+    swm = gpu_lib
+    W, mask = wl.pruned_weight(95, 0, 192, 256, 0.5)
+    X = np.random.default_rng(4).standard_normal((6, 256)).astype(np.float16)
+    f = _compress(swm, W, mask)
+    Xbig = torch.zeros((6, 300), dtype=torch.float16, device="cuda")
+    Xbig[:, :256] = _t(X)
+    Ybig = torch.full((6, 200), 7.0, dtype=torch.float16, device="cuda")
+    swm.spmm(f, Xbig[:, :256], Ybig[:, :192])
+    Yb = _np(Ybig)
+    assert_close(Yb[:, :192], oracle.masked_matmul(W, mask, X), "strided")
+    assert np.all(Yb[:, 192:] == 7.0)  # columns beyond M untouched
+
+
+# ------------------------------------------------------------------ full-size decode (q_proj)
+@pytest.fixture(scope="module")
+def qproj(gpu_lib):
+    W, mask, X = wl.decode_qproj(16)
+    return W, mask, X, gpu_lib.sparse_compress(W, mask)
+
+
+@pytest.mark.parametrize("N", [1, 8, 16])
+def test_qproj_decode(gpu_lib, qproj, N):
+    W, mask, X, f = qproj
+    Y = _np(gpu_lib.spmm(f, _t(X[:N])))
+    assert_close(Y, oracle.masked_matmul(W, mask, X[:N]), f"q_proj N={N}")
+
+
+def test_qproj_deterministic(gpu_lib, qproj):
+    W, mask, X, f = qproj
+    a = _np(gpu_lib.spmm(f, _t(X)))
+    b = _np(gpu_lib.spmm(f, _t(X)))
+    assert np.array_equal(a.view(np.uint16), b.view(np.uint16))
+
+
+@pytest.mark.parametrize("N", [1, 8, 16])
+def test_qproj_dense_gemm(gpu_lib, qproj, N):
+    W, mask, X, _ = qproj
+    Y = _np(gpu_lib.dense_gemm(_t(W), _t(X[:N])))
+    assert_close(Y, oracle.masked_matmul(W, None, X[:N]), f"dense q_proj N={N}")
+
+
+# ------------------------------------------------------------------ spMspV (down_proj, SiLU-gated x)
+@pytest.fixture(scope="module")
+def down(gpu_lib):
+    W, mask, x = wl.spmspv_down(4, 0.3)
+    return W, mask, x, gpu_lib.sparse_compress(W, mask)
+
+
+@pytest.mark.parametrize("n", [1, 4])
+def test_spmspv_down(gpu_lib, down, n):
+    W, mask, x, f = down
+    frac = float(np.mean(x[:n] == 0))
+    assert 0.6 < frac < 0.8
+    y = _np(gpu_lib.spmspv(f, _t(x[:n])))
+    assert_close(y, oracle.masked_matmul_skip(W, mask, x[:n]), f"spmspv n={n}")
+    y2 = _np(gpu_lib.spmm(f, _t(x[:n])))
+    assert_close(y2, oracle.masked_matmul(W, mask, x[:n]), f"spmm on sparse x n={n}")
+
+
+def test_spmspv_zero_and_dense_inputs(gpu_lib, down):
+    W, mask, x, f = down
+    z = np.zeros((2, W.shape[1]), dtype=np.float16)
+    z[1, 5] = np.float16(-0.0)
+    assert np.all(_np(gpu_lib.spmspv(f, _t(z))) == 0)
+    xd = np.random.default_rng(5).standard_normal((3, W.shape[1])).astype(np.float16)
+    a = _np(gpu_lib.spmspv(f, _t(xd))).view(np.uint16)
+    b = _np(gpu_lib.spmm(f, _t(xd))).view(np.uint16)
+    assert np.array_equal(a, b)  # nothing to skip: identical arithmetic
+
+
+# ------------------------------------------------------------------ dense baseline, ragged
+@pytest.mark.parametrize("M,K,N", [(1, 1, 1), (65, 129, 3), (300, 1000, 16), (100, 64, 20)])
+def test_dense_gemm_ragged(gpu_lib, M, K, N):
+    g = np.random.default_rng(M * K)
+    W = (0.02 * g.standard_normal((M, K))).astype(np.float16)
+    X = g.standard_normal((N, K)).astype(np.float16)
+    Y = _np(gpu_lib.dense_gemm(_t(W), _t(X)))
+    assert_close(Y, oracle.masked_matmul(W, None, X), f"dense {M}x{K}x{N}")
+
+
+# ------------------------------------------------------------------ error paths through the ABI
+def test_error_codes(gpu_lib):
+    import ctypes
+    import torch
+    swm = gpu_lib
+    lib = swm.load()
+    W, mask, X = wl.tiny()
+    f = swm.sparse_compress(W, mask)
+    x = _t(X)
+    y = torch.empty((8, 256), dtype=torch.float16, device="cuda")
+    s = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    xp, yp = ctypes.c_void_p(x.data_ptr()), ctypes.c_void_p(y.data_ptr())
+    assert lib.swm_spmm(f._h, xp, 512, yp, 256, 0, s) == 1        # N <= 0
+    assert lib.swm_spmm(f._h, xp, 100, yp, 256, 8, s) == 1        # ldx < K
+    assert lib.swm_spmm(f._h, xp, 512, yp, 100, 8, s) == 1        # ldy < M
+    assert lib.swm_spmspv(f._h, xp, 512, yp, 256, 17, s) == 1     # n > 16
+    assert lib.swm_spmspv(f._h, xp, 512, yp, 256, 0, s) == 1      # n < 1
+    assert lib.swm_dense_gemm(xp, 512, xp, 512, yp, 256, 256, 512, -1, s) == 1
+    g = swm.sparse_compress(W, mask, tile=(128, 64))
+    assert lib.swm_spmm(g._h, xp, 512, yp, 256, 8, s) == 8        # no kernel for tm=128
