@@ -1,18 +1,22 @@
 """Benchmark of the sparse-weight matmul hot path on one MI355X.
 
-Default workload: decode on the q_proj shape -- W 4096x4096 fp16, 50% per-row
-magnitude pruning, compressed to the tiled column-bitmap format; one step is
-three sparse products with N = 1, 8 and 16 tokens.  The same step is timed for
-the in-house dense GEMM on the same (masked, dense-stored) W for the speedup.
+Default workload (``--workload decode``): the q_proj shape -- W 4096x4096 fp16
+at 50% per-row magnitude pruning, compressed to the tiled column-bitmap format.
+One step = three sparse products with N = 1, 8 and 16 tokens.  The same step
+is timed with the in-house dense GEMM on the masked W stored dense, for the
+speedup.  ``value`` = algorithmic bytes of the sparse products (compressed
+weight + X + Y) / their GPU time, in GB/s, inputs resident in HBM.
 
-value = algorithmic bytes moved by the sparse products (compressed weight
-+ X + Y) / their time, in GB/s, inputs resident in HBM.  Copies of the weight
-are rotated so that the working set exceeds 1 GiB (4x the 256 MB Infinity
-Cache) and every launch streams its weight from HBM.
+Timing: launches are captured once into HIP graphs (torch.cuda.CUDAGraph) and
+replayed, so host launch overhead does not starve the GPU; HIP events on the
+launch stream bracket the replays.  Copies of the weight are rotated so the
+working set exceeds 1 GiB (4x the 256 MB Infinity Cache) and every launch
+streams its weight from HBM.
 
-Other workloads (--workload): spmspv (down_proj, SiLU-gated x, N=1 and 4),
-prefill (up/gate 11008x4096, N = 512/2048/4096, s = 0.5/0.6/0.7),
-layer (seven Llama-2-7B linears back to back, N = 16 and 4096).
+Other workloads: ``spmspv`` (down_proj 4096x11008, SiLU-gated x with |x|<0.3
+zeroed, N = 1 and 4), ``prefill`` (up/gate 11008x4096, N = 512/2048/4096,
+sparsity 0.5/0.6/0.7), ``layer`` (seven Llama-2-7B linears back to back, N =
+16 and 4096).  Each prints one JSON line.
 """
 from __future__ import annotations
 
@@ -36,124 +40,251 @@ def _log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
-def _fmt_bytes(info):
+def fmt_bytes(info):
     return int(info["bytes_tile_ptr"] + info["bytes_bits"] + info["bytes_values"])
 
 
-class Timer:
-    """HIP events on the launch stream (torch's current stream)."""
+class Graphs:
+    """Capture launch sequences into HIP graphs and time their replays with events."""
 
     def __init__(self, torch):
         self.torch = torch
 
-    def run(self, fn, reps):
+    def capture(self, fns):
+        torch = self.torch
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for fn in fns:
+                fn()
+        g.replay()
+        torch.cuda.synchronize()
+        return g
+
+    def time(self, g, reps=1):
         torch = self.torch
         s = torch.cuda.current_stream()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
         e0.record(s)
-        for r in range(reps):
-            fn(r)
+        for _ in range(reps):
+            g.replay()
         e1.record(s)
         e1.synchronize()
-        return e0.elapsed_time(e1) / reps  # ms per call
+        return e0.elapsed_time(e1) / reps  # ms per replay
 
 
-def cpu_oracle_baseline(W, mask, X_list, alg_bytes_list, budget_s=20.0):
-    """Time the oracle (numpy fp64 product of the masked W) on the host cores."""
+def rotating_formats(swm, W, mask, min_bytes=ROTATE_BYTES):
+    f0 = swm.sparse_compress(W, mask)
+    fb = fmt_bytes(f0.info)
+    copies = max(2, int(np.ceil(min_bytes / fb)))
+    blob = f0.export()
+    return [f0] + [swm.format_import(blob) for _ in range(copies - 1)], fb
+
+
+def rotating_dense(torch, W, min_bytes=ROTATE_BYTES):
+    Wd = torch.from_numpy(W).cuda()
+    copies = max(2, int(np.ceil(min_bytes / (W.size * 2))))
+    return [Wd] + [Wd.clone() for _ in range(copies - 1)]
+
+
+def threads_used():
+    try:
+        from threadpoolctl import threadpool_info
+        return int(max([d.get("num_threads", 1) for d in threadpool_info()] or [1]))
+    except Exception:
+        return len(os.sched_getaffinity(0))
+
+
+def cpu_oracle(W, mask, X_list, units, unit, budget_s=20.0):
+    """The oracle (numpy float64 masked-W @ X, as it stands) on the host cores."""
     import oracle
-    from threadpoolctl import threadpool_info
-    Wm = np.where(mask, W.astype(np.float64), 0.0)  # precomputed, untimed
-    times, nbytes = [], 0
-    for X, ab in zip(X_list, alg_bytes_list):
+    Wm = np.where(mask, W.astype(np.float64), 0.0)  # untimed preparation
+    t_tot, u_tot = 0.0, 0.0
+    for X, u in zip(X_list, units):
+        oracle.masked_matmul(W[:4], mask[:4], X[:1])
         X64 = X.astype(np.float64)
-        oracle.masked_matmul(W[:8], mask[:8], X[:1])  # warm the code path
-        t = []
+        ts = []
         for _ in range(3):
             t0 = time.perf_counter()
             _ = Wm @ X64.T
-            t.append(time.perf_counter() - t0)
-        times.append(float(np.median(t)))
-        nbytes += ab
-    threads = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
-    return {"value": nbytes / sum(times) / 1e9, "unit": "GB/s", "cores": int(threads), "kind": "oracle",
-            "sample": "the full decode step (N = 1, 8, 16) as numpy float64 masked-W @ X, median of 3"}
+            ts.append(time.perf_counter() - t0)
+            if sum(ts) > budget_s:
+                break
+        t_tot += float(np.median(ts))
+        u_tot += u
+    return {"value": u_tot / t_tot, "unit": unit, "cores": threads_used(), "kind": "oracle"}
 
 
-def bench_decode(args, torch, swm, wl):
-    _log("building q_proj workload")
+# ------------------------------------------------------------------ decode (default)
+def bench_decode(args, torch, swm, wl, G):
+    _log("workload: decode q_proj 4096x4096, 50%")
     W, mask, X = wl.decode_qproj(16)
-    f0 = swm.sparse_compress(W, mask)
-    info = f0.info
-    fbytes = _fmt_bytes(info)
-    blob = f0.export()
-    copies = max(2, int(np.ceil(ROTATE_BYTES / fbytes)))
-    _log(f"format {fbytes / 1e6:.2f} MB, {copies} rotating copies")
-    fmts = [f0] + [swm.format_import(blob) for _ in range(copies - 1)]
-    Wd = torch.from_numpy(W).cuda()
-    dcopies = max(2, int(np.ceil(ROTATE_BYTES / (W.size * 2))))
-    Wds = [Wd] + [Wd.clone() for _ in range(dcopies - 1)]
+    fmts, fb = rotating_formats(swm, W, mask)
+    Wds = rotating_dense(torch, W)
+    C, CD = len(fmts), len(Wds)
+    _log(f"format {fb / 1e6:.2f} MB, {C} sparse / {CD} dense rotating copies")
     Xd = torch.from_numpy(X).cuda()
     Ns = (1, 8, 16)
-    Ys = {n: torch.empty((n, 4096), dtype=torch.float16, device="cuda") for n in Ns}
     M, K = W.shape
-    alg = {n: fbytes + 2 * K * n + 2 * M * n for n in Ns}
-    dense_bytes = {n: 2 * M * K + 2 * K * n + 2 * M * n for n in Ns}
-    timer = Timer(torch)
+    Ys = {n: torch.empty((n, M), dtype=torch.float16, device="cuda") for n in Ns}
+    alg = {n: fb + 2 * K * n + 2 * M * n for n in Ns}
+    dense_b = {n: 2 * M * K + 2 * K * n + 2 * M * n for n in Ns}
 
-    def sparse_step(r):
+    def sp(i, n):
+        return lambda: swm.spmm(fmts[i % C], Xd[:n], Ys[n])
+
+    def de(i, n):
+        return lambda: swm.dense_gemm(Wds[i % CD], Xd[:n], Ys[n])
+
+    for r in range(2):  # untimed: builds workspaces, warms the code paths
         for n in Ns:
-            swm.spmm(fmts[(r * 3 + n) % copies], Xd[:n], Ys[n])
-
-    def dense_step(r):
-        for n in Ns:
-            swm.dense_gemm(Wds[(r * 3 + n) % dcopies], Xd[:n], Ys[n])
-
-    # warmup
-    for r in range(args.warmup):
-        sparse_step(r)
-        dense_step(r)
+            sp(r, n)()
+            de(r, n)()
     torch.cuda.synchronize()
-    per_n, per_n_dense = {}, {}
-    reps_n = max(50, args.steps * 5)
+    per_n, per_n_d = {}, {}
     for n in Ns:
-        per_n[n] = timer.run(lambda r, n=n: swm.spmm(fmts[r % copies], Xd[:n], Ys[n]), reps_n)
-        per_n_dense[n] = timer.run(lambda r, n=n: swm.dense_gemm(Wds[r % dcopies], Xd[:n], Ys[n]), reps_n)
+        gs = G.capture([sp(i, n) for i in range(C)])
+        gd = G.capture([de(i, n) for i in range(CD)])
+        per_n[n] = G.time(gs, 3) / C
+        per_n_d[n] = G.time(gd, 3) / CD
+    # The contract's steps: W warmup steps, then exactly K timed steps.
+    g_warm = G.capture([sp(s * 3 + j, n) for s in range(args.warmup) for j, n in enumerate(Ns)])
+    g_steps = G.capture([sp(s * 3 + j, n) for s in range(args.steps) for j, n in enumerate(Ns)])
+    g_dsteps = G.capture([de(s * 3 + j, n) for s in range(args.steps) for j, n in enumerate(Ns)])
+    g_warm.replay()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    ms_sparse = timer.run(sparse_step, args.steps)
+    ms_total = G.time(g_steps, 1)
     wall = time.perf_counter() - t0
-    ms_dense = timer.run(dense_step, args.steps)
-    total_alg = sum(alg.values())
-    value = total_alg / (ms_sparse * 1e-3) / 1e9
-    detail = {
-        str(n): {"sparse_us": per_n[n] * 1e3, "dense_us": per_n_dense[n] * 1e3,
-                 "speedup_vs_dense": per_n_dense[n] / per_n[n],
-                 "sparse_GBps_alg": alg[n] / (per_n[n] * 1e-3) / 1e9,
-                 "dense_GBps": dense_bytes[n] / (per_n_dense[n] * 1e-3) / 1e9}
-        for n in Ns
-    }
-    dom_n = 16
-    achieved = alg[dom_n] / (per_n[dom_n] * 1e-3) / 1e9
-    roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": achieved / HBM_PEAK_GBS, "traffic": None,
-            "kernel": "decode_kernel (spmm, N=16)", "alg_bytes_per_launch": alg[dom_n]}
+    ms_dense = G.time(g_dsteps, 1)
+    ms_step = ms_total / args.steps
+    value = sum(alg.values()) / (ms_step * 1e-3) / 1e9
+    detail = {str(n): {"sparse_us": per_n[n] * 1e3, "dense_us": per_n_d[n] * 1e3,
+                       "speedup_vs_dense": per_n_d[n] / per_n[n],
+                       "sparse_GBps_alg": alg[n] / (per_n[n] * 1e-3) / 1e9,
+                       "sparse_frac_hbm": alg[n] / (per_n[n] * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                       "dense_GBps": dense_b[n] / (per_n_d[n] * 1e-3) / 1e9} for n in Ns}
+    dom = 16
+    ach = alg[dom] / (per_n[dom] * 1e-3) / 1e9
     out = {
         "metric": "decode SpMM HBM throughput on compressed bytes (q_proj 4096x4096, 50%)",
         "value": value, "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
-        "ms_per_step": ms_sparse, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "f16", "data": "synthetic (seeded N(0,1) fp16, 50% per-row magnitude pruning)",
-        "config": {"workload": "decode q_proj 4096x4096, 50% unstructured, N in {1,8,16}",
-                   "format": "SWM-TCB v1 tm=64 tk=64", "format_bytes": fbytes,
-                   "rotating_copies": copies},
-        "speedup_vs_dense": ms_dense / ms_sparse,
-        "dense_ms_per_step": ms_dense,
+        "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f16", "data": "synthetic (seeded N(0,1) fp16 W and X, 50% per-row magnitude pruning)",
+        "config": {"workload": "decode q_proj 4096x4096, 50% unstructured, N in {1,8,16} per step",
+                   "format": "SWM-TCB v1 tm=64 tk=64", "format_bytes": fb, "rotating_copies": C},
+        "speedup_vs_dense": ms_dense / ms_total,
+        "dense_ms_per_step": ms_dense / args.steps,
         "detail": detail,
-        "roofline": roof,
-        "wall_s_timed_region": wall,
+        "roofline": {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": ach / HBM_PEAK_GBS, "traffic": None,
+                     "kernel": "decode_kernel, N=16", "alg_bytes_per_launch": alg[dom],
+                     "avg_launch_us": per_n[dom] * 1e3},
+        "timed_wall_s": wall,
     }
     if not args.no_cpu:
         _log("timing the CPU oracle")
-        out["cpu_baseline"] = cpu_oracle_baseline(W, mask, [X[:n] for n in Ns], [alg[n] for n in Ns])
+        cb = cpu_oracle(W, mask, [X[:n] for n in Ns], [alg[n] for n in Ns], "B")
+        cb["value"] = cb["value"] / 1e9
+        cb["unit"] = "GB/s"
+        cb["sample"] = "one full decode step (N = 1, 8, 16), numpy float64 masked-W @ X, median of 3"
+        out["cpu_baseline"] = cb
+    return out
+
+
+# ------------------------------------------------------------------ spMspV
+def bench_spmspv(args, torch, swm, wl, G):
+    _log("workload: spMspV down_proj 4096x11008, 50%, SiLU-gated x")
+    W, mask, x = wl.spmspv_down(4, args.tau)
+    fmts, fb = rotating_formats(swm, W, mask)
+    Wds = rotating_dense(torch, W)
+    C, CD = len(fmts), len(Wds)
+    M, K = W.shape
+    xd = torch.from_numpy(x).cuda()
+    info = fmts[0].info
+    out = {"metric": "decode spMspV HBM throughput on algorithmic bytes", "unit": "GB/s", "n_gpus": 1,
+           "higher_is_better": True, "dtype": "f16", "data": "synthetic", "detail": {}}
+    for n in (1, 4):
+        active = np.any(x[:n] != 0, axis=0)
+        alg = int(info["bytes_tile_ptr"] + info["bytes_bits"] + 2 * mask[:, active].sum()) + 2 * K * n + 2 * M * n
+        y = torch.empty((n, M), dtype=torch.float16, device="cuda")
+        for i in range(2):
+            swm.spmspv(fmts[i], xd[:n], y)
+            swm.spmm(fmts[i], xd[:n], y)
+            swm.dense_gemm(Wds[i], xd[:n], y)
+        torch.cuda.synchronize()
+        t_skip = G.time(G.capture([lambda i=i: swm.spmspv(fmts[i % C], xd[:n], y) for i in range(C)]), 3) / C
+        t_full = G.time(G.capture([lambda i=i: swm.spmm(fmts[i % C], xd[:n], y) for i in range(C)]), 3) / C
+        t_dense = G.time(G.capture([lambda i=i: swm.dense_gemm(Wds[i % CD], xd[:n], y) for i in range(CD)]), 3) / CD
+        out["detail"][str(n)] = {
+            "zero_frac": float(np.mean(x[:n] == 0)), "inactive_cols": float(1 - active.mean()),
+            "spmspv_us": t_skip * 1e3, "spmm_us": t_full * 1e3, "dense_us": t_dense * 1e3,
+            "alg_bytes": alg, "spmspv_GBps_alg": alg / (t_skip * 1e-3) / 1e9,
+            "speedup_vs_dense": t_dense / t_skip, "speedup_vs_spmm": t_full / t_skip}
+    out["value"] = out["detail"]["1"]["spmspv_GBps_alg"]
+    return out
+
+
+# ------------------------------------------------------------------ prefill
+def bench_prefill(args, torch, swm, wl, G):
+    _log("workload: prefill up/gate 11008x4096")
+    out = {"metric": "prefill SpMM useful TFLOP/s (2*nnz*N / t)", "unit": "TFLOP/s", "n_gpus": 1,
+           "higher_is_better": True, "dtype": "f16", "data": "synthetic", "detail": {}}
+    Ns = [int(v) for v in args.prefill_n.split(",")]
+    sps = [float(v) for v in args.prefill_s.split(",")]
+    Xfull = None
+    for s in sps:
+        W, mask, X = wl.prefill_upgate(s, max(Ns))
+        if Xfull is None:
+            Xfull = torch.from_numpy(X).cuda()
+        f = swm.sparse_compress(W, mask)
+        Wd = torch.from_numpy(W).cuda()
+        M, K = W.shape
+        nnz = int(mask.sum())
+        for n in Ns:
+            y = torch.empty((n, M), dtype=torch.float16, device="cuda")
+            swm.spmm(f, Xfull[:n], y)
+            swm.dense_gemm(Wd, Xfull[:n], y)
+            torch.cuda.synchronize()
+            reps = 5
+            t_sp = G.time(G.capture([lambda: swm.spmm(f, Xfull[:n], y)] * reps), 3) / reps
+            t_de = G.time(G.capture([lambda: swm.dense_gemm(Wd, Xfull[:n], y)] * reps), 3) / reps
+            useful = 2.0 * nnz * n
+            dense_fl = 2.0 * M * K * n
+            out["detail"][f"s{s}_n{n}"] = {
+                "sparse_us": t_sp * 1e3, "dense_us": t_de * 1e3, "speedup_vs_dense": t_de / t_sp,
+                "useful_TFLOPs": useful / (t_sp * 1e-3) / 1e12,
+                "sparse_dense_equiv_TFLOPs": dense_fl / (t_sp * 1e-3) / 1e12,
+                "dense_TFLOPs": dense_fl / (t_de * 1e-3) / 1e12}
+        del f, Wd
+    k0 = f"s{sps[0]}_n{Ns[-1]}"
+    out["value"] = out["detail"][k0]["useful_TFLOPs"]
+    return out
+
+
+# ------------------------------------------------------------------ layer
+def bench_layer(args, torch, swm, wl, G):
+    _log("workload: Llama-2-7B-shaped layer, 7 linears")
+    out = {"metric": "layer time, 7 linears back to back", "unit": "us", "n_gpus": 1,
+           "higher_is_better": False, "dtype": "f16", "data": "synthetic", "detail": {}}
+    lin = []
+    for i in range(7):
+        W, mask, X = wl.layer_linear(i, 4096)
+        f = swm.sparse_compress(W, mask)
+        lin.append((f, torch.from_numpy(W).cuda(), torch.from_numpy(X).cuda(), W.shape))
+    for n in (16, 4096):
+        ys = [torch.empty((n, shp[0]), dtype=torch.float16, device="cuda") for (_, _, _, shp) in lin]
+        for (f, Wd, Xd, _), y in zip(lin, ys):
+            swm.spmm(f, Xd[:n], y)
+            swm.dense_gemm(Wd, Xd[:n], y)
+        torch.cuda.synchronize()
+        gs = G.capture([lambda f=f, Xd=Xd, y=y: swm.spmm(f, Xd[:n], y) for (f, _, Xd, _), y in zip(lin, ys)])
+        gd = G.capture([lambda Wd=Wd, Xd=Xd, y=y: swm.dense_gemm(Wd, Xd[:n], y) for (_, Wd, Xd, _), y in zip(lin, ys)])
+        ts, td = G.time(gs, 5), G.time(gd, 5)
+        out["detail"][str(n)] = {"sparse_us": ts * 1e3, "dense_us": td * 1e3, "speedup_vs_dense": td / ts,
+                                 "note": "no rotation: the compressed layer (228 MB) fits the 256 MB "
+                                         "Infinity Cache, the dense one (405 MB) does not"}
+    out["value"] = out["detail"]["16"]["sparse_us"]
     return out
 
 
@@ -162,20 +293,26 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="decode", choices=["decode"])
+    ap.add_argument("--workload", default="decode", choices=["decode", "spmspv", "prefill", "layer"])
+    ap.add_argument("--tau", type=float, default=0.3)
+    ap.add_argument("--prefill-n", default="512,2048,4096")
+    ap.add_argument("--prefill-s", default="0.5,0.6,0.7")
     ap.add_argument("--no-cpu", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              "(the product path has no multi-GPU code)", file=sys.stderr)
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported: the library "
+              "has no multi-GPU path (the sharding design is described in the docs)", file=sys.stderr)
         sys.exit(2)
     import torch
     import sparse_weight_matmul_amd as swm
     import swm_workloads as wl
     swm.load()
     torch.cuda.set_device(0)
-    out = bench_decode(args, torch, swm, wl)
-    print(json.dumps(out))
+    G = Graphs(torch)
+    fn = {"decode": bench_decode, "spmspv": bench_spmspv, "prefill": bench_prefill, "layer": bench_layer}
+    out = fn[args.workload](args, torch, swm, wl, G)
+    out.setdefault("n_gpus", 1)
+    print(json.dumps(out), flush=True)
 
 
 if __name__ == "__main__":

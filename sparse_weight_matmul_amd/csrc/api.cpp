@@ -308,7 +308,11 @@ static swm_status run_products(const swm_format* f, const void* X, int64_t ldx, 
     SWM_HIP(swm::launch_decode(f->d, f->plan, x, ldx, y, ldy, int(N), skip, s));
     return SWM_OK;
   }
-  // Large N: sixteen-token slices through the decode kernel.
+  if (!skip && swm::prefill_supported(f->h.k, ldx, X) && swm::prefill_sparse_lds(f->h) <= 160 * 1024) {
+    SWM_HIP(swm::launch_prefill_sparse(f->d, x, ldx, y, ldy, N, s));
+    return SWM_OK;
+  }
+  // Otherwise: sixteen-token slices through the decode kernel.
   for (int64_t n0 = 0; n0 < N; n0 += 16) {
     const int nn = int(std::min<int64_t>(16, N - n0));
     SWM_HIP(swm::launch_decode(f->d, f->plan, x + n0 * ldx, ldx, y + n0 * ldy, ldy, nn, skip, s));
@@ -335,6 +339,12 @@ swm_status swm_dense_gemm(const void* W, int64_t ldw, const void* X, int64_t ldx
   if (M > (int64_t(1) << 31) - 64 || K > (int64_t(1) << 31) - 64) return SWM_ERR_UNSUPPORTED;
   if (M == 0) return SWM_OK;
   hipStream_t s = static_cast<hipStream_t>(stream);
+  if (N > 16 && swm::prefill_supported(K, ldx, X) && ldw % 8 == 0 &&
+      (reinterpret_cast<uintptr_t>(W) & 15) == 0) {
+    SWM_HIP(swm::launch_prefill_dense(static_cast<const uint16_t*>(W), ldw, static_cast<const uint16_t*>(X),
+                                      ldx, static_cast<uint16_t*>(Y), ldy, M, K, N, s));
+    return SWM_OK;
+  }
   int dev = 0;
   SWM_HIP(hipGetDevice(&dev));
   const auto p = swm::plan_dense_small(M, K, int(std::min<int64_t>(N, 16)), num_cus(dev));

@@ -233,3 +233,42 @@ def test_error_codes(gpu_lib):
     assert lib.swm_dense_gemm(xp, 512, xp, 512, yp, 256, 256, 512, -1, s) == 1
     g = swm.sparse_compress(W, mask, tile=(128, 64))
     assert lib.swm_spmm(g._h, xp, 512, yp, 256, 8, s) == 8        # no kernel for tm=128
+
+
+# ------------------------------------------------------------------ prefill (N > 16)
+@pytest.mark.parametrize("M,K,N", [(256, 64, 256), (300, 512, 300), (1000, 1024, 257), (257, 4104, 513),
+                                   (64, 128, 17), (520, 200, 40)])
+def test_prefill_ragged(gpu_lib, M, K, N):
+    swm = gpu_lib
+    W, mask = wl.pruned_weight(96, M + K, M, K, 0.5)
+    X = np.random.default_rng(M * 3 + N).standard_normal((N, K)).astype(np.float16)
+    f = _compress(swm, W, mask)
+    ref = oracle.masked_matmul(W, mask, X)
+    assert_close(_np(swm.spmm(f, _t(X))), ref, f"prefill sparse {M}x{K}x{N}")
+    assert_close(_np(swm.dense_gemm(_t(W), _t(X))), ref, f"prefill dense {M}x{K}x{N}")
+
+
+def test_prefill_sparse_equals_dense_bitwise(gpu_lib):
+    """Same MFMA sequence on the same (exactly expanded) operands: identical bits."""
+    swm = gpu_lib
+    W, mask = wl.pruned_weight(97, 0, 512, 1024, 0.5)
+    X = np.random.default_rng(6).standard_normal((300, 1024)).astype(np.float16)
+    f = _compress(swm, W, mask)
+    a = _np(swm.spmm(f, _t(X))).view(np.uint16)
+    b = _np(swm.dense_gemm(_t(W), _t(X))).view(np.uint16)
+    assert np.array_equal(a, b)
+
+
+@pytest.mark.parametrize("s,N", [(0.5, 512), (0.5, 4096), (0.6, 2048), (0.7, 512)])
+def test_prefill_upgate_sampled_rows(gpu_lib, s, N):
+    swm = gpu_lib
+    W, mask, X = wl.prefill_upgate(s, N)
+    f = _compress(swm, W, mask)
+    Y = _np(swm.spmm(f, _t(X)))
+    rows = np.random.default_rng(int(s * 10) + N).choice(W.shape[0], 192, replace=False)
+    rows = np.concatenate([rows, [0, W.shape[0] - 1]])
+    ref = oracle.masked_matmul(W[rows], mask[rows], X)
+    assert_close(Y[:, rows], ref, f"up/gate s={s} N={N}")
+    if s == 0.5 and N == 512:
+        Yd = _np(swm.dense_gemm(_t(W), _t(X)))
+        assert np.array_equal(Yd.view(np.uint16), Y.view(np.uint16))
