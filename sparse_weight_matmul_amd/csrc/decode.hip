@@ -28,6 +28,8 @@
 //    The result is bitwise reproducible run to run.
 #include <hip/hip_runtime.h>
 
+#include <cstdlib>
+
 #include "kernels.h"
 
 namespace swm {
@@ -88,6 +90,16 @@ __device__ __forceinline__ half8 load_x8(const uint16_t* row, int64_t col, int64
   }
 }
 
+// How a split-K partial reaches the output.
+//  kRedFence : fp32 partial stores, device-scope fence, arrival counter; the
+//              last workgroup of a row block sums the partials (fences write
+//              back and invalidate the L2 of every XCD that executes them).
+//  kRedAtomic: partial stores and loads are device-coherent relaxed atomics
+//              (they bypass the non-coherent L2); the writer waits for its
+//              stores to complete before it bumps the arrival counter.
+//  kRedKernel: partials only; a second kernel sums them in split order.
+enum RedMode { kRedFence = 0, kRedAtomic = 1, kRedKernel = 2 };
+
 struct DecodeArgs {
   const uint32_t* tile_ptr;
   const uint64_t* bits;
@@ -100,13 +112,14 @@ struct DecodeArgs {
   int64_t ldx, ldy;
   int M, K, N, kt;
   int tpw, splits, buf_vals;
+  int red;  // RedMode
 };
 
 // Shared tail of the split-K decode kernels: reduce the waves' 64x16 fp32
-// accumulators in LDS, then either store fp16 Y (one split) or publish a
-// partial and let the last workgroup of the row block finish.
+// accumulators in LDS (fixed wave order), then either store fp16 Y (one
+// split) or publish a partial that is summed in fixed split order.
 // `red` must hold nwaves*16*64 floats; `flag` one word.
-__device__ __forceinline__ void reduce_and_store(float* red, uint32_t* flag, int nwaves, int wave,
+__device__ __forceinline__ void reduce_and_store(int kRed, float* red, uint32_t* flag, int nwaves, int wave,
                                                  int lane, const float (&accv)[16], int rowblk,
                                                  int split, int splits, int M, int N, uint16_t* Y,
                                                  int64_t ldy, float* partials, uint32_t* counters,
@@ -126,41 +139,83 @@ __device__ __forceinline__ void reduce_and_store(float* red, uint32_t* flag, int
   __syncthreads();
   const int m0 = rowblk * kTM;
   const int nout = N * 64;
+  float* mypart = partials + (size_t(rowblk) * splits + split) * 16 * 64;
   for (int e = threadIdx.x; e < nout; e += blockDim.x) {
     const int tok = e >> 6, row = e & 63;
     float sum = 0.f;
     for (int w = 0; w < nwaves; ++w) sum += red[(w * 16 + tok) * 64 + row];
     if (splits == 1) {
       if (m0 + row < M) Y[int64_t(tok) * ldy + m0 + row] = __builtin_bit_cast(uint16_t, _Float16(sum));
+    } else if (kRed == kRedAtomic) {
+      __hip_atomic_store(mypart + e, sum, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     } else {
-      partials[((size_t(rowblk) * splits + split) * 16 + tok) * 64 + row] = sum;
+      mypart[e] = sum;
     }
   }
-  if (splits == 1) return;
-  __threadfence();
+  if (splits == 1 || kRed == kRedKernel) return;
+  if (kRed == kRedFence) {
+    __threadfence();
+  } else {
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this thread's partial stores are done
+  }
   __syncthreads();
   if (threadIdx.x == 0) {
-    const uint32_t old = atomicAdd(&counters[rowblk], 1u);
+    const uint32_t old = __hip_atomic_fetch_add(&counters[rowblk], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     *flag = (old == uint32_t(splits - 1)) ? 1u : 0u;
   }
   __syncthreads();
   if (*flag == 0u) return;
-  __threadfence();
+  if (kRed == kRedFence) __threadfence();
+  const float* base = partials + size_t(rowblk) * splits * 16 * 64;
   for (int e = threadIdx.x; e < nout; e += blockDim.x) {
     const int tok = e >> 6, row = e & 63;
-    const float* p = partials + (size_t(rowblk) * splits * 16 + tok) * 64 + row;
     float sum = 0.f;
-    for (int q = 0; q < splits; ++q) sum += __builtin_nontemporal_load(p + size_t(q) * 16 * 64);
+    for (int q = 0; q < splits; ++q) {
+      const float* p = base + size_t(q) * 16 * 64 + e;
+      sum += (kRed == kRedAtomic) ? __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                                  : __builtin_nontemporal_load(p);
+    }
     if (m0 + row < M) Y[int64_t(tok) * ldy + m0 + row] = __builtin_bit_cast(uint16_t, _Float16(sum));
   }
-  if (threadIdx.x == 0) counters[rowblk] = 0u;  // ready for the next stream-ordered call
+  if (threadIdx.x == 0)
+    __hip_atomic_store(&counters[rowblk], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Sum split-K partials in split order and store fp16 Y (kRedKernel).
+// One thread per (row, token) output; partial layout [rowblk][split][16][64].
+__global__ __launch_bounds__(256) void reduce_partials_kernel(const float* __restrict__ partials,
+                                                              uint16_t* __restrict__ Y, int64_t ldy,
+                                                              int M, int N, int splits) {
+  const int rowblk = blockIdx.x;
+  const float* base = partials + size_t(rowblk) * splits * 16 * 64;
+  for (int e = threadIdx.x; e < N * 64; e += blockDim.x) {
+    const int tok = e >> 6, row = e & 63;
+    float sum = 0.f;
+    for (int q = 0; q < splits; ++q) sum += base[size_t(q) * 16 * 64 + e];
+    const int m = rowblk * kTM + row;
+    if (m < M) Y[int64_t(tok) * ldy + m] = __builtin_bit_cast(uint16_t, _Float16(sum));
+  }
+}
+
+typedef uint32_t u32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint64_t word_of(const u32x16& w, int e) {
+  return uint64_t(w[2 * e]) | (uint64_t(w[2 * e + 1]) << 32);
 }
 
 // One workgroup = `nwaves` waves on the same 64-row block; wave w decodes the
 // `tpw` consecutive 64x64 tiles starting at tile column (split*nwaves + w)*tpw.
+//
+// Per tile every global access has a fixed count so the compiler can keep
+// loads in flight across tiles: the run is fetched as kR 1 KiB chunks one tile
+// ahead (addresses clamped into the run, so chunks past its end re-read
+// cached bytes instead of branching), the next tile's bitmap words are touched
+// with a vector load to bring them into L2, bitmap words reach SGPRs one
+// 8-column group ahead (s_load_dwordx16), and B operands two groups ahead.
 // kSkip: input channels whose activation is zero in every token are not
-// decoded (their run is still streamed in this kernel).
-template <bool kSkip, bool kVec>
+// decoded (their run is still streamed).
+template <int kR, bool kSkip, bool kVec>
 __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   const int lane = lane_id();
@@ -169,13 +224,12 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   const int rowblk = int(blockIdx.x) / a.splits;
   const int split = int(blockIdx.x) - rowblk * a.splits;
 
-  // LDS: [0,16) zeros | flag (16 B) | nwaves run buffers; the reduction area
-  // reuses the run buffers after a barrier.
+  // LDS: [0,16) zeros | flag | nwaves run buffers (kR KiB each); the
+  // reduction area reuses the run buffers after a barrier.
   if (threadIdx.x < 8) reinterpret_cast<uint32_t*>(smem)[threadIdx.x] = 0u;
   __syncthreads();
   const uint32_t zero_addr = lds_addr(smem);
-  uint8_t* bufp = smem + 32 + size_t(wave) * a.buf_vals * 2;
-  const uint32_t buf = lds_addr(bufp);
+  const uint32_t buf = lds_addr(smem + 32 + size_t(wave) * kR * 1024);
 
   const int j0 = (split * nwaves + wave) * a.tpw;
   const int j1 = min(j0 + a.tpw, a.kt);
@@ -184,85 +238,108 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   const int q = lane >> 5, jj = lane & 31, tok = lane & 15;
   const bool xlane = ((jj >> 4) == q) && (tok < a.N);
   const uint16_t* xrow = xlane ? a.X + int64_t(tok) * a.ldx : a.zeros;
+  const int64_t kmax8 = a.K >= 8 ? a.K - 8 : 0;  // clamp for groups past K (their A is zero)
 
   f32x16 acc;
 #pragma unroll
   for (int v = 0; v < 16; ++v) acc[v] = 0.f;
+  uint32_t keep = 0;  // consumes the L2 prefetch so it is not removed
 
   if (j0 < j1) {
     const uint64_t tbase = uint64_t(rowblk) * a.kt;
-    u32x4 pre[kMaxChunks];
-    {
-      const uint32_t p0 = a.tile_ptr[tbase + j0], p1 = a.tile_ptr[tbase + j0 + 1];
-      const int nch = int((p1 - p0 + 511) >> 9);
-      const u32x4* src = reinterpret_cast<const u32x4*>(a.vals + p0) + lane;
+    auto load_run = [&](int j, u32x4 (&pre)[kR]) {
+      const uint32_t p0 = a.tile_ptr[tbase + j], p1 = a.tile_ptr[tbase + j + 1];
+      const uint32_t last = p1 > p0 + 8 ? p1 - 8 : p0;  // last 8-value slot of the run
 #pragma unroll
-      for (int c = 0; c < kMaxChunks; ++c)
-        if (c < nch) pre[c] = __builtin_nontemporal_load(src + c * 64);
-    }
+      for (int c = 0; c < kR; ++c) {
+        const uint32_t off = min(p0 + uint32_t(c * 512 + lane * 8), last);
+        pre[c] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(a.vals + off));
+      }
+    };
+    auto load_b = [&](int j, int g) -> half8 {
+      int64_t col = int64_t(j) * 64 + 8 * g;
+      if constexpr (kVec) {
+        col = col < a.K ? col : kmax8;
+        return __builtin_bit_cast(half8, *reinterpret_cast<const u32x4*>(xrow + col));
+      } else {
+        return load_x8<false>(xrow, col, a.K);
+      }
+    };
+    auto load_words = [&](int j, int g) -> u32x16 {
+      return *reinterpret_cast<const u32x16*>(a.bits + (tbase + j) * 64 + 8 * g);
+    };
+
+    u32x4 pre[kR];
+    load_run(j0, pre);
+    half8 bop[8];
+    bop[0] = load_b(j0, 0);
+    bop[1] = load_b(j0, 1);
+    u32x16 wslot[2];
+    wslot[0] = load_words(j0, 0);
+
     for (int j = j0; j < j1; ++j) {
+      const int jn = min(j + 1, j1 - 1);
       const uint64_t t = tbase + j;
-      const uint32_t p0 = a.tile_ptr[t], p1 = a.tile_ptr[t + 1];
-      const int nch = int((p1 - p0 + 511) >> 9);
+      // Stage this tile's run, then fetch the next tile's run behind it.
 #pragma unroll
-      for (int c = 0; c < kMaxChunks; ++c)
-        if (c < nch) *reinterpret_cast<lds_u32x4*>(static_cast<uintptr_t>(buf + c * 1024 + lane * 16)) = pre[c];
+      for (int c = 0; c < kR; ++c)
+        *reinterpret_cast<lds_u32x4*>(static_cast<uintptr_t>(buf + c * 1024 + lane * 16)) = pre[c];
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_wave_barrier();
-      if (j + 1 < j1) {
-        const uint32_t n0 = p1, n1 = a.tile_ptr[t + 2];
-        const int nn = int((n1 - n0 + 511) >> 9);
-        const u32x4* src = reinterpret_cast<const u32x4*>(a.vals + n0) + lane;
-#pragma unroll
-        for (int c = 0; c < kMaxChunks; ++c)
-          if (c < nn) pre[c] = __builtin_nontemporal_load(src + c * 64);
+      load_run(jn, pre);
+      {
+        const u32x2 w = *reinterpret_cast<const u32x2*>(a.bits + (tbase + jn) * 64 + lane);
+        keep ^= w[0] ^ w[1];
       }
-      const int64_t col0 = int64_t(j) * 64;
-      half8 bop[8];
-#pragma unroll
-      for (int g = 0; g < 8; ++g) bop[g] = load_x8<kVec>(xrow, col0 + 8 * g, a.K);
-
       uint64_t active = ~0ull;
       if constexpr (kSkip) {
         bool nz = false;
-        const int64_t col = col0 + lane;
+        const int64_t col = int64_t(j) * 64 + lane;
         if (col < a.K)
           for (int n = 0; n < a.N; ++n) nz |= (a.X[int64_t(n) * a.ldx + col] & 0x7FFFu) != 0;
         active = __ballot(nz);
       }
-
-      const uint64_t* tb = a.bits + t * 64;
+      (void)t;
       uint32_t base = buf;
 #pragma unroll
       for (int g = 0; g < 8; ++g) {
-        if (col0 + 8 * g >= a.K) break;  // whole group beyond K (K % 8 == 0 on the vector path)
-        half8 aop;
+        // This group's words (scalar popcounts force their wait first), then
+        // the lookahead: words one group ahead, B operands two groups ahead.
+        const u32x16 wv = wslot[g & 1];
+        uint32_t pc[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) pc[e] = 2u * uint32_t(__builtin_popcountll(word_of(wv, e)));
+        __builtin_amdgcn_sched_barrier(0);
+        wslot[(g + 1) & 1] = (g < 7) ? load_words(j, g + 1) : load_words(jn, 0);
+        bop[(g + 2) & 7] = (g < 6) ? load_b(j, g + 2) : load_b(jn, g - 6);
+        __builtin_amdgcn_sched_barrier(0);  // keep both loads ahead of this group's decode
         if constexpr (kSkip) {
           if (((active >> (8 * g)) & 0xFFull) == 0) {
 #pragma unroll
-            for (int e = 0; e < 8; ++e) base += 2u * uint32_t(__builtin_popcountll(tb[8 * g + e]));
+            for (int e = 0; e < 8; ++e) base += pc[e];
             continue;
           }
         }
+        half8 aop;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          const uint64_t w = tb[8 * g + e];
-          const uint32_t ad = run_addr(w, base, zero_addr);
-          base += 2u * uint32_t(__builtin_popcountll(w));
+          const uint32_t ad = run_addr(word_of(wv, e), base, zero_addr);
+          base += pc[e];
           aop[e] = lds_half(ad);
         }
         acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(aop, bop[g], acc, 0, 0, 0);
       }
     }
   }
+  if (keep == 0x9E3779B9u && a.N < 0) a.Y[0] = 0;  // never true: keeps the prefetch alive
 
   __syncthreads();  // all run buffers are free: reuse them as the reduction area
   float accv[16];
 #pragma unroll
   for (int v = 0; v < 16; ++v) accv[v] = acc[v];
-  reduce_and_store(reinterpret_cast<float*>(smem + 32), reinterpret_cast<uint32_t*>(smem + 16),
+  reduce_and_store(a.red, reinterpret_cast<float*>(smem + 32), reinterpret_cast<uint32_t*>(smem + 16),
                    nwaves, wave, lane, accv, rowblk, split, a.splits, a.M, a.N, a.Y, a.ldy,
-                   a.partials, a.counters, true);
+                         a.partials, a.counters, true);
 }
 
 // ------------------------------------------------------------------ dense, N <= 16
@@ -275,13 +352,15 @@ struct DenseArgs {
   uint32_t* counters;
   int64_t ldw, ldx, ldy, M, K;
   int N, kchunk, splits;
+  int red;  // RedMode
 };
 
 // One workgroup = nwaves waves on one 64-row block, wave w covers columns
-// [(split*nwaves + w)*kchunk, +kchunk).  Per 32 columns: four
-// v_mfma_f32_16x16x32_f16 (16 rows each); lane l loads W[row][k0 + 8(l/16) ..+7]
-// and X[l%16][k0 + 8(l/16) ..+7], 16 B each.  Next step's loads are issued
-// before the current step's products.
+// [(split*nwaves + w)*kchunk, +kchunk) (kchunk a multiple of 128).  Per 32
+// columns: four v_mfma_f32_16x16x32_f16 (16 rows each); lane l loads
+// W[row][k0 + 8(l/16) .. +7] and X[l%16][k0 + 8(l/16) .. +7], 16 B each.
+// Loads run three 32-column steps ahead through a four-slot register ring.
+// Addresses past the chunk or past K point at the zero row instead.
 template <bool kVec>
 __global__ __launch_bounds__(256) void dense_small_kernel(DenseArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
@@ -304,35 +383,46 @@ __global__ __launch_bounds__(256) void dense_small_kernel(DenseArgs a) {
     for (int v = 0; v < 4; ++v) acc[r][v] = 0.f;
 
   const uint16_t* wrow[4];
-  bool rok[4];
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const int64_t row = m0 + r * 16 + (lane & 15);
-    rok[r] = row < a.M;
-    wrow[r] = rok[r] ? a.W + row * a.ldw : a.zeros;
+    wrow[r] = row < a.M ? a.W + row * a.ldw : a.zeros;
   }
 
-  auto loadA = [&](int64_t k0, half8 (&A)[4], half8& B) {
-    const int64_t k = k0 + koff;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) A[r] = load_x8<kVec>(wrow[r], k, ke);
-    B = load_x8<kVec>(xrow, k, ke);
-  };
   if (kb < ke) {
-    half8 A0[4], B0, A1[4], B1;
-    loadA(kb, A0, B0);
-    int64_t k0 = kb;
-    for (; k0 + 32 < ke; k0 += 64) {
-      loadA(k0 + 32, A1, B1);
+    if constexpr (kVec) {
+      const int nsteps = int((ke - kb + 31) / 32);
+      half8 A[4][4], B[4];
+      auto issue = [&](int s, int slot) {
+        const int64_t k = kb + int64_t(s) * 32 + koff;
+        const bool ok = k < ke;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) acc[r] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A0[r], B0, acc[r], 0, 0, 0);
-      if (k0 + 64 < ke) loadA(k0 + 64, A0, B0);
+        for (int r = 0; r < 4; ++r)
+          A[slot][r] = __builtin_bit_cast(half8, *reinterpret_cast<const u32x4*>((ok ? wrow[r] : a.zeros) + (ok ? k : 0)));
+        B[slot] = __builtin_bit_cast(half8, *reinterpret_cast<const u32x4*>((ok ? xrow : a.zeros) + (ok ? k : 0)));
+      };
+      issue(0, 0);
+      issue(1, 1);
+      issue(2, 2);
+      for (int s0 = 0; s0 < nsteps; s0 += 4) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) acc[r] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A1[r], B1, acc[r], 0, 0, 0);
-    }
-    if (k0 < ke) {
+        for (int u = 0; u < 4; ++u) {
+          issue(s0 + u + 3, (u + 3) & 3);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) acc[r] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A0[r], B0, acc[r], 0, 0, 0);
+          for (int r = 0; r < 4; ++r)
+            acc[r] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[u][r], B[u], acc[r], 0, 0, 0);
+        }
+      }
+    } else {
+      for (int64_t k0 = kb; k0 < ke; k0 += 32) {
+        const int64_t k = k0 + koff;
+        half8 A0[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) A0[r] = load_x8<false>(wrow[r], k, ke);
+        const half8 B0 = load_x8<false>(xrow, k, ke);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[r] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A0[r], B0, acc[r], 0, 0, 0);
+      }
     }
   }
   float accv[16];
@@ -340,9 +430,9 @@ __global__ __launch_bounds__(256) void dense_small_kernel(DenseArgs a) {
   for (int r = 0; r < 4; ++r)
 #pragma unroll
     for (int v = 0; v < 4; ++v) accv[r * 4 + v] = acc[r][v];
-  reduce_and_store(reinterpret_cast<float*>(smem + 32), reinterpret_cast<uint32_t*>(smem + 16),
+  reduce_and_store(a.red, reinterpret_cast<float*>(smem + 32), reinterpret_cast<uint32_t*>(smem + 16),
                    nwaves, wave, lane, accv, rowblk, split, a.splits, int(a.M), a.N, a.Y, a.ldy,
-                   a.partials, a.counters, false);
+                         a.partials, a.counters, false);
 }
 
 // ------------------------------------------------------------------ decompress
@@ -414,6 +504,34 @@ size_t decode_partial_floats(const Header& h, const DecodePlan& p) {
   return p.splits > 1 ? size_t(h.mt) * p.splits * 16 * 64 : 0;
 }
 
+namespace {
+
+template <int kR>
+void launch_decode_r(bool skip, bool vec, dim3 grid, dim3 block, size_t lds, hipStream_t s,
+                     const DecodeArgs& a) {
+  if (skip) {
+    if (vec) hipLaunchKernelGGL((decode_kernel<kR, true, true>), grid, block, lds, s, a);
+    else hipLaunchKernelGGL((decode_kernel<8, true, false>), grid, block, lds, s, a);
+  } else {
+    if (vec) hipLaunchKernelGGL((decode_kernel<kR, false, true>), grid, block, lds, s, a);
+    else hipLaunchKernelGGL((decode_kernel<8, false, false>), grid, block, lds, s, a);
+  }
+}
+
+}  // namespace
+
+int reduce_mode_default() {
+  static int mode = -1;
+  if (mode < 0) {
+    const char* e = getenv("SWM_SPLITK_REDUCE");
+    mode = kRedKernel;
+    if (e && e[0] == 'f') mode = kRedFence;
+    if (e && e[0] == 'a') mode = kRedAtomic;
+    if (e && e[0] == 'k') mode = kRedKernel;
+  }
+  return mode;
+}
+
 hipError_t launch_decode(const DevFormat& f, const DecodePlan& p, const uint16_t* X, int64_t ldx,
                          uint16_t* Y, int64_t ldy, int n, bool skip, hipStream_t s) {
   DecodeArgs a;
@@ -433,23 +551,39 @@ hipError_t launch_decode(const DevFormat& f, const DecodePlan& p, const uint16_t
   a.kt = int(f.h.kt);
   a.tpw = p.tiles_per_wave;
   a.splits = p.splits;
-  // Runs are copied to LDS in 1 KiB (512-value) chunks: round the per-wave buffer up.
-  a.buf_vals = int((f.h.max_tile + 511) / 512 * 512);
+  a.red = reduce_mode_default();
   if (f.h.max_tile > 64u * 64u) return hipErrorInvalidValue;  // a 64x64 tile holds at most 4096 values
-  size_t run_bytes = size_t(p.waves) * a.buf_vals * 2;
-  size_t red_bytes = size_t(p.waves) * 16 * 64 * 4;
-  size_t lds = 32 + (run_bytes > red_bytes ? run_bytes : red_bytes);
+  // Runs are staged to LDS as kR 1 KiB (512-value) chunks per wave.
+  const int need = int((f.h.max_tile + 511) / 512);
   const bool vec = (f.h.k % 8 == 0) && (ldx % 8 == 0) && ((reinterpret_cast<uintptr_t>(X) & 15) == 0);
+  int kR = 8;
+  if (vec) {
+    const int opts[] = {2, 3, 4, 5, 6, 8};
+    for (int o : opts)
+      if (o >= need) { kR = o; break; }
+  }
+  a.buf_vals = kR * 512;
+  const size_t run_bytes = size_t(p.waves) * kR * 1024;
+  const size_t red_bytes = size_t(p.waves) * 16 * 64 * 4;
+  const size_t lds = 32 + (run_bytes > red_bytes ? run_bytes : red_bytes);
   if (f.h.mt == 0) return hipSuccess;
   dim3 grid(unsigned(int64_t(f.h.mt) * p.splits)), block(unsigned(p.waves * 64));
-  if (skip) {
-    if (vec) hipLaunchKernelGGL((decode_kernel<true, true>), grid, block, lds, s, a);
-    else hipLaunchKernelGGL((decode_kernel<true, false>), grid, block, lds, s, a);
-  } else {
-    if (vec) hipLaunchKernelGGL((decode_kernel<false, true>), grid, block, lds, s, a);
-    else hipLaunchKernelGGL((decode_kernel<false, false>), grid, block, lds, s, a);
+  switch (kR) {
+    case 2: launch_decode_r<2>(skip, vec, grid, block, lds, s, a); break;
+    case 3: launch_decode_r<3>(skip, vec, grid, block, lds, s, a); break;
+    case 4: launch_decode_r<4>(skip, vec, grid, block, lds, s, a); break;
+    case 5: launch_decode_r<5>(skip, vec, grid, block, lds, s, a); break;
+    case 6: launch_decode_r<6>(skip, vec, grid, block, lds, s, a); break;
+    default: launch_decode_r<8>(skip, vec, grid, block, lds, s, a); break;
   }
-  return hipGetLastError();
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (p.splits > 1 && a.red == kRedKernel) {
+    hipLaunchKernelGGL(reduce_partials_kernel, dim3(unsigned(f.h.mt)), dim3(256), 0, s, a.partials, Y, ldy,
+                       a.M, n, p.splits);
+    e = hipGetLastError();
+  }
+  return e;
 }
 
 DensePlan plan_dense_small(int64_t M, int64_t K, int n, int num_cus) {
@@ -461,7 +595,7 @@ DensePlan plan_dense_small(int64_t M, int64_t K, int n, int num_cus) {
   const int64_t want_waves = int64_t(num_cus) * 8;
   int64_t chunks = (want_waves + mt - 1) / mt;  // K chunks per row block
   int64_t kchunk = (K + chunks - 1) / chunks;
-  kchunk = (kchunk + 63) / 64 * 64;
+  kchunk = (kchunk + 127) / 128 * 128;
   if (kchunk < 256) kchunk = 256;
   p.kchunk = int(kchunk);
   p.splits = int((K + p.waves * kchunk - 1) / (p.waves * kchunk));
@@ -492,6 +626,7 @@ hipError_t launch_dense_small(const DensePlan& p, const uint16_t* W, int64_t ldw
   a.N = n;
   a.kchunk = p.kchunk;
   a.splits = p.splits;
+  a.red = reduce_mode_default();
   const bool vec = (K % 8 == 0) && (ldx % 8 == 0) && (ldw % 8 == 0) &&
                    ((reinterpret_cast<uintptr_t>(X) & 15) == 0) &&
                    ((reinterpret_cast<uintptr_t>(W) & 15) == 0);
@@ -501,7 +636,14 @@ hipError_t launch_dense_small(const DensePlan& p, const uint16_t* W, int64_t ldw
   size_t lds = 32 + size_t(p.waves) * 16 * 64 * 4;
   if (vec) hipLaunchKernelGGL((dense_small_kernel<true>), grid, block, lds, s, a);
   else hipLaunchKernelGGL((dense_small_kernel<false>), grid, block, lds, s, a);
-  return hipGetLastError();
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (p.splits > 1 && a.red == kRedKernel) {
+    hipLaunchKernelGGL(reduce_partials_kernel, dim3(unsigned(mt)), dim3(256), 0, s, partials, Y, ldy,
+                       int(M), n, p.splits);
+    e = hipGetLastError();
+  }
+  return e;
 }
 
 hipError_t launch_decompress(const DevFormat& f, uint16_t* W, int64_t ldw, hipStream_t s) {
