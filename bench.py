@@ -172,7 +172,7 @@ def bench_decode(args, torch, swm, wl, G):
         "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "f16", "data": "synthetic (seeded N(0,1) fp16 W and X, 50% per-row magnitude pruning)",
         "config": {"workload": "decode q_proj 4096x4096, 50% unstructured, N in {1,8,16} per step",
-                   "format": "SWM-TCB v1 tm=64 tk=64", "format_bytes": fb, "rotating_copies": C},
+                   "format": "SWM-TCB v2 tm=16 tk=64", "format_bytes": fb, "rotating_copies": C},
         "speedup_vs_dense": ms_dense / ms_total,
         "dense_ms_per_step": ms_dense / args.steps,
         "detail": detail,

@@ -66,8 +66,8 @@ typedef enum swm_status {
 /* Opaque compressed-weight handle (owns all of its device memory). */
 typedef struct swm_format swm_format;
 
-/* Tile shape.  tm: rows per tile, a multiple of 64 (kernels: 64).  tk: columns
- * per tile, a multiple of 8 (kernels: 64, 128 or 256).  NULL = {64, 64}. */
+/* Tile shape.  tm: rows per tile, must be 16.  tk: columns per tile, a
+ * multiple of 32 (the product kernels take 64).  NULL = {16, 64}. */
 typedef struct swm_tile_cfg {
   int32_t tm;
   int32_t tk;
@@ -87,16 +87,19 @@ typedef struct swm_format_info {
 
 /* ------------------------------------------------------------------ format */
 
-/* sparse_compress: build the tiled column-bitmap format (SWM-TCB v1) from a
+/* sparse_compress: build the tiled column-bitmap format (SWM-TCB v2) from a
  * dense fp16 W and an optional mask, and upload it to the current device.
  * Source: SPDP abstract (Tiled-CBC format, unstructured static pruning) and
  * the moderate-sparsity page, Sec. 2.1 (pattern precomputed offline).
  *  W, mask: HOST pointers.  mask is uint8 M x K (ldm >= K), nonzero = keep;
  *  NULL keeps every entry whose value is not +0/-0.  Kept entries are stored
  *  with their exact bits (also a kept +-0); pruned entries decode to +0.
- *  Layout: tiles of tm x tk, per tile column one tm-bit bitmap, kept values
- *  packed column-major within the tile, each tile run padded to 8 values,
- *  uint32 exclusive prefix of run lengths.
+ *  Layout: tiles of 16 x tk; every tile column has a 16-bit bitmap and the
+ *  bitmaps are stored four to a 64-bit word: word w = 8s + e of a tile holds
+ *  in bits 16q..16q+15 the bitmap of tile column 32s + 8q + e, so bit b is
+ *  (row b%16, column 32s + 8(b/16) + e).  Kept values are packed word by word,
+ *  bit by bit (column by column), each tile run padded to 8 values; uint32
+ *  exclusive prefix of run lengths per tile.
  *  Synchronous: returns after the upload on `stream` has completed.
  *  *out receives a new handle owned by the caller (swm_format_destroy). */
 swm_status swm_sparse_compress(const uint16_t* W, int64_t ldw, const uint8_t* mask, int64_t ldm,
@@ -111,8 +114,8 @@ swm_status swm_encode_blob(const uint16_t* W, int64_t ldw, const uint8_t* mask, 
                            size_t* size);
 
 /* Export the handle as a little-endian blob: 64-byte header ("SWMT", version
- * 1, M, K, tm, tk, nnz, padded_len, mt, kt, max_tile, 0) || tile_ptr (uint32,
- * mt*kt+1) || bits (uint64, mt*kt*tk*tm/64) || values (uint16, padded_len).
+ * 2, M, K, tm, tk, nnz, padded_len, mt, kt, max_tile, 0) || tile_ptr (uint32,
+ * mt*kt+1) || bits (uint64, mt*kt*tk/4) || values (uint16, padded_len).
  * buf NULL = size query. */
 swm_status swm_format_export(const swm_format* f, void* buf, size_t cap, size_t* size);
 
@@ -169,6 +172,17 @@ swm_status swm_spmspv(const swm_format* f, const void* x, int64_t ldx, void* y, 
  * shape). */
 swm_status swm_dense_gemm(const void* W, int64_t ldw, const void* X, int64_t ldx, void* Y,
                           int64_t ldy, int64_t M, int64_t K, int64_t N, void* stream);
+
+/* ------------------------------------------------------------------ measurement */
+
+/* hbm_stream: read `bytes` (a multiple of 16) from the device buffer `buf` with
+ * `blocks` workgroups of 256 threads, each lane keeping `unroll` (1, 2, 4, 8 or
+ * 16) 16-byte loads in flight, and fold them into out[] (device, blocks*4
+ * uint32, overwritten).  A calibration kernel: it gives the read bandwidth the
+ * memory system reaches for a given byte count and launch shape, the
+ * "achievable" reference next to the 8 TB/s peak.  Asynchronous. */
+swm_status swm_hbm_stream(const void* buf, size_t bytes, int32_t unroll, int32_t blocks,
+                          uint32_t* out, void* stream);
 
 /* ------------------------------------------------------------------ misc */
 

@@ -58,6 +58,7 @@ SIGNATURES = {
     "swm_spmm": (_i32, [_vp, _vp, _i64, _vp, _i64, _i64, _vp]),
     "swm_spmspv": (_i32, [_vp, _vp, _i64, _vp, _i64, _i32, _vp]),
     "swm_dense_gemm": (_i32, [_vp, _i64, _vp, _i64, _vp, _i64, _i64, _i64, _i64, _vp]),
+    "swm_hbm_stream": (_i32, [_vp, _sz, _i32, _i32, _vp, _vp]),
     "swm_status_str": (ctypes.c_char_p, [_i32]),
     "swm_last_hip_error": (_i32, []),
     "swm_version": (_i32, []),
@@ -182,7 +183,7 @@ class Format:
             pass
 
 
-def sparse_compress(W, mask=None, tile=(64, 64), stream=None) -> Format:
+def sparse_compress(W, mask=None, tile=(16, 64), stream=None) -> Format:
     """Compress a host fp16 W (M, K) with an optional host mask; upload to the current device."""
     lib = load()
     w = _host_u16(W)
@@ -195,7 +196,7 @@ def sparse_compress(W, mask=None, tile=(64, 64), stream=None) -> Format:
     return Format(h)
 
 
-def encode_blob(W, mask=None, tile=(64, 64)) -> bytes:
+def encode_blob(W, mask=None, tile=(16, 64)) -> bytes:
     """Host-only encoder: the export blob of compress(W, mask) without any GPU."""
     lib = load()
     w = _host_u16(W)
@@ -225,14 +226,14 @@ def format_import(blob: bytes, stream=None) -> Format:
     return Format(h)
 
 
-def size_dry_run(M: int, K: int, nnz: int, tile=(64, 64)) -> dict:
+def size_dry_run(M: int, K: int, nnz: int, tile=(16, 64)) -> dict:
     lib = load()
     inf = FormatInfo()
     _check(lib.swm_size_dry_run(M, K, nnz, _cfg(tile), ctypes.byref(inf)), "swm_size_dry_run")
     return inf.as_dict()
 
 
-def size_dry_run_status(M: int, K: int, nnz: int, tile=(64, 64)) -> int:
+def size_dry_run_status(M: int, K: int, nnz: int, tile=(16, 64)) -> int:
     lib = load()
     inf = FormatInfo()
     return int(lib.swm_size_dry_run(M, K, nnz, _cfg(tile), ctypes.byref(inf)))
@@ -289,6 +290,18 @@ def decompress(fmt: Format, W=None, stream=None):
     wp, ldw = _dev2d(W, "W", rows=fmt.M, cols=fmt.K)
     _check(lib.swm_decompress(fmt._h, wp, ldw, _stream_ptr(stream)), "swm_decompress")
     return W
+
+
+def hbm_stream(buf, unroll: int, blocks: int, out=None, stream=None):
+    """Calibration read of a whole CUDA tensor `buf` (bytes a multiple of 16)."""
+    import torch
+    lib = load()
+    if out is None:
+        out = torch.empty(blocks * 4, dtype=torch.int32, device=buf.device)
+    nbytes = buf.numel() * buf.element_size()
+    _check(lib.swm_hbm_stream(ctypes.c_void_p(buf.data_ptr()), nbytes, unroll, blocks,
+                              ctypes.c_void_p(out.data_ptr()), _stream_ptr(stream)), "swm_hbm_stream")
+    return out
 
 
 def status_str(code: int) -> str:

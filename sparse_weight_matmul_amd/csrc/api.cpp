@@ -111,7 +111,8 @@ swm_status upload(std::vector<uint8_t>&& blob, const swm::Header& h, hipStream_t
     delete f;
     return hip_fail(hipErrorNoDevice);
   }
-  f->plan = swm::plan_decode(h, 16, num_cus(f->device));
+  f->plan = swm::plan_decode(h, reinterpret_cast<const uint32_t*>(f->blob.data() + h.off_tile_ptr()),
+                             num_cus(f->device));
   const size_t T = h.tiles();
   const size_t b_tp = 4 * (T + 1), b_bits = 8 * h.n_bits(), b_vals = 2 * h.padded_len + 1024;
   const size_t n_zero = size_t(h.kt) * h.tk + 64;
@@ -159,7 +160,7 @@ swm_status upload(std::vector<uint8_t>&& blob, const swm::Header& h, hipStream_t
 }
 
 swm_status check_tile_supported(const swm::Header& h) {
-  if (h.tm != 64 || h.tk != 64) return SWM_ERR_UNSUPPORTED;
+  if (h.tm != 16 || h.tk != 64) return SWM_ERR_UNSUPPORTED;
   if (h.m > (int64_t(1) << 31) - 64 || h.k > (int64_t(1) << 31) - 64) return SWM_ERR_UNSUPPORTED;
   return SWM_OK;
 }
@@ -329,6 +330,14 @@ swm_status swm_spmspv(const swm_format* f, const void* x, int64_t ldx, void* y, 
                       int32_t n, void* stream) {
   if (n < 1 || n > 16) return SWM_ERR_INVALID_ARG;
   return run_products(f, x, ldx, y, ldy, n, true, static_cast<hipStream_t>(stream));
+}
+
+swm_status swm_hbm_stream(const void* buf, size_t bytes, int32_t unroll, int32_t blocks,
+                          uint32_t* out, void* stream) {
+  if (!buf || !out || bytes % 16 || blocks <= 0) return SWM_ERR_INVALID_ARG;
+  if (unroll != 1 && unroll != 2 && unroll != 4 && unroll != 8 && unroll != 16) return SWM_ERR_INVALID_ARG;
+  SWM_HIP(swm::launch_stream(buf, bytes, unroll, blocks, out, static_cast<hipStream_t>(stream)));
+  return SWM_OK;
 }
 
 swm_status swm_dense_gemm(const void* W, int64_t ldw, const void* X, int64_t ldx, void* Y,

@@ -1,4 +1,4 @@
-// Host side of the SWM-TCB v1 tiled column-bitmap format: encoder, blob
+// Host side of the SWM-TCB v2 tiled column-bitmap format: encoder, blob
 // header, validator and size accounting.
 //
 // The format is this library's reading of the "Tiled-Column-wise Bitmap
@@ -7,15 +7,19 @@
 // position metadata per entry keeps metadata small at ~50% sparsity, the goal
 // set in "Accelerating GPU inference of LLMs with moderately unstructured
 // sparse weight matrices", Sec. 3.1 (and Challenge 2 of its Sec. 1, where
-// per-nonzero indices cost as much as the values).  Values are packed column
-// by column inside a tile so that one input channel's weights are one
-// contiguous run: the unit that zero-activation skipping drops.
+// per-nonzero indices cost as much as the values).
 //
-// Layout (tile t = i*kt + j covers rows [i*tm, i*tm+tm), cols [j*tk, j*tk+tk)):
-//   bits[(t*tk + c)*(tm/64) + w], bit b  <=> row i*tm + 64w + b, col j*tk + c kept
-//   values: kept fp16 bits of tile t ordered by c, then w, then b; each tile
-//           run zero-padded to a multiple of 8 values
-//   tile_ptr[t] = exclusive prefix of padded run lengths (uint32)
+// Layout (TM = 16; tile t = i*kt + j covers rows [16i, 16i+16) and columns
+// [tk*j, tk*j + tk), tk a multiple of 32):
+//   a tile has tk/32 steps of 32 columns, each step eight 64-bit words; word
+//   w = 8*s + e carries in bits 16q..16q+15 the 16-row bitmap of tile column
+//   32*s + 8*q + e, i.e. bit b <=> (row 16i + b%16, column tk*j + 32s + 8(b/16) + e);
+//   values: kept fp16 bits word by word, bit by bit (column by column, rows
+//   ascending), each tile run zero-padded to a multiple of 8 values;
+//   tile_ptr[t] = exclusive prefix of padded run lengths (uint32).
+// This bit order puts, for lane b of a 64-wide wave, row b%16 and column
+// group b/16 in the same place as the A operand of a 16x16x32 matrix-core
+// product, so a decoded word feeds the matrix cores without reshuffling.
 // Pattern computation is offline: the moderate-sparsity page, Sec. 2.1.
 #include <algorithm>
 #include <cstring>
@@ -42,6 +46,12 @@ inline bool keep_entry(const uint16_t* W, int64_t ldw, const uint8_t* mask, int6
                        int64_t c) {
   if (mask) return mask[r * ldm + c] != 0;
   return (W[r * ldw + c] & 0x7FFFu) != 0;  // null mask: keep values other than +-0
+}
+
+// Row and column (inside the tile) of bit b of word w.
+inline void bit_pos(uint32_t w, uint32_t b, uint32_t* row, uint32_t* col) {
+  *row = b & 15u;
+  *col = 32u * (w >> 3) + 8u * (b >> 4) + (w & 7u);
 }
 
 }  // namespace
@@ -79,8 +89,7 @@ swm_status read_header(const void* buf, size_t size, Header* h) {
   r.kt = get<uint32_t>(b, 52);
   r.max_tile = get<uint32_t>(b, 56);
   if (get<uint32_t>(b, 60) != 0) return SWM_ERR_FORMAT;
-  if (r.m < 0 || r.k < 0 || r.tm == 0 || r.tm % 64 || r.tk == 0 || r.tk % 8) return SWM_ERR_FORMAT;
-  if (r.tm > 4096 || r.tk > 4096) return SWM_ERR_FORMAT;
+  if (r.m < 0 || r.k < 0 || r.tm != kTM || r.tk == 0 || r.tk % 32 || r.tk > 4096) return SWM_ERR_FORMAT;
   if (uint64_t(r.mt) != (uint64_t(r.m) + r.tm - 1) / r.tm) return SWM_ERR_FORMAT;
   if (uint64_t(r.kt) != (uint64_t(r.k) + r.tk - 1) / r.tk) return SWM_ERR_FORMAT;
   if (r.padded_len >= (uint64_t(1) << 32)) return SWM_ERR_FORMAT;
@@ -92,9 +101,9 @@ swm_status read_header(const void* buf, size_t size, Header* h) {
 }
 
 swm_status plan_grid(int64_t M, int64_t K, const swm_tile_cfg* cfg, Header* h) {
-  int32_t tm = cfg ? cfg->tm : 64, tk = cfg ? cfg->tk : 64;
+  int32_t tm = cfg ? cfg->tm : int32_t(kTM), tk = cfg ? cfg->tk : 64;
   if (M < 0 || K < 0) return SWM_ERR_INVALID_ARG;
-  if (tm <= 0 || tm % 64 || tm > 4096 || tk <= 0 || tk % 8 || tk > 4096) return SWM_ERR_INVALID_ARG;
+  if (tm != int32_t(kTM) || tk <= 0 || tk % 32 || tk > 4096) return SWM_ERR_INVALID_ARG;
   const int64_t lim = int64_t(1) << 40;
   if (M > lim || K > lim) return SWM_ERR_OVERFLOW;
   Header r;
@@ -107,7 +116,7 @@ swm_status plan_grid(int64_t M, int64_t K, const swm_tile_cfg* cfg, Header* h) {
     return SWM_ERR_OVERFLOW;
   r.mt = uint32_t(mt);
   r.kt = uint32_t(kt);
-  if (r.tiles() > (uint64_t(1) << 40) / (uint64_t(tk) * (tm / 64))) return SWM_ERR_OVERFLOW;
+  if (r.tiles() > (uint64_t(1) << 40) / r.words_per_tile()) return SWM_ERR_OVERFLOW;
   *h = r;
   return SWM_OK;
 }
@@ -120,7 +129,7 @@ swm_status encode_blob(const uint16_t* W, int64_t ldw, const uint8_t* mask, int6
   Header h;
   swm_status st = plan_grid(M, K, cfg, &h);
   if (st != SWM_OK) return st;
-  const uint32_t tm = h.tm, tk = h.tk, wpc = tm / 64;
+  const uint32_t tm = h.tm, tk = h.tk, nw = uint32_t(h.words_per_tile());
   const uint64_t T = h.tiles();
 
   // Pass 1: kept entries per tile -> padded run lengths -> tile_ptr.
@@ -153,7 +162,8 @@ swm_status encode_blob(const uint16_t* W, int64_t ldw, const uint8_t* mask, int6
   uint8_t* bits = blob + h.off_bits();
   uint8_t* vals = blob + h.off_values();
 
-  // Pass 2: per tile, transpose into a local column-major buffer, then emit.
+  // Pass 2: per tile, copy into a local (row, column) buffer, then emit words
+  // and values in storage order.
   std::vector<uint16_t> tv(size_t(tm) * tk);
   std::vector<uint8_t> tkp(size_t(tm) * tk);
   uint64_t pos = 0;
@@ -166,23 +176,23 @@ swm_status encode_blob(const uint16_t* W, int64_t ldw, const uint8_t* mask, int6
       const int64_t r1 = std::min<int64_t>(r0 + tm, M), c1 = std::min<int64_t>(c0 + tk, K);
       for (int64_t r = r0; r < r1; ++r)
         for (int64_t c = c0; c < c1; ++c) {
-          const size_t li = size_t(c - c0) * tm + size_t(r - r0);
+          const size_t li = size_t(r - r0) * tk + size_t(c - c0);
           tkp[li] = keep_entry(W, ldw, mask, ldm, r, c) ? 1 : 0;
           tv[li] = W[r * ldw + c];
         }
-      for (uint32_t c = 0; c < tk; ++c) {
-        for (uint32_t w = 0; w < wpc; ++w) {
-          uint64_t word = 0;
-          for (uint32_t b = 0; b < 64; ++b) {
-            const size_t li = size_t(c) * tm + 64 * w + b;
-            if (tkp[li]) {
-              word |= uint64_t(1) << b;
-              put<uint16_t>(vals, 2 * pos, tv[li]);
-              ++pos;
-            }
+      for (uint32_t w = 0; w < nw; ++w) {
+        uint64_t word = 0;
+        for (uint32_t b = 0; b < 64; ++b) {
+          uint32_t row, col;
+          bit_pos(w, b, &row, &col);
+          const size_t li = size_t(row) * tk + col;
+          if (tkp[li]) {
+            word |= uint64_t(1) << b;
+            put<uint16_t>(vals, 2 * pos, tv[li]);
+            ++pos;
           }
-          put<uint64_t>(bits, 8 * ((t * tk + c) * wpc + w), word);
         }
+        put<uint64_t>(bits, 8 * (t * nw + w), word);
       }
       pos = (pos + kPadValues - 1) / kPadValues * kPadValues;  // padding stays 0x0000
     }
@@ -200,24 +210,25 @@ swm_status validate_blob(const void* buf, size_t size, Header* hout) {
   const uint8_t* tp = b + h.off_tile_ptr();
   const uint8_t* bits = b + h.off_bits();
   const uint8_t* vals = b + h.off_values();
-  const uint64_t T = h.tiles(), wpc = h.words_per_col();
+  const uint64_t T = h.tiles(), nw = h.words_per_tile();
   if (get<uint32_t>(tp, 0) != 0) return SWM_ERR_FORMAT;
   uint64_t nnz = 0, max_tile = 0;
   for (uint64_t t = 0; t < T; ++t) {
     const uint64_t p0 = get<uint32_t>(tp, 4 * t), p1 = get<uint32_t>(tp, 4 * (t + 1));
     if (p1 < p0 || (p1 - p0) % kPadValues || p1 > h.padded_len) return SWM_ERR_FORMAT;
     const uint64_t i = t / h.kt, j = t % h.kt;
+    const int64_t rows_valid = std::max<int64_t>(0, std::min<int64_t>(16, h.m - int64_t(16 * i)));
+    const uint64_t row_ok = rows_valid >= 16 ? 0xFFFFull : ((uint64_t(1) << rows_valid) - 1);
     uint64_t pc = 0;
-    for (uint64_t c = 0; c < h.tk; ++c) {
-      const bool col_out = j * h.tk + c >= uint64_t(h.k);
-      for (uint64_t w = 0; w < wpc; ++w) {
-        const uint64_t word = get<uint64_t>(bits, 8 * ((t * h.tk + c) * wpc + w));
-        if (word && col_out) return SWM_ERR_FORMAT;
-        const int64_t row0 = int64_t(i * h.tm + 64 * w);
-        const int64_t valid = std::max<int64_t>(0, std::min<int64_t>(64, h.m - row0));
-        if (valid < 64 && (word >> valid) != 0) return SWM_ERR_FORMAT;
-        pc += uint64_t(__builtin_popcountll(word));
+    for (uint64_t w = 0; w < nw; ++w) {
+      const uint64_t word = get<uint64_t>(bits, 8 * (t * nw + w));
+      uint64_t allowed = 0;
+      for (uint32_t q = 0; q < 4; ++q) {
+        const int64_t col = int64_t(j * h.tk + 32 * (w >> 3) + 8 * q + (w & 7));
+        if (col < h.k) allowed |= row_ok << (16 * q);
       }
+      if (word & ~allowed) return SWM_ERR_FORMAT;
+      pc += uint64_t(__builtin_popcountll(word));
     }
     if (p1 - p0 < pc || p1 - p0 >= pc + kPadValues) return SWM_ERR_FORMAT;
     for (uint64_t q = p0 + pc; q < p1; ++q)

@@ -23,18 +23,26 @@ struct DevFormat {
 
 // Work split of the decode kernel for one call.
 struct DecodePlan {
-  int waves = 4;           // waves per workgroup (all on the same 64-row block)
-  int tiles_per_wave = 1;  // consecutive tiles of one row block per wave
-  int splits = 1;          // workgroups per row block (split-K)
+  int waves = 1;           // waves per workgroup (one workgroup per 16-row slab)
+  int tiles_per_wave = 1;  // consecutive tiles of the slab per wave
+  int seg_tiles = 4;       // tiles per streamed segment
+  int seg_chunks = 1;      // 1 KiB loads per segment (covers the largest segment)
+  int splits = 1;
 };
 
-DecodePlan plan_decode(const Header& h, int n, int num_cus);
+// Work split of the decode kernel; `tile_ptr` (host, mt*kt+1 entries) sizes
+// the segment loads.
+DecodePlan plan_decode(const Header& h, const uint32_t* tile_ptr, int num_cus);
 size_t decode_partial_floats(const Header& h, const DecodePlan& p);
 
 hipError_t launch_decode(const DevFormat& f, const DecodePlan& p, const uint16_t* X, int64_t ldx,
                          uint16_t* Y, int64_t ldy, int n, bool skip, hipStream_t s);
 
 hipError_t launch_decompress(const DevFormat& f, uint16_t* W, int64_t ldw, hipStream_t s);
+
+// HBM read-bandwidth calibration: `blocks` workgroups of 256 threads stream `bytes`.
+hipError_t launch_stream(const void* src, size_t bytes, int unroll, int blocks, uint32_t* out,
+                         hipStream_t s);
 
 // Dense W (row-major) times token-major X for n <= 16 tokens.
 struct DensePlan {

@@ -39,7 +39,6 @@ typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
 
 constexpr int BM = 256, BN = 256, BK = 64;
 constexpr int kTileBytes = BM * BK * 2;  // 32 KiB per operand stage
-constexpr int kMaxChunks = 8;
 
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p));
@@ -79,8 +78,8 @@ struct PrefillArgs {
   int64_t ldw, ldx, ldy;
   int M, N, K;
   int tiles_m, tiles_n, kt;
-  int group_m;  // output-tile rows per L2 group
-  int run_vals; // per-wave run buffer (values), sparse variant
+  int group_m;     // output-tile rows per L2 group
+  int run_chunks;  // 512-byte run chunks per tile (1..4), sparse variant
 };
 
 // Map the workgroup id to an output tile: regroup ids so that each XCD (id % 8)
@@ -115,7 +114,7 @@ __global__ __launch_bounds__(256, 1) void prefill_kernel(PrefillArgs a) {
   // LDS: A stages [2][32 KiB] | B stages [2][32 KiB] | zero (16 B) | run buffers
   const uint32_t sA = lds_addr(smem), sB = sA + 2 * kTileBytes;
   const uint32_t zero_addr = sB + 2 * kTileBytes;
-  const uint32_t runbuf = zero_addr + 16 + uint32_t(wave) * uint32_t(a.run_vals) * 2u;
+  const uint32_t runbuf = zero_addr + 16 + uint32_t(wave) * 4u * uint32_t(a.run_chunks) * 512u;
   if (kSparse && tid < 4) reinterpret_cast<uint32_t*>(smem + 4 * kTileBytes)[tid] = 0u;
 
   // Global fetch map: thread -> (row r*32 + tid/8, chunk tid%8), r = 0..7.
@@ -123,6 +122,7 @@ __global__ __launch_bounds__(256, 1) void prefill_kernel(PrefillArgs a) {
   const int nsteps = (a.K + BK - 1) / BK;
 
   u32x4 regA[8], regB[8];
+  u32x2 runreg[16];  // sparse: 4 tiles x up to 4 chunks of 8 bytes per lane
   auto fetch_B = [&](int ks) {
     const int k = ks * BK + fch * 8;
 #pragma unroll
@@ -151,37 +151,49 @@ __global__ __launch_bounds__(256, 1) void prefill_kernel(PrefillArgs a) {
 #pragma unroll
     for (int r = 0; r < 8; ++r) lds_store16(sA + stage * kTileBytes + swz(r * 32 + frow, fch), regA[r]);
   };
-  // Sparse: this wave's tile of step ks is (row block m0/64 + wave, tile column ks).
-  const int my_rb = m0 / 64 + wave;
-  const bool rb_ok = my_rb * 64 < a.M;
+  // Sparse: at step ks this wave expands the four 16x64 tiles (slabs
+  // m0/16 + 4*wave + tt, tile column ks), tt = 0..3, into A-stage rows
+  // 64*wave + 16*tt .. +15.  Their runs are staged in this wave's LDS run
+  // buffer in 512-byte chunks (8 bytes per lane), run_chunks per tile.
+  const int slab0 = m0 / 16 + 4 * wave;
+  const uint32_t tile_run_bytes = uint32_t(a.run_chunks) * 512u;
   auto fetch_A_run = [&](int ks) {
-    if (!rb_ok) return;
-    const uint64_t t = uint64_t(my_rb) * a.kt + ks;
-    const uint32_t p0 = a.tile_ptr[t], p1 = a.tile_ptr[t + 1];
-    const int nch = int((p1 - p0 + 511) >> 9);
-    const u32x4* src = reinterpret_cast<const u32x4*>(a.vals + p0) + lane;
 #pragma unroll
-    for (int c = 0; c < kMaxChunks; ++c)
-      if (c < nch) regA[c] = __builtin_nontemporal_load(src + c * 64);
+    for (int tt = 0; tt < 4; ++tt) {
+      if ((slab0 + tt) * 16 >= a.M) continue;
+      const uint64_t t = uint64_t(slab0 + tt) * a.kt + ks;
+      const uint32_t p0 = a.tile_ptr[t], p1 = a.tile_ptr[t + 1];
+      const uint32_t last = p1 > p0 + 4 ? p1 - 4 : p0;
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        if (c < a.run_chunks) {
+          const uint32_t off = min(p0 + uint32_t(c * 256 + lane * 4), last);
+          runreg[tt * 4 + c] = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(a.vals + off));
+        }
+    }
   };
-  auto stage_A_run = [&](int ks) {
-    if (!rb_ok) return;
-    const uint64_t t = uint64_t(my_rb) * a.kt + ks;
-    const uint32_t p0 = a.tile_ptr[t], p1 = a.tile_ptr[t + 1];
-    const int nch = int((p1 - p0 + 511) >> 9);
+  auto stage_A_run = [&]() {
 #pragma unroll
-    for (int c = 0; c < kMaxChunks; ++c)
-      if (c < nch) lds_store16(runbuf + c * 1024 + lane * 16, regA[c]);
+    for (int tt = 0; tt < 4; ++tt) {
+      if ((slab0 + tt) * 16 >= a.M) continue;
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        if (c < a.run_chunks)
+          *reinterpret_cast<__attribute__((address_space(3))) u32x2*>(
+              static_cast<uintptr_t>(runbuf + tt * tile_run_bytes + c * 512 + lane * 8)) = runreg[tt * 4 + c];
+    }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
   };
-  // Expand 8 columns (group g) of this wave's tile into the A stage.
-  auto expand_group = [&](int ks, int stage, int g, uint32_t& base) {
-    const int row = wave * 64 + lane;
+  // Expand step s (32 columns) of tile tt: eight words -> this lane's row
+  // l%16, columns 32s + 8(l/16) .. +7 -> one 16-byte store.  `base` walks the
+  // tile's run in LDS (bytes).
+  auto expand_unit = [&](int ks, int stage, int tt, int s, uint32_t& base) {
+    const int row = wave * 64 + tt * 16 + (lane & 15);
     u32x4 out = {0u, 0u, 0u, 0u};
-    if (rb_ok) {
-      const uint64_t t = uint64_t(my_rb) * a.kt + ks;
-      const uint64_t* tb = a.bits + t * 64 + 8 * g;
+    if ((slab0 + tt) * 16 < a.M) {
+      const uint64_t t = uint64_t(slab0 + tt) * a.kt + ks;
+      const uint64_t* tb = a.bits + t * 16 + 8 * s;
       half8 h;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
@@ -192,7 +204,7 @@ __global__ __launch_bounds__(256, 1) void prefill_kernel(PrefillArgs a) {
       }
       out = __builtin_bit_cast(u32x4, h);
     }
-    lds_store16(sA + stage * kTileBytes + swz(row, g), out);
+    lds_store16(sA + stage * kTileBytes + swz(row, 4 * s + (lane >> 4)), out);
   };
 
   f32x16 acc[4][4];
@@ -210,9 +222,11 @@ __global__ __launch_bounds__(256, 1) void prefill_kernel(PrefillArgs a) {
   if constexpr (kSparse) {
     __syncthreads();  // zero word visible
     fetch_A_run(0);
-    stage_A_run(0);
-    uint32_t base = runbuf;
-    for (int g = 0; g < 8; ++g) expand_group(0, 0, g, base);
+    stage_A_run();
+    for (int tt = 0; tt < 4; ++tt) {
+      uint32_t base = runbuf + uint32_t(tt) * tile_run_bytes;
+      for (int s2 = 0; s2 < 2; ++s2) expand_unit(0, 0, tt, s2, base);
+    }
     if (nsteps > 1) fetch_A_run(1);
   } else {
     fetch_A_dense(0);
@@ -225,7 +239,7 @@ __global__ __launch_bounds__(256, 1) void prefill_kernel(PrefillArgs a) {
     const int st = ks & 1;
     const bool more = ks + 1 < nsteps;
     if constexpr (kSparse) {
-      if (more) stage_A_run(ks + 1);
+      if (more) stage_A_run();
       if (ks + 2 < nsteps) fetch_A_run(ks + 2);
     }
     if (more) {
@@ -249,7 +263,13 @@ __global__ __launch_bounds__(256, 1) void prefill_kernel(PrefillArgs a) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[i], fb[j], acc[i][j], 0, 0, 0);
         if constexpr (kSparse) {
-          if (more && (i & 1)) expand_group(ks + 1, st ^ 1, kk * 2 + (i >> 1), base);
+          // eight expansion units per step (tile tt = unit/2, step s = unit%2),
+          // one after every second product
+          if (more && (i & 1)) {
+            const int unit = kk * 2 + (i >> 1), tt = unit >> 1, s2 = unit & 1;
+            if (s2 == 0) base = runbuf + uint32_t(tt) * tile_run_bytes;
+            expand_unit(ks + 1, st ^ 1, tt, s2, base);
+          }
         }
       }
     }
@@ -313,8 +333,8 @@ bool prefill_supported(int64_t K, int64_t ldx, const void* X) {
 }
 
 size_t prefill_sparse_lds(const Header& h) {
-  const size_t run = (size_t(h.max_tile) + 511) / 512 * 512;
-  return size_t(4) * kTileBytes + 16 + 4 * run * 2;
+  const size_t chunks = (size_t(h.max_tile) + 255) / 256;  // 512-byte chunks per tile run
+  return size_t(4) * kTileBytes + 16 + 4 /*waves*/ * 4 /*tiles*/ * (chunks ? chunks : 1) * 512;
 }
 
 hipError_t launch_prefill_dense(const uint16_t* W, int64_t ldw, const uint16_t* X, int64_t ldx,
@@ -336,7 +356,9 @@ hipError_t launch_prefill_sparse(const DevFormat& f, const uint16_t* X, int64_t 
   a.bits = f.bits;
   a.vals = f.vals;
   a.kt = int(f.h.kt);
-  a.run_vals = int((f.h.max_tile + 511) / 512 * 512);
+  a.run_chunks = int((f.h.max_tile + 255) / 256);
+  if (a.run_chunks < 1) a.run_chunks = 1;
+  if (f.h.tm != 16 || f.h.tk != 64 || f.h.max_tile > 1024) return hipErrorInvalidValue;
   if (a.tiles_m == 0 || a.tiles_n == 0) return hipSuccess;
   const size_t lds = prefill_sparse_lds(f.h);
   if (lds > 160 * 1024) return hipErrorInvalidValue;

@@ -9,11 +9,12 @@
 
 namespace swm {
 
-constexpr uint32_t kVersion = 1;
+constexpr uint32_t kVersion = 2;
+constexpr uint32_t kTM = 16;  // rows per tile
 constexpr size_t kHeaderBytes = 64;
 constexpr int kPadValues = 8;  // each tile run is padded to a multiple of 8 values (16 B)
 
-// Parsed SWM-TCB v1 header (little-endian on disk; this build targets x86-64 hosts).
+// Parsed SWM-TCB v2 header (little-endian on disk; this build targets x86-64 hosts).
 struct Header {
   int64_t m = 0, k = 0;
   uint32_t tm = 0, tk = 0;
@@ -22,8 +23,8 @@ struct Header {
   uint32_t max_tile = 0;
 
   uint64_t tiles() const { return uint64_t(mt) * kt; }
-  uint64_t words_per_col() const { return tm / 64; }
-  uint64_t n_bits() const { return tiles() * tk * words_per_col(); }
+  uint64_t words_per_tile() const { return tk / 4; }  // 4 column bitmaps of 16 bits per word
+  uint64_t n_bits() const { return tiles() * words_per_tile(); }
   size_t off_tile_ptr() const { return kHeaderBytes; }
   size_t off_bits() const { return off_tile_ptr() + 4 * (tiles() + 1); }
   size_t off_values() const { return off_bits() + 8 * n_bits(); }

@@ -47,14 +47,14 @@ def _case(seed, M, K, density, signed_zero=True):
 
 
 @pytest.mark.parametrize("M,K,tile,density", [
-    (1, 1, (64, 64), 1.0), (3, 10, (64, 8), 0.5), (64, 64, (64, 64), 0.5), (100, 70, (64, 64), 0.5),
-    (130, 300, (128, 64), 0.3), (65, 257, (64, 256), 0.01), (200, 40, (256, 8), 0.99),
-    (256, 512, (64, 64), 0.0), (257, 129, (64, 128), 1.0),
+    (1, 1, (16, 64), 1.0), (3, 10, (16, 32), 0.5), (64, 64, (16, 64), 0.5), (100, 70, (16, 64), 0.5),
+    (130, 300, (16, 96), 0.3), (65, 257, (16, 256), 0.01), (200, 40, (16, 32), 0.99),
+    (256, 512, (16, 64), 0.0), (257, 129, (16, 128), 1.0), (17, 65, (16, 64), 0.5),
 ])
 def test_cpp_encoder_matches_numpy_encoder_bytes(M, K, tile, density):
     W, mask = _case(M * 7 + K, M, K, density)
     a = swm.encode_blob(W, mask, tile=tile)
-    b = oracle.tcb_encode(W, mask, TM=tile[0], TK=tile[1]).blob()
+    b = oracle.tcb_encode(W, mask, TK=tile[1]).blob()
     assert a == b
     assert swm.validate_blob(a) == 0
 
@@ -83,26 +83,29 @@ def test_validator_rejects_corruption():
     blob = swm.encode_blob(W, mask)
     f = oracle.tcb_parse(blob)
     T = f.Mt * f.Kt
+    nW = f.TK // 4
     off_tp = 64
     off_bits = off_tp + 4 * (T + 1)
-    off_vals = off_bits + 8 * T * f.TK
+    off_vals = off_bits + 8 * T * nW
     assert swm.validate_blob(blob) == 0
     bad = {
         "magic": _corrupt(blob, 0, b"XXXX"),
-        "version": _corrupt(blob, 4, (2).to_bytes(4, "little")),
+        "version": _corrupt(blob, 4, (3).to_bytes(4, "little")),
         "reserved": _corrupt(blob, 60, (1).to_bytes(4, "little")),
         "truncated": blob[:-2],
         "extra": blob + b"\0\0",
         "nnz": _corrupt(blob, 32, (f.nnz + 1).to_bytes(8, "little")),
         "max_tile": _corrupt(blob, 56, (f.max_tile + 8).to_bytes(4, "little")),
         "tile_ptr_nonmonotone": _corrupt(blob, off_tp + 4, (int(f.tile_ptr[2]) + 8).to_bytes(4, "little")),
-        "bit_beyond_M": _corrupt(blob, off_bits + 8 * ((f.Kt * 1) * f.TK + 3), (1 << 63).to_bytes(8, "little")),
-        "bit_beyond_K": _corrupt(blob, off_bits + 8 * ((f.Kt - 1) * f.TK + 63), (1).to_bytes(8, "little")),
+        # 100 rows: the last slab (rows 96..111) has 4 valid rows; bit 5 of any word is row 5
+        "bit_beyond_M": _corrupt(blob, off_bits + 8 * (((f.Mt - 1) * f.Kt) * nW + 3), (1 << 5).to_bytes(8, "little")),
+        # 130 columns: the last tile column starts at 128; its word 15 (step 1, e = 7) is column 128+39
+        "bit_beyond_K": _corrupt(blob, off_bits + 8 * ((f.Kt - 1) * nW + 15), (1).to_bytes(8, "little")),
         "popcount_mismatch": _corrupt(blob, off_bits, (int(f.bits[0]) ^ 1).to_bytes(8, "little")),
     }
     # nonzero padding: find a tile whose run has padding
     lens = np.diff(f.tile_ptr.astype(np.int64))
-    pcs = np.array([bin(int(x)).count("1") for x in f.bits]).reshape(T, f.TK).sum(1)
+    pcs = np.array([bin(int(x)).count("1") for x in f.bits]).reshape(T, nW).sum(1)
     t = int(np.nonzero(lens > pcs)[0][0])
     bad["padding"] = _corrupt(blob, off_vals + 2 * (int(f.tile_ptr[t + 1]) - 1), b"\x01\x00")
     for name, b in bad.items():
@@ -111,14 +114,15 @@ def test_validator_rejects_corruption():
 
 def test_dry_run_sizes_and_overflow():
     info = swm.size_dry_run(4096, 4096, 4096 * 2048)
-    assert info["mt"] == 64 and info["kt"] == 64
-    assert info["bytes_bits"] == 64 * 64 * 64 * 8
-    assert info["padded_len"] == 4096 * 2048 + 64 * 64 * 7
-    assert info["bytes_total"] == 64 + 4 * (64 * 64 + 1) + info["bytes_bits"] + 2 * info["padded_len"]
+    assert info["mt"] == 256 and info["kt"] == 64
+    assert info["bytes_bits"] == 256 * 64 * 16 * 8
+    assert info["padded_len"] == 4096 * 2048 + 256 * 64 * 7
+    assert info["bytes_total"] == 64 + 4 * (256 * 64 + 1) + info["bytes_bits"] + 2 * info["padded_len"]
     assert swm.size_dry_run_status(1 << 20, 1 << 20, 1 << 33) == 5  # padded length >= 2^32
     assert swm.size_dry_run_status(10, 10, 101) == 1  # nnz > M*K
     assert swm.size_dry_run_status(-1, 10, 0) == 1
-    assert swm.size_dry_run_status(64, 64, 0, tile=(32, 64)) == 1  # tm not a multiple of 64
+    assert swm.size_dry_run_status(64, 64, 0, tile=(32, 64)) == 1  # tm must be 16
+    assert swm.size_dry_run_status(64, 64, 0, tile=(16, 48)) == 1  # tk not a multiple of 32
 
 
 def test_dry_run_bounds_the_real_format():
@@ -140,7 +144,7 @@ def test_encoder_rejects_bad_arguments():
     # null size pointer
     assert lib.swm_encode_blob(W.ctypes.data, 4, None, 4, 4, 4, None, None, 0, None) == 1
     # bad tile shape
-    cfg = swm.TileCfg(64, 12)
+    cfg = swm.TileCfg(16, 12)
     assert lib.swm_encode_blob(W.ctypes.data, 4, None, 4, 4, 4, ctypes.byref(cfg), None, 0, ctypes.byref(size)) == 1
     # empty matrix is fine
     assert lib.swm_encode_blob(None, 0, None, 0, 0, 0, None, None, 0, ctypes.byref(size)) == 0

@@ -231,8 +231,8 @@ def test_error_codes(gpu_lib):
     assert lib.swm_spmspv(f._h, xp, 512, yp, 256, 17, s) == 1     # n > 16
     assert lib.swm_spmspv(f._h, xp, 512, yp, 256, 0, s) == 1      # n < 1
     assert lib.swm_dense_gemm(xp, 512, xp, 512, yp, 256, 256, 512, -1, s) == 1
-    g = swm.sparse_compress(W, mask, tile=(128, 64))
-    assert lib.swm_spmm(g._h, xp, 512, yp, 256, 8, s) == 8        # no kernel for tm=128
+    g = swm.sparse_compress(W, mask, tile=(16, 32))
+    assert lib.swm_spmm(g._h, xp, 512, yp, 256, 8, s) == 8        # no kernel for tk=32
 
 
 # ------------------------------------------------------------------ prefill (N > 16)

@@ -132,33 +132,33 @@ def test_skip_ignores_all_zero_channels_only():
 def test_format_hand_worked_bytes():
     d = json.load(open(os.path.join(GOLDEN, "tcb_hand_example.json")))
     W = np.array(d["W_rows_fp16"], dtype=np.float16)
-    f = oracle.tcb_encode(W, None, TM=d["TM"], TK=d["TK"])
+    f = oracle.tcb_encode(W, None, TK=d["TK"])
+    assert f.TM == d["TM"]
     assert (f.Mt, f.Kt, f.nnz, f.padded_len, f.max_tile) == (d["Mt"], d["Kt"], d["nnz"], d["padded_len"], d["max_tile"])
     assert list(f.tile_ptr) == d["tile_ptr"]
     assert [int(b) for b in f.bits] == d["bits"]
     assert [format(int(v), "04x") for v in f.values] == d["values_hex"]
     assert f.header() == bytes.fromhex(d["header_hex"].replace(" ", ""))
     blob = f.blob()
-    assert len(blob) == 64 + 4 * 3 + 8 * 16 + 2 * 16
+    assert len(blob) == 64 + 4 * 2 + 8 * 8 + 2 * 8
     g = oracle.tcb_parse(blob)
     assert np.array_equal(oracle.tcb_decode(g), W.view(np.uint16))
 
 
-@pytest.mark.parametrize("M,K,TM,TK,density", [
-    (1, 1, 64, 8, 1.0), (64, 64, 64, 64, 0.5), (100, 70, 64, 64, 0.5), (130, 300, 128, 64, 0.3),
-    (65, 257, 64, 256, 0.01), (200, 40, 256, 8, 0.99), (64, 64, 64, 64, 0.0),
+@pytest.mark.parametrize("M,K,TK,density", [
+    (1, 1, 32, 1.0), (16, 64, 64, 0.5), (100, 70, 64, 0.5), (130, 300, 96, 0.3),
+    (65, 257, 256, 0.01), (200, 40, 32, 0.99), (64, 64, 64, 0.0),
 ])
-def test_format_round_trip_and_invariants(M, K, TM, TK, density):
+def test_format_round_trip_and_invariants(M, K, TK, density):
     W, mask, _ = _rand_case(M * 1000 + K, M, K, 1, density, signed_zero=True)
-    f = oracle.tcb_encode(W, mask, TM=TM, TK=TK)
+    f = oracle.tcb_encode(W, mask, TK=TK)
     dec = oracle.tcb_decode(oracle.tcb_parse(f.blob()))
     want = np.where(mask, W.view(np.uint16), np.uint16(0))
     assert np.array_equal(dec, want)  # bit-exact, -0 kept where the mask keeps it
     assert f.nnz == int(mask.sum())
     pc = np.array([bin(int(b)).count("1") for b in f.bits])
     assert pc.sum() == f.nnz
-    WPC = TM // 64
-    per_tile = pc.reshape(f.Mt * f.Kt, TK * WPC).sum(axis=1)
+    per_tile = pc.reshape(f.Mt * f.Kt, TK // 4).sum(axis=1)
     lens = np.diff(f.tile_ptr.astype(np.int64))
     assert np.all(lens % 8 == 0) and np.all(lens >= per_tile) and np.all(lens - per_tile < 8)
     for t in range(f.Mt * f.Kt):
@@ -170,7 +170,7 @@ def test_format_round_trip_and_invariants(M, K, TM, TK, density):
 def test_null_mask_keeps_nonzeros():
     W, _, _ = _rand_case(13, 70, 70, 1, 1.0, signed_zero=True)
     W[3, 3] = 0
-    f = oracle.tcb_encode(W, None, TM=64, TK=64)
+    f = oracle.tcb_encode(W, None, TK=64)
     keep = (W.view(np.uint16) & 0x7FFF) != 0
     assert f.nnz == int(keep.sum())
     dec = oracle.tcb_decode(f)
@@ -207,10 +207,16 @@ def test_planted_mistakes_fail_the_pins(mut):
     assert not ok
 
 
-def test_planted_format_mistake_fails_hand_bytes():
-    # a row-major value order instead of column-major must not reproduce the hand bytes
+def test_planted_format_mistakes_fail_hand_bytes():
+    # plain row-major or plain column-major value orders must not reproduce the hand bytes
     d = json.load(open(os.path.join(GOLDEN, "tcb_hand_example.json")))
     W = np.array(d["W_rows_fp16"], dtype=np.float16)
     Wb = W.view(np.uint16)
-    rowmajor = [format(int(v), "04x") for v in Wb[:, :8][Wb[:, :8] != 0]]
-    assert rowmajor != d["values_hex"][:len(rowmajor)]
+    rowmajor = [format(int(v), "04x") for v in Wb[Wb != 0]]
+    colmajor = [format(int(v), "04x") for v in Wb.T[Wb.T != 0]]
+    assert rowmajor != d["values_hex"][:7]
+    assert colmajor != d["values_hex"][:7]
+    # a word layout with one column per 16-bit group in plain order (no interleave) differs
+    f = oracle.tcb_encode(W, None, TK=32)
+    assert [int(b) for b in f.bits] == d["bits"]
+    assert int(f.bits[0]) != (1 | 4 | (1 << 17))
