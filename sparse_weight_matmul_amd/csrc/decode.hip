@@ -151,14 +151,24 @@ __global__ __launch_bounds__(1024) void decode_kernel(DecodeArgs a) {
     const int jlast = j1 - 1;
     const int nseg = (j1 - j0 + kSegTiles - 1) / kSegTiles;
     auto seg_first = [&](int g) { return j0 + kSegTiles * min(g, nseg - 1); };
-    auto load_seg = [&](int g, u32x4 (&r)[kC]) {
+    // A segment in flight: its kC 1 KiB loads and its kSegTiles+1 tile
+    // pointers (wave-uniform).  Segments past the wave's last one load one
+    // cached 16-byte slot instead of repeating the last segment.
+    struct Seg {
+      u32x4 r[kC];
+      uint32_t tp[kSegTiles + 1];
+    };
+    auto load_seg = [&](int g, Seg& sg) {
       const int ja = seg_first(g), jb = min(ja + kSegTiles, j1);
-      const uint32_t p0 = a.tile_ptr[tbase + ja], p1 = a.tile_ptr[tbase + jb];
-      const uint32_t last = p1 > p0 + 8 ? p1 - 8 : p0;  // last 8-value slot of the segment
+#pragma unroll
+      for (int i = 0; i <= kSegTiles; ++i) sg.tp[i] = a.tile_ptr[tbase + min(ja + i, jb)];
+      const uint32_t p0 = sg.tp[0], p1 = sg.tp[kSegTiles];
+      const bool real = g < nseg;
+      const uint32_t last = (real && p1 > p0 + 8) ? p1 - 8 : p0;  // last 8-value slot
 #pragma unroll
       for (int c = 0; c < kC; ++c) {
         const uint32_t off = min(p0 + uint32_t(c * 512 + lane * 8), last);
-        r[c] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(a.vals + off));
+        sg.r[c] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(a.vals + off));
       }
     };
     auto touch_seg_words = [&](int g) {
@@ -180,7 +190,7 @@ __global__ __launch_bounds__(1024) void decode_kernel(DecodeArgs a) {
       }
     };
 
-    u32x4 segA[kC], segB[kC];
+    Seg segA, segB;
     touch_seg_words(0);
     touch_seg_words(1);
     load_seg(0, segA);
@@ -235,23 +245,25 @@ __global__ __launch_bounds__(1024) void decode_kernel(DecodeArgs a) {
       }
     };
 
-    // Stage segment g (in `r`) into LDS, request segment g+2 into `r`, then
+    // Stage segment g (in `sg`) into LDS, request segment g+2 into `sg`, then
     // decode the segment's tiles.
-    auto do_seg = [&](int g, u32x4 (&r)[kC]) {
+    auto do_seg = [&](int g, Seg& sg) {
 #pragma unroll
       for (int c = 0; c < kC; ++c)
-        *reinterpret_cast<lds_u32x4*>(static_cast<uintptr_t>(buf + c * 1024 + lane * 16)) = r[c];
+        *reinterpret_cast<lds_u32x4*>(static_cast<uintptr_t>(buf + c * 1024 + lane * 16)) = sg.r[c];
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_wave_barrier();
       const int ja = j0 + kSegTiles * g;
-      const uint32_t p0 = a.tile_ptr[tbase + ja];
-      load_seg(g + 2, r);
+      uint32_t run[kSegTiles];
+#pragma unroll
+      for (int tt = 0; tt < kSegTiles; ++tt) run[tt] = buf + 2u * (sg.tp[tt] - sg.tp[0]);
+      load_seg(g + 2, sg);
       touch_seg_words(g + 2);
 #pragma unroll
       for (int tt = 0; tt < kSegTiles; ++tt) {
         const int j = ja + tt;
         if (j >= j1) break;
-        do_tile(j, buf + 2u * (a.tile_ptr[tbase + j] - p0), tt & 1);
+        do_tile(j, run[tt], tt & 1);
       }
     };
 
