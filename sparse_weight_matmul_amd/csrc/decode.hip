@@ -56,12 +56,65 @@ __device__ __forceinline__ uint32_t run_addr(uint64_t word, uint32_t run_base, u
   return a;
 }
 
+// A operand of one 32-column step from its eight bitmap words: element e of
+// lane l is the lane's value in word e, or +0 where its bit is clear.  Per
+// pair of words: each lane reads the halfword at its rank in either run (lanes
+// whose bit is clear read a neighbour), then one v_cndmask zeroes the low half
+// and a v_cndmask with SDWA (destination = upper word, lower word preserved)
+// zeroes and packs the high half in one instruction.  `base` is the LDS byte
+// address of word 0's run and advances past the step's eight runs.
+__device__ __forceinline__ half8 decode_step(const u32x16& w, uint32_t& base) {
+  typedef __attribute__((address_space(3))) uint16_t lds_u16;
+  u32x4 out;
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const uint64_t w0 = uint64_t(w[4 * p]) | (uint64_t(w[4 * p + 1]) << 32);
+    const uint64_t w1 = uint64_t(w[4 * p + 2]) | (uint64_t(w[4 * p + 3]) << 32);
+    const uint32_t r0 = __builtin_amdgcn_mbcnt_hi(uint32_t(w0 >> 32), __builtin_amdgcn_mbcnt_lo(uint32_t(w0), 0u));
+    const uint32_t r1 = __builtin_amdgcn_mbcnt_hi(uint32_t(w1 >> 32), __builtin_amdgcn_mbcnt_lo(uint32_t(w1), 0u));
+    // Run bases in bytes, one s_bcnt1 + s_lshl1_add per word, and the lane
+    // address in one v_lshl_add (written out so that they are not
+    // re-associated into a separate add per lane).
+    uint32_t b1, b2, c0, c1, a0, a1;
+    asm("s_bcnt1_i32_b64 %2, %4\n\t"
+        "s_lshl1_add_u32 %0, %2, %6\n\t"
+        "s_bcnt1_i32_b64 %3, %5\n\t"
+        "s_lshl1_add_u32 %1, %3, %0"
+        : "=&s"(b1), "=&s"(b2), "=&s"(c0), "=&s"(c1)
+        : "s"(w0), "s"(w1), "s"(base)
+        : "scc");
+    asm("v_lshl_add_u32 %0, %1, 1, %2" : "=v"(a0) : "v"(r0), "s"(base));
+    asm("v_lshl_add_u32 %0, %1, 1, %2" : "=v"(a1) : "v"(r1), "s"(b1));
+    const uint32_t d0 = *reinterpret_cast<const lds_u16*>(static_cast<uintptr_t>(a0));
+    const uint32_t d1 = *reinterpret_cast<const lds_u16*>(static_cast<uintptr_t>(a1));
+    base = b2;
+    uint32_t v;
+    asm("v_cndmask_b32_e64 %0, 0, %1, %3\n\t"
+        "s_mov_b64 vcc, %4\n\t"
+        "v_cndmask_b32_sdwa %0, 0, %2, vcc dst_sel:WORD_1 dst_unused:UNUSED_PRESERVE src0_sel:DWORD "
+        "src1_sel:WORD_0"
+        : "=&v"(v)
+        : "v"(d0), "v"(d1), "s"(w0), "s"(w1)
+        : "vcc");
+    out[p] = v;
+  }
+  return __builtin_bit_cast(half8, out);
+}
+
 __device__ __forceinline__ _Float16 lds_half(uint32_t addr) {
   return *reinterpret_cast<const lds_f16*>(static_cast<uintptr_t>(addr));
 }
 
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p));
+}
+
+// Wave-uniform reads of the format's read-only arrays through the constant
+// address space: always scalar loads, whatever other memory operations the
+// kernel performs before them.
+template <typename T>
+__device__ __forceinline__ T const_load(const void* p) {
+  return *reinterpret_cast<const __attribute__((address_space(4))) T*>(reinterpret_cast<uintptr_t>(p));
 }
 
 __device__ __forceinline__ uint64_t word_of(const u32x16& w, int e) {
@@ -89,8 +142,13 @@ __device__ __forceinline__ void slab_reduce_store(float* red, int nwaves, int wa
   const int m0 = slab * kSlab;
   for (int e = threadIdx.x; e < N * kSlab; e += blockDim.x) {
     const int tok = e >> 4, row = e & 15;
+    // all (at most 16) partials are read at once, then added in wave order
+    float v[16];
+#pragma unroll
+    for (int w = 0; w < 16; ++w) v[w] = red[min(w, nwaves - 1) * 256 + e];
     float sum = 0.f;
-    for (int w = 0; w < nwaves; ++w) sum += red[w * 256 + tok * 16 + row];
+#pragma unroll
+    for (int w = 0; w < 16; ++w) sum += w < nwaves ? v[w] : 0.f;
     if (m0 + row < M) Y[int64_t(tok) * ldy + m0 + row] = __builtin_bit_cast(uint16_t, _Float16(sum));
   }
 }
@@ -161,7 +219,7 @@ __global__ __launch_bounds__(1024) void decode_kernel(DecodeArgs a) {
     auto load_seg = [&](int g, Seg& sg) {
       const int ja = seg_first(g), jb = min(ja + kSegTiles, j1);
 #pragma unroll
-      for (int i = 0; i <= kSegTiles; ++i) sg.tp[i] = a.tile_ptr[tbase + min(ja + i, jb)];
+      for (int i = 0; i <= kSegTiles; ++i) sg.tp[i] = const_load<uint32_t>(a.tile_ptr + tbase + min(ja + i, jb));
       const uint32_t p0 = sg.tp[0], p1 = sg.tp[kSegTiles];
       const bool real = g < nseg;
       const uint32_t last = (real && p1 > p0 + 8) ? p1 - 8 : p0;  // last 8-value slot
@@ -178,7 +236,7 @@ __global__ __launch_bounds__(1024) void decode_kernel(DecodeArgs a) {
       keep ^= v[0] ^ v[1];
     };
     auto load_words = [&](int j, int s) -> u32x16 {
-      return *reinterpret_cast<const u32x16*>(a.bits + (tbase + j) * 16 + 8 * s);
+      return const_load<u32x16>(a.bits + (tbase + j) * 16 + 8 * s);
     };
     auto load_b = [&](int j, int s) -> half8 {
       int64_t col = int64_t(j) * kTK + 32 * s + kq;
@@ -275,6 +333,173 @@ __global__ __launch_bounds__(1024) void decode_kernel(DecodeArgs a) {
   if (keep == 0x9E3779B9u && a.N < 0) a.Y[0] = 0;  // never true: keeps the prefetch loads
 
   __syncthreads();  // all segment buffers are free: reuse them as the reduction area
+  slab_reduce_store(reinterpret_cast<float*>(smem + 16), nwaves, wave, lane, acc, slab, a.M, a.N,
+                    a.Y, a.ldy);
+}
+
+// ------------------------------------------------------------------ sparse, straight-line schedule
+// Same work split as decode_kernel (one workgroup per slab, wave w owns tiles
+// [w*tpw, w*tpw + tpw) with tpw <= 2*NS), but the whole wave program is
+// unrolled so that every vector load is issued unconditionally in a fixed
+// order, and each wait covers exactly the data it needs (vector loads return
+// in issue order):
+//   * the wave's tile pointers and the first bitmap step are requested first
+//     (scalar), then the bitmap words of the range are touched into L2 so
+//     that the per-step scalar loads hit there;
+//   * per segment of two tiles, the activations of its 128 columns for the N
+//     tokens are loaded first (kXI loads of 1 KiB: 256 contiguous bytes per
+//     token, whole cache lines), then its value chunks; using the
+//     activations never waits for value bytes;
+//   * two segments are in flight.  At a segment's start its activations go
+//     to the wave's LDS (B operands are then read with ds_read_b128); its
+//     chunks are copied tile by tile, each as soon as the chunks that hold it
+//     have arrived, so decoding overlaps the rest of the stream.
+constexpr int kXRow = 272;  // LDS bytes per token row of a segment's activations (256 + pad)
+
+template <int NS, int kC, int kXI>
+__global__ __launch_bounds__(1024) void decode_seq_kernel(DecodeArgs a) {
+  constexpr int kT = 2 * NS;      // tile slots per wave
+  constexpr int kSteps = 2 * kT;  // 32-column steps
+  constexpr int kTouch = (kT * 128 + 1023) / 1024;
+  constexpr int kXRows = 4 * kXI;  // token rows of the activation buffer
+  constexpr uint32_t kWaveLds = kC * 1024 + kXRows * kXRow;
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  const int lane = lane_id();
+  const int wave = __builtin_amdgcn_readfirstlane(int(threadIdx.x >> 6));
+  const int nwaves = int(blockDim.x >> 6);
+  const int slab = int(blockIdx.x);
+
+  // LDS: [0,16) zeros | per wave: kC KiB of value chunks, then the segment's
+  // activations [kXRows][kXRow]; the reduction area reuses it after a barrier.
+  if (threadIdx.x < 4) reinterpret_cast<uint32_t*>(smem)[threadIdx.x] = 0u;
+  __syncthreads();
+  const uint32_t zero_addr = lds_addr(smem);
+  const uint32_t buf = lds_addr(smem + 16 + size_t(wave) * kWaveLds);
+  const uint32_t xbuf = buf + kC * 1024;
+
+  const int j0 = wave * a.tpw;
+  const int nt = min(a.tpw, a.kt - j0);  // tiles of this wave (<= kT)
+
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  uint32_t keep = 0;
+  if (nt > 0) {
+    const uint64_t tb = uint64_t(slab) * a.kt + j0;  // first tile of the range
+    const int kmax8 = a.K - 8;                        // K >= 8 and K % 8 == 0 on this path
+
+    uint32_t tp[kT + 1];
+#pragma unroll
+    for (int i = 0; i <= kT; ++i) tp[i] = const_load<uint32_t>(a.tile_ptr + tb + min(i, nt));
+    u32x16 wv[kSteps];
+    auto load_w = [&](int t) {
+      const int jt = min(t >> 1, nt - 1);
+      wv[t] = const_load<u32x16>(a.bits + (tb + jt) * 16 + 8 * (t & 1));
+    };
+    load_w(0);
+    __builtin_amdgcn_sched_barrier(0);
+
+    u32x4 th[kTouch];
+    {
+      const uint32_t wbytes = uint32_t(nt) * 128u;
+      const uint8_t* wb = reinterpret_cast<const uint8_t*>(a.bits + tb * 16);
+#pragma unroll
+      for (int i = 0; i < kTouch; ++i)
+        th[i] = *reinterpret_cast<const u32x4*>(wb + min(uint32_t(i * 1024 + lane * 16), wbytes - 16u));
+    }
+
+    // Activation pieces: piece p = 64 i + lane is token p/16 (rows past N
+    // repeat token N-1), columns 8 (p%16) .. +7 of the segment.  Byte offsets
+    // fit 32 bits (16 tokens of at most 2^27 halves).
+    uint32_t xrow_off[kXI], xcol[kXI], xl[kXI];
+#pragma unroll
+    for (int i = 0; i < kXI; ++i) {
+      const int pce = i * 64 + lane;
+      xrow_off[i] = 2u * uint32_t(min(pce >> 4, a.N - 1)) * uint32_t(a.ldx);
+      xcol[i] = 8u * uint32_t(pce & 15);
+      xl[i] = xbuf + uint32_t(pce >> 4) * kXRow + 16u * uint32_t(pce & 15);
+    }
+    // B operand: lane l carries token l%16 (rows past kXRows repeat a valid
+    // row; their accumulator columns are never stored), columns 8(l/16) .. +7.
+    const uint32_t xb = xbuf + uint32_t(min(lane & 15, kXRows - 1)) * kXRow + 16u * uint32_t(lane >> 4);
+
+    u32x4 xr[NS][kXI];
+    u32x4 r[NS][kC];
+    // Segment g: its activations, then its value chunks.  For g = 0 the first
+    // step's bitmap is folded into the first tile pointer with a mask that is
+    // always zero (N >= 1), so the wait for the pointers also covers that
+    // scalar load, which would otherwise sink behind the first staging
+    // branches and be waited for there.
+    auto issue_seg = [&](int g) {
+      const int c0 = (j0 + 2 * g) * kTK;
+#pragma unroll
+      for (int i = 0; i < kXI; ++i) {
+        const uint32_t col = uint32_t(min(c0 + int(xcol[i]), kmax8));
+        xr[g][i] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint8_t*>(a.X) + xrow_off[i] +
+                                                   2u * col);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      if (g == 0) tp[0] += wv[0][0] & uint32_t(a.N >> 31);
+      const uint32_t p0 = tp[2 * g], p1 = tp[2 * g + 2];
+      const uint32_t last = p1 > p0 + 8 ? p1 - 8 : p0;  // last 8-value slot of the segment
+#pragma unroll
+      for (int c = 0; c < kC; ++c) {
+        const uint32_t off = min(p0 + uint32_t(c * 512 + lane * 8), last);
+        r[g][c] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(a.vals + off));
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    };
+
+    issue_seg(0);
+    if constexpr (NS > 1) issue_seg(1);
+
+#pragma unroll
+    for (int g = 0; g < NS; ++g) {
+      const uint32_t p0 = tp[2 * g];
+      if (2 * g < nt) {
+#pragma unroll
+        for (int i = 0; i < kXI; ++i)
+          *reinterpret_cast<lds_u32x4*>(static_cast<uintptr_t>(xl[i])) = xr[g][i];
+      }
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+        const int jt = 2 * g + tt;
+        if (jt == 0 || jt < nt) {  // tile slot 0 always exists (nt >= 1)
+          // Copy the chunks that complete this tile (chunks are used in issue order).
+          const uint32_t have = tt == 0 ? 0u : (2u * (tp[jt] - p0) + 1023u) >> 10;
+          const uint32_t need = (2u * (tp[jt + 1] - p0) + 1023u) >> 10;
+#pragma unroll
+          for (int c = 0; c < kC; ++c)
+            if (uint32_t(c) >= have && uint32_t(c) < need)
+              *reinterpret_cast<lds_u32x4*>(static_cast<uintptr_t>(buf + c * 1024 + lane * 16)) = r[g][c];
+          if (jt == 0) {
+#pragma unroll
+            for (int i = 0; i < kTouch; ++i) keep ^= th[i][0] ^ th[i][1] ^ th[i][2] ^ th[i][3];
+          }
+          __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+          __builtin_amdgcn_wave_barrier();
+          uint32_t base = buf + 2u * (tp[jt] - p0);
+#pragma unroll
+          for (int s = 0; s < 2; ++s) {
+            const int t = 2 * jt + s;
+            const u32x16 w = wv[t];
+            // wait for this step's words, then request the next step's
+            __builtin_amdgcn_sched_barrier(0);
+            const uint32_t wk = w[0];
+            asm volatile("" ::"s"(wk));
+            if (t + 1 < kSteps) load_w(t + 1);
+            __builtin_amdgcn_sched_barrier(0);
+            const half8 bop = __builtin_bit_cast(
+                half8, *reinterpret_cast<const lds_u32x4*>(static_cast<uintptr_t>(xb + tt * 128 + s * 64)));
+            const half8 aop = decode_step(w, base);
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(aop, bop, acc, 0, 0, 0);
+          }
+        }
+      }
+      if (g + 2 < NS) issue_seg(g + 2);
+    }
+  }
+  if (keep == 0x9E3779B9u && a.N < 0) a.Y[0] = 0;  // never true: keeps the L2 touch loads
+
+  __syncthreads();  // all wave buffers are free: reuse them as the reduction area
   slab_reduce_store(reinterpret_cast<float*>(smem + 16), nwaves, wave, lane, acc, slab, a.M, a.N,
                     a.Y, a.ldy);
 }
@@ -425,6 +650,31 @@ __global__ __launch_bounds__(256) void decompress_kernel(DecompArgs a) {
   }
 }
 
+template <int NS, int kXI>
+void launch_seq_x(int kc, dim3 grid, dim3 block, size_t lds, hipStream_t s, const DecodeArgs& a) {
+  switch (kc) {
+    case 1: hipLaunchKernelGGL((decode_seq_kernel<NS, 1, kXI>), grid, block, lds, s, a); break;
+    case 2: hipLaunchKernelGGL((decode_seq_kernel<NS, 2, kXI>), grid, block, lds, s, a); break;
+    case 3: hipLaunchKernelGGL((decode_seq_kernel<NS, 3, kXI>), grid, block, lds, s, a); break;
+    default: hipLaunchKernelGGL((decode_seq_kernel<NS, 4, kXI>), grid, block, lds, s, a); break;
+  }
+}
+
+template <int NS>
+void launch_seq_ns(int kc, int kxi, dim3 grid, dim3 block, size_t lds, hipStream_t s, const DecodeArgs& a) {
+  if (kxi == 1) launch_seq_x<NS, 1>(kc, grid, block, lds, s, a);
+  else if (kxi == 2) launch_seq_x<NS, 2>(kc, grid, block, lds, s, a);
+  else launch_seq_x<NS, 4>(kc, grid, block, lds, s, a);
+}
+
+// Smallest instantiated segment count covering `segs` two-tile segments (0: none).
+int seq_instance(int segs) {
+  static const int kInst[] = {1, 2, 3, 4, 6, 8};
+  for (int v : kInst)
+    if (segs <= v) return v;
+  return 0;
+}
+
 template <int kC>
 void launch_decode_c(bool skip, dim3 grid, dim3 block, size_t lds, hipStream_t s, const DecodeArgs& a) {
   if (skip) hipLaunchKernelGGL((decode_kernel<kC, true, true>), grid, block, lds, s, a);
@@ -467,6 +717,20 @@ DecodePlan plan_decode(const Header& h, const uint32_t* tp, int num_cus) {
       }
   p.seg_chunks = int((max_bytes + 1023) / 1024);
   if (p.seg_chunks < 1) p.seg_chunks = 1;
+  // Straight-line schedule: two-tile segments aligned to each wave's range.
+  p.seq_segs = seq_instance(int((tpw + 1) / 2));
+  uint64_t max2 = 0;
+  for (uint64_t i = 0; i < h.mt; ++i)
+    for (int64_t ja = 0; ja < int64_t(h.kt); ja += tpw)
+      for (int64_t js = ja; js < std::min<int64_t>(ja + tpw, h.kt); js += 2) {
+        const int64_t je = std::min<int64_t>({js + 2, ja + tpw, int64_t(h.kt)});
+        const uint64_t b = 2ull * (tp[i * h.kt + je] - tp[i * h.kt + js]);
+        if (b > max2) max2 = b;
+      }
+  p.seq_chunks = int((max2 + 1023) / 1024);
+  if (p.seq_chunks < 1) p.seq_chunks = 1;
+  if (p.seq_chunks > 4) p.seq_segs = 0;  // cannot happen: two tiles hold at most 4 KiB
+  if (getenv("SWM_DECODE_LOOP")) p.seq_segs = 0;
   p.splits = 1;
   return p;
 }
@@ -498,6 +762,22 @@ hipError_t launch_decode(const DevFormat& f, const DecodePlan& p, const uint16_t
   const size_t lds = 16 + (run_bytes > red_bytes ? run_bytes : red_bytes);
   if (f.h.mt == 0) return hipSuccess;
   const dim3 grid{unsigned(f.h.mt), 1, 1}, block{unsigned(p.waves * 64), 1, 1};
+  // The straight-line kernel addresses X with 32-bit byte offsets.
+  const bool x32 = 2 * ((int64_t(n) - 1) * ldx + f.h.k) < (int64_t(1) << 32);
+  if (vec && !skip && p.seq_segs > 0 && a.K >= 8 && x32) {
+    const int kxi = n <= 4 ? 1 : n <= 8 ? 2 : 4;
+    const size_t per_wave = size_t(p.seq_chunks) * 1024 + size_t(4 * kxi) * kXRow;
+    const size_t seq_lds = 16 + size_t(p.waves) * per_wave;
+    switch (p.seq_segs) {
+      case 1: launch_seq_ns<1>(p.seq_chunks, kxi, grid, block, seq_lds, s, a); break;
+      case 2: launch_seq_ns<2>(p.seq_chunks, kxi, grid, block, seq_lds, s, a); break;
+      case 3: launch_seq_ns<3>(p.seq_chunks, kxi, grid, block, seq_lds, s, a); break;
+      case 4: launch_seq_ns<4>(p.seq_chunks, kxi, grid, block, seq_lds, s, a); break;
+      case 6: launch_seq_ns<6>(p.seq_chunks, kxi, grid, block, seq_lds, s, a); break;
+      default: launch_seq_ns<8>(p.seq_chunks, kxi, grid, block, seq_lds, s, a); break;
+    }
+    return hipGetLastError();
+  }
   if (!vec) {
     if (skip) hipLaunchKernelGGL((decode_kernel<8, true, false>), grid, block, lds, s, a);
     else hipLaunchKernelGGL((decode_kernel<8, false, false>), grid, block, lds, s, a);

@@ -9,7 +9,7 @@
 
 namespace swm {
 
-// Device memory of one SWM-TCB v1 handle (TM = 64).
+// Device memory of one SWM-TCB v2 handle (16-row tiles).
 struct DevFormat {
   Header h;
   const uint32_t* tile_ptr = nullptr;  // mt*kt + 1
@@ -27,6 +27,8 @@ struct DecodePlan {
   int tiles_per_wave = 1;  // consecutive tiles of the slab per wave
   int seg_tiles = 4;       // tiles per streamed segment
   int seg_chunks = 1;      // 1 KiB loads per segment (covers the largest segment)
+  int seq_segs = 0;        // straight-line kernel: two-tile segments per wave (0 = not used)
+  int seq_chunks = 1;      // 1 KiB loads per two-tile segment
   int splits = 1;
 };
 

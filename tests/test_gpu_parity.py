@@ -131,6 +131,25 @@ def test_ragged_shapes(gpu_lib, M, K, N):
     assert_close(Y, oracle.masked_matmul(W, mask, X), f"{M}x{K}x{N}")
 
 
+# Decode schedules: K sets the tiles per wave (segments of two tiles per wave:
+# 1, 2, 3, 4, 6, 8; odd counts end on a one-tile segment, K % 64 != 0 ends on
+# a partial tile) and the sparsity sets how many 1 KiB loads a segment needs.
+@pytest.mark.parametrize("K,s,N", [
+    (2048, 0.5, 1), (4096, 0.5, 16), (4104, 0.5, 3), (6144, 0.8, 7), (8192, 0.0, 16), (8192, 1.0, 2),
+    (11008, 0.5, 4), (11008, 0.3, 16), (16384, 0.5, 1), (16384, 0.05, 9), (1024, 0.5, 16), (520, 0.5, 5),
+])
+def test_decode_schedules(gpu_lib, K, s, N):
+    swm = gpu_lib
+    M = 40
+    W, mask = wl.pruned_weight(96, K // 8 + int(100 * s), M, K, s)
+    X = np.random.default_rng(K + N).standard_normal((N, K)).astype(np.float16)
+    f = _compress(swm, W, mask)
+    Y = _np(swm.spmm(f, _t(X)))
+    assert_close(Y, oracle.masked_matmul(W, mask, X), f"{M}x{K}x{N} s={s}")
+    if s == 1.0:
+        assert np.all(Y == 0)
+
+
 def test_strided_activations_and_outputs(gpu_lib):
     import torch
     swm = gpu_lib
