@@ -87,6 +87,22 @@ def rotating_dense(torch, W, min_bytes=ROTATE_BYTES):
     return [Wd] + [Wd.clone() for _ in range(copies - 1)]
 
 
+def profiled_traffic(profile_md):
+    """HBM bytes per launch from a committed counter summary, if the kernel
+    source it was taken on is the one built now; else None."""
+    import hashlib
+    import re
+    try:
+        text = open(os.path.join(ROOT, "profiles", profile_md)).read()
+        meta = json.loads(re.search(r"<!-- bench-traffic: (\{.*\}) -->", text).group(1))
+        src = open(os.path.join(ROOT, meta["source"]), "rb").read()
+    except (OSError, AttributeError, ValueError, KeyError):
+        return None
+    if hashlib.sha256(src).hexdigest() != meta["source_sha256"]:
+        return None
+    return int(meta["traffic_bytes_per_launch"])
+
+
 def threads_used():
     try:
         from threadpoolctl import threadpool_info
@@ -177,8 +193,9 @@ def bench_decode(args, torch, swm, wl, G):
         "dense_ms_per_step": ms_dense / args.steps,
         "detail": detail,
         "roofline": {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": ach / HBM_PEAK_GBS, "traffic": None,
-                     "kernel": "decode_kernel, N=16", "alg_bytes_per_launch": alg[dom],
+                     "frac": ach / HBM_PEAK_GBS,
+                     "traffic": profiled_traffic("decode_seq_kernel_qproj_pmc.md"),
+                     "kernel": "decode_seq_kernel, N=16", "alg_bytes_per_launch": alg[dom],
                      "avg_launch_us": per_n[dom] * 1e3},
         "timed_wall_s": wall,
     }
@@ -288,12 +305,27 @@ def bench_layer(args, torch, swm, wl, G):
     return out
 
 
+# ------------------------------------------------------------------ copy calibration
+def bench_calib(args, torch, swm, wl, G):
+    """A plain device copy of known size: its FETCH_SIZE / WRITE_SIZE counter
+    readings scale the counters of the other kernels to bytes."""
+    nbytes = 256 << 20
+    src = torch.empty(nbytes // 4, dtype=torch.int32, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    t = G.time(G.capture([lambda: dst.copy_(src)] * 5), 3) / 5
+    return {"metric": "device copy bandwidth (read + write)", "value": 2 * nbytes / (t * 1e-3) / 1e9,
+            "unit": "GB/s", "n_gpus": 1, "higher_is_better": True, "dtype": "i32", "data": "synthetic",
+            "config": {"workload": f"copy of {nbytes} bytes, 5 per graph replay"}}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="decode", choices=["decode", "spmspv", "prefill", "layer"])
+    ap.add_argument("--workload", default="decode", choices=["decode", "spmspv", "prefill", "layer", "calib"])
     ap.add_argument("--tau", type=float, default=0.3)
     ap.add_argument("--prefill-n", default="512,2048,4096")
     ap.add_argument("--prefill-s", default="0.5,0.6,0.7")
@@ -309,7 +341,8 @@ def main():
     swm.load()
     torch.cuda.set_device(0)
     G = Graphs(torch)
-    fn = {"decode": bench_decode, "spmspv": bench_spmspv, "prefill": bench_prefill, "layer": bench_layer}
+    fn = {"decode": bench_decode, "spmspv": bench_spmspv, "prefill": bench_prefill, "layer": bench_layer,
+          "calib": bench_calib}
     out = fn[args.workload](args, torch, swm, wl, G)
     out.setdefault("n_gpus", 1)
     print(json.dumps(out), flush=True)
