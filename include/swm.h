@@ -155,10 +155,15 @@ swm_status swm_decompress(const swm_format* f, void* W_dev, int64_t ldw, void* s
 swm_status swm_spmm(const swm_format* f, const void* X, int64_t ldx, void* Y, int64_t ldy,
                     int64_t N, void* stream);
 
-/* spmspv: as swm_spmm for 1 <= n <= 16 tokens, skipping every input channel
- * k with x[t][k] == 0 (+0 or -0) for all tokens t: its weight column is
- * neither fetched nor decoded.  Same result as swm_spmm up to fp32 summation
- * order (skipped terms are exact zeros for finite inputs).
+/* spmspv: as swm_spmm for 1 <= n <= 16 tokens, for activations with zero
+ * input channels (x[t][k] == +0 or -0 for all tokens t).  Such channels
+ * contribute exact zeros, so the result equals swm_spmm's up to fp32
+ * summation order.  Skipping is applied only where it pays: on the aligned
+ * path (K % 8 == 0, 16-byte aligned x, ldx % 8 == 0) the full product is
+ * computed, because a 16-row tile stores each column in at most 32 bytes and
+ * packs four columns into each bitmap word, so dropping inactive columns
+ * saves neither fetches nor decode work; the unaligned path skips the decode
+ * of bitmap words whose four columns are all inactive.
  * Source: SPDP abstract (input-adaptive dynamic pruning; run-time activation
  * skipping in the spMspV kernel); "Reduced Matrix Multiplication" blog page,
  * Sec. 4.2 (an FFN down projection multiplies only the kept channels). */

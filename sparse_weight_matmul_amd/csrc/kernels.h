@@ -65,7 +65,7 @@ hipError_t launch_prefill_dense(const uint16_t* W, int64_t ldw, const uint16_t* 
                                 hipStream_t s);
 hipError_t launch_prefill_sparse(const DevFormat& f, const uint16_t* X, int64_t ldx, uint16_t* Y,
                                  int64_t ldy, int64_t N, hipStream_t s);
-// The prefill kernels need K % 8 == 0, ldx % 8 == 0 and a 16-byte aligned X.
+// The prefill kernels need K >= 8, K % 8 == 0, ldx % 8 == 0 and a 16-byte aligned X.
 bool prefill_supported(int64_t K, int64_t ldx, const void* X);
 size_t prefill_sparse_lds(const Header& h);
 

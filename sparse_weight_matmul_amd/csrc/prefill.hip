@@ -1,5 +1,5 @@
 // Prefill-regime kernels (large N): Y = W X on the matrix cores, with W
-// either dense (the in-house baseline) or expanded on chip from the SWM-TCB v1
+// either dense (the in-house baseline) or expanded on chip from the SWM-TCB v2
 // format, tile by tile, into the same LDS operand layout.
 //
 // Method: "Unified Static-Dynamic Pruning for Efficient LLM Inference" (SPDP),
@@ -15,14 +15,23 @@
 // own a 128 x 128 sub-block = 4 x 4 v_mfma_f32_32x32x16_f16 accumulators (256
 // fp32 per lane, in AGPRs).  A and B tiles (256 x 64 fp16 each) are double
 // buffered in LDS with an XOR swizzle of the 16-byte chunks (row r, chunk c at
-// chunk c ^ (r & 7)) so that the 16-byte fragment reads of eight consecutive
-// rows hit distinct banks without padding.  Next step's tiles are fetched into
-// VGPRs while the current step's 64 products issue.  In the sparse variant each
-// wave expands one 64 x 64 weight tile per step (the decode kernel's bitmap
-// rank scheme, then one 16-byte LDS store per 8 columns), interleaved with
-// the products of the current step.  The workgroup-to-tile map is XCD aware:
-// consecutive workgroup ids go to different XCDs, so ids are regrouped to give
-// each XCD a contiguous band of output tiles that share weight rows in its L2.
+// chunk c ^ (r & 7)), so the 16-byte fragment reads of eight consecutive rows
+// hit distinct banks without padding.  Inside a step the fragments of the next
+// 16-column slice are read while the current slice's 16 products issue, and
+// the next step's global tiles are in flight in VGPRs.  All global loads are
+// unconditional: rows past M and tokens past N read a clamped valid row (their
+// outputs are never stored) and activations past K read as zero.
+//
+// Sparse variant: at step k each wave expands the four 16 x 64 weight tiles
+// it owns for step k+1 (slabs m0/16 + 4 wave + tt, tt = 0..3) into the other
+// A stage, two expansion units (8 bitmap words -> one 16-byte store per lane)
+// per 16-column slice, interleaved with the products.  The tiles' packed runs
+// and bitmap words travel by vector loads two steps ahead; the runs are copied
+// to a per-wave LDS buffer and the words moved to SGPRs with v_readlane, so
+// the loop never waits on the scalar memory path.  The workgroup-to-tile map
+// is XCD aware: consecutive workgroup ids go to different XCDs, so ids are
+// regrouped to give each XCD a contiguous band of output tiles that share
+// weight rows in its L2.
 #include <hip/hip_runtime.h>
 
 #include "kernels.h"
@@ -34,11 +43,13 @@ typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-typedef __attribute__((address_space(3))) _Float16 lds_f16;
 typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+typedef __attribute__((address_space(3))) u32x2 lds_u32x2;
+typedef __attribute__((address_space(3))) uint16_t lds_u16;
 
 constexpr int BM = 256, BN = 256, BK = 64;
 constexpr int kTileBytes = BM * BK * 2;  // 32 KiB per operand stage
+constexpr int kRunChunksMax = 4;         // 512-byte chunks per 16x64 tile run (<= 1024 values)
 
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p));
@@ -49,23 +60,48 @@ __device__ __forceinline__ void lds_store16(uint32_t addr, u32x4 v) {
 __device__ __forceinline__ u32x4 lds_load16(uint32_t addr) {
   return *reinterpret_cast<const lds_u32x4*>(static_cast<uintptr_t>(addr));
 }
-__device__ __forceinline__ _Float16 lds_half(uint32_t addr) {
-  return *reinterpret_cast<const lds_f16*>(static_cast<uintptr_t>(addr));
-}
 // Byte offset of (row, 16-byte chunk) in a swizzled 256 x 64 fp16 tile.
 __device__ __forceinline__ uint32_t swz(int row, int chunk) {
   return uint32_t(row * 128 + ((chunk ^ (row & 7)) << 4));
 }
 
-__device__ __forceinline__ uint32_t run_addr(uint64_t word, uint32_t run_base, uint32_t zero_addr) {
-  const uint32_t rank =
-      __builtin_amdgcn_mbcnt_hi(uint32_t(word >> 32), __builtin_amdgcn_mbcnt_lo(uint32_t(word), 0u));
-  uint32_t a;
-  asm("v_lshl_add_u32 %0, %1, 1, %2\n\t"
-      "v_cndmask_b32_e64 %0, %3, %0, %4"
-      : "=&v"(a)
-      : "v"(rank), "s"(run_base), "v"(zero_addr), "s"(word));
-  return a;
+// Eight bitmap words (SGPR pairs) of one 32-column step of a 16 x 64 tile ->
+// this lane's row l%16, columns 32s + 8(l/16) .. +7, packed as eight fp16.
+// `base` is the LDS byte address of word 0's run and advances past the step.
+// Per pair of words: lanes read the halfword at their rank (lanes whose bit is
+// clear read a neighbour), one v_cndmask zeroes the low half and an SDWA
+// v_cndmask zeroes and packs the high half.
+__device__ __forceinline__ u32x4 expand_step(const uint64_t (&w)[8], uint32_t& base) {
+  u32x4 out;
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const uint64_t w0 = w[2 * p], w1 = w[2 * p + 1];
+    const uint32_t r0 = __builtin_amdgcn_mbcnt_hi(uint32_t(w0 >> 32), __builtin_amdgcn_mbcnt_lo(uint32_t(w0), 0u));
+    const uint32_t r1 = __builtin_amdgcn_mbcnt_hi(uint32_t(w1 >> 32), __builtin_amdgcn_mbcnt_lo(uint32_t(w1), 0u));
+    uint32_t b1, b2, c0, c1, a0, a1;
+    asm("s_bcnt1_i32_b64 %2, %4\n\t"
+        "s_lshl1_add_u32 %0, %2, %6\n\t"
+        "s_bcnt1_i32_b64 %3, %5\n\t"
+        "s_lshl1_add_u32 %1, %3, %0"
+        : "=&s"(b1), "=&s"(b2), "=&s"(c0), "=&s"(c1)
+        : "s"(w0), "s"(w1), "s"(base)
+        : "scc");
+    asm("v_lshl_add_u32 %0, %1, 1, %2" : "=v"(a0) : "v"(r0), "s"(base));
+    asm("v_lshl_add_u32 %0, %1, 1, %2" : "=v"(a1) : "v"(r1), "s"(b1));
+    const uint32_t d0 = *reinterpret_cast<const lds_u16*>(static_cast<uintptr_t>(a0));
+    const uint32_t d1 = *reinterpret_cast<const lds_u16*>(static_cast<uintptr_t>(a1));
+    base = b2;
+    uint32_t v;
+    asm("v_cndmask_b32_e64 %0, 0, %1, %3\n\t"
+        "s_mov_b64 vcc, %4\n\t"
+        "v_cndmask_b32_sdwa %0, 0, %2, vcc dst_sel:WORD_1 dst_unused:UNUSED_PRESERVE src0_sel:DWORD "
+        "src1_sel:WORD_0"
+        : "=&v"(v)
+        : "v"(d0), "v"(d1), "s"(w0), "s"(w1)
+        : "vcc");
+    out[p] = v;
+  }
+  return out;
 }
 
 struct PrefillArgs {
@@ -77,7 +113,7 @@ struct PrefillArgs {
   uint16_t* Y;
   int64_t ldw, ldx, ldy;
   int M, N, K;
-  int tiles_m, tiles_n, kt;
+  int tiles_m, tiles_n, kt, mt;
   int group_m;     // output-tile rows per L2 group
   int run_chunks;  // 512-byte run chunks per tile (1..4), sparse variant
 };
@@ -111,100 +147,107 @@ __global__ __launch_bounds__(256, 1) void prefill_kernel(PrefillArgs a) {
   const int wm = wave >> 1, wn = wave & 1;
   const int m0 = tm * BM, n0 = tn * BN;
 
-  // LDS: A stages [2][32 KiB] | B stages [2][32 KiB] | zero (16 B) | run buffers
+  // LDS: A stages [2][32 KiB] | B stages [2][32 KiB] | sparse: per-wave run buffers
   const uint32_t sA = lds_addr(smem), sB = sA + 2 * kTileBytes;
-  const uint32_t zero_addr = sB + 2 * kTileBytes;
-  const uint32_t runbuf = zero_addr + 16 + uint32_t(wave) * 4u * uint32_t(a.run_chunks) * 512u;
-  if (kSparse && tid < 4) reinterpret_cast<uint32_t*>(smem + 4 * kTileBytes)[tid] = 0u;
+  const uint32_t tile_run_bytes = uint32_t(a.run_chunks) * 512u;
+  const uint32_t runbuf = sB + 2 * kTileBytes + uint32_t(wave) * 4u * tile_run_bytes;
 
   // Global fetch map: thread -> (row r*32 + tid/8, chunk tid%8), r = 0..7.
   const int frow = tid >> 3, fch = tid & 7;
   const int nsteps = (a.K + BK - 1) / BK;
 
+  // B: tokens past N read token N-1 (never stored); columns past K read 0.
+  const uint16_t* xrow[8];
+#pragma unroll
+  for (int r = 0; r < 8; ++r) xrow[r] = a.X + int64_t(min(n0 + r * 32 + frow, a.N - 1)) * a.ldx;
   u32x4 regA[8], regB[8];
-  u32x2 runreg[16];  // sparse: 4 tiles x up to 4 chunks of 8 bytes per lane
+  bool bvalid = true;  // the fetched B chunk lies inside K (zeroed at the store, not at the load)
   auto fetch_B = [&](int ks) {
     const int k = ks * BK + fch * 8;
+    const int kc = min(k, a.K - 8);
+    bvalid = k < a.K;
 #pragma unroll
-    for (int r = 0; r < 8; ++r) {
-      const int n = n0 + r * 32 + frow;
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (n < a.N && k < a.K) v = *reinterpret_cast<const u32x4*>(a.X + int64_t(n) * a.ldx + k);
-      regB[r] = v;
-    }
+    for (int r = 0; r < 8; ++r) regB[r] = *reinterpret_cast<const u32x4*>(xrow[r] + kc);
   };
   auto store_B = [&](int stage) {
 #pragma unroll
-    for (int r = 0; r < 8; ++r) lds_store16(sB + stage * kTileBytes + swz(r * 32 + frow, fch), regB[r]);
+    for (int r = 0; r < 8; ++r)
+      lds_store16(sB + stage * kTileBytes + swz(r * 32 + frow, fch), bvalid ? regB[r] : u32x4{0u, 0u, 0u, 0u});
   };
+  // Dense A: rows past M read row M-1 (never stored); columns past K are
+  // multiplied by zero activations.
   auto fetch_A_dense = [&](int ks) {
-    const int k = ks * BK + fch * 8;
+    const int kc = min(ks * BK + fch * 8, a.K - 8);
 #pragma unroll
     for (int r = 0; r < 8; ++r) {
-      const int m = m0 + r * 32 + frow;
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (m < a.M && k < a.K) v = *reinterpret_cast<const u32x4*>(a.W + int64_t(m) * a.ldw + k);
-      regA[r] = v;
+      const int m = min(m0 + r * 32 + frow, a.M - 1);
+      regA[r] = *reinterpret_cast<const u32x4*>(a.W + int64_t(m) * a.ldw + kc);
     }
   };
   auto store_A_dense = [&](int stage) {
 #pragma unroll
     for (int r = 0; r < 8; ++r) lds_store16(sA + stage * kTileBytes + swz(r * 32 + frow, fch), regA[r]);
   };
-  // Sparse: at step ks this wave expands the four 16x64 tiles (slabs
-  // m0/16 + 4*wave + tt, tile column ks), tt = 0..3, into A-stage rows
-  // 64*wave + 16*tt .. +15.  Their runs are staged in this wave's LDS run
-  // buffer in 512-byte chunks (8 bytes per lane), run_chunks per tile.
+
+  // Sparse: the wave's four tiles at step ks are slabs slab0 + tt (clamped to
+  // the last slab: rows past M are never stored), tile column ks.  Their tile
+  // pointers arrive by a vector load one step before the runs (lane 2tt + h
+  // holds pointer h of tile tt) and reach SGPRs with v_readlane.  Run chunks
+  // are 8 bytes per lane, clamped into the run; the 64 bitmap words are two
+  // dwords per lane (lane l of load h holds dword l%32 of tile 2h + l/32).
   const int slab0 = m0 / 16 + 4 * wave;
-  const uint32_t tile_run_bytes = uint32_t(a.run_chunks) * 512u;
-  auto fetch_A_run = [&](int ks) {
+  u32x2 runreg[4 * kRunChunksMax];
+  uint32_t wreg[2];
+  auto fetch_tp = [&](int ks) -> uint32_t {
+    const int j = lane & 7;
+    const uint64_t t = uint64_t(min(slab0 + (j >> 1), a.mt - 1)) * a.kt + min(ks, a.kt - 1) + (j & 1);
+    return a.tile_ptr[t];
+  };
+  auto fetch_A_sparse = [&](int ks, uint32_t tpv) {
 #pragma unroll
     for (int tt = 0; tt < 4; ++tt) {
-      if ((slab0 + tt) * 16 >= a.M) continue;
-      const uint64_t t = uint64_t(slab0 + tt) * a.kt + ks;
-      const uint32_t p0 = a.tile_ptr[t], p1 = a.tile_ptr[t + 1];
+      const uint32_t p0 = __builtin_amdgcn_readlane(tpv, 2 * tt);
+      const uint32_t p1 = __builtin_amdgcn_readlane(tpv, 2 * tt + 1);
       const uint32_t last = p1 > p0 + 4 ? p1 - 4 : p0;
 #pragma unroll
-      for (int c = 0; c < 4; ++c)
+      for (int c = 0; c < kRunChunksMax; ++c)
         if (c < a.run_chunks) {
           const uint32_t off = min(p0 + uint32_t(c * 256 + lane * 4), last);
-          runreg[tt * 4 + c] = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(a.vals + off));
+          runreg[tt * kRunChunksMax + c] = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(a.vals + off));
         }
     }
-  };
-  auto stage_A_run = [&]() {
 #pragma unroll
-    for (int tt = 0; tt < 4; ++tt) {
-      if ((slab0 + tt) * 16 >= a.M) continue;
-#pragma unroll
-      for (int c = 0; c < 4; ++c)
-        if (c < a.run_chunks)
-          *reinterpret_cast<__attribute__((address_space(3))) u32x2*>(
-              static_cast<uintptr_t>(runbuf + tt * tile_run_bytes + c * 512 + lane * 8)) = runreg[tt * 4 + c];
+    for (int h = 0; h < 2; ++h) {
+      const uint64_t t = uint64_t(min(slab0 + 2 * h + (lane >> 5), a.mt - 1)) * a.kt + min(ks, a.kt - 1);
+      wreg[h] = reinterpret_cast<const uint32_t*>(a.bits + t * 16)[lane & 31];
     }
+  };
+  auto stage_A_sparse = [&]() {
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+      for (int c = 0; c < kRunChunksMax; ++c)
+        if (c < a.run_chunks)
+          *reinterpret_cast<lds_u32x2*>(static_cast<uintptr_t>(runbuf + tt * tile_run_bytes + c * 512 + lane * 8)) =
+              runreg[tt * kRunChunksMax + c];
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
   };
-  // Expand step s (32 columns) of tile tt: eight words -> this lane's row
-  // l%16, columns 32s + 8(l/16) .. +7 -> one 16-byte store.  `base` walks the
-  // tile's run in LDS (bytes).
-  auto expand_unit = [&](int ks, int stage, int tt, int s, uint32_t& base) {
-    const int row = wave * 64 + tt * 16 + (lane & 15);
-    u32x4 out = {0u, 0u, 0u, 0u};
-    if ((slab0 + tt) * 16 < a.M) {
-      const uint64_t t = uint64_t(slab0 + tt) * a.kt + ks;
-      const uint64_t* tb = a.bits + t * 16 + 8 * s;
-      half8 h;
+  // Expansion unit u = 2 tt + s (tile tt, 32-column step s) of the staged
+  // tiles into A stage `stage`: rows 64 wave + 16 tt + l%16, chunk 4s + l/16.
+  uint32_t wsave[2];
+  auto expand_unit = [&](int stage, int u, uint32_t& base) {
+    const int tt = u >> 1, s2 = u & 1;
+    uint64_t w[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const uint64_t w = tb[e];
-        const uint32_t ad = run_addr(w, base, zero_addr);
-        base += 2u * uint32_t(__builtin_popcountll(w));
-        h[e] = lds_half(ad);
-      }
-      out = __builtin_bit_cast(u32x4, h);
+    for (int e = 0; e < 8; ++e) {
+      const int d = 32 * (tt & 1) + 2 * (8 * s2 + e);
+      const uint32_t lo = __builtin_amdgcn_readlane(wsave[tt >> 1], d);
+      const uint32_t hi = __builtin_amdgcn_readlane(wsave[tt >> 1], d + 1);
+      w[e] = uint64_t(lo) | (uint64_t(hi) << 32);
     }
-    lds_store16(sA + stage * kTileBytes + swz(row, 4 * s + (lane >> 4)), out);
+    const u32x4 out = expand_step(w, base);
+    lds_store16(sA + stage * kTileBytes + swz(wave * 64 + tt * 16 + (lane & 15), 4 * s2 + (lane >> 4)), out);
   };
 
   f32x16 acc[4][4];
@@ -215,19 +258,24 @@ __global__ __launch_bounds__(256, 1) void prefill_kernel(PrefillArgs a) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
-  // Prologue: stage 0.  Sparse runs are two steps deep: the run of step k+1
-  // is already in VGPRs when step k starts, the run of step k+2 is fetched
-  // during step k.
+  // Prologue: stage 0 complete in LDS; sparse runs of step 1 and tile
+  // pointers of step 2 in flight.
   fetch_B(0);
+  uint32_t tp_next = 0;  // sparse: tile pointers of step ks+2, loaded during step ks-1
   if constexpr (kSparse) {
-    __syncthreads();  // zero word visible
-    fetch_A_run(0);
-    stage_A_run();
-    for (int tt = 0; tt < 4; ++tt) {
-      uint32_t base = runbuf + uint32_t(tt) * tile_run_bytes;
-      for (int s2 = 0; s2 < 2; ++s2) expand_unit(0, 0, tt, s2, base);
+    const uint32_t tp0 = fetch_tp(0), tp1 = fetch_tp(1);
+    tp_next = fetch_tp(2);
+    fetch_A_sparse(0, tp0);
+    stage_A_sparse();
+    wsave[0] = wreg[0];
+    wsave[1] = wreg[1];
+    fetch_A_sparse(1, tp1);
+    uint32_t base = runbuf;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      if ((u & 1) == 0) base = runbuf + uint32_t(u >> 1) * tile_run_bytes;
+      expand_unit(0, u, base);
     }
-    if (nsteps > 1) fetch_A_run(1);
   } else {
     fetch_A_dense(0);
     store_A_dense(0);
@@ -239,36 +287,53 @@ __global__ __launch_bounds__(256, 1) void prefill_kernel(PrefillArgs a) {
     const int st = ks & 1;
     const bool more = ks + 1 < nsteps;
     if constexpr (kSparse) {
-      if (more) stage_A_run();
-      if (ks + 2 < nsteps) fetch_A_run(ks + 2);
-    }
-    if (more) {
-      fetch_B(ks + 1);
-      if constexpr (!kSparse) fetch_A_dense(ks + 1);
+      // runs and words of step ks+1 (loaded during step ks-1) -> LDS / SGPR source
+      if (more) {
+        stage_A_sparse();
+        wsave[0] = wreg[0];
+        wsave[1] = wreg[1];
+      }
+      if (more) fetch_B(ks + 1);
+      const uint32_t tp_cur = tp_next;
+      tp_next = fetch_tp(ks + 3);
+      fetch_A_sparse(ks + 2, tp_cur);
+    } else {
+      if (more) {
+        fetch_B(ks + 1);
+        fetch_A_dense(ks + 1);
+      }
     }
     const uint32_t aBase = sA + st * kTileBytes, bBase = sB + st * kTileBytes;
     uint32_t base = runbuf;
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      half8 fa[4], fb[4];
+    half8 fa[2][4], fb[2][4];
+    auto load_frags = [&](int kk, int slot) {
       const int ch = kk * 2 + (lane >> 5);
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        fa[i] = __builtin_bit_cast(half8, lds_load16(aBase + swz(wm * 128 + i * 32 + (lane & 31), ch)));
+        fa[slot][i] = __builtin_bit_cast(half8, lds_load16(aBase + swz(wm * 128 + i * 32 + (lane & 31), ch)));
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        fb[j] = __builtin_bit_cast(half8, lds_load16(bBase + swz(wn * 128 + j * 32 + (lane & 31), ch)));
+        fb[slot][j] = __builtin_bit_cast(half8, lds_load16(bBase + swz(wn * 128 + j * 32 + (lane & 31), ch)));
+    };
+    load_frags(0, 0);
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      const int sl = kk & 1;
+      // the next slice's fragments go out before this slice's products
+      __builtin_amdgcn_sched_barrier(0);
+      if (kk < 3) load_frags(kk + 1, sl ^ 1);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[sl][i], fb[sl][j], acc[i][j], 0, 0, 0);
         if constexpr (kSparse) {
-          // eight expansion units per step (tile tt = unit/2, step s = unit%2),
-          // one after every second product
+          // eight expansion units per step, one after every second row of products
           if (more && (i & 1)) {
-            const int unit = kk * 2 + (i >> 1), tt = unit >> 1, s2 = unit & 1;
-            if (s2 == 0) base = runbuf + uint32_t(tt) * tile_run_bytes;
-            expand_unit(ks + 1, st ^ 1, tt, s2, base);
+            const int u = kk * 2 + (i >> 1);
+            if ((u & 1) == 0) base = runbuf + uint32_t(u >> 1) * tile_run_bytes;
+            expand_unit(st ^ 1, u, base);
           }
         }
       }
@@ -329,12 +394,12 @@ unsigned grid_size(const PrefillArgs& a) {
 }  // namespace
 
 bool prefill_supported(int64_t K, int64_t ldx, const void* X) {
-  return (K % 8 == 0) && (ldx % 8 == 0) && ((reinterpret_cast<uintptr_t>(X) & 15) == 0);
+  return K >= 8 && (K % 8 == 0) && (ldx % 8 == 0) && ((reinterpret_cast<uintptr_t>(X) & 15) == 0);
 }
 
 size_t prefill_sparse_lds(const Header& h) {
   const size_t chunks = (size_t(h.max_tile) + 255) / 256;  // 512-byte chunks per tile run
-  return size_t(4) * kTileBytes + 16 + 4 /*waves*/ * 4 /*tiles*/ * (chunks ? chunks : 1) * 512;
+  return size_t(4) * kTileBytes + 4 /*waves*/ * 4 /*tiles*/ * (chunks ? chunks : 1) * 512;
 }
 
 hipError_t launch_prefill_dense(const uint16_t* W, int64_t ldw, const uint16_t* X, int64_t ldx,
@@ -344,6 +409,7 @@ hipError_t launch_prefill_dense(const uint16_t* W, int64_t ldw, const uint16_t* 
   a.W = W;
   a.ldw = ldw;
   if (a.tiles_m == 0 || a.tiles_n == 0) return hipSuccess;
+  if (K < 8 || K % 8 != 0) return hipErrorInvalidValue;
   const size_t lds = size_t(4) * kTileBytes;
   hipLaunchKernelGGL((prefill_kernel<false>), dim3(grid_size(a)), dim3(256), lds, s, a);
   return hipGetLastError();
@@ -356,9 +422,11 @@ hipError_t launch_prefill_sparse(const DevFormat& f, const uint16_t* X, int64_t 
   a.bits = f.bits;
   a.vals = f.vals;
   a.kt = int(f.h.kt);
+  a.mt = int(f.h.mt);
   a.run_chunks = int((f.h.max_tile + 255) / 256);
   if (a.run_chunks < 1) a.run_chunks = 1;
-  if (f.h.tm != 16 || f.h.tk != 64 || f.h.max_tile > 1024) return hipErrorInvalidValue;
+  if (f.h.tm != 16 || f.h.tk != 64 || f.h.max_tile > 1024 || f.h.k < 8 || f.h.k % 8 != 0)
+    return hipErrorInvalidValue;
   if (a.tiles_m == 0 || a.tiles_n == 0) return hipSuccess;
   const size_t lds = prefill_sparse_lds(f.h);
   if (lds > 160 * 1024) return hipErrorInvalidValue;
