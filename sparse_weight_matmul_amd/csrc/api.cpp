@@ -309,7 +309,8 @@ static swm_status run_products(const swm_format* f, const void* X, int64_t ldx, 
     SWM_HIP(swm::launch_decode(f->d, f->plan, x, ldx, y, ldy, int(N), skip, s));
     return SWM_OK;
   }
-  if (!skip && swm::prefill_supported(f->h.k, ldx, X) && swm::prefill_sparse_lds(f->h) <= 160 * 1024) {
+  if (!skip && swm::prefill_supported(f->h.k, ldx, X) && swm::prefill_sparse_lds(f->h) <= 160 * 1024 &&
+      swm::prefill_sparse_fits(f->h, N, ldx)) {
     SWM_HIP(swm::launch_prefill_sparse(f->d, x, ldx, y, ldy, N, s));
     return SWM_OK;
   }

@@ -69,5 +69,7 @@ hipError_t launch_prefill_sparse(const DevFormat& f, const uint16_t* X, int64_t 
 // The prefill kernels need K >= 8, K % 8 == 0, ldx % 8 == 0 and a 16-byte aligned X.
 bool prefill_supported(int64_t K, int64_t ldx, const void* X);
 size_t prefill_sparse_lds(const Header& h);
+// The sparse prefill kernel addresses X with 32-bit byte offsets.
+bool prefill_sparse_fits(const Header& h, int64_t N, int64_t ldx);
 
 }  // namespace swm

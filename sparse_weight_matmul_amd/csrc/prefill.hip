@@ -522,6 +522,230 @@ __global__ __launch_bounds__(256, 1) void prefill_kernel(PrefillArgs a) {
     }
 }
 
+// ------------------------------------------------------------------ sparse, warp-specialized
+// 512 threads: waves 0-3 are consumers, waves 4-7 producers, one of each per
+// SIMD, so that a SIMD issues a consumer's products and a producer's
+// expansion in the same cycles instead of one wave issuing both in turn.
+// The workgroup computes a 128 (rows of W) x 256 (tokens) block of Y.
+//   * consumer c owns tokens 64c .. 64c+63: 4 x 2 v_mfma_f32_32x32x16_f16
+//     accumulators (128 fp32 per lane).  The consumers also stream the 256 x
+//     64 activation tile of the next step into LDS, loads interleaved with
+//     the first half of the step's products and stores with the last slice.
+//   * producer p owns the two 16 x 64 weight tiles of slabs m0/16 + 2p, 2p+1:
+//     for each step it copies their runs (fetched two steps ahead) into its
+//     LDS buffer and expands them into the next A stage, one bitmap word at a
+//     time (rank by v_mbcnt, halfword read, v_cndmask / SDWA pack, 16-byte
+//     store).
+// One barrier per step: afterwards the next stage is complete (both
+// operands) and the current one is free.  The A stage is 128 x 64 fp16 with
+// the same 16-row XOR swizzle as the 256-row tiles.
+constexpr int WBM = 128, WBN = 256;
+constexpr int kWATile = WBM * BK * 2;  // 16 KiB
+constexpr int kWBTile = WBN * BK * 2;  // 32 KiB
+
+__device__ __forceinline__ bool tile_of_ws(const PrefillArgs& a, int& tm, int& tn) {
+  return tile_of(a, tm, tn);  // same XCD-aware walk; tiles_m counts 128-row tiles here
+}
+
+template <int kRC>
+__global__ __launch_bounds__(512, 1) void prefill_ws_kernel(PrefillArgs a) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  int tm, tn;
+  if (!tile_of_ws(a, tm, tn)) return;
+  const int tid = int(threadIdx.x);
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int m0 = tm * WBM, n0 = tn * WBN;
+  const int nsteps = (a.K + BK - 1) / BK;
+  constexpr uint32_t tile_run_bytes = uint32_t(kRC) * 512u;
+  const uint32_t sA = lds_addr(smem), sB = sA + 2 * kWATile;
+  const uint32_t runbase = sB + 2 * kWBTile;
+
+  if (wave < 4) {
+    // ---------------------------------------------------------------- consumer
+    const int c = wave;
+    const int frow = tid >> 3, fch = tid & 7;  // B fetch map over the 256 consumer threads
+    // 32-bit byte offsets into X (the launcher checks that X fits 4 GiB)
+    uint32_t xoff[8];
+#pragma unroll
+    for (int r = 0; r < 8; ++r) xoff[r] = 2u * uint32_t(min(n0 + r * 32 + frow, a.N - 1)) * uint32_t(a.ldx);
+    u32x4 regB[8];
+    auto fetch_B = [&](int ks) {
+      const uint32_t kc = 2u * uint32_t(min(ks * BK + fch * 8, a.K - 8));  // past K the weights are zero
+#pragma unroll
+      for (int r = 0; r < 8; ++r)
+        regB[r] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint8_t*>(a.X) + (xoff[r] + kc));
+    };
+    auto store_B = [&](int stage) {
+#pragma unroll
+      for (int r = 0; r < 8; ++r) lds_store16(sB + stage * kWBTile + swz(r * 32 + frow, fch), regB[r]);
+    };
+    f32x16 acc[4][2];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+
+    fetch_B(0);
+    store_B(0);
+    __syncthreads();  // stage 0 complete (the producers expanded its A)
+
+    for (int ks = 0; ks < nsteps; ++ks) {
+      const int st = ks & 1;
+      const int kn = min(ks + 1, nsteps - 1);
+      const uint32_t aBase = sA + st * kWATile, bBase = sB + st * kWBTile;
+      half8 fa[2][4], fb[2][2];
+      auto load_frags = [&](int kk, int slot) {
+        const int ch = kk * 2 + (lane >> 5);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          fa[slot][i] = __builtin_bit_cast(half8, lds_load16(aBase + swz(i * 32 + (lane & 31), ch)));
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          fb[slot][j] = __builtin_bit_cast(half8, lds_load16(bBase + swz(c * 64 + j * 32 + (lane & 31), ch)));
+      };
+      load_frags(0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        const int sl = kk & 1;
+        if (kk < 3) load_frags(kk + 1, sl ^ 1);
+        if (kk == 0) fetch_B(kn);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int j = 0; j < 2; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[sl][i], fb[sl][j], acc[i][j], 0, 0, 0);
+        if (kk == 3) store_B(st ^ 1);
+        __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);  // DS read: next fragments
+        if (kk == 0) {
+#pragma unroll
+          for (int q = 0; q < 8; ++q) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM read
+          }
+        } else if (kk == 3) {
+#pragma unroll
+          for (int q = 0; q < 8; ++q) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+            __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);  // DS write
+          }
+        } else {
+          __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      __syncthreads();
+    }
+
+    // Epilogue: fp16 round-to-nearest-even, 4 consecutive rows per 8-byte store.
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int n = n0 + c * 64 + j * 32 + (lane & 31);
+        if (n >= a.N) continue;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int m = m0 + i * 32 + q * 8 + (lane >> 5) * 4;
+          uint16_t h[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) h[e] = __builtin_bit_cast(uint16_t, _Float16(acc[i][j][q * 4 + e]));
+          uint16_t* dst = a.Y + int64_t(n) * a.ldy + m;
+          if (m + 3 < a.M && ((reinterpret_cast<uintptr_t>(dst) & 7) == 0)) {
+            u32x2 pk = {uint32_t(h[0]) | (uint32_t(h[1]) << 16), uint32_t(h[2]) | (uint32_t(h[3]) << 16)};
+            *reinterpret_cast<u32x2*>(dst) = pk;
+          } else {
+            for (int e = 0; e < 4; ++e)
+              if (m + e < a.M) dst[e] = h[e];
+          }
+        }
+      }
+  } else {
+    // ---------------------------------------------------------------- producer
+    const int pw = wave - 4;
+    const int slab0 = m0 / 16 + 2 * pw;  // tiles tt = 0, 1: slabs slab0 + tt (clamped: rows past M unused)
+    const uint32_t runbuf = runbase + uint32_t(pw) * 2u * tile_run_bytes;
+    u32x2 runreg[2 * kRC];
+    uint32_t wreg = 0, wsave = 0;  // lane l: dword l%32 of tile l/32's 16 bitmap words
+    // tile pointers: lane 2tt + h holds pointer h of tile tt (clamped step)
+    auto fetch_tp = [&](int ks) -> uint32_t {
+      const int j = lane & 3;
+      const uint64_t t = uint64_t(min(slab0 + (j >> 1), a.mt - 1)) * a.kt + min(ks, a.kt - 1) + (j & 1);
+      return a.tile_ptr[t];
+    };
+    auto fetch_runs = [&](int ks, uint32_t tpv) {
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+        const uint32_t p0 = __builtin_amdgcn_readlane(tpv, 2 * tt);
+        const uint32_t p1 = __builtin_amdgcn_readlane(tpv, 2 * tt + 1);
+        const uint32_t last = p1 > p0 + 4 ? p1 - 4 : p0;
+#pragma unroll
+        for (int cc = 0; cc < kRC; ++cc) {
+          const uint32_t off = min(p0 + uint32_t(cc * 256 + lane * 4), last);
+          runreg[tt * kRC + cc] = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(a.vals + off));
+        }
+      }
+      const uint64_t t = uint64_t(min(slab0 + (lane >> 5), a.mt - 1)) * a.kt + min(ks, a.kt - 1);
+      wreg = reinterpret_cast<const uint32_t*>(a.bits + t * 16)[lane & 31];
+    };
+    auto stage_runs = [&]() {
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int cc = 0; cc < kRC; ++cc)
+          *reinterpret_cast<lds_u32x2*>(static_cast<uintptr_t>(runbuf + tt * tile_run_bytes + cc * 512 + lane * 8)) =
+              runreg[tt * kRC + cc];
+      wsave = wreg;
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+    };
+    // Expand the staged tiles (4 units: tile tt, 32-column step s) into A stage `stage`.
+    auto expand = [&](int stage) {
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+        uint32_t base = runbuf + uint32_t(tt) * tile_run_bytes;
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2) {
+          uint64_t w[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int d = 32 * tt + 2 * (8 * s2 + e);
+            const uint32_t lo = __builtin_amdgcn_readlane(wsave, d);  // int: zero-extend via u32
+            const uint32_t hi = __builtin_amdgcn_readlane(wsave, d + 1);
+            w[e] = uint64_t(lo) | (uint64_t(hi) << 32);
+          }
+          const u32x4 out = expand_step(w, base);
+          lds_store16(sA + stage * kWATile + swz(pw * 32 + tt * 16 + (lane & 15), 4 * s2 + (lane >> 4)), out);
+        }
+      }
+    };
+
+    uint32_t tp_next = fetch_tp(2);
+    {
+      const uint32_t tp0 = fetch_tp(0), tp1 = fetch_tp(1);
+      fetch_runs(0, tp0);
+      stage_runs();
+      fetch_runs(1, tp1);
+    }
+    expand(0);
+    __syncthreads();  // stage 0 complete
+
+    for (int ks = 0; ks < nsteps; ++ks) {
+      const int st = ks & 1;
+      // runs/words of step ks+1 (fetched during step ks-1) -> LDS, then fetch step ks+2
+      stage_runs();
+      const uint32_t tp_cur = tp_next;
+      tp_next = fetch_tp(ks + 3);
+      fetch_runs(ks + 2, tp_cur);
+      expand(st ^ 1);  // the last step expands a clamped duplicate into the unused stage
+      __syncthreads();
+    }
+  }
+}
+
 PrefillArgs make_args(int64_t M, int64_t N, int64_t K, const uint16_t* X, int64_t ldx, uint16_t* Y,
                       int64_t ldy) {
   PrefillArgs a{};
@@ -549,9 +773,13 @@ bool prefill_supported(int64_t K, int64_t ldx, const void* X) {
   return K >= 8 && (K % 8 == 0) && (ldx % 8 == 0) && ((reinterpret_cast<uintptr_t>(X) & 15) == 0);
 }
 
+bool prefill_sparse_fits(const Header& h, int64_t N, int64_t ldx) {
+  return 2 * ((N - 1) * ldx + h.k) < (int64_t(1) << 32);  // 32-bit activation offsets
+}
+
 size_t prefill_sparse_lds(const Header& h) {
   const size_t chunks = (size_t(h.max_tile) + 255) / 256;  // 512-byte chunks per tile run
-  return size_t(4) * kTileBytes + 4 /*waves*/ * 4 /*tiles*/ * (chunks ? chunks : 1) * 512;
+  return size_t(2) * kWATile + size_t(2) * kWBTile + 4 /*producers*/ * 2 /*tiles*/ * (chunks ? chunks : 1) * 512;
 }
 
 hipError_t launch_prefill_dense(const uint16_t* W, int64_t ldw, const uint16_t* X, int64_t ldx,
@@ -582,11 +810,15 @@ hipError_t launch_prefill_sparse(const DevFormat& f, const uint16_t* X, int64_t 
   if (a.tiles_m == 0 || a.tiles_n == 0) return hipSuccess;
   const size_t lds = prefill_sparse_lds(f.h);
   if (lds > 160 * 1024) return hipErrorInvalidValue;
+  if (!prefill_sparse_fits(f.h, N, ldx)) return hipErrorInvalidValue;
+  a.tiles_m = int((f.h.m + WBM - 1) / WBM);
+  a.tiles_n = int((N + WBN - 1) / WBN);
+  const dim3 grid{grid_size(a), 1, 1}, block{512, 1, 1};
   switch (a.run_chunks) {
-    case 1: hipLaunchKernelGGL((prefill_kernel<true, 1>), dim3(grid_size(a)), dim3(256), lds, s, a); break;
-    case 2: hipLaunchKernelGGL((prefill_kernel<true, 2>), dim3(grid_size(a)), dim3(256), lds, s, a); break;
-    case 3: hipLaunchKernelGGL((prefill_kernel<true, 3>), dim3(grid_size(a)), dim3(256), lds, s, a); break;
-    default: hipLaunchKernelGGL((prefill_kernel<true, 4>), dim3(grid_size(a)), dim3(256), lds, s, a); break;
+    case 1: hipLaunchKernelGGL((prefill_ws_kernel<1>), grid, block, lds, s, a); break;
+    case 2: hipLaunchKernelGGL((prefill_ws_kernel<2>), grid, block, lds, s, a); break;
+    case 3: hipLaunchKernelGGL((prefill_ws_kernel<3>), grid, block, lds, s, a); break;
+    default: hipLaunchKernelGGL((prefill_ws_kernel<4>), grid, block, lds, s, a); break;
   }
   return hipGetLastError();
 }
