@@ -34,6 +34,9 @@
 // weight rows in its L2.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
+#include <cstdlib>
+
 #include "kernels.h"
 
 namespace swm {
@@ -523,35 +526,32 @@ __global__ __launch_bounds__(256, 1) void prefill_kernel(PrefillArgs a) {
 }
 
 // ------------------------------------------------------------------ sparse, warp-specialized
-// 512 threads: waves 0-3 are consumers, waves 4-7 producers, one of each per
-// SIMD, so that a SIMD issues a consumer's products and a producer's
-// expansion in the same cycles instead of one wave issuing both in turn.
-// The workgroup computes a 128 (rows of W) x 256 (tokens) block of Y.
-//   * consumer c owns tokens 64c .. 64c+63: 4 x 2 v_mfma_f32_32x32x16_f16
-//     accumulators (128 fp32 per lane).  The consumers also stream the 256 x
-//     64 activation tile of the next step into LDS, loads interleaved with
-//     the first half of the step's products and stores with the last slice.
-//   * producer p owns the two 16 x 64 weight tiles of slabs m0/16 + 2p, 2p+1:
-//     for each step it copies their runs (fetched two steps ahead) into its
-//     LDS buffer and expands them into the next A stage, one bitmap word at a
-//     time (rank by v_mbcnt, halfword read, v_cndmask / SDWA pack, 16-byte
-//     store).
-// One barrier per step: afterwards the next stage is complete (both
-// operands) and the current one is free.  The A stage is 128 x 64 fp16 with
-// the same 16-row XOR swizzle as the 256-row tiles.
+// 512 threads, eight waves, two per SIMD; the workgroup computes a 128 (rows
+// of W) x 256 (tokens) block of Y.  Every wave expands one 16 x 64 weight
+// tile per step (slab m0/16 + wave) into the next A stage; on top of that
+//   * waves 0-3 (consumers) issue the products: consumer c owns tokens
+//     64c .. 64c+63, 4 x 2 v_mfma_f32_32x32x16_f16 accumulators (128 fp32 per
+//     lane).  Their expansion is spread one bitmap word per two products, so
+//     it issues in the shadow of the matrix pipe;
+//   * waves 4-7 (producers) stream the activations: the 256 x 64 tile of
+//     step ks+1 is loaded during step ks-1 and stored into the free B stage
+//     after the expansion.
+// The expansion of a bitmap word is lane-parallel: each lane's rank by
+// v_mbcnt, a halfword read at run base + 2 rank, and later a v_cndmask /
+// SDWA v_cndmask that zeroes and packs two words' halves into one dword; a
+// 16-byte store per 8 words.  Runs are fetched two steps ahead and copied
+// into the wave's LDS buffer one step ahead.  One barrier per step:
+// afterwards the next stage is complete (both operands) and the current one
+// is free.  Both stages use the 16-row XOR swizzle of the dense kernel.
 constexpr int WBM = 128, WBN = 256;
 constexpr int kWATile = WBM * BK * 2;  // 16 KiB
 constexpr int kWBTile = WBN * BK * 2;  // 32 KiB
-
-__device__ __forceinline__ bool tile_of_ws(const PrefillArgs& a, int& tm, int& tn) {
-  return tile_of(a, tm, tn);  // same XCD-aware walk; tiles_m counts 128-row tiles here
-}
 
 template <int kRC>
 __global__ __launch_bounds__(512, 1) void prefill_ws_kernel(PrefillArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   int tm, tn;
-  if (!tile_of_ws(a, tm, tn)) return;
+  if (!tile_of(a, tm, tn)) return;  // tiles_m / tiles_n count 128 x 256 blocks
   const int tid = int(threadIdx.x);
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -559,27 +559,129 @@ __global__ __launch_bounds__(512, 1) void prefill_ws_kernel(PrefillArgs a) {
   const int nsteps = (a.K + BK - 1) / BK;
   constexpr uint32_t tile_run_bytes = uint32_t(kRC) * 512u;
   const uint32_t sA = lds_addr(smem), sB = sA + 2 * kWATile;
-  const uint32_t runbase = sB + 2 * kWBTile;
+  const uint32_t runbuf = sB + 2 * kWBTile + uint32_t(wave) * tile_run_bytes;
 
-  if (wave < 4) {
+  // ---- the wave's weight tile: slab m0/16 + wave (clamped to the last slab:
+  // rows past M are never stored), tile column ks (clamped: the last step
+  // expands a duplicate into the unused stage).
+  const int slab = min(m0 / 16 + wave, a.mt - 1);
+  u32x2 runreg[kRC];
+  uint32_t wreg = 0, wsave = 0;  // lane l: dword l%32 of the tile's 16 bitmap words
+  // tile pointers: lane 0 / 1 hold the run's first / one-past-last index
+  auto fetch_tp = [&](int ks) -> uint32_t {
+    return a.tile_ptr[uint64_t(slab) * a.kt + min(ks, a.kt - 1) + (lane & 1)];
+  };
+  auto fetch_runs = [&](int ks, uint32_t tpv) {
+    const uint32_t p0 = __builtin_amdgcn_readlane(tpv, 0);
+    const uint32_t p1 = __builtin_amdgcn_readlane(tpv, 1);
+    const uint32_t last = p1 > p0 + 4 ? p1 - 4 : p0;
+#pragma unroll
+    for (int cc = 0; cc < kRC; ++cc) {
+      const uint32_t off = min(p0 + uint32_t(cc * 256 + lane * 4), last);
+      runreg[cc] = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(a.vals + off));
+    }
+    wreg = reinterpret_cast<const uint32_t*>(a.bits + (uint64_t(slab) * a.kt + min(ks, a.kt - 1)) * 16)[lane & 31];
+  };
+  auto stage_runs = [&]() {
+#pragma unroll
+    for (int cc = 0; cc < kRC; ++cc)
+      *reinterpret_cast<lds_u32x2*>(static_cast<uintptr_t>(runbuf + cc * 512 + lane * 8)) = runreg[cc];
+    wsave = wreg;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+  };
+  // Word g (0..15) of the staged tile: bitmap word to SGPRs, lane rank, run
+  // address, halfword read; `base` walks the run.
+  struct Word {
+    uint64_t w;
+    uint32_t d;
+  };
+  auto issue_word = [&](int g, uint32_t& base, Word& x) {
+    const uint32_t lo = __builtin_amdgcn_readlane(wsave, 2 * g);  // int: zero-extend via u32
+    const uint32_t hi = __builtin_amdgcn_readlane(wsave, 2 * g + 1);
+    x.w = uint64_t(lo) | (uint64_t(hi) << 32);
+    const uint32_t r = __builtin_amdgcn_mbcnt_hi(hi, __builtin_amdgcn_mbcnt_lo(lo, 0u));
+    uint32_t nb, c, ad;
+    asm("s_bcnt1_i32_b64 %1, %2\n\t"
+        "s_lshl1_add_u32 %0, %1, %3"
+        : "=&s"(nb), "=&s"(c)
+        : "s"(x.w), "s"(base)
+        : "scc");
+    asm("v_lshl_add_u32 %0, %1, 1, %2" : "=v"(ad) : "v"(r), "s"(base));
+    x.d = *reinterpret_cast<const lds_u16*>(static_cast<uintptr_t>(ad));
+    base = nb;
+  };
+  // Pair p (words 2p, 2p+1): zero / pack into dword p%4 of unit p/4 (32-column
+  // step s = p/4: rows 16 wave + l%16, chunk 4 s + l/16); store after p%4 = 3.
+  auto finish_pair = [&](int stage, int p, const Word& x0, const Word& x1, u32x4& out) {
+    uint32_t v;
+    asm("v_cndmask_b32_e64 %0, 0, %1, %3\n\t"
+        "s_mov_b64 vcc, %4\n\t"
+        "v_cndmask_b32_sdwa %0, 0, %2, vcc dst_sel:WORD_1 dst_unused:UNUSED_PRESERVE src0_sel:DWORD "
+        "src1_sel:WORD_0"
+        : "=&v"(v)
+        : "v"(x0.d), "v"(x1.d), "s"(x0.w), "s"(x1.w)
+        : "vcc");
+    out[p & 3] = v;
+    if ((p & 3) == 3)
+      lds_store16(sA + stage * kWATile + swz(wave * 16 + (lane & 15), 4 * (p >> 2) + (lane >> 4)), out);
+  };
+  // Whole-tile expansion with one pair of reads in flight ahead of each finish.
+  auto expand_all = [&](int stage) {
+    Word x[16];
+    u32x4 out;
+    uint32_t base = runbuf;
+#pragma unroll
+    for (int g = 0; g < 16; ++g) {
+      issue_word(g, base, x[g]);
+      if ((g & 1) && g >= 3) finish_pair(stage, (g - 3) >> 1, x[g - 3], x[g - 2], out);
+    }
+    finish_pair(stage, 7, x[14], x[15], out);
+  };
+
+  // ---- producers: activations.  Thread pt moves 16-byte chunk pt%8 of rows
+  // 32 r + pt/8 (tokens past N read token N-1; never stored).  32-bit byte
+  // offsets into X (the launcher checks that X fits 4 GiB).
+  const bool producer = wave >= 4;
+  const int pt = tid - 256;
+  const int frow = pt >> 3, fch = pt & 7;
+  uint32_t xoff[8];
+  u32x4 regB[8];
+  auto fetch_B = [&](int ks) {
+    const uint32_t kc = 2u * uint32_t(min(ks * BK + fch * 8, a.K - 8));  // past K the weights are zero
+#pragma unroll
+    for (int r = 0; r < 8; ++r)
+      regB[r] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint8_t*>(a.X) + (xoff[r] + kc));
+  };
+  auto store_B = [&](int stage) {
+#pragma unroll
+    for (int r = 0; r < 8; ++r) lds_store16(sB + stage * kWBTile + swz(r * 32 + frow, fch), regB[r]);
+  };
+
+  // ---- prologue: stage 0 complete in LDS; runs and activations of step 1
+  // and tile pointers of step 2 in flight.
+  uint32_t tp_next = fetch_tp(2);
+  {
+    const uint32_t tp0 = fetch_tp(0), tp1 = fetch_tp(1);
+    fetch_runs(0, tp0);
+    if (producer) {
+#pragma unroll
+      for (int r = 0; r < 8; ++r) xoff[r] = 2u * uint32_t(min(n0 + r * 32 + frow, a.N - 1)) * uint32_t(a.ldx);
+      fetch_B(0);
+    }
+    stage_runs();
+    fetch_runs(1, tp1);
+  }
+  expand_all(0);
+  if (producer) {
+    store_B(0);
+    fetch_B(min(1, nsteps - 1));
+  }
+  __syncthreads();
+
+  if (!producer) {
     // ---------------------------------------------------------------- consumer
     const int c = wave;
-    const int frow = tid >> 3, fch = tid & 7;  // B fetch map over the 256 consumer threads
-    // 32-bit byte offsets into X (the launcher checks that X fits 4 GiB)
-    uint32_t xoff[8];
-#pragma unroll
-    for (int r = 0; r < 8; ++r) xoff[r] = 2u * uint32_t(min(n0 + r * 32 + frow, a.N - 1)) * uint32_t(a.ldx);
-    u32x4 regB[8];
-    auto fetch_B = [&](int ks) {
-      const uint32_t kc = 2u * uint32_t(min(ks * BK + fch * 8, a.K - 8));  // past K the weights are zero
-#pragma unroll
-      for (int r = 0; r < 8; ++r)
-        regB[r] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint8_t*>(a.X) + (xoff[r] + kc));
-    };
-    auto store_B = [&](int stage) {
-#pragma unroll
-      for (int r = 0; r < 8; ++r) lds_store16(sB + stage * kWBTile + swz(r * 32 + frow, fch), regB[r]);
-    };
     f32x16 acc[4][2];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -588,55 +690,48 @@ __global__ __launch_bounds__(512, 1) void prefill_ws_kernel(PrefillArgs a) {
 #pragma unroll
         for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
-    fetch_B(0);
-    store_B(0);
-    __syncthreads();  // stage 0 complete (the producers expanded its A)
-
     for (int ks = 0; ks < nsteps; ++ks) {
       const int st = ks & 1;
-      const int kn = min(ks + 1, nsteps - 1);
       const uint32_t aBase = sA + st * kWATile, bBase = sB + st * kWBTile;
+      stage_runs();  // runs/words of step ks+1 (fetched during step ks-1)
+      const uint32_t tp_cur = tp_next;
+      tp_next = fetch_tp(ks + 3);
+      fetch_runs(ks + 2, tp_cur);
       half8 fa[2][4], fb[2][2];
-      auto load_frags = [&](int kk, int slot) {
+      auto load_frag = [&](int kk, int slot, int f) {
         const int ch = kk * 2 + (lane >> 5);
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          fa[slot][i] = __builtin_bit_cast(half8, lds_load16(aBase + swz(i * 32 + (lane & 31), ch)));
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-          fb[slot][j] = __builtin_bit_cast(half8, lds_load16(bBase + swz(c * 64 + j * 32 + (lane & 31), ch)));
+        if (f < 4)
+          fa[slot][f] = __builtin_bit_cast(half8, lds_load16(aBase + swz(f * 32 + (lane & 31), ch)));
+        else
+          fb[slot][f - 4] = __builtin_bit_cast(half8, lds_load16(bBase + swz(c * 64 + (f - 4) * 32 + (lane & 31), ch)));
       };
-      load_frags(0, 0);
+#pragma unroll
+      for (int f = 0; f < 6; ++f) load_frag(0, 0, f);
       __builtin_amdgcn_sched_barrier(0);
+      // Slot q of slice kk: product (q/2, q%2); the next slice's fragment q
+      // (q < 6); word 4 kk + q/2 on even q; on q = 3, 7 the finish of pair
+      // 2 (kk-1) + q/4, whose words were issued during the previous slice.
+      Word x[16];
+      u32x4 out;
+      uint32_t base = runbuf;
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
         const int sl = kk & 1;
-        if (kk < 3) load_frags(kk + 1, sl ^ 1);
-        if (kk == 0) fetch_B(kn);
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-          for (int j = 0; j < 2; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[sl][i], fb[sl][j], acc[i][j], 0, 0, 0);
-        if (kk == 3) store_B(st ^ 1);
-        __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);  // DS read: next fragments
-        if (kk == 0) {
-#pragma unroll
-          for (int q = 0; q < 8; ++q) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM read
+        for (int q = 0; q < 8; ++q) {
+          acc[q >> 1][q & 1] =
+              __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[sl][q >> 1], fb[sl][q & 1], acc[q >> 1][q & 1], 0, 0, 0);
+          if (kk < 3 && q < 6) load_frag(kk + 1, sl ^ 1, q);
+          if ((q & 1) == 0) issue_word(4 * kk + (q >> 1), base, x[4 * kk + (q >> 1)]);
+          if ((q == 3 || q == 7) && kk > 0) {
+            const int p = 2 * (kk - 1) + (q >> 2);
+            finish_pair(st ^ 1, p, x[2 * p], x[2 * p + 1], out);
           }
-        } else if (kk == 3) {
-#pragma unroll
-          for (int q = 0; q < 8; ++q) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-            __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);  // DS write
-          }
-        } else {
-          __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+          __builtin_amdgcn_sched_barrier(0);
         }
-        __builtin_amdgcn_sched_barrier(0);
       }
+      finish_pair(st ^ 1, 6, x[12], x[13], out);
+      finish_pair(st ^ 1, 7, x[14], x[15], out);
       __syncthreads();
     }
 
@@ -665,82 +760,15 @@ __global__ __launch_bounds__(512, 1) void prefill_ws_kernel(PrefillArgs a) {
       }
   } else {
     // ---------------------------------------------------------------- producer
-    const int pw = wave - 4;
-    const int slab0 = m0 / 16 + 2 * pw;  // tiles tt = 0, 1: slabs slab0 + tt (clamped: rows past M unused)
-    const uint32_t runbuf = runbase + uint32_t(pw) * 2u * tile_run_bytes;
-    u32x2 runreg[2 * kRC];
-    uint32_t wreg = 0, wsave = 0;  // lane l: dword l%32 of tile l/32's 16 bitmap words
-    // tile pointers: lane 2tt + h holds pointer h of tile tt (clamped step)
-    auto fetch_tp = [&](int ks) -> uint32_t {
-      const int j = lane & 3;
-      const uint64_t t = uint64_t(min(slab0 + (j >> 1), a.mt - 1)) * a.kt + min(ks, a.kt - 1) + (j & 1);
-      return a.tile_ptr[t];
-    };
-    auto fetch_runs = [&](int ks, uint32_t tpv) {
-#pragma unroll
-      for (int tt = 0; tt < 2; ++tt) {
-        const uint32_t p0 = __builtin_amdgcn_readlane(tpv, 2 * tt);
-        const uint32_t p1 = __builtin_amdgcn_readlane(tpv, 2 * tt + 1);
-        const uint32_t last = p1 > p0 + 4 ? p1 - 4 : p0;
-#pragma unroll
-        for (int cc = 0; cc < kRC; ++cc) {
-          const uint32_t off = min(p0 + uint32_t(cc * 256 + lane * 4), last);
-          runreg[tt * kRC + cc] = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(a.vals + off));
-        }
-      }
-      const uint64_t t = uint64_t(min(slab0 + (lane >> 5), a.mt - 1)) * a.kt + min(ks, a.kt - 1);
-      wreg = reinterpret_cast<const uint32_t*>(a.bits + t * 16)[lane & 31];
-    };
-    auto stage_runs = [&]() {
-#pragma unroll
-      for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-        for (int cc = 0; cc < kRC; ++cc)
-          *reinterpret_cast<lds_u32x2*>(static_cast<uintptr_t>(runbuf + tt * tile_run_bytes + cc * 512 + lane * 8)) =
-              runreg[tt * kRC + cc];
-      wsave = wreg;
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-    };
-    // Expand the staged tiles (4 units: tile tt, 32-column step s) into A stage `stage`.
-    auto expand = [&](int stage) {
-#pragma unroll
-      for (int tt = 0; tt < 2; ++tt) {
-        uint32_t base = runbuf + uint32_t(tt) * tile_run_bytes;
-#pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2) {
-          uint64_t w[8];
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const int d = 32 * tt + 2 * (8 * s2 + e);
-            const uint32_t lo = __builtin_amdgcn_readlane(wsave, d);  // int: zero-extend via u32
-            const uint32_t hi = __builtin_amdgcn_readlane(wsave, d + 1);
-            w[e] = uint64_t(lo) | (uint64_t(hi) << 32);
-          }
-          const u32x4 out = expand_step(w, base);
-          lds_store16(sA + stage * kWATile + swz(pw * 32 + tt * 16 + (lane & 15), 4 * s2 + (lane >> 4)), out);
-        }
-      }
-    };
-
-    uint32_t tp_next = fetch_tp(2);
-    {
-      const uint32_t tp0 = fetch_tp(0), tp1 = fetch_tp(1);
-      fetch_runs(0, tp0);
-      stage_runs();
-      fetch_runs(1, tp1);
-    }
-    expand(0);
-    __syncthreads();  // stage 0 complete
-
     for (int ks = 0; ks < nsteps; ++ks) {
       const int st = ks & 1;
-      // runs/words of step ks+1 (fetched during step ks-1) -> LDS, then fetch step ks+2
-      stage_runs();
+      stage_runs();  // runs/words of step ks+1 (fetched during step ks-1)
       const uint32_t tp_cur = tp_next;
       tp_next = fetch_tp(ks + 3);
       fetch_runs(ks + 2, tp_cur);
-      expand(st ^ 1);  // the last step expands a clamped duplicate into the unused stage
+      expand_all(st ^ 1);
+      store_B(st ^ 1);  // activations of step ks+1 (clamped past the end)
+      fetch_B(min(ks + 2, nsteps - 1));
       __syncthreads();
     }
   }
@@ -777,11 +805,6 @@ bool prefill_sparse_fits(const Header& h, int64_t N, int64_t ldx) {
   return 2 * ((N - 1) * ldx + h.k) < (int64_t(1) << 32);  // 32-bit activation offsets
 }
 
-size_t prefill_sparse_lds(const Header& h) {
-  const size_t chunks = (size_t(h.max_tile) + 255) / 256;  // 512-byte chunks per tile run
-  return size_t(2) * kWATile + size_t(2) * kWBTile + 4 /*producers*/ * 2 /*tiles*/ * (chunks ? chunks : 1) * 512;
-}
-
 hipError_t launch_prefill_dense(const uint16_t* W, int64_t ldw, const uint16_t* X, int64_t ldx,
                                 uint16_t* Y, int64_t ldy, int64_t M, int64_t K, int64_t N,
                                 hipStream_t s) {
@@ -793,6 +816,11 @@ hipError_t launch_prefill_dense(const uint16_t* W, int64_t ldw, const uint16_t* 
   const size_t lds = size_t(4) * kTileBytes;
   hipLaunchKernelGGL((prefill_kernel<false, 1>), dim3(grid_size(a)), dim3(256), lds, s, a);
   return hipGetLastError();
+}
+
+size_t prefill_sparse_lds(const Header& h) {
+  const size_t chunks = std::max<size_t>((size_t(h.max_tile) + 255) / 256, 1);  // 512-byte chunks per tile run
+  return size_t(2) * kWATile + size_t(2) * kWBTile + 8 /*waves*/ * chunks * 512;
 }
 
 hipError_t launch_prefill_sparse(const DevFormat& f, const uint16_t* X, int64_t ldx, uint16_t* Y,
