@@ -163,7 +163,6 @@ struct DecodeArgs {
   int64_t ldx, ldy;
   int M, K, N, kt;
   int tpw;  // tiles per wave
-  int16_t wstart[17];  // straight-line kernel: tile range [wstart[w], wstart[w+1]) of wave w
 };
 
 constexpr int kSegTiles = 4;  // tiles per streamed segment
@@ -378,8 +377,8 @@ __global__ __launch_bounds__(1024) void decode_seq_kernel(DecodeArgs a) {
   const uint32_t buf = lds_addr(smem + 16 + size_t(wave) * kWaveLds);
   const uint32_t xbuf = buf + kC * 1024;
 
-  const int j0 = a.wstart[wave];
-  const int nt = a.wstart[wave + 1] - j0;  // tiles of this wave (<= kT)
+  const int j0 = wave * a.tpw;
+  const int nt = min(a.tpw, a.kt - j0);  // tiles of this wave (<= kT)
 
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   uint32_t keep = 0;
@@ -718,17 +717,13 @@ DecodePlan plan_decode(const Header& h, const uint32_t* tp, int num_cus) {
       }
   p.seg_chunks = int((max_bytes + 1023) / 1024);
   if (p.seg_chunks < 1) p.seg_chunks = 1;
-  // Straight-line schedule: per-wave tile ranges (tpw tiles each, the last
-  // wave fewer), two-tile segments aligned to each range.
-  for (int w = 0; w <= p.waves; ++w) p.wstart[w] = int16_t(std::min<int64_t>(int64_t(w) * tpw, h.kt));
-  int max_nt = 0;
-  for (int w = 0; w < p.waves; ++w) max_nt = std::max(max_nt, int(p.wstart[w + 1] - p.wstart[w]));
-  p.seq_segs = h.kt <= 16 * 16 ? seq_instance((max_nt + 1) / 2) : 0;
+  // Straight-line schedule: two-tile segments aligned to each wave's range.
+  p.seq_segs = seq_instance(int((tpw + 1) / 2));
   uint64_t max2 = 0;
   for (uint64_t i = 0; i < h.mt; ++i)
-    for (int w = 0; w < p.waves; ++w)
-      for (int64_t js = p.wstart[w]; js < p.wstart[w + 1]; js += 2) {
-        const int64_t je = std::min<int64_t>(js + 2, p.wstart[w + 1]);
+    for (int64_t ja = 0; ja < int64_t(h.kt); ja += tpw)
+      for (int64_t js = ja; js < std::min<int64_t>(ja + tpw, h.kt); js += 2) {
+        const int64_t je = std::min<int64_t>({js + 2, ja + tpw, int64_t(h.kt)});
         const uint64_t b = 2ull * (tp[i * h.kt + je] - tp[i * h.kt + js]);
         if (b > max2) max2 = b;
       }
@@ -758,7 +753,6 @@ hipError_t launch_decode(const DevFormat& f, const DecodePlan& p, const uint16_t
   a.N = n;
   a.kt = int(f.h.kt);
   a.tpw = p.tiles_per_wave;
-  for (int w = 0; w < 17; ++w) a.wstart[w] = p.wstart[w];
   if (f.h.tm != uint32_t(kSlab) || f.h.tk != uint32_t(kTK)) return hipErrorInvalidValue;
   if (p.seg_chunks > 8) return hipErrorInvalidValue;  // 4 tiles hold at most 8 KiB
   const bool vec = (f.h.k % 8 == 0) && (ldx % 8 == 0) && ((reinterpret_cast<uintptr_t>(X) & 15) == 0);

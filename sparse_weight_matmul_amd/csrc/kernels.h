@@ -29,7 +29,6 @@ struct DecodePlan {
   int seg_chunks = 1;      // 1 KiB loads per segment (covers the largest segment)
   int seq_segs = 0;        // straight-line kernel: two-tile segments per wave (0 = not used)
   int seq_chunks = 1;      // 1 KiB loads per two-tile segment
-  int16_t wstart[17] = {};  // straight-line kernel: first tile of wave w (wstart[waves] = kt)
   int splits = 1;
 };
 

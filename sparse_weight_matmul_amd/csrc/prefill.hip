@@ -10,28 +10,23 @@
 // its prior art; at moderate sparsity the dense-executed products are the same
 // as the dense GEMM's, so the sparse kernel can at best tie once compute bound.
 //
-// gfx950 design: one 256-thread workgroup computes a 256 (rows of W) x 256
+// Dense kernel: one 256-thread workgroup computes a 256 (rows of W) x 256
 // (tokens) block of Y over K in steps of 64.  Four waves in a 2 x 2 layout each
 // own a 128 x 128 sub-block = 4 x 4 v_mfma_f32_32x32x16_f16 accumulators (256
 // fp32 per lane, in AGPRs).  A and B tiles (256 x 64 fp16 each) are double
-// buffered in LDS with an XOR swizzle of the 16-byte chunks (row r, chunk c at
-// chunk c ^ (r & 7)), so the 16-byte fragment reads of eight consecutive rows
-// hit distinct banks without padding.  Inside a step the fragments of the next
-// 16-column slice are read while the current slice's 16 products issue, and
-// the next step's global tiles are in flight in VGPRs.  All global loads are
-// unconditional: rows past M and tokens past N read a clamped valid row (their
-// outputs are never stored) and activations past K read as zero.
+// buffered in LDS with an XOR swizzle of the 16-byte chunks, so the 16-byte
+// fragment reads of consecutive rows hit distinct banks without padding.
+// Inside a step the fragments of the next 16-column slice are read while the
+// current slice's 16 products issue, and the next step's global tiles are in
+// flight in VGPRs.  All global loads are unconditional: rows past M and tokens
+// past N read a clamped valid row (their outputs are never stored) and
+// activations past K read as zero.
 //
-// Sparse variant: at step k each wave expands the four 16 x 64 weight tiles
-// it owns for step k+1 (slabs m0/16 + 4 wave + tt, tt = 0..3) into the other
-// A stage, two expansion units (8 bitmap words -> one 16-byte store per lane)
-// per 16-column slice, interleaved with the products.  The tiles' packed runs
-// and bitmap words travel by vector loads two steps ahead; the runs are copied
-// to a per-wave LDS buffer and the words moved to SGPRs with v_readlane, so
-// the loop never waits on the scalar memory path.  The workgroup-to-tile map
-// is XCD aware: consecutive workgroup ids go to different XCDs, so ids are
-// regrouped to give each XCD a contiguous band of output tiles that share
-// weight rows in its L2.
+// Sparse kernel: see prefill_ws_kernel below (eight waves, two per SIMD, the
+// expansion shared by all of them).  Both kernels map workgroups to tiles XCD
+// aware: consecutive workgroup ids go to different XCDs, so ids are regrouped
+// to give each XCD a contiguous band of output tiles that share weight rows
+// in its L2.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -71,45 +66,6 @@ __device__ __forceinline__ uint32_t swz(int row, int chunk) {
   return uint32_t(row * 128 + ((chunk ^ ((row >> 1) & 7)) << 4));
 }
 
-// Eight bitmap words (SGPR pairs) of one 32-column step of a 16 x 64 tile ->
-// this lane's row l%16, columns 32s + 8(l/16) .. +7, packed as eight fp16.
-// `base` is the LDS byte address of word 0's run and advances past the step.
-// Per pair of words: lanes read the halfword at their rank (lanes whose bit is
-// clear read a neighbour), one v_cndmask zeroes the low half and an SDWA
-// v_cndmask zeroes and packs the high half.
-__device__ __forceinline__ u32x4 expand_step(const uint64_t (&w)[8], uint32_t& base) {
-  u32x4 out;
-#pragma unroll
-  for (int p = 0; p < 4; ++p) {
-    const uint64_t w0 = w[2 * p], w1 = w[2 * p + 1];
-    const uint32_t r0 = __builtin_amdgcn_mbcnt_hi(uint32_t(w0 >> 32), __builtin_amdgcn_mbcnt_lo(uint32_t(w0), 0u));
-    const uint32_t r1 = __builtin_amdgcn_mbcnt_hi(uint32_t(w1 >> 32), __builtin_amdgcn_mbcnt_lo(uint32_t(w1), 0u));
-    uint32_t b1, b2, c0, c1, a0, a1;
-    asm("s_bcnt1_i32_b64 %2, %4\n\t"
-        "s_lshl1_add_u32 %0, %2, %6\n\t"
-        "s_bcnt1_i32_b64 %3, %5\n\t"
-        "s_lshl1_add_u32 %1, %3, %0"
-        : "=&s"(b1), "=&s"(b2), "=&s"(c0), "=&s"(c1)
-        : "s"(w0), "s"(w1), "s"(base)
-        : "scc");
-    asm("v_lshl_add_u32 %0, %1, 1, %2" : "=v"(a0) : "v"(r0), "s"(base));
-    asm("v_lshl_add_u32 %0, %1, 1, %2" : "=v"(a1) : "v"(r1), "s"(b1));
-    const uint32_t d0 = *reinterpret_cast<const lds_u16*>(static_cast<uintptr_t>(a0));
-    const uint32_t d1 = *reinterpret_cast<const lds_u16*>(static_cast<uintptr_t>(a1));
-    base = b2;
-    uint32_t v;
-    asm("v_cndmask_b32_e64 %0, 0, %1, %3\n\t"
-        "s_mov_b64 vcc, %4\n\t"
-        "v_cndmask_b32_sdwa %0, 0, %2, vcc dst_sel:WORD_1 dst_unused:UNUSED_PRESERVE src0_sel:DWORD "
-        "src1_sel:WORD_0"
-        : "=&v"(v)
-        : "v"(d0), "v"(d1), "s"(w0), "s"(w1)
-        : "vcc");
-    out[p] = v;
-  }
-  return out;
-}
-
 struct PrefillArgs {
   const uint16_t* W;  // dense variant
   const uint32_t* tile_ptr;
@@ -142,10 +98,7 @@ __device__ __forceinline__ bool tile_of(const PrefillArgs& a, int& tm, int& tn) 
   return true;
 }
 
-// kRC: 512-byte run chunks per tile (sparse variant; the host passes the
-// smallest count that holds the largest tile run).
-template <bool kSparse, int kRC>
-__global__ __launch_bounds__(256, 1) void prefill_kernel(PrefillArgs a) {
+__global__ __launch_bounds__(256, 1) void dense_kernel(PrefillArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   int tm, tn;
   if (!tile_of(a, tm, tn)) return;
@@ -155,10 +108,8 @@ __global__ __launch_bounds__(256, 1) void prefill_kernel(PrefillArgs a) {
   const int wm = wave >> 1, wn = wave & 1;
   const int m0 = tm * BM, n0 = tn * BN;
 
-  // LDS: A stages [2][32 KiB] | B stages [2][32 KiB] | sparse: per-wave run buffers
+  // LDS: A stages [2][32 KiB] | B stages [2][32 KiB]
   const uint32_t sA = lds_addr(smem), sB = sA + 2 * kTileBytes;
-  constexpr uint32_t tile_run_bytes = uint32_t(kRC) * 512u;
-  const uint32_t runbuf = sB + 2 * kTileBytes + uint32_t(wave) * 4u * tile_run_bytes;
 
   // Global fetch map: thread -> (row r*32 + tid/8, chunk tid%8), r = 0..7.
   const int frow = tid >> 3, fch = tid & 7;
@@ -180,9 +131,7 @@ __global__ __launch_bounds__(256, 1) void prefill_kernel(PrefillArgs a) {
   auto store_B = [&](int stage) {
 #pragma unroll
     for (int r = 0; r < 8; ++r) {
-      // the sparse A is zero past K (no bitmap bits there), so only the
-      // dense variant needs the activations zeroed
-      const u32x4 v = (kSparse || bvalid) ? regB[r] : u32x4{0u, 0u, 0u, 0u};
+      const u32x4 v = bvalid ? regB[r] : u32x4{0u, 0u, 0u, 0u};
       lds_store16(sB + stage * kTileBytes + swz(r * 32 + frow, fch), v);
     }
   };
@@ -201,154 +150,6 @@ __global__ __launch_bounds__(256, 1) void prefill_kernel(PrefillArgs a) {
     for (int r = 0; r < 8; ++r) lds_store16(sA + stage * kTileBytes + swz(r * 32 + frow, fch), regA[r]);
   };
 
-  // Sparse: the wave's four tiles at step ks are slabs slab0 + tt (clamped to
-  // the last slab: rows past M are never stored), tile column ks.  Their tile
-  // pointers arrive by a vector load one step before the runs (lane 2tt + h
-  // holds pointer h of tile tt) and reach SGPRs with v_readlane.  Run chunks
-  // are 8 bytes per lane, clamped into the run; the 64 bitmap words are two
-  // dwords per lane (lane l of load h holds dword l%32 of tile 2h + l/32).
-  const int slab0 = m0 / 16 + 4 * wave;
-  u32x2 runreg[4 * kRC];
-  uint32_t wreg[2];
-  auto fetch_tp = [&](int ks) -> uint32_t {
-    const int j = lane & 7;
-    const uint64_t t = uint64_t(min(slab0 + (j >> 1), a.mt - 1)) * a.kt + min(ks, a.kt - 1) + (j & 1);
-    return a.tile_ptr[t];
-  };
-  auto fetch_A_sparse = [&](int ks, uint32_t tpv) {
-#pragma unroll
-    for (int tt = 0; tt < 4; ++tt) {
-      const uint32_t p0 = __builtin_amdgcn_readlane(tpv, 2 * tt);
-      const uint32_t p1 = __builtin_amdgcn_readlane(tpv, 2 * tt + 1);
-      const uint32_t last = p1 > p0 + 4 ? p1 - 4 : p0;
-#pragma unroll
-      for (int c = 0; c < kRC; ++c) {
-        const uint32_t off = min(p0 + uint32_t(c * 256 + lane * 4), last);
-        runreg[tt * kRC + c] = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(a.vals + off));
-      }
-    }
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const uint64_t t = uint64_t(min(slab0 + 2 * h + (lane >> 5), a.mt - 1)) * a.kt + min(ks, a.kt - 1);
-      wreg[h] = reinterpret_cast<const uint32_t*>(a.bits + t * 16)[lane & 31];
-    }
-  };
-  auto stage_A_sparse = [&]() {
-#pragma unroll
-    for (int tt = 0; tt < 4; ++tt)
-#pragma unroll
-      for (int c = 0; c < kRC; ++c)
-        *reinterpret_cast<lds_u32x2*>(static_cast<uintptr_t>(runbuf + tt * tile_run_bytes + c * 512 + lane * 8)) =
-            runreg[tt * kRC + c];
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-  };
-  // Expansion unit u = 2 tt + s (tile tt, 32-column step s) of the staged
-  // tiles into A stage `stage`: rows 64 wave + 16 tt + l%16, chunk 4s + l/16.
-  uint32_t wsave[2];
-  auto expand_unit = [&](int stage, int u, uint32_t& base) {
-    const int tt = u >> 1, s2 = u & 1;
-    uint64_t w[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int d = 32 * (tt & 1) + 2 * (8 * s2 + e);
-      const uint32_t lo = __builtin_amdgcn_readlane(wsave[tt >> 1], d);
-      const uint32_t hi = __builtin_amdgcn_readlane(wsave[tt >> 1], d + 1);
-      w[e] = uint64_t(lo) | (uint64_t(hi) << 32);
-    }
-    const u32x4 out = expand_step(w, base);
-    lds_store16(sA + stage * kTileBytes + swz(wave * 64 + tt * 16 + (lane & 15), 4 * s2 + (lane >> 4)), out);
-  };
-  struct Pending {
-    uint64_t w[8];
-    uint32_t d[8];
-  };
-  // Word-granular halves of a unit, spread one word per product: word e of
-  // unit u to SGPRs, its rank and run address, and its halfword read; later,
-  // pair p's zero / pack, and the unit's 16-byte store after pair 3.
-  auto issue_word = [&](int u, int e, uint32_t& base, Pending& pd) {
-    const int tt = u >> 1, s2 = u & 1;
-    const int d = 32 * (tt & 1) + 2 * (8 * s2 + e);
-    const uint32_t lo = __builtin_amdgcn_readlane(wsave[tt >> 1], d);
-    const uint32_t hi = __builtin_amdgcn_readlane(wsave[tt >> 1], d + 1);
-    const uint64_t w = uint64_t(lo) | (uint64_t(hi) << 32);
-    pd.w[e] = w;
-    const uint32_t r = __builtin_amdgcn_mbcnt_hi(hi, __builtin_amdgcn_mbcnt_lo(lo, 0u));
-    uint32_t nb, c, ad;
-    asm("s_bcnt1_i32_b64 %1, %2\n\t"
-        "s_lshl1_add_u32 %0, %1, %3"
-        : "=&s"(nb), "=&s"(c)
-        : "s"(w), "s"(base)
-        : "scc");
-    asm("v_lshl_add_u32 %0, %1, 1, %2" : "=v"(ad) : "v"(r), "s"(base));
-    pd.d[e] = *reinterpret_cast<const lds_u16*>(static_cast<uintptr_t>(ad));
-    base = nb;
-  };
-  auto finish_pair = [&](int stage, int u, int p, const Pending& pd, u32x4& out) {
-    uint32_t v;
-    asm("v_cndmask_b32_e64 %0, 0, %1, %3\n\t"
-        "s_mov_b64 vcc, %4\n\t"
-        "v_cndmask_b32_sdwa %0, 0, %2, vcc dst_sel:WORD_1 dst_unused:UNUSED_PRESERVE src0_sel:DWORD "
-        "src1_sel:WORD_0"
-        : "=&v"(v)
-        : "v"(pd.d[2 * p]), "v"(pd.d[2 * p + 1]), "s"(pd.w[2 * p]), "s"(pd.w[2 * p + 1])
-        : "vcc");
-    out[p] = v;
-    if (p == 3) {
-      const int tt = u >> 1, s2 = u & 1;
-      lds_store16(sA + stage * kTileBytes + swz(wave * 64 + tt * 16 + (lane & 15), 4 * s2 + (lane >> 4)), out);
-    }
-  };
-  // The same unit in two halves, so that products issue while its LDS reads
-  // are in flight: issue = words to SGPRs, ranks, run bases, halfword reads;
-  // finish = zero / pack (v_cndmask, SDWA v_cndmask) and the 16-byte store.
-  auto expand_issue = [&](int u, uint32_t& base, Pending& pd) {
-    const int tt = u >> 1, s2 = u & 1;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int d = 32 * (tt & 1) + 2 * (8 * s2 + e);
-      const uint32_t lo = __builtin_amdgcn_readlane(wsave[tt >> 1], d);
-      const uint32_t hi = __builtin_amdgcn_readlane(wsave[tt >> 1], d + 1);
-      pd.w[e] = uint64_t(lo) | (uint64_t(hi) << 32);
-    }
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      const uint64_t w0 = pd.w[2 * p], w1 = pd.w[2 * p + 1];
-      const uint32_t r0 = __builtin_amdgcn_mbcnt_hi(uint32_t(w0 >> 32), __builtin_amdgcn_mbcnt_lo(uint32_t(w0), 0u));
-      const uint32_t r1 = __builtin_amdgcn_mbcnt_hi(uint32_t(w1 >> 32), __builtin_amdgcn_mbcnt_lo(uint32_t(w1), 0u));
-      uint32_t b1, b2, c0, c1, a0, a1;
-      asm("s_bcnt1_i32_b64 %2, %4\n\t"
-          "s_lshl1_add_u32 %0, %2, %6\n\t"
-          "s_bcnt1_i32_b64 %3, %5\n\t"
-          "s_lshl1_add_u32 %1, %3, %0"
-          : "=&s"(b1), "=&s"(b2), "=&s"(c0), "=&s"(c1)
-          : "s"(w0), "s"(w1), "s"(base)
-          : "scc");
-      asm("v_lshl_add_u32 %0, %1, 1, %2" : "=v"(a0) : "v"(r0), "s"(base));
-      asm("v_lshl_add_u32 %0, %1, 1, %2" : "=v"(a1) : "v"(r1), "s"(b1));
-      pd.d[2 * p] = *reinterpret_cast<const lds_u16*>(static_cast<uintptr_t>(a0));
-      pd.d[2 * p + 1] = *reinterpret_cast<const lds_u16*>(static_cast<uintptr_t>(a1));
-      base = b2;
-    }
-  };
-  auto expand_finish = [&](int stage, int u, const Pending& pd) {
-    const int tt = u >> 1, s2 = u & 1;
-    u32x4 out;
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      uint32_t v;
-      asm("v_cndmask_b32_e64 %0, 0, %1, %3\n\t"
-          "s_mov_b64 vcc, %4\n\t"
-          "v_cndmask_b32_sdwa %0, 0, %2, vcc dst_sel:WORD_1 dst_unused:UNUSED_PRESERVE src0_sel:DWORD "
-          "src1_sel:WORD_0"
-          : "=&v"(v)
-          : "v"(pd.d[2 * p]), "v"(pd.d[2 * p + 1]), "s"(pd.w[2 * p]), "s"(pd.w[2 * p + 1])
-          : "vcc");
-      out[p] = v;
-    }
-    lds_store16(sA + stage * kTileBytes + swz(wave * 64 + tt * 16 + (lane & 15), 4 * s2 + (lane >> 4)), out);
-  };
-
   f32x16 acc[4][4];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
@@ -357,147 +158,70 @@ __global__ __launch_bounds__(256, 1) void prefill_kernel(PrefillArgs a) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
-  // Prologue: stage 0 complete in LDS; sparse runs of step 1 and tile
-  // pointers of step 2 in flight.
+  // Prologue: stage 0 complete in LDS.
   fetch_B(0);
-  uint32_t tp_next = 0;  // sparse: tile pointers of step ks+2, loaded during step ks-1
-  if constexpr (kSparse) {
-    const uint32_t tp0 = fetch_tp(0), tp1 = fetch_tp(1);
-    tp_next = fetch_tp(2);
-    fetch_A_sparse(0, tp0);
-    stage_A_sparse();
-    wsave[0] = wreg[0];
-    wsave[1] = wreg[1];
-    fetch_A_sparse(1, tp1);
-    uint32_t base = runbuf;
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      if ((u & 1) == 0) base = runbuf + uint32_t(u >> 1) * tile_run_bytes;
-      expand_unit(0, u, base);
-    }
-  } else {
-    fetch_A_dense(0);
-    store_A_dense(0);
-  }
+  fetch_A_dense(0);
+  store_A_dense(0);
   store_B(0);
   __syncthreads();
 
-  if constexpr (!kSparse) {
-    // Dense: one basic block per step.  The next step's tiles are fetched
-    // interleaved with the first two slices' products (the vector memory
-    // path then works in the background instead of stalling the issue of a
-    // burst), and stored into the free stage interleaved with the last
-    // slice's products.  The last step refetches itself into the unused stage.
-    for (int ks = 0; ks < nsteps; ++ks) {
-      const int st = ks & 1;
-      const int kn = min(ks + 1, nsteps - 1);
-      const uint32_t aBase = sA + st * kTileBytes, bBase = sB + st * kTileBytes;
-      half8 fa[2][4], fb[2][4];
-      auto load_frags = [&](int kk, int slot) {
-        const int ch = kk * 2 + (lane >> 5);
+  // One basic block per step.  The next step's tiles are fetched
+  // interleaved with the first two slices' products (the vector memory
+  // path then works in the background instead of stalling the issue of a
+  // burst), and stored into the free stage interleaved with the last
+  // slice's products.  The last step refetches itself into the unused stage.
+  for (int ks = 0; ks < nsteps; ++ks) {
+    const int st = ks & 1;
+    const int kn = min(ks + 1, nsteps - 1);
+    const uint32_t aBase = sA + st * kTileBytes, bBase = sB + st * kTileBytes;
+    half8 fa[2][4], fb[2][4];
+    auto load_frags = [&](int kk, int slot) {
+      const int ch = kk * 2 + (lane >> 5);
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          fa[slot][i] = __builtin_bit_cast(half8, lds_load16(aBase + swz(wm * 128 + i * 32 + (lane & 31), ch)));
+      for (int i = 0; i < 4; ++i)
+        fa[slot][i] = __builtin_bit_cast(half8, lds_load16(aBase + swz(wm * 128 + i * 32 + (lane & 31), ch)));
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        fb[slot][j] = __builtin_bit_cast(half8, lds_load16(bBase + swz(wn * 128 + j * 32 + (lane & 31), ch)));
+    };
+    load_frags(0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      const int sl = kk & 1;
+      if (kk < 3) load_frags(kk + 1, sl ^ 1);
+      if (kk == 0) fetch_A_dense(kn);
+      if (kk == 1) fetch_B(kn);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-          fb[slot][j] = __builtin_bit_cast(half8, lds_load16(bBase + swz(wn * 128 + j * 32 + (lane & 31), ch)));
-      };
-      load_frags(0, 0);
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        const int sl = kk & 1;
-        if (kk < 3) load_frags(kk + 1, sl ^ 1);
-        if (kk == 0) fetch_A_dense(kn);
-        if (kk == 1) fetch_B(kn);
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-          for (int j = 0; j < 4; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[sl][i], fb[sl][j], acc[i][j], 0, 0, 0);
-        if (kk == 3) {
-          store_A_dense(st ^ 1);
-          store_B(st ^ 1);
-        }
-        // issue pattern of this slice: next fragments first, then products
-        // with the slice's global loads or LDS stores spread between them
-        __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);  // DS read
-        if (kk <= 1) {
-#pragma unroll
-          for (int q = 0; q < 8; ++q) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // MFMA
-            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM read
-          }
-        } else if (kk == 3) {
-#pragma unroll
-          for (int q = 0; q < 16; ++q) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-            __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);  // DS write
-          }
-        } else {
-          __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);
-        }
-        __builtin_amdgcn_sched_barrier(0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[sl][i], fb[sl][j], acc[i][j], 0, 0, 0);
+      if (kk == 3) {
+        store_A_dense(st ^ 1);
+        store_B(st ^ 1);
       }
-      __syncthreads();
-    }
-  } else {
-    // Sparse: one basic block per step (the last step stages, expands and
-    // stores into the unused stage; all its loads are clamped).  Per slice:
-    // the next fragments, the two expansion units' reads, eight products,
-    // the units' pack and store, eight products.
-    for (int ks = 0; ks < nsteps; ++ks) {
-      const int st = ks & 1;
-      // runs and words of step ks+1 (loaded during step ks-1) -> LDS / SGPR source
-      stage_A_sparse();
-      wsave[0] = wreg[0];
-      wsave[1] = wreg[1];
-      fetch_B(min(ks + 1, nsteps - 1));
-      const uint32_t tp_cur = tp_next;
-      tp_next = fetch_tp(ks + 3);
-      fetch_A_sparse(ks + 2, tp_cur);
-      const uint32_t aBase = sA + st * kTileBytes, bBase = sB + st * kTileBytes;
-      half8 fa[2][4], fb[2][4];
-      auto load_frags = [&](int kk, int slot) {
-        const int ch = kk * 2 + (lane >> 5);
+      // issue pattern of this slice: next fragments first, then products
+      // with the slice's global loads or LDS stores spread between them
+      __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);  // DS read
+      if (kk <= 1) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          fa[slot][i] = __builtin_bit_cast(half8, lds_load16(aBase + swz(wm * 128 + i * 32 + (lane & 31), ch)));
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          fb[slot][j] = __builtin_bit_cast(half8, lds_load16(bBase + swz(wn * 128 + j * 32 + (lane & 31), ch)));
-      };
-      load_frags(0, 0);
-      // Units 2kk and 2kk+1 (tile kk, both 32-column steps) are read word by
-      // word between the products of slice kk; each unit is packed and
-      // stored during the following half-slice (eight products later).
-      Pending pu[2];
-      u32x4 outv[2];
-      uint32_t base = runbuf;
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        const int sl = kk & 1;
-        __builtin_amdgcn_sched_barrier(0);
-        if (kk < 3) load_frags(kk + 1, sl ^ 1);
-        base = runbuf + uint32_t(kk) * tile_run_bytes;
+        for (int q = 0; q < 8; ++q) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // MFMA
+          __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM read
+        }
+      } else if (kk == 3) {
 #pragma unroll
         for (int q = 0; q < 16; ++q) {
-          __builtin_amdgcn_sched_barrier(0);
-          const int i = q >> 2, j = q & 3;
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[sl][i], fb[sl][j], acc[i][j], 0, 0, 0);
-          const int u = 2 * kk + (q >> 3);  // unit being read
-          issue_word(u, q & 7, base, pu[u & 1]);
-          if ((q & 1) && u >= 1)  // unit u-1 was read during the previous half-slice
-            finish_pair(st ^ 1, u - 1, (q & 7) >> 1, pu[(u - 1) & 1], outv[(u - 1) & 1]);
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+          __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);  // DS write
         }
+      } else {
+        __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);
       }
       __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int p = 0; p < 4; ++p) finish_pair(st ^ 1, 7, p, pu[1], outv[1]);
-      __builtin_amdgcn_sched_barrier(0);
-      store_B(st ^ 1);
-      __syncthreads();
     }
+    __syncthreads();
   }
 
   // Epilogue: fp16 round-to-nearest-even, 4 consecutive rows per 8-byte store.
@@ -814,7 +538,7 @@ hipError_t launch_prefill_dense(const uint16_t* W, int64_t ldw, const uint16_t* 
   if (a.tiles_m == 0 || a.tiles_n == 0) return hipSuccess;
   if (K < 8 || K % 8 != 0) return hipErrorInvalidValue;
   const size_t lds = size_t(4) * kTileBytes;
-  hipLaunchKernelGGL((prefill_kernel<false, 1>), dim3(grid_size(a)), dim3(256), lds, s, a);
+  hipLaunchKernelGGL(dense_kernel, dim3(grid_size(a)), dim3(256), lds, s, a);
   return hipGetLastError();
 }
 
