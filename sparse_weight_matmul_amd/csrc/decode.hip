@@ -350,10 +350,17 @@ __global__ __launch_bounds__(1024) void decode_kernel(DecodeArgs a) {
 //     tokens are loaded first (kXI loads of 1 KiB: 256 contiguous bytes per
 //     token, whole cache lines), then its value chunks; using the
 //     activations never waits for value bytes;
-//   * two segments are in flight.  At a segment's start its activations go
-//     to the wave's LDS (B operands are then read with ds_read_b128); its
-//     chunks are copied tile by tile, each as soon as the chunks that hold it
-//     have arrived, so decoding overlaps the rest of the stream.
+//   * one segment is requested ahead: segment g+1 is issued when segment g
+//     has been decoded.  With every wave's whole range in flight at once, the
+//     memory system served the waves of a SIMD in launch order and the last
+//     one decoded its entire range after the stream had ended; one segment
+//     ahead interleaves the waves' requests, so each wave has at most one
+//     segment left when the last bytes arrive (measured 5-9% faster on the
+//     q_proj, down and up shapes);
+//   * at a segment's start its activations go to the wave's LDS (B operands
+//     are then read with ds_read_b128); its chunks are copied tile by tile,
+//     each as soon as the chunks that hold it have arrived, so decoding
+//     overlaps the rest of the stream.
 constexpr int kXRow = 272;  // LDS bytes per token row of a segment's activations (256 + pad)
 
 template <int NS, int kC, int kXI>
@@ -449,7 +456,6 @@ __global__ __launch_bounds__(1024) void decode_seq_kernel(DecodeArgs a) {
     };
 
     issue_seg(0);
-    if constexpr (NS > 1) issue_seg(1);
 
 #pragma unroll
     for (int g = 0; g < NS; ++g) {
@@ -494,7 +500,7 @@ __global__ __launch_bounds__(1024) void decode_seq_kernel(DecodeArgs a) {
           }
         }
       }
-      if (g + 2 < NS) issue_seg(g + 2);
+      if (g + 1 < NS) issue_seg(g + 1);
     }
   }
   if (keep == 0x9E3779B9u && a.N < 0) a.Y[0] = 0;  // never true: keeps the L2 touch loads
