@@ -45,8 +45,7 @@ typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
 typedef __attribute__((address_space(3))) u32x2 lds_u32x2;
 typedef __attribute__((address_space(3))) uint16_t lds_u16;
 
-constexpr int BM = 256, BN = 256, BK = 64;
-constexpr int kTileBytes = BM * BK * 2;  // 32 KiB per operand stage
+constexpr int BM = 256, BN = 256, BK = 64;  // default block (launchers set the grid per kernel shape)
 
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p));
@@ -98,7 +97,14 @@ __device__ __forceinline__ bool tile_of(const PrefillArgs& a, int& tm, int& tn) 
   return true;
 }
 
-__global__ __launch_bounds__(256, 1) void dense_kernel(PrefillArgs a) {
+// Dense block shapes: waves in a 2 x 2 layout, each owning kWI x kWJ 32 x 32
+// accumulators, so the block is 64 kWI (rows of W) x 64 kWJ (tokens).  The
+// host takes the largest block that still gives every CU work.
+template <int kWI, int kWJ>
+__global__ __launch_bounds__(256) void dense_kernel(PrefillArgs a) {
+  constexpr int kBM = 64 * kWI, kBN = 64 * kWJ;
+  constexpr int kAT = kBM * BK * 2, kBT = kBN * BK * 2;  // stage bytes
+  constexpr int kRA = kBM / 32, kRB = kBN / 32;         // 16-byte loads per thread
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   int tm, tn;
   if (!tile_of(a, tm, tn)) return;
@@ -106,62 +112,62 @@ __global__ __launch_bounds__(256, 1) void dense_kernel(PrefillArgs a) {
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
-  const int m0 = tm * BM, n0 = tn * BN;
+  const int m0 = tm * kBM, n0 = tn * kBN;
 
-  // LDS: A stages [2][32 KiB] | B stages [2][32 KiB]
-  const uint32_t sA = lds_addr(smem), sB = sA + 2 * kTileBytes;
+  // LDS: A stages [2][kAT] | B stages [2][kBT]
+  const uint32_t sA = lds_addr(smem), sB = sA + 2 * kAT;
 
-  // Global fetch map: thread -> (row r*32 + tid/8, chunk tid%8), r = 0..7.
+  // Global fetch map: thread -> (row r*32 + tid/8, chunk tid%8).
   const int frow = tid >> 3, fch = tid & 7;
   const int nsteps = (a.K + BK - 1) / BK;
 
   // B: tokens past N read token N-1 (never stored); columns past K read 0.
-  const uint16_t* xrow[8];
+  const uint16_t* xrow[kRB];
 #pragma unroll
-  for (int r = 0; r < 8; ++r) xrow[r] = a.X + int64_t(min(n0 + r * 32 + frow, a.N - 1)) * a.ldx;
-  u32x4 regA[8], regB[8];
+  for (int r = 0; r < kRB; ++r) xrow[r] = a.X + int64_t(min(n0 + r * 32 + frow, a.N - 1)) * a.ldx;
+  u32x4 regA[kRA], regB[kRB];
   bool bvalid = true;  // the fetched B chunk lies inside K (zeroed at the store, not at the load)
   auto fetch_B = [&](int ks) {
     const int k = ks * BK + fch * 8;
     const int kc = min(k, a.K - 8);
     bvalid = k < a.K;
 #pragma unroll
-    for (int r = 0; r < 8; ++r) regB[r] = *reinterpret_cast<const u32x4*>(xrow[r] + kc);
+    for (int r = 0; r < kRB; ++r) regB[r] = *reinterpret_cast<const u32x4*>(xrow[r] + kc);
   };
   auto store_B = [&](int stage) {
 #pragma unroll
-    for (int r = 0; r < 8; ++r) {
+    for (int r = 0; r < kRB; ++r) {
       const u32x4 v = bvalid ? regB[r] : u32x4{0u, 0u, 0u, 0u};
-      lds_store16(sB + stage * kTileBytes + swz(r * 32 + frow, fch), v);
+      lds_store16(sB + stage * kBT + swz(r * 32 + frow, fch), v);
     }
   };
-  // Dense A: rows past M read row M-1 (never stored); columns past K are
+  // A: rows past M read row M-1 (never stored); columns past K are
   // multiplied by zero activations.
-  auto fetch_A_dense = [&](int ks) {
+  auto fetch_A = [&](int ks) {
     const int kc = min(ks * BK + fch * 8, a.K - 8);
 #pragma unroll
-    for (int r = 0; r < 8; ++r) {
+    for (int r = 0; r < kRA; ++r) {
       const int m = min(m0 + r * 32 + frow, a.M - 1);
       regA[r] = *reinterpret_cast<const u32x4*>(a.W + int64_t(m) * a.ldw + kc);
     }
   };
-  auto store_A_dense = [&](int stage) {
+  auto store_A = [&](int stage) {
 #pragma unroll
-    for (int r = 0; r < 8; ++r) lds_store16(sA + stage * kTileBytes + swz(r * 32 + frow, fch), regA[r]);
+    for (int r = 0; r < kRA; ++r) lds_store16(sA + stage * kAT + swz(r * 32 + frow, fch), regA[r]);
   };
 
-  f32x16 acc[4][4];
+  f32x16 acc[kWI][kWJ];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < kWI; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < kWJ; ++j)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
   // Prologue: stage 0 complete in LDS.
   fetch_B(0);
-  fetch_A_dense(0);
-  store_A_dense(0);
+  fetch_A(0);
+  store_A(0);
   store_B(0);
   __syncthreads();
 
@@ -170,19 +176,21 @@ __global__ __launch_bounds__(256, 1) void dense_kernel(PrefillArgs a) {
   // path then works in the background instead of stalling the issue of a
   // burst), and stored into the free stage interleaved with the last
   // slice's products.  The last step refetches itself into the unused stage.
+  constexpr int kM = kWI * kWJ;                          // products per slice
+  constexpr int kW = (kRA + kRB + kM - 1) / kM;          // LDS stores per product in the last slice
   for (int ks = 0; ks < nsteps; ++ks) {
     const int st = ks & 1;
     const int kn = min(ks + 1, nsteps - 1);
-    const uint32_t aBase = sA + st * kTileBytes, bBase = sB + st * kTileBytes;
-    half8 fa[2][4], fb[2][4];
+    const uint32_t aBase = sA + st * kAT, bBase = sB + st * kBT;
+    half8 fa[2][kWI], fb[2][kWJ];
     auto load_frags = [&](int kk, int slot) {
       const int ch = kk * 2 + (lane >> 5);
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        fa[slot][i] = __builtin_bit_cast(half8, lds_load16(aBase + swz(wm * 128 + i * 32 + (lane & 31), ch)));
+      for (int i = 0; i < kWI; ++i)
+        fa[slot][i] = __builtin_bit_cast(half8, lds_load16(aBase + swz((wm * kWI + i) * 32 + (lane & 31), ch)));
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        fb[slot][j] = __builtin_bit_cast(half8, lds_load16(bBase + swz(wn * 128 + j * 32 + (lane & 31), ch)));
+      for (int j = 0; j < kWJ; ++j)
+        fb[slot][j] = __builtin_bit_cast(half8, lds_load16(bBase + swz((wn * kWJ + j) * 32 + (lane & 31), ch)));
     };
     load_frags(0, 0);
     __builtin_amdgcn_sched_barrier(0);
@@ -190,34 +198,42 @@ __global__ __launch_bounds__(256, 1) void dense_kernel(PrefillArgs a) {
     for (int kk = 0; kk < 4; ++kk) {
       const int sl = kk & 1;
       if (kk < 3) load_frags(kk + 1, sl ^ 1);
-      if (kk == 0) fetch_A_dense(kn);
+      if (kk == 0) fetch_A(kn);
       if (kk == 1) fetch_B(kn);
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < kWI; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < kWJ; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[sl][i], fb[sl][j], acc[i][j], 0, 0, 0);
       if (kk == 3) {
-        store_A_dense(st ^ 1);
+        store_A(st ^ 1);
         store_B(st ^ 1);
       }
       // issue pattern of this slice: next fragments first, then products
       // with the slice's global loads or LDS stores spread between them
-      __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);  // DS read
-      if (kk <= 1) {
+      __builtin_amdgcn_sched_group_barrier(0x100, kWI + kWJ, 0);  // DS read
+      if (kk == 0) {
+        constexpr int kL = kRA < kM ? kRA : kM;
 #pragma unroll
-        for (int q = 0; q < 8; ++q) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // MFMA
-          __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM read
+        for (int q = 0; q < kL; ++q) {
+          __builtin_amdgcn_sched_group_barrier(0x008, kM / kL, 0);  // MFMA
+          __builtin_amdgcn_sched_group_barrier(0x020, kRA / kL, 0);  // VMEM read
+        }
+      } else if (kk == 1) {
+        constexpr int kL = kRB < kM ? kRB : kM;
+#pragma unroll
+        for (int q = 0; q < kL; ++q) {
+          __builtin_amdgcn_sched_group_barrier(0x008, kM / kL, 0);  // MFMA
+          __builtin_amdgcn_sched_group_barrier(0x020, kRB / kL, 0);  // VMEM read
         }
       } else if (kk == 3) {
 #pragma unroll
-        for (int q = 0; q < 16; ++q) {
+        for (int q = 0; q < kM; ++q) {
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-          __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);  // DS write
+          __builtin_amdgcn_sched_group_barrier(0x200, kW, 0);  // DS write
         }
       } else {
-        __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, kM, 0);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -226,14 +242,14 @@ __global__ __launch_bounds__(256, 1) void dense_kernel(PrefillArgs a) {
 
   // Epilogue: fp16 round-to-nearest-even, 4 consecutive rows per 8-byte store.
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < kWI; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int n = n0 + wn * 128 + j * 32 + (lane & 31);
+    for (int j = 0; j < kWJ; ++j) {
+      const int n = n0 + (wn * kWJ + j) * 32 + (lane & 31);
       if (n >= a.N) continue;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int m = m0 + wm * 128 + i * 32 + q * 8 + (lane >> 5) * 4;
+        const int m = m0 + (wm * kWI + i) * 32 + q * 8 + (lane >> 5) * 4;
         uint16_t h[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) h[e] = __builtin_bit_cast(uint16_t, _Float16(acc[i][j][q * 4 + e]));
@@ -529,6 +545,17 @@ bool prefill_sparse_fits(const Header& h, int64_t N, int64_t ldx) {
   return 2 * ((N - 1) * ldx + h.k) < (int64_t(1) << 32);  // 32-bit activation offsets
 }
 
+namespace {
+template <int kWI, int kWJ>
+hipError_t launch_dense(PrefillArgs a, hipStream_t s) {
+  a.tiles_m = int((a.M + 64 * kWI - 1) / (64 * kWI));
+  a.tiles_n = int((a.N + 64 * kWJ - 1) / (64 * kWJ));
+  const size_t lds = size_t(2) * (64 * kWI + 64 * kWJ) * BK * 2;
+  hipLaunchKernelGGL((dense_kernel<kWI, kWJ>), dim3(grid_size(a)), dim3(256), lds, s, a);
+  return hipGetLastError();
+}
+}  // namespace
+
 hipError_t launch_prefill_dense(const uint16_t* W, int64_t ldw, const uint16_t* X, int64_t ldx,
                                 uint16_t* Y, int64_t ldy, int64_t M, int64_t K, int64_t N,
                                 hipStream_t s) {
@@ -537,9 +564,20 @@ hipError_t launch_prefill_dense(const uint16_t* W, int64_t ldw, const uint16_t* 
   a.ldw = ldw;
   if (a.tiles_m == 0 || a.tiles_n == 0) return hipSuccess;
   if (K < 8 || K % 8 != 0) return hipErrorInvalidValue;
-  const size_t lds = size_t(4) * kTileBytes;
-  hipLaunchKernelGGL(dense_kernel, dim3(grid_size(a)), dim3(256), lds, s, a);
-  return hipGetLastError();
+  // Block shape: the largest of 256 x 256, 256 x 128, 128 x 128 that gives at
+  // least 60% of the CUs a block (measured on the layer shapes, N = 64-4096:
+  // a larger block on fewer CUs beats a smaller one that needs a second
+  // round); SWM_DENSE_BLOCK = 1 / 2 / 3 forces one.
+  const int64_t b256 = ((M + 255) / 256) * ((N + 255) / 256);
+  const int64_t b128 = ((M + 255) / 256) * ((N + 127) / 128);
+  const int64_t enough = 154;  // 0.6 x 256 CUs
+  int shape = b256 >= enough ? 1 : b128 >= enough ? 2 : 3;
+  if (const char* e = getenv("SWM_DENSE_BLOCK")) {
+    if (*e >= '1' && *e <= '3') shape = *e - '0';
+  }
+  if (shape == 1) return launch_dense<4, 4>(a, s);
+  if (shape == 2) return launch_dense<4, 2>(a, s);
+  return launch_dense<2, 2>(a, s);
 }
 
 size_t prefill_sparse_lds(const Header& h) {
