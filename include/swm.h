@@ -172,9 +172,12 @@ swm_status swm_spmspv(const swm_format* f, const void* x, int64_t ldx, void* y, 
 
 /* dense_gemm: Y = W X with a DENSE fp16 W (row-major M x K, ldw >= K, device),
  * the same X / Y conventions, any N >= 1.  The in-house dense baseline and the
- * fallback to the full product.  Source: moderate-sparsity page, Sec. 1 (a
- * sparse kernel is only useful if it beats the dense product at the same
- * shape). */
+ * fallback to the full product.  Asynchronous on stream, except that for
+ * N <= 16 (or an unaligned operand) the first call on a device, and any later
+ * call that needs a larger workspace, allocates a library-owned workspace and
+ * synchronizes the device: make such a call once before capturing a graph.
+ * Source: moderate-sparsity page, Sec. 1 (a sparse kernel is only useful if it
+ * beats the dense product at the same shape). */
 swm_status swm_dense_gemm(const void* W, int64_t ldw, const void* X, int64_t ldx, void* Y,
                           int64_t ldy, int64_t M, int64_t K, int64_t N, void* stream);
 
