@@ -461,21 +461,19 @@ __global__ __launch_bounds__(1024) void decode_seq_kernel(DecodeArgs a) {
     for (int g = 0; g < NS; ++g) {
       const uint32_t p0 = tp[2 * g];
       if (2 * g < nt) {
+        // The segment's activations and all its value chunks (chunks past the
+        // segment hold clamped duplicates and are never read).
 #pragma unroll
         for (int i = 0; i < kXI; ++i)
           *reinterpret_cast<lds_u32x4*>(static_cast<uintptr_t>(xl[i])) = xr[g][i];
+#pragma unroll
+        for (int c = 0; c < kC; ++c)
+          *reinterpret_cast<lds_u32x4*>(static_cast<uintptr_t>(buf + c * 1024 + lane * 16)) = r[g][c];
       }
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt) {
         const int jt = 2 * g + tt;
         if (jt == 0 || jt < nt) {  // tile slot 0 always exists (nt >= 1)
-          // Copy the chunks that complete this tile (chunks are used in issue order).
-          const uint32_t have = tt == 0 ? 0u : (2u * (tp[jt] - p0) + 1023u) >> 10;
-          const uint32_t need = (2u * (tp[jt + 1] - p0) + 1023u) >> 10;
-#pragma unroll
-          for (int c = 0; c < kC; ++c)
-            if (uint32_t(c) >= have && uint32_t(c) < need)
-              *reinterpret_cast<lds_u32x4*>(static_cast<uintptr_t>(buf + c * 1024 + lane * 16)) = r[g][c];
           if (jt == 0) {
 #pragma unroll
             for (int i = 0; i < kTouch; ++i) keep ^= th[i][0] ^ th[i][1] ^ th[i][2] ^ th[i][3];
