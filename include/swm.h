@@ -164,11 +164,45 @@ swm_status swm_spmm(const swm_format* f, const void* X, int64_t ldx, void* Y, in
  * packs four columns into each bitmap word, so dropping inactive columns
  * saves neither fetches nor decode work; the unaligned path skips the decode
  * of bitmap words whose four columns are all inactive.
+ * When swm_format_enable_skipping has been called on f and n <= 4, the
+ * column-run kernel runs instead: per 256-row block it builds the list of
+ * active input columns (any of the n tokens nonzero) and reads and decodes
+ * only their runs, bitmaps and pointers, then a second launch adds the
+ * column ranges' partial sums in a fixed order; results are bitwise
+ * reproducible and equal the full product up to fp32 summation order.  That
+ * path uses the handle's workspace: calls on one handle must be ordered on
+ * one stream.
  * Source: SPDP abstract (input-adaptive dynamic pruning; run-time activation
  * skipping in the spMspV kernel); "Reduced Matrix Multiplication" blog page,
  * Sec. 4.2 (an FFN down projection multiplies only the kept channels). */
 swm_status swm_spmspv(const swm_format* f, const void* x, int64_t ldx, void* y, int64_t ldy,
                       int32_t n, void* stream);
+
+/* format_enable_skipping: attach to f the column-run encoding (SWM-CR v1)
+ * that lets swm_spmspv skip zero activations, and upload it to f's device.
+ * Source: SPDP abstract (run-time skipping of zero activations in the decode
+ * spMspV kernel); "Reduced Matrix Multiplication" blog page, Sec. 4.2 (the
+ * product over the kept input channels equals the full product).
+ *  The encoding holds the same kept entries as f, regrouped column by column
+ *  inside blocks of 256 rows: entry e = b*K + k (column k of row block b) has
+ *  4 bitmap words (bit i of word q <=> row 256b + 64q + i), a run of its kept
+ *  fp16 values in row order padded to 4 values, and a uint32 exclusive prefix
+ *  of run lengths.  The handle owns the device copy (freed by
+ *  swm_format_destroy) and a workspace for the per-workgroup partial sums.
+ *  Synchronous.  Idempotent.  Call it before f is used by other threads or
+ *  streams (like creation).  *bytes (nullable) receives the encoding's size.
+ *  Errors: SWM_ERR_INVALID_ARG (null f, f on another device), SWM_ERR_OOM,
+ *  SWM_ERR_OVERFLOW, SWM_ERR_UNSUPPORTED (M or K too large), SWM_ERR_HIP. */
+swm_status swm_format_enable_skipping(swm_format* f, void* stream, uint64_t* bytes);
+
+/* colruns_encode_blob: host-only derivation of the SWM-CR v1 blob (32-byte
+ * header b"SWMC", u32 version 1, i64 M, i64 K, u32 rows per block = 256,
+ * u32 row blocks; then ptr, bits, values as described above) from a SWM-TCB v2
+ * export blob, for byte-exact checks of the encoding.  Same sizing protocol as
+ * swm_format_export: *size receives the blob size; out may be NULL to query;
+ * cap < size gives SWM_ERR_INVALID_ARG.  An invalid input blob gives the
+ * validator's status.  Source: as swm_format_enable_skipping. */
+swm_status swm_colruns_encode_blob(const void* tcb_blob, size_t size, void* out, size_t cap, size_t* size_out);
 
 /* dense_gemm: Y = W X with a DENSE fp16 W (row-major M x K, ldw >= K, device),
  * the same X / Y conventions, any N >= 1.  The in-house dense baseline and the

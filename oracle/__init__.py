@@ -13,6 +13,8 @@ Contents
 ``tcb``        an independent numpy encoder / decoder of the tiled
                column-bitmap format (SWM-TCB v1), written from its spec.
 ``exact``      exact integer brute force used to pin the fp64 reference.
+``colruns``    an independent numpy encoder / decoder of the column-run
+               encoding (SWM-CR v1) used by activation skipping.
 
 Parity status: every function here is pinned by the CPU tests in
 ``tests/test_oracle_pins.py`` against closed forms, brute force, hand-worked
@@ -22,9 +24,11 @@ pin compares against a value printed on the pages themselves.
 from .reference import masked_matmul, masked_matmul_skip, active_inputs, to_fp16
 from .tcb import tcb_encode, tcb_decode, tcb_parse, TcbFormat
 from .exact import exact_masked_matmul, fp64_error_bound
+from .colruns import colruns_encode, colruns_parse, colruns_decode, ColRuns
 
 __all__ = [
     "masked_matmul", "masked_matmul_skip", "active_inputs", "to_fp16",
     "tcb_encode", "tcb_decode", "tcb_parse", "TcbFormat",
     "exact_masked_matmul", "fp64_error_bound",
+    "colruns_encode", "colruns_parse", "colruns_decode", "ColRuns",
 ]

@@ -57,6 +57,8 @@ SIGNATURES = {
     "swm_decompress": (_i32, [_vp, _vp, _i64, _vp]),
     "swm_spmm": (_i32, [_vp, _vp, _i64, _vp, _i64, _i64, _vp]),
     "swm_spmspv": (_i32, [_vp, _vp, _i64, _vp, _i64, _i32, _vp]),
+    "swm_format_enable_skipping": (_i32, [_vp, _vp, ctypes.POINTER(_u64)]),
+    "swm_colruns_encode_blob": (_i32, [_vp, _sz, _vp, _sz, ctypes.POINTER(_sz)]),
     "swm_dense_gemm": (_i32, [_vp, _i64, _vp, _i64, _vp, _i64, _i64, _i64, _i64, _vp]),
     "swm_hbm_stream": (_i32, [_vp, _sz, _i32, _i32, _vp, _vp]),
     "swm_status_str": (ctypes.c_char_p, [_i32]),
@@ -171,6 +173,14 @@ class Format:
         _check(lib.swm_format_export(self._h, buf, size.value, ctypes.byref(size)), "swm_format_export")
         return buf.raw[:size.value]
 
+    def enable_skipping(self, stream=None) -> int:
+        """Attach the column-run encoding used by spmspv for n <= 4; returns its bytes."""
+        lib = load()
+        nbytes = _u64(0)
+        _check(lib.swm_format_enable_skipping(self._h, _stream_ptr(stream), ctypes.byref(nbytes)),
+               "swm_format_enable_skipping")
+        return int(nbytes.value)
+
     def close(self):
         if self._h:
             load().swm_format_destroy(self._h)
@@ -209,6 +219,18 @@ def encode_blob(W, mask=None, tile=(16, 64)) -> bytes:
     _check(lib.swm_encode_blob(w.ctypes.data, w.shape[1], mp, w.shape[1], w.shape[0], w.shape[1],
                                _cfg(tile), buf, size.value, ctypes.byref(size)), "swm_encode_blob")
     return buf.raw[:size.value]
+
+
+def colruns_encode_blob(tcb_blob: bytes) -> bytes:
+    """Host-only: the SWM-CR v1 column-run blob derived from a SWM-TCB v2 blob."""
+    lib = load()
+    b = ctypes.create_string_buffer(bytes(tcb_blob), max(len(tcb_blob), 1))
+    size = ctypes.c_size_t(0)
+    _check(lib.swm_colruns_encode_blob(b, len(tcb_blob), None, 0, ctypes.byref(size)), "swm_colruns_encode_blob")
+    out = ctypes.create_string_buffer(max(size.value, 1))
+    _check(lib.swm_colruns_encode_blob(b, len(tcb_blob), out, size.value, ctypes.byref(size)),
+           "swm_colruns_encode_blob")
+    return out.raw[:size.value]
 
 
 def validate_blob(blob: bytes) -> int:

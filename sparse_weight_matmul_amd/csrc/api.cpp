@@ -20,6 +20,8 @@ struct swm_format {
   void* dev_mem = nullptr;     // one allocation for every device section
   swm::DevFormat d;
   swm::DecodePlan plan;
+  void* cr_mem = nullptr;  // column-run encoding for activation skipping (optional)
+  swm::DevColRuns cr;
 };
 
 namespace {
@@ -274,16 +276,86 @@ swm_status swm_size_dry_run(int64_t M, int64_t K, uint64_t nnz, const swm_tile_c
 swm_status swm_format_destroy(swm_format* f) {
   if (!f) return SWM_OK;
   swm_status st = SWM_OK;
-  if (f->dev_mem) {
+  if (f->dev_mem || f->cr_mem) {
     int cur = 0;
     (void)hipGetDevice(&cur);
     if (cur != f->device) (void)hipSetDevice(f->device);
-    hipError_t e = hipFree(f->dev_mem);
+    if (f->dev_mem) {
+      hipError_t e = hipFree(f->dev_mem);
+      if (e != hipSuccess) st = hip_fail(e);
+    }
+    if (f->cr_mem) {
+      hipError_t e = hipFree(f->cr_mem);
+      if (e != hipSuccess) st = hip_fail(e);
+    }
     if (cur != f->device) (void)hipSetDevice(cur);
-    if (e != hipSuccess) st = hip_fail(e);
   }
   delete f;
   return st;
+}
+
+swm_status swm_colruns_encode_blob(const void* tcb_blob, size_t size, void* out, size_t cap, size_t* size_out) {
+  if (!tcb_blob || !size_out) return SWM_ERR_INVALID_ARG;
+  swm::ColRunsHost c;
+  swm_status st = swm::colruns_from_tcb(tcb_blob, size, &c);
+  if (st != SWM_OK) return st;
+  const size_t need = swm::colruns_blob_bytes(c);
+  *size_out = need;
+  if (!out) return SWM_OK;
+  if (cap < need) return SWM_ERR_INVALID_ARG;
+  swm::colruns_write_blob(c, static_cast<uint8_t*>(out));
+  return SWM_OK;
+}
+
+swm_status swm_format_enable_skipping(swm_format* f, void* stream, uint64_t* bytes) {
+  if (!f) return SWM_ERR_INVALID_ARG;
+  if (!on_current_device(f)) return SWM_ERR_INVALID_ARG;
+  if (f->cr_mem) {
+    if (bytes) *bytes = f->cr.bytes;
+    return SWM_OK;
+  }
+  if (f->h.m > (int64_t(1) << 31) - 256 || f->h.k > (int64_t(1) << 31) - 64) return SWM_ERR_UNSUPPORTED;
+  swm::ColRunsHost c;
+  swm_status st = swm::colruns_from_tcb(f->blob.data(), f->blob.size(), &c);
+  if (st != SWM_OK) return st;
+  const swm::ColRunsPlan plan = swm::plan_colruns(c.m, c.k);
+  const uint64_t E = uint64_t(c.mb) * uint64_t(c.k);
+  const size_t b_ptr = 4 * (E + 1), b_bits = 32 * E, b_vals = 2 * c.values.size() + 16;
+  const size_t b_part = 4 * size_t(plan.mb) * size_t(plan.splits) * 4 * 256;
+  size_t off = 0;
+  const size_t o_ptr = off;
+  off = align_up(off + b_ptr, 256);
+  const size_t o_bits = off;
+  off = align_up(off + b_bits, 256);
+  const size_t o_vals = off;
+  off = align_up(off + b_vals, 256);
+  const size_t o_part = off;
+  off = align_up(off + b_part, 256);
+  void* mem = nullptr;
+  if (hipMalloc(&mem, off) != hipSuccess) return SWM_ERR_OOM;
+  uint8_t* base = static_cast<uint8_t*>(mem);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = hipMemsetAsync(base, 0, off, s);
+  if (e == hipSuccess) e = hipMemcpyAsync(base + o_ptr, c.ptr.data(), b_ptr, hipMemcpyHostToDevice, s);
+  if (e == hipSuccess && E) e = hipMemcpyAsync(base + o_bits, c.bits.data(), b_bits, hipMemcpyHostToDevice, s);
+  if (e == hipSuccess && !c.values.empty())
+    e = hipMemcpyAsync(base + o_vals, c.values.data(), 2 * c.values.size(), hipMemcpyHostToDevice, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) {
+    (void)hipFree(mem);
+    return hip_fail(e);
+  }
+  f->cr.m = c.m;
+  f->cr.k = c.k;
+  f->cr.ptr = reinterpret_cast<const uint32_t*>(base + o_ptr);
+  f->cr.bits = reinterpret_cast<const uint64_t*>(base + o_bits);
+  f->cr.vals = reinterpret_cast<const uint16_t*>(base + o_vals);
+  f->cr.partials = reinterpret_cast<float*>(base + o_part);
+  f->cr.plan = plan;
+  f->cr.bytes = b_ptr + b_bits + 2 * c.values.size();
+  f->cr_mem = mem;
+  if (bytes) *bytes = f->cr.bytes;
+  return SWM_OK;
 }
 
 swm_status swm_decompress(const swm_format* f, void* W_dev, int64_t ldw, void* stream) {
@@ -330,6 +402,13 @@ swm_status swm_spmm(const swm_format* f, const void* X, int64_t ldx, void* Y, in
 swm_status swm_spmspv(const swm_format* f, const void* x, int64_t ldx, void* y, int64_t ldy,
                       int32_t n, void* stream) {
   if (n < 1 || n > 16) return SWM_ERR_INVALID_ARG;
+  if (f && f->cr_mem && n <= 4) {
+    if (!x || !y || ldx < f->h.k || ldy < f->h.m || ldx <= 0 || ldy <= 0) return SWM_ERR_INVALID_ARG;
+    if (!on_current_device(f)) return SWM_ERR_INVALID_ARG;
+    SWM_HIP(swm::launch_spmspv_cr(f->cr, static_cast<const uint16_t*>(x), ldx, static_cast<uint16_t*>(y), ldy, n,
+                                  static_cast<hipStream_t>(stream)));
+    return SWM_OK;
+  }
   return run_products(f, x, ldx, y, ldy, n, true, static_cast<hipStream_t>(stream));
 }
 

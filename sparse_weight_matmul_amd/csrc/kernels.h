@@ -40,6 +40,26 @@ size_t decode_partial_floats(const Header& h, const DecodePlan& p);
 hipError_t launch_decode(const DevFormat& f, const DecodePlan& p, const uint16_t* X, int64_t ldx,
                          uint16_t* Y, int64_t ldy, int n, bool skip, hipStream_t s);
 
+// Activation-skipping decode over the SWM-CR v1 column-run encoding.
+constexpr int kCrMaxCols = 512;  // input columns per workgroup
+struct ColRunsPlan {
+  int mb = 0;      // 256-row blocks
+  int splits = 0;  // column ranges (S)
+  int cps = 0;     // columns per range
+};
+struct DevColRuns {
+  int64_t m = 0, k = 0;
+  const uint32_t* ptr = nullptr;   // mb*k + 1
+  const uint64_t* bits = nullptr;  // mb*k*4
+  const uint16_t* vals = nullptr;  // padded runs + 8 bytes of slack
+  float* partials = nullptr;       // mb*splits*4*256
+  ColRunsPlan plan;
+  uint64_t bytes = 0;              // ptr + bits + values
+};
+ColRunsPlan plan_colruns(int64_t M, int64_t K);
+hipError_t launch_spmspv_cr(const DevColRuns& c, const uint16_t* x, int64_t ldx, uint16_t* y, int64_t ldy,
+                            int n, hipStream_t s);
+
 hipError_t launch_decompress(const DevFormat& f, uint16_t* W, int64_t ldw, hipStream_t s);
 
 // HBM read-bandwidth calibration: `blocks` workgroups of 256 threads stream `bytes`.

@@ -1,0 +1,296 @@
+// Activation-skipping decode (spMspV) over the SWM-CR v1 column-run encoding.
+//
+// Method: "Unified Static-Dynamic Pruning for Efficient LLM Inference" (SPDP),
+// abstract -- at decode time the input-adaptive (dynamic) sparsity of the
+// activations is exploited by a sparse-matrix x sparse-vector kernel that
+// skips zero activations at run time.  "Reduced Matrix Multiplication" (blog
+// page, Sec. 4.2) states the identity it rests on: input channels whose
+// activation is zero contribute nothing, so the product over the kept
+// channels equals the full product.
+//
+// gfx950 design.  A workgroup (4 waves) owns a 256-row block b and a range of
+// cps input columns (split s), so the grid is S x Mb workgroups (about four
+// per CU).  Consecutive workgroup ids share the column range, so their
+// activation reads hit in L2.
+//  1. Active columns: each thread tests up to two columns (any of the n <= 4
+//     tokens nonzero); a wave ballot and v_mbcnt give each active column its
+//     slot in a list ordered by (round, wave, lane), so the list is a
+//     deterministic function of x.  The list, the columns' activations (as
+//     fp32) and their run bounds go to LDS.  The run pointers of the whole
+//     range are read in this pass (8 bytes per column), so the runs need no
+//     extra round trip later; inactive columns' runs and bitmaps are never
+//     read.
+//  2. Each wave takes every fourth list entry, in batches of 16: one vector
+//     load brings the batch's 4 x 16 bitmap words (lane 4i + q = word q of
+//     slot i) and, in the same round trip, all 16 runs are requested (8 bytes
+//     per lane, clamped into the run).  Each run is copied to one of the
+//     wave's four LDS slots (used in turn) when it arrives.  With under 30 KiB
+//     of LDS per workgroup, every workgroup of the grid is resident at once,
+//     so their latency phases overlap.  Decode per 64-row word q: v_readlane
+//     moves the word to SGPRs, v_mbcnt gives the lane's rank, a halfword read
+//     at run base + 2 rank the value, v_cndmask on the SGPR word zeroes lanes
+//     whose bit is clear, and n fp32 FMAs accumulate (the kernel is
+//     instantiated per n).  Lane l holds rows 64q + l, q = 0..3, for every
+//     token.
+//  3. The four waves' sums are added in LDS in wave order and written as the
+//     workgroup's partial (256 rows x n).  A second launch adds the S
+//     partials of each row in a fixed order (four contiguous groups of
+//     splits, then the groups) and stores fp16 Y.  (A last-arriving
+//     workgroup doing that instead needs an agent-scope release per
+//     workgroup; on this chip that writes back the XCD's L2 each time and was
+//     measured 7x slower than the whole product.)  Every sum runs in a fixed
+//     order, so results are bitwise reproducible.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+
+#include "kernels.h"
+
+namespace swm {
+namespace {
+
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) u32x2 lds_u32x2;
+typedef __attribute__((address_space(3))) uint16_t lds_u16;
+
+constexpr int kCrBatch = 16;  // list entries per wave batch
+constexpr int kCrSlots = 4;   // LDS run slots per wave
+
+struct CrArgs {
+  const uint32_t* ptr;   // mb*K + 1
+  const uint64_t* bits;  // mb*K*4
+  const uint16_t* vals;  // padded runs (+ 8 bytes of slack)
+  const uint16_t* x;     // token-major n x K
+  uint16_t* y;           // token-major n x M
+  float* partials;       // [mb][S][4][256]
+  int64_t ldx, ldy;
+  int M, K, n, mb, S, cps;
+};
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p));
+}
+
+template <int kN>
+__global__ __launch_bounds__(256) void spmspv_cr_kernel(CrArgs a) {
+  __shared__ uint16_t s_col[kCrMaxCols];
+  __shared__ u32x2 s_p[kCrMaxCols + 1];      // run [start, end) of each listed column
+  __shared__ f32x4 s_x[kCrMaxCols + 1];      // entry kCrMaxCols stays zero: unused batch slots read it
+  __shared__ uint32_t s_cnt[8];
+  // kCrSlots run slots of 512 B per wave, reused in turn (a wave's LDS
+  // accesses complete in order); 16 B of slack: a lane whose bit is clear may
+  // read the halfword just past the last slot (its value is discarded).  The
+  // wave sums of step 3 reuse this area (16 KiB).
+  __shared__ __attribute__((aligned(16))) uint32_t s_run[4 * 4 * 256 + 4];
+  const int tid = int(threadIdx.x);
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int s = int(blockIdx.x) / a.mb, b = int(blockIdx.x) % a.mb;
+  const int k0 = s * a.cps;
+  const int kend = min(k0 + a.cps, a.K);
+  const uint64_t ebase = uint64_t(b) * uint64_t(a.K) + uint64_t(k0);
+
+  // ---- 1. active columns of [k0, kend), in (round, wave, lane) order, with
+  // their activations and run bounds (the pointers are read for every column
+  // of the range, so the runs can be requested together with the bitmaps)
+  bool act[2];
+  uint64_t bal[2];
+  f32x4 xv[2];
+  u32x2 pr[2];
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    const int k = k0 + r * 256 + tid;
+    bool on = false;
+    f32x4 v = {0.f, 0.f, 0.f, 0.f};
+    u32x2 p = {0u, 0u};
+    if (k < kend) {
+#pragma unroll
+      for (int t = 0; t < kN; ++t) {
+        const uint16_t h = a.x[int64_t(t) * a.ldx + k];
+        v[t] = float(__builtin_bit_cast(_Float16, h));
+        on |= (h & 0x7FFFu) != 0;
+      }
+      p[0] = a.ptr[ebase + uint64_t(k - k0)];
+      p[1] = a.ptr[ebase + uint64_t(k - k0) + 1];
+    }
+    act[r] = on;
+    xv[r] = v;
+    pr[r] = p;
+    bal[r] = __builtin_amdgcn_ballot_w64(on);
+    if (lane == 0) s_cnt[r * 4 + wave] = uint32_t(__builtin_popcountll(bal[r]));
+  }
+  if (tid == 0) {
+    s_x[kCrMaxCols] = f32x4{0.f, 0.f, 0.f, 0.f};
+    s_p[kCrMaxCols] = u32x2{0u, 0u};
+  }
+  __syncthreads();
+  int L = 0, base0 = 0, base1 = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    if (i == wave) base0 = L;
+    if (i == 4 + wave) base1 = L;
+    L += int(s_cnt[i]);
+  }
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    if (act[r]) {
+      const uint32_t rank =
+          __builtin_amdgcn_mbcnt_hi(uint32_t(bal[r] >> 32), __builtin_amdgcn_mbcnt_lo(uint32_t(bal[r]), 0u));
+      const int pos = (r == 0 ? base0 : base1) + int(rank);
+      s_col[pos] = uint16_t(r * 256 + tid);
+      s_x[pos] = xv[r];
+      s_p[pos] = pr[r];
+    }
+  }
+  __syncthreads();
+
+  // ---- 2. this wave's entries: wave, wave + 4, ...
+  f32x4 acc[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) acc[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const uint32_t slots = lds_addr(s_run) + uint32_t(wave) * (kCrSlots * 512);
+  for (int jb = wave; jb < L; jb += 4 * kCrBatch) {
+    const int nb = min(kCrBatch, (L - jb + 3) / 4);  // entries jb + 4i < L, i < nb
+    // Run bounds of the batch (lane i < 16: slot i; slots past nb repeat the
+    // last entry) and bitmap words (lane 4i + q: word q of slot i).
+    const u32x2 pb = s_p[jb + 4 * min(lane & 15, nb - 1)];
+    const int lb = min(lane >> 2, nb - 1);
+    const uint32_t cb = s_col[jb + 4 * lb];
+    const uint64_t bv = a.bits[(ebase + cb) * 4 + uint64_t(lane & 3)];
+    const uint32_t bv_lo = uint32_t(bv), bv_hi = uint32_t(bv >> 32);
+    // All runs of the batch in flight with the bitmaps: 8 bytes per lane,
+    // clamped into the run (runs are padded to 4 values; an empty run reads
+    // the 8 bytes at its start, which the allocation's slack covers).
+    u32x2 rr[kCrBatch];
+#pragma unroll
+    for (int i = 0; i < kCrBatch; ++i) {
+      const uint32_t p0 = __builtin_amdgcn_readlane(pb[0], i);
+      const uint32_t p1 = __builtin_amdgcn_readlane(pb[1], i);
+      const uint32_t last = p1 > p0 ? p1 - 4u : p0;
+      const uint32_t off = min(p0 + 4u * uint32_t(lane), last);
+      rr[i] = *reinterpret_cast<const u32x2*>(a.vals + off);
+    }
+    // Branch-free over the batch (a branch per slot lets the compiler sink
+    // the run loads and wait for all of them first): slots past nb decode a
+    // duplicate run against the zero activation entry.
+#pragma unroll
+    for (int i = 0; i < kCrBatch; ++i) {
+      const uint32_t slot = slots + uint32_t(i % kCrSlots) * 512u;
+      *reinterpret_cast<lds_u32x2*>(static_cast<uintptr_t>(slot + 8u * uint32_t(lane))) = rr[i];
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      const f32x4 xs = s_x[i < nb ? jb + 4 * i : kCrMaxCols];
+      uint32_t base = slot;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const uint32_t lo = __builtin_amdgcn_readlane(bv_lo, 4 * i + q);
+        const uint32_t hi = __builtin_amdgcn_readlane(bv_hi, 4 * i + q);
+        const uint64_t w = uint64_t(lo) | (uint64_t(hi) << 32);
+        const uint32_t rank = __builtin_amdgcn_mbcnt_hi(hi, __builtin_amdgcn_mbcnt_lo(lo, 0u));
+        const uint32_t d = *reinterpret_cast<const lds_u16*>(static_cast<uintptr_t>(base + 2u * rank));
+        base += 2u * uint32_t(__builtin_popcountll(w));
+        // zero where the lane's bit is clear: v_cndmask on the SGPR word
+        uint32_t dz;
+        asm("v_cndmask_b32_e64 %0, 0, %1, %2" : "=v"(dz) : "v"(d), "s"(w));
+        const float v = float(__builtin_bit_cast(_Float16, uint16_t(dz)));
+#pragma unroll
+        for (int t = 0; t < kN; ++t) acc[q][t] = __builtin_fmaf(v, xs[t], acc[q][t]);
+      }
+    }
+  }
+
+  // ---- 3. workgroup partial (wave sums in wave order)
+  __syncthreads();  // every wave is done with its run slots
+  float* red = reinterpret_cast<float*>(s_run);  // [wave][token][256 rows]
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+#pragma unroll
+    for (int t = 0; t < kN; ++t) red[(wave * 4 + t) * 256 + q * 64 + lane] = acc[q][t];
+  __syncthreads();
+  float* part = a.partials + (size_t(b) * a.S + s) * 4 * 256;
+#pragma unroll
+  for (int t = 0; t < kN; ++t) {
+    const float v = ((red[(0 * 4 + t) * 256 + tid] + red[(1 * 4 + t) * 256 + tid]) + red[(2 * 4 + t) * 256 + tid]) +
+                    red[(3 * 4 + t) * 256 + tid];
+    part[t * 256 + tid] = v;
+  }
+}
+
+// Sum of the S partials of 64 rows of one token: workgroup (b, quarter, t),
+// 4 waves; wave w adds splits [w*S/4, (w+1)*S/4) in order with independent
+// (unrolled) loads, then the four wave sums are added in wave order and the
+// result is rounded once to fp16.
+__global__ __launch_bounds__(256) void spmspv_cr_reduce(CrArgs a) {
+  __shared__ float s_sum[4][64];
+  const int tid = int(threadIdx.x), lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int b = int(blockIdx.x) / 4, rq = int(blockIdx.x) % 4, t = int(blockIdx.y);
+  const int r = rq * 64 + lane;
+  const int s0 = (a.S * wave) / 4, s1 = (a.S * (wave + 1)) / 4;
+  const float* pb = a.partials + (size_t(b) * a.S * 4 + t) * 256 + r;
+  float v = 0.f;
+  int ss = s0;
+  for (; ss + 8 <= s1; ss += 8) {
+    float u[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) u[i] = pb[size_t(ss + i) * 4 * 256];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v += u[i];
+  }
+  for (; ss < s1; ++ss) v += pb[size_t(ss) * 4 * 256];
+  s_sum[wave][lane] = v;
+  __syncthreads();
+  if (wave == 0) {
+    const float sum = ((s_sum[0][lane] + s_sum[1][lane]) + s_sum[2][lane]) + s_sum[3][lane];
+    const int m = b * 256 + r;
+    if (m < a.M) a.y[int64_t(t) * a.ldy + m] = __builtin_bit_cast(uint16_t, _Float16(sum));
+  }
+}
+
+}  // namespace
+
+ColRunsPlan plan_colruns(int64_t M, int64_t K) {
+  ColRunsPlan p;
+  p.mb = int((M + 255) / 256);
+  const int64_t want = std::max<int64_t>((1024 + p.mb - 1) / p.mb, (K + kCrMaxCols - 1) / kCrMaxCols);
+  int64_t cps = (K + want - 1) / want;
+  if (cps < 1) cps = 1;
+  p.cps = int(cps);
+  p.splits = int((K + cps - 1) / cps);
+  return p;
+}
+
+hipError_t launch_spmspv_cr(const DevColRuns& c, const uint16_t* x, int64_t ldx, uint16_t* y, int64_t ldy,
+                            int n, hipStream_t s) {
+  if (n < 1 || n > 4 || c.plan.cps > kCrMaxCols) return hipErrorInvalidValue;
+  CrArgs a;
+  a.ptr = c.ptr;
+  a.bits = c.bits;
+  a.vals = c.vals;
+  a.x = x;
+  a.y = y;
+  a.partials = c.partials;
+  a.ldx = ldx;
+  a.ldy = ldy;
+  a.M = int(c.m);
+  a.K = int(c.k);
+  a.n = n;
+  a.mb = c.plan.mb;
+  a.S = c.plan.splits;
+  a.cps = c.plan.cps;
+  if (a.mb == 0 || a.S == 0) return hipSuccess;
+  const dim3 grid(unsigned(a.mb) * unsigned(a.S));
+  switch (n) {
+    case 1: hipLaunchKernelGGL(spmspv_cr_kernel<1>, grid, dim3(256), 0, s, a); break;
+    case 2: hipLaunchKernelGGL(spmspv_cr_kernel<2>, grid, dim3(256), 0, s, a); break;
+    case 3: hipLaunchKernelGGL(spmspv_cr_kernel<3>, grid, dim3(256), 0, s, a); break;
+    default: hipLaunchKernelGGL(spmspv_cr_kernel<4>, grid, dim3(256), 0, s, a); break;
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(spmspv_cr_reduce, dim3(unsigned(a.mb) * 4u, unsigned(n)), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace swm

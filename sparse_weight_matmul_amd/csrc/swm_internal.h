@@ -46,4 +46,19 @@ swm_status validate_blob(const void* buf, size_t size, Header* h);
 
 void fill_info(const Header& h, swm_format_info* info);
 
+// SWM-CR v1 column-run encoding (activation skipping): kept entries grouped
+// by input column inside blocks of kColRunRows rows.
+constexpr int kColRunRows = 256;
+constexpr size_t kColRunHeaderBytes = 32;
+struct ColRunsHost {
+  int64_t m = 0, k = 0, mb = 0;
+  std::vector<uint32_t> ptr;     // mb*k + 1
+  std::vector<uint64_t> bits;    // mb*k*4
+  std::vector<uint16_t> values;  // padded runs
+};
+// Derive the encoding from a SWM-TCB v2 blob (validated first).
+swm_status colruns_from_tcb(const void* tcb, size_t size, ColRunsHost* out);
+size_t colruns_blob_bytes(const ColRunsHost& c);
+void colruns_write_blob(const ColRunsHost& c, uint8_t* dst);
+
 }  // namespace swm

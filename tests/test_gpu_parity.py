@@ -222,6 +222,80 @@ def test_spmspv_zero_and_dense_inputs(gpu_lib, down):
     assert np.array_equal(a, b)  # nothing to skip: identical arithmetic
 
 
+# ------------------------------------------------------------------ spMspV over the column-run encoding
+@pytest.fixture(scope="module")
+def down_skip(gpu_lib, down):
+    W, mask, x, f = down
+    g = gpu_lib.format_import(f.export())
+    nbytes = g.enable_skipping()
+    assert nbytes > 0 and g.enable_skipping() == nbytes  # idempotent
+    return W, mask, x, g
+
+
+@pytest.mark.parametrize("n", [1, 2, 3, 4])
+def test_spmspv_skip_down(gpu_lib, down_skip, n):
+    W, mask, x, g = down_skip
+    y = _np(gpu_lib.spmspv(g, _t(x[:n])))
+    assert_close(y, oracle.masked_matmul_skip(W, mask, x[:n]), f"spmspv skip n={n}")
+
+
+def test_spmspv_skip_repeatable_and_deterministic(gpu_lib, down_skip):
+    # the last workgroup of each row block resets its counter: calls in a row agree bitwise
+    W, mask, x, g = down_skip
+    xs = _t(x[:4])
+    ys = [_np(gpu_lib.spmspv(g, xs)).view(np.uint16) for _ in range(3)]
+    assert np.array_equal(ys[0], ys[1]) and np.array_equal(ys[0], ys[2])
+    y1 = _np(gpu_lib.spmspv(g, _t(x[:1])))  # n changes between calls on one handle
+    assert_close(y1, oracle.masked_matmul_skip(W, mask, x[:1]), "after n=4")
+
+
+def test_spmspv_skip_zero_dense_and_fallback(gpu_lib, down_skip):
+    W, mask, x, g = down_skip
+    z = np.zeros((3, W.shape[1]), dtype=np.float16)
+    z[1, 7] = np.float16(-0.0)
+    assert np.all(_np(gpu_lib.spmspv(g, _t(z))).view(np.uint16) == 0)  # nothing active: +0 everywhere
+    xd = np.random.default_rng(6).standard_normal((4, W.shape[1])).astype(np.float16)
+    assert_close(_np(gpu_lib.spmspv(g, _t(xd))), oracle.masked_matmul(W, mask, xd), "all columns active")
+    x5 = x[:4].copy()
+    x5 = np.concatenate([x5, x[:1]], axis=0)  # n = 5: the full-product path
+    assert_close(_np(gpu_lib.spmspv(g, _t(x5))), oracle.masked_matmul_skip(W, mask, x5), "n=5 fallback")
+    assert_close(_np(gpu_lib.spmm(g, _t(x[:4]))), oracle.masked_matmul(W, mask, x[:4]), "spmm unaffected")
+
+
+@pytest.mark.parametrize("M,K,density,n,zero_frac", [
+    (1, 1, 1.0, 1, 0.0), (300, 70, 0.5, 3, 0.5), (257, 1000, 0.3, 4, 0.7), (513, 2049, 0.5, 2, 0.9),
+    (100, 513, 1.0, 1, 0.0), (4096, 64, 0.5, 4, 0.5), (4096, 5, 0.5, 2, 0.4), (40, 11008, 0.5, 1, 0.7),
+])
+def test_spmspv_skip_ragged(gpu_lib, M, K, density, n, zero_frac):
+    g = np.random.default_rng(M * 31 + K)
+    W = (0.02 * g.standard_normal((M, K))).astype(np.float16)
+    mask = g.random((M, K)) < density
+    x = g.standard_normal((n, K)).astype(np.float16)
+    x[:, g.random(K) < zero_frac] = 0  # whole input channels off, as after an activation threshold
+    f = gpu_lib.sparse_compress(W, mask)
+    f.enable_skipping()
+    assert_close(_np(gpu_lib.spmspv(f, _t(x))), oracle.masked_matmul_skip(W, mask, x), f"{M}x{K} n={n}")
+
+
+def test_spmspv_skip_strided(gpu_lib):
+    import torch
+    g = np.random.default_rng(8)
+    M, K, n = 300, 700, 3
+    W = (0.02 * g.standard_normal((M, K))).astype(np.float16)
+    mask = g.random((M, K)) < 0.5
+    x = g.standard_normal((n, K)).astype(np.float16)
+    x[:, g.random(K) < 0.6] = 0
+    f = gpu_lib.sparse_compress(W, mask)
+    f.enable_skipping()
+    xb = torch.zeros((n, K + 37), dtype=torch.float16, device="cuda")
+    xb[:, :K] = _t(x)
+    yb = torch.full((n, M + 11), 7.0, dtype=torch.float16, device="cuda")
+    gpu_lib.spmspv(f, xb[:, :K], yb[:, :M])
+    out = _np(yb)
+    assert_close(out[:, :M], oracle.masked_matmul_skip(W, mask, x), "strided")
+    assert np.all(out[:, M:] == 7.0)  # outside the output view untouched
+
+
 # ------------------------------------------------------------------ dense baseline, ragged
 @pytest.mark.parametrize("M,K,N", [(1, 1, 1), (65, 129, 3), (300, 1000, 16), (100, 64, 20)])
 def test_dense_gemm_ragged(gpu_lib, M, K, N):

@@ -177,6 +177,44 @@ def test_null_mask_keeps_nonzeros():
     assert np.array_equal(dec, np.where(keep, W.view(np.uint16), 0))
 
 
+# ---------------------------------------------------------------- column-run encoding (skipping)
+def test_colruns_hand_worked_bytes():
+    d = json.load(open(os.path.join(GOLDEN, "colruns_hand_example.json")))
+    W = np.array(d["W_rows_fp16"], dtype=np.float16)
+    c = oracle.colruns_encode(W, None)
+    assert c.Mb == d["Mb"]
+    assert list(c.ptr) == d["ptr"]
+    assert [int(b) for b in c.bits] == d["bits"]
+    assert [format(int(v), "04x") for v in c.values] == d["values_hex"]
+    blob = c.blob()
+    assert blob[:32] == bytes.fromhex(d["header_hex"].replace(" ", ""))
+    Wd, keep = oracle.colruns_decode(oracle.colruns_parse(blob))
+    assert np.array_equal(Wd, W.view(np.uint16)) and np.array_equal(keep, W != 0)
+    # a row-major value order (the tiled format's is column by column in 16-row
+    # slabs) must not reproduce the hand bytes
+    Wb = W.view(np.uint16)
+    assert [format(int(v), "04x") for v in Wb[Wb != 0]] != [v for v in d["values_hex"] if v != "0000"]
+
+
+@pytest.mark.parametrize("M,K,density", [(1, 1, 1.0), (256, 64, 0.5), (257, 70, 0.3), (600, 40, 0.0),
+                                         (513, 130, 1.0), (64, 300, 0.05)])
+def test_colruns_round_trip_and_invariants(M, K, density):
+    W, mask, _ = _rand_case(M * 977 + K, M, K, 1, density, signed_zero=True)
+    c = oracle.colruns_encode(W, mask)
+    Wd, keep = oracle.colruns_decode(oracle.colruns_parse(c.blob()))
+    assert np.array_equal(keep, mask)
+    assert np.array_equal(Wd, np.where(mask, W.view(np.uint16), np.uint16(0)))  # -0 kept where the mask keeps it
+    pc = np.array([bin(int(b)).count("1") for b in c.bits]).reshape(-1, 4).sum(axis=1)
+    assert pc.sum() == int(mask.sum())
+    lens = np.diff(c.ptr.astype(np.int64))
+    assert np.all(lens % 4 == 0) and np.all(lens >= pc) and np.all(lens - pc < 4)
+    for e in range(len(lens)):
+        assert np.all(c.values[c.ptr[e] + pc[e]:c.ptr[e + 1]] == 0)
+    # same kept entries as the tiled format
+    t = oracle.tcb_encode(W, mask, TK=64)
+    assert np.array_equal(oracle.tcb_decode(t), Wd)
+
+
 # ---------------------------------------------------------------- planted mistakes
 def _mut_dropped_last_term(W, mask, X):
     return oracle.masked_matmul(W[:, :-1], None if mask is None else mask[:, :-1], X[:, :-1])
