@@ -225,7 +225,7 @@ def bench_spmspv(args, torch, swm, wl, G):
     mpad = np.zeros((Mb * 256, K), dtype=bool)
     mpad[:M] = mask
     counts = mpad.reshape(Mb, 256, K).sum(axis=1)        # (Mb, K)
-    run_bytes = 2 * (-(-counts // 4) * 4) + 32 + 4         # values (padded to 4) + 4 bitmap words + pointer
+    run_bytes = 2 * counts + 32 + 4                        # kept values + 4 bitmap words + pointer (no padding)
     out = {"metric": "decode spMspV HBM throughput on algorithmic bytes", "unit": "GB/s", "n_gpus": 1,
            "higher_is_better": True, "dtype": "f16", "data": "synthetic", "detail": {},
            "config": {"workload": "spMspV down_proj 4096x11008, 50% unstructured, x = SiLU(g)*u, |x| < tau zeroed",

@@ -57,6 +57,13 @@ typedef __attribute__((address_space(3))) uint16_t lds_u16;
 constexpr int kCrBatch = 16;  // list entries per wave batch
 constexpr int kCrSlots = 4;   // LDS run slots per wave
 
+// One batch in registers: the slots' bitmap words and one 8-byte piece of
+// each slot's run per lane.
+struct CrBatchRegs {
+  uint32_t bits_lo, bits_hi;
+  u32x2 run[kCrBatch];
+};
+
 struct CrArgs {
   const uint32_t* ptr;   // mb*K + 1
   const uint64_t* bits;  // mb*K*4
@@ -72,11 +79,56 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p));
 }
 
+// acc[t] += f16(d) * x[t] for t < kN, in the lanes whose bit of w is set.  exec
+// is narrowed to w for the FMAs (lanes with a clear bit keep acc), and
+// v_fma_mix_f32 takes the fp16 operand directly (its conversion to fp32 is
+// exact), so the word costs no select and no conversion.  The caller runs
+// with every lane of the wave active.
+template <int kN>
+__device__ __forceinline__ void fma_masked(float (&acc)[4], _Float16 d, const float (&x)[kN], uint64_t w) {
+  uint64_t sv;
+  if constexpr (kN == 1) {
+    asm("s_and_saveexec_b64 %[sv], %[w]\n\t"
+        "v_fma_mix_f32 %[a0], %[d], %[x0], %[a0] op_sel_hi:[1,0,0]\n\t"
+        "s_mov_b64 exec, %[sv]"
+        : [a0] "+v"(acc[0]), [sv] "=&s"(sv)
+        : [d] "v"(d), [x0] "v"(x[0]), [w] "s"(w)
+        : "scc");
+  } else if constexpr (kN == 2) {
+    asm("s_and_saveexec_b64 %[sv], %[w]\n\t"
+        "v_fma_mix_f32 %[a0], %[d], %[x0], %[a0] op_sel_hi:[1,0,0]\n\t"
+        "v_fma_mix_f32 %[a1], %[d], %[x1], %[a1] op_sel_hi:[1,0,0]\n\t"
+        "s_mov_b64 exec, %[sv]"
+        : [a0] "+v"(acc[0]), [a1] "+v"(acc[1]), [sv] "=&s"(sv)
+        : [d] "v"(d), [x0] "v"(x[0]), [x1] "v"(x[1]), [w] "s"(w)
+        : "scc");
+  } else if constexpr (kN == 3) {
+    asm("s_and_saveexec_b64 %[sv], %[w]\n\t"
+        "v_fma_mix_f32 %[a0], %[d], %[x0], %[a0] op_sel_hi:[1,0,0]\n\t"
+        "v_fma_mix_f32 %[a1], %[d], %[x1], %[a1] op_sel_hi:[1,0,0]\n\t"
+        "v_fma_mix_f32 %[a2], %[d], %[x2], %[a2] op_sel_hi:[1,0,0]\n\t"
+        "s_mov_b64 exec, %[sv]"
+        : [a0] "+v"(acc[0]), [a1] "+v"(acc[1]), [a2] "+v"(acc[2]), [sv] "=&s"(sv)
+        : [d] "v"(d), [x0] "v"(x[0]), [x1] "v"(x[1]), [x2] "v"(x[2]), [w] "s"(w)
+        : "scc");
+  } else {
+    asm("s_and_saveexec_b64 %[sv], %[w]\n\t"
+        "v_fma_mix_f32 %[a0], %[d], %[x0], %[a0] op_sel_hi:[1,0,0]\n\t"
+        "v_fma_mix_f32 %[a1], %[d], %[x1], %[a1] op_sel_hi:[1,0,0]\n\t"
+        "v_fma_mix_f32 %[a2], %[d], %[x2], %[a2] op_sel_hi:[1,0,0]\n\t"
+        "v_fma_mix_f32 %[a3], %[d], %[x3], %[a3] op_sel_hi:[1,0,0]\n\t"
+        "s_mov_b64 exec, %[sv]"
+        : [a0] "+v"(acc[0]), [a1] "+v"(acc[1]), [a2] "+v"(acc[2]), [a3] "+v"(acc[3]), [sv] "=&s"(sv)
+        : [d] "v"(d), [x0] "v"(x[0]), [x1] "v"(x[1]), [x2] "v"(x[2]), [x3] "v"(x[3]), [w] "s"(w)
+        : "scc");
+  }
+}
+
 template <int kN>
 __global__ __launch_bounds__(256) void spmspv_cr_kernel(CrArgs a) {
   __shared__ uint16_t s_col[kCrMaxCols];
-  __shared__ u32x2 s_p[kCrMaxCols + 1];      // run [start, end) of each listed column
-  __shared__ f32x4 s_x[kCrMaxCols + 1];      // entry kCrMaxCols stays zero: unused batch slots read it
+  __shared__ u32x2 s_p[kCrMaxCols];          // run [start, end) of each listed column
+  __shared__ float s_x[kCrMaxCols][4];        // activations of each listed column, as fp32
   __shared__ uint32_t s_cnt[8];
   // kCrSlots run slots of 512 B per wave, reused in turn (a wave's LDS
   // accesses complete in order); 16 B of slack: a lane whose bit is clear may
@@ -120,10 +172,6 @@ __global__ __launch_bounds__(256) void spmspv_cr_kernel(CrArgs a) {
     bal[r] = __builtin_amdgcn_ballot_w64(on);
     if (lane == 0) s_cnt[r * 4 + wave] = uint32_t(__builtin_popcountll(bal[r]));
   }
-  if (tid == 0) {
-    s_x[kCrMaxCols] = f32x4{0.f, 0.f, 0.f, 0.f};
-    s_p[kCrMaxCols] = u32x2{0u, 0u};
-  }
   __syncthreads();
   int L = 0, base0 = 0, base1 = 0;
 #pragma unroll
@@ -139,64 +187,100 @@ __global__ __launch_bounds__(256) void spmspv_cr_kernel(CrArgs a) {
           __builtin_amdgcn_mbcnt_hi(uint32_t(bal[r] >> 32), __builtin_amdgcn_mbcnt_lo(uint32_t(bal[r]), 0u));
       const int pos = (r == 0 ? base0 : base1) + int(rank);
       s_col[pos] = uint16_t(r * 256 + tid);
-      s_x[pos] = xv[r];
+      *reinterpret_cast<f32x4*>(s_x[pos]) = xv[r];
       s_p[pos] = pr[r];
     }
   }
   __syncthreads();
 
-  // ---- 2. this wave's entries: wave, wave + 4, ...
-  f32x4 acc[4];
+  // ---- 2. this wave's entries j = wave + 4 e, e = 0 .. nw-1, in batches of
+  // kCrBatch; batch g + 1 is fetched before batch g is decoded, so only the
+  // first batch's round trip is exposed.
+  float acc[4][4];
 #pragma unroll
-  for (int q = 0; q < 4; ++q) acc[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int q = 0; q < 4; ++q)
+#pragma unroll
+    for (int t = 0; t < 4; ++t) acc[q][t] = 0.f;
+  const int nw = __builtin_amdgcn_readfirstlane(L > wave ? (L - wave + 3) / 4 : 0);
   const uint32_t slots = lds_addr(s_run) + uint32_t(wave) * (kCrSlots * 512);
-  for (int jb = wave; jb < L; jb += 4 * kCrBatch) {
-    const int nb = min(kCrBatch, (L - jb + 3) / 4);  // entries jb + 4i < L, i < nb
-    // Run bounds of the batch (lane i < 16: slot i; slots past nb repeat the
-    // last entry) and bitmap words (lane 4i + q: word q of slot i).
-    const u32x2 pb = s_p[jb + 4 * min(lane & 15, nb - 1)];
-    const int lb = min(lane >> 2, nb - 1);
-    const uint32_t cb = s_col[jb + 4 * lb];
+  // Fetch of batch g: bitmap words (lane 4i + q: word q of slot i) and the 16
+  // runs, 8 bytes per lane clamped into the run (runs are padded to 4 values;
+  // an empty run reads the 8 bytes at its start, which the allocation's slack
+  // covers).  Slots past the wave's last
+  // entry repeat that entry, so the loads of a batch past the end hit in
+  // cache and need no branch.
+  auto fetch = [&](int g, CrBatchRegs& B) {
+    const int e0 = g * kCrBatch;
+    const u32x2 pb = s_p[wave + 4 * min(e0 + (lane & 15), nw - 1)];
+    const uint32_t cb = s_col[wave + 4 * min(e0 + (lane >> 2), nw - 1)];
     const uint64_t bv = a.bits[(ebase + cb) * 4 + uint64_t(lane & 3)];
-    const uint32_t bv_lo = uint32_t(bv), bv_hi = uint32_t(bv >> 32);
-    // All runs of the batch in flight with the bitmaps: 8 bytes per lane,
-    // clamped into the run (runs are padded to 4 values; an empty run reads
-    // the 8 bytes at its start, which the allocation's slack covers).
-    u32x2 rr[kCrBatch];
+    B.bits_lo = uint32_t(bv);
+    B.bits_hi = uint32_t(bv >> 32);
 #pragma unroll
     for (int i = 0; i < kCrBatch; ++i) {
       const uint32_t p0 = __builtin_amdgcn_readlane(pb[0], i);
       const uint32_t p1 = __builtin_amdgcn_readlane(pb[1], i);
       const uint32_t last = p1 > p0 ? p1 - 4u : p0;
       const uint32_t off = min(p0 + 4u * uint32_t(lane), last);
-      rr[i] = *reinterpret_cast<const u32x2*>(a.vals + off);
+      B.run[i] = *reinterpret_cast<const u32x2*>(a.vals + off);
     }
-    // Branch-free over the batch (a branch per slot lets the compiler sink
-    // the run loads and wait for all of them first): slots past nb decode a
-    // duplicate run against the zero activation entry.
+  };
+  // Decode of batch g, in groups of kCrSlots slots (entry 16 g + i for slot
+  // i; a group is skipped when its first entry does not exist, later slots
+  // past the end decode with zero activations).  The group's runs go to the
+  // wave's LDS slots; per slot and 64-row word q, v_readlane moves the word to
+  // SGPRs, v_mbcnt ranks the lane among the set bits, a halfword read fetches
+  // the value (all 16 reads of a group are in flight together) and the FMAs
+  // run with exec narrowed to the word.
+  auto decode = [&](int g, const CrBatchRegs& B) {
 #pragma unroll
-    for (int i = 0; i < kCrBatch; ++i) {
-      const uint32_t slot = slots + uint32_t(i % kCrSlots) * 512u;
-      *reinterpret_cast<lds_u32x2*>(static_cast<uintptr_t>(slot + 8u * uint32_t(lane))) = rr[i];
+    for (int i0 = 0; i0 < kCrBatch; i0 += kCrSlots) {
+      if (g * kCrBatch + i0 >= nw) break;  // uniform
+#pragma unroll
+      for (int u = 0; u < kCrSlots; ++u)
+        *reinterpret_cast<lds_u32x2*>(static_cast<uintptr_t>(slots + uint32_t(u) * 512u + 8u * uint32_t(lane))) =
+            B.run[i0 + u];
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_wave_barrier();
-      const f32x4 xs = s_x[i < nb ? jb + 4 * i : kCrMaxCols];
-      uint32_t base = slot;
+      uint64_t w[kCrSlots][4];
+      _Float16 d[kCrSlots][4];  // high halves of the registers are not used
+      float xs[kCrSlots][kN];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const uint32_t lo = __builtin_amdgcn_readlane(bv_lo, 4 * i + q);
-        const uint32_t hi = __builtin_amdgcn_readlane(bv_hi, 4 * i + q);
-        const uint64_t w = uint64_t(lo) | (uint64_t(hi) << 32);
-        const uint32_t rank = __builtin_amdgcn_mbcnt_hi(hi, __builtin_amdgcn_mbcnt_lo(lo, 0u));
-        const uint32_t d = *reinterpret_cast<const lds_u16*>(static_cast<uintptr_t>(base + 2u * rank));
-        base += 2u * uint32_t(__builtin_popcountll(w));
-        // zero where the lane's bit is clear: v_cndmask on the SGPR word
-        uint32_t dz;
-        asm("v_cndmask_b32_e64 %0, 0, %1, %2" : "=v"(dz) : "v"(d), "s"(w));
-        const float v = float(__builtin_bit_cast(_Float16, uint16_t(dz)));
+      for (int u = 0; u < kCrSlots; ++u) {
+        const int e = g * kCrBatch + i0 + u;
+        const int j = wave + 4 * min(e, nw - 1);
 #pragma unroll
-        for (int t = 0; t < kN; ++t) acc[q][t] = __builtin_fmaf(v, xs[t], acc[q][t]);
+        for (int t = 0; t < kN; ++t) xs[u][t] = e < nw ? s_x[j][t] : 0.f;
+        // byte address of word q's first value (uniform: scalar arithmetic)
+        uint32_t base = slots + uint32_t(u) * 512u;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const uint32_t lo = __builtin_amdgcn_readlane(B.bits_lo, 4 * (i0 + u) + q);
+          const uint32_t hi = __builtin_amdgcn_readlane(B.bits_hi, 4 * (i0 + u) + q);
+          w[u][q] = uint64_t(lo) | (uint64_t(hi) << 32);
+          const uint32_t rank = __builtin_amdgcn_mbcnt_hi(hi, __builtin_amdgcn_mbcnt_lo(lo, 0u));
+          d[u][q] = __builtin_bit_cast(_Float16, *reinterpret_cast<const lds_u16*>(static_cast<uintptr_t>(base + 2u * rank)));
+          base += 2u * uint32_t(__builtin_popcountll(w[u][q]));
+          asm("" : "+s"(base));  // keeps base scalar: one v_lshl_add per word
+        }
       }
+#pragma unroll
+      for (int u = 0; u < kCrSlots; ++u)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) fma_masked<kN>(acc[q], d[u][q], xs[u], w[u][q]);
+    }
+  };
+  if (nw > 0) {
+    const int G = (nw + kCrBatch - 1) / kCrBatch;
+    CrBatchRegs A, B;
+    fetch(0, A);
+    for (int g = 0;; g += 2) {
+      fetch(g + 1, B);
+      decode(g, A);
+      if (g + 1 >= G) break;
+      fetch(g + 2, A);
+      decode(g + 1, B);
+      if (g + 2 >= G) break;
     }
   }
 
@@ -218,8 +302,8 @@ __global__ __launch_bounds__(256) void spmspv_cr_kernel(CrArgs a) {
 }
 
 // Sum of the S partials of 64 rows of one token: workgroup (b, quarter, t),
-// 4 waves; wave w adds splits [w*S/4, (w+1)*S/4) in order with independent
-// (unrolled) loads, then the four wave sums are added in wave order and the
+// 4 waves; wave w adds splits [w S / 4, (w + 1) S / 4) in order, 8 loads in
+// flight at a time, then the four wave sums are added in wave order and the
 // result is rounded once to fp16.
 __global__ __launch_bounds__(256) void spmspv_cr_reduce(CrArgs a) {
   __shared__ float s_sum[4][64];
