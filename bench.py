@@ -230,7 +230,7 @@ def bench_spmspv(args, torch, swm, wl, G):
            "higher_is_better": True, "dtype": "f16", "data": "synthetic", "detail": {},
            "config": {"workload": "spMspV down_proj 4096x11008, 50% unstructured, x = SiLU(g)*u, |x| < tau zeroed",
                       "tau": args.tau, "column_run_bytes": cr_bytes[0], "tiled_format_bytes": fb}}
-    for n in (1, 4):
+    for n in (1, 2, 4):
         active = np.any(x[:n] != 0, axis=0)
         alg = int(run_bytes[:, active].sum()) + 2 * K * n + 2 * M * n
         y = torch.empty((n, M), dtype=torch.float16, device="cuda")

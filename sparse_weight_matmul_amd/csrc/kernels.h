@@ -41,7 +41,7 @@ hipError_t launch_decode(const DevFormat& f, const DecodePlan& p, const uint16_t
                          uint16_t* Y, int64_t ldy, int n, bool skip, hipStream_t s);
 
 // Activation-skipping decode over the SWM-CR v1 column-run encoding.
-constexpr int kCrMaxCols = 512;  // input columns per workgroup
+constexpr int kCrMaxCols = 1024;  // input columns per workgroup (one per thread)
 struct ColRunsPlan {
   int mb = 0;      // 256-row blocks
   int splits = 0;  // column ranges (S)
@@ -51,8 +51,8 @@ struct DevColRuns {
   int64_t m = 0, k = 0;
   const uint32_t* ptr = nullptr;   // mb*k + 1
   const uint64_t* bits = nullptr;  // mb*k*4
-  const uint16_t* vals = nullptr;  // padded runs + 8 bytes of slack
-  float* partials = nullptr;       // mb*splits*4*256
+  const uint16_t* vals = nullptr;  // padded runs + 16 bytes of slack
+  float* partials = nullptr;       // mb*splits*4*256 per-workgroup partial sums
   ColRunsPlan plan;
   uint64_t bytes = 0;              // ptr + bits + values
 };

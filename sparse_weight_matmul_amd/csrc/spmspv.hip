@@ -8,38 +8,38 @@
 // activation is zero contribute nothing, so the product over the kept
 // channels equals the full product.
 //
-// gfx950 design.  A workgroup (4 waves) owns a 256-row block b and a range of
-// cps input columns (split s), so the grid is S x Mb workgroups (about four
-// per CU).  Consecutive workgroup ids share the column range, so their
-// activation reads hit in L2.
-//  1. Active columns: each thread tests up to two columns (any of the n <= 4
-//     tokens nonzero); a wave ballot and v_mbcnt give each active column its
-//     slot in a list ordered by (round, wave, lane), so the list is a
-//     deterministic function of x.  The list, the columns' activations (as
-//     fp32) and their run bounds go to LDS.  The run pointers of the whole
-//     range are read in this pass (8 bytes per column), so the runs need no
-//     extra round trip later; inactive columns' runs and bitmaps are never
-//     read.
-//  2. Each wave takes every fourth list entry, in batches of 16: one vector
-//     load brings the batch's 4 x 16 bitmap words (lane 4i + q = word q of
-//     slot i) and, in the same round trip, all 16 runs are requested (8 bytes
-//     per lane, clamped into the run).  Each run is copied to one of the
-//     wave's four LDS slots (used in turn) when it arrives.  With under 30 KiB
-//     of LDS per workgroup, every workgroup of the grid is resident at once,
-//     so their latency phases overlap.  Decode per 64-row word q: v_readlane
+// gfx950 design.  A workgroup (16 waves, one per CU) owns a 256-row block b
+// and a range of cps <= 1024 input columns (split s); the grid is S x Mb
+// workgroups, about one per CU.
+//  1. Active columns: each thread tests one column (any of the n <= 4 tokens
+//     nonzero); a wave ballot and v_mbcnt give each active column its slot in
+//     a list ordered by (wave, lane), so the list is a deterministic function
+//     of x.  The list, the columns' activations (as fp32) and their run
+//     bounds go to LDS.  The run pointers of the whole range are read in this
+//     pass (8 bytes per column), so the runs need no extra round trip later;
+//     inactive columns' runs and bitmaps are never read.
+//  2. Wave w takes list entries w, w + 16, ..., in batches of 16; the next
+//     batch's loads are issued before the current batch is decoded.  One
+//     vector load brings a batch's 4 x 16 bitmap words (lane 4i + q = word q
+//     of slot i) and, in the same round trip, all 16 runs are requested (8
+//     bytes per lane, clamped into the run).  Runs are copied to the wave's
+//     four LDS slots, four at a time.  Decode per 64-row word q: v_readlane
 //     moves the word to SGPRs, v_mbcnt gives the lane's rank, a halfword read
-//     at run base + 2 rank the value, v_cndmask on the SGPR word zeroes lanes
-//     whose bit is clear, and n fp32 FMAs accumulate (the kernel is
-//     instantiated per n).  Lane l holds rows 64q + l, q = 0..3, for every
+//     at run base + 2 rank the value, and v_fma_mix_f32 (fp16 operand, fp32
+//     accumulate) runs with exec narrowed to the word, so lanes whose bit is
+//     clear are untouched.  Lane l holds rows 64q + l, q = 0..3, for every
 //     token.
-//  3. The four waves' sums are added in LDS in wave order and written as the
-//     workgroup's partial (256 rows x n).  A second launch adds the S
-//     partials of each row in a fixed order (four contiguous groups of
-//     splits, then the groups) and stores fp16 Y.  (A last-arriving
-//     workgroup doing that instead needs an agent-scope release per
-//     workgroup; on this chip that writes back the XCD's L2 each time and was
-//     measured 7x slower than the whole product.)  Every sum runs in a fixed
-//     order, so results are bitwise reproducible.
+//  3. The 16 waves' sums are added in LDS in wave order and stored as the
+//     workgroup's partial (256 rows x n, fp32).  A second launch adds the S
+//     partials of each row in split order (one round of loads at S <= 16)
+//     and stores fp16 Y.  Both ways of doing that inside the first launch
+//     were measured slower on this chip: the last-arriving workgroup needs
+//     an agent-scope release per workgroup, which writes back the XCD's L2
+//     each time (several times the whole product), or partials tagged per
+//     call and read back with relaxed device-scope atomics (1.1 us slower
+//     than the second launch for down_proj, n = 1).  Every sum runs in a
+//     fixed order, so results are bitwise reproducible, and the calls keep
+//     no state on the device between launches.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -54,6 +54,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) u32x2 lds_u32x2;
 typedef __attribute__((address_space(3))) uint16_t lds_u16;
 
+constexpr int kCrWaves = 16;  // waves per workgroup
 constexpr int kCrBatch = 16;  // list entries per wave batch
 constexpr int kCrSlots = 4;   // LDS run slots per wave
 
@@ -125,16 +126,18 @@ __device__ __forceinline__ void fma_masked(float (&acc)[4], _Float16 d, const fl
 }
 
 template <int kN>
-__global__ __launch_bounds__(256) void spmspv_cr_kernel(CrArgs a) {
+__global__ __launch_bounds__(1024) void spmspv_cr_kernel(CrArgs a) {
   __shared__ uint16_t s_col[kCrMaxCols];
   __shared__ u32x2 s_p[kCrMaxCols];          // run [start, end) of each listed column
-  __shared__ float s_x[kCrMaxCols][4];        // activations of each listed column, as fp32
-  __shared__ uint32_t s_cnt[8];
+  __shared__ float s_x[kCrMaxCols][4];       // activations of each listed column, as fp32
+  __shared__ uint32_t s_cnt[kCrWaves];
   // kCrSlots run slots of 512 B per wave, reused in turn (a wave's LDS
   // accesses complete in order); 16 B of slack: a lane whose bit is clear may
-  // read the halfword just past the last slot (its value is discarded).  The
-  // wave sums of step 3 reuse this area (16 KiB).
-  __shared__ __attribute__((aligned(16))) uint32_t s_run[4 * 4 * 256 + 4];
+  // read the halfword just past the last slot (its value is not used).  The
+  // wave sums of step 3 reuse this area.
+  constexpr int kRunWords = kCrWaves * kCrSlots * 128;
+  constexpr int kRedWords = kCrWaves * kN * 256;
+  __shared__ __attribute__((aligned(16))) uint32_t s_run[(kRunWords > kRedWords ? kRunWords : kRedWords) + 4];
   const int tid = int(threadIdx.x);
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -143,16 +146,11 @@ __global__ __launch_bounds__(256) void spmspv_cr_kernel(CrArgs a) {
   const int kend = min(k0 + a.cps, a.K);
   const uint64_t ebase = uint64_t(b) * uint64_t(a.K) + uint64_t(k0);
 
-  // ---- 1. active columns of [k0, kend), in (round, wave, lane) order, with
-  // their activations and run bounds (the pointers are read for every column
-  // of the range, so the runs can be requested together with the bitmaps)
-  bool act[2];
-  uint64_t bal[2];
-  f32x4 xv[2];
-  u32x2 pr[2];
-#pragma unroll
-  for (int r = 0; r < 2; ++r) {
-    const int k = k0 + r * 256 + tid;
+  // ---- 1. active columns of [k0, kend), in (wave, lane) order, with their
+  // activations and run bounds (the pointers are read for every column of
+  // the range, so the runs can be requested together with the bitmaps)
+  {
+    const int k = k0 + tid;
     bool on = false;
     f32x4 v = {0.f, 0.f, 0.f, 0.f};
     u32x2 p = {0u, 0u};
@@ -163,37 +161,30 @@ __global__ __launch_bounds__(256) void spmspv_cr_kernel(CrArgs a) {
         v[t] = float(__builtin_bit_cast(_Float16, h));
         on |= (h & 0x7FFFu) != 0;
       }
-      p[0] = a.ptr[ebase + uint64_t(k - k0)];
-      p[1] = a.ptr[ebase + uint64_t(k - k0) + 1];
+      p[0] = a.ptr[ebase + uint64_t(tid)];
+      p[1] = a.ptr[ebase + uint64_t(tid) + 1];
     }
-    act[r] = on;
-    xv[r] = v;
-    pr[r] = p;
-    bal[r] = __builtin_amdgcn_ballot_w64(on);
-    if (lane == 0) s_cnt[r * 4 + wave] = uint32_t(__builtin_popcountll(bal[r]));
-  }
-  __syncthreads();
-  int L = 0, base0 = 0, base1 = 0;
+    const uint64_t bal = __builtin_amdgcn_ballot_w64(on);
+    if (lane == 0) s_cnt[wave] = uint32_t(__builtin_popcountll(bal));
+    __syncthreads();
+    int base = 0;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    if (i == wave) base0 = L;
-    if (i == 4 + wave) base1 = L;
-    L += int(s_cnt[i]);
-  }
-#pragma unroll
-  for (int r = 0; r < 2; ++r) {
-    if (act[r]) {
-      const uint32_t rank =
-          __builtin_amdgcn_mbcnt_hi(uint32_t(bal[r] >> 32), __builtin_amdgcn_mbcnt_lo(uint32_t(bal[r]), 0u));
-      const int pos = (r == 0 ? base0 : base1) + int(rank);
-      s_col[pos] = uint16_t(r * 256 + tid);
-      *reinterpret_cast<f32x4*>(s_x[pos]) = xv[r];
-      s_p[pos] = pr[r];
+    for (int i = 0; i < kCrWaves; ++i)
+      if (i < wave) base += int(s_cnt[i]);
+    if (on) {
+      const uint32_t rank = __builtin_amdgcn_mbcnt_hi(uint32_t(bal >> 32), __builtin_amdgcn_mbcnt_lo(uint32_t(bal), 0u));
+      const int pos = base + int(rank);
+      s_col[pos] = uint16_t(tid);
+      *reinterpret_cast<f32x4*>(s_x[pos]) = v;
+      s_p[pos] = p;
     }
   }
+  int L = 0;
+#pragma unroll
+  for (int i = 0; i < kCrWaves; ++i) L += int(s_cnt[i]);
   __syncthreads();
 
-  // ---- 2. this wave's entries j = wave + 4 e, e = 0 .. nw-1, in batches of
+  // ---- 2. this wave's entries j = wave + 16 e, e = 0 .. nw-1, in batches of
   // kCrBatch; batch g + 1 is fetched before batch g is decoded, so only the
   // first batch's round trip is exposed.
   float acc[4][4];
@@ -201,7 +192,7 @@ __global__ __launch_bounds__(256) void spmspv_cr_kernel(CrArgs a) {
   for (int q = 0; q < 4; ++q)
 #pragma unroll
     for (int t = 0; t < 4; ++t) acc[q][t] = 0.f;
-  const int nw = __builtin_amdgcn_readfirstlane(L > wave ? (L - wave + 3) / 4 : 0);
+  const int nw = __builtin_amdgcn_readfirstlane(L > wave ? (L - wave + kCrWaves - 1) / kCrWaves : 0);
   const uint32_t slots = lds_addr(s_run) + uint32_t(wave) * (kCrSlots * 512);
   // Fetch of batch g: bitmap words (lane 4i + q: word q of slot i) and the 16
   // runs, 8 bytes per lane clamped into the run (runs are padded to 4 values;
@@ -211,8 +202,8 @@ __global__ __launch_bounds__(256) void spmspv_cr_kernel(CrArgs a) {
   // cache and need no branch.
   auto fetch = [&](int g, CrBatchRegs& B) {
     const int e0 = g * kCrBatch;
-    const u32x2 pb = s_p[wave + 4 * min(e0 + (lane & 15), nw - 1)];
-    const uint32_t cb = s_col[wave + 4 * min(e0 + (lane >> 2), nw - 1)];
+    const u32x2 pb = s_p[wave + kCrWaves * min(e0 + (lane & 15), nw - 1)];
+    const uint32_t cb = s_col[wave + kCrWaves * min(e0 + (lane >> 2), nw - 1)];
     const uint64_t bv = a.bits[(ebase + cb) * 4 + uint64_t(lane & 3)];
     B.bits_lo = uint32_t(bv);
     B.bits_hi = uint32_t(bv >> 32);
@@ -248,7 +239,7 @@ __global__ __launch_bounds__(256) void spmspv_cr_kernel(CrArgs a) {
 #pragma unroll
       for (int u = 0; u < kCrSlots; ++u) {
         const int e = g * kCrBatch + i0 + u;
-        const int j = wave + 4 * min(e, nw - 1);
+        const int j = wave + kCrWaves * min(e, nw - 1);
 #pragma unroll
         for (int t = 0; t < kN; ++t) xs[u][t] = e < nw ? s_x[j][t] : 0.f;
         // byte address of word q's first value (uniform: scalar arithmetic)
@@ -290,54 +281,42 @@ __global__ __launch_bounds__(256) void spmspv_cr_kernel(CrArgs a) {
 #pragma unroll
   for (int q = 0; q < 4; ++q)
 #pragma unroll
-    for (int t = 0; t < kN; ++t) red[(wave * 4 + t) * 256 + q * 64 + lane] = acc[q][t];
+    for (int t = 0; t < kN; ++t) red[(wave * kN + t) * 256 + q * 64 + lane] = acc[q][t];
   __syncthreads();
-  float* part = a.partials + (size_t(b) * a.S + s) * 4 * 256;
+  const int t = tid >> 8, r = tid & 255;  // thread tid < 256 kN: token t, row r of the block
+  if (t < kN) {
+    float v = red[t * 256 + r];
 #pragma unroll
-  for (int t = 0; t < kN; ++t) {
-    const float v = ((red[(0 * 4 + t) * 256 + tid] + red[(1 * 4 + t) * 256 + tid]) + red[(2 * 4 + t) * 256 + tid]) +
-                    red[(3 * 4 + t) * 256 + tid];
-    part[t * 256 + tid] = v;
+    for (int w = 1; w < kCrWaves; ++w) v += red[(w * kN + t) * 256 + r];
+    a.partials[((size_t(b) * a.S + s) * 4 + t) * 256 + r] = v;
   }
 }
 
-// Sum of the S partials of 64 rows of one token: workgroup (b, quarter, t),
-// 4 waves; wave w adds splits [w S / 4, (w + 1) S / 4) in order, 8 loads in
-// flight at a time, then the four wave sums are added in wave order and the
-// result is rounded once to fp16.
+// Sum of the S partials of one row block and token (workgroup (b, t), one
+// row per thread), in split order with up to 16 loads in flight, rounded once
+// to fp16.
 __global__ __launch_bounds__(256) void spmspv_cr_reduce(CrArgs a) {
-  __shared__ float s_sum[4][64];
-  const int tid = int(threadIdx.x), lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int b = int(blockIdx.x) / 4, rq = int(blockIdx.x) % 4, t = int(blockIdx.y);
-  const int r = rq * 64 + lane;
-  const int s0 = (a.S * wave) / 4, s1 = (a.S * (wave + 1)) / 4;
-  const float* pb = a.partials + (size_t(b) * a.S * 4 + t) * 256 + r;
-  float v = 0.f;
-  int ss = s0;
-  for (; ss + 8 <= s1; ss += 8) {
-    float u[8];
+  const int b = int(blockIdx.x), t = int(blockIdx.y), r = int(threadIdx.x);
+  const float* pp = a.partials + (size_t(b) * a.S * 4 + t) * 256 + r;
+  float sum = 0.f;
+  for (int s0 = 0; s0 < a.S; s0 += 16) {
+    float u[16];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) u[i] = pb[size_t(ss + i) * 4 * 256];
+    for (int i = 0; i < 16; ++i) u[i] = s0 + i < a.S ? pp[size_t(s0 + i) * 4 * 256] : 0.f;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) v += u[i];
+    for (int i = 0; i < 16; ++i) sum += u[i];
   }
-  for (; ss < s1; ++ss) v += pb[size_t(ss) * 4 * 256];
-  s_sum[wave][lane] = v;
-  __syncthreads();
-  if (wave == 0) {
-    const float sum = ((s_sum[0][lane] + s_sum[1][lane]) + s_sum[2][lane]) + s_sum[3][lane];
-    const int m = b * 256 + r;
-    if (m < a.M) a.y[int64_t(t) * a.ldy + m] = __builtin_bit_cast(uint16_t, _Float16(sum));
-  }
+  const int m = b * 256 + r;
+  if (m < a.M) a.y[int64_t(t) * a.ldy + m] = __builtin_bit_cast(uint16_t, _Float16(sum));
 }
 
 }  // namespace
 
 ColRunsPlan plan_colruns(int64_t M, int64_t K) {
+  // about one workgroup per CU (256), at most kCrMaxCols columns each
   ColRunsPlan p;
   p.mb = int((M + 255) / 256);
-  const int64_t want = std::max<int64_t>((1024 + p.mb - 1) / p.mb, (K + kCrMaxCols - 1) / kCrMaxCols);
+  const int64_t want = std::max<int64_t>((256 + p.mb - 1) / p.mb, (K + kCrMaxCols - 1) / kCrMaxCols);
   int64_t cps = (K + want - 1) / want;
   if (cps < 1) cps = 1;
   p.cps = int(cps);
@@ -364,16 +343,16 @@ hipError_t launch_spmspv_cr(const DevColRuns& c, const uint16_t* x, int64_t ldx,
   a.S = c.plan.splits;
   a.cps = c.plan.cps;
   if (a.mb == 0 || a.S == 0) return hipSuccess;
-  const dim3 grid(unsigned(a.mb) * unsigned(a.S));
+  const dim3 grid(unsigned(a.mb) * unsigned(a.S)), block(64 * kCrWaves);
   switch (n) {
-    case 1: hipLaunchKernelGGL(spmspv_cr_kernel<1>, grid, dim3(256), 0, s, a); break;
-    case 2: hipLaunchKernelGGL(spmspv_cr_kernel<2>, grid, dim3(256), 0, s, a); break;
-    case 3: hipLaunchKernelGGL(spmspv_cr_kernel<3>, grid, dim3(256), 0, s, a); break;
-    default: hipLaunchKernelGGL(spmspv_cr_kernel<4>, grid, dim3(256), 0, s, a); break;
+    case 1: hipLaunchKernelGGL(spmspv_cr_kernel<1>, grid, block, 0, s, a); break;
+    case 2: hipLaunchKernelGGL(spmspv_cr_kernel<2>, grid, block, 0, s, a); break;
+    case 3: hipLaunchKernelGGL(spmspv_cr_kernel<3>, grid, block, 0, s, a); break;
+    default: hipLaunchKernelGGL(spmspv_cr_kernel<4>, grid, block, 0, s, a); break;
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(spmspv_cr_reduce, dim3(unsigned(a.mb) * 4u, unsigned(n)), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(spmspv_cr_reduce, dim3(unsigned(a.mb), unsigned(n)), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

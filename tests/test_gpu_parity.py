@@ -249,6 +249,34 @@ def test_spmspv_skip_repeatable_and_deterministic(gpu_lib, down_skip):
     assert_close(y1, oracle.masked_matmul_skip(W, mask, x[:1]), "after n=4")
 
 
+def test_spmspv_skip_graph_replays(gpu_lib, down_skip):
+    # the per-call tag that validates the partial sums lives in device memory and
+    # advances on every replay of a captured graph; x changes between replays
+    import torch
+    W, mask, x, g = down_skip
+    n = 2
+    xb = _t(x[:n])
+    yb = torch.empty((n, W.shape[0]), dtype=torch.float16, device="cuda")
+    gpu_lib.spmspv(g, xb, yb)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        gpu_lib.spmspv(g, xb, yb)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(11)
+    for rep in range(4):
+        xr = x[:n].copy()
+        xr[:, rng.random(W.shape[1]) < 0.3] = 0
+        xb.copy_(_t(xr))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        y_graph = yb.cpu().numpy().copy()
+        y_eager = _np(gpu_lib.spmspv(g, _t(xr)))  # eager call between replays
+        assert np.array_equal(y_graph.view(np.uint16), y_eager.view(np.uint16)), f"replay {rep}"
+        assert_close(y_graph, oracle.masked_matmul_skip(W, mask, xr), f"replay {rep}")
+
+
 def test_spmspv_skip_zero_dense_and_fallback(gpu_lib, down_skip):
     W, mask, x, g = down_skip
     z = np.zeros((3, W.shape[1]), dtype=np.float16)
