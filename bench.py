@@ -220,6 +220,9 @@ def bench_spmspv(args, torch, swm, wl, G):
     _log(f"column-run encoding for {C} rotated copies")
     cr_bytes = [f.enable_skipping() for f in fmts]
     xd = torch.from_numpy(x).cuda()
+    # the same activations before zeroing: the fused-threshold call drops |x| < tau itself
+    x_raw = wl.silu_gated_sparse(wl.CFG_SPMSPV, 0, 4, K, 0.0)
+    xrd = torch.from_numpy(x_raw).cuda()
     # kept entries per (256-row block, column): the runs the skipping kernel reads
     Mb = -(-M // 256)
     mpad = np.zeros((Mb * 256, K), dtype=bool)
@@ -242,7 +245,10 @@ def bench_spmspv(args, torch, swm, wl, G):
         t_skip = G.time(G.capture([lambda i=i: swm.spmspv(fmts[i % C], xd[:n], y) for i in range(C)]), 3) / C
         t_full = G.time(G.capture([lambda i=i: swm.spmm(fmts[i % C], xd[:n], y) for i in range(C)]), 3) / C
         t_dense = G.time(G.capture([lambda i=i: swm.dense_gemm(Wds[i % CD], xd[:n], y) for i in range(CD)]), 3) / CD
+        t_thr = G.time(G.capture([lambda i=i: swm.spmspv_threshold(fmts[i % C], xrd[:n], args.tau, y)
+                                  for i in range(C)]), 3) / C
         out["detail"][str(n)] = {
+            "fused_threshold_us": t_thr * 1e3,
             "zero_frac": float(np.mean(x[:n] == 0)), "inactive_cols": float(1 - active.mean()),
             "spmspv_us": t_skip * 1e3, "spmm_us": t_full * 1e3, "dense_us": t_dense * 1e3,
             "alg_bytes": alg, "spmspv_GBps_alg": alg / (t_skip * 1e-3) / 1e9,

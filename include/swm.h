@@ -181,6 +181,24 @@ swm_status swm_spmm(const swm_format* f, const void* X, int64_t ldx, void* Y, in
 swm_status swm_spmspv(const swm_format* f, const void* x, int64_t ldx, void* y, int64_t ldy,
                       int32_t n, void* stream);
 
+/* spmspv_threshold: swm_spmspv with input-adaptive channel selection fused
+ * in: an activation with |x[t][k]| < tau counts as zero, so
+ *   Y = (W (.) mask) x~,  x~[t][k] = (|x[t][k]| < tau) ? 0 : x[t][k].
+ * The comparison takes the fp16 activation exactly in fp32 against tau (fp32);
+ * a column whose every token is below tau is skipped like a zero column.
+ * tau = 0 gives swm_spmspv's result bitwise.  Inputs are assumed finite (a NaN
+ * activation counts as zero).
+ * Source: SPDP abstract (input-adaptive dynamic pruning in the decode spMspV
+ * kernel); "Reduced Matrix Multiplication" blog page, Sec. 4.2 (an FFN keeps
+ * only the high-response channels of its hidden activation and multiplies
+ * them with the matching part of the down projection).
+ *  Runs on the column-run path only: swm_format_enable_skipping must have been
+ *  called on f and 1 <= n <= 4, else SWM_ERR_UNSUPPORTED (nothing launched).
+ *  Same buffers, ownership, ordering and errors as swm_spmspv; tau < 0, NaN
+ *  or above 65504 gives SWM_ERR_INVALID_ARG. */
+swm_status swm_spmspv_threshold(const swm_format* f, const void* x, int64_t ldx, void* y, int64_t ldy,
+                                int32_t n, float tau, void* stream);
+
 /* format_enable_skipping: attach to f the column-run encoding (SWM-CR v1)
  * that lets swm_spmspv skip zero activations, and upload it to f's device.
  * Source: SPDP abstract (run-time skipping of zero activations in the decode

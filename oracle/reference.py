@@ -70,6 +70,24 @@ def masked_matmul_skip(W: np.ndarray, mask: np.ndarray | None, X_tok: np.ndarray
     return (Wm @ X64.T).T
 
 
+def threshold_activations(X_tok: np.ndarray, tau: float) -> np.ndarray:
+    """Input-adaptive channel selection ("Reduced Matrix Multiplication" blog
+    page, Sec. 4.2: an FFN keeps only the high-response channels of its hidden
+    activation).  An activation whose magnitude is below tau is dropped (+0);
+    one at or above tau is kept unchanged.  The comparison takes the fp16 value
+    exactly in float32 against tau as float32."""
+    X = np.asarray(X_tok, dtype=np.float16)
+    keep = np.abs(X.astype(np.float32)) >= np.float32(tau)
+    return np.where(keep, X, np.float16(0.0))
+
+
+def masked_matmul_threshold(W: np.ndarray, mask: np.ndarray | None, X_tok: np.ndarray, tau: float) -> np.ndarray:
+    """Thresholded spMspV: (1) drop activations below tau, (2) the skipping
+    product over the channels that stay active (SPDP abstract: input-adaptive
+    dynamic pruning at decode)."""
+    return masked_matmul_skip(W, mask, threshold_activations(X_tok, tau))
+
+
 def to_fp16(Y: np.ndarray) -> np.ndarray:
     """Round a float64 result to fp16, round-to-nearest-even."""
     return np.asarray(Y, dtype=np.float64).astype(np.float16)

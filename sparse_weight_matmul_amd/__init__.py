@@ -57,6 +57,7 @@ SIGNATURES = {
     "swm_decompress": (_i32, [_vp, _vp, _i64, _vp]),
     "swm_spmm": (_i32, [_vp, _vp, _i64, _vp, _i64, _i64, _vp]),
     "swm_spmspv": (_i32, [_vp, _vp, _i64, _vp, _i64, _i32, _vp]),
+    "swm_spmspv_threshold": (_i32, [_vp, _vp, _i64, _vp, _i64, _i32, ctypes.c_float, _vp]),
     "swm_format_enable_skipping": (_i32, [_vp, _vp, ctypes.POINTER(_u64)]),
     "swm_colruns_encode_blob": (_i32, [_vp, _sz, _vp, _sz, ctypes.POINTER(_sz)]),
     "swm_dense_gemm": (_i32, [_vp, _i64, _vp, _i64, _vp, _i64, _i64, _i64, _i64, _vp]),
@@ -287,6 +288,18 @@ def spmspv(fmt: Format, x, y=None, stream=None):
     y = _out(y, n, fmt.M, x)
     yp, ldy = _dev2d(y, "y", rows=n, cols=fmt.M)
     _check(lib.swm_spmspv(fmt._h, xp, ldx, yp, ldy, n, _stream_ptr(stream)), "swm_spmspv")
+    return y
+
+
+def spmspv_threshold(fmt: Format, x, tau: float, y=None, stream=None):
+    """spmspv with activations |x| < tau counted as zero (skipping must be enabled, n <= 4)."""
+    lib = load()
+    n = x.shape[0]
+    xp, ldx = _dev2d(x, "x", cols=fmt.K)
+    y = _out(y, n, fmt.M, x)
+    yp, ldy = _dev2d(y, "y", rows=n, cols=fmt.M)
+    _check(lib.swm_spmspv_threshold(fmt._h, xp, ldx, yp, ldy, n, float(tau), _stream_ptr(stream)),
+           "swm_spmspv_threshold")
     return y
 
 

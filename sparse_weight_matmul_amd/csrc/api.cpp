@@ -399,17 +399,27 @@ swm_status swm_spmm(const swm_format* f, const void* X, int64_t ldx, void* Y, in
   return run_products(f, X, ldx, Y, ldy, N, false, static_cast<hipStream_t>(stream));
 }
 
+static swm_status run_colruns(const swm_format* f, const void* x, int64_t ldx, void* y, int64_t ldy, int32_t n,
+                              float tau, void* stream) {
+  if (!x || !y || ldx < f->h.k || ldy < f->h.m || ldx <= 0 || ldy <= 0) return SWM_ERR_INVALID_ARG;
+  if (!on_current_device(f)) return SWM_ERR_INVALID_ARG;
+  SWM_HIP(swm::launch_spmspv_cr(f->cr, static_cast<const uint16_t*>(x), ldx, static_cast<uint16_t*>(y), ldy, n, tau,
+                                static_cast<hipStream_t>(stream)));
+  return SWM_OK;
+}
+
 swm_status swm_spmspv(const swm_format* f, const void* x, int64_t ldx, void* y, int64_t ldy,
                       int32_t n, void* stream) {
   if (n < 1 || n > 16) return SWM_ERR_INVALID_ARG;
-  if (f && f->cr_mem && n <= 4) {
-    if (!x || !y || ldx < f->h.k || ldy < f->h.m || ldx <= 0 || ldy <= 0) return SWM_ERR_INVALID_ARG;
-    if (!on_current_device(f)) return SWM_ERR_INVALID_ARG;
-    SWM_HIP(swm::launch_spmspv_cr(f->cr, static_cast<const uint16_t*>(x), ldx, static_cast<uint16_t*>(y), ldy, n,
-                                  static_cast<hipStream_t>(stream)));
-    return SWM_OK;
-  }
+  if (f && f->cr_mem && n <= 4) return run_colruns(f, x, ldx, y, ldy, n, 0.f, stream);
   return run_products(f, x, ldx, y, ldy, n, true, static_cast<hipStream_t>(stream));
+}
+
+swm_status swm_spmspv_threshold(const swm_format* f, const void* x, int64_t ldx, void* y, int64_t ldy,
+                                int32_t n, float tau, void* stream) {
+  if (!f || n < 1 || n > 16 || !(tau >= 0.f) || !(tau <= 65504.f)) return SWM_ERR_INVALID_ARG;
+  if (!f->cr_mem || n > 4) return SWM_ERR_UNSUPPORTED;
+  return run_colruns(f, x, ldx, y, ldy, n, tau, stream);
 }
 
 swm_status swm_hbm_stream(const void* buf, size_t bytes, int32_t unroll, int32_t blocks,

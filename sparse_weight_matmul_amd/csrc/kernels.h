@@ -57,8 +57,9 @@ struct DevColRuns {
   uint64_t bytes = 0;              // ptr + bits + values
 };
 ColRunsPlan plan_colruns(int64_t M, int64_t K);
+// tau: activations with |x| < tau count as zero (0 = only exact zeros).
 hipError_t launch_spmspv_cr(const DevColRuns& c, const uint16_t* x, int64_t ldx, uint16_t* y, int64_t ldy,
-                            int n, hipStream_t s);
+                            int n, float tau, hipStream_t s);
 
 hipError_t launch_decompress(const DevFormat& f, uint16_t* W, int64_t ldw, hipStream_t s);
 

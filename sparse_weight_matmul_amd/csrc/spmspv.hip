@@ -73,6 +73,7 @@ struct CrArgs {
   uint16_t* y;           // token-major n x M
   float* partials;       // [mb][S][4][256]
   int64_t ldx, ldy;
+  float tau;             // |x| < tau counts as zero
   int M, K, n, mb, S, cps;
 };
 
@@ -157,9 +158,13 @@ __global__ __launch_bounds__(1024) void spmspv_cr_kernel(CrArgs a) {
     if (k < kend) {
 #pragma unroll
       for (int t = 0; t < kN; ++t) {
+        // a token's activation counts when it is nonzero and |x| >= tau
+        // (the fp16 value is exact in fp32; tau = 0 keeps every nonzero)
         const uint16_t h = a.x[int64_t(t) * a.ldx + k];
-        v[t] = float(__builtin_bit_cast(_Float16, h));
-        on |= (h & 0x7FFFu) != 0;
+        const float xv = float(__builtin_bit_cast(_Float16, h));
+        const bool keep = (h & 0x7FFFu) != 0 && __builtin_fabsf(xv) >= a.tau;
+        v[t] = keep ? xv : 0.f;
+        on |= keep;
       }
       p[0] = a.ptr[ebase + uint64_t(tid)];
       p[1] = a.ptr[ebase + uint64_t(tid) + 1];
@@ -325,7 +330,7 @@ ColRunsPlan plan_colruns(int64_t M, int64_t K) {
 }
 
 hipError_t launch_spmspv_cr(const DevColRuns& c, const uint16_t* x, int64_t ldx, uint16_t* y, int64_t ldy,
-                            int n, hipStream_t s) {
+                            int n, float tau, hipStream_t s) {
   if (n < 1 || n > 4 || c.plan.cps > kCrMaxCols) return hipErrorInvalidValue;
   CrArgs a;
   a.ptr = c.ptr;
@@ -336,6 +341,7 @@ hipError_t launch_spmspv_cr(const DevColRuns& c, const uint16_t* x, int64_t ldx,
   a.partials = c.partials;
   a.ldx = ldx;
   a.ldy = ldy;
+  a.tau = tau;
   a.M = int(c.m);
   a.K = int(c.k);
   a.n = n;

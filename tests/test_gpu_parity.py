@@ -290,6 +290,42 @@ def test_spmspv_skip_zero_dense_and_fallback(gpu_lib, down_skip):
     assert_close(_np(gpu_lib.spmm(g, _t(x[:4]))), oracle.masked_matmul(W, mask, x[:4]), "spmm unaffected")
 
 
+@pytest.mark.parametrize("n", [1, 2, 4])
+def test_spmspv_threshold_down(gpu_lib, down_skip, n):
+    # raw x = SiLU(g)*u with no zeroing; the kernel drops |x| < 0.3 itself
+    W, mask, x_zeroed, g = down_skip
+    x_raw = wl.silu_gated_sparse(wl.CFG_SPMSPV, 0, 4, W.shape[1], 0.0)[:n]
+    y = _np(gpu_lib.spmspv_threshold(g, _t(x_raw), 0.3))
+    assert_close(y, oracle.masked_matmul_threshold(W, mask, x_raw, 0.3), f"threshold n={n}")
+    # same active list and values as zeroing x first: bitwise the same result
+    y0 = _np(gpu_lib.spmspv(g, _t(x_zeroed[:n])))
+    assert np.array_equal(y.view(np.uint16), y0.view(np.uint16))
+    # tau = 0 is the plain call; tau above every |x| gives zeros
+    ya = _np(gpu_lib.spmspv_threshold(g, _t(x_raw), 0.0))
+    yb = _np(gpu_lib.spmspv(g, _t(x_raw)))
+    assert np.array_equal(ya.view(np.uint16), yb.view(np.uint16))
+    assert np.all(_np(gpu_lib.spmspv_threshold(g, _t(x_raw), 1e4)).view(np.uint16) == 0)
+
+
+def test_spmspv_threshold_errors(gpu_lib, down, down_skip):
+    import ctypes
+    import torch
+    W, mask, x, f = down                     # skipping not enabled on f
+    g = down_skip[3]
+    lib = gpu_lib.load()
+    xd = _t(x)
+    y = torch.empty((4, W.shape[0]), dtype=torch.float16, device="cuda")
+    s = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    xp, yp = ctypes.c_void_p(xd.data_ptr()), ctypes.c_void_p(y.data_ptr())
+    K, M = W.shape[1], W.shape[0]
+    assert lib.swm_spmspv_threshold(f._h, xp, K, yp, M, 1, ctypes.c_float(0.3), s) == 8    # not enabled
+    assert lib.swm_spmspv_threshold(g._h, xp, K, yp, M, 5, ctypes.c_float(0.3), s) == 8    # n > 4
+    assert lib.swm_spmspv_threshold(g._h, xp, K, yp, M, 1, ctypes.c_float(-1.0), s) == 1   # tau < 0
+    assert lib.swm_spmspv_threshold(g._h, xp, K, yp, M, 1, ctypes.c_float(float("nan")), s) == 1
+    assert lib.swm_spmspv_threshold(g._h, xp, K - 1, yp, M, 1, ctypes.c_float(0.3), s) == 1  # ldx < K
+    assert lib.swm_spmspv_threshold(g._h, xp, K, yp, M, 0, ctypes.c_float(0.3), s) == 1      # n < 1
+
+
 @pytest.mark.parametrize("M,K,density,n,zero_frac", [
     (1, 1, 1.0, 1, 0.0), (300, 70, 0.5, 3, 0.5), (257, 1000, 0.3, 4, 0.7), (513, 2049, 0.5, 2, 0.9),
     (100, 513, 1.0, 1, 0.0), (4096, 64, 0.5, 4, 0.5), (4096, 5, 0.5, 2, 0.4), (40, 11008, 0.5, 1, 0.7),

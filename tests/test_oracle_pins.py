@@ -178,6 +178,44 @@ def test_null_mask_keeps_nonzeros():
 
 
 # ---------------------------------------------------------------- column-run encoding (skipping)
+def test_threshold_hand_worked():
+    # values worked by hand from the rule (keep |x| >= tau); the tau = 0.5 case
+    # sits on the boundary, so a strict comparison fails it, and thresholding W
+    # instead of x or dropping the sign of x fails the others
+    d = json.load(open(os.path.join(GOLDEN, "threshold_hand_example.json")))
+    W = np.array(d["W"], dtype=np.float16)
+    x = np.array([d["x"]], dtype=np.float16)
+    for c in d["cases"]:
+        xk = oracle.threshold_activations(x, c["tau"])
+        assert np.array_equal(xk.astype(np.float64)[0], np.array(c["x_kept"])), c["tau"]
+        y = oracle.masked_matmul_threshold(W, None, x, c["tau"])
+        assert np.array_equal(y[0], np.array(c["y"])), c["tau"]
+
+
+def test_threshold_invariants():
+    g = np.random.default_rng(21)
+    W = (0.1 * g.standard_normal((40, 300))).astype(np.float16)
+    mask = g.random((40, 300)) < 0.5
+    x = g.standard_normal((3, 300)).astype(np.float16)
+    # tau = 0 is the plain product; tau above every |x| gives exact zeros
+    assert np.allclose(oracle.masked_matmul_threshold(W, mask, x, 0.0), oracle.masked_matmul(W, mask, x), atol=1e-12)
+    assert np.all(oracle.masked_matmul_threshold(W, mask, x, 1e4) == 0)
+    # the kept set only shrinks as tau grows, and kept values are untouched
+    prev = np.ones(x.shape, dtype=bool)
+    for tau in (0.0, 0.1, 0.5, 1.0, 2.0):
+        xk = oracle.threshold_activations(x, tau)
+        kept = xk != 0
+        assert np.all(kept <= prev) and np.array_equal(xk[kept], x[kept])
+        prev = kept
+    # a channel whose every token is below tau takes no part: changing its
+    # weights changes nothing
+    tau = 0.8
+    dead = ~np.any(np.abs(x.astype(np.float32)) >= tau, axis=0)
+    W2 = W.copy()
+    W2[:, dead] = np.float16(7.0)
+    assert np.array_equal(oracle.masked_matmul_threshold(W2, mask, x, tau), oracle.masked_matmul_threshold(W, mask, x, tau))
+
+
 def test_colruns_hand_worked_bytes():
     d = json.load(open(os.path.join(GOLDEN, "colruns_hand_example.json")))
     W = np.array(d["W_rows_fp16"], dtype=np.float16)
