@@ -340,12 +340,65 @@ def bench_calib(args, torch, swm, wl, G):
             "config": {"workload": f"copy of {nbytes} bytes, 5 per graph replay"}}
 
 
+# ------------------------------------------------------------------ wider workloads
+def bench_wide(args, torch, swm, wl, G):
+    """q_proj decode at 60% / 70% and with a 2:4 mask (N = 1, 16), and the
+    moderate-sparsity paper's Fig. 1 shape 65536x16384 at N = 32 (and 16),
+    each against the in-house dense kernel on W (.) mask."""
+    _log("workload: wider shapes and sparsities")
+    out = {"metric": "sparse speedup over the in-house dense kernel", "unit": "x", "n_gpus": 1,
+           "higher_is_better": True, "dtype": "f16", "data": "synthetic", "detail": {},
+           "config": {"workload": "q_proj 4096x4096 at 50% (N = 24, 32), 60% / 70% / 2:4 (N = 1, 16); 65536x16384 at 50% (N = 16, 32)"}}
+
+    def measure(name, W, mask, X, Ns, rotate=True):
+        M, K = W.shape
+        if rotate:
+            fmts, fb = rotating_formats(swm, W, mask)
+            Wds = rotating_dense(torch, W)
+        else:
+            f0 = swm.sparse_compress(W, mask)
+            fmts, fb = [f0], fmt_bytes(f0.info)
+            Wds = [torch.from_numpy(W).cuda()]
+        C, CD = len(fmts), len(Wds)
+        Xd = torch.from_numpy(X).cuda()
+        for n in Ns:
+            y = torch.empty((n, M), dtype=torch.float16, device="cuda")
+            for i in range(2):
+                swm.spmm(fmts[i % C], Xd[:n], y)
+                swm.dense_gemm(Wds[i % CD], Xd[:n], y)
+            torch.cuda.synchronize()
+            reps = max(C, 4)
+            t_sp = G.time(G.capture([lambda i=i: swm.spmm(fmts[i % C], Xd[:n], y) for i in range(reps)]), 3) / reps
+            t_de = G.time(G.capture([lambda i=i: swm.dense_gemm(Wds[i % CD], Xd[:n], y) for i in range(reps)]), 3) / reps
+            alg = fb + 2 * K * n + 2 * M * n
+            out["detail"][f"{name} N={n}"] = {
+                "sparse_us": t_sp * 1e3, "dense_us": t_de * 1e3, "speedup_vs_dense": t_de / t_sp,
+                "format_MB": fb / 1e6, "sparse_GBps_alg": alg / (t_sp * 1e-3) / 1e9,
+                "useful_TFLOPs": 2 * int(mask.sum()) * n / (t_sp * 1e-3) / 1e12}
+            _log(f"{name} N={n}: sparse {t_sp * 1e3:.2f} us, dense {t_de * 1e3:.2f} us")
+        del fmts, Wds
+        torch.cuda.empty_cache()
+
+    W, mask, X = wl.decode_qproj(32)
+    measure("q_proj s=0.5", W, mask, X, (24, 32))
+    for s in (0.6, 0.7):
+        W, mask, X = wl.decode_qproj_sparsity(s, 16)
+        measure(f"q_proj s={s}", W, mask, X, (1, 16))
+    W, mask, X = wl.decode_qproj_2_4(16)
+    measure("q_proj 2:4", W, mask, X, (1, 16))
+    W, mask, X = wl.fig1_shape()
+    measure("fig1 65536x16384 s=0.5", W, mask, X, (16, 32), rotate=False)
+    sp = [v["speedup_vs_dense"] for v in out["detail"].values()]
+    out["value"] = float(np.exp(np.mean(np.log(sp))))  # geometric mean over the lines
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="decode", choices=["decode", "spmspv", "prefill", "layer", "calib"])
+    ap.add_argument("--workload", default="decode", choices=["decode", "spmspv", "prefill", "layer", "wide", "calib"])
     ap.add_argument("--tau", type=float, default=0.3)
     ap.add_argument("--prefill-n", default="512,2048,4096")
     ap.add_argument("--prefill-s", default="0.5,0.6,0.7")
@@ -362,7 +415,7 @@ def main():
     torch.cuda.set_device(0)
     G = Graphs(torch)
     fn = {"decode": bench_decode, "spmspv": bench_spmspv, "prefill": bench_prefill, "layer": bench_layer,
-          "calib": bench_calib}
+          "wide": bench_wide, "calib": bench_calib}
     out = fn[args.workload](args, torch, swm, wl, G)
     out.setdefault("n_gpus", 1)
     print(json.dumps(out), flush=True)

@@ -150,8 +150,9 @@ swm_status swm_decompress(const swm_format* f, void* W_dev, int64_t ldw, void* s
  * Source: SPDP abstract (decode-phase spMspV kernel and prefill SpMM kernel over
  * one format); moderate-sparsity page Sec. 2.1 (prefill [BL,H], decode [B,H]).
  *  X: DEVICE fp16 token-major N x K (ldx >= K).  Y: DEVICE fp16 N x M (ldy >=
- *  M), overwritten.  N <= 16 runs the decode kernel, larger N the prefill
- *  kernel.  Asynchronous on stream. */
+ *  M), overwritten.  N <= 32 runs the decode kernels (the weights are read
+ *  once; N > 16 feeds each decoded operand to two 16-token MFMAs), larger N
+ *  the prefill kernel.  Asynchronous on stream. */
 swm_status swm_spmm(const swm_format* f, const void* X, int64_t ldx, void* Y, int64_t ldy,
                     int64_t N, void* stream);
 
@@ -227,9 +228,12 @@ swm_status swm_colruns_encode_blob(const void* tcb_blob, size_t size, void* out,
 
 /* dense_gemm: Y = W X with a DENSE fp16 W (row-major M x K, ldw >= K, device),
  * the same X / Y conventions, any N >= 1.  The in-house dense baseline and the
- * fallback to the full product.  Asynchronous on stream, except that for
- * N <= 16 (or an unaligned operand) the first call on a device, and any later
- * call that needs a larger workspace, allocates a library-owned workspace and
+ * fallback to the full product.  N <= 16 runs the streaming kernel; larger N
+ * the MFMA-tiled kernel, except N <= 32 when its 256x256 blocks would occupy
+ * under a quarter of the CUs (then two 16-token streaming passes).
+ * Asynchronous on stream, except that when the streaming kernel runs (or an
+ * operand is unaligned) the first call on a device, and any later call that
+ * needs a larger workspace, allocates a library-owned workspace and
  * synchronizes the device: make such a call once before capturing a graph.
  * Source: moderate-sparsity page, Sec. 1 (a sparse kernel is only useful if it
  * beats the dense product at the same shape). */

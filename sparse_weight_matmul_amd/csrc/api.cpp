@@ -377,7 +377,9 @@ static swm_status run_products(const swm_format* f, const void* X, int64_t ldx, 
   if (!on_current_device(f)) return SWM_ERR_INVALID_ARG;
   const uint16_t* x = static_cast<const uint16_t*>(X);
   uint16_t* y = static_cast<uint16_t*>(Y);
-  if (N <= 16) {
+  // N <= 32 is memory bound (the weights are read once per call): the decode
+  // kernels, with one or two 16-token groups per decoded operand.
+  if (N <= 16 || (N <= 32 && !skip)) {
     SWM_HIP(swm::launch_decode(f->d, f->plan, x, ldx, y, ldy, int(N), skip, s));
     return SWM_OK;
   }
@@ -386,9 +388,11 @@ static swm_status run_products(const swm_format* f, const void* X, int64_t ldx, 
     SWM_HIP(swm::launch_prefill_sparse(f->d, x, ldx, y, ldy, N, s));
     return SWM_OK;
   }
-  // Otherwise: sixteen-token slices through the decode kernel.
-  for (int64_t n0 = 0; n0 < N; n0 += 16) {
-    const int nn = int(std::min<int64_t>(16, N - n0));
+  // Otherwise: token slices through the decode kernel (32 at a time; 16 when
+  // skipping, whose decode kernel serves one group of 16).
+  const int64_t slice = skip ? 16 : 32;
+  for (int64_t n0 = 0; n0 < N; n0 += slice) {
+    const int nn = int(std::min<int64_t>(slice, N - n0));
     SWM_HIP(swm::launch_decode(f->d, f->plan, x + n0 * ldx, ldx, y + n0 * ldy, ldy, nn, skip, s));
   }
   return SWM_OK;
@@ -438,14 +442,20 @@ swm_status swm_dense_gemm(const void* W, int64_t ldw, const void* X, int64_t ldx
   if (M > (int64_t(1) << 31) - 64 || K > (int64_t(1) << 31) - 64) return SWM_ERR_UNSUPPORTED;
   if (M == 0) return SWM_OK;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (N > 16 && swm::prefill_supported(K, ldx, X) && ldw % 8 == 0 &&
+  int dev = 0;
+  SWM_HIP(hipGetDevice(&dev));
+  // The MFMA-tiled kernel for N > 16, unless N <= 32 and its 256x256 output
+  // blocks (at least one per 256 tokens) would occupy under a quarter of the
+  // CUs: then two 16-token passes of the streaming kernel are faster (each
+  // reads W once at full bandwidth).
+  const int64_t tiled_blocks = ((M + 255) / 256) * ((N + 255) / 256);
+  const bool small_tiled = N <= 32 && tiled_blocks * 4 < num_cus(dev);
+  if (N > 16 && !small_tiled && swm::prefill_supported(K, ldx, X) && ldw % 8 == 0 &&
       (reinterpret_cast<uintptr_t>(W) & 15) == 0) {
     SWM_HIP(swm::launch_prefill_dense(static_cast<const uint16_t*>(W), ldw, static_cast<const uint16_t*>(X),
                                       ldx, static_cast<uint16_t*>(Y), ldy, M, K, N, s));
     return SWM_OK;
   }
-  int dev = 0;
-  SWM_HIP(hipGetDevice(&dev));
   const auto p = swm::plan_dense_small(M, K, int(std::min<int64_t>(N, 16)), num_cus(dev));
   DenseWs* ws = nullptr;
   swm_status st = dense_workspace(dev, swm::dense_partial_floats(M, p), size_t((M + 63) / 64) + 1,

@@ -1,4 +1,4 @@
-// Decode-regime kernels (N <= 16 tokens): sparse SpMM / spMspV over the
+// Decode-regime kernels (N <= 32 tokens): sparse SpMM / spMspV over the
 // SWM-TCB v2 format, the dense small-N baseline, format expansion and an HBM
 // streaming calibration kernel.
 //
@@ -177,8 +177,10 @@ constexpr int kSegTiles = 4;  // tiles per streamed segment
 // ahead (into L2) and read by s_load_dwordx16 one step ahead; B operands
 // (activations, L2 resident) run two steps ahead.  kSkip: words whose four
 // columns carry a zero activation in every token are not decoded (their run
-// is still streamed).
-template <int kC, bool kSkip, bool kVec>
+// is still streamed).  kH = 2 serves 17 <= N <= 32 tokens: each decoded A
+// operand feeds two MFMAs, one per group of 16 tokens, so the weight stream is
+// read once for all of them.
+template <int kC, bool kSkip, bool kVec, int kH = 1>
 __global__ __launch_bounds__(1024) void decode_kernel(DecodeArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   const int lane = lane_id();
@@ -196,12 +198,17 @@ __global__ __launch_bounds__(1024) void decode_kernel(DecodeArgs a) {
   const int j0 = wave * a.tpw;
   const int j1 = min(j0 + a.tpw, a.kt);
 
-  // B operand: lane l carries token l%16, columns 8(l/16) .. +7 of the step.
+  // B operand: lane l carries token 16h + l%16 (token group h < kH), columns
+  // 8(l/16) .. +7 of the step.
   const int tok = lane & 15, kq = 8 * (lane >> 4);
-  const uint16_t* xrow = (tok < a.N) ? a.X + int64_t(tok) * a.ldx : a.zeros;
+  const uint16_t* xrow[kH];
+#pragma unroll
+  for (int h = 0; h < kH; ++h) xrow[h] = (16 * h + tok < a.N) ? a.X + int64_t(16 * h + tok) * a.ldx : a.zeros;
   const int64_t kmax8 = a.K >= 8 ? a.K - 8 : 0;  // clamp for steps past K (their A is zero)
 
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  f32x4 acc[kH];
+#pragma unroll
+  for (int h = 0; h < kH; ++h) acc[h] = f32x4{0.f, 0.f, 0.f, 0.f};
   uint32_t keep = 0;  // consumes the L2 prefetches so they are kept
 
   if (j0 < j1) {
@@ -238,13 +245,13 @@ __global__ __launch_bounds__(1024) void decode_kernel(DecodeArgs a) {
     auto load_words = [&](int j, int s) -> u32x16 {
       return const_load<u32x16>(a.bits + (tbase + j) * 16 + 8 * s);
     };
-    auto load_b = [&](int j, int s) -> half8 {
+    auto load_b = [&](int j, int s, int h) -> half8 {
       int64_t col = int64_t(j) * kTK + 32 * s + kq;
       if constexpr (kVec) {
         col = col < a.K ? col : kmax8;
-        return __builtin_bit_cast(half8, *reinterpret_cast<const u32x4*>(xrow + col));
+        return __builtin_bit_cast(half8, *reinterpret_cast<const u32x4*>(xrow[h] + col));
       } else {
-        return load8_checked(xrow, col, a.K);
+        return load8_checked(xrow[h], col, a.K);
       }
     };
 
@@ -253,9 +260,12 @@ __global__ __launch_bounds__(1024) void decode_kernel(DecodeArgs a) {
     touch_seg_words(1);
     load_seg(0, segA);
     load_seg(1, segB);
-    half8 bop[4];
-    bop[0] = load_b(j0, 0);
-    bop[1] = load_b(j0, 1);
+    half8 bop[kH][4];
+#pragma unroll
+    for (int h = 0; h < kH; ++h) {
+      bop[h][0] = load_b(j0, 0, h);
+      bop[h][1] = load_b(j0, 1, h);
+    }
     u32x16 wslot[2];
     wslot[0] = load_words(j0, 0);
 
@@ -282,7 +292,8 @@ __global__ __launch_bounds__(1024) void decode_kernel(DecodeArgs a) {
         for (int e = 0; e < 8; ++e) pc[e] = 2u * uint32_t(__builtin_popcountll(word_of(wv, e)));
         __builtin_amdgcn_sched_barrier(0);
         wslot[s ^ 1] = (s == 0) ? load_words(j, 1) : load_words(jn, 0);
-        bop[(2 * par + s + 2) & 3] = load_b(jn, s);
+#pragma unroll
+        for (int h = 0; h < kH; ++h) bop[h][(2 * par + s + 2) & 3] = load_b(jn, s, h);
         __builtin_amdgcn_sched_barrier(0);
         half8 aop;
 #pragma unroll
@@ -299,7 +310,9 @@ __global__ __launch_bounds__(1024) void decode_kernel(DecodeArgs a) {
           base += pc[e];
           aop[e] = lds_half(ad);
         }
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(aop, bop[(2 * par + s) & 3], acc, 0, 0, 0);
+#pragma unroll
+        for (int h = 0; h < kH; ++h)
+          acc[h] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aop, bop[h][(2 * par + s) & 3], acc[h], 0, 0, 0);
       }
     };
 
@@ -333,8 +346,13 @@ __global__ __launch_bounds__(1024) void decode_kernel(DecodeArgs a) {
   if (keep == 0x9E3779B9u && a.N < 0) a.Y[0] = 0;  // never true: keeps the prefetch loads
 
   __syncthreads();  // all segment buffers are free: reuse them as the reduction area
-  slab_reduce_store(reinterpret_cast<float*>(smem + 16), nwaves, wave, lane, acc, slab, a.M, a.N,
+  slab_reduce_store(reinterpret_cast<float*>(smem + 16), nwaves, wave, lane, acc[0], slab, a.M, min(a.N, 16),
                     a.Y, a.ldy);
+  if constexpr (kH == 2) {
+    __syncthreads();  // every thread is done reading the first group's partials
+    slab_reduce_store(reinterpret_cast<float*>(smem + 16), nwaves, wave, lane, acc[1], slab, a.M, a.N - 16,
+                      a.Y + 16 * a.ldy, a.ldy);
+  }
 }
 
 // ------------------------------------------------------------------ sparse, straight-line schedule
@@ -681,7 +699,8 @@ int seq_instance(int segs) {
 
 template <int kC>
 void launch_decode_c(bool skip, dim3 grid, dim3 block, size_t lds, hipStream_t s, const DecodeArgs& a) {
-  if (skip) hipLaunchKernelGGL((decode_kernel<kC, true, true>), grid, block, lds, s, a);
+  if (a.N > 16) hipLaunchKernelGGL((decode_kernel<kC, false, true, 2>), grid, block, lds, s, a);
+  else if (skip) hipLaunchKernelGGL((decode_kernel<kC, true, true>), grid, block, lds, s, a);
   else hipLaunchKernelGGL((decode_kernel<kC, false, true>), grid, block, lds, s, a);
 }
 
@@ -773,7 +792,7 @@ hipError_t launch_decode(const DevFormat& f, const DecodePlan& p, const uint16_t
   // words at 70% zero activations) and a column run is at most 32 bytes, so
   // neither the decode nor the fetch of inactive columns can be dropped
   // profitably; the product is computed in full (same result).
-  if (vec && p.seq_segs > 0 && a.K >= 8 && x32) {
+  if (vec && p.seq_segs > 0 && a.K >= 8 && x32 && n <= 16) {
     const int kxi = n <= 4 ? 1 : n <= 8 ? 2 : 4;
     const size_t per_wave = size_t(p.seq_chunks) * 1024 + size_t(4 * kxi) * kXRow;
     const size_t seq_lds = 16 + size_t(p.waves) * per_wave;
@@ -788,7 +807,17 @@ hipError_t launch_decode(const DevFormat& f, const DecodePlan& p, const uint16_t
     return hipGetLastError();
   }
   if (!vec) {
-    if (skip) hipLaunchKernelGGL((decode_kernel<8, true, false>), grid, block, lds, s, a);
+    if (n > 16) {
+      // unaligned activations: two passes of 16 and n - 16 tokens (a
+      // two-group instance of the unaligned kernel would spill registers)
+      DecodeArgs a2 = a;
+      a2.N = 16;
+      hipLaunchKernelGGL((decode_kernel<8, false, false>), grid, block, lds, s, a2);
+      a2.X = a.X + 16 * a.ldx;
+      a2.Y = a.Y + 16 * a.ldy;
+      a2.N = n - 16;
+      hipLaunchKernelGGL((decode_kernel<8, false, false>), grid, block, lds, s, a2);
+    } else if (skip) hipLaunchKernelGGL((decode_kernel<8, true, false>), grid, block, lds, s, a);
     else hipLaunchKernelGGL((decode_kernel<8, false, false>), grid, block, lds, s, a);
     return hipGetLastError();
   }

@@ -26,7 +26,7 @@ import numpy as np
 ROLE_W, ROLE_MASK, ROLE_X, ROLE_G, ROLE_U = 0, 1, 2, 3, 4
 
 # Workload ids (the first element of every seed).
-CFG_TINY, CFG_DECODE, CFG_SPMSPV, CFG_PREFILL, CFG_LAYER = 1, 2, 3, 4, 5
+CFG_TINY, CFG_DECODE, CFG_SPMSPV, CFG_PREFILL, CFG_LAYER, CFG_WIDE = 1, 2, 3, 4, 5, 6
 
 LLAMA7B_LINEARS = (
     ("q_proj", 4096, 4096),
@@ -78,6 +78,26 @@ def magnitude_prune_mask(W: np.ndarray, sparsity: float) -> np.ndarray:
     return mask
 
 
+def prune_2_4_mask(W: np.ndarray) -> np.ndarray:
+    """2:4 pruning along K: in every group of 4 consecutive columns of a row the
+    2 largest-|w| entries are kept (equal magnitudes: lower column first); a
+    trailing group shorter than 4 keeps its first half, rounded up."""
+    W = np.asarray(W, dtype=np.float16)
+    M, K = W.shape
+    mask = np.zeros((M, K), dtype=bool)
+    K4 = K - K % 4
+    if K4:
+        absbits = (W[:, :K4].view(np.uint16) & np.uint16(0x7FFF)).astype(np.int32).reshape(M, K4 // 4, 4)
+        key = (0x7FFF - absbits) * 4 + np.arange(4, dtype=np.int32)  # larger |w| first, then lower column
+        order = np.argsort(key, axis=2, kind="stable")[:, :, :2]
+        g = np.zeros((M, K4 // 4, 4), dtype=bool)
+        np.put_along_axis(g, order, True, axis=2)
+        mask[:, :K4] = g.reshape(M, K4)
+    if K % 4:
+        mask[:, K4:K4 + (K % 4 + 1) // 2] = True
+    return mask
+
+
 def apply_mask(W: np.ndarray, mask: np.ndarray) -> np.ndarray:
     """W with pruned entries replaced by +0 (bit pattern 0x0000)."""
     out = np.asarray(W, dtype=np.float16).copy()
@@ -123,6 +143,37 @@ def decode_qproj(n_max: int = 16):
     """q_proj 4096x4096 at 50% per-row magnitude pruning; X (n_max, 4096)."""
     W, mask = pruned_weight(CFG_DECODE, 0, 4096, 4096, 0.5)
     return W, mask, activations(CFG_DECODE, 0, n_max, 4096)
+
+
+def decode_qproj_sparsity(sparsity: float, n_max: int = 16):
+    """q_proj 4096x4096 magnitude-pruned to 0.6 or 0.7 (the pages' 60% / 70% points)."""
+    idx = {0.6: 1, 0.7: 2}[sparsity]
+    W, mask = pruned_weight(CFG_WIDE, idx, 4096, 4096, sparsity)
+    return W, mask, activations(CFG_WIDE, idx, n_max, 4096)
+
+
+def decode_qproj_2_4(n_max: int = 16):
+    """q_proj 4096x4096 with a 2:4 magnitude mask along K (the pages' 2:4 point)."""
+    W = normal_fp16(rng(CFG_WIDE, ROLE_W, 3), (4096, 4096), 0.02)
+    mask = prune_2_4_mask(W)
+    return apply_mask(W, mask), mask, activations(CFG_WIDE, 3, n_max, 4096)
+
+
+def fig1_shape(n: int = 32, M: int = 65536, K: int = 16384):
+    """The moderate-sparsity paper's Fig. 1 shape, M/K/N = 66K/16K/32 (66K read as
+    65536), at 50%: i.i.d. Bernoulli(0.5) mask (per-row magnitude pruning of 2^30
+    entries is left out to keep generation short), W ~ 0.02 N(0,1), X ~ N(0,1).
+    Generated in row chunks of float32 to bound host memory."""
+    gw, gm = rng(CFG_WIDE, ROLE_W, 4), rng(CFG_WIDE, ROLE_MASK, 4)
+    W = np.empty((M, K), dtype=np.float16)
+    mask = np.empty((M, K), dtype=bool)
+    step = 4096
+    for r in range(0, M, step):
+        h = min(step, M - r)
+        W[r:r + h] = (0.02 * gw.standard_normal((h, K), dtype=np.float32)).astype(np.float16)
+        mask[r:r + h] = gm.random((h, K), dtype=np.float32) < 0.5
+    W[~mask] = np.float16(0.0)
+    return W, mask, activations(CFG_WIDE, 4, n, K)
 
 
 def spmspv_down(n_max: int = 4, tau: float = 0.3):

@@ -121,6 +121,7 @@ def test_all_zero_mask_gives_zero(gpu_lib):
 # ------------------------------------------------------------------ ragged shapes and N sweep
 @pytest.mark.parametrize("M,K,N", [
     (1, 1, 1), (65, 129, 2), (300, 1000, 16), (64, 4096, 5), (130, 72, 17), (77, 333, 9), (513, 260, 33),
+    (77, 333, 20), (40, 1000, 32), (17, 4100, 31),   # N = 17..32: two token groups (unaligned K: two passes)
 ])
 def test_ragged_shapes(gpu_lib, M, K, N):
     swm = gpu_lib
@@ -137,6 +138,7 @@ def test_ragged_shapes(gpu_lib, M, K, N):
 @pytest.mark.parametrize("K,s,N", [
     (2048, 0.5, 1), (4096, 0.5, 16), (4104, 0.5, 3), (6144, 0.8, 7), (8192, 0.0, 16), (8192, 1.0, 2),
     (11008, 0.5, 4), (11008, 0.3, 16), (16384, 0.5, 1), (16384, 0.05, 9), (1024, 0.5, 16), (520, 0.5, 5),
+    (4096, 0.5, 32), (11008, 0.5, 24), (16384, 0.5, 17), (520, 0.5, 32), (8192, 1.0, 20),
 ])
 def test_decode_schedules(gpu_lib, K, s, N):
     swm = gpu_lib
@@ -150,15 +152,16 @@ def test_decode_schedules(gpu_lib, K, s, N):
         assert np.all(Y == 0)
 
 
-def test_strided_activations_and_outputs(gpu_lib):
+@pytest.mark.parametrize("N", [6, 28])
+def test_strided_activations_and_outputs(gpu_lib, N):
     import torch
     swm = gpu_lib
     W, mask = wl.pruned_weight(95, 0, 192, 256, 0.5)
-    X = np.random.default_rng(4).standard_normal((6, 256)).astype(np.float16)
+    X = np.random.default_rng(4).standard_normal((N, 256)).astype(np.float16)
     f = _compress(swm, W, mask)
-    Xbig = torch.zeros((6, 300), dtype=torch.float16, device="cuda")
+    Xbig = torch.zeros((N, 304), dtype=torch.float16, device="cuda")
     Xbig[:, :256] = _t(X)
-    Ybig = torch.full((6, 200), 7.0, dtype=torch.float16, device="cuda")
+    Ybig = torch.full((N, 200), 7.0, dtype=torch.float16, device="cuda")
     swm.spmm(f, Xbig[:, :256], Ybig[:, :192])
     Yb = _np(Ybig)
     assert_close(Yb[:, :192], oracle.masked_matmul(W, mask, X), "strided")
@@ -175,6 +178,14 @@ def qproj(gpu_lib):
 @pytest.mark.parametrize("N", [1, 8, 16])
 def test_qproj_decode(gpu_lib, qproj, N):
     W, mask, X, f = qproj
+    Y = _np(gpu_lib.spmm(f, _t(X[:N])))
+    assert_close(Y, oracle.masked_matmul(W, mask, X[:N]), f"q_proj N={N}")
+
+
+@pytest.mark.parametrize("N", [24, 32])
+def test_qproj_decode_two_token_groups(gpu_lib, N):
+    W, mask, X = wl.decode_qproj(32)
+    f = gpu_lib.sparse_compress(W, mask)
     Y = _np(gpu_lib.spmm(f, _t(X[:N])))
     assert_close(Y, oracle.masked_matmul(W, mask, X[:N]), f"q_proj N={N}")
 
@@ -361,7 +372,8 @@ def test_spmspv_skip_strided(gpu_lib):
 
 
 # ------------------------------------------------------------------ dense baseline, ragged
-@pytest.mark.parametrize("M,K,N", [(1, 1, 1), (65, 129, 3), (300, 1000, 16), (100, 64, 20)])
+@pytest.mark.parametrize("M,K,N", [(1, 1, 1), (65, 129, 3), (300, 1000, 16), (100, 64, 20), (1000, 512, 32),
+                                   (3000, 256, 30), (20000, 64, 32), (257, 4104, 17)])
 def test_dense_gemm_ragged(gpu_lib, M, K, N):
     g = np.random.default_rng(M * K)
     W = (0.02 * g.standard_normal((M, K))).astype(np.float16)
@@ -429,3 +441,34 @@ def test_prefill_upgate_sampled_rows(gpu_lib, s, N):
     if s == 0.5 and N == 512:
         Yd = _np(swm.dense_gemm(_t(W), _t(X)))
         assert np.array_equal(Yd.view(np.uint16), Y.view(np.uint16))
+
+
+# ------------------------------------------------------------------ wider workloads
+@pytest.mark.parametrize("s", [0.6, 0.7])
+@pytest.mark.parametrize("N", [1, 16])
+def test_qproj_decode_higher_sparsity(gpu_lib, s, N):
+    W, mask, X = wl.decode_qproj_sparsity(s, N)
+    f = gpu_lib.sparse_compress(W, mask)
+    assert_close(_np(gpu_lib.spmm(f, _t(X))), oracle.masked_matmul(W, mask, X), f"q_proj s={s} N={N}")
+
+
+@pytest.mark.parametrize("N", [1, 16])
+def test_qproj_decode_2_4_mask(gpu_lib, N):
+    W, mask, X = wl.decode_qproj_2_4(N)
+    f = gpu_lib.sparse_compress(W, mask)
+    assert_close(_np(gpu_lib.spmm(f, _t(X))), oracle.masked_matmul(W, mask, X), f"q_proj 2:4 N={N}")
+
+
+def test_fig1_shape_sampled_rows(gpu_lib):
+    # M/K/N = 65536/16384/32 at 50%: the full result on the GPU, 256 rows (and
+    # the first and last) against the oracle; the dense kernel on the same rows
+    swm = gpu_lib
+    W, mask, X = wl.fig1_shape()
+    f = swm.sparse_compress(W, mask)
+    Y = _np(swm.spmm(f, _t(X)))
+    rows = np.random.default_rng(66).choice(W.shape[0], 256, replace=False)
+    rows = np.concatenate([rows, [0, W.shape[0] - 1]])
+    assert_close(Y[:, rows], oracle.masked_matmul(W[rows], mask[rows], X), "fig1 spmm")
+    del f
+    Yd = _np(swm.dense_gemm(_t(W), _t(X)))
+    assert_close(Yd[:, rows], oracle.masked_matmul(W[rows], mask[rows], X), "fig1 dense")

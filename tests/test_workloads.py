@@ -70,3 +70,22 @@ def test_silu_threshold_zero_fraction_matches_distribution():
     assert 0.69 < p < 0.72  # roughly 70% of entries fall below 0.3
     assert abs(frac - p) < 0.01
     assert np.all(np.abs(x[x != 0].astype(np.float64)) >= tau)
+
+
+def test_prune_2_4_mask_rule():
+    # every full group of 4 along K keeps exactly its 2 largest |w| (lower column
+    # on ties); a short trailing group keeps its first half, rounded up
+    g = np.random.default_rng(5)
+    W = (g.standard_normal((50, 27)) * 0.02).astype(np.float16)
+    W[0, :4] = np.float16(0.5)                     # all tied: columns 0, 1
+    W[1, :4] = np.array([1, -3, 2, 2], dtype=np.float16)  # -3 then the first 2
+    m = wl.prune_2_4_mask(W)
+    assert m[0, :4].tolist() == [True, True, False, False]
+    assert m[1, :4].tolist() == [False, True, True, False]
+    groups = m[:, :24].reshape(50, 6, 4)
+    assert np.all(groups.sum(axis=2) == 2)
+    a = np.abs(W[:, :24].astype(np.float32)).reshape(50, 6, 4)
+    kept_min = np.where(groups, a, np.inf).min(axis=2)
+    drop_max = np.where(~groups, a, -np.inf).max(axis=2)
+    assert np.all(kept_min >= drop_max)
+    assert np.all(m[:, 24:26]) and not np.any(m[:, 26])
