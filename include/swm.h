@@ -38,8 +38,11 @@
  *    On a validation error no output is touched.  Kernel faults are reported
  *    as SWM_ERR_HIP by a later checked call (swm_last_hip_error() holds the
  *    hipError_t of the last failing runtime call).
- *  - Calls that use the same handle share its split-K workspace and must be
- *    ordered on one stream; handles are otherwise read-only after creation.
+ *  - Handles are read-only after creation, except that
+ *    swm_format_enable_skipping attaches the column-run encoding and its
+ *    partial-sum workspace; skipping calls on one handle share that workspace
+ *    and must be ordered on one stream.  Other product calls on one handle may
+ *    run concurrently.
  */
 #ifndef SWM_H_
 #define SWM_H_

@@ -55,51 +55,30 @@ int num_cus(int dev) {
   return cache[dev];
 }
 
-// Per-device workspace of the dense small-N kernel (split-K partials, arrival
-// counters and a zero row).  Calls on one device must be stream-ordered.
+// Per-device workspace of the dense small-N kernel: a zero row that loads past
+// K or past a wave's columns read instead of W.  It only grows; growing
+// synchronizes the device, because queued work may still read the old row.
 struct DenseWs {
-  float* partials = nullptr;
-  size_t partial_floats = 0;
-  uint32_t* counters = nullptr;
-  size_t n_counters = 0;
   uint16_t* zeros = nullptr;
   size_t n_zeros = 0;
 };
 
-swm_status dense_workspace(int dev, size_t pf, size_t nc, size_t nz, hipStream_t s, DenseWs** out) {
+swm_status dense_workspace(int dev, size_t nz, DenseWs** out) {
   static std::mutex mu;
   static std::vector<DenseWs> ws;
   std::lock_guard<std::mutex> g(mu);
   if (dev >= int(ws.size())) ws.resize(dev + 1);
   DenseWs& w = ws[dev];
-  if (pf > w.partial_floats || nc > w.n_counters || nz > w.n_zeros) {
-    SWM_HIP(hipDeviceSynchronize());  // old buffers may still be in use by queued work
-    if (pf > w.partial_floats) {
-      if (w.partials) (void)hipFree(w.partials);
-      w.partials = nullptr;
-      w.partial_floats = 0;
-      if (hipMalloc(&w.partials, pf * sizeof(float)) != hipSuccess) return SWM_ERR_OOM;
-      w.partial_floats = pf;
-    }
-    if (nc > w.n_counters) {
-      if (w.counters) (void)hipFree(w.counters);
-      w.counters = nullptr;
-      w.n_counters = 0;
-      if (hipMalloc(&w.counters, nc * sizeof(uint32_t)) != hipSuccess) return SWM_ERR_OOM;
-      SWM_HIP(hipMemset(w.counters, 0, nc * sizeof(uint32_t)));
-      w.n_counters = nc;
-    }
-    if (nz > w.n_zeros) {
-      if (w.zeros) (void)hipFree(w.zeros);
-      w.zeros = nullptr;
-      w.n_zeros = 0;
-      if (hipMalloc(&w.zeros, nz * sizeof(uint16_t)) != hipSuccess) return SWM_ERR_OOM;
-      SWM_HIP(hipMemset(w.zeros, 0, nz * sizeof(uint16_t)));
-      w.n_zeros = nz;
-    }
+  if (nz > w.n_zeros) {
     SWM_HIP(hipDeviceSynchronize());
+    if (w.zeros) (void)hipFree(w.zeros);
+    w.zeros = nullptr;
+    w.n_zeros = 0;
+    if (hipMalloc(&w.zeros, nz * sizeof(uint16_t)) != hipSuccess) return SWM_ERR_OOM;
+    SWM_HIP(hipMemset(w.zeros, 0, nz * sizeof(uint16_t)));
+    SWM_HIP(hipDeviceSynchronize());
+    w.n_zeros = nz;
   }
-  (void)s;
   *out = &w;
   return SWM_OK;
 }
@@ -118,7 +97,6 @@ swm_status upload(std::vector<uint8_t>&& blob, const swm::Header& h, hipStream_t
   const size_t T = h.tiles();
   const size_t b_tp = 4 * (T + 1), b_bits = 8 * h.n_bits(), b_vals = 2 * h.padded_len + 1024;
   const size_t n_zero = size_t(h.kt) * h.tk + 64;
-  const size_t pf = swm::decode_partial_floats(h, f->plan);
   size_t off = 0;
   const size_t o_tp = off;
   off = align_up(off + b_tp, 256);
@@ -128,10 +106,6 @@ swm_status upload(std::vector<uint8_t>&& blob, const swm::Header& h, hipStream_t
   off = align_up(off + b_vals, 256);
   const size_t o_zero = off;
   off = align_up(off + 2 * n_zero, 256);
-  const size_t o_part = off;
-  off = align_up(off + 4 * pf, 256);
-  const size_t o_cnt = off;
-  off = align_up(off + 4 * size_t(h.mt) + 4, 256);
   if (hipMalloc(&f->dev_mem, off) != hipSuccess) {
     delete f;
     return SWM_ERR_OOM;
@@ -154,9 +128,6 @@ swm_status upload(std::vector<uint8_t>&& blob, const swm::Header& h, hipStream_t
   f->d.bits = reinterpret_cast<const uint64_t*>(base + o_bits);
   f->d.vals = reinterpret_cast<const uint16_t*>(base + o_vals);
   f->d.zeros = reinterpret_cast<const uint16_t*>(base + o_zero);
-  f->d.partials = reinterpret_cast<float*>(base + o_part);
-  f->d.counters = reinterpret_cast<uint32_t*>(base + o_cnt);
-  f->d.partial_floats = pf;
   *out = f;
   return SWM_OK;
 }
@@ -458,16 +429,14 @@ swm_status swm_dense_gemm(const void* W, int64_t ldw, const void* X, int64_t ldx
   }
   const auto p = swm::plan_dense_small(M, K, int(std::min<int64_t>(N, 16)), num_cus(dev));
   DenseWs* ws = nullptr;
-  swm_status st = dense_workspace(dev, swm::dense_partial_floats(M, p), size_t((M + 63) / 64) + 1,
-                                  size_t(K) + 64, s, &ws);
+  swm_status st = dense_workspace(dev, size_t(K) + 64, &ws);
   if (st != SWM_OK) return st;
   const uint16_t* w = static_cast<const uint16_t*>(W);
   const uint16_t* x = static_cast<const uint16_t*>(X);
   uint16_t* y = static_cast<uint16_t*>(Y);
   for (int64_t n0 = 0; n0 < N; n0 += 16) {
     const int nn = int(std::min<int64_t>(16, N - n0));
-    SWM_HIP(swm::launch_dense_small(p, w, ldw, x + n0 * ldx, ldx, y + n0 * ldy, ldy, M, K, nn,
-                                    ws->partials, ws->counters, ws->zeros, s));
+    SWM_HIP(swm::launch_dense_small(p, w, ldw, x + n0 * ldx, ldx, y + n0 * ldy, ldy, M, K, nn, ws->zeros, s));
   }
   return SWM_OK;
 }

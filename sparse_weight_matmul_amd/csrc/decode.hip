@@ -754,11 +754,8 @@ DecodePlan plan_decode(const Header& h, const uint32_t* tp, int num_cus) {
   if (p.seq_chunks < 1) p.seq_chunks = 1;
   if (p.seq_chunks > 4) p.seq_segs = 0;  // cannot happen: two tiles hold at most 4 KiB
   if (getenv("SWM_DECODE_LOOP")) p.seq_segs = 0;
-  p.splits = 1;
   return p;
 }
-
-size_t decode_partial_floats(const Header&, const DecodePlan&) { return 0; }
 
 hipError_t launch_decode(const DevFormat& f, const DecodePlan& p, const uint16_t* X, int64_t ldx,
                          uint16_t* Y, int64_t ldy, int n, bool skip, hipStream_t s) {
@@ -850,15 +847,12 @@ DensePlan plan_dense_small(int64_t M, int64_t K, int n, int num_cus) {
   p.kchunk = int(kc);
   p.waves = int((K + kc - 1) / kc);
   if (p.waves < 1) p.waves = 1;
-  p.splits = 1;
   return p;
 }
 
-size_t dense_partial_floats(int64_t, const DensePlan&) { return 0; }
-
 hipError_t launch_dense_small(const DensePlan& p, const uint16_t* W, int64_t ldw, const uint16_t* X,
                               int64_t ldx, uint16_t* Y, int64_t ldy, int64_t M, int64_t K, int n,
-                              float*, uint32_t*, const uint16_t* zeros, hipStream_t s) {
+                              const uint16_t* zeros, hipStream_t s) {
   DenseArgs a;
   a.W = W;
   a.X = X;

@@ -16,9 +16,6 @@ struct DevFormat {
   const uint64_t* bits = nullptr;      // mt*kt*tk words
   const uint16_t* vals = nullptr;      // padded_len values (+ slack for over-reads)
   const uint16_t* zeros = nullptr;     // >= kt*tk + 64 zero halves (device)
-  float* partials = nullptr;           // split-K partial sums
-  uint32_t* counters = nullptr;        // one arrival counter per row block, kept at 0 between calls
-  size_t partial_floats = 0;
 };
 
 // Work split of the decode kernel for one call.
@@ -29,13 +26,11 @@ struct DecodePlan {
   int seg_chunks = 1;      // 1 KiB loads per segment (covers the largest segment)
   int seq_segs = 0;        // straight-line kernel: two-tile segments per wave (0 = not used)
   int seq_chunks = 1;      // 1 KiB loads per two-tile segment
-  int splits = 1;
 };
 
 // Work split of the decode kernel; `tile_ptr` (host, mt*kt+1 entries) sizes
 // the segment loads.
 DecodePlan plan_decode(const Header& h, const uint32_t* tile_ptr, int num_cus);
-size_t decode_partial_floats(const Header& h, const DecodePlan& p);
 
 hipError_t launch_decode(const DevFormat& f, const DecodePlan& p, const uint16_t* X, int64_t ldx,
                          uint16_t* Y, int64_t ldy, int n, bool skip, hipStream_t s);
@@ -71,14 +66,11 @@ hipError_t launch_stream(const void* src, size_t bytes, int unroll, int blocks, 
 struct DensePlan {
   int waves = 4;
   int kchunk = 512;  // columns per wave
-  int splits = 1;
 };
 DensePlan plan_dense_small(int64_t M, int64_t K, int n, int num_cus);
-size_t dense_partial_floats(int64_t M, const DensePlan& p);
 hipError_t launch_dense_small(const DensePlan& p, const uint16_t* W, int64_t ldw, const uint16_t* X,
                               int64_t ldx, uint16_t* Y, int64_t ldy, int64_t M, int64_t K, int n,
-                              float* partials, uint32_t* counters, const uint16_t* zeros,
-                              hipStream_t s);
+                              const uint16_t* zeros, hipStream_t s);
 
 // Tiled MFMA GEMM for larger N: dense W, or W expanded from the format tile by tile.
 hipError_t launch_prefill_dense(const uint16_t* W, int64_t ldw, const uint16_t* X, int64_t ldx,
