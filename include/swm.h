@@ -203,16 +203,17 @@ swm_status swm_spmspv(const swm_format* f, const void* x, int64_t ldx, void* y, 
 swm_status swm_spmspv_threshold(const swm_format* f, const void* x, int64_t ldx, void* y, int64_t ldy,
                                 int32_t n, float tau, void* stream);
 
-/* format_enable_skipping: attach to f the column-run encoding (SWM-CR v1)
+/* format_enable_skipping: attach to f the column-run encoding (SWM-CR v2)
  * that lets swm_spmspv skip zero activations, and upload it to f's device.
  * Source: SPDP abstract (run-time skipping of zero activations in the decode
  * spMspV kernel); "Reduced Matrix Multiplication" blog page, Sec. 4.2 (the
  * product over the kept input channels equals the full product).
  *  The encoding holds the same kept entries as f, regrouped column by column
- *  inside blocks of 256 rows: entry e = b*K + k (column k of row block b) has
- *  4 bitmap words (bit i of word q <=> row 256b + 64q + i), a run of its kept
- *  fp16 values in row order padded to 4 values, and a uint32 exclusive prefix
- *  of run lengths.  The handle owns the device copy (freed by
+ *  inside blocks of 256 rows, the blocks of a column stored four at a time:
+ *  block b = 4g + j, entry e = (g*K + k)*4 + j (column k of block b; blocks
+ *  past the last one are empty entries) has 4 bitmap words (bit i of word q
+ *  <=> row 256b + 64q + i), a run of its kept fp16 values in row order padded
+ *  to 4 values, and a uint32 exclusive prefix of run lengths.  The handle owns the device copy (freed by
  *  swm_format_destroy) and a workspace for the per-workgroup partial sums.
  *  Synchronous.  Idempotent.  Call it before f is used by other threads or
  *  streams (like creation).  *bytes (nullable) receives the encoding's size.
@@ -220,8 +221,8 @@ swm_status swm_spmspv_threshold(const swm_format* f, const void* x, int64_t ldx,
  *  SWM_ERR_OVERFLOW, SWM_ERR_UNSUPPORTED (M or K too large), SWM_ERR_HIP. */
 swm_status swm_format_enable_skipping(swm_format* f, void* stream, uint64_t* bytes);
 
-/* colruns_encode_blob: host-only derivation of the SWM-CR v1 blob (32-byte
- * header b"SWMC", u32 version 1, i64 M, i64 K, u32 rows per block = 256,
+/* colruns_encode_blob: host-only derivation of the SWM-CR v2 blob (32-byte
+ * header b"SWMC", u32 version 2, i64 M, i64 K, u32 rows per block = 256,
  * u32 row blocks; then ptr, bits, values as described above) from a SWM-TCB v2
  * export blob, for byte-exact checks of the encoding.  Same sizing protocol as
  * swm_format_export: *size receives the blob size; out may be NULL to query;

@@ -14,7 +14,7 @@ Contents
                column-bitmap format (SWM-TCB v1), written from its spec.
 ``exact``      exact integer brute force used to pin the fp64 reference.
 ``colruns``    an independent numpy encoder / decoder of the column-run
-               encoding (SWM-CR v1) used by activation skipping.
+               encoding (SWM-CR v2) used by activation skipping.
 
 Parity status: every function here is pinned by the CPU tests in
 ``tests/test_oracle_pins.py`` against closed forms, brute force, hand-worked

@@ -223,7 +223,7 @@ def encode_blob(W, mask=None, tile=(16, 64)) -> bytes:
 
 
 def colruns_encode_blob(tcb_blob: bytes) -> bytes:
-    """Host-only: the SWM-CR v1 column-run blob derived from a SWM-TCB v2 blob."""
+    """Host-only: the SWM-CR v2 column-run blob derived from a SWM-TCB v2 blob."""
     lib = load()
     b = ctypes.create_string_buffer(bytes(tcb_blob), max(len(tcb_blob), 1))
     size = ctypes.c_size_t(0)

@@ -290,7 +290,7 @@ swm_status swm_format_enable_skipping(swm_format* f, void* stream, uint64_t* byt
   swm_status st = swm::colruns_from_tcb(f->blob.data(), f->blob.size(), &c);
   if (st != SWM_OK) return st;
   const swm::ColRunsPlan plan = swm::plan_colruns(c.m, c.k);
-  const uint64_t E = uint64_t(c.mb) * uint64_t(c.k);
+  const uint64_t E = c.entries();
   const size_t b_ptr = 4 * (E + 1), b_bits = 32 * E, b_vals = 2 * c.values.size() + 16;
   const size_t b_part = 4 * size_t(plan.mb) * size_t(plan.splits) * 4 * 256;
   size_t off = 0;

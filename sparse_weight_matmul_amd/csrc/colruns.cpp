@@ -1,4 +1,4 @@
-// Host side of the SWM-CR v1 column-run encoding used by activation skipping.
+// Host side of the SWM-CR v2 column-run encoding used by activation skipping.
 //
 // The decode kernel of "Unified Static-Dynamic Pruning for Efficient LLM
 // Inference" (SPDP, abstract) skips at run time the input channels whose
@@ -9,14 +9,18 @@
 // and skipping it saves nothing.  This encoding regroups the same kept
 // entries column by column inside blocks of R = 256 rows, so a column's run is
 // about 256 bytes at 50% sparsity and skipping it skips whole cache lines.
+// Blocks are stored in groups of four per column: the four bitmap entries of
+// a column (4 x 32 bytes) fill one 128-byte line and its four runs are
+// adjacent, so an active column's data shares lines only with itself.
 //
-// Layout (entry e = b*K + k is column k inside row block b, rows
-// [256b, 256b + 256)):
+// Layout (block b = 4g + j, j = 0..3, rows [256b, 256b + 256); entry
+// e = (g*K + k)*4 + j is column k of block b; blocks past Mb in the last
+// group are empty entries):
 //   bits[e][q], q = 0..3: bit i <=> row 256b + 64q + i kept;
 //   values: kept fp16 bits of entry e in increasing row order, each run
 //   zero-padded to a multiple of 4 values (8 bytes);
 //   ptr[e] = exclusive prefix of padded run lengths (uint32).
-// Blob: 32-byte header (b"SWMC", u32 version 1, i64 M, i64 K, u32 R, u32 Mb)
+// Blob: 32-byte header (b"SWMC", u32 version 2, i64 M, i64 K, u32 R, u32 Mb)
 // || ptr || bits || values.  The encoding is derived from a validated SWM-TCB
 // v2 blob, so both hold exactly the same kept entries and bits.
 #include <cstring>
@@ -36,12 +40,15 @@ swm_status colruns_from_tcb(const void* tcb, size_t size, ColRunsHost* out) {
   const uint8_t* vals_b = blob + h.off_values();
   const int64_t M = h.m, K = h.k;
   const int64_t Mb = (M + kColRunRows - 1) / kColRunRows;
-  const uint64_t E = uint64_t(Mb) * uint64_t(K);
   const uint64_t wpt = h.words_per_tile();
   ColRunsHost c;
   c.m = M;
   c.k = K;
   c.mb = Mb;
+  const uint64_t E = c.entries();
+  auto entry_of = [&](int64_t b, int64_t col) -> uint64_t {
+    return (uint64_t(b / kColRunGroup) * uint64_t(K) + uint64_t(col)) * kColRunGroup + uint64_t(b % kColRunGroup);
+  };
   try {
     c.ptr.assign(E + 1, 0);
     c.bits.assign(4 * E, 0);
@@ -60,7 +67,7 @@ swm_status colruns_from_tcb(const void* tcb, size_t size, ColRunsHost* out) {
             const int64_t row = int64_t(i) * 16 + bit % 16;
             const int64_t col = int64_t(j) * h.tk + 32 * s + 8 * (bit / 16) + e;
             const int64_t b = row / kColRunRows, r = row % kColRunRows;
-            const uint64_t en = uint64_t(b) * K + col;
+            const uint64_t en = entry_of(b, col);
             ++count[en];
             c.bits[4 * en + r / 64] |= uint64_t(1) << (r % 64);
           }
@@ -91,7 +98,7 @@ swm_status colruns_from_tcb(const void* tcb, size_t size, ColRunsHost* out) {
             word &= word - 1;
             const int64_t row = int64_t(i) * 16 + bit % 16;
             const int64_t col = int64_t(j) * h.tk + 32 * s + 8 * (bit / 16) + e;
-            const uint64_t en = uint64_t(row / kColRunRows) * K + col;
+            const uint64_t en = entry_of(row / kColRunRows, col);
             uint16_t v;
             std::memcpy(&v, vals_b + 2 * pos, 2);
             ++pos;
@@ -107,15 +114,15 @@ swm_status colruns_from_tcb(const void* tcb, size_t size, ColRunsHost* out) {
 }
 
 size_t colruns_blob_bytes(const ColRunsHost& c) {
-  const uint64_t E = uint64_t(c.mb) * uint64_t(c.k);
+  const uint64_t E = c.entries();
   return kColRunHeaderBytes + 4 * (E + 1) + 32 * E + 2 * c.values.size();
 }
 
 void colruns_write_blob(const ColRunsHost& c, uint8_t* dst) {
-  const uint64_t E = uint64_t(c.mb) * uint64_t(c.k);
+  const uint64_t E = c.entries();
   std::memset(dst, 0, kColRunHeaderBytes);
   std::memcpy(dst, "SWMC", 4);
-  const uint32_t ver = 1, r = kColRunRows, mb = uint32_t(c.mb);
+  const uint32_t ver = 2, r = kColRunRows, mb = uint32_t(c.mb);
   std::memcpy(dst + 4, &ver, 4);
   std::memcpy(dst + 8, &c.m, 8);
   std::memcpy(dst + 16, &c.k, 8);

@@ -35,7 +35,7 @@ DecodePlan plan_decode(const Header& h, const uint32_t* tile_ptr, int num_cus);
 hipError_t launch_decode(const DevFormat& f, const DecodePlan& p, const uint16_t* X, int64_t ldx,
                          uint16_t* Y, int64_t ldy, int n, bool skip, hipStream_t s);
 
-// Activation-skipping decode over the SWM-CR v1 column-run encoding.
+// Activation-skipping decode over the SWM-CR v2 column-run encoding.
 constexpr int kCrMaxCols = 1024;  // input columns per workgroup (one per thread)
 struct ColRunsPlan {
   int mb = 0;      // 256-row blocks
@@ -44,8 +44,8 @@ struct ColRunsPlan {
 };
 struct DevColRuns {
   int64_t m = 0, k = 0;
-  const uint32_t* ptr = nullptr;   // mb*k + 1
-  const uint64_t* bits = nullptr;  // mb*k*4
+  const uint32_t* ptr = nullptr;   // entries + 1 (entries = ceil(mb/4)*4*k)
+  const uint64_t* bits = nullptr;  // entries * 4
   const uint16_t* vals = nullptr;  // padded runs + 16 bytes of slack
   float* partials = nullptr;       // mb*splits*4*256 per-workgroup partial sums
   ColRunsPlan plan;

@@ -1,4 +1,4 @@
-// Activation-skipping decode (spMspV) over the SWM-CR v1 column-run encoding.
+// Activation-skipping decode (spMspV) over the SWM-CR v2 column-run encoding.
 //
 // Method: "Unified Static-Dynamic Pruning for Efficient LLM Inference" (SPDP),
 // abstract -- at decode time the input-adaptive (dynamic) sparsity of the
@@ -10,7 +10,10 @@
 //
 // gfx950 design.  A workgroup (16 waves, one per CU) owns a 256-row block b
 // and a range of cps <= 1024 input columns (split s); the grid is S x Mb
-// workgroups, about one per CU.
+// workgroups, about one per CU.  The encoding stores the blocks of a column
+// four at a time (one 128-byte line of bitmap words, adjacent runs), and the
+// four workgroups of one (split, group of four blocks) are placed on the same
+// XCD, so the lines they share are fetched into that XCD's L2 once.
 //  1. Active columns: each thread tests one column (any of the n <= 4 tokens
 //     nonzero); a wave ballot and v_mbcnt give each active column its slot in
 //     a list ordered by (wave, lane), so the list is a deterministic function
@@ -66,8 +69,8 @@ struct CrBatchRegs {
 };
 
 struct CrArgs {
-  const uint32_t* ptr;   // mb*K + 1
-  const uint64_t* bits;  // mb*K*4
+  const uint32_t* ptr;   // entries + 1
+  const uint64_t* bits;  // entries * 4
   const uint16_t* vals;  // padded runs (+ 8 bytes of slack)
   const uint16_t* x;     // token-major n x K
   uint16_t* y;           // token-major n x M
@@ -142,10 +145,19 @@ __global__ __launch_bounds__(1024) void spmspv_cr_kernel(CrArgs a) {
   const int tid = int(threadIdx.x);
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int s = int(blockIdx.x) / a.mb, b = int(blockIdx.x) % a.mb;
+  // Workgroup -> (split s, block b = 4g + j).  Workgroups are handed to the
+  // eight XCDs in turn, so ids x, x + 8, x + 16, x + 24 of each run of 32
+  // share an XCD: they take the four blocks of one (split, group) item.  The
+  // placement only affects speed; any mapping gives the same result.
+  const int id = int(blockIdx.x);
+  const int item = (id >> 5) * 8 + (id & 7), j = (id >> 3) & 3;
+  const int gn = (a.mb + 3) >> 2;
+  const int g = item % gn, s = item / gn, b = 4 * g + j;
+  if (s >= a.S || b >= a.mb) return;  // uniform, before any barrier
   const int k0 = s * a.cps;
   const int kend = min(k0 + a.cps, a.K);
-  const uint64_t ebase = uint64_t(b) * uint64_t(a.K) + uint64_t(k0);
+  // entry of column k0 + t in block b: ebase + 4 t
+  const uint64_t ebase = (uint64_t(g) * uint64_t(a.K) + uint64_t(k0)) * 4 + uint64_t(j);
 
   // ---- 1. active columns of [k0, kend), in (wave, lane) order, with their
   // activations and run bounds (the pointers are read for every column of
@@ -166,8 +178,8 @@ __global__ __launch_bounds__(1024) void spmspv_cr_kernel(CrArgs a) {
         v[t] = keep ? xv : 0.f;
         on |= keep;
       }
-      p[0] = a.ptr[ebase + uint64_t(tid)];
-      p[1] = a.ptr[ebase + uint64_t(tid) + 1];
+      p[0] = a.ptr[ebase + 4 * uint64_t(tid)];
+      p[1] = a.ptr[ebase + 4 * uint64_t(tid) + 1];
     }
     const uint64_t bal = __builtin_amdgcn_ballot_w64(on);
     if (lane == 0) s_cnt[wave] = uint32_t(__builtin_popcountll(bal));
@@ -209,7 +221,7 @@ __global__ __launch_bounds__(1024) void spmspv_cr_kernel(CrArgs a) {
     const int e0 = g * kCrBatch;
     const u32x2 pb = s_p[wave + kCrWaves * min(e0 + (lane & 15), nw - 1)];
     const uint32_t cb = s_col[wave + kCrWaves * min(e0 + (lane >> 2), nw - 1)];
-    const uint64_t bv = a.bits[(ebase + cb) * 4 + uint64_t(lane & 3)];
+    const uint64_t bv = a.bits[(ebase + 4 * uint64_t(cb)) * 4 + uint64_t(lane & 3)];
     B.bits_lo = uint32_t(bv);
     B.bits_hi = uint32_t(bv >> 32);
 #pragma unroll
@@ -349,7 +361,8 @@ hipError_t launch_spmspv_cr(const DevColRuns& c, const uint16_t* x, int64_t ldx,
   a.S = c.plan.splits;
   a.cps = c.plan.cps;
   if (a.mb == 0 || a.S == 0) return hipSuccess;
-  const dim3 grid(unsigned(a.mb) * unsigned(a.S)), block(64 * kCrWaves);
+  const unsigned items = unsigned((a.mb + 3) / 4) * unsigned(a.S);  // (split, group) pairs
+  const dim3 grid(32u * ((items + 7u) / 8u)), block(64 * kCrWaves);
   switch (n) {
     case 1: hipLaunchKernelGGL(spmspv_cr_kernel<1>, grid, block, 0, s, a); break;
     case 2: hipLaunchKernelGGL(spmspv_cr_kernel<2>, grid, block, 0, s, a); break;

@@ -46,15 +46,18 @@ swm_status validate_blob(const void* buf, size_t size, Header* h);
 
 void fill_info(const Header& h, swm_format_info* info);
 
-// SWM-CR v1 column-run encoding (activation skipping): kept entries grouped
-// by input column inside blocks of kColRunRows rows.
+// SWM-CR v2 column-run encoding (activation skipping): kept entries grouped
+// by input column inside blocks of kColRunRows rows, the blocks of a column
+// stored kColRunGroup at a time.
 constexpr int kColRunRows = 256;
+constexpr int kColRunGroup = 4;  // row blocks stored together per column
 constexpr size_t kColRunHeaderBytes = 32;
 struct ColRunsHost {
-  int64_t m = 0, k = 0, mb = 0;
-  std::vector<uint32_t> ptr;     // mb*k + 1
-  std::vector<uint64_t> bits;    // mb*k*4
+  int64_t m = 0, k = 0, mb = 0;  // mb row blocks, in ceil(mb / 4) groups
+  std::vector<uint32_t> ptr;     // entries + 1
+  std::vector<uint64_t> bits;    // entries * 4
   std::vector<uint16_t> values;  // padded runs
+  uint64_t entries() const { return uint64_t((mb + kColRunGroup - 1) / kColRunGroup) * uint64_t(k) * kColRunGroup; }
 };
 // Derive the encoding from a SWM-TCB v2 blob (validated first).
 swm_status colruns_from_tcb(const void* tcb, size_t size, ColRunsHost* out);

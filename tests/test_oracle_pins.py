@@ -234,8 +234,25 @@ def test_colruns_hand_worked_bytes():
     assert [format(int(v), "04x") for v in Wb[Wb != 0]] != [v for v in d["values_hex"] if v != "0000"]
 
 
+def test_colruns_group_order_hand_worked():
+    # 1024 x 2 (four 256-row blocks, one group); kept: (row 700, column 0) and
+    # (row 5, column 1).  Row 700 is block 2, word 2 ((700 - 512) // 64), bit
+    # 60; its entry is (0*2 + 0)*4 + 2 = 2.  Row 5 is block 0, word 0, bit 5;
+    # its entry is (0*2 + 1)*4 + 0 = 4.  Each run is one value padded to 4.
+    W = np.zeros((1024, 2), dtype=np.float16)
+    W[700, 0] = np.float16(1.5)
+    W[5, 1] = np.float16(-2.0)
+    c = oracle.colruns_encode(W, None)
+    expect_bits = [0] * 32
+    expect_bits[2 * 4 + 2] = 1 << 60
+    expect_bits[4 * 4 + 0] = 1 << 5
+    assert [int(v) for v in c.bits] == expect_bits
+    assert list(c.ptr) == [0, 0, 0, 4, 4, 8, 8, 8, 8]
+    assert [format(int(v), "04x") for v in c.values] == ["3e00", "0000", "0000", "0000", "c000", "0000", "0000", "0000"]
+
+
 @pytest.mark.parametrize("M,K,density", [(1, 1, 1.0), (256, 64, 0.5), (257, 70, 0.3), (600, 40, 0.0),
-                                         (513, 130, 1.0), (64, 300, 0.05)])
+                                         (513, 130, 1.0), (64, 300, 0.05), (1100, 40, 0.5)])
 def test_colruns_round_trip_and_invariants(M, K, density):
     W, mask, _ = _rand_case(M * 977 + K, M, K, 1, density, signed_zero=True)
     c = oracle.colruns_encode(W, mask)
