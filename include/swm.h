@@ -176,9 +176,10 @@ swm_status swm_spmm(const swm_format* f, const void* X, int64_t ldx, void* Y, in
  * reproducible and equal the full product up to fp32 summation order.  That
  * path uses the handle's workspace: calls on one handle must be ordered on
  * one stream.  It pays when most columns are inactive: measured on one
- * MI355X for a 4096 x 11008 weight at 50%, it matches the full product at
- * about 70-74% inactive columns and is 1.3x faster at 86%, 1.5x at 92%; with
- * fewer inactive columns it is slower, so enable it only for such inputs. 
+ * MI355X for a 4096 x 11008 weight at 50% and one token, it is 1.1x faster
+ * than the full product at 70% inactive columns, 1.4x at 86% and 1.5x at
+ * 92%; with four tokens it breaks even at about 74%.  With fewer inactive
+ * columns it is slower, so enable it only for such inputs. 
  * Source: SPDP abstract (input-adaptive dynamic pruning; run-time activation
  * skipping in the spMspV kernel); "Reduced Matrix Multiplication" blog page,
  * Sec. 4.2 (an FFN down projection multiplies only the kept channels). */
