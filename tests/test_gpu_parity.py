@@ -472,3 +472,20 @@ def test_fig1_shape_sampled_rows(gpu_lib):
     del f
     Yd = _np(swm.dense_gemm(_t(W), _t(X)))
     assert_close(Yd[:, rows], oracle.masked_matmul(W[rows], mask[rows], X), "fig1 dense")
+
+
+# ------------------------------------------------------------------ layer shapes in the bench's launch configuration
+@pytest.mark.parametrize("i", [0, 4, 6])   # q_proj 4096x4096, gate_proj 11008x4096, down_proj 4096x11008
+@pytest.mark.parametrize("N", [16, 4096])
+def test_layer_linears_as_benchmarked(gpu_lib, i, N):
+    # the layer workload's own seeded inputs; full outputs at N = 16, 256
+    # sampled rows (and the first and last) at N = 4096
+    W, mask, X = wl.layer_linear(i, N)
+    f = gpu_lib.sparse_compress(W, mask)
+    Y = _np(gpu_lib.spmm(f, _t(X)))
+    if N == 16:
+        assert_close(Y, oracle.masked_matmul(W, mask, X), f"linear {i} N={N}")
+    else:
+        rows = np.random.default_rng(i).choice(W.shape[0], 256, replace=False)
+        rows = np.concatenate([rows, [0, W.shape[0] - 1]])
+        assert_close(Y[:, rows], oracle.masked_matmul(W[rows], mask[rows], X), f"linear {i} N={N}")
