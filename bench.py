@@ -348,7 +348,7 @@ def bench_wide(args, torch, swm, wl, G):
     _log("workload: wider shapes and sparsities")
     out = {"metric": "sparse speedup over the in-house dense kernel", "unit": "x", "n_gpus": 1,
            "higher_is_better": True, "dtype": "f16", "data": "synthetic", "detail": {},
-           "config": {"workload": "q_proj 4096x4096 at 50% (N = 24, 32), 60% / 70% / 2:4 (N = 1, 16); 65536x16384 at 50% (N = 16, 32)"}}
+           "config": {"workload": "q_proj 4096x4096 at 50% (N = 24, 32), 60% / 70% / 2:4 (N = 1, 16); down / up at 50% (N = 1, 16); 65536x16384 at 50% (N = 16, 32)"}}
 
     def measure(name, W, mask, X, Ns, rotate=True):
         M, K = W.shape
@@ -381,6 +381,9 @@ def bench_wide(args, torch, swm, wl, G):
 
     W, mask, X = wl.decode_qproj(32)
     measure("q_proj s=0.5", W, mask, X, (24, 32))
+    for i, name in ((6, "down_proj 4096x11008 s=0.5"), (5, "up_proj 11008x4096 s=0.5")):
+        W, mask, X = wl.layer_linear(i, 16)
+        measure(name, W, mask, X, (1, 16))
     for s in (0.6, 0.7):
         W, mask, X = wl.decode_qproj_sparsity(s, 16)
         measure(f"q_proj s={s}", W, mask, X, (1, 16))
