@@ -48,7 +48,8 @@
  *    (use the looped decode kernel), SWM_DECODE_TPW / SWM_DECODE_WAVES_PER_CU
  *    (decode tiles per wave / waves per CU, read when a handle is created),
  *    SWM_DENSE_WAVES_PER_CU (streaming dense kernel), SWM_DENSE_BLOCK = 1 / 2
- *    / 3 (tiled dense block 256x256 / 256x128 / 128x128).
+ *    / 3 (tiled dense block 256x256 / 256x128 / 128x128), SWM_EXPAND_MIN_N
+ *    (tokens from which swm_spmm_ws expands W, at least 33; read once).
  */
 #ifndef SWM_H_
 #define SWM_H_
@@ -164,6 +165,34 @@ swm_status swm_decompress(const swm_format* f, void* W_dev, int64_t ldw, void* s
  *  the prefill kernel.  Asynchronous on stream. */
 swm_status swm_spmm(const swm_format* f, const void* X, int64_t ldx, void* Y, int64_t ldy,
                     int64_t N, void* stream);
+
+/* Bytes of device workspace swm_spmm_ws uses for N tokens: M*K*2 rounded up
+ * to 256 when N reaches the expansion threshold (1024 tokens; the
+ * SWM_EXPAND_MIN_N environment variable, read once per process, changes it;
+ * values below 33 count as 33)
+ * and K is a multiple of 8, else 0.  NULL handle -> 0.  No device work. */
+size_t swm_spmm_workspace_bytes(const swm_format* f, int64_t N);
+
+/* spmm_ws: swm_spmm with a caller-owned device workspace; same operation,
+ * arguments and result (moderate-sparsity page Sec. 2.1, the prefill
+ * product [BL, H] x W^T).  At prefill sizes the product is bound by the
+ * matrix cores, and with unstructured sparsity it executes as many MFMAs as
+ * the dense product; the on-chip path re-expands every tile once per
+ * 256-token block.  When swm_spmm_workspace_bytes(f, N) > 0 and X is 16-byte
+ * aligned with ldx % 8 == 0, this call instead expands W (.) mask once into
+ * the workspace (row-major, leading dimension K, the layout of
+ * swm_decompress) and runs the library's dense MFMA kernel on it: two
+ * launches on stream, the second reading what the first wrote.  Otherwise it
+ * runs swm_spmm's kernels and leaves the workspace untouched.
+ *  workspace: DEVICE, 16-byte aligned, ws_bytes >= swm_spmm_workspace_bytes(f,
+ *  N), owned by the caller, contents undefined afterwards; it may be shared by
+ *  the handles of several layers as long as the calls are ordered on one
+ *  stream (concurrent calls sharing it race).  workspace NULL with ws_bytes 0
+ *  is swm_spmm.  SWM_ERR_INVALID_ARG: NULL handle, X or Y; a workspace that
+ *  is NULL with ws_bytes > 0, misaligned, or too small for a call that
+ *  expands; swm_spmm's argument errors.  Asynchronous on stream. */
+swm_status swm_spmm_ws(const swm_format* f, const void* X, int64_t ldx, void* Y, int64_t ldy, int64_t N,
+                       void* workspace, size_t ws_bytes, void* stream);
 
 /* spmspv: as swm_spmm for 1 <= n <= 16 tokens, for activations with zero
  * input channels (x[t][k] == +0 or -0 for all tokens t).  Such channels

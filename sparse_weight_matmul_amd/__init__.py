@@ -56,6 +56,8 @@ SIGNATURES = {
     "swm_format_destroy": (_i32, [_vp]),
     "swm_decompress": (_i32, [_vp, _vp, _i64, _vp]),
     "swm_spmm": (_i32, [_vp, _vp, _i64, _vp, _i64, _i64, _vp]),
+    "swm_spmm_workspace_bytes": (_sz, [_vp, _i64]),
+    "swm_spmm_ws": (_i32, [_vp, _vp, _i64, _vp, _i64, _i64, _vp, _sz, _vp]),
     "swm_spmspv": (_i32, [_vp, _vp, _i64, _vp, _i64, _i32, _vp]),
     "swm_spmspv_threshold": (_i32, [_vp, _vp, _i64, _vp, _i64, _i32, ctypes.c_float, _vp]),
     "swm_format_enable_skipping": (_i32, [_vp, _vp, ctypes.POINTER(_u64)]),
@@ -277,6 +279,30 @@ def spmm(fmt: Format, X, Y=None, stream=None):
     Y = _out(Y, N, fmt.M, X)
     yp, ldy = _dev2d(Y, "Y", rows=N, cols=fmt.M)
     _check(lib.swm_spmm(fmt._h, xp, ldx, yp, ldy, N, _stream_ptr(stream)), "swm_spmm")
+    return Y
+
+
+def spmm_workspace_bytes(fmt: Format, N: int) -> int:
+    """Device workspace bytes spmm(..., workspace=) uses for N tokens (0: none)."""
+    return int(load().swm_spmm_workspace_bytes(fmt._h, int(N)))
+
+
+def spmm_ws(fmt: Format, X, workspace, Y=None, stream=None):
+    """spmm with a caller-owned device workspace (a CUDA uint8 tensor of at
+    least spmm_workspace_bytes(fmt, N) bytes, or None): for large N the library
+    expands W into it once and runs its dense MFMA kernel.  Same result."""
+    lib = load()
+    N = X.shape[0]
+    xp, ldx = _dev2d(X, "X", cols=fmt.K)
+    Y = _out(Y, N, fmt.M, X)
+    yp, ldy = _dev2d(Y, "Y", rows=N, cols=fmt.M)
+    if workspace is None:
+        wp, wb = None, 0
+    else:
+        if not workspace.is_cuda or not workspace.is_contiguous():
+            raise ValueError("workspace must be a contiguous CUDA tensor")
+        wp, wb = ctypes.c_void_p(workspace.data_ptr()), workspace.numel() * workspace.element_size()
+    _check(lib.swm_spmm_ws(fmt._h, xp, ldx, yp, ldy, N, wp, wb, _stream_ptr(stream)), "swm_spmm_ws")
     return Y
 
 

@@ -3,6 +3,7 @@
 // throws across the boundary or prints.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <atomic>
 #include <cstring>
 #include <mutex>
@@ -372,6 +373,49 @@ static swm_status run_products(const swm_format* f, const void* X, int64_t ldx, 
 swm_status swm_spmm(const swm_format* f, const void* X, int64_t ldx, void* Y, int64_t ldy,
                     int64_t N, void* stream) {
   return run_products(f, X, ldx, Y, ldy, N, false, static_cast<hipStream_t>(stream));
+}
+
+// Tokens from which swm_spmm_ws expands W once into the workspace and runs the
+// dense MFMA kernel (SWM_EXPAND_MIN_N overrides it, read once per process; at
+// least 33: from there swm_spmm's own prefill kernel sums each output in the
+// same order as the dense kernel, so moving the threshold does not change
+// the bits of a result).
+static int64_t expand_min_n() {
+  static const int64_t v = [] {
+    const char* e = getenv("SWM_EXPAND_MIN_N");
+    const long long n = e ? atoll(e) : 0;
+    return n > 0 ? std::max<int64_t>(int64_t(n), 33) : int64_t(1024);
+  }();
+  return v;
+}
+
+static bool expand_route(const swm::Header& h, int64_t N) {
+  return N >= expand_min_n() && h.k >= 8 && h.k % 8 == 0 && h.m > 0;
+}
+
+size_t swm_spmm_workspace_bytes(const swm_format* f, int64_t N) {
+  if (!f || !expand_route(f->h, N)) return 0;
+  return align_up(size_t(f->h.m) * size_t(f->h.k) * 2, 256);
+}
+
+swm_status swm_spmm_ws(const swm_format* f, const void* X, int64_t ldx, void* Y, int64_t ldy, int64_t N,
+                       void* workspace, size_t ws_bytes, void* stream) {
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (!f || !X || !Y) return SWM_ERR_INVALID_ARG;
+  if (!workspace && ws_bytes == 0) return run_products(f, X, ldx, Y, ldy, N, false, s);
+  if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 15)) return SWM_ERR_INVALID_ARG;
+  const size_t need = swm_spmm_workspace_bytes(f, N);
+  if (need == 0 || !swm::prefill_supported(f->h.k, ldx, X)) return run_products(f, X, ldx, Y, ldy, N, false, s);
+  if (ws_bytes < need) return SWM_ERR_INVALID_ARG;
+  if (N <= 0 || ldx < f->h.k || ldy < f->h.m) return SWM_ERR_INVALID_ARG;
+  swm_status st = check_tile_supported(f->h);
+  if (st != SWM_OK) return st;
+  if (!on_current_device(f)) return SWM_ERR_INVALID_ARG;
+  uint16_t* w = static_cast<uint16_t*>(workspace);
+  SWM_HIP(swm::launch_decompress(f->d, w, f->h.k, s));
+  SWM_HIP(swm::launch_prefill_dense(w, f->h.k, static_cast<const uint16_t*>(X), ldx, static_cast<uint16_t*>(Y),
+                                    ldy, f->h.m, f->h.k, N, s));
+  return SWM_OK;
 }
 
 static swm_status run_colruns(const swm_format* f, const void* x, int64_t ldx, void* y, int64_t ldy, int32_t n,

@@ -625,8 +625,11 @@ __global__ __launch_bounds__(256) void stream_kernel(const u32x4* __restrict__ s
 }
 
 // ------------------------------------------------------------------ decompress
-// One wave per 16x64 tile: decode the 16 words into an LDS tile [16][64+8]
-// (padded rows), then write the rows of W with 16-byte stores.
+// One wave per 16x64 tile.  The tile's value run (at most 1024 halves, two
+// coalesced 1 KiB loads) and its 16 bitmap words (two scalar 64-byte loads)
+// are requested together, so a tile waits for one memory round trip; the run
+// is staged in LDS, each word is decoded against it into an LDS tile
+// [16][64+8] (padded rows), and the rows of W are written with 16-byte stores.
 struct DecompArgs {
   const uint32_t* tile_ptr;
   const uint64_t* bits;
@@ -639,25 +642,40 @@ struct DecompArgs {
 };
 
 __global__ __launch_bounds__(256) void decompress_kernel(DecompArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t run[4][1024];
   __shared__ __attribute__((aligned(16))) uint16_t tile[4][16][72];
   const int lane = lane_id();
   const int wave = __builtin_amdgcn_readfirstlane(int(threadIdx.x >> 6));
   const int64_t t = int64_t(blockIdx.x) * 4 + wave;
   if (t >= a.tiles) return;
   const int slab = int(t / a.kt), tj = int(t % a.kt);
-  const uint64_t* tb = a.bits + t * 16;
-  uint32_t pos = a.tile_ptr[t];
+  const uint32_t p0 = const_load<uint32_t>(a.tile_ptr + t);
+  const uint32_t n = const_load<uint32_t>(a.tile_ptr + t + 1) - p0;  // multiple of 8, <= 1024
+  const u32x16 wa = const_load<u32x16>(a.bits + t * 16);
+  const u32x16 wb = const_load<u32x16>(a.bits + t * 16 + 8);
+  u32x4 v0 = {0u, 0u, 0u, 0u}, v1 = {0u, 0u, 0u, 0u};
+  if (uint32_t(lane) * 8u < n) v0 = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(a.vals + p0 + lane * 8));
+  if (512u + uint32_t(lane) * 8u < n)
+    v1 = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(a.vals + p0 + 512 + lane * 8));
+  *reinterpret_cast<u32x4*>(&run[wave][lane * 8]) = v0;
+  *reinterpret_cast<u32x4*>(&run[wave][512 + lane * 8]) = v1;
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  uint32_t pos = 0;
+#pragma unroll
   for (int w = 0; w < 16; ++w) {
-    const uint64_t word = tb[w];
+    const uint64_t word = word_of(w < 8 ? wa : wb, w & 7);
     const bool set = (word >> lane) & 1ull;
     const uint32_t rank =
         __builtin_amdgcn_mbcnt_hi(uint32_t(word >> 32), __builtin_amdgcn_mbcnt_lo(uint32_t(word), 0u));
     const int col = 32 * (w >> 3) + 8 * (lane >> 4) + (w & 7);
-    tile[wave][lane & 15][col] = set ? a.vals[pos + rank] : uint16_t(0);
+    tile[wave][lane & 15][col] = set ? run[wave][min(pos + rank, 1023u)] : uint16_t(0);
     pos += uint32_t(__builtin_popcountll(word));
   }
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   // lane -> (row = lane/8 + 8*it, 8-column chunk = lane%8)
   for (int it = 0; it < 2; ++it) {
     const int r = it * 8 + (lane >> 3), ch = lane & 7;

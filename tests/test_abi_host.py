@@ -161,6 +161,8 @@ def test_null_handle_calls_are_rejected():
     assert lib.swm_spmspv(None, None, 1, None, 1, 1, None) == 1
     assert lib.swm_dense_gemm(None, 1, None, 1, None, 1, 1, 1, 1, None) == 1
     assert lib.swm_decompress(None, None, 1, None) == 1
+    assert lib.swm_spmm_ws(None, None, 1, None, 1, 1024, None, 0, None) == 1
+    assert lib.swm_spmm_workspace_bytes(None, 4096) == 0
     assert lib.swm_format_destroy(None) == 0
     assert lib.swm_format_validate_blob(None, 0) == 1
 

@@ -443,6 +443,100 @@ def test_prefill_upgate_sampled_rows(gpu_lib, s, N):
         assert np.array_equal(Yd.view(np.uint16), Y.view(np.uint16))
 
 
+# ------------------------------------------------------------------ prefill through the workspace (expand once, dense MFMA)
+def _workspace(swm, f, N, extra=0):
+    import torch
+    nb = swm.spmm_workspace_bytes(f, N)
+    return torch.empty(nb + extra, dtype=torch.uint8, device="cuda"), nb
+
+
+@pytest.mark.parametrize("M,K,N", [(520, 392, 1100), (256, 4096, 1024), (1000, 1024, 1031)])
+def test_spmm_ws_expand_route(gpu_lib, M, K, N):
+    """N >= 1024: W is expanded into the workspace and multiplied by the dense
+    kernel.  Checked against the oracle, and bitwise against dense_gemm on
+    the exactly expanded W (same kernel, same operands)."""
+    swm = gpu_lib
+    W, mask = wl.pruned_weight(98, M + K + N, M, K, 0.5)
+    X = np.random.default_rng(M + 7 * N).standard_normal((N, K)).astype(np.float16)
+    f = _compress(swm, W, mask)
+    ws, nb = _workspace(swm, f, N)
+    assert nb >= 2 * M * K and nb % 256 == 0
+    Xd = _t(X)
+    Y = _np(swm.spmm_ws(f, Xd, ws))
+    assert_close(Y, oracle.masked_matmul(W, mask, X), f"spmm_ws {M}x{K}x{N}")
+    Yd = _np(swm.dense_gemm(_t(np.where(mask, W, np.float16(0))), Xd))
+    assert np.array_equal(Y.view(np.uint16), Yd.view(np.uint16))
+    # the workspace holds the expanded W afterwards (row-major, ld = K)
+    got = _np(ws[:2 * M * K]).view(np.uint16).reshape(M, K)
+    assert np.array_equal(got, np.where(mask, W.view(np.uint16), np.uint16(0)))
+
+
+def test_spmm_ws_upgate_n4096_sampled_rows(gpu_lib):
+    """The benchmarked prefill shape through the workspace route."""
+    swm = gpu_lib
+    W, mask, X = wl.prefill_upgate(0.5, 4096)
+    f = _compress(swm, W, mask)
+    ws, _ = _workspace(swm, f, 4096)
+    Y = _np(swm.spmm_ws(f, _t(X), ws))
+    rows = np.random.default_rng(4096).choice(W.shape[0], 128, replace=False)
+    rows = np.concatenate([rows, [0, W.shape[0] - 1]])
+    assert_close(Y[:, rows], oracle.masked_matmul(W[rows], mask[rows], X), "up/gate ws N=4096")
+    Yo = _np(swm.spmm(f, _t(X)))  # on-chip expansion: same MFMA order on the same operands
+    assert np.array_equal(Yo.view(np.uint16), Y.view(np.uint16))
+
+
+def test_spmm_ws_below_threshold_and_fallbacks(gpu_lib):
+    """Below the threshold, without a workspace, or with unaligned X the call
+    runs spmm's kernels (identical bits) and leaves the workspace untouched."""
+    import torch
+    swm = gpu_lib
+    M, K = 300, 512
+    W, mask = wl.pruned_weight(99, 0, M, K, 0.5)
+    f = _compress(swm, W, mask)
+    assert swm.spmm_workspace_bytes(f, 1023) == 0
+    assert swm.spmm_workspace_bytes(f, 1024) == (2 * M * K + 255) // 256 * 256
+    for N in (16, 300, 1023):
+        X = _t(np.random.default_rng(N).standard_normal((N, K)).astype(np.float16))
+        ws = torch.full((4096,), 0xA5, dtype=torch.uint8, device="cuda")
+        a = _np(swm.spmm_ws(f, X, ws)).view(np.uint16)
+        b = _np(swm.spmm(f, X)).view(np.uint16)
+        assert np.array_equal(a, b), N
+        assert bool((ws == 0xA5).all())
+        c = _np(swm.spmm_ws(f, X, None)).view(np.uint16)
+        assert np.array_equal(c, b), N
+    # N above the threshold, X with ldx % 8 != 0: spmm's path, workspace untouched
+    N = 1030
+    Xs = np.random.default_rng(5).standard_normal((N, K + 4)).astype(np.float16)
+    Xv = _t(Xs)[:, :K]
+    ws = torch.full((swm.spmm_workspace_bytes(f, N),), 0x5A, dtype=torch.uint8, device="cuda")
+    a = _np(swm.spmm_ws(f, Xv, ws))
+    assert bool((ws == 0x5A).all())
+    assert np.array_equal(a.view(np.uint16), _np(swm.spmm(f, Xv)).view(np.uint16))
+    assert_close(a, oracle.masked_matmul(W, mask, Xs[:, :K]), "spmm_ws unaligned fallback")
+
+
+def test_spmm_ws_errors(gpu_lib):
+    import ctypes
+    import torch
+    swm = gpu_lib
+    lib = swm.load()
+    M, K, N = 256, 512, 1024
+    W, mask = wl.pruned_weight(99, 1, M, K, 0.5)
+    f = _compress(swm, W, mask)
+    X = torch.zeros((N, K), dtype=torch.float16, device="cuda")
+    Y = torch.empty((N, M), dtype=torch.float16, device="cuda")
+    need = swm.spmm_workspace_bytes(f, N)
+    ws = torch.empty(need + 256, dtype=torch.uint8, device="cuda")
+    xp, yp, wp = ctypes.c_void_p(X.data_ptr()), ctypes.c_void_p(Y.data_ptr()), ctypes.c_void_p(ws.data_ptr())
+    s = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    assert lib.swm_spmm_ws(f._h, xp, K, yp, M, N, wp, need - 1, s) == 1           # too small
+    assert lib.swm_spmm_ws(f._h, xp, K, yp, M, N, None, need, s) == 1             # NULL with bytes
+    assert lib.swm_spmm_ws(f._h, xp, K, yp, M, N, ctypes.c_void_p(ws.data_ptr() + 8), need, s) == 1  # misaligned
+    assert lib.swm_spmm_ws(f._h, xp, K - 8, yp, M, N, wp, need, s) == 1           # ldx < K
+    assert lib.swm_spmm_ws(f._h, xp, K, yp, M, N, wp, need, s) == 0
+    torch.cuda.synchronize()
+
+
 # ------------------------------------------------------------------ wider workloads
 @pytest.mark.parametrize("s", [0.6, 0.7])
 @pytest.mark.parametrize("N", [1, 16])
