@@ -22,13 +22,14 @@ format bytes and invariants.  The pages print no worked numeric example, so no
 pin compares against a value printed on the pages themselves.
 """
 from .reference import (masked_matmul, masked_matmul_skip, active_inputs, to_fp16, threshold_activations,
-                        masked_matmul_threshold)
+                        masked_matmul_threshold, silu, gate_up_silu)
 from .tcb import tcb_encode, tcb_decode, tcb_parse, TcbFormat
 from .exact import exact_masked_matmul, fp64_error_bound
 from .colruns import colruns_encode, colruns_parse, colruns_decode, ColRuns
 
 __all__ = [
     "masked_matmul", "masked_matmul_skip", "active_inputs", "to_fp16", "threshold_activations", "masked_matmul_threshold",
+    "silu", "gate_up_silu",
     "tcb_encode", "tcb_decode", "tcb_parse", "TcbFormat",
     "exact_masked_matmul", "fp64_error_bound",
     "colruns_encode", "colruns_parse", "colruns_decode", "ColRuns",

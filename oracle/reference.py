@@ -88,6 +88,36 @@ def masked_matmul_threshold(W: np.ndarray, mask: np.ndarray | None, X_tok: np.nd
     return masked_matmul_skip(W, mask, threshold_activations(X_tok, tau))
 
 
+def silu(z: np.ndarray) -> np.ndarray:
+    """SiLU(z) = z * sigmoid(z) = z / (1 + exp(-z)) in float64: the activation
+    whose saturation at negative inputs leaves many FFN hidden channels near
+    zero ("Reduced Matrix Multiplication" blog page, Sec. 3.2)."""
+    z = np.asarray(z, dtype=np.float64)
+    with np.errstate(over="ignore"):
+        return z / (1.0 + np.exp(-z))
+
+
+def gate_up_silu(Wg: np.ndarray, mg: np.ndarray | None, Wu: np.ndarray, mu: np.ndarray | None,
+                 X_tok: np.ndarray, tau: float = 0.0) -> np.ndarray:
+    """Hidden activation of a gated FFN block and its input-adaptive threshold.
+
+    The blog page (Sec. 4.2) writes the FFN as H = activation(X W_up),
+    Y = H W_down, and keeps only the high-response channels of H before the
+    down projection; Sec. 4.1 lists the model's own gate output as a ready
+    score.  For the gated (Llama-style) block of these workloads this reads
+    H = SiLU(g) * u with g, u the statically pruned gate and up products of
+    the same tokens (both shaped (N, M)).  A channel is then dropped (+0)
+    when |H| rounded to fp16 is below tau (compared in float32, the same
+    decision rule as threshold_activations); kept entries are returned
+    unrounded, in float64.
+    """
+    g = masked_matmul(Wg, mg, X_tok)
+    u = masked_matmul(Wu, mu, X_tok)
+    h = silu(g) * u
+    keep = np.abs(h.astype(np.float16).astype(np.float32)) >= np.float32(tau)
+    return np.where(keep, h, 0.0)
+
+
 def to_fp16(Y: np.ndarray) -> np.ndarray:
     """Round a float64 result to fp16, round-to-nearest-even."""
     return np.asarray(Y, dtype=np.float64).astype(np.float16)

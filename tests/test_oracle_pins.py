@@ -313,3 +313,72 @@ def test_planted_format_mistakes_fail_hand_bytes():
     f = oracle.tcb_encode(W, None, TK=32)
     assert [int(b) for b in f.bits] == d["bits"]
     assert int(f.bits[0]) != (1 | 4 | (1 << 17))
+
+
+# ------------------------------------------------------------------ gated FFN hidden activation
+def test_silu_closed_forms():
+    """SiLU(z) = z / (1 + e^-z): values worked by hand, its odd-part identity
+    SiLU(z) - SiLU(-z) = z, and its limits."""
+    z = np.array([0.0, 1.0, -1.0, 2.0, -2.0])
+    want = [0.0, 0.7310585786300049, -0.2689414213699951, 1.7615941559557649, -0.2384058440442351]
+    assert np.allclose(oracle.silu(z), want, rtol=0, atol=1e-15)
+    g = np.random.default_rng(31).standard_normal(1000) * 5
+    assert np.allclose(oracle.silu(g) - oracle.silu(-g), g, rtol=0, atol=1e-12)
+    assert abs(oracle.silu(np.array([40.0]))[0] - 40.0) < 1e-15
+    assert 0 > oracle.silu(np.array([-40.0]))[0] > -1e-15
+    assert oracle.silu(np.array([-1000.0]))[0] == 0.0  # exp overflow handled
+
+
+def test_gate_up_silu_hand_example():
+    d = json.load(open(os.path.join(GOLDEN, "gate_up_silu_hand_example.json")))
+    Wg, Wu = np.array(d["Wg"], dtype=np.float16), np.array(d["Wu"], dtype=np.float16)
+    mg, mu = np.array(d["mask_g"], dtype=bool), np.array(d["mask_u"], dtype=bool)
+    X = np.array(d["X"], dtype=np.float16)
+    H = np.array(d["H"])
+    for c in d["cases"]:
+        got = oracle.gate_up_silu(Wg, mg, Wu, mu, X, c["tau"])
+        want = np.where(np.array(c["kept"]), H, 0.0)
+        assert np.allclose(got, want, rtol=0, atol=1e-15), c["tau"]
+    # gate and up are not interchangeable, and the gate mask is applied
+    assert not np.allclose(oracle.gate_up_silu(Wu, mu, Wg, mg, X), H, atol=1e-3)
+    assert not np.allclose(oracle.gate_up_silu(Wg, None, Wu, mu, X), H, atol=1e-3)
+
+
+def test_gate_up_silu_brute_force():
+    """Pure-Python loops with math.exp on a small random case."""
+    import math
+    g = np.random.default_rng(32)
+    M, K, N = 7, 13, 3
+    Wg = (0.3 * g.standard_normal((M, K))).astype(np.float16)
+    Wu = (0.3 * g.standard_normal((M, K))).astype(np.float16)
+    mg, mu = g.random((M, K)) < 0.5, g.random((M, K)) < 0.6
+    X = g.standard_normal((N, K)).astype(np.float16)
+    got = oracle.gate_up_silu(Wg, mg, Wu, mu, X, 0.0)
+    for t in range(N):
+        for m in range(M):
+            gs = sum(float(Wg[m, k]) * float(X[t, k]) for k in range(K) if mg[m, k])
+            us = sum(float(Wu[m, k]) * float(X[t, k]) for k in range(K) if mu[m, k])
+            h = gs / (1.0 + math.exp(-gs)) * us
+            assert abs(got[t, m] - h) <= 1e-12 * max(1.0, abs(h)), (t, m)
+
+
+def test_gate_up_silu_threshold_invariants():
+    g = np.random.default_rng(33)
+    M, K, N = 40, 64, 4
+    Wg = (0.1 * g.standard_normal((M, K))).astype(np.float16)
+    Wu = (0.1 * g.standard_normal((M, K))).astype(np.float16)
+    mg, mu = g.random((M, K)) < 0.5, g.random((M, K)) < 0.5
+    X = g.standard_normal((N, K)).astype(np.float16)
+    full = oracle.gate_up_silu(Wg, mg, Wu, mu, X, 0.0)
+    assert np.all(oracle.gate_up_silu(Wg, mg, Wu, mu, X, 1e4) == 0)
+    prev = np.ones(full.shape, dtype=bool)
+    for tau in (0.0, 0.05, 0.1, 0.3):
+        h = oracle.gate_up_silu(Wg, mg, Wu, mu, X, tau)
+        kept = h != 0
+        assert np.all(kept <= prev) and np.array_equal(h[kept], full[kept])
+        # the decision is taken on the fp16-rounded value
+        dec = np.abs(full.astype(np.float16).astype(np.float32)) >= np.float32(tau)
+        assert np.array_equal(kept, dec & (full != 0))
+        prev = kept
+    # an all-pruned gate gives SiLU(0) = 0 everywhere
+    assert np.all(oracle.gate_up_silu(Wg, np.zeros_like(mg), Wu, mu, X) == 0)
