@@ -262,6 +262,100 @@ def bench_spmspv(args, torch, swm, wl, G):
     return out
 
 
+# ------------------------------------------------------------------ decode FFN block
+def bench_mlp(args, torch, swm, wl, G):
+    """Decode FFN block of the Llama-2-7B-shaped layer (gate/up 11008x4096, down
+    4096x11008, 50%): gate and up in one launch with the SiLU * mul epilogue
+    and the threshold tau, then the skipping down projection; against the
+    same chain unfused (two sparse products, SiLU * mul and the threshold as
+    torch element-wise ops, the full sparse down product) and the dense chain
+    (in-house dense kernel, same element-wise ops)."""
+    _log("workload: decode FFN block, fused gate/up + threshold + skipping down")
+    F = torch.nn.functional
+    tau = args.tau
+    Wg, mg, X = wl.layer_linear(4, 16)
+    Wu, mu, _ = wl.layer_linear(5, 16)
+    Wd, md, _ = wl.layer_linear(6, 1)
+    fgs, fbg = rotating_formats(swm, Wg, mg)
+    fus, fbu = rotating_formats(swm, Wu, mu)
+    fds, fbd = rotating_formats(swm, Wd, md)
+    _log(f"column-run encoding for {len(fds)} rotated down copies")
+    for f in fds:
+        f.enable_skipping()
+    dgs, dus, dds = rotating_dense(torch, Wg), rotating_dense(torch, Wu), rotating_dense(torch, Wd)
+    C, CD = min(len(fgs), len(fus), len(fds)), min(len(dgs), len(dus), len(dds))
+    M, K = Wg.shape
+    Xd = torch.from_numpy(X).cuda()
+    out = {"metric": "decode FFN block time (gate/up fused with SiLU*mul and threshold, skipping down)",
+           "unit": "us", "n_gpus": 1, "higher_is_better": False, "dtype": "f16", "data": "synthetic",
+           "detail": {}, "config": {"workload": "Llama-2-7B FFN block, gate/up 11008x4096 + down 4096x11008, "
+                                                "50% unstructured", "tau": tau}}
+    for n in (1, 4, 16):
+        H = torch.empty((n, M), dtype=torch.float16, device="cuda")
+        g = torch.empty((n, M), dtype=torch.float16, device="cuda")
+        u = torch.empty((n, M), dtype=torch.float16, device="cuda")
+        y = torch.empty((n, K), dtype=torch.float16, device="cuda")
+        x = Xd[:n]
+
+        def epilogue():
+            h = (F.silu(g.float()) * u.float()).half()
+            return torch.where(h.abs() >= tau, h, torch.zeros_like(h))
+
+        def glu(i):
+            swm.gate_up_silu(fgs[i], fus[i], x, tau, H)
+
+        def fused(i):
+            swm.gate_up_silu(fgs[i], fus[i], x, tau, H)
+            swm.spmspv(fds[i], H, y)
+
+        def fused_full(i):
+            swm.gate_up_silu(fgs[i], fus[i], x, tau, H)
+            swm.spmm(fds[i], H, y)
+
+        def two(i):
+            swm.spmm(fgs[i], x, g)
+            swm.spmm(fus[i], x, u)
+
+        def unfused(i):
+            swm.spmm(fgs[i], x, g)
+            swm.spmm(fus[i], x, u)
+            swm.spmm(fds[i], epilogue(), y)
+
+        def dense(i):
+            swm.dense_gemm(dgs[i], x, g)
+            swm.dense_gemm(dus[i], x, u)
+            swm.dense_gemm(dds[i], epilogue(), y)
+
+        for i in range(2):
+            fused(i), fused_full(i), unfused(i), dense(i)
+        torch.cuda.synchronize()
+        t = {name: G.time(G.capture([lambda i=i, fn=fn: fn(i % cc) for i in range(cc)]), 3) / cc * 1e3
+             for name, fn, cc in (("fused_glu", glu, C), ("two_spmm", two, C), ("fused_chain", fused, C),
+                                  ("fused_full_chain", fused_full, C), ("unfused_chain", unfused, C),
+                                  ("dense_chain", dense, CD))}
+        best = min(t["fused_chain"], t["fused_full_chain"])
+        glu_alg = fbg + fbu + 2 * K * n + 2 * M * n
+        swm.gate_up_silu(fgs[0], fus[0], x, tau, H)
+        torch.cuda.synchronize()
+        out["detail"][str(n)] = {
+            "fused_glu_us": t["fused_glu"], "two_spmm_us": t["two_spmm"],
+            "fused_glu_GBps_alg": glu_alg / (t["fused_glu"] * 1e-6) / 1e9,
+            "fused_skip_chain_us": t["fused_chain"], "fused_full_chain_us": t["fused_full_chain"],
+            "best_fused_chain_us": best, "unfused_chain_us": t["unfused_chain"],
+            "dense_chain_us": t["dense_chain"], "h_zero_frac": float((H == 0).float().mean()),
+            "h_inactive_cols": float((H == 0).all(dim=0).float().mean()),
+            "speedup_vs_unfused": t["unfused_chain"] / best, "speedup_vs_dense": t["dense_chain"] / best}
+        _log(f"n={n}: fused {t['fused_chain']:.2f} / {t['fused_full_chain']:.2f} us (skipping / full down), "
+             f"unfused {t['unfused_chain']:.2f} us, dense {t['dense_chain']:.2f} us")
+    out["value"] = out["detail"]["1"]["best_fused_chain_us"]
+    d1 = out["detail"]["1"]
+    out["roofline"] = {"bound": "hbm", "achieved": d1["fused_glu_GBps_alg"], "peak": 8000.0, "unit": "GB/s",
+                       "frac": d1["fused_glu_GBps_alg"] / 8000.0, "traffic": None,
+                       "kernel": "decode_seq_kernel (gated), gate+up, n=1",
+                       "alg_bytes_per_launch": fbg + fbu + 2 * K + 2 * M, "avg_launch_us": d1["fused_glu_us"]}
+    return out
+
+
 # ------------------------------------------------------------------ prefill
 def bench_prefill(args, torch, swm, wl, G):
     _log("workload: prefill up/gate 11008x4096")
@@ -422,7 +516,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="decode", choices=["decode", "spmspv", "prefill", "layer", "wide", "calib"])
+    ap.add_argument("--workload", default="decode", choices=["decode", "spmspv", "prefill", "layer", "wide", "mlp", "calib"])
     ap.add_argument("--tau", type=float, default=0.3)
     ap.add_argument("--prefill-n", default="512,2048,4096")
     ap.add_argument("--prefill-s", default="0.5,0.6,0.7")
@@ -439,7 +533,7 @@ def main():
     torch.cuda.set_device(0)
     G = Graphs(torch)
     fn = {"decode": bench_decode, "spmspv": bench_spmspv, "prefill": bench_prefill, "layer": bench_layer,
-          "wide": bench_wide, "calib": bench_calib}
+          "wide": bench_wide, "mlp": bench_mlp, "calib": bench_calib}
     out = fn[args.workload](args, torch, swm, wl, G)
     out.setdefault("n_gpus", 1)
     print(json.dumps(out), flush=True)

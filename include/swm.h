@@ -194,7 +194,30 @@ size_t swm_spmm_workspace_bytes(const swm_format* f, int64_t N);
 swm_status swm_spmm_ws(const swm_format* f, const void* X, int64_t ldx, void* Y, int64_t ldy, int64_t N,
                        void* workspace, size_t ws_bytes, void* stream);
 
-/* spmspv: as swm_spmm for 1 <= n <= 16 tokens, for activations with zero
+/* gate_up_silu: the hidden activation of a gated FFN block for 1 <= n <= 16
+ * decode tokens, H = SiLU(X W_g^T) (.) (X W_u^T), with the input-adaptive
+ * threshold applied: an entry whose magnitude (after rounding to fp16) is
+ * below tau is stored as +0.  Source: "Reduced Matrix Multiplication" blog
+ * page, Sec. 3.2 (SiLU leaves many hidden channels near zero) and Secs.
+ * 4.1-4.2 (H = activation(X W_up) with the model's gate output as the score;
+ * only high-response channels of H enter the down projection).  SiLU(z) =
+ * z / (1 + e^-z).  Both products run in one launch of the decode kernel (the
+ * waves of a slab's workgroup split between the two formats); g and u stay
+ * in fp32 and h = SiLU(g) * u is rounded once to fp16.  The output is the
+ * input of swm_spmspv / swm_spmspv_threshold on the down projection.
+ *  g, u: handles of the gate and up weights, same M and K.  X: DEVICE fp16
+ *  token-major n x K (ldx >= K).  H: DEVICE fp16 n x M (ldh >= M),
+ *  overwritten.  tau: 0 <= tau <= 65504 (0 keeps every entry).
+ *  SWM_ERR_INVALID_ARG: NULL pointers, n outside 1..16, tau outside its
+ *  range or NaN, shapes that differ, leading dimensions too small, a handle
+ *  on another device.  SWM_ERR_UNSUPPORTED: X not 16-byte aligned or ldx % 8
+ *  != 0 or K % 8 != 0, n*ldx beyond 32-bit byte offsets, tiles other than
+ *  16 x 64, or K above 8192 (more than 128 tiles per row: the two formats
+ *  no longer fit one workgroup).  Asynchronous on stream. */
+swm_status swm_gate_up_silu(const swm_format* g, const swm_format* u, const void* X, int64_t ldx, void* H,
+                            int64_t ldh, int32_t n, float tau, void* stream);
+
+/* spmspv: as swm_spmm for 1 <= n <= 16 tokens/* spmspv: as swm_spmm for 1 <= n <= 16 tokens, for activations with zero
  * input channels (x[t][k] == +0 or -0 for all tokens t).  Such channels
  * contribute exact zeros, so the result equals swm_spmm's up to fp32
  * summation order.  Skipping is applied only where it pays: on the aligned

@@ -60,6 +60,7 @@ SIGNATURES = {
     "swm_spmm_ws": (_i32, [_vp, _vp, _i64, _vp, _i64, _i64, _vp, _sz, _vp]),
     "swm_spmspv": (_i32, [_vp, _vp, _i64, _vp, _i64, _i32, _vp]),
     "swm_spmspv_threshold": (_i32, [_vp, _vp, _i64, _vp, _i64, _i32, ctypes.c_float, _vp]),
+    "swm_gate_up_silu": (_i32, [_vp, _vp, _vp, _i64, _vp, _i64, _i32, ctypes.c_float, _vp]),
     "swm_format_enable_skipping": (_i32, [_vp, _vp, ctypes.POINTER(_u64)]),
     "swm_colruns_encode_blob": (_i32, [_vp, _sz, _vp, _sz, ctypes.POINTER(_sz)]),
     "swm_dense_gemm": (_i32, [_vp, _i64, _vp, _i64, _vp, _i64, _i64, _i64, _i64, _vp]),
@@ -304,6 +305,19 @@ def spmm_ws(fmt: Format, X, workspace, Y=None, stream=None):
         wp, wb = ctypes.c_void_p(workspace.data_ptr()), workspace.numel() * workspace.element_size()
     _check(lib.swm_spmm_ws(fmt._h, xp, ldx, yp, ldy, N, wp, wb, _stream_ptr(stream)), "swm_spmm_ws")
     return Y
+
+
+def gate_up_silu(gate: Format, up: Format, X, tau: float = 0.0, H=None, stream=None):
+    """Gated FFN hidden activation for 1..16 decode tokens: H (n, M) =
+    SiLU(X @ W_g.T) * (X @ W_u.T), entries with |H| < tau stored as +0."""
+    lib = load()
+    n = X.shape[0]
+    xp, ldx = _dev2d(X, "X", cols=gate.K)
+    H = _out(H, n, gate.M, X)
+    hp, ldh = _dev2d(H, "H", rows=n, cols=gate.M)
+    _check(lib.swm_gate_up_silu(gate._h, up._h, xp, ldx, hp, ldh, n, float(tau), _stream_ptr(stream)),
+           "swm_gate_up_silu")
+    return H
 
 
 def spmspv(fmt: Format, x, y=None, stream=None):

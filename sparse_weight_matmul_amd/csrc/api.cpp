@@ -441,6 +441,27 @@ swm_status swm_spmspv_threshold(const swm_format* f, const void* x, int64_t ldx,
   return run_colruns(f, x, ldx, y, ldy, n, tau, stream);
 }
 
+swm_status swm_gate_up_silu(const swm_format* g, const swm_format* u, const void* X, int64_t ldx, void* H,
+                            int64_t ldh, int32_t n, float tau, void* stream) {
+  if (!g || !u || !X || !H) return SWM_ERR_INVALID_ARG;
+  if (n < 1 || n > 16 || !(tau >= 0.f) || !(tau <= 65504.f)) return SWM_ERR_INVALID_ARG;
+  if (g->h.m != u->h.m || g->h.k != u->h.k) return SWM_ERR_INVALID_ARG;
+  if (ldx < g->h.k || ldh < g->h.m || ldx <= 0 || ldh <= 0) return SWM_ERR_INVALID_ARG;
+  swm_status st = check_tile_supported(g->h);
+  if (st == SWM_OK) st = check_tile_supported(u->h);
+  if (st != SWM_OK) return st;
+  if (!on_current_device(g) || !on_current_device(u)) return SWM_ERR_INVALID_ARG;
+  if (!swm::prefill_supported(g->h.k, ldx, X)) return SWM_ERR_UNSUPPORTED;  // aligned X, K % 8 == 0
+  if (2 * ((int64_t(n) - 1) * ldx + g->h.k) >= (int64_t(1) << 32)) return SWM_ERR_UNSUPPORTED;
+  int dev = 0;
+  SWM_HIP(hipGetDevice(&dev));
+  const swm::DecodePlan p = swm::plan_decode_glu(g->h, u->h, num_cus(dev));
+  if (p.seq_segs == 0) return SWM_ERR_UNSUPPORTED;
+  SWM_HIP(swm::launch_decode_glu(g->d, u->d, p, static_cast<const uint16_t*>(X), ldx, static_cast<uint16_t*>(H), ldh,
+                                 n, tau, static_cast<hipStream_t>(stream)));
+  return SWM_OK;
+}
+
 swm_status swm_hbm_stream(const void* buf, size_t bytes, int32_t unroll, int32_t blocks,
                           uint32_t* out, void* stream) {
   if (!buf || !out || bytes % 16 || blocks <= 0) return SWM_ERR_INVALID_ARG;

@@ -153,6 +153,37 @@ __device__ __forceinline__ void slab_reduce_store(float* red, int nwaves, int wa
   }
 }
 
+// Gated epilogue: the partials of waves [0, wpm) sum to g and those of waves
+// [wpm, 2 wpm) to u, each in fixed wave order; the stored value is
+// h = SiLU(g) * u = g / (1 + e^-g) * u in fp32, rounded once to fp16, and +0
+// where |h| (as rounded) is below tau.
+__device__ __forceinline__ void slab_reduce_glu_store(float* red, int wpm, int wave, int lane, const f32x4& acc,
+                                                      int slab, int M, int N, uint16_t* Y, int64_t ldy,
+                                                      float tau) {
+#pragma unroll
+  for (int v = 0; v < 4; ++v) red[wave * 256 + (lane & 15) * 16 + (lane >> 4) * 4 + v] = acc[v];
+  __syncthreads();
+  const int m0 = slab * kSlab;
+  for (int e = threadIdx.x; e < N * kSlab; e += blockDim.x) {
+    const int tok = e >> 4, row = e & 15;
+    float vg[8], vu[8];
+#pragma unroll
+    for (int w = 0; w < 8; ++w) {
+      vg[w] = red[min(w, wpm - 1) * 256 + e];
+      vu[w] = red[(wpm + min(w, wpm - 1)) * 256 + e];
+    }
+    float g = 0.f, u = 0.f;
+#pragma unroll
+    for (int w = 0; w < 8; ++w) {
+      g += w < wpm ? vg[w] : 0.f;
+      u += w < wpm ? vu[w] : 0.f;
+    }
+    _Float16 h = _Float16(g / (1.f + expf(-g)) * u);
+    if (!(fabsf(float(h)) >= tau)) h = _Float16(0.f);
+    if (m0 + row < M) Y[int64_t(tok) * ldy + m0 + row] = __builtin_bit_cast(uint16_t, h);
+  }
+}
+
 struct DecodeArgs {
   const uint32_t* tile_ptr;
   const uint64_t* bits;
@@ -163,6 +194,26 @@ struct DecodeArgs {
   int64_t ldx, ldy;
   int M, K, N, kt;
   int tpw;  // tiles per wave
+};
+
+// Arguments of the gated instances of the straight-line kernel: waves
+// [0, wpm) decode the first format (gate), waves [wpm, 2 wpm) the second (up,
+// same M and K), and the epilogue stores SiLU(g) * u with |.| < tau dropped.
+// A separate type keeps the ungated instances' arguments as they are.
+struct GluArgs : DecodeArgs {
+  const uint32_t* tile_ptr2;
+  const uint64_t* bits2;
+  const uint16_t* vals2;
+  int wpm;
+  float tau;
+};
+template <bool kGlu>
+struct SeqArgs {
+  using type = DecodeArgs;
+};
+template <>
+struct SeqArgs<true> {
+  using type = GluArgs;
 };
 
 constexpr int kSegTiles = 4;  // tiles per streamed segment
@@ -357,7 +408,8 @@ __global__ __launch_bounds__(1024) void decode_kernel(DecodeArgs a) {
 
 // ------------------------------------------------------------------ sparse, straight-line schedule
 // Same work split as decode_kernel (one workgroup per slab, wave w owns tiles
-// [w*tpw, w*tpw + tpw) with tpw <= 2*NS), but the whole wave program is
+// [w*tpw, w*tpw + tpw) with tpw <= 2*NS; in gated mode the second half of the
+// waves does the same over the second format), but the whole wave program is
 // unrolled so that every vector load is issued unconditionally in a fixed
 // order, and each wait covers exactly the data it needs (vector loads return
 // in issue order):
@@ -381,8 +433,8 @@ __global__ __launch_bounds__(1024) void decode_kernel(DecodeArgs a) {
 //     overlaps the rest of the stream.
 constexpr int kXRow = 272;  // LDS bytes per token row of a segment's activations (256 + pad)
 
-template <int NS, int kC, int kXI>
-__global__ __launch_bounds__(1024) void decode_seq_kernel(DecodeArgs a) {
+template <int NS, int kC, int kXI, bool kGlu = false>
+__global__ __launch_bounds__(1024) void decode_seq_kernel(typename SeqArgs<kGlu>::type a) {
   constexpr int kT = 2 * NS;      // tile slots per wave
   constexpr int kSteps = 2 * kT;  // 32-column steps
   constexpr int kTouch = (kT * 128 + 1023) / 1024;
@@ -402,7 +454,21 @@ __global__ __launch_bounds__(1024) void decode_seq_kernel(DecodeArgs a) {
   const uint32_t buf = lds_addr(smem + 16 + size_t(wave) * kWaveLds);
   const uint32_t xbuf = buf + kC * 1024;
 
-  const int j0 = wave * a.tpw;
+  // The format this wave decodes (wave-uniform; the second one only in the
+  // gated instances).
+  const uint32_t* tile_ptr = a.tile_ptr;
+  const uint64_t* bits = a.bits;
+  const uint16_t* vals = a.vals;
+  int fwave = wave;
+  if constexpr (kGlu) {
+    if (wave >= a.wpm) {
+      tile_ptr = a.tile_ptr2;
+      bits = a.bits2;
+      vals = a.vals2;
+      fwave = wave - a.wpm;
+    }
+  }
+  const int j0 = fwave * a.tpw;
   const int nt = min(a.tpw, a.kt - j0);  // tiles of this wave (<= kT)
 
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -413,11 +479,11 @@ __global__ __launch_bounds__(1024) void decode_seq_kernel(DecodeArgs a) {
 
     uint32_t tp[kT + 1];
 #pragma unroll
-    for (int i = 0; i <= kT; ++i) tp[i] = const_load<uint32_t>(a.tile_ptr + tb + min(i, nt));
+    for (int i = 0; i <= kT; ++i) tp[i] = const_load<uint32_t>(tile_ptr + tb + min(i, nt));
     u32x16 wv[kSteps];
     auto load_w = [&](int t) {
       const int jt = min(t >> 1, nt - 1);
-      wv[t] = const_load<u32x16>(a.bits + (tb + jt) * 16 + 8 * (t & 1));
+      wv[t] = const_load<u32x16>(bits + (tb + jt) * 16 + 8 * (t & 1));
     };
     load_w(0);
     __builtin_amdgcn_sched_barrier(0);
@@ -425,7 +491,7 @@ __global__ __launch_bounds__(1024) void decode_seq_kernel(DecodeArgs a) {
     u32x4 th[kTouch];
     {
       const uint32_t wbytes = uint32_t(nt) * 128u;
-      const uint8_t* wb = reinterpret_cast<const uint8_t*>(a.bits + tb * 16);
+      const uint8_t* wb = reinterpret_cast<const uint8_t*>(bits + tb * 16);
 #pragma unroll
       for (int i = 0; i < kTouch; ++i)
         th[i] = *reinterpret_cast<const u32x4*>(wb + min(uint32_t(i * 1024 + lane * 16), wbytes - 16u));
@@ -468,7 +534,7 @@ __global__ __launch_bounds__(1024) void decode_seq_kernel(DecodeArgs a) {
 #pragma unroll
       for (int c = 0; c < kC; ++c) {
         const uint32_t off = min(p0 + uint32_t(c * 512 + lane * 8), last);
-        r[g][c] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(a.vals + off));
+        r[g][c] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vals + off));
       }
       __builtin_amdgcn_sched_barrier(0);
     };
@@ -522,8 +588,11 @@ __global__ __launch_bounds__(1024) void decode_seq_kernel(DecodeArgs a) {
   if (keep == 0x9E3779B9u && a.N < 0) a.Y[0] = 0;  // never true: keeps the L2 touch loads
 
   __syncthreads();  // all wave buffers are free: reuse them as the reduction area
-  slab_reduce_store(reinterpret_cast<float*>(smem + 16), nwaves, wave, lane, acc, slab, a.M, a.N,
-                    a.Y, a.ldy);
+  if constexpr (kGlu)
+    slab_reduce_glu_store(reinterpret_cast<float*>(smem + 16), a.wpm, wave, lane, acc, slab, a.M, a.N, a.Y, a.ldy,
+                          a.tau);
+  else
+    slab_reduce_store(reinterpret_cast<float*>(smem + 16), nwaves, wave, lane, acc, slab, a.M, a.N, a.Y, a.ldy);
 }
 
 // ------------------------------------------------------------------ dense, N <= 16
@@ -690,21 +759,22 @@ __global__ __launch_bounds__(256) void decompress_kernel(DecompArgs a) {
   }
 }
 
-template <int NS, int kXI>
-void launch_seq_x(int kc, dim3 grid, dim3 block, size_t lds, hipStream_t s, const DecodeArgs& a) {
+template <int NS, int kXI, bool kGlu>
+void launch_seq_x(int kc, dim3 grid, dim3 block, size_t lds, hipStream_t s, const typename SeqArgs<kGlu>::type& a) {
   switch (kc) {
-    case 1: hipLaunchKernelGGL((decode_seq_kernel<NS, 1, kXI>), grid, block, lds, s, a); break;
-    case 2: hipLaunchKernelGGL((decode_seq_kernel<NS, 2, kXI>), grid, block, lds, s, a); break;
-    case 3: hipLaunchKernelGGL((decode_seq_kernel<NS, 3, kXI>), grid, block, lds, s, a); break;
-    default: hipLaunchKernelGGL((decode_seq_kernel<NS, 4, kXI>), grid, block, lds, s, a); break;
+    case 1: hipLaunchKernelGGL((decode_seq_kernel<NS, 1, kXI, kGlu>), grid, block, lds, s, a); break;
+    case 2: hipLaunchKernelGGL((decode_seq_kernel<NS, 2, kXI, kGlu>), grid, block, lds, s, a); break;
+    case 3: hipLaunchKernelGGL((decode_seq_kernel<NS, 3, kXI, kGlu>), grid, block, lds, s, a); break;
+    default: hipLaunchKernelGGL((decode_seq_kernel<NS, 4, kXI, kGlu>), grid, block, lds, s, a); break;
   }
 }
 
-template <int NS>
-void launch_seq_ns(int kc, int kxi, dim3 grid, dim3 block, size_t lds, hipStream_t s, const DecodeArgs& a) {
-  if (kxi == 1) launch_seq_x<NS, 1>(kc, grid, block, lds, s, a);
-  else if (kxi == 2) launch_seq_x<NS, 2>(kc, grid, block, lds, s, a);
-  else launch_seq_x<NS, 4>(kc, grid, block, lds, s, a);
+template <int NS, bool kGlu = false>
+void launch_seq_ns(int kc, int kxi, dim3 grid, dim3 block, size_t lds, hipStream_t s,
+                   const typename SeqArgs<kGlu>::type& a) {
+  if (kxi == 1) launch_seq_x<NS, 1, kGlu>(kc, grid, block, lds, s, a);
+  else if (kxi == 2) launch_seq_x<NS, 2, kGlu>(kc, grid, block, lds, s, a);
+  else launch_seq_x<NS, 4, kGlu>(kc, grid, block, lds, s, a);
 }
 
 // Smallest instantiated segment count covering `segs` two-tile segments (0: none).
@@ -892,6 +962,75 @@ hipError_t launch_dense_small(const DensePlan& p, const uint16_t* W, int64_t ldw
   const size_t lds = size_t(p.waves) * 256 * 4;
   if (vec) hipLaunchKernelGGL((dense_small_kernel<true>), grid, block, lds, s, a);
   else hipLaunchKernelGGL((dense_small_kernel<false>), grid, block, lds, s, a);
+  return hipGetLastError();
+}
+
+DecodePlan plan_decode_glu(const Header& g, const Header& u, int num_cus) {
+  // Both formats' tiles in one launch: enough tiles per wave for about one
+  // round of 16 waves per CU, at most 8 waves per format (16 per workgroup)
+  // and at most 16 tiles per wave (the largest straight-line instance).
+  DecodePlan p;
+  const int64_t kt = g.kt;
+  const int64_t min_tpw = (kt + 7) / 8;
+  int64_t tpw = (2 * int64_t(g.mt) * kt + int64_t(num_cus) * 16 - 1) / (int64_t(num_cus) * 16);
+  tpw = std::min<int64_t>(std::max<int64_t>(tpw, min_tpw), 16);
+  static const int env_tpw = env_int("SWM_GLU_TPW", 0);
+  if (env_tpw > 0) tpw = env_tpw;
+  if (tpw < min_tpw || tpw > 16 || kt < 1) {
+    p.seq_segs = 0;  // no instance covers this shape
+    return p;
+  }
+  p.tiles_per_wave = int(tpw);
+  p.waves = 2 * int((kt + tpw - 1) / tpw);
+  // gated instances exist for 1, 2, 4 and 8 two-tile segments per wave
+  const int segs = int((tpw + 1) / 2);
+  p.seq_segs = segs <= 1 ? 1 : segs <= 2 ? 2 : segs <= 4 ? 4 : 8;
+  // Two tiles hold at most 2 * max_tile values: a bound on every segment.
+  const uint64_t max2 = 4ull * std::max(g.max_tile, u.max_tile);
+  p.seq_chunks = int(std::max<uint64_t>((max2 + 1023) / 1024, 1));
+  if (p.seq_chunks > 4) p.seq_segs = 0;
+  return p;
+}
+
+hipError_t launch_decode_glu(const DevFormat& g, const DevFormat& u, const DecodePlan& p, const uint16_t* X,
+                             int64_t ldx, uint16_t* H, int64_t ldh, int n, float tau, hipStream_t s) {
+  GluArgs a;
+  a.tile_ptr = g.tile_ptr;
+  a.bits = g.bits;
+  a.vals = g.vals;
+  a.zeros = g.zeros;
+  a.X = X;
+  a.Y = H;
+  a.ldx = ldx;
+  a.ldy = ldh;
+  a.M = int(g.h.m);
+  a.K = int(g.h.k);
+  a.N = n;
+  a.kt = int(g.h.kt);
+  a.tpw = p.tiles_per_wave;
+  a.tile_ptr2 = u.tile_ptr;
+  a.bits2 = u.bits;
+  a.vals2 = u.vals;
+  a.wpm = p.waves / 2;
+  a.tau = tau;
+  // The caller has checked these; they are what the straight-line kernel assumes.
+  if (g.h.tm != uint32_t(kSlab) || g.h.tk != uint32_t(kTK) || u.h.tm != g.h.tm || u.h.tk != g.h.tk ||
+      u.h.m != g.h.m || u.h.k != g.h.k)
+    return hipErrorInvalidValue;
+  if (p.seq_segs == 0 || p.waves < 2 || p.waves > 16 || p.waves % 2 || n < 1 || n > 16 || a.K < 8 || a.K % 8 ||
+      ldx % 8 || (reinterpret_cast<uintptr_t>(X) & 15) || 2 * ((int64_t(n) - 1) * ldx + g.h.k) >= (int64_t(1) << 32))
+    return hipErrorInvalidValue;
+  if (g.h.mt == 0) return hipSuccess;
+  const dim3 grid{unsigned(g.h.mt), 1, 1}, block{unsigned(p.waves * 64), 1, 1};
+  const int kxi = n <= 4 ? 1 : n <= 8 ? 2 : 4;
+  const size_t per_wave = size_t(p.seq_chunks) * 1024 + size_t(4 * kxi) * kXRow;
+  const size_t lds = 16 + size_t(p.waves) * per_wave;
+  switch (p.seq_segs) {
+    case 1: launch_seq_ns<1, true>(p.seq_chunks, kxi, grid, block, lds, s, a); break;
+    case 2: launch_seq_ns<2, true>(p.seq_chunks, kxi, grid, block, lds, s, a); break;
+    case 4: launch_seq_ns<4, true>(p.seq_chunks, kxi, grid, block, lds, s, a); break;
+    default: launch_seq_ns<8, true>(p.seq_chunks, kxi, grid, block, lds, s, a); break;
+  }
   return hipGetLastError();
 }
 

@@ -56,6 +56,13 @@ ColRunsPlan plan_colruns(int64_t M, int64_t K);
 hipError_t launch_spmspv_cr(const DevColRuns& c, const uint16_t* x, int64_t ldx, uint16_t* y, int64_t ldy,
                             int n, float tau, hipStream_t s);
 
+// Gated FFN decode: H = SiLU(W_g X) * (W_u X) with |H| < tau dropped, both
+// formats in one launch of the straight-line kernel (seq_segs == 0: no
+// instance covers the shape).
+DecodePlan plan_decode_glu(const Header& g, const Header& u, int num_cus);
+hipError_t launch_decode_glu(const DevFormat& g, const DevFormat& u, const DecodePlan& p, const uint16_t* X,
+                             int64_t ldx, uint16_t* H, int64_t ldh, int n, float tau, hipStream_t s);
+
 hipError_t launch_decompress(const DevFormat& f, uint16_t* W, int64_t ldw, hipStream_t s);
 
 // HBM read-bandwidth calibration: `blocks` workgroups of 256 threads stream `bytes`.

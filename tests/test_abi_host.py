@@ -163,6 +163,7 @@ def test_null_handle_calls_are_rejected():
     assert lib.swm_decompress(None, None, 1, None) == 1
     assert lib.swm_spmm_ws(None, None, 1, None, 1, 1024, None, 0, None) == 1
     assert lib.swm_spmm_workspace_bytes(None, 4096) == 0
+    assert lib.swm_gate_up_silu(None, None, None, 1, None, 1, 1, 0.0, None) == 1
     assert lib.swm_format_destroy(None) == 0
     assert lib.swm_format_validate_blob(None, 0) == 1
 

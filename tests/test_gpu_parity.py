@@ -537,6 +537,112 @@ def test_spmm_ws_errors(gpu_lib):
     torch.cuda.synchronize()
 
 
+# ------------------------------------------------------------------ gated FFN hidden activation (decode)
+def assert_glu_close(H_gpu, H_full, tau, what):
+    """H_gpu: the kernel's fp16 output; H_full: the oracle's H without the
+    threshold (float64).  h is rounded once to fp16, so on top of the 1e-2
+    absolute bound an entry may differ by half an fp16 ulp of its own size
+    (2^-11 |h|, |h| reaches ~30 here): |err| <= 1e-2 + 1e-3 |h|, and the
+    relative Frobenius error stays <= 1e-3.  The threshold decision is taken on
+    the fp16-rounded h on both sides; where the oracle's |h| lies within that
+    error of tau both decisions are valid, so such an entry must be +0 or
+    within the bound; every other entry must take the oracle's decision."""
+    Hg = np.asarray(H_gpu, dtype=np.float64)
+    assert np.all(np.isfinite(Hg)), what
+    tol = 1e-2 + 1e-3 * np.abs(H_full)
+    mag = np.abs(H_full.astype(np.float16).astype(np.float64))
+    band = np.abs(mag - tau) <= tol
+    kept = mag >= tau
+    want = np.where(kept, H_full, 0.0)
+    ok = np.abs(Hg - want) <= tol
+    ok_band = (Hg == 0) | (np.abs(Hg - H_full) <= tol)
+    bad = ~np.where(band, ok_band, ok)
+    assert not bad.any(), f"{what}: {int(bad.sum())} entries off, first at {np.argwhere(bad)[0]}"
+    out = ~band
+    den = float(np.linalg.norm(want[out]))
+    if den > 0:
+        rel = float(np.linalg.norm(Hg[out] - want[out])) / den
+        assert rel <= REL_FRO, f"{what}: rel Frobenius err {rel}"
+    if tau > 0:  # the threshold must have dropped something clear of the band
+        assert np.any((Hg == 0) & ~band & (H_full != 0)), what
+
+
+@pytest.fixture(scope="module")
+def gate_up(gpu_lib):
+    Wg, mg, X = wl.layer_linear(4, 16)
+    Wu, mu, _ = wl.layer_linear(5, 16)
+    fg, fu = gpu_lib.sparse_compress(Wg, mg), gpu_lib.sparse_compress(Wu, mu)
+    full = oracle.gate_up_silu(Wg, mg, Wu, mu, X, 0.0)
+    return Wg, mg, Wu, mu, X, fg, fu, full
+
+
+@pytest.mark.parametrize("N", [1, 4, 16])
+@pytest.mark.parametrize("tau", [0.0, 0.3])
+def test_gate_up_silu_llama_shape(gpu_lib, gate_up, N, tau):
+    """gate/up 11008x4096 at 50%, one launch for both products."""
+    Wg, mg, Wu, mu, X, fg, fu, full = gate_up
+    H = _np(gpu_lib.gate_up_silu(fg, fu, _t(X[:N]), tau))
+    assert_glu_close(H, full[:N], tau, f"gate/up N={N} tau={tau}")
+
+
+@pytest.mark.parametrize("M,K,N,tau", [(1000, 1032, 3, 0.1), (40, 64, 16, 0.0), (300, 8192, 5, 0.2),
+                                       (17, 136, 1, 0.05), (4096, 4096, 8, 0.3)])
+def test_gate_up_silu_ragged(gpu_lib, M, K, N, tau):
+    swm = gpu_lib
+    Wg, mg = wl.pruned_weight(100, M + K, M, K, 0.5)
+    Wu, mu = wl.pruned_weight(100, M + K + 1, M, K, 0.6)
+    X = wl.activations(100, M + N, N, K)
+    H = _np(swm.gate_up_silu(swm.sparse_compress(Wg, mg), swm.sparse_compress(Wu, mu), _t(X), tau))
+    assert_glu_close(H, oracle.gate_up_silu(Wg, mg, Wu, mu, X, 0.0), tau, f"glu {M}x{K} N={N} tau={tau}")
+
+
+def test_gate_up_silu_feeds_skipping_down(gpu_lib, gate_up):
+    """The fused activation, thresholded, drives the skipping down projection:
+    y = W_down H over the channels H keeps (checked with the GPU's own H)."""
+    swm = gpu_lib
+    Wg, mg, Wu, mu, X, fg, fu, full = gate_up
+    Wd, md, _ = wl.layer_linear(6, 1)
+    fd = swm.sparse_compress(Wd, md)
+    fd.enable_skipping()
+    for n in (1, 4):
+        Hd = swm.gate_up_silu(fg, fu, _t(X[:n]), 0.3)
+        y = _np(swm.spmspv(fd, Hd))
+        Hh = _np(Hd)
+        assert (Hh == 0).mean() > 0.3
+        assert_close(y, oracle.masked_matmul_skip(Wd, md, Hh), f"down after glu n={n}")
+
+
+def test_gate_up_silu_errors(gpu_lib):
+    import ctypes
+    import torch
+    swm = gpu_lib
+    lib = swm.load()
+    M, K = 64, 128
+    Wg, mg = wl.pruned_weight(101, 0, M, K, 0.5)
+    fg, fu = swm.sparse_compress(Wg, mg), swm.sparse_compress(Wg, mg)
+    fo = swm.sparse_compress(*wl.pruned_weight(101, 1, M + 16, K, 0.5))
+    X = torch.zeros((16, K + 8), dtype=torch.float16, device="cuda")
+    H = torch.empty((16, M), dtype=torch.float16, device="cuda")
+    xp, hp = ctypes.c_void_p(X.data_ptr()), ctypes.c_void_p(H.data_ptr())
+    s = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    f = lambda a, b, ldx, n, tau, x=xp: lib.swm_gate_up_silu(a, b, x, ldx, hp, M, n, tau, s)
+    assert f(fg._h, fu._h, K, 4, 0.0) == 0
+    assert f(fg._h, fo._h, K, 4, 0.0) == 1               # shapes differ
+    assert f(fg._h, None, K, 4, 0.0) == 1
+    assert f(fg._h, fu._h, K, 0, 0.0) == 1               # n < 1
+    assert f(fg._h, fu._h, K, 17, 0.0) == 1              # n > 16
+    assert f(fg._h, fu._h, K, 4, float("nan")) == 1
+    assert f(fg._h, fu._h, K, 4, -1.0) == 1
+    assert f(fg._h, fu._h, K - 8, 4, 0.0) == 1           # ldx < K
+    assert f(fg._h, fu._h, K + 4, 4, 0.0) == 8           # ldx % 8 != 0
+    assert f(fg._h, fu._h, K, 4, 0.0, ctypes.c_void_p(X.data_ptr() + 2)) == 8  # misaligned X
+    Wb, mb = wl.pruned_weight(101, 2, 32, 8256, 0.5)     # 129 tiles per row
+    fb = swm.sparse_compress(Wb, mb)
+    Xb = torch.zeros((1, 8256), dtype=torch.float16, device="cuda")
+    assert lib.swm_gate_up_silu(fb._h, fb._h, ctypes.c_void_p(Xb.data_ptr()), 8256, hp, 32, 1, 0.0, s) == 8
+    torch.cuda.synchronize()
+
+
 # ------------------------------------------------------------------ wider workloads
 @pytest.mark.parametrize("s", [0.6, 0.7])
 @pytest.mark.parametrize("N", [1, 16])
