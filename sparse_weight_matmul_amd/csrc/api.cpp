@@ -455,7 +455,7 @@ swm_status swm_gate_up_silu(const swm_format* g, const swm_format* u, const void
   if (2 * ((int64_t(n) - 1) * ldx + g->h.k) >= (int64_t(1) << 32)) return SWM_ERR_UNSUPPORTED;
   int dev = 0;
   SWM_HIP(hipGetDevice(&dev));
-  const swm::DecodePlan p = swm::plan_decode_glu(g->h, u->h, num_cus(dev));
+  const swm::DecodePlan p = swm::plan_decode_glu(g->h, u->h, num_cus(dev), n);
   if (p.seq_segs == 0) return SWM_ERR_UNSUPPORTED;
   SWM_HIP(swm::launch_decode_glu(g->d, u->d, p, static_cast<const uint16_t*>(X), ldx, static_cast<uint16_t*>(H), ldh,
                                  n, tau, static_cast<hipStream_t>(stream)));

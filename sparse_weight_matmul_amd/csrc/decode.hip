@@ -965,14 +965,19 @@ hipError_t launch_dense_small(const DensePlan& p, const uint16_t* W, int64_t ldw
   return hipGetLastError();
 }
 
-DecodePlan plan_decode_glu(const Header& g, const Header& u, int num_cus) {
-  // Both formats' tiles in one launch: enough tiles per wave for about one
-  // round of 16 waves per CU, at most 8 waves per format (16 per workgroup)
-  // and at most 16 tiles per wave (the largest straight-line instance).
+DecodePlan plan_decode_glu(const Header& g, const Header& u, int num_cus, int n) {
+  // Both formats' tiles in one launch, at most 8 waves per format (16 per
+  // workgroup) and at most 16 tiles per wave (the largest straight-line
+  // instance).  Up to 8 tokens: as many waves as that allows (measured on
+  // gate/up 11008x4096: 26.3 us at 8 tiles per wave against 28.1 at 16).
+  // More tokens stage 16 activation rows per wave, and 16 such waves fill
+  // a CU's LDS: then enough tiles per wave for about one round of 16 waves
+  // per CU (35.5 us at 16 tiles per wave against 37.0 at 8).
   DecodePlan p;
   const int64_t kt = g.kt;
   const int64_t min_tpw = (kt + 7) / 8;
   int64_t tpw = (2 * int64_t(g.mt) * kt + int64_t(num_cus) * 16 - 1) / (int64_t(num_cus) * 16);
+  if (n <= 8) tpw = min_tpw;
   tpw = std::min<int64_t>(std::max<int64_t>(tpw, min_tpw), 16);
   static const int env_tpw = env_int("SWM_GLU_TPW", 0);
   if (env_tpw > 0) tpw = env_tpw;

@@ -59,7 +59,7 @@ hipError_t launch_spmspv_cr(const DevColRuns& c, const uint16_t* x, int64_t ldx,
 // Gated FFN decode: H = SiLU(W_g X) * (W_u X) with |H| < tau dropped, both
 // formats in one launch of the straight-line kernel (seq_segs == 0: no
 // instance covers the shape).
-DecodePlan plan_decode_glu(const Header& g, const Header& u, int num_cus);
+DecodePlan plan_decode_glu(const Header& g, const Header& u, int num_cus, int n);
 hipError_t launch_decode_glu(const DevFormat& g, const DevFormat& u, const DecodePlan& p, const uint16_t* X,
                              int64_t ldx, uint16_t* H, int64_t ldh, int n, float tau, hipStream_t s);
 
