@@ -800,16 +800,22 @@ int env_int(const char* name, int dflt) {
 }  // namespace
 
 // ------------------------------------------------------------------ host launchers
-DecodePlan plan_decode(const Header& h, const uint32_t* tp, int num_cus) {
+DecodePlan plan_decode(const Header& h, const uint32_t* tp, int num_cus, int waves_per_cu) {
   DecodePlan p;
-  // One workgroup per slab.  Enough tiles per wave that the whole call is one
-  // round of about `wpc` resident waves per CU, and at most 16 waves per
-  // workgroup (SWM_DECODE_WAVES_PER_CU / SWM_DECODE_TPW override for tuning).
-  const int64_t wpc = env_int("SWM_DECODE_WAVES_PER_CU", 16);
+  // One workgroup per slab.  Enough tiles per wave that the whole call is
+  // about `waves_per_cu` waves per CU, and at most 16 waves per workgroup
+  // (SWM_DECODE_WAVES_PER_CU / SWM_DECODE_TPW override for tuning).  When
+  // that leaves more tiles per wave than the straight-line kernel holds, the
+  // looped kernel runs one round of 16 waves per CU (on the 65536x16384
+  // shape, 386 us at N = 16 against 414 us with twice the waves).
   const int64_t tiles = int64_t(h.mt) * h.kt;
-  int64_t tpw = (tiles + int64_t(num_cus) * wpc - 1) / (int64_t(num_cus) * wpc);
   const int64_t min_tpw = (int64_t(h.kt) + 15) / 16;
-  if (tpw < min_tpw) tpw = min_tpw;
+  auto split = [&](int64_t wpc) {
+    const int64_t t = (tiles + int64_t(num_cus) * wpc - 1) / (int64_t(num_cus) * wpc);
+    return t < min_tpw ? min_tpw : t;
+  };
+  int64_t tpw = split(env_int("SWM_DECODE_WAVES_PER_CU", waves_per_cu));
+  if (seq_instance(int((tpw + 1) / 2)) == 0) tpw = split(16);
   if (tpw < 1) tpw = 1;
   tpw = env_int("SWM_DECODE_TPW", int(tpw));
   if (tpw < min_tpw) tpw = min_tpw;

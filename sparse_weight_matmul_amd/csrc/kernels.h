@@ -28,9 +28,10 @@ struct DecodePlan {
   int seq_chunks = 1;      // 1 KiB loads per two-tile segment
 };
 
-// Work split of the decode kernel; `tile_ptr` (host, mt*kt+1 entries) sizes
-// the segment loads.
-DecodePlan plan_decode(const Header& h, const uint32_t* tile_ptr, int num_cus);
+// Work split of the decode kernel for about `waves_per_cu` waves per CU (at
+// least one wave per 16 tiles of a slab row); `tile_ptr` (host, mt*kt+1
+// entries) sizes the segment loads.
+DecodePlan plan_decode(const Header& h, const uint32_t* tile_ptr, int num_cus, int waves_per_cu);
 
 hipError_t launch_decode(const DevFormat& f, const DecodePlan& p, const uint16_t* X, int64_t ldx,
                          uint16_t* Y, int64_t ldy, int n, bool skip, hipStream_t s);
