@@ -612,6 +612,73 @@ def test_gate_up_silu_feeds_skipping_down(gpu_lib, gate_up):
         assert_close(y, oracle.masked_matmul_skip(Wd, md, Hh), f"down after glu n={n}")
 
 
+def test_gate_up_silu_chain_graph_replays(gpu_lib, gate_up):
+    """The fused FFN step and the skipping down product captured in one HIP
+    graph: every replay, with new activations and eager calls in between,
+    equals the eager chain bit for bit."""
+    import torch
+    swm = gpu_lib
+    Wg, mg, Wu, mu, X, fg, fu, full = gate_up
+    Wd, md, _ = wl.layer_linear(6, 1)
+    fd = swm.sparse_compress(Wd, md)
+    fd.enable_skipping()
+    n, tau = 2, 0.3
+    xb = _t(X[:n])
+    hb = torch.empty((n, Wg.shape[0]), dtype=torch.float16, device="cuda")
+    yb = torch.empty((n, Wd.shape[0]), dtype=torch.float16, device="cuda")
+    swm.gate_up_silu(fg, fu, xb, tau, hb)
+    swm.spmspv(fd, hb, yb)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        swm.gate_up_silu(fg, fu, xb, tau, hb)
+        swm.spmspv(fd, hb, yb)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(12)
+    for rep in range(3):
+        xr = (X[:n].astype(np.float32) * (0.5 + rng.random(X.shape[1]))).astype(np.float16)
+        xb.copy_(_t(xr))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        h_graph, y_graph = hb.cpu().numpy().copy(), yb.cpu().numpy().copy()
+        h_eager = swm.gate_up_silu(fg, fu, _t(xr), tau)
+        y_eager = _np(swm.spmspv(fd, h_eager))
+        assert np.array_equal(h_graph.view(np.uint16), _np(h_eager).view(np.uint16)), f"replay {rep}"
+        assert np.array_equal(y_graph.view(np.uint16), y_eager.view(np.uint16)), f"replay {rep}"
+    assert_glu_close(h_graph, oracle.gate_up_silu(Wg, mg, Wu, mu, xr, 0.0), tau, "graph replay")
+
+
+def test_spmm_ws_graph_replays(gpu_lib):
+    """Expansion and dense product captured in one graph; replays with new
+    activations equal eager calls bit for bit."""
+    import torch
+    swm = gpu_lib
+    M, K, N = 520, 392, 1100
+    W, mask = wl.pruned_weight(102, 0, M, K, 0.5)
+    f = _compress(swm, W, mask)
+    ws, _ = _workspace(swm, f, N)
+    xb = torch.empty((N, K), dtype=torch.float16, device="cuda")
+    yb = torch.empty((N, M), dtype=torch.float16, device="cuda")
+    xb.copy_(_t(wl.activations(102, 0, N, K)))
+    swm.spmm_ws(f, xb, ws, yb)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        swm.spmm_ws(f, xb, ws, yb)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        X = wl.activations(102, rep + 1, N, K)
+        xb.copy_(_t(X))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        y_graph = yb.cpu().numpy().copy()
+        y_eager = _np(swm.spmm_ws(f, _t(X), ws))
+        assert np.array_equal(y_graph.view(np.uint16), y_eager.view(np.uint16)), f"replay {rep}"
+        assert_close(y_graph, oracle.masked_matmul(W, mask, X), f"replay {rep}")
+
+
 def test_gate_up_silu_errors(gpu_lib):
     import ctypes
     import torch
