@@ -166,11 +166,13 @@ swm_status swm_decompress(const swm_format* f, void* W_dev, int64_t ldw, void* s
 swm_status swm_spmm(const swm_format* f, const void* X, int64_t ldx, void* Y, int64_t ldy,
                     int64_t N, void* stream);
 
-/* Bytes of device workspace swm_spmm_ws uses for N tokens: M*K*2 rounded up
- * to 256 when N reaches the expansion threshold (1024 tokens; the
- * SWM_EXPAND_MIN_N environment variable, read once per process, changes it;
- * values below 33 count as 33)
- * and K is a multiple of 8, else 0.  NULL handle -> 0.  No device work. */
+/* Bytes of device workspace swm_spmm_ws uses for N tokens on the current
+ * device: M*K*2 rounded up to 256 when that call would expand W (K a
+ * multiple of 8, and N >= 1024, or N >= 256 with the on-chip prefill
+ * kernel's ceil(M/128)*ceil(N/256) blocks at most half the CUs or above one
+ * round of them), else 0.  The SWM_EXPAND_MIN_N environment variable, read
+ * once per process, replaces the rule by N >= its value (values below 33
+ * count as 33).  NULL handle -> 0.  Queries the device's CU count only. */
 size_t swm_spmm_workspace_bytes(const swm_format* f, int64_t N);
 
 /* spmm_ws: swm_spmm with a caller-owned device workspace; same operation,

@@ -383,22 +383,36 @@ swm_status swm_spmm(const swm_format* f, const void* X, int64_t ldx, void* Y, in
   return run_products(f, X, ldx, Y, ldy, N, false, static_cast<hipStream_t>(stream));
 }
 
-// Tokens from which swm_spmm_ws expands W once into the workspace and runs the
-// dense MFMA kernel (SWM_EXPAND_MIN_N overrides it, read once per process; at
-// least 33: from there swm_spmm's own prefill kernel sums each output in the
-// same order as the dense kernel, so moving the threshold does not change
-// the bits of a result).
+// When swm_spmm_ws expands W once into the workspace and runs the dense MFMA
+// kernel instead of the on-chip prefill kernel (128 x 256 blocks): from 1024
+// tokens, and from 256 tokens when the on-chip kernel's blocks would leave
+// at least half of the CUs idle or spill into a second round, where the
+// dense kernel's block choice fits the chip better (measured at N = 256-1024:
+// q_proj 4096x4096 71 against 80 us, down 4096x11008 168 against 200 us,
+// up 11008x4096 at N = 640 107 against 162 us).  SWM_EXPAND_MIN_N replaces
+// the rule by a plain token threshold (read once per process; at least 33:
+// from there swm_spmm's own prefill kernel sums each output in the same
+// order as the dense kernel, so the route does not change the bits of a
+// result).
 static int64_t expand_min_n() {
   static const int64_t v = [] {
     const char* e = getenv("SWM_EXPAND_MIN_N");
     const long long n = e ? atoll(e) : 0;
-    return n > 0 ? std::max<int64_t>(int64_t(n), 33) : int64_t(1024);
+    return n > 0 ? std::max<int64_t>(int64_t(n), 33) : int64_t(0);
   }();
   return v;
 }
 
 static bool expand_route(const swm::Header& h, int64_t N) {
-  return N >= expand_min_n() && h.k >= 8 && h.k % 8 == 0 && h.m > 0;
+  if (!(h.k >= 8 && h.k % 8 == 0 && h.m > 0)) return false;
+  if (expand_min_n() > 0) return N >= expand_min_n();
+  if (N >= 1024) return true;
+  if (N < 256) return false;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return false;
+  const int64_t cus = num_cus(dev);
+  const int64_t blocks = ((h.m + 127) / 128) * ((N + 255) / 256);
+  return 2 * blocks <= cus || blocks > cus;
 }
 
 size_t swm_spmm_workspace_bytes(const swm_format* f, int64_t N) {
@@ -421,8 +435,10 @@ swm_status swm_spmm_ws(const swm_format* f, const void* X, int64_t ldx, void* Y,
   if (!on_current_device(f)) return SWM_ERR_INVALID_ARG;
   uint16_t* w = static_cast<uint16_t*>(workspace);
   SWM_HIP(swm::launch_decompress(f->d, w, f->h.k, s));
+  int dev = 0;
+  SWM_HIP(hipGetDevice(&dev));
   SWM_HIP(swm::launch_prefill_dense(w, f->h.k, static_cast<const uint16_t*>(X), ldx, static_cast<uint16_t*>(Y),
-                                    ldy, f->h.m, f->h.k, N, s));
+                                    ldy, f->h.m, f->h.k, N, num_cus(dev), s));
   return SWM_OK;
 }
 
@@ -497,7 +513,7 @@ swm_status swm_dense_gemm(const void* W, int64_t ldw, const void* X, int64_t ldx
   if (N > 16 && !small_tiled && swm::prefill_supported(K, ldx, X) && ldw % 8 == 0 &&
       (reinterpret_cast<uintptr_t>(W) & 15) == 0) {
     SWM_HIP(swm::launch_prefill_dense(static_cast<const uint16_t*>(W), ldw, static_cast<const uint16_t*>(X),
-                                      ldx, static_cast<uint16_t*>(Y), ldy, M, K, N, s));
+                                      ldx, static_cast<uint16_t*>(Y), ldy, M, K, N, num_cus(dev), s));
     return SWM_OK;
   }
   const auto p = swm::plan_dense_small(M, K, int(std::min<int64_t>(N, 16)), num_cus(dev));

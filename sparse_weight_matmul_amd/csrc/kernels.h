@@ -82,7 +82,7 @@ hipError_t launch_dense_small(const DensePlan& p, const uint16_t* W, int64_t ldw
 
 // Tiled MFMA GEMM for larger N: dense W, or W expanded from the format tile by tile.
 hipError_t launch_prefill_dense(const uint16_t* W, int64_t ldw, const uint16_t* X, int64_t ldx,
-                                uint16_t* Y, int64_t ldy, int64_t M, int64_t K, int64_t N,
+                                uint16_t* Y, int64_t ldy, int64_t M, int64_t K, int64_t N, int num_cus,
                                 hipStream_t s);
 hipError_t launch_prefill_sparse(const DevFormat& f, const uint16_t* X, int64_t ldx, uint16_t* Y,
                                  int64_t ldy, int64_t N, hipStream_t s);

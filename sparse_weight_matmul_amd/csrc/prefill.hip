@@ -557,21 +557,32 @@ hipError_t launch_dense(PrefillArgs a, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_prefill_dense(const uint16_t* W, int64_t ldw, const uint16_t* X, int64_t ldx,
-                                uint16_t* Y, int64_t ldy, int64_t M, int64_t K, int64_t N,
+                                uint16_t* Y, int64_t ldy, int64_t M, int64_t K, int64_t N, int num_cus,
                                 hipStream_t s) {
   PrefillArgs a = make_args(M, N, K, X, ldx, Y, ldy);
   a.W = W;
   a.ldw = ldw;
   if (a.tiles_m == 0 || a.tiles_n == 0) return hipSuccess;
   if (K < 8 || K % 8 != 0) return hipErrorInvalidValue;
-  // Block shape: the largest of 256 x 256, 256 x 128, 128 x 128 that gives at
-  // least 60% of the CUs a block (measured on the layer shapes, N = 64-4096:
-  // a larger block on fewer CUs beats a smaller one that needs a second
-  // round); SWM_DENSE_BLOCK = 1 / 2 / 3 forces one.
-  const int64_t b256 = ((M + 255) / 256) * ((N + 255) / 256);
-  const int64_t b128 = ((M + 255) / 256) * ((N + 127) / 128);
-  const int64_t enough = 154;  // 0.6 x 256 CUs
-  int shape = b256 >= enough ? 1 : b128 >= enough ? 2 : 3;
+  // Block shape 256 x 256, 256 x 128 or 128 x 128: the one with the fewest
+  // rounds of blocks over the CUs, each round weighted by its block's
+  // measured time relative to 256 x 256 (1, 0.73, 0.54 on up/gate
+  // 11008x4096).  A shape whose blocks spill a few past one round loses to a
+  // larger one (N = 768: 258 blocks of 256 x 128 took 153 us, 129 of
+  // 256 x 256 109 us).  SWM_DENSE_BLOCK = 1 / 2 / 3 forces one.
+  const int64_t cus = num_cus > 0 ? num_cus : 256;
+  const int64_t mb = (M + 255) / 256, mb128 = (M + 127) / 128;
+  const int64_t blocks[3] = {mb * ((N + 255) / 256), mb * ((N + 127) / 128), mb128 * ((N + 127) / 128)};
+  const double weight[3] = {1.0, 0.73, 0.54};
+  int shape = 1;
+  double best = 0.0;
+  for (int i = 0; i < 3; ++i) {
+    const double cost = double((blocks[i] + cus - 1) / cus) * weight[i];
+    if (i == 0 || cost < best) {
+      best = cost;
+      shape = i + 1;
+    }
+  }
   if (const char* e = getenv("SWM_DENSE_BLOCK")) {
     if (*e >= '1' && *e <= '3') shape = *e - '0';
   }

@@ -485,17 +485,33 @@ def test_spmm_ws_upgate_n4096_sampled_rows(gpu_lib):
     assert np.array_equal(Yo.view(np.uint16), Y.view(np.uint16))
 
 
+def test_spmm_ws_route_rule(gpu_lib):
+    """The expansion route: always from 1024 tokens; from 256 when the on-chip
+    kernel's ceil(M/128)*ceil(N/256) blocks fill at most half of the 256 CUs or
+    spill past one round; never below 256."""
+    swm = gpu_lib
+    Ws, ms = wl.pruned_weight(99, 3, 300, 64, 0.5)     # 3 row blocks: always under-filled
+    Wb, mb = wl.pruned_weight(99, 4, 11008, 64, 0.5)   # 86 row blocks
+    fs, fb = swm.sparse_compress(Ws, ms), swm.sparse_compress(Wb, mb)
+    need_s, need_b = (2 * 300 * 64 + 255) // 256 * 256, (2 * 11008 * 64 + 255) // 256 * 256
+    assert [swm.spmm_workspace_bytes(fs, n) for n in (33, 255, 256, 700, 1024)] == [0, 0, need_s, need_s, need_s]
+    # 86 blocks (N = 256): at most half; 172 (N = 512): on chip; 258 (N = 640): a second round
+    assert [swm.spmm_workspace_bytes(fb, n) for n in (255, 256, 512, 640, 1024, 4096)] == \
+        [0, need_b, 0, need_b, need_b, need_b]
+
+
 def test_spmm_ws_below_threshold_and_fallbacks(gpu_lib):
-    """Below the threshold, without a workspace, or with unaligned X the call
-    runs spmm's kernels (identical bits) and leaves the workspace untouched."""
+    """Below the route's threshold, without a workspace, or with unaligned X
+    the call runs spmm's kernels (identical bits) and leaves the workspace
+    untouched."""
     import torch
     swm = gpu_lib
     M, K = 300, 512
     W, mask = wl.pruned_weight(99, 0, M, K, 0.5)
     f = _compress(swm, W, mask)
-    assert swm.spmm_workspace_bytes(f, 1023) == 0
+    assert swm.spmm_workspace_bytes(f, 255) == 0
     assert swm.spmm_workspace_bytes(f, 1024) == (2 * M * K + 255) // 256 * 256
-    for N in (16, 300, 1023):
+    for N in (16, 100, 255):
         X = _t(np.random.default_rng(N).standard_normal((N, K)).astype(np.float16))
         ws = torch.full((4096,), 0xA5, dtype=torch.uint8, device="cuda")
         a = _np(swm.spmm_ws(f, X, ws)).view(np.uint16)
