@@ -196,8 +196,9 @@ size_t swm_spmm_workspace_bytes(const swm_format* f, int64_t N);
 swm_status swm_spmm_ws(const swm_format* f, const void* X, int64_t ldx, void* Y, int64_t ldy, int64_t N,
                        void* workspace, size_t ws_bytes, void* stream);
 
-/* gate_up_silu: the hidden activation of a gated FFN block for 1 <= n <= 16
- * decode tokens, H = SiLU(X W_g^T) (.) (X W_u^T), with the input-adaptive
+/* gate_up_silu: the hidden activation of a gated FFN block for 1 <= n <= 32
+ * decode tokens (17-32 tokens run as two launches of at most 16, each
+ * reading the weights once), H = SiLU(X W_g^T) (.) (X W_u^T), with the input-adaptive
  * threshold applied: an entry whose magnitude (after rounding to fp16) is
  * below tau is stored as +0.  Source: "Reduced Matrix Multiplication" blog
  * page, Sec. 3.2 (SiLU leaves many hidden channels near zero) and Secs.
@@ -210,7 +211,7 @@ swm_status swm_spmm_ws(const swm_format* f, const void* X, int64_t ldx, void* Y,
  *  g, u: handles of the gate and up weights, same M and K.  X: DEVICE fp16
  *  token-major n x K (ldx >= K).  H: DEVICE fp16 n x M (ldh >= M),
  *  overwritten.  tau: 0 <= tau <= 65504 (0 keeps every entry).
- *  SWM_ERR_INVALID_ARG: NULL pointers, n outside 1..16, tau outside its
+ *  SWM_ERR_INVALID_ARG: NULL pointers, n outside 1..32, tau outside its
  *  range or NaN, shapes that differ, leading dimensions too small, a handle
  *  on another device.  SWM_ERR_UNSUPPORTED: X not 16-byte aligned or ldx % 8
  *  != 0 or K % 8 != 0, n*ldx beyond 32-bit byte offsets, tiles other than

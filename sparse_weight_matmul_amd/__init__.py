@@ -308,7 +308,7 @@ def spmm_ws(fmt: Format, X, workspace, Y=None, stream=None):
 
 
 def gate_up_silu(gate: Format, up: Format, X, tau: float = 0.0, H=None, stream=None):
-    """Gated FFN hidden activation for 1..16 decode tokens: H (n, M) =
+    """Gated FFN hidden activation for 1..32 decode tokens: H (n, M) =
     SiLU(X @ W_g.T) * (X @ W_u.T), entries with |H| < tau stored as +0."""
     lib = load()
     n = X.shape[0]

@@ -468,7 +468,7 @@ swm_status swm_spmspv_threshold(const swm_format* f, const void* x, int64_t ldx,
 swm_status swm_gate_up_silu(const swm_format* g, const swm_format* u, const void* X, int64_t ldx, void* H,
                             int64_t ldh, int32_t n, float tau, void* stream) {
   if (!g || !u || !X || !H) return SWM_ERR_INVALID_ARG;
-  if (n < 1 || n > 16 || !(tau >= 0.f) || !(tau <= 65504.f)) return SWM_ERR_INVALID_ARG;
+  if (n < 1 || n > 32 || !(tau >= 0.f) || !(tau <= 65504.f)) return SWM_ERR_INVALID_ARG;
   if (g->h.m != u->h.m || g->h.k != u->h.k) return SWM_ERR_INVALID_ARG;
   if (ldx < g->h.k || ldh < g->h.m || ldx <= 0 || ldh <= 0) return SWM_ERR_INVALID_ARG;
   swm_status st = check_tile_supported(g->h);
@@ -479,10 +479,17 @@ swm_status swm_gate_up_silu(const swm_format* g, const swm_format* u, const void
   if (2 * ((int64_t(n) - 1) * ldx + g->h.k) >= (int64_t(1) << 32)) return SWM_ERR_UNSUPPORTED;
   int dev = 0;
   SWM_HIP(hipGetDevice(&dev));
-  const swm::DecodePlan p = swm::plan_decode_glu(g->h, u->h, num_cus(dev), n);
-  if (p.seq_segs == 0) return SWM_ERR_UNSUPPORTED;
-  SWM_HIP(swm::launch_decode_glu(g->d, u->d, p, static_cast<const uint16_t*>(X), ldx, static_cast<uint16_t*>(H), ldh,
-                                 n, tau, static_cast<hipStream_t>(stream)));
+  // Up to 16 tokens per launch (the straight-line kernel stages at most 16
+  // activation rows per wave); 17-32 tokens take two launches.
+  const int n0 = std::min(n, 16);
+  const swm::DecodePlan p0 = swm::plan_decode_glu(g->h, u->h, num_cus(dev), n0);
+  const swm::DecodePlan p1 = swm::plan_decode_glu(g->h, u->h, num_cus(dev), std::max(n - 16, 1));
+  if (p0.seq_segs == 0 || p1.seq_segs == 0) return SWM_ERR_UNSUPPORTED;
+  const uint16_t* x = static_cast<const uint16_t*>(X);
+  uint16_t* h = static_cast<uint16_t*>(H);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  SWM_HIP(swm::launch_decode_glu(g->d, u->d, p0, x, ldx, h, ldh, n0, tau, s));
+  if (n > 16) SWM_HIP(swm::launch_decode_glu(g->d, u->d, p1, x + 16 * ldx, ldx, h + 16 * ldh, ldh, n - 16, tau, s));
   return SWM_OK;
 }
 

@@ -585,14 +585,14 @@ def assert_glu_close(H_gpu, H_full, tau, what):
 
 @pytest.fixture(scope="module")
 def gate_up(gpu_lib):
-    Wg, mg, X = wl.layer_linear(4, 16)
-    Wu, mu, _ = wl.layer_linear(5, 16)
+    Wg, mg, X = wl.layer_linear(4, 32)
+    Wu, mu, _ = wl.layer_linear(5, 32)
     fg, fu = gpu_lib.sparse_compress(Wg, mg), gpu_lib.sparse_compress(Wu, mu)
     full = oracle.gate_up_silu(Wg, mg, Wu, mu, X, 0.0)
     return Wg, mg, Wu, mu, X, fg, fu, full
 
 
-@pytest.mark.parametrize("N", [1, 4, 16])
+@pytest.mark.parametrize("N", [1, 4, 16, 24])
 @pytest.mark.parametrize("tau", [0.0, 0.3])
 def test_gate_up_silu_llama_shape(gpu_lib, gate_up, N, tau):
     """gate/up 11008x4096 at 50%, one launch for both products."""
@@ -602,7 +602,7 @@ def test_gate_up_silu_llama_shape(gpu_lib, gate_up, N, tau):
 
 
 @pytest.mark.parametrize("M,K,N,tau", [(1000, 1032, 3, 0.1), (40, 64, 16, 0.0), (300, 8192, 5, 0.2),
-                                       (17, 136, 1, 0.05), (4096, 4096, 8, 0.3)])
+                                       (17, 136, 1, 0.05), (4096, 4096, 8, 0.3), (520, 392, 31, 0.1)])
 def test_gate_up_silu_ragged(gpu_lib, M, K, N, tau):
     swm = gpu_lib
     Wg, mg = wl.pruned_weight(100, M + K, M, K, 0.5)
@@ -713,7 +713,7 @@ def test_gate_up_silu_errors(gpu_lib):
     assert f(fg._h, fo._h, K, 4, 0.0) == 1               # shapes differ
     assert f(fg._h, None, K, 4, 0.0) == 1
     assert f(fg._h, fu._h, K, 0, 0.0) == 1               # n < 1
-    assert f(fg._h, fu._h, K, 17, 0.0) == 1              # n > 16
+    assert f(fg._h, fu._h, K, 33, 0.0) == 1              # n > 32
     assert f(fg._h, fu._h, K, 4, float("nan")) == 1
     assert f(fg._h, fu._h, K, 4, -1.0) == 1
     assert f(fg._h, fu._h, K - 8, 4, 0.0) == 1           # ldx < K
