@@ -21,7 +21,8 @@ struct swm_format {
   void* dev_mem = nullptr;     // one allocation for every device section
   swm::DevFormat d;
   swm::DecodePlan plan;       // decode split for N <= 8
-  swm::DecodePlan plan_wide;  // and for 8 < N <= 32
+  swm::DecodePlan plan_wide;  // 8 < N <= 16
+  swm::DecodePlan plan_pair;  // 16 < N <= 32 (two token groups, looped kernel)
   void* cr_mem = nullptr;  // column-run encoding for activation skipping (optional)
   swm::DevColRuns cr;
 };
@@ -100,8 +101,9 @@ swm_status upload(std::vector<uint8_t>&& blob, const swm::Header& h, hipStream_t
   // and about 32 waves per CU is best (up at N = 16: 19.3 against 20.2).
   // Shapes whose slabs are short (q_proj, down) get the same split from both.
   const uint32_t* tp = reinterpret_cast<const uint32_t*>(f->blob.data() + h.off_tile_ptr());
-  f->plan = swm::plan_decode(h, tp, num_cus(f->device), 64);
-  f->plan_wide = swm::plan_decode(h, tp, num_cus(f->device), 32);
+  f->plan = swm::plan_decode(h, tp, num_cus(f->device), 64, true);
+  f->plan_wide = swm::plan_decode(h, tp, num_cus(f->device), 32, true);
+  f->plan_pair = swm::plan_decode(h, tp, num_cus(f->device), 32, false);
   const size_t T = h.tiles();
   const size_t b_tp = 4 * (T + 1), b_bits = 8 * h.n_bits(), b_vals = 2 * h.padded_len + 1024;
   const size_t n_zero = size_t(h.kt) * h.tk + 64;
@@ -347,6 +349,10 @@ swm_status swm_decompress(const swm_format* f, void* W_dev, int64_t ldw, void* s
   return SWM_OK;
 }
 
+static const swm::DecodePlan& decode_plan(const swm_format* f, int64_t n) {
+  return n <= 8 ? f->plan : n <= 16 ? f->plan_wide : f->plan_pair;
+}
+
 static swm_status run_products(const swm_format* f, const void* X, int64_t ldx, void* Y, int64_t ldy,
                                int64_t N, bool skip, hipStream_t s) {
   if (!f || !X || !Y) return SWM_ERR_INVALID_ARG;
@@ -359,7 +365,7 @@ static swm_status run_products(const swm_format* f, const void* X, int64_t ldx, 
   // N <= 32 is memory bound (the weights are read once per call): the decode
   // kernels, with one or two 16-token groups per decoded operand.
   if (N <= 16 || (N <= 32 && !skip)) {
-    SWM_HIP(swm::launch_decode(f->d, N <= 8 ? f->plan : f->plan_wide, x, ldx, y, ldy, int(N), skip, s));
+    SWM_HIP(swm::launch_decode(f->d, decode_plan(f, N), x, ldx, y, ldy, int(N), skip, s));
     return SWM_OK;
   }
   if (!skip && swm::prefill_supported(f->h.k, ldx, X) && swm::prefill_sparse_lds(f->h) <= 160 * 1024 &&
@@ -372,8 +378,7 @@ static swm_status run_products(const swm_format* f, const void* X, int64_t ldx, 
   const int64_t slice = skip ? 16 : 32;
   for (int64_t n0 = 0; n0 < N; n0 += slice) {
     const int nn = int(std::min<int64_t>(slice, N - n0));
-    SWM_HIP(swm::launch_decode(f->d, nn <= 8 ? f->plan : f->plan_wide, x + n0 * ldx, ldx, y + n0 * ldy, ldy, nn,
-                               skip, s));
+    SWM_HIP(swm::launch_decode(f->d, decode_plan(f, nn), x + n0 * ldx, ldx, y + n0 * ldy, ldy, nn, skip, s));
   }
   return SWM_OK;
 }

@@ -800,14 +800,19 @@ int env_int(const char* name, int dflt) {
 }  // namespace
 
 // ------------------------------------------------------------------ host launchers
-DecodePlan plan_decode(const Header& h, const uint32_t* tp, int num_cus, int waves_per_cu) {
+DecodePlan plan_decode(const Header& h, const uint32_t* tp, int num_cus, int waves_per_cu, bool straight_line) {
   DecodePlan p;
   // One workgroup per slab.  Enough tiles per wave that the whole call is
   // about `waves_per_cu` waves per CU, and at most 16 waves per workgroup
   // (SWM_DECODE_WAVES_PER_CU / SWM_DECODE_TPW override for tuning).  When
-  // that leaves more tiles per wave than the straight-line kernel holds, the
-  // looped kernel runs one round of 16 waves per CU (on the 65536x16384
-  // shape, 386 us at N = 16 against 414 us with twice the waves).
+  // that leaves more tiles per wave than the straight-line kernel holds, it
+  // runs with its largest instance (16 tiles per wave) if a slab row fits 16
+  // such waves and the split is for token counts it serves (on the
+  // 65536x16384 shape: 339 / 363 us at N = 1 / 16 against 368 / 373 us for
+  // one round of 16 waves per CU of the looped kernel, and 414 us at N = 16
+  // for 128 tiles per wave); else the looped kernel runs one round of 16
+  // waves per CU (at N = 32 on that shape: 581 us, against 666 us with 16
+  // tiles per wave).
   const int64_t tiles = int64_t(h.mt) * h.kt;
   const int64_t min_tpw = (int64_t(h.kt) + 15) / 16;
   auto split = [&](int64_t wpc) {
@@ -815,7 +820,7 @@ DecodePlan plan_decode(const Header& h, const uint32_t* tp, int num_cus, int wav
     return t < min_tpw ? min_tpw : t;
   };
   int64_t tpw = split(env_int("SWM_DECODE_WAVES_PER_CU", waves_per_cu));
-  if (seq_instance(int((tpw + 1) / 2)) == 0) tpw = split(16);
+  if (seq_instance(int((tpw + 1) / 2)) == 0) tpw = straight_line && min_tpw <= 16 ? 16 : split(16);
   if (tpw < 1) tpw = 1;
   tpw = env_int("SWM_DECODE_TPW", int(tpw));
   if (tpw < min_tpw) tpw = min_tpw;

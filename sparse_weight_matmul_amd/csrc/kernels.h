@@ -29,9 +29,10 @@ struct DecodePlan {
 };
 
 // Work split of the decode kernel for about `waves_per_cu` waves per CU (at
-// least one wave per 16 tiles of a slab row); `tile_ptr` (host, mt*kt+1
-// entries) sizes the segment loads.
-DecodePlan plan_decode(const Header& h, const uint32_t* tile_ptr, int num_cus, int waves_per_cu);
+// least one wave per 16 tiles of a slab row); `straight_line`: the split is
+// for token counts the straight-line kernel serves (N <= 16).  `tile_ptr`
+// (host, mt*kt+1 entries) sizes the segment loads.
+DecodePlan plan_decode(const Header& h, const uint32_t* tile_ptr, int num_cus, int waves_per_cu, bool straight_line);
 
 hipError_t launch_decode(const DevFormat& f, const DecodePlan& p, const uint16_t* X, int64_t ldx,
                          uint16_t* Y, int64_t ldy, int n, bool skip, hipStream_t s);
