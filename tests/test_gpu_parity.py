@@ -612,6 +612,25 @@ def test_gate_up_silu_ragged(gpu_lib, M, K, N, tau):
     assert_glu_close(H, oracle.gate_up_silu(Wg, mg, Wu, mu, X, 0.0), tau, f"glu {M}x{K} N={N} tau={tau}")
 
 
+def test_gate_up_silu_degenerate_cases(gpu_lib):
+    """Zero activations give exact +0; the largest tau drops every entry; the
+    same handle as gate and up gives SiLU(g) * g; an all-pruned gate gives
+    SiLU(0) * u = 0."""
+    swm = gpu_lib
+    M, K = 520, 392
+    Wg, mg = wl.pruned_weight(103, 0, M, K, 0.5)
+    Wu, mu = wl.pruned_weight(103, 1, M, K, 0.5)
+    fg, fu = swm.sparse_compress(Wg, mg), swm.sparse_compress(Wu, mu)
+    X = wl.activations(103, 0, 5, K)
+    Z = np.zeros((5, K), dtype=np.float16)
+    assert np.all(_np(swm.gate_up_silu(fg, fu, _t(Z), 0.0)).view(np.uint16) == 0)
+    assert np.all(_np(swm.gate_up_silu(fg, fu, _t(X), 65504.0)).view(np.uint16) == 0)
+    H = _np(swm.gate_up_silu(fg, fg, _t(X), 0.0))
+    assert_glu_close(H, oracle.gate_up_silu(Wg, mg, Wg, mg, X, 0.0), 0.0, "gate == up")
+    f0 = swm.sparse_compress(Wg, np.zeros_like(mg))
+    assert np.all(_np(swm.gate_up_silu(f0, fu, _t(X), 0.0)) == 0)
+
+
 def test_gate_up_silu_feeds_skipping_down(gpu_lib, gate_up):
     """The fused activation, thresholded, drives the skipping down projection:
     y = W_down H over the channels H keeps (checked with the GPU's own H)."""
