@@ -471,6 +471,30 @@ def test_spmm_ws_expand_route(gpu_lib, M, K, N):
     assert np.array_equal(got, np.where(mask, W.view(np.uint16), np.uint16(0)))
 
 
+def test_spmm_ws_degenerate_cases(gpu_lib):
+    """Through the expansion route: an all-pruned W and zero activations give
+    exact +0; a single kept entry per row gives that entry times x."""
+    import torch
+    swm = gpu_lib
+    M, K, N = 100, 200, 1024
+    W, _ = wl.pruned_weight(104, 0, M, K, 0.5)
+    X = wl.activations(104, 0, N, K)
+    f0 = swm.sparse_compress(W, np.zeros((M, K), dtype=bool))
+    ws, nb = _workspace(swm, f0, N)
+    assert nb > 0
+    assert np.all(_np(swm.spmm_ws(f0, _t(X), ws)).view(np.uint16) == 0)
+    f = swm.sparse_compress(W, np.ones((M, K), dtype=bool))
+    assert np.all(_np(swm.spmm_ws(f, _t(np.zeros((N, K), dtype=np.float16)), ws)).view(np.uint16) == 0)
+    one = np.zeros((M, K), dtype=bool)
+    cols = np.arange(M) % K
+    one[np.arange(M), cols] = True
+    f1 = swm.sparse_compress(W, one)
+    Y = _np(swm.spmm_ws(f1, _t(X), ws))
+    want = (X[:, cols].astype(np.float32) * W[np.arange(M), cols].astype(np.float32)).astype(np.float16)
+    # exact values; a zero product may carry either sign (the accumulator starts at +0)
+    assert np.array_equal(Y.astype(np.float32), want.astype(np.float32))
+
+
 def test_spmm_ws_upgate_n4096_sampled_rows(gpu_lib):
     """The benchmarked prefill shape through the workspace route."""
     swm = gpu_lib
