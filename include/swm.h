@@ -49,7 +49,8 @@
  *    (decode tiles per wave / waves per CU, read when a handle is created),
  *    SWM_DENSE_WAVES_PER_CU (streaming dense kernel), SWM_DENSE_BLOCK = 1 / 2
  *    / 3 (tiled dense block 256x256 / 256x128 / 128x128), SWM_EXPAND_MIN_N
- *    (tokens from which swm_spmm_ws expands W, at least 33; read once).
+ *    (tokens from which swm_spmm_ws expands W, at least 33; read once),
+ *    SWM_GLU_TPW (tiles per wave of swm_gate_up_silu; read once).
  */
 #ifndef SWM_H_
 #define SWM_H_
