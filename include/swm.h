@@ -43,8 +43,9 @@
  *    partial-sum workspace; skipping calls on one handle share that workspace
  *    and must be ordered on one stream.  Other product calls on one handle may
  *    run concurrently.
- *  - Environment variables, for tuning and measurement only (results do not
- *    depend on them; the defaults are the measured best): SWM_DECODE_LOOP
+ *  - Environment variables, for tuning and measurement only (they change the
+ *    work split, so a result can change only in its fp32 summation order;
+ *    the defaults are the measured best): SWM_DECODE_LOOP
  *    (use the looped decode kernel), SWM_DECODE_TPW / SWM_DECODE_WAVES_PER_CU
  *    (decode tiles per wave / waves per CU, read when a handle is created),
  *    SWM_DENSE_WAVES_PER_CU (streaming dense kernel), SWM_DENSE_BLOCK = 1 / 2
