@@ -513,15 +513,22 @@ def test_spmm_ws_route_rule(gpu_lib):
     """The expansion route: always from 1024 tokens; from 256 when the on-chip
     kernel's ceil(M/128)*ceil(N/256) blocks fill at most half of the 256 CUs or
     spill past one round; never below 256."""
+    import torch
     swm = gpu_lib
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
     Ws, ms = wl.pruned_weight(99, 3, 300, 64, 0.5)     # 3 row blocks: always under-filled
     Wb, mb = wl.pruned_weight(99, 4, 11008, 64, 0.5)   # 86 row blocks
     fs, fb = swm.sparse_compress(Ws, ms), swm.sparse_compress(Wb, mb)
     need_s, need_b = (2 * 300 * 64 + 255) // 256 * 256, (2 * 11008 * 64 + 255) // 256 * 256
     assert [swm.spmm_workspace_bytes(fs, n) for n in (33, 255, 256, 700, 1024)] == [0, 0, need_s, need_s, need_s]
-    # 86 blocks (N = 256): at most half; 172 (N = 512): on chip; 258 (N = 640): a second round
-    assert [swm.spmm_workspace_bytes(fb, n) for n in (255, 256, 512, 640, 1024, 4096)] == \
-        [0, need_b, 0, need_b, need_b, need_b]
+
+    def expect(n):  # the rule written out for the 86-row-block matrix
+        blocks = 86 * -(-n // 256)
+        return need_b if n >= 1024 or (n >= 256 and (2 * blocks <= cus or blocks > cus)) else 0
+    Ns = (255, 256, 512, 640, 1024, 4096)
+    assert [swm.spmm_workspace_bytes(fb, n) for n in Ns] == [expect(n) for n in Ns]
+    if cus == 256:  # MI355X: 86 blocks at most half, 172 on chip, 258 a second round
+        assert [expect(n) for n in Ns] == [0, need_b, 0, need_b, need_b, need_b]
 
 
 def test_spmm_ws_below_threshold_and_fallbacks(gpu_lib):
