@@ -1,22 +1,35 @@
 """Benchmark of the sparse-weight matmul hot path on one MI355X.
 
-Default workload (``--workload decode``): the q_proj shape -- W 4096x4096 fp16
-at 50% per-row magnitude pruning, compressed to the tiled column-bitmap format.
-One step = three sparse products with N = 1, 8 and 16 tokens.  The same step
-is timed with the in-house dense GEMM on the masked W stored dense, for the
-speedup.  ``value`` = algorithmic bytes of the sparse products (compressed
-weight + X + Y) / their GPU time, in GB/s, inputs resident in HBM.
+Default workload (``--workload decode``) prints one JSON line with:
+
+* ``value``: decode on the q_proj shape -- W 4096x4096 fp16 at 50% per-row
+  magnitude pruning, compressed to the tiled column-bitmap format.  One step =
+  three sparse products with N = 1, 8 and 16 tokens; ``value`` = algorithmic
+  bytes of the sparse products (kept values, bitmaps and tile pointers without
+  run padding, + X + Y) / their GPU time, in GB/s, inputs resident in HBM.  The
+  same step is timed with the in-house dense GEMM on the masked W stored dense,
+  for the speedup.  ``roofline`` is the N = 16 launch against 8 TB/s and
+  against the library's streaming kernel at the same byte count and rotation.
+* ``prefill``: up/gate 11008x4096 at 50%, N = 4096, through the workspace
+  route, the on-chip kernel and the dense kernel, with an MFMA roofline on
+  useful (2 nnz N) and executed (2 M K N) FLOPs and the oracle timed on the
+  host on a 512-token slice.
+* ``layer``: the seven Llama-2-7B-shaped linears back to back, N = 16 and
+  4096, rotated over 5 compressed and 3 dense copies of the layer.
+* ``device``: name, CU count, clocks, ROCm and HIP versions.
 
 Timing: launches are captured once into HIP graphs (torch.cuda.CUDAGraph) and
 replayed, so host launch overhead does not starve the GPU; HIP events on the
-launch stream bracket the replays.  Copies of the weight are rotated so the
-working set exceeds 1 GiB (4x the 256 MB Infinity Cache) and every launch
-streams its weight from HBM.
+launch stream bracket the replays (one event pair per replay for the
+median / p10 / p90).  Copies of the weight are rotated so the working set
+exceeds 1 GiB (4x the 256 MB Infinity Cache) and every launch streams its
+weight from HBM.
 
 Other workloads: ``spmspv`` (down_proj 4096x11008, SiLU-gated x with |x|<0.3
-zeroed, N = 1 and 4), ``prefill`` (up/gate 11008x4096, N = 512/2048/4096,
-sparsity 0.5/0.6/0.7), ``layer`` (seven Llama-2-7B linears back to back, N =
-16 and 4096).  Each prints one JSON line.
+zeroed, N = 1, 2, 4), ``prefill`` (up/gate 11008x4096, N = 512/2048/4096,
+sparsity 0.5/0.6/0.7), ``layer`` (the layer block alone), ``mlp`` (decode FFN
+block), ``wide`` (other shapes and sparsities), ``calib`` (copy of known size
+for the counter scale).  Each prints one JSON line.
 """
 from __future__ import annotations
 
@@ -41,7 +54,52 @@ def _log(msg):
 
 
 def fmt_bytes(info):
+    """Resident bytes of a format's device sections (tile pointers, bitmaps,
+    padded value runs)."""
     return int(info["bytes_tile_ptr"] + info["bytes_bits"] + info["bytes_values"])
+
+
+def fmt_alg_bytes(info):
+    """Algorithmic bytes of a format: tile pointers, bitmaps and the kept fp16
+    values; the run padding is not counted."""
+    return int(info["bytes_tile_ptr"] + info["bytes_bits"] + 2 * info["nnz"])
+
+
+def pct(ts):
+    """median / p10 / p90 of a list of per-launch times (ms) -> dict in us."""
+    a = np.asarray(ts, dtype=np.float64) * 1e3
+    return {"median_us": float(np.median(a)), "p10_us": float(np.percentile(a, 10)),
+            "p90_us": float(np.percentile(a, 90)), "replays": int(a.size)}
+
+
+def device_info(torch):
+    """Device name, CU count, clocks, LDS, L2 and the ROCm / HIP versions."""
+    import ctypes
+    p = torch.cuda.get_device_properties(0)
+    info = {"name": p.name, "arch": getattr(p, "gcnArchName", ""), "cus": p.multi_processor_count,
+            "hbm_bytes": int(p.total_memory), "hip": torch.version.hip, "torch": torch.__version__}
+    try:
+        info["rocm"] = open("/opt/rocm/.info/version").read().strip()
+    except OSError:
+        info["rocm"] = None
+    try:
+        hip = ctypes.CDLL("libamdhip64.so")
+        v = ctypes.c_int(0)
+        for key, attr in (("clock_khz", 5), ("mem_clock_khz", 60), ("lds_per_block", 74), ("l2_bytes", 19)):
+            # hipDeviceAttributeClockRate, MemoryClockRate, MaxSharedMemoryPerBlock, L2CacheSize
+            if hip.hipDeviceGetAttribute(ctypes.byref(v), attr, 0) == 0:
+                info[key] = int(v.value)
+    except OSError:
+        pass
+    return info
+
+
+def blas_vendor():
+    try:
+        b = np.show_config(mode="dicts")["Build Dependencies"]["blas"]
+        return f"{b.get('name')} {b.get('version')}"
+    except Exception:
+        return None
 
 
 class Graphs:
@@ -72,13 +130,28 @@ class Graphs:
         e1.synchronize()
         return e0.elapsed_time(e1) / reps  # ms per replay
 
+    def samples(self, g, reps, per):
+        """ms per launch of each of `reps` replays (one event pair per replay of
+        a graph of `per` launches)."""
+        torch = self.torch
+        s = torch.cuda.current_stream()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+        torch.cuda.synchronize()
+        ev[0].record(s)
+        for r in range(reps):
+            g.replay()
+            ev[r + 1].record(s)
+        ev[-1].synchronize()
+        return [ev[r].elapsed_time(ev[r + 1]) / per for r in range(reps)]
+
 
 def rotating_formats(swm, W, mask, min_bytes=ROTATE_BYTES):
+    """Copies of the compressed W whose resident bytes add up to >= min_bytes;
+    returns them and the format's algorithmic bytes (no run padding)."""
     f0 = swm.sparse_compress(W, mask)
-    fb = fmt_bytes(f0.info)
-    copies = max(2, int(np.ceil(min_bytes / fb)))
+    copies = max(2, int(np.ceil(min_bytes / fmt_bytes(f0.info))))
     blob = f0.export()
-    return [f0] + [swm.format_import(blob) for _ in range(copies - 1)], fb
+    return [f0] + [swm.format_import(blob) for _ in range(copies - 1)], fmt_alg_bytes(f0.info)
 
 
 def rotating_dense(torch, W, min_bytes=ROTATE_BYTES):
@@ -101,6 +174,31 @@ def profiled_traffic(profile_md):
     if hashlib.sha256(src).hexdigest() != meta["source_sha256"]:
         return None
     return int(meta["traffic_bytes_per_launch"])
+
+
+def stream_achievable(torch, swm, G, nbytes, min_bytes=ROTATE_BYTES):
+    """Read bandwidth of the library's streaming kernel for `nbytes` per launch
+    under the same rotation (>= 1 GiB of distinct buffers): the best launch
+    shape of a small sweep.  The 'achievable' reference beside the 8 TB/s peak."""
+    nb = (int(nbytes) + 255) // 256 * 256
+    copies = max(2, int(np.ceil(min_bytes / nb)))
+    buf = torch.empty(copies * nb, dtype=torch.uint8, device="cuda")
+    buf.fill_(1)
+    out = torch.empty(4096 * 4, dtype=torch.int32, device="cuda")
+    views = [buf[i * nb:i * nb + (nbytes // 16) * 16] for i in range(copies)]
+    best = None
+    for unroll in (4, 8, 16):
+        for blocks in (256, 512, 1024, 2048):
+            fns = [lambda v=v: swm.hbm_stream(v, unroll, blocks, out) for v in views]
+            for f in fns[:2]:
+                f()
+            t = G.time(G.capture(fns), 3) / copies
+            if best is None or t < best[0]:
+                best = (t, unroll, blocks)
+    del buf
+    t, unroll, blocks = best
+    return {"GBps": (nbytes // 16) * 16 / (t * 1e-3) / 1e9, "us": t * 1e3, "bytes": int(nbytes),
+            "unroll": unroll, "blocks": blocks, "copies": copies}
 
 
 def threads_used():
@@ -128,22 +226,23 @@ def cpu_oracle(W, mask, X_list, units, unit, budget_s=20.0):
                 break
         t_tot += float(np.median(ts))
         u_tot += u
-    return {"value": u_tot / t_tot, "unit": unit, "cores": threads_used(), "kind": "oracle"}
+    return {"value": u_tot / t_tot, "unit": unit, "cores": threads_used(), "kind": "oracle", "blas": blas_vendor()}
 
 
 # ------------------------------------------------------------------ decode (default)
 def bench_decode(args, torch, swm, wl, G):
     _log("workload: decode q_proj 4096x4096, 50%")
     W, mask, X = wl.decode_qproj(16)
-    fmts, fb = rotating_formats(swm, W, mask)
+    fmts, fa = rotating_formats(swm, W, mask)
+    fb = fmt_bytes(fmts[0].info)
     Wds = rotating_dense(torch, W)
     C, CD = len(fmts), len(Wds)
-    _log(f"format {fb / 1e6:.2f} MB, {C} sparse / {CD} dense rotating copies")
+    _log(f"format {fb / 1e6:.2f} MB resident ({fa / 1e6:.2f} MB algorithmic), {C} sparse / {CD} dense rotating copies")
     Xd = torch.from_numpy(X).cuda()
     Ns = (1, 8, 16)
     M, K = W.shape
     Ys = {n: torch.empty((n, M), dtype=torch.float16, device="cuda") for n in Ns}
-    alg = {n: fb + 2 * K * n + 2 * M * n for n in Ns}
+    alg = {n: fa + 2 * K * n + 2 * M * n for n in Ns}
     dense_b = {n: 2 * M * K + 2 * K * n + 2 * M * n for n in Ns}
 
     def sp(i, n):
@@ -152,17 +251,19 @@ def bench_decode(args, torch, swm, wl, G):
     def de(i, n):
         return lambda: swm.dense_gemm(Wds[i % CD], Xd[:n], Ys[n])
 
-    for r in range(2):  # untimed: builds workspaces, warms the code paths
+    for r in range(2):  # untimed: warms the code paths
         for n in Ns:
             sp(r, n)()
             de(r, n)()
     torch.cuda.synchronize()
-    per_n, per_n_d = {}, {}
+    per_n, per_n_d, dist = {}, {}, {}
     for n in Ns:
         gs = G.capture([sp(i, n) for i in range(C)])
         gd = G.capture([de(i, n) for i in range(CD)])
-        per_n[n] = G.time(gs, 3) / C
-        per_n_d[n] = G.time(gd, 3) / CD
+        ts = G.samples(gs, 20, C)
+        per_n[n] = float(np.mean(ts))
+        dist[n] = pct(ts)
+        per_n_d[n] = G.time(gd, 5) / CD
     # The contract's steps: W warmup steps, then exactly K timed steps.
     g_warm = G.capture([sp(s * 3 + j, n) for s in range(args.warmup) for j, n in enumerate(Ns)])
     g_steps = G.capture([sp(s * 3 + j, n) for s in range(args.steps) for j, n in enumerate(Ns)])
@@ -175,20 +276,23 @@ def bench_decode(args, torch, swm, wl, G):
     ms_dense = G.time(g_dsteps, 1)
     ms_step = ms_total / args.steps
     value = sum(alg.values()) / (ms_step * 1e-3) / 1e9
-    detail = {str(n): {"sparse_us": per_n[n] * 1e3, "dense_us": per_n_d[n] * 1e3,
+    detail = {str(n): {"sparse_us": per_n[n] * 1e3, "sparse_dist": dist[n], "dense_us": per_n_d[n] * 1e3,
                        "speedup_vs_dense": per_n_d[n] / per_n[n],
                        "sparse_GBps_alg": alg[n] / (per_n[n] * 1e-3) / 1e9,
                        "sparse_frac_hbm": alg[n] / (per_n[n] * 1e-3) / 1e9 / HBM_PEAK_GBS,
                        "dense_GBps": dense_b[n] / (per_n_d[n] * 1e-3) / 1e9} for n in Ns}
     dom = 16
     ach = alg[dom] / (per_n[dom] * 1e-3) / 1e9
+    _log("stream calibration at the decode launch's byte count")
+    st = stream_achievable(torch, swm, G, alg[dom])
     out = {
         "metric": "decode SpMM HBM throughput on compressed bytes (q_proj 4096x4096, 50%)",
         "value": value, "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "f16", "data": "synthetic (seeded N(0,1) fp16 W and X, 50% per-row magnitude pruning)",
         "config": {"workload": "decode q_proj 4096x4096, 50% unstructured, N in {1,8,16} per step",
-                   "format": "SWM-TCB v2 tm=16 tk=64", "format_bytes": fb, "rotating_copies": C},
+                   "format": "SWM-TCB v2 tm=16 tk=64", "format_resident_bytes": fb,
+                   "format_alg_bytes": fa, "rotating_copies": C},
         "speedup_vs_dense": ms_dense / ms_total,
         "dense_ms_per_step": ms_dense / args.steps,
         "detail": detail,
@@ -196,7 +300,9 @@ def bench_decode(args, torch, swm, wl, G):
                      "frac": ach / HBM_PEAK_GBS,
                      "traffic": profiled_traffic("decode_seq_kernel_qproj_pmc.md"),
                      "kernel": "decode_seq_kernel, N=16", "alg_bytes_per_launch": alg[dom],
-                     "avg_launch_us": per_n[dom] * 1e3},
+                     "avg_launch_us": per_n[dom] * 1e3, "launch_dist": dist[dom],
+                     "achievable": st["GBps"], "frac_of_achievable": ach / st["GBps"],
+                     "achievable_kernel": st},
         "timed_wall_s": wall,
     }
     if not args.no_cpu:
@@ -206,6 +312,129 @@ def bench_decode(args, torch, swm, wl, G):
         cb["unit"] = "GB/s"
         cb["sample"] = "one full decode step (N = 1, 8, 16), numpy float64 masked-W @ X, median of 3"
         out["cpu_baseline"] = cb
+    return out
+
+
+def prefill_block(args, torch, swm, wl, G):
+    """Config-4 headline point: up/gate 11008x4096 at 50%, N = 4096, through
+    swm_spmm_ws (W expanded once, dense MFMA), the on-chip kernel and the
+    dense kernel; MFMA roofline on useful and executed FLOPs."""
+    _log("prefill block: up/gate 11008x4096, 50%, N = 4096")
+    n = 4096
+    W, mask, X = wl.prefill_upgate(0.5, n)
+    M, K = W.shape
+    nnz = int(mask.sum())
+    f = swm.sparse_compress(W, mask)
+    Wd = torch.from_numpy(W).cuda()
+    Xd = torch.from_numpy(X).cuda()
+    ws = torch.empty(max(swm.spmm_workspace_bytes(f, n), 256), dtype=torch.uint8, device="cuda")
+    y = torch.empty((n, M), dtype=torch.float16, device="cuda")
+    swm.spmm(f, Xd, y)
+    swm.spmm_ws(f, Xd, ws, y)
+    swm.dense_gemm(Wd, Xd, y)
+    torch.cuda.synchronize()
+    reps = 4
+    d_ws = pct(G.samples(G.capture([lambda: swm.spmm_ws(f, Xd, ws, y)] * reps), 10, reps))
+    d_on = pct(G.samples(G.capture([lambda: swm.spmm(f, Xd, y)] * reps), 10, reps))
+    d_de = pct(G.samples(G.capture([lambda: swm.dense_gemm(Wd, Xd, y)] * reps), 10, reps))
+    d_dc = pct(G.samples(G.capture([lambda: swm.decompress(f, ws.view(torch.float16)[:M * K].view(M, K))] * reps),
+                         10, reps))
+    useful, executed = 2.0 * nnz * n, 2.0 * M * K * n
+    t_ws, t_on, t_de = d_ws["median_us"] * 1e-6, d_on["median_us"] * 1e-6, d_de["median_us"] * 1e-6
+    blk = {
+        "workload": "prefill up/gate 11008x4096, 50% per-row magnitude pruning, N = 4096",
+        "spmm_ws": d_ws, "onchip": d_on, "dense": d_de, "expand_only": d_dc,
+        "useful_TFLOPs_ws": useful / t_ws / 1e12, "useful_TFLOPs_onchip": useful / t_on / 1e12,
+        "dense_TFLOPs": executed / t_de / 1e12,
+        "speedup_ws_vs_dense": t_de / t_ws, "speedup_onchip_vs_dense": t_de / t_on,
+        "roofline": {"bound": "mfma", "unit": "TFLOP/s", "peak": MFMA_F16_PEAK_TFLOPS,
+                     "kernel": "swm_spmm_ws (decompress_kernel + dense_kernel), N=4096",
+                     "achieved": useful / t_ws / 1e12, "frac": useful / t_ws / 1e12 / MFMA_F16_PEAK_TFLOPS,
+                     "executed_TFLOPs": executed / t_ws / 1e12,
+                     "frac_executed": executed / t_ws / 1e12 / MFMA_F16_PEAK_TFLOPS,
+                     "useful_flops_per_launch": useful, "executed_flops_per_launch": executed, "traffic": None},
+    }
+    if not args.no_cpu:
+        _log("timing the CPU oracle on a 512-token slice")
+        cb = cpu_oracle(W, mask, [X[:512]], [2.0 * nnz * 512], "FLOP")
+        cb["value"] = cb["value"] / 1e12
+        cb["unit"] = "TFLOP/s"
+        cb["sample"] = "512 of the 4096 tokens, numpy float64 masked-W @ X, median of 3, useful FLOPs"
+        blk["cpu_baseline"] = cb
+    del f, Wd, ws, y
+    torch.cuda.empty_cache()
+    return blk
+
+
+def layer_copies(swm, torch, n_max, min_sparse=5, min_dense=3):
+    """The seven Llama-2-7B-shaped linears, >= min_sparse compressed copies and
+    >= min_dense dense copies of the whole layer (rotated so that each layer
+    pass streams its weights from HBM: 5 x 228 MB and 3 x 405 MB are above
+    4x the 256 MB Infinity Cache)."""
+    import swm_workloads as wl
+    fmts, dens, xs, shapes, alg = [], [], [], [], 0
+    for i in range(7):
+        W, mask, X = wl.layer_linear(i, n_max)
+        f0 = swm.sparse_compress(W, mask)
+        blob = f0.export()
+        fmts.append([f0] + [swm.format_import(blob) for _ in range(min_sparse - 1)])
+        Wd = torch.from_numpy(W).cuda()
+        dens.append([Wd] + [Wd.clone() for _ in range(min_dense - 1)])
+        xs.append(torch.from_numpy(X).cuda())
+        shapes.append(W.shape)
+        alg += fmt_alg_bytes(f0.info)
+    return fmts, dens, xs, shapes, alg
+
+
+def layer_block(args, torch, swm, wl, G):
+    """Config 5: the seven linears back to back on one stream, N = 16 and 4096,
+    rotated over 5 compressed / 3 dense copies of the layer."""
+    _log("layer block: 7 linears, 5 compressed / 3 dense rotating copies")
+    CS, CD = 5, 3
+    fmts, dens, xs, shapes, fa = layer_copies(swm, torch, 4096, CS, CD)
+    ws = torch.empty(max(max(swm.spmm_workspace_bytes(f[0], 4096) for f in fmts), 256), dtype=torch.uint8,
+                     device="cuda")
+    blk = {"workload": "Llama-2-7B layer: q/k/v/o 4096x4096, gate/up 11008x4096, down 4096x11008, 50%",
+           "rotation": {"compressed_layer_copies": CS, "dense_layer_copies": CD}, "format_alg_bytes": fa}
+    for n in (16, 4096):
+        ys = [torch.empty((n, shp[0]), dtype=torch.float16, device="cuda") for shp in shapes]
+
+        def sp(c, i):
+            return lambda: swm.spmm_ws(fmts[i][c], xs[i][:n], ws, ys[i])
+
+        def de(c, i):
+            return lambda: swm.dense_gemm(dens[i][c], xs[i][:n], ys[i])
+        for i in range(7):
+            sp(0, i)()
+            de(0, i)()
+        torch.cuda.synchronize()
+        gs = G.capture([sp(c, i) for c in range(CS) for i in range(7)])
+        gd = G.capture([de(c, i) for c in range(CD) for i in range(7)])
+        reps = 10 if n == 16 else 3
+        ds, dd = pct(G.samples(gs, reps, CS)), pct(G.samples(gd, reps, CD))
+        alg = fa + sum(2 * (shp[0] + shp[1]) * n for shp in shapes)
+        e = {"sparse_layer": ds, "dense_layer": dd, "speedup_vs_dense": dd["median_us"] / ds["median_us"],
+             "route": "decode kernels" if n <= 32 else "swm_spmm_ws (expand + dense MFMA; one shared workspace)"}
+        if n == 16:
+            e["alg_bytes"] = alg
+            e["GBps_alg"] = alg / (ds["median_us"] * 1e-6) / 1e9
+            e["frac_hbm"] = e["GBps_alg"] / HBM_PEAK_GBS
+        else:
+            useful = sum(2.0 * f[0].info["nnz"] * n for f in fmts)
+            e["useful_TFLOPs"] = useful / (ds["median_us"] * 1e-6) / 1e12
+        blk[str(n)] = e
+        del ys
+    del fmts, dens, xs, ws
+    torch.cuda.empty_cache()
+    return blk
+
+
+def bench_default(args, torch, swm, wl, G):
+    out = bench_decode(args, torch, swm, wl, G)
+    if not args.decode_only:
+        out["prefill"] = prefill_block(args, torch, swm, wl, G)
+        out["layer"] = layer_block(args, torch, swm, wl, G)
+    out["device"] = device_info(torch)
     return out
 
 
@@ -381,7 +610,7 @@ def bench_prefill(args, torch, swm, wl, G):
         t_dc = G.time(G.capture([lambda: swm.decompress(f, Wx)] * reps), 3) / reps
         del Wx
         out["detail"][f"s{s}_decompress"] = {
-            "us": t_dc * 1e3, "alg_GBs": (fmt_bytes(f.query()) + 2 * M * K) / (t_dc * 1e-3) / 1e9}
+            "us": t_dc * 1e3, "alg_GBs": (fmt_alg_bytes(f.query()) + 2 * M * K) / (t_dc * 1e-3) / 1e9}
         for n in Ns:
             y = torch.empty((n, M), dtype=torch.float16, device="cuda")
             swm.spmm(f, Xfull[:n], y)
@@ -409,35 +638,10 @@ def bench_prefill(args, torch, swm, wl, G):
 
 # ------------------------------------------------------------------ layer
 def bench_layer(args, torch, swm, wl, G):
-    _log("workload: Llama-2-7B-shaped layer, 7 linears")
-    out = {"metric": "layer time, 7 linears back to back", "unit": "us", "n_gpus": 1,
-           "higher_is_better": False, "dtype": "f16", "data": "synthetic", "detail": {}}
-    lin = []
-    for i in range(7):
-        W, mask, X = wl.layer_linear(i, 4096)
-        f = swm.sparse_compress(W, mask)
-        lin.append((f, torch.from_numpy(W).cuda(), torch.from_numpy(X).cuda(), W.shape))
-    # one workspace shared by the seven linears (calls ordered on one stream)
-    ws = torch.empty(max(max(swm.spmm_workspace_bytes(f, 4096) for (f, _, _, _) in lin), 256),
-                     dtype=torch.uint8, device="cuda")
-    for n in (16, 4096):
-        ys = [torch.empty((n, shp[0]), dtype=torch.float16, device="cuda") for (_, _, _, shp) in lin]
-        for (f, Wd, Xd, _), y in zip(lin, ys):
-            swm.spmm(f, Xd[:n], y)
-            swm.spmm_ws(f, Xd[:n], ws, y)
-            swm.dense_gemm(Wd, Xd[:n], y)
-        torch.cuda.synchronize()
-        gs = G.capture([lambda f=f, Xd=Xd, y=y: swm.spmm(f, Xd[:n], y) for (f, _, Xd, _), y in zip(lin, ys)])
-        gw = G.capture([lambda f=f, Xd=Xd, y=y: swm.spmm_ws(f, Xd[:n], ws, y) for (f, _, Xd, _), y in zip(lin, ys)])
-        gd = G.capture([lambda Wd=Wd, Xd=Xd, y=y: swm.dense_gemm(Wd, Xd[:n], y) for (_, Wd, Xd, _), y in zip(lin, ys)])
-        ts, tw, td = G.time(gs, 5), G.time(gw, 5), G.time(gd, 5)
-        out["detail"][str(n)] = {"sparse_us": ts * 1e3, "spmm_ws_us": tw * 1e3, "dense_us": td * 1e3,
-                                 "speedup_vs_dense": td / ts, "ws_speedup_vs_dense": td / tw,
-                                 "note": "no rotation: the compressed layer (228 MB) fits the 256 MB "
-                                         "Infinity Cache, the dense one (405 MB) does not; spmm_ws "
-                                         "shares one workspace across the seven linears"}
-    out["value"] = out["detail"]["16"]["sparse_us"]
-    return out
+    blk = layer_block(args, torch, swm, wl, G)
+    return {"metric": "layer time, 7 linears back to back (N = 16)", "unit": "us", "n_gpus": 1,
+            "higher_is_better": False, "dtype": "f16", "data": "synthetic",
+            "value": blk["16"]["sparse_layer"]["median_us"], "detail": blk}
 
 
 # ------------------------------------------------------------------ copy calibration
@@ -472,7 +676,7 @@ def bench_wide(args, torch, swm, wl, G):
             Wds = rotating_dense(torch, W)
         else:
             f0 = swm.sparse_compress(W, mask)
-            fmts, fb = [f0], fmt_bytes(f0.info)
+            fmts, fb = [f0], fmt_alg_bytes(f0.info)
             Wds = [torch.from_numpy(W).cuda()]
         C, CD = len(fmts), len(Wds)
         Xd = torch.from_numpy(X).cuda()
@@ -521,6 +725,7 @@ def main():
     ap.add_argument("--prefill-n", default="512,2048,4096")
     ap.add_argument("--prefill-s", default="0.5,0.6,0.7")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--decode-only", action="store_true", help="default workload without the prefill and layer blocks")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported: the library "
@@ -532,7 +737,7 @@ def main():
     swm.load()
     torch.cuda.set_device(0)
     G = Graphs(torch)
-    fn = {"decode": bench_decode, "spmspv": bench_spmspv, "prefill": bench_prefill, "layer": bench_layer,
+    fn = {"decode": bench_default, "spmspv": bench_spmspv, "prefill": bench_prefill, "layer": bench_layer,
           "wide": bench_wide, "mlp": bench_mlp, "calib": bench_calib}
     out = fn[args.workload](args, torch, swm, wl, G)
     out.setdefault("n_gpus", 1)

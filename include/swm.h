@@ -193,8 +193,9 @@ size_t swm_spmm_workspace_bytes(const swm_format* f, int64_t N);
  *  the handles of several layers as long as the calls are ordered on one
  *  stream (concurrent calls sharing it race).  workspace NULL with ws_bytes 0
  *  is swm_spmm.  SWM_ERR_INVALID_ARG: NULL handle, X or Y; a workspace that
- *  is NULL with ws_bytes > 0, misaligned, or too small for a call that
- *  expands; swm_spmm's argument errors.  Asynchronous on stream. */
+ *  is NULL with ws_bytes > 0 or too small for a call that expands; swm_spmm's
+ *  argument errors.  SWM_ERR_ALIGN: a workspace that is not 16-byte aligned.
+ *  Asynchronous on stream. */
 swm_status swm_spmm_ws(const swm_format* f, const void* X, int64_t ldx, void* Y, int64_t ldy, int64_t N,
                        void* workspace, size_t ws_bytes, void* stream);
 
@@ -215,14 +216,15 @@ swm_status swm_spmm_ws(const swm_format* f, const void* X, int64_t ldx, void* Y,
  *  overwritten.  tau: 0 <= tau <= 65504 (0 keeps every entry).
  *  SWM_ERR_INVALID_ARG: NULL pointers, n outside 1..32, tau outside its
  *  range or NaN, shapes that differ, leading dimensions too small, a handle
- *  on another device.  SWM_ERR_UNSUPPORTED: X not 16-byte aligned or ldx % 8
- *  != 0 or K % 8 != 0, n*ldx beyond 32-bit byte offsets, tiles other than
- *  16 x 64, or K above 8192 (more than 128 tiles per row: the two formats
- *  no longer fit one workgroup).  Asynchronous on stream. */
+ *  on another device.  SWM_ERR_ALIGN: X not 16-byte aligned or ldx % 8 != 0.
+ *  SWM_ERR_UNSUPPORTED: K < 8 or K % 8 != 0, n*ldx beyond 32-bit byte
+ *  offsets, tiles other than 16 x 64, or K above 8192 (more than 128 tiles
+ *  per row: the two formats no longer fit one workgroup).  Asynchronous on
+ *  stream. */
 swm_status swm_gate_up_silu(const swm_format* g, const swm_format* u, const void* X, int64_t ldx, void* H,
                             int64_t ldh, int32_t n, float tau, void* stream);
 
-/* spmspv: as swm_spmm for 1 <= n <= 16 tokens/* spmspv: as swm_spmm for 1 <= n <= 16 tokens, for activations with zero
+/* spmspv: as swm_spmm for 1 <= n <= 16 tokens, for activations with zero
  * input channels (x[t][k] == +0 or -0 for all tokens t).  Such channels
  * contribute exact zeros, so the result equals swm_spmm's up to fp32
  * summation order.  Skipping is applied only where it pays: on the aligned
@@ -254,8 +256,8 @@ swm_status swm_spmspv(const swm_format* f, const void* x, int64_t ldx, void* y, 
  *   Y = (W (.) mask) x~,  x~[t][k] = (|x[t][k]| < tau) ? 0 : x[t][k].
  * The comparison takes the fp16 activation exactly in fp32 against tau (fp32);
  * a column whose every token is below tau is skipped like a zero column.
- * tau = 0 gives swm_spmspv's result bitwise.  Inputs are assumed finite (a NaN
- * activation counts as zero).
+ * tau = 0 gives swm_spmspv's result bitwise.  A NaN activation is never
+ * below tau: it is kept and propagates into the outputs it touches.
  * Source: SPDP abstract (input-adaptive dynamic pruning in the decode spMspV
  * kernel); "Reduced Matrix Multiplication" blog page, Sec. 4.2 (an FFN keeps
  * only the high-response channels of its hidden activation and multiplies
@@ -299,10 +301,8 @@ swm_status swm_colruns_encode_blob(const void* tcb_blob, size_t size, void* out,
  * fallback to the full product.  N <= 16 runs the streaming kernel; larger N
  * the MFMA-tiled kernel, except N <= 32 when its 256x256 blocks would occupy
  * under a quarter of the CUs (then two 16-token streaming passes).
- * Asynchronous on stream, except that when the streaming kernel runs (or an
- * operand is unaligned) the first call on a device, and any later call that
- * needs a larger workspace, allocates a library-owned workspace and
- * synchronizes the device: make such a call once before capturing a graph.
+ * Asynchronous on stream; allocates nothing and never synchronizes, so it
+ * may be captured into a graph on any call.
  * Source: moderate-sparsity page, Sec. 1 (a sparse kernel is only useful if it
  * beats the dense product at the same shape). */
 swm_status swm_dense_gemm(const void* W, int64_t ldw, const void* X, int64_t ldx, void* Y,

@@ -74,10 +74,12 @@ def threshold_activations(X_tok: np.ndarray, tau: float) -> np.ndarray:
     """Input-adaptive channel selection ("Reduced Matrix Multiplication" blog
     page, Sec. 4.2: an FFN keeps only the high-response channels of its hidden
     activation).  An activation whose magnitude is below tau is dropped (+0);
-    one at or above tau is kept unchanged.  The comparison takes the fp16 value
+    every other one is kept unchanged (a NaN is not below tau, so it stays and
+    propagates, as in the plain product).  The comparison takes the fp16 value
     exactly in float32 against tau as float32."""
     X = np.asarray(X_tok, dtype=np.float16)
-    keep = np.abs(X.astype(np.float32)) >= np.float32(tau)
+    with np.errstate(invalid="ignore"):
+        keep = ~(np.abs(X.astype(np.float32)) < np.float32(tau))
     return np.where(keep, X, np.float16(0.0))
 
 

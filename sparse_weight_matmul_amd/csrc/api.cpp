@@ -58,34 +58,6 @@ int num_cus(int dev) {
   return cache[dev];
 }
 
-// Per-device workspace of the dense small-N kernel: a zero row that loads past
-// K or past a wave's columns read instead of W.  It only grows; growing
-// synchronizes the device, because queued work may still read the old row.
-struct DenseWs {
-  uint16_t* zeros = nullptr;
-  size_t n_zeros = 0;
-};
-
-swm_status dense_workspace(int dev, size_t nz, DenseWs** out) {
-  static std::mutex mu;
-  static std::vector<DenseWs> ws;
-  std::lock_guard<std::mutex> g(mu);
-  if (dev >= int(ws.size())) ws.resize(dev + 1);
-  DenseWs& w = ws[dev];
-  if (nz > w.n_zeros) {
-    SWM_HIP(hipDeviceSynchronize());
-    if (w.zeros) (void)hipFree(w.zeros);
-    w.zeros = nullptr;
-    w.n_zeros = 0;
-    if (hipMalloc(&w.zeros, nz * sizeof(uint16_t)) != hipSuccess) return SWM_ERR_OOM;
-    SWM_HIP(hipMemset(w.zeros, 0, nz * sizeof(uint16_t)));
-    SWM_HIP(hipDeviceSynchronize());
-    w.n_zeros = nz;
-  }
-  *out = &w;
-  return SWM_OK;
-}
-
 swm_status upload(std::vector<uint8_t>&& blob, const swm::Header& h, hipStream_t s, swm_format** out) {
   swm_format* f = new (std::nothrow) swm_format;
   if (!f) return SWM_ERR_OOM;
@@ -430,7 +402,8 @@ swm_status swm_spmm_ws(const swm_format* f, const void* X, int64_t ldx, void* Y,
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (!f || !X || !Y) return SWM_ERR_INVALID_ARG;
   if (!workspace && ws_bytes == 0) return run_products(f, X, ldx, Y, ldy, N, false, s);
-  if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 15)) return SWM_ERR_INVALID_ARG;
+  if (!workspace) return SWM_ERR_INVALID_ARG;
+  if (reinterpret_cast<uintptr_t>(workspace) & 15) return SWM_ERR_ALIGN;
   const size_t need = swm_spmm_workspace_bytes(f, N);
   if (need == 0 || !swm::prefill_supported(f->h.k, ldx, X)) return run_products(f, X, ldx, Y, ldy, N, false, s);
   if (ws_bytes < need) return SWM_ERR_INVALID_ARG;
@@ -480,7 +453,8 @@ swm_status swm_gate_up_silu(const swm_format* g, const swm_format* u, const void
   if (st == SWM_OK) st = check_tile_supported(u->h);
   if (st != SWM_OK) return st;
   if (!on_current_device(g) || !on_current_device(u)) return SWM_ERR_INVALID_ARG;
-  if (!swm::prefill_supported(g->h.k, ldx, X)) return SWM_ERR_UNSUPPORTED;  // aligned X, K % 8 == 0
+  if (g->h.k < 8 || g->h.k % 8 != 0) return SWM_ERR_UNSUPPORTED;
+  if (ldx % 8 != 0 || (reinterpret_cast<uintptr_t>(X) & 15) != 0) return SWM_ERR_ALIGN;
   if (2 * ((int64_t(n) - 1) * ldx + g->h.k) >= (int64_t(1) << 32)) return SWM_ERR_UNSUPPORTED;
   int dev = 0;
   SWM_HIP(hipGetDevice(&dev));
@@ -529,15 +503,12 @@ swm_status swm_dense_gemm(const void* W, int64_t ldw, const void* X, int64_t ldx
     return SWM_OK;
   }
   const auto p = swm::plan_dense_small(M, K, int(std::min<int64_t>(N, 16)), num_cus(dev));
-  DenseWs* ws = nullptr;
-  swm_status st = dense_workspace(dev, size_t(K) + 64, &ws);
-  if (st != SWM_OK) return st;
   const uint16_t* w = static_cast<const uint16_t*>(W);
   const uint16_t* x = static_cast<const uint16_t*>(X);
   uint16_t* y = static_cast<uint16_t*>(Y);
   for (int64_t n0 = 0; n0 < N; n0 += 16) {
     const int nn = int(std::min<int64_t>(16, N - n0));
-    SWM_HIP(swm::launch_dense_small(p, w, ldw, x + n0 * ldx, ldx, y + n0 * ldy, ldy, M, K, nn, ws->zeros, s));
+    SWM_HIP(swm::launch_dense_small(p, w, ldw, x + n0 * ldx, ldx, y + n0 * ldy, ldy, M, K, nn, s));
   }
   return SWM_OK;
 }

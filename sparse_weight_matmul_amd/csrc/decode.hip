@@ -599,19 +599,24 @@ __global__ __launch_bounds__(1024) void decode_seq_kernel(typename SeqArgs<kGlu>
 struct DenseArgs {
   const uint16_t* W;
   const uint16_t* X;
-  const uint16_t* zeros;
   uint16_t* Y;
   int64_t ldw, ldx, ldy;
   int M, K, N;
   int kc;  // columns per wave, a multiple of 256
 };
 
+// Sixteen zero bytes in the code object's own data (zero-initialised when the
+// module loads, never written): the source of the dense kernel's loads past
+// the end of a wave's columns.
+__device__ __attribute__((aligned(16))) uint16_t g_zero_chunk[8];
+
 // Same slab decomposition as the sparse kernel: one workgroup per 16-row slab,
 // wave w covers columns [w*kc, w*kc + kc).  Per 32 columns one
 // v_mfma_f32_16x16x32_f16 with A = W[16 rows][32 columns] (lane l loads row
 // l%16, columns 8(l/16) .. +7: 16 B) and B = X[16 tokens][32 columns].  Loads
-// run seven steps ahead through an eight-slot register ring; addresses past
-// the wave's columns or past K point at the zero row.
+// run seven steps ahead through an eight-slot register ring; loads past the
+// wave's columns read g_zero_chunk.  Rows past M read row M-1 and tokens past
+// N read token N-1: their accumulator entries are never stored.
 template <bool kVec>
 __global__ __launch_bounds__(1024) void dense_small_kernel(DenseArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
@@ -623,9 +628,9 @@ __global__ __launch_bounds__(1024) void dense_small_kernel(DenseArgs a) {
   const int64_t ke = min(kb + a.kc, int64_t(a.K));
   const int kq = 8 * (lane >> 4);
   const int tok = lane & 15;
-  const int64_t row = int64_t(slab) * kSlab + (lane & 15);
-  const uint16_t* wrow = row < a.M ? a.W + row * a.ldw : a.zeros;
-  const uint16_t* xrow = tok < a.N ? a.X + int64_t(tok) * a.ldx : a.zeros;
+  const int64_t row = min(int64_t(slab) * kSlab + (lane & 15), int64_t(a.M) - 1);
+  const uint16_t* wrow = a.W + row * a.ldw;
+  const uint16_t* xrow = a.X + int64_t(min(tok, a.N - 1)) * a.ldx;
 
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   if (kb < ke) {
@@ -635,8 +640,8 @@ __global__ __launch_bounds__(1024) void dense_small_kernel(DenseArgs a) {
       auto issue = [&](int s, int slot) {
         const int64_t k = kb + int64_t(s) * 32 + kq;
         const bool ok = k < ke;
-        A[slot] = __builtin_bit_cast(half8, *reinterpret_cast<const u32x4*>((ok ? wrow : a.zeros) + (ok ? k : 0)));
-        B[slot] = __builtin_bit_cast(half8, *reinterpret_cast<const u32x4*>((ok ? xrow : a.zeros) + (ok ? k : 0)));
+        A[slot] = __builtin_bit_cast(half8, *reinterpret_cast<const u32x4*>(ok ? wrow + k : g_zero_chunk));
+        B[slot] = __builtin_bit_cast(half8, *reinterpret_cast<const u32x4*>(ok ? xrow + k : g_zero_chunk));
       };
 #pragma unroll
       for (int u = 0; u < 7; ++u) issue(u, u);
@@ -950,12 +955,10 @@ DensePlan plan_dense_small(int64_t M, int64_t K, int n, int num_cus) {
 }
 
 hipError_t launch_dense_small(const DensePlan& p, const uint16_t* W, int64_t ldw, const uint16_t* X,
-                              int64_t ldx, uint16_t* Y, int64_t ldy, int64_t M, int64_t K, int n,
-                              const uint16_t* zeros, hipStream_t s) {
+                              int64_t ldx, uint16_t* Y, int64_t ldy, int64_t M, int64_t K, int n, hipStream_t s) {
   DenseArgs a;
   a.W = W;
   a.X = X;
-  a.zeros = zeros;
   a.Y = Y;
   a.ldw = ldw;
   a.ldx = ldx;
@@ -969,6 +972,7 @@ hipError_t launch_dense_small(const DensePlan& p, const uint16_t* W, int64_t ldw
                    ((reinterpret_cast<uintptr_t>(W) & 15) == 0);
   const int64_t slabs = (M + 15) / 16;
   if (slabs == 0) return hipSuccess;
+  if (n < 1 || n > 16) return hipErrorInvalidValue;
   const dim3 grid{unsigned(slabs), 1, 1}, block{unsigned(p.waves * 64), 1, 1};
   const size_t lds = size_t(p.waves) * 256 * 4;
   if (vec) hipLaunchKernelGGL((dense_small_kernel<true>), grid, block, lds, s, a);

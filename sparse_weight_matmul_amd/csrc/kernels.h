@@ -78,8 +78,7 @@ struct DensePlan {
 };
 DensePlan plan_dense_small(int64_t M, int64_t K, int n, int num_cus);
 hipError_t launch_dense_small(const DensePlan& p, const uint16_t* W, int64_t ldw, const uint16_t* X,
-                              int64_t ldx, uint16_t* Y, int64_t ldy, int64_t M, int64_t K, int n,
-                              const uint16_t* zeros, hipStream_t s);
+                              int64_t ldx, uint16_t* Y, int64_t ldy, int64_t M, int64_t K, int n, hipStream_t s);
 
 // Tiled MFMA GEMM for larger N: dense W, or W expanded from the format tile by tile.
 hipError_t launch_prefill_dense(const uint16_t* W, int64_t ldw, const uint16_t* X, int64_t ldx,

@@ -170,11 +170,12 @@ __global__ __launch_bounds__(1024) void spmspv_cr_kernel(CrArgs a) {
     if (k < kend) {
 #pragma unroll
       for (int t = 0; t < kN; ++t) {
-        // a token's activation counts when it is nonzero and |x| >= tau
-        // (the fp16 value is exact in fp32; tau = 0 keeps every nonzero)
+        // a token's activation counts when it is nonzero and not below tau
+        // (the fp16 value is exact in fp32; tau = 0 keeps every nonzero, and
+        // a NaN is never below tau, so it is kept and propagates)
         const uint16_t h = a.x[int64_t(t) * a.ldx + k];
         const float xv = float(__builtin_bit_cast(_Float16, h));
-        const bool keep = (h & 0x7FFFu) != 0 && __builtin_fabsf(xv) >= a.tau;
+        const bool keep = (h & 0x7FFFu) != 0 && !(__builtin_fabsf(xv) < a.tau);
         v[t] = keep ? xv : 0.f;
         on |= keep;
       }

@@ -216,6 +216,27 @@ def test_threshold_invariants():
     assert np.array_equal(oracle.masked_matmul_threshold(W2, mask, x, tau), oracle.masked_matmul_threshold(W, mask, x, tau))
 
 
+def test_threshold_keeps_nan_like_the_plain_product():
+    # A NaN activation is not below any tau: it is kept, so the thresholded
+    # product agrees with the plain skipping product at tau = 0 (NaN reaches
+    # exactly the outputs whose kept weight in that column is nonzero or zero:
+    # 0 * NaN is NaN), and an Inf stays too.  Infinities and NaNs in the same
+    # column would make a dropped-versus-kept mistake visible as a NaN or as a
+    # finite value.
+    W = np.array([[1.0, 0.5, 0.0], [0.0, 2.0, 1.0]], dtype=np.float16)
+    x = np.array([[np.nan, 0.25, np.inf]], dtype=np.float16)
+    for tau in (0.0, 0.3, 1e4):
+        xk = oracle.threshold_activations(x, tau)
+        assert np.isnan(xk[0, 0]) and np.isinf(xk[0, 2])
+    assert xk[0, 1] == 0  # 0.25 < 1e4 is dropped
+    with np.errstate(invalid="ignore"):
+        y0 = oracle.masked_matmul_threshold(W, None, x, 0.0)
+        ys = oracle.masked_matmul_skip(W, None, x)
+        y1 = oracle.masked_matmul_threshold(W, None, x, 0.3)
+    assert np.array_equal(np.isnan(y0), np.isnan(ys)) and np.all(np.isnan(y0))
+    assert np.all(np.isnan(y1))  # row 0: 1*NaN; row 1: 0*NaN + 2*0 + 1*Inf
+
+
 def test_colruns_hand_worked_bytes():
     d = json.load(open(os.path.join(GOLDEN, "colruns_hand_example.json")))
     W = np.array(d["W_rows_fp16"], dtype=np.float16)
