@@ -251,6 +251,24 @@ swm_status swm_gate_up_silu(const swm_format* g, const swm_format* u, const void
 swm_status swm_spmspv(const swm_format* f, const void* x, int64_t ldx, void* y, int64_t ldy,
                       int32_t n, void* stream);
 
+/* spmspv_noalloc: swm_spmspv for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc).  Same arguments, kernels and result as swm_spmspv, bitwise; the
+ * difference is where the skipping path keeps its per-workgroup partial sums:
+ * in a fixed array of 4 MiB compiled into the library (each GPU the library
+ * runs on holds its own copy until the process ends) instead of the handle's
+ * workspace.  The call allocates and frees nothing.
+ *  The skipping path (swm_format_enable_skipping called on f, n <= 4) needs
+ *  ceil(M/256) * S * 4 * 256 floats of partials (S column splits of the
+ *  handle; 1 MiB for a 4096 x 11008 weight); a handle that needs more than
+ *  the 4 MiB array gives SWM_ERR_UNSUPPORTED and launches nothing.  Every
+ *  call on one GPU shares that GPU's array: calls that overlap in time on one
+ *  GPU (concurrent streams, or host threads) race and must be ordered on one
+ *  stream.  Each call writes every partial it reads, so no state carries
+ *  over between calls.  Other errors as swm_spmspv. */
+swm_status swm_spmspv_noalloc(const swm_format* f, const void* x, int64_t ldx, void* y, int64_t ldy,
+                              int32_t n, void* stream);
+
 /* spmspv_threshold: swm_spmspv with input-adaptive channel selection fused
  * in: an activation with |x[t][k]| < tau counts as zero, so
  *   Y = (W (.) mask) x~,  x~[t][k] = (|x[t][k]| < tau) ? 0 : x[t][k].

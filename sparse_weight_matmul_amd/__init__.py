@@ -59,6 +59,7 @@ SIGNATURES = {
     "swm_spmm_workspace_bytes": (_sz, [_vp, _i64]),
     "swm_spmm_ws": (_i32, [_vp, _vp, _i64, _vp, _i64, _i64, _vp, _sz, _vp]),
     "swm_spmspv": (_i32, [_vp, _vp, _i64, _vp, _i64, _i32, _vp]),
+    "swm_spmspv_noalloc": (_i32, [_vp, _vp, _i64, _vp, _i64, _i32, _vp]),
     "swm_spmspv_threshold": (_i32, [_vp, _vp, _i64, _vp, _i64, _i32, ctypes.c_float, _vp]),
     "swm_gate_up_silu": (_i32, [_vp, _vp, _vp, _i64, _vp, _i64, _i32, ctypes.c_float, _vp]),
     "swm_format_enable_skipping": (_i32, [_vp, _vp, ctypes.POINTER(_u64)]),
@@ -328,6 +329,18 @@ def spmspv(fmt: Format, x, y=None, stream=None):
     y = _out(y, n, fmt.M, x)
     yp, ldy = _dev2d(y, "y", rows=n, cols=fmt.M)
     _check(lib.swm_spmspv(fmt._h, xp, ldx, yp, ldy, n, _stream_ptr(stream)), "swm_spmspv")
+    return y
+
+
+def spmspv_noalloc(fmt: Format, x, y=None, stream=None):
+    """spmspv whose skipping path keeps its partial sums in the library's fixed
+    device array (no allocation inside the call); same result, bitwise."""
+    lib = load()
+    n = x.shape[0]
+    xp, ldx = _dev2d(x, "x", cols=fmt.K)
+    y = _out(y, n, fmt.M, x)
+    yp, ldy = _dev2d(y, "y", rows=n, cols=fmt.M)
+    _check(lib.swm_spmspv_noalloc(fmt._h, xp, ldx, yp, ldy, n, _stream_ptr(stream)), "swm_spmspv_noalloc")
     return y
 
 

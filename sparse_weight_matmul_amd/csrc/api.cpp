@@ -436,6 +436,25 @@ swm_status swm_spmspv(const swm_format* f, const void* x, int64_t ldx, void* y, 
   return run_products(f, x, ldx, y, ldy, n, true, static_cast<hipStream_t>(stream));
 }
 
+swm_status swm_spmspv_noalloc(const swm_format* f, const void* x, int64_t ldx, void* y, int64_t ldy,
+                              int32_t n, void* stream) {
+  if (n < 1 || n > 16) return SWM_ERR_INVALID_ARG;
+  if (f && f->cr_mem && n <= 4) {
+    float* scr = nullptr;
+    size_t cap = 0;
+    SWM_HIP(swm::spmspv_scratch(&scr, &cap));
+    if (swm::colruns_partial_floats(f->cr.plan) > cap) return SWM_ERR_UNSUPPORTED;
+    if (!x || !y || ldx < f->h.k || ldy < f->h.m || ldx <= 0 || ldy <= 0) return SWM_ERR_INVALID_ARG;
+    if (!on_current_device(f)) return SWM_ERR_INVALID_ARG;
+    swm::DevColRuns c = f->cr;
+    c.partials = scr;
+    SWM_HIP(swm::launch_spmspv_cr(c, static_cast<const uint16_t*>(x), ldx, static_cast<uint16_t*>(y), ldy, n, 0.f,
+                                  static_cast<hipStream_t>(stream)));
+    return SWM_OK;
+  }
+  return run_products(f, x, ldx, y, ldy, n, true, static_cast<hipStream_t>(stream));
+}
+
 swm_status swm_spmspv_threshold(const swm_format* f, const void* x, int64_t ldx, void* y, int64_t ldy,
                                 int32_t n, float tau, void* stream) {
   if (!f || n < 1 || n > 16 || !(tau >= 0.f) || !(tau <= 65504.f)) return SWM_ERR_INVALID_ARG;

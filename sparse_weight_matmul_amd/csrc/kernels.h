@@ -54,6 +54,11 @@ struct DevColRuns {
   uint64_t bytes = 0;              // ptr + bits + values
 };
 ColRunsPlan plan_colruns(int64_t M, int64_t K);
+// Floats of per-workgroup partial sums one skipping call writes.
+size_t colruns_partial_floats(const ColRunsPlan& p);
+// Device address and size (floats) of the library's fixed partial-sum array
+// on the current device (resolved once per device).
+hipError_t spmspv_scratch(float** out, size_t* floats);
 // tau: activations with |x| < tau count as zero (0 = only exact zeros).
 hipError_t launch_spmspv_cr(const DevColRuns& c, const uint16_t* x, int64_t ldx, uint16_t* y, int64_t ldy,
                             int n, float tau, hipStream_t s);

@@ -46,6 +46,8 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <mutex>
+#include <vector>
 
 #include "kernels.h"
 
@@ -328,7 +330,37 @@ __global__ __launch_bounds__(256) void spmspv_cr_reduce(CrArgs a) {
   if (m < a.M) a.y[int64_t(t) * a.ldy + m] = __builtin_bit_cast(uint16_t, _Float16(sum));
 }
 
+// Partial sums of swm_spmspv_noalloc: a fixed device array in this code
+// object (each GPU that loads the library holds its own copy until the
+// process ends).  Host code never passes the array's name to a kernel: in
+// host code that name is a host-side stand-in, not a device address.  The
+// device address comes from hipGetSymbolAddress, taken once per device.
+constexpr size_t kScratchFloats = size_t(1) << 20;  // 4 MiB
+static __device__ __attribute__((aligned(256))) float scratch[kScratchFloats];
+
 }  // namespace
+
+hipError_t spmspv_scratch(float** out, size_t* floats) {
+  static std::mutex mu;
+  static std::vector<float*> ptrs;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> g(mu);
+  if (dev >= int(ptrs.size())) ptrs.resize(dev + 1, nullptr);
+  if (!ptrs[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    ptrs[dev] = static_cast<float*>(p);
+  }
+  *out = ptrs[dev];
+  *floats = kScratchFloats;
+  return hipSuccess;
+}
+
+size_t colruns_partial_floats(const ColRunsPlan& p) { return size_t(p.mb) * size_t(p.splits) * 4 * 256; }
 
 ColRunsPlan plan_colruns(int64_t M, int64_t K) {
   // about one workgroup per CU (256), at most kCrMaxCols columns each

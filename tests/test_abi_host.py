@@ -159,6 +159,7 @@ def test_null_handle_calls_are_rejected():
     assert lib.swm_format_query(None, ctypes.byref(inf)) == 1
     assert lib.swm_spmm(None, None, 1, None, 1, 1, None) == 1
     assert lib.swm_spmspv(None, None, 1, None, 1, 1, None) == 1
+    assert lib.swm_spmspv_noalloc(None, None, 1, None, 1, 1, None) == 1
     assert lib.swm_dense_gemm(None, 1, None, 1, None, 1, 1, 1, 1, None) == 1
     assert lib.swm_decompress(None, None, 1, None) == 1
     assert lib.swm_spmm_ws(None, None, 1, None, 1, 1024, None, 0, None) == 1
