@@ -448,6 +448,7 @@ def bench_spmspv(args, torch, swm, wl, G):
     M, K = W.shape
     _log(f"column-run encoding for {C} rotated copies")
     cr_bytes = [f.enable_skipping() for f in fmts]
+    resident = fmt_bytes(fmts[0].info) + cr_bytes[0]
     xd = torch.from_numpy(x).cuda()
     # the same activations before zeroing: the fused-threshold call drops |x| < tau itself
     x_raw = wl.silu_gated_sparse(wl.CFG_SPMSPV, 0, 4, K, 0.0)
@@ -461,7 +462,8 @@ def bench_spmspv(args, torch, swm, wl, G):
     out = {"metric": "decode spMspV HBM throughput on algorithmic bytes", "unit": "GB/s", "n_gpus": 1,
            "higher_is_better": True, "dtype": "f16", "data": "synthetic", "detail": {},
            "config": {"workload": "spMspV down_proj 4096x11008, 50% unstructured, x = SiLU(g)*u, |x| < tau zeroed",
-                      "tau": args.tau, "column_run_bytes": cr_bytes[0], "tiled_format_bytes": fb}}
+                      "tau": args.tau, "column_run_bytes": cr_bytes[0], "tiled_format_alg_bytes": fb,
+                      "resident_bytes_per_handle": resident, "dense_weight_bytes": 2 * M * K}}
     for n in (1, 2, 4):
         active = np.any(x[:n] != 0, axis=0)
         alg = int(run_bytes[:, active].sum()) + 2 * K * n + 2 * M * n
@@ -476,8 +478,11 @@ def bench_spmspv(args, torch, swm, wl, G):
         t_dense = G.time(G.capture([lambda i=i: swm.dense_gemm(Wds[i % CD], xd[:n], y) for i in range(CD)]), 3) / CD
         t_thr = G.time(G.capture([lambda i=i: swm.spmspv_threshold(fmts[i % C], xrd[:n], args.tau, y)
                                   for i in range(C)]), 3) / C
+        t_cr = G.time(G.capture([lambda i=i: swm.spmspv_threshold(fmts[i % C], xd[:n], 0.0, y)
+                                 for i in range(C)]), 3) / C
         out["detail"][str(n)] = {
-            "fused_threshold_us": t_thr * 1e3,
+            "fused_threshold_us": t_thr * 1e3, "column_run_kernel_us": t_cr * 1e3,
+            "spmspv_route": "column-run skipping kernel" if n <= 2 else "full product (tiled)",
             "zero_frac": float(np.mean(x[:n] == 0)), "inactive_cols": float(1 - active.mean()),
             "spmspv_us": t_skip * 1e3, "spmm_us": t_full * 1e3, "dense_us": t_dense * 1e3,
             "alg_bytes": alg, "spmspv_GBps_alg": alg / (t_skip * 1e-3) / 1e9,
@@ -715,12 +720,143 @@ def bench_wide(args, torch, swm, wl, G):
     return out
 
 
+# ------------------------------------------------------------------ batch-aware skipping experiment
+def group_tokens(zero, size, greedy=True, seed=0):
+    """Partition the tokens (rows of the boolean zero-pattern matrix) into
+    groups of `size`: greedy by the number of columns zero in every member
+    (the columns a group's skipping call can drop), or at random."""
+    T = zero.shape[0]
+    left = list(range(T))
+    if size == 1:
+        return [[t] for t in left]
+    if not greedy:
+        left = list(np.random.default_rng(seed).permutation(T))
+        return [left[i:i + size] for i in range(0, T, size)]
+    groups = []
+    while left:
+        best = None
+        for a in left:  # seed each group with the token pair sharing the most zeros
+            for b in left:
+                if a < b:
+                    c = int(np.count_nonzero(zero[a] & zero[b]))
+                    if best is None or c > best[0]:
+                        best = (c, [a, b])
+        g = best[1] if best else [left[0]]
+        common = np.logical_and.reduce(zero[g], axis=0)
+        while len(g) < size and len(g) < len(left):
+            c, t = max((int(np.count_nonzero(common & zero[t])), t) for t in left if t not in g)
+            g.append(t)
+            common &= zero[t]
+        groups.append(g)
+        left = [t for t in left if t not in g]
+    return groups
+
+
+def bench_batchskip(args, torch, swm, wl, G):
+    """Batch-aware skipping for 16 decode tokens on the down_proj shape
+    ("Reduced Matrix Multiplication" blog page, Sec. 6.2: group tokens by
+    channel pattern so skipping survives in a batch): the tokens are split
+    into groups (greedy by shared zero columns, or random) and every group
+    runs the column-run skipping kernel, each group reading the active runs
+    of W again; against one full product of all 16 tokens."""
+    _log("workload: batch-aware skipping, 16 tokens, down_proj 4096x11008")
+    T = 16
+    W, mask, _ = wl.spmspv_down(1, args.tau)
+    M, K = W.shape
+    fmts, fa = rotating_formats(swm, W, mask)
+    for f in fmts:
+        f.enable_skipping()
+    C = len(fmts)
+    x = wl.silu_gated_sparse(wl.CFG_SPMSPV, 1, T, K, args.tau)
+    zero = x == 0
+    xd = torch.from_numpy(x).cuda()
+    y = torch.empty((T, M), dtype=torch.float16, device="cuda")
+    out = {"metric": "batch-aware skipping: time for 16 decode tokens", "unit": "us", "n_gpus": 1,
+           "higher_is_better": False, "dtype": "f16", "data": "synthetic", "detail": {},
+           "config": {"workload": "down_proj 4096x11008 50%, 16 tokens of x = SiLU(g)*u with |x| < tau zeroed",
+                      "tau": args.tau, "zero_frac": float(zero.mean()),
+                      "inactive_cols_all16": float(np.logical_and.reduce(zero, axis=0).mean())}}
+    swm.spmm(fmts[0], xd, y)
+    torch.cuda.synchronize()
+    full = G.time(G.capture([lambda i=i: swm.spmm(fmts[i % C], xd, y) for i in range(C)]), 5) / C
+    out["detail"]["full product, N=16"] = {"us": full * 1e3, "calls": 1}
+    for size in (1, 2, 4):
+        for greedy in ((True, False) if size > 1 else (True,)):
+            groups = group_tokens(zero, size, greedy)
+            idx = [torch.tensor(g, device="cuda") for g in groups]
+            xs = [xd.index_select(0, t).contiguous() for t in idx]   # gathered once, outside the timing
+            ys = [torch.empty((len(g), M), dtype=torch.float16, device="cuda") for g in groups]
+            inact = [float(np.logical_and.reduce(zero[g], axis=0).mean()) for g in groups]
+
+            def run(i):
+                for xg, yg in zip(xs, ys):
+                    swm.spmspv_threshold(fmts[i % C], xg, 0.0, yg)
+            run(0)
+            torch.cuda.synchronize()
+            t = G.time(G.capture([lambda i=i: run(i) for i in range(C)]), 3) / C
+            name = f"groups of {size}" + ("" if size == 1 else (", greedy" if greedy else ", random"))
+            out["detail"][name] = {"us": t * 1e3, "calls": len(groups), "vs_full": full / t,
+                                   "mean_inactive_cols": float(np.mean(inact)),
+                                   "min_inactive_cols": float(np.min(inact)), "max_inactive_cols": float(np.max(inact))}
+            _log(f"{name}: {t * 1e3:.1f} us in {len(groups)} calls (full product {full * 1e3:.1f} us), "
+                 f"inactive columns per group {np.mean(inact):.3f}")
+    out["value"] = min(v["us"] for v in out["detail"].values())
+    return out
+
+
+# ------------------------------------------------------------------ decode across shapes (also the profiling driver)
+def bench_decodeshapes(args, torch, swm, wl, G):
+    """Decode SpMM on the layer's shapes (q_proj 4096x4096, up 11008x4096, down
+    4096x11008, 50%) at N = 1 and 16, each against the library's streaming
+    kernel at the same algorithmic byte count and rotation, and the dense
+    kernel.  Short: also the driver for kernel traces and counter passes."""
+    _log("workload: decode across the layer's shapes")
+    out = {"metric": "decode HBM throughput on algorithmic bytes across shapes", "unit": "GB/s", "n_gpus": 1,
+           "higher_is_better": True, "dtype": "f16", "data": "synthetic", "detail": {}}
+    reps = args.reps
+    for i, name in ((0, "q_proj 4096x4096"), (5, "up 11008x4096"), (6, "down 4096x11008")):
+        W, mask, X = wl.layer_linear(i, 16)
+        fmts, fa = rotating_formats(swm, W, mask)
+        Wds = rotating_dense(torch, W)
+        C, CD = len(fmts), len(Wds)
+        M, K = W.shape
+        Xd = torch.from_numpy(X).cuda()
+        for n in (1, 16):
+            y = torch.empty((n, M), dtype=torch.float16, device="cuda")
+            for f in fmts[:2]:
+                swm.spmm(f, Xd[:n], y)
+            swm.dense_gemm(Wds[0], Xd[:n], y)
+            torch.cuda.synchronize()
+            ds = pct(G.samples(G.capture([lambda i=i: swm.spmm(fmts[i % C], Xd[:n], y) for i in range(C)]), reps, C))
+            dd = pct(G.samples(G.capture([lambda i=i: swm.dense_gemm(Wds[i % CD], Xd[:n], y) for i in range(CD)]),
+                               reps, CD))
+            alg = fa + 2 * K * n + 2 * M * n
+            st = stream_achievable(torch, swm, G, alg) if not args.no_stream else None
+            e = {"sparse": ds, "dense": dd, "alg_bytes": alg,
+                 "GBps_alg": alg / (ds["median_us"] * 1e-6) / 1e9,
+                 "speedup_vs_dense": dd["median_us"] / ds["median_us"]}
+            if st:
+                e["stream"] = st
+                e["frac_of_stream"] = st["us"] / ds["median_us"]
+            out["detail"][f"{name} N={n}"] = e
+            _log(f"{name} N={n}: sparse {ds['median_us']:.2f} us ({e['GBps_alg']:.0f} GB/s), dense "
+                 f"{dd['median_us']:.2f} us" + (f", stream {st['us']:.2f} us" if st else ""))
+        del fmts, Wds
+        torch.cuda.empty_cache()
+    out["value"] = out["detail"]["q_proj 4096x4096 N=16"]["GBps_alg"]
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="decode", choices=["decode", "spmspv", "prefill", "layer", "wide", "mlp", "calib"])
+    ap.add_argument("--workload", default="decode",
+                    choices=["decode", "spmspv", "prefill", "layer", "wide", "mlp", "calib", "decodeshapes",
+                             "batchskip"])
+    ap.add_argument("--reps", type=int, default=20, help="graph replays per timing (decodeshapes)")
+    ap.add_argument("--no-stream", action="store_true", help="decodeshapes without the streaming-kernel sweep")
     ap.add_argument("--tau", type=float, default=0.3)
     ap.add_argument("--prefill-n", default="512,2048,4096")
     ap.add_argument("--prefill-s", default="0.5,0.6,0.7")
@@ -738,7 +874,8 @@ def main():
     torch.cuda.set_device(0)
     G = Graphs(torch)
     fn = {"decode": bench_default, "spmspv": bench_spmspv, "prefill": bench_prefill, "layer": bench_layer,
-          "wide": bench_wide, "mlp": bench_mlp, "calib": bench_calib}
+          "wide": bench_wide, "mlp": bench_mlp, "calib": bench_calib, "decodeshapes": bench_decodeshapes,
+          "batchskip": bench_batchskip}
     out = fn[args.workload](args, torch, swm, wl, G)
     out.setdefault("n_gpus", 1)
     print(json.dumps(out), flush=True)

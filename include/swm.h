@@ -78,11 +78,17 @@ typedef enum swm_status {
 /* Opaque compressed-weight handle (owns all of its device memory). */
 typedef struct swm_format swm_format;
 
-/* Tile shape.  tm: rows per tile, must be 16.  tk: columns per tile, a
- * multiple of 32 (the product kernels take 64).  NULL = {16, 64}. */
+/* Compress options (swm_tile_cfg.flags). */
+#define SWM_CFG_SKIPPING 1 /* also build the column-run encoding of swm_format_enable_skipping */
+
+/* Tile shape and compress options.  tm: rows per tile, must be 16.  tk:
+ * columns per tile, a multiple of 32 (the product kernels take 64).  flags:
+ * 0 or SWM_CFG_SKIPPING (other bits give SWM_ERR_INVALID_ARG); the host
+ * encoders (swm_encode_blob, swm_size_dry_run) ignore it.  NULL = {16, 64, 0}. */
 typedef struct swm_tile_cfg {
   int32_t tm;
   int32_t tk;
+  int32_t flags;
 } swm_tile_cfg;
 
 /* Sizes of a format; bytes_* are the sections of the export blob. */
@@ -112,6 +118,9 @@ typedef struct swm_format_info {
  *  (row b%16, column 32s + 8(b/16) + e).  Kept values are packed word by word,
  *  bit by bit (column by column), each tile run padded to 8 values; uint32
  *  exclusive prefix of run lengths per tile.
+ *  With cfg->flags = SWM_CFG_SKIPPING the handle also carries the column-run
+ *  encoding that lets swm_spmspv skip zero activations (the same as calling
+ *  swm_format_enable_skipping afterwards; the resident size roughly doubles).
  *  Synchronous: returns after the upload on `stream` has completed.
  *  *out receives a new handle owned by the caller (swm_format_destroy). */
 swm_status swm_sparse_compress(const uint16_t* W, int64_t ldw, const uint8_t* mask, int64_t ldm,
@@ -227,27 +236,31 @@ swm_status swm_gate_up_silu(const swm_format* g, const swm_format* u, const void
 /* spmspv: as swm_spmm for 1 <= n <= 16 tokens, for activations with zero
  * input channels (x[t][k] == +0 or -0 for all tokens t).  Such channels
  * contribute exact zeros, so the result equals swm_spmm's up to fp32
- * summation order.  Skipping is applied only where it pays: on the aligned
- * path (K % 8 == 0, 16-byte aligned x, ldx % 8 == 0) the full product is
- * computed, because a 16-row tile stores each column in at most 32 bytes and
- * packs four columns into each bitmap word, so dropping inactive columns
- * saves neither fetches nor decode work; the unaligned path skips the decode
- * of bitmap words whose four columns are all inactive.
- * When swm_format_enable_skipping has been called on f and n <= 4, the
- * column-run kernel runs instead: per 256-row block it builds the list of
- * active input columns (any of the n tokens nonzero) and reads and decodes
- * only their runs, bitmaps and pointers, then a second launch adds the
- * column ranges' partial sums in a fixed order; results are bitwise
- * reproducible and equal the full product up to fp32 summation order.  That
- * path uses the handle's workspace: calls on one handle must be ordered on
- * one stream.  It pays when most columns are inactive: measured on one
- * MI355X for a 4096 x 11008 weight at 50% and one token, it is 1.1x faster
- * than the full product at 70% inactive columns, 1.4x at 86% and 1.5x at
- * 92%; with four tokens it breaks even at about 74%.  With fewer inactive
- * columns it is slower, so enable it only for such inputs. 
+ * summation order.
  * Source: SPDP abstract (input-adaptive dynamic pruning; run-time activation
  * skipping in the spMspV kernel); "Reduced Matrix Multiplication" blog page,
- * Sec. 4.2 (an FFN down projection multiplies only the kept channels). */
+ * Sec. 4.2 (an FFN down projection multiplies only the kept channels).
+ *  Which kernel runs:
+ *  - the handle carries the column-run encoding (SWM_CFG_SKIPPING at
+ *    compress time, or swm_format_enable_skipping) and n <= 2: the skipping
+ *    kernel.  Per 256-row block it lists the active input columns (any of the
+ *    n tokens nonzero) and reads and decodes only their runs, bitmaps and
+ *    pointers; a second launch adds the column ranges' partial sums in a
+ *    fixed order (bitwise reproducible).  It uses the handle's workspace:
+ *    skipping calls on one handle must be ordered on one stream.  Measured on
+ *    one MI355X (4096 x 11008 at 50%, one token): 1.1x faster than the full
+ *    product at 70% inactive columns, 1.4x at 86%, 1.5x at 92%; it breaks
+ *    even near 65% at one token and near 74% at two to four;
+ *  - otherwise the full product on the tiled format (swm_spmm's kernels):
+ *    with three or more tokens the columns inactive in every token are too
+ *    few, and the column-run decode costs 1.5-2.3x the vector instructions
+ *    per position of the tiled one.  On the aligned path (K % 8 == 0,
+ *    16-byte aligned x, ldx % 8 == 0) nothing is skipped: a 16-row tile
+ *    stores each column in at most 32 bytes and packs four columns into each
+ *    bitmap word, so dropping inactive columns saves neither fetches nor
+ *    decode work; the unaligned path skips the decode of bitmap words whose
+ *    four columns are all inactive.
+ *  swm_spmspv_threshold runs the skipping kernel for up to 4 tokens. */
 swm_status swm_spmspv(const swm_format* f, const void* x, int64_t ldx, void* y, int64_t ldy,
                       int32_t n, void* stream);
 
@@ -258,7 +271,7 @@ swm_status swm_spmspv(const swm_format* f, const void* x, int64_t ldx, void* y, 
  * in a fixed array of 4 MiB compiled into the library (each GPU the library
  * runs on holds its own copy until the process ends) instead of the handle's
  * workspace.  The call allocates and frees nothing.
- *  The skipping path (swm_format_enable_skipping called on f, n <= 4) needs
+ *  The skipping path (column-run encoding on f, n <= 2) needs
  *  ceil(M/256) * S * 4 * 256 floats of partials (S column splits of the
  *  handle; 1 MiB for a 4096 x 11008 weight); a handle that needs more than
  *  the 4 MiB array gives SWM_ERR_UNSUPPORTED and launches nothing.  Every
@@ -280,8 +293,9 @@ swm_status swm_spmspv_noalloc(const swm_format* f, const void* x, int64_t ldx, v
  * kernel); "Reduced Matrix Multiplication" blog page, Sec. 4.2 (an FFN keeps
  * only the high-response channels of its hidden activation and multiplies
  * them with the matching part of the down projection).
- *  Runs on the column-run path only: swm_format_enable_skipping must have been
- *  called on f and 1 <= n <= 4, else SWM_ERR_UNSUPPORTED (nothing launched).
+ *  Runs on the column-run path only: f must carry the column-run encoding
+ *  (SWM_CFG_SKIPPING or swm_format_enable_skipping) and 1 <= n <= 4, else
+ *  SWM_ERR_UNSUPPORTED (nothing launched).
  *  Same buffers, ownership, ordering and errors as swm_spmspv; tau < 0, NaN
  *  or above 65504 gives SWM_ERR_INVALID_ARG. */
 swm_status swm_spmspv_threshold(const swm_format* f, const void* x, int64_t ldx, void* y, int64_t ldy,

@@ -29,8 +29,11 @@ STATUS = {
 _i64, _u64, _i32, _sz, _vp = ctypes.c_int64, ctypes.c_uint64, ctypes.c_int32, ctypes.c_size_t, ctypes.c_void_p
 
 
+SWM_CFG_SKIPPING = 1
+
+
 class TileCfg(ctypes.Structure):
-    _fields_ = [("tm", ctypes.c_int32), ("tk", ctypes.c_int32)]
+    _fields_ = [("tm", ctypes.c_int32), ("tk", ctypes.c_int32), ("flags", ctypes.c_int32)]
 
 
 class FormatInfo(ctypes.Structure):
@@ -104,10 +107,11 @@ def _check(code: int, where: str):
         raise SwmError(code, where)
 
 
-def _cfg(tile):
-    if tile is None:
+def _cfg(tile, flags=0):
+    if tile is None and not flags:
         return None
-    c = TileCfg(int(tile[0]), int(tile[1]))
+    tm, tk = tile if tile is not None else (16, 64)
+    c = TileCfg(int(tm), int(tk), int(flags))
     return ctypes.byref(c)
 
 
@@ -198,14 +202,17 @@ class Format:
             pass
 
 
-def sparse_compress(W, mask=None, tile=(16, 64), stream=None) -> Format:
-    """Compress a host fp16 W (M, K) with an optional host mask; upload to the current device."""
+def sparse_compress(W, mask=None, tile=(16, 64), stream=None, skipping=False) -> Format:
+    """Compress a host fp16 W (M, K) with an optional host mask; upload to the
+    current device.  skipping=True also builds the column-run encoding that
+    lets spmspv skip zero activations (SWM_CFG_SKIPPING)."""
     lib = load()
     w = _host_u16(W)
     m = _host_mask(mask, w.shape)
     h = ctypes.c_void_p()
     code = lib.swm_sparse_compress(w.ctypes.data, w.shape[1], None if m is None else m.ctypes.data,
-                                   w.shape[1], w.shape[0], w.shape[1], _cfg(tile), _stream_ptr(stream),
+                                   w.shape[1], w.shape[0], w.shape[1],
+                                   _cfg(tile, SWM_CFG_SKIPPING if skipping else 0), _stream_ptr(stream),
                                    ctypes.byref(h))
     _check(code, "swm_sparse_compress")
     return Format(h)
@@ -322,7 +329,8 @@ def gate_up_silu(gate: Format, up: Format, X, tau: float = 0.0, H=None, stream=N
 
 
 def spmspv(fmt: Format, x, y=None, stream=None):
-    """Zero-activation-skipping product for 1..16 tokens; x (n, K), y (n, M)."""
+    """Zero-activation-skipping product for 1..16 tokens; x (n, K), y (n, M).
+    Skips on the column-run encoding for n <= 2 when the handle carries it."""
     lib = load()
     n = x.shape[0]
     xp, ldx = _dev2d(x, "x", cols=fmt.K)

@@ -153,6 +153,16 @@ def test_encoder_rejects_bad_arguments():
     assert size.value == 64 + 4
 
 
+def test_compress_rejects_unknown_flags():
+    # flag bits other than SWM_CFG_SKIPPING are refused before any encoding or upload
+    lib = swm.load()
+    W = np.ones((4, 4), dtype=np.float16)
+    h = ctypes.c_void_p()
+    cfg = swm.TileCfg(16, 64, 2)
+    assert lib.swm_sparse_compress(W.ctypes.data, 4, None, 4, 4, 4, ctypes.byref(cfg), None, ctypes.byref(h)) == 1
+    assert not h.value
+
+
 def test_null_handle_calls_are_rejected():
     lib = swm.load()
     inf = swm.FormatInfo()

@@ -245,17 +245,45 @@ def down_skip(gpu_lib, down):
 
 @pytest.mark.parametrize("n", [1, 2, 3, 4])
 def test_spmspv_skip_down(gpu_lib, down_skip, n):
+    # n <= 2: the skipping kernel; n = 3, 4: the full product on the tiled
+    # format.  The skipping kernel itself serves up to four tokens through
+    # spmspv_threshold with tau = 0 (the same activations, nothing dropped).
     W, mask, x, g = down_skip
+    ref = oracle.masked_matmul_skip(W, mask, x[:n])
     y = _np(gpu_lib.spmspv(g, _t(x[:n])))
-    assert_close(y, oracle.masked_matmul_skip(W, mask, x[:n]), f"spmspv skip n={n}")
+    assert_close(y, ref, f"spmspv n={n}")
+    yc = _np(gpu_lib.spmspv_threshold(g, _t(x[:n]), 0.0))
+    assert_close(yc, ref, f"column-run kernel n={n}")
+    if n <= 2:
+        assert np.array_equal(y.view(np.uint16), yc.view(np.uint16))
+    else:
+        assert np.array_equal(y.view(np.uint16), _np(gpu_lib.spmm(g, _t(x[:n]))).view(np.uint16))
+
+
+def test_compress_with_skipping_flag(gpu_lib, down):
+    # SWM_CFG_SKIPPING at compress time gives the same handle as
+    # enable_skipping afterwards: same encoding size, bitwise the same results
+    W, mask, x, f = down
+    h = gpu_lib.sparse_compress(W, mask, skipping=True)
+    g = gpu_lib.sparse_compress(W, mask)
+    nb = g.enable_skipping()
+    assert h.enable_skipping() == nb  # already attached: idempotent, same size
+    for n in (1, 2):
+        a = _np(gpu_lib.spmspv(h, _t(x[:n]))).view(np.uint16)
+        b = _np(gpu_lib.spmspv(g, _t(x[:n]))).view(np.uint16)
+        assert np.array_equal(a, b)
+        assert_close(a.view(np.float16), oracle.masked_matmul_skip(W, mask, x[:n]), f"flag n={n}")
+    assert h.export() == f.export()  # the tiled format is unchanged
 
 
 def test_spmspv_skip_repeatable_and_deterministic(gpu_lib, down_skip):
     # every sum runs in a fixed order: calls in a row agree bitwise
     W, mask, x, g = down_skip
     xs = _t(x[:4])
-    ys = [_np(gpu_lib.spmspv(g, xs)).view(np.uint16) for _ in range(3)]
+    ys = [_np(gpu_lib.spmspv_threshold(g, xs, 0.0)).view(np.uint16) for _ in range(3)]
     assert np.array_equal(ys[0], ys[1]) and np.array_equal(ys[0], ys[2])
+    y2 = [_np(gpu_lib.spmspv(g, _t(x[:2]))).view(np.uint16) for _ in range(2)]
+    assert np.array_equal(y2[0], y2[1])
     y1 = _np(gpu_lib.spmspv(g, _t(x[:1])))  # n changes between calls on one handle
     assert_close(y1, oracle.masked_matmul_skip(W, mask, x[:1]), "after n=4")
 
@@ -292,7 +320,11 @@ def test_spmspv_skip_zero_dense_and_fallback(gpu_lib, down_skip):
     W, mask, x, g = down_skip
     z = np.zeros((3, W.shape[1]), dtype=np.float16)
     z[1, 7] = np.float16(-0.0)
-    assert np.all(_np(gpu_lib.spmspv(g, _t(z))).view(np.uint16) == 0)  # nothing active: +0 everywhere
+    # nothing active: +0 everywhere, through the skipping kernel (n = 2, and
+    # n = 3 via the threshold call) and the full product (n = 3)
+    assert np.all(_np(gpu_lib.spmspv(g, _t(z[:2]))).view(np.uint16) == 0)
+    assert np.all(_np(gpu_lib.spmspv_threshold(g, _t(z), 0.0)).view(np.uint16) == 0)
+    assert np.all(_np(gpu_lib.spmspv(g, _t(z))) == 0)
     xd = np.random.default_rng(6).standard_normal((4, W.shape[1])).astype(np.float16)
     assert_close(_np(gpu_lib.spmspv(g, _t(xd))), oracle.masked_matmul(W, mask, xd), "all columns active")
     x5 = x[:4].copy()
@@ -309,12 +341,19 @@ def test_spmspv_threshold_down(gpu_lib, down_skip, n):
     y = _np(gpu_lib.spmspv_threshold(g, _t(x_raw), 0.3))
     assert_close(y, oracle.masked_matmul_threshold(W, mask, x_raw, 0.3), f"threshold n={n}")
     # same active list and values as zeroing x first: bitwise the same result
-    y0 = _np(gpu_lib.spmspv(g, _t(x_zeroed[:n])))
+    # (through the same kernel; swm_spmspv takes it for n <= 2)
+    y0 = _np(gpu_lib.spmspv_threshold(g, _t(x_zeroed[:n]), 0.0))
     assert np.array_equal(y.view(np.uint16), y0.view(np.uint16))
-    # tau = 0 is the plain call; tau above every |x| gives zeros
+    if n <= 2:
+        assert np.array_equal(y.view(np.uint16), _np(gpu_lib.spmspv(g, _t(x_zeroed[:n]))).view(np.uint16))
+    # tau = 0 is the plain call (bitwise where swm_spmspv runs the same
+    # kernel); tau above every |x| gives zeros
     ya = _np(gpu_lib.spmspv_threshold(g, _t(x_raw), 0.0))
     yb = _np(gpu_lib.spmspv(g, _t(x_raw)))
-    assert np.array_equal(ya.view(np.uint16), yb.view(np.uint16))
+    if n <= 2:
+        assert np.array_equal(ya.view(np.uint16), yb.view(np.uint16))
+    assert_close(ya, oracle.masked_matmul(W, mask, x_raw), f"threshold 0 n={n}")
+    assert_close(yb, oracle.masked_matmul(W, mask, x_raw), f"spmspv n={n}")
     assert np.all(_np(gpu_lib.spmspv_threshold(g, _t(x_raw), 1e4)).view(np.uint16) == 0)
 
 
@@ -347,9 +386,10 @@ def test_spmspv_skip_ragged(gpu_lib, M, K, density, n, zero_frac):
     mask = g.random((M, K)) < density
     x = g.standard_normal((n, K)).astype(np.float16)
     x[:, g.random(K) < zero_frac] = 0  # whole input channels off, as after an activation threshold
-    f = gpu_lib.sparse_compress(W, mask)
-    f.enable_skipping()
-    assert_close(_np(gpu_lib.spmspv(f, _t(x))), oracle.masked_matmul_skip(W, mask, x), f"{M}x{K} n={n}")
+    f = gpu_lib.sparse_compress(W, mask, skipping=True)
+    ref = oracle.masked_matmul_skip(W, mask, x)
+    assert_close(_np(gpu_lib.spmspv(f, _t(x))), ref, f"{M}x{K} n={n}")
+    assert_close(_np(gpu_lib.spmspv_threshold(f, _t(x), 0.0)), ref, f"column-run kernel {M}x{K} n={n}")
 
 
 def test_spmspv_skip_strided(gpu_lib):

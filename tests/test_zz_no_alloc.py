@@ -31,21 +31,21 @@ def _close(Y, ref, what):
 
 def test_noalloc_matches_spmspv_two_calls_second_smaller(gpu_lib):
     swm = gpu_lib
-    # first call: down_proj 4096x11008 at 50%, SiLU-gated x (about 70% zeros), n = 4
-    W, mask, x = wl.spmspv_down(4, 0.3)
-    f = swm.sparse_compress(W, mask)
-    f.enable_skipping()
+    # first call: down_proj 4096x11008 at 50%, SiLU-gated x (about 70% zeros),
+    # n = 2 (the skipping kernel serves up to two tokens)
+    W, mask, x = wl.spmspv_down(2, 0.3)
+    f = swm.sparse_compress(W, mask, skipping=True)
     xd = _t(x)
     a = _np(swm.spmspv(f, xd)).view(np.uint16)
     b = _np(swm.spmspv_noalloc(f, xd)).view(np.uint16)
     assert np.array_equal(a, b)
-    _close(b.view(np.float16), oracle.masked_matmul_skip(W, mask, x), "down n=4")
-    # second call, smaller: 300 x 700 weight, n = 2 (fewer row blocks and
+    _close(b.view(np.float16), oracle.masked_matmul_skip(W, mask, x), "down n=2")
+    # second call, smaller: 300 x 700 weight, n = 1 (fewer row blocks and
     # splits: the array keeps the first call's partials beyond this call's)
     g = np.random.default_rng(41)
     W2 = (0.02 * g.standard_normal((300, 700))).astype(np.float16)
     m2 = g.random((300, 700)) < 0.5
-    x2 = g.standard_normal((2, 700)).astype(np.float16)
+    x2 = g.standard_normal((1, 700)).astype(np.float16)
     x2[:, g.random(700) < 0.6] = 0
     f2 = swm.sparse_compress(W2, m2)
     f2.enable_skipping()
@@ -53,8 +53,8 @@ def test_noalloc_matches_spmspv_two_calls_second_smaller(gpu_lib):
     a2 = _np(swm.spmspv(f2, x2d)).view(np.uint16)
     b2 = _np(swm.spmspv_noalloc(f2, x2d)).view(np.uint16)
     assert np.array_equal(a2, b2)
-    _close(b2.view(np.float16), oracle.masked_matmul_skip(W2, m2, x2), "300x700 n=2")
-    # the tiled path (skipping not enabled, or n > 4) is swm_spmspv's too
+    _close(b2.view(np.float16), oracle.masked_matmul_skip(W2, m2, x2), "300x700 n=1")
+    # the tiled path (no column-run encoding, or n > 2) is swm_spmspv's too
     h = swm.sparse_compress(W2, m2)
     assert np.array_equal(_np(swm.spmspv_noalloc(h, x2d)).view(np.uint16), _np(swm.spmspv(h, x2d)).view(np.uint16))
 
