@@ -720,6 +720,60 @@ def bench_wide(args, torch, swm, wl, G):
     return out
 
 
+# ------------------------------------------------------------------ prefill on the sparse matrix cores
+def bench_smfmac(args, torch, swm, wl, G):
+    """The 2:4 + residual route (compact W into the 2:4 operand layout once
+    per call, then v_smfmac) against the expansion route (expand W to dense,
+    then the dense MFMA kernel) and the dense kernel on W (.) mask: q_proj
+    4096x4096 with a 2:4 mask (no residual layer) and up/gate 11008x4096 at
+    50/60/70% forced onto the route with its residual layer."""
+    _log("workload: prefill on the sparse matrix cores")
+    out = {"metric": "prefill useful TFLOP/s on the sparse matrix cores", "unit": "TFLOP/s", "n_gpus": 1,
+           "higher_is_better": True, "dtype": "f16", "data": "synthetic", "detail": {}}
+    reps = 4
+    cases = [("q_proj 2:4", wl.decode_qproj_2_4(1)[:2], (4096,) if args.quick else (1024, 2048, 4096))]
+    for sp in (() if args.quick else (0.5, 0.6, 0.7)):
+        W, mask, _ = wl.prefill_upgate(sp, 1)
+        cases.append((f"up/gate {int(sp * 100)}%", (W, mask), (2048, 4096)))
+    Xall = torch.from_numpy(wl.activations(wl.CFG_PREFILL, 0, 4096, 11008)).cuda()
+    for name, (W, mask), Ns in cases:
+        M, K = W.shape
+        nnz = int(mask.sum())
+        f = swm.sparse_compress(W, mask, smfmac=True)
+        Wd = torch.from_numpy(W).cuda()
+        Wx = torch.empty_like(Wd)
+        for n in Ns:
+            X = Xall[:n, :K].contiguous()
+            y = torch.empty((n, M), dtype=torch.float16, device="cuda")
+            ws = torch.empty(max(swm.spmm_workspace_bytes(f, n), 256), dtype=torch.uint8, device="cuda")
+            def route():
+                swm.spmm_ws(f, X, ws, y)
+            def expand():
+                swm.decompress(f, Wx)
+                swm.dense_gemm(Wx, X, y)
+            def dense():
+                swm.dense_gemm(Wd, X, y)
+            for fn in (route, expand, dense):
+                fn()
+            torch.cuda.synchronize()
+            t = {nm: pct(G.samples(G.capture([fn] * reps), 8, reps))["median_us"]
+                 for nm, fn in (("smfmac_route", route), ("expand_route", expand), ("dense", dense))}
+            useful = 2.0 * nnz * n
+            e = {k + "_us": v for k, v in t.items()}
+            e.update({"useful_TFLOPs": useful / (t["smfmac_route"] * 1e-6) / 1e12,
+                      "speedup_vs_dense": t["dense"] / t["smfmac_route"],
+                      "speedup_vs_expand": t["expand_route"] / t["smfmac_route"],
+                      "workspace_bytes": int(ws.numel())})
+            out["detail"][f"{name} N={n}"] = e
+            _log(f"{name} N={n}: smfmac route {t['smfmac_route']:.1f} us, expand route {t['expand_route']:.1f} us, "
+                 f"dense {t['dense']:.1f} us")
+            del ws, y
+        del f, Wd, Wx
+        torch.cuda.empty_cache()
+    out["value"] = out["detail"]["q_proj 2:4 N=4096"]["useful_TFLOPs"]
+    return out
+
+
 # ------------------------------------------------------------------ batch-aware skipping experiment
 def group_tokens(zero, size, greedy=True, seed=0):
     """Partition the tokens (rows of the boolean zero-pattern matrix) into
@@ -854,9 +908,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="decode",
                     choices=["decode", "spmspv", "prefill", "layer", "wide", "mlp", "calib", "decodeshapes",
-                             "batchskip"])
+                             "batchskip", "smfmac"])
     ap.add_argument("--reps", type=int, default=20, help="graph replays per timing (decodeshapes)")
     ap.add_argument("--no-stream", action="store_true", help="decodeshapes without the streaming-kernel sweep")
+    ap.add_argument("--quick", action="store_true", help="smfmac: only q_proj 2:4 at N = 4096 (profiling driver)")
     ap.add_argument("--tau", type=float, default=0.3)
     ap.add_argument("--prefill-n", default="512,2048,4096")
     ap.add_argument("--prefill-s", default="0.5,0.6,0.7")
@@ -875,7 +930,7 @@ def main():
     G = Graphs(torch)
     fn = {"decode": bench_default, "spmspv": bench_spmspv, "prefill": bench_prefill, "layer": bench_layer,
           "wide": bench_wide, "mlp": bench_mlp, "calib": bench_calib, "decodeshapes": bench_decodeshapes,
-          "batchskip": bench_batchskip}
+          "batchskip": bench_batchskip, "smfmac": bench_smfmac}
     out = fn[args.workload](args, torch, swm, wl, G)
     out.setdefault("n_gpus", 1)
     print(json.dumps(out), flush=True)

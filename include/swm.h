@@ -51,7 +51,9 @@
  *    SWM_DENSE_WAVES_PER_CU (streaming dense kernel), SWM_DENSE_BLOCK = 1 / 2
  *    / 3 (tiled dense block 256x256 / 256x128 / 128x128), SWM_EXPAND_MIN_N
  *    (tokens from which swm_spmm_ws expands W, at least 33; read once),
- *    SWM_GLU_TPW (tiles per wave of swm_gate_up_silu; read once).
+ *    SWM_GLU_TPW (tiles per wave of swm_gate_up_silu; read once), SWM_SMFMAC
+ *    (0 / 1: the sparse-matrix-core prefill route off / for every handle;
+ *    read once).
  */
 #ifndef SWM_H_
 #define SWM_H_
@@ -80,11 +82,13 @@ typedef struct swm_format swm_format;
 
 /* Compress options (swm_tile_cfg.flags). */
 #define SWM_CFG_SKIPPING 1 /* also build the column-run encoding of swm_format_enable_skipping */
+#define SWM_CFG_SMFMAC 2   /* swm_spmm_ws takes the sparse-matrix-core route (see swm_spmm_ws) */
 
 /* Tile shape and compress options.  tm: rows per tile, must be 16.  tk:
  * columns per tile, a multiple of 32 (the product kernels take 64).  flags:
- * 0 or SWM_CFG_SKIPPING (other bits give SWM_ERR_INVALID_ARG); the host
- * encoders (swm_encode_blob, swm_size_dry_run) ignore it.  NULL = {16, 64, 0}. */
+ * 0 or a combination of SWM_CFG_SKIPPING and SWM_CFG_SMFMAC (other bits give
+ * SWM_ERR_INVALID_ARG); the host encoders (swm_encode_blob, swm_size_dry_run)
+ * ignore it.  NULL = {16, 64, 0}. */
 typedef struct swm_tile_cfg {
   int32_t tm;
   int32_t tk;
@@ -178,7 +182,8 @@ swm_status swm_spmm(const swm_format* f, const void* X, int64_t ldx, void* Y, in
                     int64_t N, void* stream);
 
 /* Bytes of device workspace swm_spmm_ws uses for N tokens on the current
- * device: M*K*2 rounded up to 256 when that call would expand W (K a
+ * device: M*K*2 rounded up to 256 when that call would expand W (on the
+ * sparse-matrix-core route the compacted layers' size instead) (K a
  * multiple of 8, and N >= 1024, or N >= 256 with the on-chip prefill
  * kernel's ceil(M/128)*ceil(N/256) blocks at most half the CUs or above one
  * round of them), else 0.  The SWM_EXPAND_MIN_N environment variable, read
@@ -197,6 +202,21 @@ size_t swm_spmm_workspace_bytes(const swm_format* f, int64_t N);
  * swm_decompress) and runs the library's dense MFMA kernel on it: two
  * launches on stream, the second reading what the first wrote.  Otherwise it
  * runs swm_spmm's kernels and leaves the workspace untouched.
+ *  Sparse-matrix-core route (handles compressed with SWM_CFG_SMFMAC, or
+ *  every handle when the SWM_SMFMAC environment variable is 1; 0 turns it
+ *  off): where this call would expand W, it instead compacts W (.) mask into a
+ *  2:4 layer (in every aligned group of 4 columns of a row, the first two
+ *  kept entries) and, when some row keeps 3 or 4 of a group, a residual layer
+ *  with the rest, each as values [M][Kp/2] fp16 plus 2-bit positions
+ *  [M][Kp/16] uint16 (Kp = K rounded up to 64; M*Kp*1.125 bytes per layer),
+ *  and multiplies both with v_smfmac_f32_32x32x32_f16 into one fp32
+ *  accumulator (moderate-sparsity page, abstract and Sec. 1: a
+ *  sparse-tensor-core layer plus a residual layer).  The result is the same
+ *  product (fp32 summation order differs).  Measured on one MI355X it does not
+ *  beat the expansion route (q_proj 4096x4096 with a 2:4 mask, N = 4096:
+ *  138.5 against 145 us), hence opt-in.  The activations must fit 32-bit
+ *  byte offsets ((N-1)*ldx + K < 2^31) and M*Kp < 2^32; otherwise the call
+ *  expands as usual.
  *  workspace: DEVICE, 16-byte aligned, ws_bytes >= swm_spmm_workspace_bytes(f,
  *  N), owned by the caller, contents undefined afterwards; it may be shared by
  *  the handles of several layers as long as the calls are ordered on one

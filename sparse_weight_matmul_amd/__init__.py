@@ -30,6 +30,7 @@ _i64, _u64, _i32, _sz, _vp = ctypes.c_int64, ctypes.c_uint64, ctypes.c_int32, ct
 
 
 SWM_CFG_SKIPPING = 1
+SWM_CFG_SMFMAC = 2
 
 
 class TileCfg(ctypes.Structure):
@@ -202,17 +203,20 @@ class Format:
             pass
 
 
-def sparse_compress(W, mask=None, tile=(16, 64), stream=None, skipping=False) -> Format:
+def sparse_compress(W, mask=None, tile=(16, 64), stream=None, skipping=False, smfmac=False) -> Format:
     """Compress a host fp16 W (M, K) with an optional host mask; upload to the
     current device.  skipping=True also builds the column-run encoding that
-    lets spmspv skip zero activations (SWM_CFG_SKIPPING)."""
+    lets spmspv skip zero activations (SWM_CFG_SKIPPING); smfmac=True makes
+    spmm_ws take the sparse-matrix-core route even when the mask needs a
+    residual layer (SWM_CFG_SMFMAC)."""
     lib = load()
     w = _host_u16(W)
     m = _host_mask(mask, w.shape)
     h = ctypes.c_void_p()
     code = lib.swm_sparse_compress(w.ctypes.data, w.shape[1], None if m is None else m.ctypes.data,
                                    w.shape[1], w.shape[0], w.shape[1],
-                                   _cfg(tile, SWM_CFG_SKIPPING if skipping else 0), _stream_ptr(stream),
+                                   _cfg(tile, (SWM_CFG_SKIPPING if skipping else 0) | (SWM_CFG_SMFMAC if smfmac else 0)),
+                                   _stream_ptr(stream),
                                    ctypes.byref(h))
     _check(code, "swm_sparse_compress")
     return Format(h)

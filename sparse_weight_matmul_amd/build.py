@@ -21,7 +21,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libswm.so")
 
-SOURCES = ["format.cpp", "colruns.cpp", "api.cpp", "decode.hip", "prefill.hip", "spmspv.hip"]
+SOURCES = ["format.cpp", "colruns.cpp", "api.cpp", "decode.hip", "prefill.hip", "spmspv.hip", "smfmac.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

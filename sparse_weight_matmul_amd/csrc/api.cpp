@@ -25,6 +25,8 @@ struct swm_format {
   swm::DecodePlan plan_pair;  // 16 < N <= 32 (two token groups, looped kernel)
   void* cr_mem = nullptr;  // column-run encoding for activation skipping (optional)
   swm::DevColRuns cr;
+  bool res24 = true;       // some row keeps 3 or 4 of an aligned group of 4 columns
+  bool smf_force = false;  // SWM_CFG_SMFMAC: the sparse-matrix-core route also with a residual layer
 };
 
 namespace {
@@ -76,6 +78,7 @@ swm_status upload(std::vector<uint8_t>&& blob, const swm::Header& h, hipStream_t
   f->plan = swm::plan_decode(h, tp, num_cus(f->device), 64, true);
   f->plan_wide = swm::plan_decode(h, tp, num_cus(f->device), 32, true);
   f->plan_pair = swm::plan_decode(h, tp, num_cus(f->device), 32, false);
+  f->res24 = swm::mask_exceeds_2_of_4(h, f->blob.data());
   const size_t T = h.tiles();
   const size_t b_tp = 4 * (T + 1), b_bits = 8 * h.n_bits(), b_vals = 2 * h.padded_len + 1024;
   const size_t n_zero = size_t(h.kt) * h.tk + 64;
@@ -166,7 +169,7 @@ swm_status swm_sparse_compress(const uint16_t* W, int64_t ldw, const uint8_t* ma
                                int64_t M, int64_t K, const swm_tile_cfg* cfg, void* stream,
                                swm_format** out) {
   if (!out) return SWM_ERR_INVALID_ARG;
-  if (cfg && (cfg->flags & ~int32_t(SWM_CFG_SKIPPING))) return SWM_ERR_INVALID_ARG;
+  if (cfg && (cfg->flags & ~int32_t(SWM_CFG_SKIPPING | SWM_CFG_SMFMAC))) return SWM_ERR_INVALID_ARG;
   std::vector<uint8_t> blob;
   swm_status st = swm::encode_blob(W, ldw, mask, ldm, M, K, cfg, &blob);
   if (st != SWM_OK) return st;
@@ -176,6 +179,7 @@ swm_status swm_sparse_compress(const uint16_t* W, int64_t ldw, const uint8_t* ma
   swm_format* f = nullptr;
   st = upload(std::move(blob), h, static_cast<hipStream_t>(stream), &f);
   if (st != SWM_OK) return st;
+  f->smf_force = cfg && (cfg->flags & SWM_CFG_SMFMAC);
   if (cfg && (cfg->flags & SWM_CFG_SKIPPING)) {
     st = swm_format_enable_skipping(f, stream, nullptr);
     if (st != SWM_OK) {
@@ -404,8 +408,35 @@ static bool expand_route(const swm::Header& h, int64_t N) {
   return 2 * blocks <= cus || blocks > cus;
 }
 
+// The sparse-matrix-core route (compact W into a 2:4 layer, plus a residual
+// layer where the mask needs one, then v_smfmac), taken where the expansion
+// route would be, for handles compressed with SWM_CFG_SMFMAC (or every
+// handle with SWM_SMFMAC = 1; SWM_SMFMAC = 0 turns it off; read once).  It
+// is opt-in because on this chip it does not beat the expansion route: on
+// q_proj 4096x4096 with a 2:4 mask the SMFMAC kernel issues half the matrix
+// instructions of the dense kernel but is bound by LDS bandwidth (each step
+// reads the same activation fragments in half the matrix time), 126 against
+// 134 us at N = 4096, and with the compaction (21 us) the route is 138.5 us
+// against 145 us for the expansion route and 131 us dense; at N = 1024-2048
+// it is slower.  With a residual layer it runs twice the instructions.
+static int smfmac_mode() {
+  static const int v = [] {
+    const char* e = getenv("SWM_SMFMAC");
+    return e ? atoi(e) : -1;
+  }();
+  return v;
+}
+
+static bool smf_route(const swm_format* f, int64_t N) {
+  if (f->h.tm != 16 || f->h.tk != 64 || !expand_route(f->h, N)) return false;
+  const int mode = smfmac_mode();
+  if (mode == 0) return false;
+  return mode == 1 || f->smf_force;
+}
+
 size_t swm_spmm_workspace_bytes(const swm_format* f, int64_t N) {
   if (!f || !expand_route(f->h, N)) return 0;
+  if (smf_route(f, N)) return swm::sparse24_layout(f->h, f->res24).bytes;
   return align_up(size_t(f->h.m) * size_t(f->h.k) * 2, 256);
 }
 
@@ -423,6 +454,13 @@ swm_status swm_spmm_ws(const swm_format* f, const void* X, int64_t ldx, void* Y,
   swm_status st = check_tile_supported(f->h);
   if (st != SWM_OK) return st;
   if (!on_current_device(f)) return SWM_ERR_INVALID_ARG;
+  if (smf_route(f, N) && swm::smf_fits(f->h, N, ldx)) {
+    const swm::Sparse24Layout L = swm::sparse24_layout(f->h, f->res24);
+    SWM_HIP(swm::launch_compact24(f->d, L, f->res24, workspace, s));
+    SWM_HIP(swm::launch_smf(f->h, L, f->res24, workspace, static_cast<const uint16_t*>(X), ldx,
+                            static_cast<uint16_t*>(Y), ldy, N, s));
+    return SWM_OK;
+  }
   uint16_t* w = static_cast<uint16_t*>(workspace);
   SWM_HIP(swm::launch_decompress(f->d, w, f->h.k, s));
   int dev = 0;

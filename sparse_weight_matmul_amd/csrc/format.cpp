@@ -260,4 +260,24 @@ void fill_info(const Header& h, swm_format_info* info) {
   info->bytes_total = h.total_bytes();
 }
 
+bool mask_exceeds_2_of_4(const Header& h, const uint8_t* blob) {
+  // Tiles start at multiples of 32 columns, so aligned groups of 4 never
+  // straddle a 32-column step.  Group a (0..7) of step s is columns
+  // 32s + 4a .. +3: quarter q = a/2 of the words 8s + 4(a%2) .. +3, whose
+  // bits 16q .. 16q+15 are the 16 rows.  A row keeps 3 or 4 entries of the
+  // group iff three of its four bits are set.
+  const uint64_t* bits = reinterpret_cast<const uint64_t*>(blob + h.off_bits());
+  const uint64_t wpt = h.words_per_tile();
+  for (uint64_t t = 0; t < h.tiles(); ++t)
+    for (uint64_t sidx = 0; sidx < h.tk / 32; ++sidx)
+      for (int a = 0; a < 8; ++a) {
+        const uint64_t* w = bits + t * wpt + 8 * sidx + 4 * (a % 2);
+        const int q = a / 2;
+        const uint32_t f0 = uint32_t(w[0] >> (16 * q)) & 0xFFFF, f1 = uint32_t(w[1] >> (16 * q)) & 0xFFFF;
+        const uint32_t f2 = uint32_t(w[2] >> (16 * q)) & 0xFFFF, f3 = uint32_t(w[3] >> (16 * q)) & 0xFFFF;
+        if ((f0 & f1 & f2) | (f0 & f1 & f3) | (f0 & f2 & f3) | (f1 & f2 & f3)) return true;
+      }
+  return false;
+}
+
 }  // namespace swm

@@ -97,4 +97,19 @@ size_t prefill_sparse_lds(const Header& h);
 // The sparse prefill kernel addresses X with 32-bit byte offsets.
 bool prefill_sparse_fits(const Header& h, int64_t N, int64_t ldx);
 
+// Prefill on the sparse matrix cores: W (.) mask as a 2:4 layer plus a
+// residual layer (both 2:4 conforming), compacted per call into a workspace
+// and multiplied with v_smfmac_f32_32x32x32_f16.
+struct Sparse24Layout {
+  int64_t kp = 0, ldv = 0, ldm = 0;  // K rounded up to 64; values / index leading dimensions
+  size_t off_m24 = 0, off_vres = 0, off_mres = 0, bytes = 0;
+};
+Sparse24Layout sparse24_layout(const Header& h, bool residual);
+hipError_t launch_compact24(const DevFormat& f, const Sparse24Layout& L, bool residual, void* ws, hipStream_t s);
+hipError_t launch_smf(const Header& h, const Sparse24Layout& L, bool residual, const void* ws, const uint16_t* X,
+                      int64_t ldx, uint16_t* Y, int64_t ldy, int64_t N, hipStream_t s);
+size_t smf_lds(bool residual);
+// The SMFMAC kernel addresses the compacted layers and X with 32-bit byte offsets.
+bool smf_fits(const Header& h, int64_t N, int64_t ldx);
+
 }  // namespace swm

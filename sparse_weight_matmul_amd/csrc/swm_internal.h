@@ -46,6 +46,10 @@ swm_status validate_blob(const void* buf, size_t size, Header* h);
 
 void fill_info(const Header& h, swm_format_info* info);
 
+// True if some row keeps more than 2 entries in an aligned group of 4
+// columns (the mask is not 2:4 along K), from a validated blob's bitmaps.
+bool mask_exceeds_2_of_4(const Header& h, const uint8_t* blob);
+
 // SWM-CR v2 column-run encoding (activation skipping): kept entries grouped
 // by input column inside blocks of kColRunRows rows, the blocks of a column
 // stored kColRunGroup at a time.

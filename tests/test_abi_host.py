@@ -154,11 +154,11 @@ def test_encoder_rejects_bad_arguments():
 
 
 def test_compress_rejects_unknown_flags():
-    # flag bits other than SWM_CFG_SKIPPING are refused before any encoding or upload
+    # flag bits other than SWM_CFG_SKIPPING and SWM_CFG_SMFMAC are refused before any encoding or upload
     lib = swm.load()
     W = np.ones((4, 4), dtype=np.float16)
     h = ctypes.c_void_p()
-    cfg = swm.TileCfg(16, 64, 2)
+    cfg = swm.TileCfg(16, 64, 4)
     assert lib.swm_sparse_compress(W.ctypes.data, 4, None, 4, 4, 4, ctypes.byref(cfg), None, ctypes.byref(h)) == 1
     assert not h.value
 

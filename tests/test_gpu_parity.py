@@ -566,10 +566,11 @@ def test_spmm_ws_degenerate_cases(gpu_lib):
     W, _ = wl.pruned_weight(104, 0, M, K, 0.5)
     X = wl.activations(104, 0, N, K)
     f0 = swm.sparse_compress(W, np.zeros((M, K), dtype=bool))
-    ws, nb = _workspace(swm, f0, N)
-    assert nb > 0
-    assert np.all(_np(swm.spmm_ws(f0, _t(X), ws)).view(np.uint16) == 0)
     f = swm.sparse_compress(W, np.ones((M, K), dtype=bool))
+    nb0, nbf = swm.spmm_workspace_bytes(f0, N), swm.spmm_workspace_bytes(f, N)
+    assert 0 < nb0 == nbf
+    ws = torch.empty(nbf, dtype=torch.uint8, device="cuda")
+    assert np.all(_np(swm.spmm_ws(f0, _t(X), ws)).view(np.uint16) == 0)
     assert np.all(_np(swm.spmm_ws(f, _t(np.zeros((N, K), dtype=np.float16)), ws)).view(np.uint16) == 0)
     one = np.zeros((M, K), dtype=bool)
     cols = np.arange(M) % K
@@ -632,6 +633,60 @@ def test_spmm_ws_below_threshold_and_fallbacks(gpu_lib):
     assert bool((ws == 0x5A).all())
     assert np.array_equal(a.view(np.uint16), _np(swm.spmm(f, Xv)).view(np.uint16))
     assert_close(a, oracle.masked_matmul(W, mask, Xs[:, :K]), "spmm_ws unaligned fallback")
+
+
+# ------------------------------------------------------------------ prefill on the sparse matrix cores (2:4 layer + residual)
+def _layer24_bytes(M, K, residual):
+    kp = -(-K // 64) * 64
+    vb = -(-(M * kp) // 256) * 256              # values: M x kp/2 fp16
+    mb = -(-(M * (kp // 16) * 2) // 256) * 256  # indices: M x kp/16 uint16
+    return 2 * (vb + mb) if residual else vb + mb
+
+
+@pytest.mark.parametrize("N", [1024, 2048, 4096])
+def test_smfmac_route_2_4_qproj(gpu_lib, N):
+    """q_proj 4096x4096 with a 2:4 magnitude mask on the sparse-matrix-core
+    route: no residual layer, so spmm_ws compacts W into the 2:4 operand
+    layout (workspace 1.125 bytes per position) and runs v_smfmac; full
+    outputs against the oracle.  Without the option the handle expands."""
+    swm = gpu_lib
+    W, mask, _ = wl.decode_qproj_2_4(1)
+    X = wl.activations(wl.CFG_WIDE, 13, N, 4096)
+    assert swm.spmm_workspace_bytes(swm.sparse_compress(W, mask), N) == 2 * 4096 * 4096
+    f = swm.sparse_compress(W, mask, smfmac=True)
+    ws, nb = _workspace(swm, f, N)
+    assert nb == _layer24_bytes(4096, 4096, False)
+    Y = _np(swm.spmm_ws(f, _t(X), ws))
+    assert_close(Y, oracle.masked_matmul(W, mask, X), f"2:4 q_proj N={N}")
+
+
+@pytest.mark.parametrize("M,K,N,s", [(520, 392, 1100, 0.5), (300, 4104, 1024, 0.7), (1000, 1024, 1031, 0.6),
+                                     (256, 64, 1024, 0.0), (64, 200, 1500, 1.0)])
+def test_smfmac_route_with_residual(gpu_lib, M, K, N, s):
+    """Unstructured masks through the sparse-matrix-core route (forced per
+    handle): the 2:4 layer and the residual layer add up to the exact masked
+    product (ragged M, K not a multiple of 64, N not a multiple of 256; a
+    dense mask, where every group keeps 4, and an all-pruned one)."""
+    swm = gpu_lib
+    W, mask = wl.pruned_weight(105, M + K + N, M, K, s)
+    X = wl.activations(105, M + N, N, K)
+    f = swm.sparse_compress(W, mask, smfmac=True)
+    ws, nb = _workspace(swm, f, N)
+    assert nb == _layer24_bytes(M, K, s < 1.0)
+    Y = _np(swm.spmm_ws(f, _t(X), ws))
+    assert_close(Y, oracle.masked_matmul(W, mask, X), f"smfmac {M}x{K}x{N} s={s}")
+    if s == 1.0:
+        assert np.all(Y.view(np.uint16) == 0)
+
+
+def test_smfmac_route_upgate_70_full(gpu_lib):
+    """up/gate 11008x4096 at 70% (the config's highest sparsity) forced onto
+    the sparse matrix cores with its residual layer, N = 2048, full outputs."""
+    swm = gpu_lib
+    W, mask, X = wl.prefill_upgate(0.7, 2048)
+    f = swm.sparse_compress(W, mask, smfmac=True)
+    ws, _ = _workspace(swm, f, 2048)
+    assert_close(_np(swm.spmm_ws(f, _t(X), ws)), oracle.masked_matmul(W, mask, X), "up/gate 70% smfmac")
 
 
 def test_spmm_ws_errors(gpu_lib):
