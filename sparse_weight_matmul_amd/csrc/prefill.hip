@@ -265,6 +265,228 @@ __global__ __launch_bounds__(256) void dense_kernel(PrefillArgs a) {
     }
 }
 
+// ------------------------------------------------------------------ dense, tiles loaded straight into LDS
+// Sixteen zero bytes: the source of activation chunks past K.
+__device__ __attribute__((aligned(16))) uint16_t g_pf_zero[8];
+
+// Global -> LDS without registers: lane l writes 16 bytes at lds + 16 l
+// (`lds` is the same for every lane of the wave).
+__device__ __forceinline__ void lds_dma16(const void* src, uint8_t* lds) {
+  __builtin_amdgcn_global_load_lds(src, lds, 16, 0, 0);
+}
+
+// s_waitcnt: at most n vector memory operations of this wave outstanding and
+// every LDS operation complete (gfx9 encoding: vmcnt in bits 3:0 and 15:14,
+// expcnt 6:4 left at 7, lgkmcnt 11:8 = 0).
+template <int n>
+__device__ __forceinline__ void wait_vm_lgkm0() {
+  static_assert(n >= 0 && n < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((n & 15) | (7 << 4) | (((n >> 4) & 3) << 14));
+}
+
+// kWM x kWN waves, each owning kWI x kWJ accumulators of 32 x 32: the block
+// is 32 kWI kWM rows of W by 32 kWJ kWN tokens.
+template <int kWI, int kWJ, int kWM, int kWN>
+struct DmaShape {
+  static constexpr int kNW = kWM * kWN;                              // waves
+  static constexpr int kBR = 32 * kWI * kWM, kBT = 32 * kWJ * kWN;  // block rows, tokens
+  static constexpr int kAT = kBR * BK * 2, kBTB = kBT * BK * 2;     // stage bytes
+  // three stages where the block is alone on its CU anyway; the 128x128
+  // block keeps two, so that two blocks share a CU
+  static constexpr int kStages = kBR * kBT >= 256 * 128 && 3 * (kAT + kBTB) <= 160 * 1024 ? 3 : 2;
+  static constexpr int kIA = kAT / (1024 * kNW), kIB = kBTB / (1024 * kNW);  // 1 KiB loads per wave per step
+  static_assert(kIA * 1024 * kNW == kAT && kIB * 1024 * kNW == kBTB, "whole loads per wave");
+  // the stages, or the per-wave epilogue regions (a padded token row each) if larger
+  static constexpr int kEpi = kNW * (32 * kWJ) * (64 * kWI + 8);
+  static constexpr int kLds = kStages * (kAT + kBTB) > kEpi ? kStages * (kAT + kBTB) : kEpi;
+  static_assert(kLds <= 160 * 1024, "LDS");
+};
+
+// The dense product with the A and B tiles loaded by global_load_lds_dwordx4
+// into kStages LDS stages (no staging registers, no LDS store instructions):
+// instruction i of wave w fills LDS bytes (w n + i) KiB + 16 lane of its
+// tile, row r = 8 (w n + i) + lane/8, stored chunk lane%8, so the lane loads
+// the logical chunk (lane%8) ^ ((r >> 1) & 7) of the swizzled layout.  One
+// barrier per step, in its last 16-column slice, once every wave holds that
+// slice's fragments: after it the first fragments of step ks + 1 and the
+// loads of step ks + kStages (into the stage just released) are spread
+// between the slice's products, so a load has kStages - 1 steps to arrive
+// and the matrix cores do not wait for the first fragments of a step.
+template <int kWI, int kWJ, int kWM, int kWN>
+__global__ __launch_bounds__(64 * kWM * kWN) void dense_dma_kernel(PrefillArgs a) {
+  using S = DmaShape<kWI, kWJ, kWM, kWN>;
+  constexpr int kAT = S::kAT, kStage = kAT + S::kBTB;
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  int tm, tn;
+  if (!tile_of(a, tm, tn)) return;
+  const int tid = int(threadIdx.x);
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / kWN, wn = wave % kWN;
+  const int m0 = tm * S::kBR, n0 = tn * S::kBT;
+  const int nsteps = (a.K + BK - 1) / BK;
+  const uint32_t base = lds_addr(smem);
+
+  // per-lane sources (32-bit byte offsets; the launcher checks W and X fit 4 GiB)
+  const uint8_t* wb = reinterpret_cast<const uint8_t*>(a.W);
+  const uint8_t* xb = reinterpret_cast<const uint8_t*>(a.X);
+  uint32_t aoff[S::kIA], boff[S::kIB];
+  int acol[S::kIA], bcol[S::kIB];
+#pragma unroll
+  for (int i = 0; i < S::kIA; ++i) {
+    const int r = 8 * (wave * S::kIA + i) + (lane >> 3);
+    acol[i] = 8 * ((lane & 7) ^ ((r >> 1) & 7));
+    aoff[i] = 2u * uint32_t(min(m0 + r, a.M - 1)) * uint32_t(a.ldw);  // rows past M: never stored
+  }
+#pragma unroll
+  for (int i = 0; i < S::kIB; ++i) {
+    const int r = 8 * (wave * S::kIB + i) + (lane >> 3);
+    bcol[i] = 8 * ((lane & 7) ^ ((r >> 1) & 7));
+    boff[i] = 2u * uint32_t(min(n0 + r, a.N - 1)) * uint32_t(a.ldx);  // tokens past N: never stored
+  }
+  const void* zero = g_pf_zero;
+  asm volatile("" : "+s"(zero));  // address kept in registers, not reloaded every step
+  // load q of step kq (A rows for q < kIA, else activations) into its stage;
+  // past the end: the last step again, into a stage no later step reads (no
+  // branch, and the per-step count of loads the waits assume is kept)
+  auto issue_one = [&](int kq, int q) {
+    uint8_t* sa = smem + (kq % S::kStages) * kStage;
+    const int ks = min(kq, nsteps - 1);
+    if (q < S::kIA) {
+      // columns past K multiply zero activations: read a clamped in-row chunk
+      const uint32_t kc = 2u * uint32_t(min(ks * BK + acol[q], a.K - 8));
+      lds_dma16(wb + (aoff[q] + kc), sa + (wave * S::kIA + q) * 1024);
+    } else {
+      const int i = q - S::kIA;
+      const int col = ks * BK + bcol[i];  // K % 8 == 0: a chunk is wholly inside or outside
+      const void* src = col < a.K ? static_cast<const void*>(xb + (boff[i] + 2u * uint32_t(col))) : zero;
+      lds_dma16(src, sa + kAT + (wave * S::kIB + i) * 1024);
+    }
+  };
+
+  f32x16 acc[kWI][kWJ];
+#pragma unroll
+  for (int i = 0; i < kWI; ++i)
+#pragma unroll
+    for (int j = 0; j < kWJ; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+
+  half8 fa[2][kWI], fb[2][kWJ];
+  // fragment q of a slice: A rows for q < kWI, else B tokens
+  auto read_frag = [&](int stage, int kk, int slot, int q) {
+    const uint32_t aBase = base + stage * kStage, bBase = aBase + kAT;
+    const int ch = kk * 2 + (lane >> 5);
+    if (q < kWI)
+      fa[slot][q] = __builtin_bit_cast(half8, lds_load16(aBase + swz((wm * kWI + q) * 32 + (lane & 31), ch)));
+    else
+      fb[slot][q - kWI] =
+          __builtin_bit_cast(half8, lds_load16(bBase + swz((wn * kWJ + q - kWI) * 32 + (lane & 31), ch)));
+  };
+  auto product = [&](int sl, int m) {
+    const int i = m / kWJ, j = m % kWJ;
+    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[sl][i], fb[sl][j], acc[i][j], 0, 0, 0);
+  };
+  constexpr int kI = S::kIA + S::kIB;  // loads per wave per step
+  constexpr int kG = kWI + kWJ;        // fragment reads per slice
+  constexpr int kM = kWI * kWJ;        // products per slice
+  constexpr int kH = kM / 2;
+
+  // Steps 0 .. kStages-1 fill every stage; step ks + kStages is requested in
+  // step ks once every wave has read its last fragments of step ks.
+#pragma unroll
+  for (int p = 0; p < S::kStages; ++p)
+#pragma unroll
+    for (int q = 0; q < kI; ++q) issue_one(p, q);
+  wait_vm_lgkm0<(S::kStages - 1) * kI>();
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int q = 0; q < kG; ++q) read_frag(0, 0, 0, q);
+  __builtin_amdgcn_sched_barrier(0);
+
+  // Each slice: its products in a fixed order, the next slice's fragment
+  // reads (and in the last slice the loads of a later step) spread between
+  // them; sched_barrier pins that order.
+  for (int ks = 0; ks < nsteps; ++ks) {
+    const int st = ks % S::kStages, nst = (ks + 1) % S::kStages;
+#pragma unroll
+    for (int kk = 0; kk < 3; ++kk) {
+      const int sl = kk & 1;
+#pragma unroll
+      for (int m = 0; m < kM; ++m) {
+        product(sl, m);
+        // all reads in the first half: they land before the next slice starts
+#pragma unroll
+        for (int q = m * kG / kH; q < (m + 1) * kG / kH && q < kG; ++q) read_frag(st, kk + 1, sl ^ 1, q);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    // last slice: one product, then the step's barrier (every fragment of
+    // step ks is in registers, this wave's loads of step ks + 1 are in LDS;
+    // after it both hold for all waves), then step ks + 1's first fragments
+    // and step ks + kStages's loads between the remaining products
+    product(1, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    wait_vm_lgkm0<(S::kStages - 2) * kI>();
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    constexpr int kE = kG + kI;  // reads first, then loads; none after the last two products
+#pragma unroll
+    for (int m = 1; m < kM; ++m) {
+#pragma unroll
+      for (int e = (m - 1) * kE / (kM - 2); e < m * kE / (kM - 2) && e < kE; ++e) {
+        if (e < kG)
+          read_frag(nst, 0, 0, e);  // unused after the last step
+        else
+          issue_one(ks + S::kStages, e - kG);
+      }
+      product(1, m);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+
+  // Epilogue: fp16 round-to-nearest-even.  Each wave transposes its
+  // 32 kWI x 32 kWJ quadrant through its own LDS region (a row per token,
+  // padded by 8 bytes) so that the stores are 16 contiguous bytes per lane;
+  // every wave's loads must have landed before any region is written.
+  wait_vm_lgkm0<0>();
+  __builtin_amdgcn_s_barrier();
+  constexpr int kTM = 32 * kWI, kTN = 32 * kWJ, kRS = 2 * kTM + 8;
+  const uint32_t reg = base + wave * (kTN * kRS);
+#pragma unroll
+  for (int i = 0; i < kWI; ++i)
+#pragma unroll
+    for (int j = 0; j < kWJ; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int n = j * 32 + (lane & 31), m = i * 32 + q * 8 + (lane >> 5) * 4;
+        uint16_t h[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) h[e] = __builtin_bit_cast(uint16_t, _Float16(acc[i][j][q * 4 + e]));
+        const u32x2 pk = {uint32_t(h[0]) | (uint32_t(h[1]) << 16), uint32_t(h[2]) | (uint32_t(h[3]) << 16)};
+        *reinterpret_cast<lds_u32x2*>(static_cast<uintptr_t>(reg + n * kRS + 2 * m)) = pk;
+      }
+  constexpr int kLPR = kTM / 8;    // lanes per token row
+  constexpr int kRPI = 64 / kLPR;  // rows per instruction
+  const int gm = m0 + wm * kTM + (lane % kLPR) * 8;
+  const bool vec = (a.ldy % 8 == 0) && ((reinterpret_cast<uintptr_t>(a.Y) & 15) == 0) && gm + 8 <= a.M;
+#pragma unroll
+  for (int r = 0; r < kTN; r += kRPI) {
+    const int nl = r + lane / kLPR;
+    const int n = n0 + wn * kTN + nl;
+    const u32x4 v = lds_load16(reg + nl * kRS + (lane % kLPR) * 16);
+    if (n >= a.N) continue;
+    uint16_t* dst = a.Y + int64_t(n) * a.ldy + gm;
+    if (vec) {
+      *reinterpret_cast<u32x4*>(dst) = v;
+    } else {
+      for (int e = 0; e < 8; ++e)
+        if (gm + e < a.M) dst[e] = uint16_t(v[e / 2] >> (16 * (e % 2)));
+    }
+  }
+}
+
 // ------------------------------------------------------------------ sparse, warp-specialized
 // 512 threads, eight waves, two per SIMD; the workgroup computes a 128 (rows
 // of W) x 256 (tokens) block of Y.  Every wave expands one 16 x 64 weight
@@ -550,6 +772,23 @@ template <int kWI, int kWJ>
 hipError_t launch_dense(PrefillArgs a, hipStream_t s) {
   a.tiles_m = int((a.M + 64 * kWI - 1) / (64 * kWI));
   a.tiles_n = int((a.N + 64 * kWJ - 1) / (64 * kWJ));
+  // The LDS-direct kernel where W and X fit 32-bit byte offsets; otherwise
+  // (or with SWM_DENSE_DMA=0) the register-staged one.
+  static const bool dma = [] {
+    const char* e = getenv("SWM_DENSE_DMA");
+    return !(e && *e == '0');
+  }();
+  const bool fits = 2 * (int64_t(a.M - 1) * a.ldw + a.K) < (int64_t(1) << 32) &&
+                    2 * (int64_t(a.N - 1) * a.ldx + a.K) < (int64_t(1) << 32);
+  if (dma && fits) {
+    // 256 x 256 with eight waves (two per SIMD, 128 x 64 each); the smaller
+    // blocks with four
+    constexpr int kWN = kWI == 4 && kWJ == 4 ? 4 : 2;
+    constexpr int kJ = kWI == 4 && kWJ == 4 ? 2 : kWJ;
+    using S = DmaShape<kWI, kJ, 2, kWN>;
+    hipLaunchKernelGGL((dense_dma_kernel<kWI, kJ, 2, kWN>), dim3(grid_size(a)), dim3(64 * S::kNW), S::kLds, s, a);
+    return hipGetLastError();
+  }
   const size_t lds = size_t(2) * (64 * kWI + 64 * kWJ) * BK * 2;
   hipLaunchKernelGGL((dense_kernel<kWI, kWJ>), dim3(grid_size(a)), dim3(256), lds, s, a);
   return hipGetLastError();

@@ -422,6 +422,42 @@ def test_dense_gemm_ragged(gpu_lib, M, K, N):
     assert_close(Y, oracle.masked_matmul(W, None, X), f"dense {M}x{K}x{N}")
 
 
+_REG_STAGED_CHECK = r"""
+import sys
+import numpy as np
+sys.path.insert(0, sys.argv[1])
+sys.path.insert(0, sys.argv[2])
+import torch
+import sparse_weight_matmul_amd as swm
+import oracle
+for M, K, N in [(100, 64, 20), (1000, 512, 32), (257, 4104, 17), (3000, 256, 300), (4096, 4096, 512)]:
+    g = np.random.default_rng(M * K + N)
+    W = (0.02 * g.standard_normal((M, K))).astype(np.float16)
+    X = g.standard_normal((N, K)).astype(np.float16)
+    Y = swm.dense_gemm(torch.from_numpy(W).cuda(), torch.from_numpy(X).cuda()).float().cpu().numpy()
+    ref = oracle.masked_matmul(W, None, X)
+    mx = float(np.abs(Y - ref).max())
+    rel = float(np.linalg.norm(Y - ref) / np.linalg.norm(ref))
+    print(M, K, N, mx, rel, flush=True)
+    assert np.all(np.isfinite(Y)) and mx <= MAX_ABS and rel <= REL_FRO, (M, K, N, mx, rel)
+print("ok")
+"""
+
+
+def test_dense_gemm_register_staged_kernel():
+    """The register-staged MFMA kernel (taken for operands past 4 GiB, or
+    with SWM_DENSE_DMA=0, read once per process: hence a child process)."""
+    import os
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    env = dict(os.environ, SWM_DENSE_DMA="0")
+    code = f"MAX_ABS = {MAX_ABS}\nREL_FRO = {REL_FRO}\n" + _REG_STAGED_CHECK
+    r = subprocess.run([sys.executable, "-c", code, root, os.path.join(root, "tests")], env=env,
+                       capture_output=True, text=True, timeout=110)
+    assert r.returncode == 0 and r.stdout.strip().endswith("ok"), r.stdout[-2000:] + r.stderr[-2000:]
+
+
 def test_dense_gemm_graph_replay_after_larger_k(gpu_lib):
     """The streaming dense kernel allocates nothing: a captured small-K call
     still replays correctly after an eager call with a much larger K (the
