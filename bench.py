@@ -366,15 +366,13 @@ def prefill_block(args, torch, swm, wl, G):
     return blk
 
 
-def layer_copies(swm, torch, n_max, min_sparse=5, min_dense=3):
-    """The seven Llama-2-7B-shaped linears, >= min_sparse compressed copies and
-    >= min_dense dense copies of the whole layer (rotated so that each layer
-    pass streams its weights from HBM: 5 x 228 MB and 3 x 405 MB are above
-    4x the 256 MB Infinity Cache)."""
-    import swm_workloads as wl
+def layer_copies(swm, torch, parts, min_sparse=5, min_dense=3):
+    """Linears given as (W, mask, X): >= min_sparse compressed copies and
+    >= min_dense dense copies of each (rotated so that each layer pass streams
+    its weights from HBM: 5 x 228 MB and 3 x 405 MB are above 4x the 256 MB
+    Infinity Cache)."""
     fmts, dens, xs, shapes, alg = [], [], [], [], 0
-    for i in range(7):
-        W, mask, X = wl.layer_linear(i, n_max)
+    for W, mask, X in parts:
         f0 = swm.sparse_compress(W, mask)
         blob = f0.export()
         fmts.append([f0] + [swm.format_import(blob) for _ in range(min_sparse - 1)])
@@ -386,16 +384,14 @@ def layer_copies(swm, torch, n_max, min_sparse=5, min_dense=3):
     return fmts, dens, xs, shapes, alg
 
 
-def layer_block(args, torch, swm, wl, G):
-    """Config 5: the seven linears back to back on one stream, N = 16 and 4096,
-    rotated over 5 compressed / 3 dense copies of the layer."""
-    _log("layer block: 7 linears, 5 compressed / 3 dense rotating copies")
-    CS, CD = 5, 3
-    fmts, dens, xs, shapes, fa = layer_copies(swm, torch, 4096, CS, CD)
+def layer_pass(args, torch, swm, G, parts, CS, CD):
+    """One layer pass = each of `parts` once, back to back on one stream,
+    sparse through spmm_ws and dense through dense_gemm, at N = 16 and 4096."""
+    fmts, dens, xs, shapes, fa = layer_copies(swm, torch, parts, CS, CD)
     ws = torch.empty(max(max(swm.spmm_workspace_bytes(f[0], 4096) for f in fmts), 256), dtype=torch.uint8,
                      device="cuda")
-    blk = {"workload": "Llama-2-7B layer: q/k/v/o 4096x4096, gate/up 11008x4096, down 4096x11008, 50%",
-           "rotation": {"compressed_layer_copies": CS, "dense_layer_copies": CD}, "format_alg_bytes": fa}
+    L = len(parts)
+    blk = {"launches_per_pass": L, "format_alg_bytes": fa}
     for n in (16, 4096):
         ys = [torch.empty((n, shp[0]), dtype=torch.float16, device="cuda") for shp in shapes]
 
@@ -404,12 +400,12 @@ def layer_block(args, torch, swm, wl, G):
 
         def de(c, i):
             return lambda: swm.dense_gemm(dens[i][c], xs[i][:n], ys[i])
-        for i in range(7):
+        for i in range(L):
             sp(0, i)()
             de(0, i)()
         torch.cuda.synchronize()
-        gs = G.capture([sp(c, i) for c in range(CS) for i in range(7)])
-        gd = G.capture([de(c, i) for c in range(CD) for i in range(7)])
+        gs = G.capture([sp(c, i) for c in range(CS) for i in range(L)])
+        gd = G.capture([de(c, i) for c in range(CD) for i in range(L)])
         reps = 10 if n == 16 else 3
         ds, dd = pct(G.samples(gs, reps, CS)), pct(G.samples(gd, reps, CD))
         alg = fa + sum(2 * (shp[0] + shp[1]) * n for shp in shapes)
@@ -426,6 +422,26 @@ def layer_block(args, torch, swm, wl, G):
         del ys
     del fmts, dens, xs, ws
     torch.cuda.empty_cache()
+    return blk
+
+
+def layer_block(args, torch, swm, wl, G):
+    """Config 5: the seven linears back to back on one stream, N = 16 and 4096,
+    rotated over 5 compressed / 3 dense copies of the layer; then the same
+    layer with q/k/v and gate/up row-stacked (four launches a pass, as
+    inference engines run it; the dense side stacked the same way)."""
+    CS, CD = 5, 3
+    _log("layer block: 7 linears, 5 compressed / 3 dense rotating copies")
+    parts = [wl.layer_linear(i, 4096) for i in range(7)]
+    blk = layer_pass(args, torch, swm, G, parts, CS, CD)
+    blk.update({"workload": "Llama-2-7B layer: q/k/v/o 4096x4096, gate/up 11008x4096, down 4096x11008, 50%",
+                "rotation": {"compressed_layer_copies": CS, "dense_layer_copies": CD}})
+    _log("layer block: stacked projections qkv / o / gate_up / down")
+    fused = [wl.stack_linears([parts[i] for i in idx]) for _, idx in wl.LAYER_FUSED]
+    del parts
+    fb = layer_pass(args, torch, swm, G, fused, CS, CD)
+    fb["workload"] = "the same layer as qkv 12288x4096, o 4096x4096, gate_up 22016x4096, down 4096x11008"
+    blk["stacked_projections"] = fb
     return blk
 
 

@@ -197,3 +197,24 @@ def layer_linear(i: int, n_max: int):
     _, M, K = LLAMA7B_LINEARS[i]
     W, mask = pruned_weight(CFG_LAYER, i, M, K, 0.5)
     return W, mask, activations(CFG_LAYER, i, n_max, K)
+
+
+# The layer's projections as an inference engine launches them: q, k, v read
+# the same input and are stacked by rows into one 12288x4096 matrix, gate and
+# up likewise into one 22016x4096 matrix.
+LAYER_FUSED = (("qkv", (0, 1, 2)), ("o", (3,)), ("gate_up", (4, 5)), ("down", (6,)))
+
+
+def stack_linears(parts):
+    """Row-stack (W, mask, X) triples that share their input: the stacked W,
+    mask, and the first part's X."""
+    W = np.concatenate([p[0] for p in parts], axis=0)
+    mask = np.concatenate([p[1] for p in parts], axis=0)
+    return W, mask, parts[0][2]
+
+
+def layer_fused(g: int, n_max: int):
+    """Projection group g (qkv, o, gate_up, down = 0..3) of the layer, its
+    linears row-stacked, with the group's shared input."""
+    _, idx = LAYER_FUSED[g]
+    return stack_linears([layer_linear(i, n_max) for i in idx])

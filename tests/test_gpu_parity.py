@@ -972,6 +972,26 @@ def test_fig1_shape_full(gpu_lib):
         assert_close(Yd[:, r:r + 8192], ref, f"fig1 dense rows {r}..")
 
 
+# ------------------------------------------------------------------ the layer's stacked projections, as benchmarked
+@pytest.mark.parametrize("g,N", [(0, 16), (2, 16), (0, 4096)])   # qkv 12288x4096, gate_up 22016x4096
+def test_layer_stacked_projections_as_benchmarked(gpu_lib, g, N):
+    # row-stacked q;k;v and gate;up through spmm_ws, full outputs; each row
+    # range must equal its own linear's product with the group's input
+    swm = gpu_lib
+    W, mask, X = wl.layer_fused(g, N)
+    f = swm.sparse_compress(W, mask)
+    ref = oracle.masked_matmul(W, mask, X)
+    ws, nb = _workspace(swm, f, N)
+    assert (nb > 0) == (N == 4096)
+    Y = _np(swm.spmm_ws(f, _t(X), ws))
+    assert_close(Y, ref, f"stacked group {g} N={N}")
+    r0 = 0
+    for i in wl.LAYER_FUSED[g][1]:
+        Wi, mi, _ = wl.layer_linear(i, N)
+        assert_close(Y[:, r0:r0 + Wi.shape[0]], oracle.masked_matmul(Wi, mi, X), f"linear {i} inside group {g}")
+        r0 += Wi.shape[0]
+
+
 # ------------------------------------------------------------------ layer shapes in the bench's launch configuration
 @pytest.mark.parametrize("i", [0, 4, 6])   # q_proj 4096x4096, gate_proj 11008x4096, down_proj 4096x11008
 @pytest.mark.parametrize("N", [16, 4096])

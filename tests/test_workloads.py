@@ -89,3 +89,20 @@ def test_prune_2_4_mask_rule():
     drop_max = np.where(~groups, a, -np.inf).max(axis=2)
     assert np.all(kept_min >= drop_max)
     assert np.all(m[:, 24:26]) and not np.any(m[:, 26])
+
+
+def test_layer_fused_groups_cover_each_linear_once():
+    idx = [i for _, g in wl.LAYER_FUSED for i in g]
+    assert sorted(idx) == list(range(7))
+    for _, g in wl.LAYER_FUSED:   # a group's linears share K, so their rows stack
+        assert len({wl.LLAMA7B_LINEARS[i][2] for i in g}) == 1
+
+
+def test_stack_linears_rows_and_input():
+    g = np.random.default_rng(3)
+    parts = [(g.standard_normal((m, 8)).astype(np.float16), g.random((m, 8)) < 0.5,
+              g.standard_normal((2, 8)).astype(np.float16)) for m in (3, 5)]
+    W, mask, X = wl.stack_linears(parts)
+    assert W.shape == (8, 8) and mask.shape == (8, 8)
+    assert np.array_equal(W[3:], parts[1][0]) and np.array_equal(mask[:3], parts[0][1])
+    assert X is parts[0][2]
