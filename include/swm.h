@@ -34,7 +34,10 @@
  *    X and Y alive until the stream work completes.  Y must not alias X.
  *  - Device pointers must belong to the device that is current when the call
  *    is made; a format handle is bound to the device current at creation.
- *  - Every call returns an swm_status.  Nothing aborts, throws or prints.
+ *  - Every call returns an swm_status.  Nothing aborts or throws, and nothing
+ *    prints unless SWM_LOG=1 (read once), which writes one stderr line per
+ *    dispatch decision (kernel route, work split) of compress and the
+ *    product calls.
  *    On a validation error no output is touched.  Kernel faults are reported
  *    as SWM_ERR_HIP by a later checked call (swm_last_hip_error() holds the
  *    hipError_t of the last failing runtime call).
@@ -45,8 +48,12 @@
  *    run concurrently.
  *  - Environment variables, for tuning and measurement only (they change the
  *    work split, so a result can change only in its fp32 summation order;
- *    the defaults are the measured best): SWM_DECODE_LOOP
- *    (use the looped decode kernel), SWM_DECODE_TPW / SWM_DECODE_WAVES_PER_CU
+ *    the defaults are the measured best): SWM_DECODE_PATH=loop or
+ *    SWM_DECODE_LOOP (use the looped decode kernel, read when a handle is
+ *    created), SWM_SKIP = off / on (swm_spmspv never / for every n <= 4 takes
+ *    the column-run skipping kernel on a handle that carries it; default up
+ *    to 2 tokens; read once), SWM_DENSE_DMA=0 (the register-staged tiled
+ *    dense kernel; read once), SWM_DECODE_TPW / SWM_DECODE_WAVES_PER_CU
  *    (decode tiles per wave / waves per CU, read when a handle is created),
  *    SWM_DENSE_WAVES_PER_CU (streaming dense kernel), SWM_DENSE_BLOCK = 1 / 2
  *    / 3 (tiled dense block 256x256 / 256x128 / 128x128), SWM_EXPAND_MIN_N

@@ -1,10 +1,13 @@
 // C ABI of the sparse-weight matmul library: handle management, argument
-// checks, dispatch by token count, error mapping.  No entry point aborts,
-// throws across the boundary or prints.
+// checks, dispatch by token count, error mapping.  No entry point aborts or
+// throws across the boundary; nothing is printed unless SWM_LOG=1, which
+// writes one line per dispatch decision to stderr.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
 #include <atomic>
+#include <cstdarg>
+#include <cstdio>
 #include <cstring>
 #include <mutex>
 #include <new>
@@ -32,6 +35,39 @@ struct swm_format {
 namespace {
 
 std::atomic<int32_t> g_last_hip{0};
+
+// SWM_LOG=1 (read once): one stderr line per dispatch decision.
+bool log_on() {
+  static const bool v = [] {
+    const char* e = getenv("SWM_LOG");
+    return e && *e == '1';
+  }();
+  return v;
+}
+
+__attribute__((format(printf, 1, 2))) void swm_log(const char* fmt, ...) {
+  if (!log_on()) return;
+  char line[256];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(line, sizeof(line), fmt, ap);
+  va_end(ap);
+  fprintf(stderr, "[swm] %s\n", line);
+}
+
+// SWM_SKIP (read once): "off" never takes the column-run kernel, "on" takes
+// it for every token count it serves (n <= 4), anything else (default) up to
+// the measured break-even token count.  An ablation switch: the result
+// changes only in fp32 summation order.
+int skip_mode() {
+  static const int v = [] {
+    const char* e = getenv("SWM_SKIP");
+    if (e && !strcmp(e, "off")) return 0;
+    if (e && !strcmp(e, "on")) return 2;
+    return 1;
+  }();
+  return v;
+}
 
 swm_status hip_fail(hipError_t e) {
   g_last_hip.store(int32_t(e));
@@ -180,6 +216,11 @@ swm_status swm_sparse_compress(const uint16_t* W, int64_t ldw, const uint8_t* ma
   st = upload(std::move(blob), h, static_cast<hipStream_t>(stream), &f);
   if (st != SWM_OK) return st;
   f->smf_force = cfg && (cfg->flags & SWM_CFG_SMFMAC);
+  swm_log("sparse_compress M=%lld K=%lld nnz=%llu blob=%zu B flags=%d: decode split %d / %d tiles per wave "
+          "(N <= 8 / <= 16), %s",
+          (long long)h.m, (long long)h.k, (unsigned long long)h.nnz, f->blob.size(), cfg ? cfg->flags : 0,
+          f->plan.tiles_per_wave, f->plan_wide.tiles_per_wave,
+          f->res24 ? "mask exceeds 2:4 (SMFMAC needs a residual layer)" : "mask within 2:4");
   if (cfg && (cfg->flags & SWM_CFG_SKIPPING)) {
     st = swm_format_enable_skipping(f, stream, nullptr);
     if (st != SWM_OK) {
@@ -353,14 +394,22 @@ static swm_status run_products(const swm_format* f, const void* X, int64_t ldx, 
   // N <= 32 is memory bound (the weights are read once per call): the decode
   // kernels, with one or two 16-token groups per decoded operand.
   if (N <= 16 || (N <= 32 && !skip)) {
-    SWM_HIP(swm::launch_decode(f->d, decode_plan(f, N), x, ldx, y, ldy, int(N), skip, s));
+    const swm::DecodePlan& p = decode_plan(f, N);
+    swm_log("%s M=%lld K=%lld N=%lld: decode (%s, %d tiles x %d waves per slab)", skip ? "spmspv" : "spmm",
+            (long long)f->h.m, (long long)f->h.k, (long long)N, p.seq_segs > 0 && N <= 16 ? "straight-line" : "looped",
+            p.tiles_per_wave, p.waves);
+    SWM_HIP(swm::launch_decode(f->d, p, x, ldx, y, ldy, int(N), skip, s));
     return SWM_OK;
   }
   if (!skip && swm::prefill_supported(f->h.k, ldx, X) && swm::prefill_sparse_lds(f->h) <= 160 * 1024 &&
       swm::prefill_sparse_fits(f->h, N, ldx)) {
+    swm_log("spmm M=%lld K=%lld N=%lld: on-chip prefill (128x256 blocks)", (long long)f->h.m, (long long)f->h.k,
+            (long long)N);
     SWM_HIP(swm::launch_prefill_sparse(f->d, x, ldx, y, ldy, N, s));
     return SWM_OK;
   }
+  swm_log("%s M=%lld K=%lld N=%lld: decode in %d-token slices", skip ? "spmspv" : "spmm", (long long)f->h.m,
+          (long long)f->h.k, (long long)N, skip ? 16 : 32);
   // Otherwise: token slices through the decode kernel (32 at a time; 16 when
   // skipping, whose decode kernel serves one group of 16).
   const int64_t slice = skip ? 16 : 32;
@@ -455,12 +504,16 @@ swm_status swm_spmm_ws(const swm_format* f, const void* X, int64_t ldx, void* Y,
   if (st != SWM_OK) return st;
   if (!on_current_device(f)) return SWM_ERR_INVALID_ARG;
   if (smf_route(f, N) && swm::smf_fits(f->h, N, ldx)) {
+    swm_log("spmm_ws M=%lld K=%lld N=%lld: 2:4 compaction + SMFMAC (%s)", (long long)f->h.m, (long long)f->h.k,
+            (long long)N, f->res24 ? "with residual layer" : "no residual");
     const swm::Sparse24Layout L = swm::sparse24_layout(f->h, f->res24);
     SWM_HIP(swm::launch_compact24(f->d, L, f->res24, workspace, s));
     SWM_HIP(swm::launch_smf(f->h, L, f->res24, workspace, static_cast<const uint16_t*>(X), ldx,
                             static_cast<uint16_t*>(Y), ldy, N, s));
     return SWM_OK;
   }
+  swm_log("spmm_ws M=%lld K=%lld N=%lld: expand into the workspace + dense MFMA", (long long)f->h.m,
+          (long long)f->h.k, (long long)N);
   uint16_t* w = static_cast<uint16_t*>(workspace);
   SWM_HIP(swm::launch_decompress(f->d, w, f->h.k, s));
   int dev = 0;
@@ -488,17 +541,26 @@ static swm_status run_colruns(const swm_format* f, const void* x, int64_t ldx, v
 // or more tokens run the full product.
 constexpr int32_t kSkipMaxTokens = 2;
 
+// Whether swm_spmspv takes the column-run kernel (SWM_SKIP can force either way).
+static bool skip_route(const swm_format* f, int32_t n) {
+  const int mode = skip_mode();
+  const bool r = f && f->cr_mem && mode > 0 && n <= (mode == 2 ? 4 : kSkipMaxTokens);
+  if (f && r)
+    swm_log("spmspv M=%lld K=%lld n=%d: column-run skipping kernel + reduce", (long long)f->h.m, (long long)f->h.k, n);
+  return r;
+}
+
 swm_status swm_spmspv(const swm_format* f, const void* x, int64_t ldx, void* y, int64_t ldy,
                       int32_t n, void* stream) {
   if (n < 1 || n > 16) return SWM_ERR_INVALID_ARG;
-  if (f && f->cr_mem && n <= kSkipMaxTokens) return run_colruns(f, x, ldx, y, ldy, n, 0.f, stream);
+  if (skip_route(f, n)) return run_colruns(f, x, ldx, y, ldy, n, 0.f, stream);
   return run_products(f, x, ldx, y, ldy, n, true, static_cast<hipStream_t>(stream));
 }
 
 swm_status swm_spmspv_noalloc(const swm_format* f, const void* x, int64_t ldx, void* y, int64_t ldy,
                               int32_t n, void* stream) {
   if (n < 1 || n > 16) return SWM_ERR_INVALID_ARG;
-  if (f && f->cr_mem && n <= kSkipMaxTokens) {
+  if (skip_route(f, n)) {
     float* scr = nullptr;
     size_t cap = 0;
     SWM_HIP(swm::spmspv_scratch(&scr, &cap));
@@ -545,6 +607,8 @@ swm_status swm_gate_up_silu(const swm_format* g, const swm_format* u, const void
   const uint16_t* x = static_cast<const uint16_t*>(X);
   uint16_t* h = static_cast<uint16_t*>(H);
   hipStream_t s = static_cast<hipStream_t>(stream);
+  swm_log("gate_up_silu M=%lld K=%lld n=%d: one gated decode launch per 16 tokens (%d tiles per wave)",
+          (long long)g->h.m, (long long)g->h.k, n, p0.tiles_per_wave);
   SWM_HIP(swm::launch_decode_glu(g->d, u->d, p0, x, ldx, h, ldh, n0, tau, s));
   if (n > 16) SWM_HIP(swm::launch_decode_glu(g->d, u->d, p1, x + 16 * ldx, ldx, h + 16 * ldh, ldh, n - 16, tau, s));
   return SWM_OK;
@@ -576,11 +640,14 @@ swm_status swm_dense_gemm(const void* W, int64_t ldw, const void* X, int64_t ldx
   const bool small_tiled = N <= 32 && tiled_blocks * 4 < num_cus(dev);
   if (N > 16 && !small_tiled && swm::prefill_supported(K, ldx, X) && ldw % 8 == 0 &&
       (reinterpret_cast<uintptr_t>(W) & 15) == 0) {
+    swm_log("dense_gemm M=%lld K=%lld N=%lld: MFMA tiled", (long long)M, (long long)K, (long long)N);
     SWM_HIP(swm::launch_prefill_dense(static_cast<const uint16_t*>(W), ldw, static_cast<const uint16_t*>(X),
                                       ldx, static_cast<uint16_t*>(Y), ldy, M, K, N, num_cus(dev), s));
     return SWM_OK;
   }
   const auto p = swm::plan_dense_small(M, K, int(std::min<int64_t>(N, 16)), num_cus(dev));
+  swm_log("dense_gemm M=%lld K=%lld N=%lld: streaming, %d waves per slab, 16 tokens a pass", (long long)M,
+          (long long)K, (long long)N, p.waves);
   const uint16_t* w = static_cast<const uint16_t*>(W);
   const uint16_t* x = static_cast<const uint16_t*>(X);
   uint16_t* y = static_cast<uint16_t*>(Y);

@@ -24,6 +24,7 @@
 
 #include <algorithm>
 #include <cstdlib>
+#include <cstring>
 
 #include "kernels.h"
 
@@ -857,7 +858,9 @@ DecodePlan plan_decode(const Header& h, const uint32_t* tp, int num_cus, int wav
   p.seq_chunks = int((max2 + 1023) / 1024);
   if (p.seq_chunks < 1) p.seq_chunks = 1;
   if (p.seq_chunks > 4) p.seq_segs = 0;  // cannot happen: two tiles hold at most 4 KiB
-  if (getenv("SWM_DECODE_LOOP")) p.seq_segs = 0;
+  // ablation: the looped kernel everywhere (SWM_DECODE_PATH=loop, or SWM_DECODE_LOOP set)
+  const char* path = getenv("SWM_DECODE_PATH");
+  if (getenv("SWM_DECODE_LOOP") || (path && !strcmp(path, "loop"))) p.seq_segs = 0;
   return p;
 }
 

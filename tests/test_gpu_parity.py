@@ -458,6 +458,54 @@ def test_dense_gemm_register_staged_kernel():
     assert r.returncode == 0 and r.stdout.strip().endswith("ok"), r.stdout[-2000:] + r.stderr[-2000:]
 
 
+_LOG_SKIP_CHECK = r"""
+import sys
+import numpy as np
+sys.path.insert(0, sys.argv[1])
+sys.path.insert(0, sys.argv[2])
+import torch
+import sparse_weight_matmul_amd as swm
+import oracle
+import swm_workloads as wl
+W, mask, x = wl.spmspv_down(4, 0.3)
+f = swm.sparse_compress(W, mask, skipping=True)
+X = torch.from_numpy(x).cuda()
+for n in (1, 4):
+    y = swm.spmspv(f, X[:n]).float().cpu().numpy()
+    ref = oracle.masked_matmul_skip(W, mask, x[:n])
+    assert np.abs(y - ref).max() <= 1e-2, n
+    if sys.argv[3] == "off":
+        assert np.array_equal(y, swm.spmm(f, X[:n]).float().cpu().numpy()), n
+swm.dense_gemm(torch.from_numpy(W).cuda(), X[:1])
+torch.cuda.synchronize()
+print("ok", flush=True)
+"""
+
+
+@pytest.mark.parametrize("mode", ["off", "on"])
+def test_dispatch_log_and_skip_switch(mode):
+    """SWM_LOG=1 names every dispatch decision on stderr; SWM_SKIP forces the
+    skipping kernel off (then spmspv equals spmm bitwise) or on for n <= 4.
+    Both are read once per process: hence a child process."""
+    import os
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    env = dict(os.environ, SWM_LOG="1", SWM_SKIP=mode)
+    r = subprocess.run([sys.executable, "-c", _LOG_SKIP_CHECK, root, os.path.join(root, "tests"), mode], env=env,
+                       capture_output=True, text=True, timeout=110)
+    assert r.returncode == 0 and r.stdout.strip().endswith("ok"), r.stdout[-2000:] + r.stderr[-2000:]
+    log = [ln for ln in r.stderr.splitlines() if ln.startswith("[swm] ")]
+    assert any(ln.startswith("[swm] sparse_compress M=4096 K=11008") for ln in log), log
+    assert any(ln.startswith("[swm] dense_gemm M=4096 K=11008 N=1: streaming") for ln in log), log
+    cr = [ln for ln in log if "column-run skipping kernel" in ln]
+    dec = [ln for ln in log if ln.startswith("[swm] spmspv") and ": decode" in ln]
+    if mode == "off":
+        assert not cr and len(dec) == 2, log
+    else:
+        assert len(cr) == 2 and not dec, log
+
+
 def test_dense_gemm_graph_replay_after_larger_k(gpu_lib):
     """The streaming dense kernel allocates nothing: a captured small-K call
     still replays correctly after an eager call with a much larger K (the
