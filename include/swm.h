@@ -221,7 +221,7 @@ size_t swm_spmm_workspace_bytes(const swm_format* f, int64_t N);
  *  sparse-tensor-core layer plus a residual layer).  The result is the same
  *  product (fp32 summation order differs).  Measured on one MI355X it does not
  *  beat the expansion route (q_proj 4096x4096 with a 2:4 mask, N = 4096:
- *  138.5 against 145 us), hence opt-in.  The activations must fit 32-bit
+ *  144 against 134 us), hence opt-in.  The activations must fit 32-bit
  *  byte offsets ((N-1)*ldx + K < 2^31) and M*Kp < 2^32; otherwise the call
  *  expands as usual.
  *  workspace: DEVICE, 16-byte aligned, ws_bytes >= swm_spmm_workspace_bytes(f,

@@ -463,11 +463,11 @@ static bool expand_route(const swm::Header& h, int64_t N) {
 // handle with SWM_SMFMAC = 1; SWM_SMFMAC = 0 turns it off; read once).  It
 // is opt-in because on this chip it does not beat the expansion route: on
 // q_proj 4096x4096 with a 2:4 mask the SMFMAC kernel issues half the matrix
-// instructions of the dense kernel but is bound by LDS bandwidth (each step
-// reads the same activation fragments in half the matrix time), 126 against
-// 134 us at N = 4096, and with the compaction (21 us) the route is 138.5 us
-// against 145 us for the expansion route and 131 us dense; at N = 1024-2048
-// it is slower.  With a residual layer it runs twice the instructions.
+// instructions of the dense kernel but is bound by the activation side (each
+// step loads and reads the same activation tile in half the matrix time);
+// with the compaction (21 us) the route took 144 us at N = 4096 against
+// 134 us for the expansion route and 119 us dense, and it is slower at
+// N = 1024-2048.  With a residual layer it runs twice the instructions.
 static int smfmac_mode() {
   static const int v = [] {
     const char* e = getenv("SWM_SMFMAC");
