@@ -718,7 +718,11 @@ struct DecompArgs {
 
 __global__ __launch_bounds__(256) void decompress_kernel(DecompArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t run[4][1024];
-  __shared__ __attribute__((aligned(16))) uint16_t tile[4][16][72];
+  // A wave's 16 x 64 tile as 16 rows of 32 dwords (two fp16 each); dword d
+  // of row r is stored at d ^ swz(r), swz flipping bits 0, 1 and 4 by the row,
+  // so that neither the paired-column stores (16 rows x 4 column groups per
+  // instruction) nor the 16-byte row reads meet in an LDS bank.
+  __shared__ __attribute__((aligned(16))) uint32_t tile[4][16][32];
   const int lane = lane_id();
   const int wave = __builtin_amdgcn_readfirstlane(int(threadIdx.x >> 6));
   const int64_t t = int64_t(blockIdx.x) * 4 + wave;
@@ -737,16 +741,25 @@ __global__ __launch_bounds__(256) void decompress_kernel(DecompArgs a) {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  auto swz = [](int r) { return uint32_t(((r >> 1) & 3) | (((r >> 3) & 1) << 4)); };
+  const int row = lane & 15;
+  const uint32_t h = swz(row);
   uint32_t pos = 0;
 #pragma unroll
-  for (int w = 0; w < 16; ++w) {
-    const uint64_t word = word_of(w < 8 ? wa : wb, w & 7);
-    const bool set = (word >> lane) & 1ull;
-    const uint32_t rank =
-        __builtin_amdgcn_mbcnt_hi(uint32_t(word >> 32), __builtin_amdgcn_mbcnt_lo(uint32_t(word), 0u));
+  for (int w = 0; w < 16; w += 2) {
+    // words w and w + 1 hold this lane's columns col and col + 1 (col even)
+    uint32_t v2[2];
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const uint64_t word = word_of((w + e) < 8 ? wa : wb, (w + e) & 7);
+      const bool set = (word >> lane) & 1ull;
+      const uint32_t rank =
+          __builtin_amdgcn_mbcnt_hi(uint32_t(word >> 32), __builtin_amdgcn_mbcnt_lo(uint32_t(word), 0u));
+      v2[e] = set ? uint32_t(run[wave][min(pos + rank, 1023u)]) : 0u;
+      pos += uint32_t(__builtin_popcountll(word));
+    }
     const int col = 32 * (w >> 3) + 8 * (lane >> 4) + (w & 7);
-    tile[wave][lane & 15][col] = set ? run[wave][min(pos + rank, 1023u)] : uint16_t(0);
-    pos += uint32_t(__builtin_popcountll(word));
+    tile[wave][row][uint32_t(col >> 1) ^ h] = v2[0] | (v2[1] << 16);
   }
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
@@ -754,13 +767,18 @@ __global__ __launch_bounds__(256) void decompress_kernel(DecompArgs a) {
   // lane -> (row = lane/8 + 8*it, 8-column chunk = lane%8)
   for (int it = 0; it < 2; ++it) {
     const int r = it * 8 + (lane >> 3), ch = lane & 7;
-    const int64_t row = int64_t(slab) * kSlab + r, col = int64_t(tj) * kTK + ch * 8;
-    if (row >= a.M) continue;
-    if (a.vec && col + 8 <= a.K) {
-      *reinterpret_cast<u32x4*>(a.W + row * a.ldw + col) = *reinterpret_cast<const u32x4*>(&tile[wave][r][ch * 8]);
+    const uint32_t hr = swz(r);
+    // the chunk's four dwords: physical chunk ch ^ (bit 4 of swz) / 4, dword j at j ^ (swz & 3)
+    const u32x4 raw = *reinterpret_cast<const u32x4*>(&tile[wave][r][uint32_t(4 * ch) ^ (hr & 16u)]);
+    const u32x4 s1 = (hr & 1u) ? u32x4{raw[1], raw[0], raw[3], raw[2]} : raw;
+    const u32x4 c = (hr & 2u) ? u32x4{s1[2], s1[3], s1[0], s1[1]} : s1;
+    const int64_t grow = int64_t(slab) * kSlab + r, gcol = int64_t(tj) * kTK + ch * 8;
+    if (grow >= a.M) continue;
+    if (a.vec && gcol + 8 <= a.K) {
+      *reinterpret_cast<u32x4*>(a.W + grow * a.ldw + gcol) = c;
     } else {
       for (int e = 0; e < 8; ++e)
-        if (col + e < a.K) a.W[row * a.ldw + col + e] = tile[wave][r][ch * 8 + e];
+        if (gcol + e < a.K) a.W[grow * a.ldw + gcol + e] = uint16_t(c[e / 2] >> (16 * (e % 2)));
     }
   }
 }

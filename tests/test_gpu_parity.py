@@ -422,6 +422,19 @@ def test_dense_gemm_ragged(gpu_lib, M, K, N):
     assert_close(Y, oracle.masked_matmul(W, None, X), f"dense {M}x{K}x{N}")
 
 
+@pytest.mark.parametrize("block", ["1", "2", "3"])    # 256x256 (eight waves), 256x128, 128x128
+@pytest.mark.parametrize("M,K,N", [(300, 72, 40), (1000, 1032, 300), (257, 4104, 513), (4096, 256, 1024)])
+def test_dense_gemm_each_block_shape(gpu_lib, block, M, K, N, monkeypatch):
+    """Every block shape of the tiled dense kernel on ragged M, N and K
+    (K % 64 != 0 included); SWM_DENSE_BLOCK is read on every call."""
+    monkeypatch.setenv("SWM_DENSE_BLOCK", block)
+    g = np.random.default_rng(M + K + N)
+    W = (0.02 * g.standard_normal((M, K))).astype(np.float16)
+    X = g.standard_normal((N, K)).astype(np.float16)
+    Y = _np(gpu_lib.dense_gemm(_t(W), _t(X)))
+    assert_close(Y, oracle.masked_matmul(W, None, X), f"dense block {block} {M}x{K}x{N}")
+
+
 _REG_STAGED_CHECK = r"""
 import sys
 import numpy as np
