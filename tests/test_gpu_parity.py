@@ -1069,3 +1069,66 @@ def test_layer_linears_as_benchmarked(gpu_lib, i, N):
         ws, nb = _workspace(swm, f, N)
         assert nb > 0
         assert_close(_np(swm.spmm_ws(f, Xd, ws)), ref, f"linear {i} N={N} spmm_ws")
+
+
+# ------------------------------------------------------------------ guard bands and run-twice determinism
+def _guarded(torch, rows, cols, pad_rows=2, pad_cols=64):
+    """An fp16 buffer with guard bands around a (rows, cols) view; the view
+    starts 16-byte aligned and its leading dimension is a multiple of 8."""
+    buf = torch.full((rows + pad_rows, cols + pad_cols), 7.0, dtype=torch.float16, device="cuda")
+    view = buf[1:rows + 1, 32:32 + cols]
+    return buf, view
+
+
+def _guard_ok(buf, rows, cols):
+    b = _np(buf)
+    inside = np.zeros(b.shape, dtype=bool)
+    inside[1:rows + 1, 32:32 + cols] = True
+    return bool(np.all(b[~inside] == 7.0))
+
+
+@pytest.mark.parametrize("route,N", [("spmm", 5), ("spmm", 24), ("spmm", 300), ("spmm_ws", 1100),
+                                     ("dense", 7), ("dense", 300), ("spmspv_skip", 1), ("spmspv_skip", 2),
+                                     ("spmspv_tiled", 3), ("glu", 5), ("glu", 20)])
+def test_outputs_stay_in_their_view_and_repeat_bitwise(gpu_lib, route, N):
+    """Every product writes exactly its strided output view (a guard band of
+    7.0 around it stays intact) and a second call gives the same bits: the
+    reductions have a fixed order, so a difference would show a race."""
+    import torch
+    swm = gpu_lib
+    M, K = 1000, 1032
+    g = np.random.default_rng(N * 31 + len(route))
+    W = (0.02 * g.standard_normal((M, K))).astype(np.float16)
+    mask = g.random((M, K)) < 0.5
+    X = g.standard_normal((N, K)).astype(np.float16)
+    if route.startswith("spmspv"):
+        X[:, g.random(K) < 0.7] = 0
+    f = swm.sparse_compress(W, mask, skipping=route == "spmspv_skip")
+    fu = swm.sparse_compress((0.02 * g.standard_normal((M, K))).astype(np.float16), mask) if route == "glu" else None
+    Xd = _t(X)
+    outs = []
+    for _ in range(2):
+        buf, view = _guarded(torch, N, M)
+        if route == "spmm":
+            swm.spmm(f, Xd, view)
+            ref = oracle.masked_matmul(W, mask, X)
+        elif route == "spmm_ws":
+            ws, nb = _workspace(swm, f, N)
+            assert nb > 0
+            swm.spmm_ws(f, Xd, ws, view)
+            ref = oracle.masked_matmul(W, mask, X)
+        elif route == "dense":
+            swm.dense_gemm(_t(np.where(mask, W, np.float16(0))), Xd, view)
+            ref = oracle.masked_matmul(W, mask, X)
+        elif route.startswith("spmspv"):
+            swm.spmspv(f, Xd, view)
+            ref = oracle.masked_matmul_skip(W, mask, X)
+        else:
+            swm.gate_up_silu(f, fu, Xd, 0.0, view)
+            ref = None   # values: the gate/up parity tests
+        torch.cuda.synchronize()
+        assert _guard_ok(buf, N, M), f"{route} N={N} wrote outside its view"
+        if ref is not None:
+            assert_close(_np(view), ref, f"{route} N={N}")
+        outs.append(_np(view).copy())
+    assert np.array_equal(outs[0].view(np.uint16), outs[1].view(np.uint16)), f"{route} N={N} not repeatable"
