@@ -738,11 +738,12 @@ def bench_wide(args, torch, swm, wl, G):
 
 # ------------------------------------------------------------------ prefill on the sparse matrix cores
 def bench_smfmac(args, torch, swm, wl, G):
-    """The 2:4 + residual route (compact W into the 2:4 operand layout once
-    per call, then v_smfmac) against the expansion route (expand W to dense,
-    then the dense MFMA kernel) and the dense kernel on W (.) mask: q_proj
-    4096x4096 with a 2:4 mask (no residual layer) and up/gate 11008x4096 at
-    50/60/70% forced onto the route with its residual layer."""
+    """The 2:4 + residual route (W compacted into the 2:4 operand layout once,
+    at compress time; spmm_ws then runs v_smfmac) against the expansion route
+    (expand W to dense per call, then the dense MFMA kernel) and the dense
+    kernel on W (.) mask: q_proj 4096x4096 with a 2:4 mask (no residual
+    layer) and up/gate 11008x4096 at 50/60/70% forced onto the route with
+    its residual layer."""
     _log("workload: prefill on the sparse matrix cores")
     out = {"metric": "prefill useful TFLOP/s on the sparse matrix cores", "unit": "TFLOP/s", "n_gpus": 1,
            "higher_is_better": True, "dtype": "f16", "data": "synthetic", "detail": {}}
@@ -778,8 +779,7 @@ def bench_smfmac(args, torch, swm, wl, G):
             e = {k + "_us": v for k, v in t.items()}
             e.update({"useful_TFLOPs": useful / (t["smfmac_route"] * 1e-6) / 1e12,
                       "speedup_vs_dense": t["dense"] / t["smfmac_route"],
-                      "speedup_vs_expand": t["expand_route"] / t["smfmac_route"],
-                      "workspace_bytes": int(ws.numel())})
+                      "speedup_vs_expand": t["expand_route"] / t["smfmac_route"]})
             out["detail"][f"{name} N={n}"] = e
             _log(f"{name} N={n}: smfmac route {t['smfmac_route']:.1f} us, expand route {t['expand_route']:.1f} us, "
                  f"dense {t['dense']:.1f} us")

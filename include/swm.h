@@ -59,7 +59,7 @@
  *    / 3 (tiled dense block 256x256 / 256x128 / 128x128), SWM_EXPAND_MIN_N
  *    (tokens from which swm_spmm_ws expands W, at least 33; read once),
  *    SWM_GLU_TPW (tiles per wave of swm_gate_up_silu; read once), SWM_SMFMAC
- *    (0 / 1: the sparse-matrix-core prefill route off / for every handle;
+ *    (0: the sparse-matrix-core route of SWM_CFG_SMFMAC handles off;
  *    read once).
  */
 #ifndef SWM_H_
@@ -89,7 +89,7 @@ typedef struct swm_format swm_format;
 
 /* Compress options (swm_tile_cfg.flags). */
 #define SWM_CFG_SKIPPING 1 /* also build the column-run encoding of swm_format_enable_skipping */
-#define SWM_CFG_SMFMAC 2   /* swm_spmm_ws takes the sparse-matrix-core route (see swm_spmm_ws) */
+#define SWM_CFG_SMFMAC 2   /* keep 2:4 layers for the sparse-matrix-core route (see swm_spmm_ws) */
 
 /* Tile shape and compress options.  tm: rows per tile, must be 16.  tk:
  * columns per tile, a multiple of 32 (the product kernels take 64).  flags:
@@ -132,6 +132,11 @@ typedef struct swm_format_info {
  *  With cfg->flags = SWM_CFG_SKIPPING the handle also carries the column-run
  *  encoding that lets swm_spmspv skip zero activations (the same as calling
  *  swm_format_enable_skipping afterwards; the resident size roughly doubles).
+ *  With SWM_CFG_SMFMAC it also compacts W (.) mask on the device into the 2:4
+ *  layers of the sparse-matrix-core route (see swm_spmm_ws) and keeps them
+ *  (M*Kp*1.125 bytes per layer, Kp = K rounded up to 64; one layer for a
+ *  mask within 2:4, two otherwise).  An export blob does not carry them: an
+ *  imported handle runs the other routes.
  *  Synchronous: returns after the upload on `stream` has completed.
  *  *out receives a new handle owned by the caller (swm_format_destroy). */
 swm_status swm_sparse_compress(const uint16_t* W, int64_t ldw, const uint8_t* mask, int64_t ldm,
@@ -189,8 +194,8 @@ swm_status swm_spmm(const swm_format* f, const void* X, int64_t ldx, void* Y, in
                     int64_t N, void* stream);
 
 /* Bytes of device workspace swm_spmm_ws uses for N tokens on the current
- * device: M*K*2 rounded up to 256 when that call would expand W (on the
- * sparse-matrix-core route the compacted layers' size instead) (K a
+ * device: M*K*2 rounded up to 256 when that call would expand W (0 where a
+ * SWM_CFG_SMFMAC handle takes the sparse-matrix-core route instead) (K a
  * multiple of 8, and N >= 1024, or N >= 256 with the on-chip prefill
  * kernel's ceil(M/128)*ceil(N/256) blocks at most half the CUs or above one
  * round of them), else 0.  The SWM_EXPAND_MIN_N environment variable, read
@@ -209,21 +214,23 @@ size_t swm_spmm_workspace_bytes(const swm_format* f, int64_t N);
  * swm_decompress) and runs the library's dense MFMA kernel on it: two
  * launches on stream, the second reading what the first wrote.  Otherwise it
  * runs swm_spmm's kernels and leaves the workspace untouched.
- *  Sparse-matrix-core route (handles compressed with SWM_CFG_SMFMAC, or
- *  every handle when the SWM_SMFMAC environment variable is 1; 0 turns it
- *  off): where this call would expand W, it instead compacts W (.) mask into a
- *  2:4 layer (in every aligned group of 4 columns of a row, the first two
- *  kept entries) and, when some row keeps 3 or 4 of a group, a residual layer
- *  with the rest, each as values [M][Kp/2] fp16 plus 2-bit positions
- *  [M][Kp/16] uint16 (Kp = K rounded up to 64; M*Kp*1.125 bytes per layer),
- *  and multiplies both with v_smfmac_f32_32x32x32_f16 into one fp32
- *  accumulator (moderate-sparsity page, abstract and Sec. 1: a
- *  sparse-tensor-core layer plus a residual layer).  The result is the same
- *  product (fp32 summation order differs).  Measured on one MI355X it does not
- *  beat the expansion route (q_proj 4096x4096 with a 2:4 mask, N = 4096:
- *  144 against 134 us), hence opt-in.  The activations must fit 32-bit
- *  byte offsets ((N-1)*ldx + K < 2^31) and M*Kp < 2^32; otherwise the call
- *  expands as usual.
+ *  Sparse-matrix-core route (handles compressed with SWM_CFG_SMFMAC; the
+ *  SWM_SMFMAC environment variable 0 turns it off): at compress time W (.)
+ *  mask is compacted once into a 2:4 layer (in every aligned group of 4
+ *  columns of a row, the first two kept entries) and, when some row keeps 3
+ *  or 4 of a group, a residual layer with the rest, each as values [M][Kp/2]
+ *  fp16 plus 2-bit positions [M][Kp/16] uint16 (Kp = K rounded up to 64;
+ *  M*Kp*1.125 bytes per layer, device memory held by the handle beside the
+ *  tiled format).  Where this call (or swm_spmm) would expand W, it instead
+ *  multiplies both layers with v_smfmac_f32_32x32x32_f16 into one fp32
+ *  accumulator, with no workspace (moderate-sparsity page, abstract and Sec.
+ *  1: a sparse-tensor-core layer plus a residual layer).  The result is the
+ *  same product (fp32 summation order differs).  It pays only with a 2:4
+ *  mask and 256x256 output blocks on every CU (q_proj 4096x4096 at N = 4096
+ *  on one MI355X); a residual layer doubles its matrix instructions, hence
+ *  opt-in.  The activations must fit 32-bit byte offsets ((N-1)*ldx + K <
+ *  2^31) and M*Kp < 2^32, with X 16-byte aligned and ldx % 8 == 0; otherwise
+ *  the call takes the other routes.
  *  workspace: DEVICE, 16-byte aligned, ws_bytes >= swm_spmm_workspace_bytes(f,
  *  N), owned by the caller, contents undefined afterwards; it may be shared by
  *  the handles of several layers as long as the calls are ordered on one

@@ -206,9 +206,9 @@ class Format:
 def sparse_compress(W, mask=None, tile=(16, 64), stream=None, skipping=False, smfmac=False) -> Format:
     """Compress a host fp16 W (M, K) with an optional host mask; upload to the
     current device.  skipping=True also builds the column-run encoding that
-    lets spmspv skip zero activations (SWM_CFG_SKIPPING); smfmac=True makes
-    spmm_ws take the sparse-matrix-core route even when the mask needs a
-    residual layer (SWM_CFG_SMFMAC)."""
+    lets spmspv skip zero activations (SWM_CFG_SKIPPING); smfmac=True also
+    keeps W compacted into 2:4 layers, which spmm and spmm_ws multiply on the
+    sparse matrix cores at prefill token counts (SWM_CFG_SMFMAC)."""
     lib = load()
     w = _host_u16(W)
     m = _host_mask(mask, w.shape)

@@ -29,7 +29,8 @@ struct swm_format {
   void* cr_mem = nullptr;  // column-run encoding for activation skipping (optional)
   swm::DevColRuns cr;
   bool res24 = true;       // some row keeps 3 or 4 of an aligned group of 4 columns
-  bool smf_force = false;  // SWM_CFG_SMFMAC: the sparse-matrix-core route also with a residual layer
+  void* smf_mem = nullptr; // SWM_CFG_SMFMAC: the 2:4 layers (and residual layer), compacted once
+  swm::Sparse24Layout smf_layout;
 };
 
 namespace {
@@ -215,12 +216,26 @@ swm_status swm_sparse_compress(const uint16_t* W, int64_t ldw, const uint8_t* ma
   swm_format* f = nullptr;
   st = upload(std::move(blob), h, static_cast<hipStream_t>(stream), &f);
   if (st != SWM_OK) return st;
-  f->smf_force = cfg && (cfg->flags & SWM_CFG_SMFMAC);
+  if (cfg && (cfg->flags & SWM_CFG_SMFMAC) && h.tm == 16 && h.tk == 64 && h.m > 0) {
+    // compact once into the sparse-matrix-core layers; they stay with the handle
+    f->smf_layout = swm::sparse24_layout(h, f->res24);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = hipMalloc(&f->smf_mem, f->smf_layout.bytes);
+    if (e == hipSuccess) e = swm::launch_compact24(f->d, f->smf_layout, f->res24, f->smf_mem, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (e != hipSuccess) {
+      (void)swm_format_destroy(f);
+      return e == hipErrorOutOfMemory ? SWM_ERR_OOM : hip_fail(e);
+    }
+  }
   swm_log("sparse_compress M=%lld K=%lld nnz=%llu blob=%zu B flags=%d: decode split %d / %d tiles per wave "
           "(N <= 8 / <= 16), %s",
           (long long)h.m, (long long)h.k, (unsigned long long)h.nnz, f->blob.size(), cfg ? cfg->flags : 0,
           f->plan.tiles_per_wave, f->plan_wide.tiles_per_wave,
           f->res24 ? "mask exceeds 2:4 (SMFMAC needs a residual layer)" : "mask within 2:4");
+  if (f->smf_mem)
+    swm_log("sparse_compress: 2:4 layers resident, %zu B (%s)", f->smf_layout.bytes,
+            f->res24 ? "2:4 layer + residual layer" : "2:4 layer only");
   if (cfg && (cfg->flags & SWM_CFG_SKIPPING)) {
     st = swm_format_enable_skipping(f, stream, nullptr);
     if (st != SWM_OK) {
@@ -286,12 +301,16 @@ swm_status swm_size_dry_run(int64_t M, int64_t K, uint64_t nnz, const swm_tile_c
 swm_status swm_format_destroy(swm_format* f) {
   if (!f) return SWM_OK;
   swm_status st = SWM_OK;
-  if (f->dev_mem || f->cr_mem) {
+  if (f->dev_mem || f->cr_mem || f->smf_mem) {
     int cur = 0;
     (void)hipGetDevice(&cur);
     if (cur != f->device) (void)hipSetDevice(f->device);
     if (f->dev_mem) {
       hipError_t e = hipFree(f->dev_mem);
+      if (e != hipSuccess) st = hip_fail(e);
+    }
+    if (f->smf_mem) {
+      hipError_t e = hipFree(f->smf_mem);
       if (e != hipSuccess) st = hip_fail(e);
     }
     if (f->cr_mem) {
@@ -382,6 +401,9 @@ static const swm::DecodePlan& decode_plan(const swm_format* f, int64_t n) {
   return n <= 8 ? f->plan : n <= 16 ? f->plan_wide : f->plan_pair;
 }
 
+static bool run_smf(const swm_format* f, const void* X, int64_t ldx, void* Y, int64_t ldy, int64_t N,
+                    hipStream_t s, swm_status* st);
+
 static swm_status run_products(const swm_format* f, const void* X, int64_t ldx, void* Y, int64_t ldy,
                                int64_t N, bool skip, hipStream_t s) {
   if (!f || !X || !Y) return SWM_ERR_INVALID_ARG;
@@ -401,6 +423,8 @@ static swm_status run_products(const swm_format* f, const void* X, int64_t ldx, 
     SWM_HIP(swm::launch_decode(f->d, p, x, ldx, y, ldy, int(N), skip, s));
     return SWM_OK;
   }
+  swm_status sst = SWM_OK;
+  if (!skip && run_smf(f, X, ldx, Y, ldy, N, s, &sst)) return sst;
   if (!skip && swm::prefill_supported(f->h.k, ldx, X) && swm::prefill_sparse_lds(f->h) <= 160 * 1024 &&
       swm::prefill_sparse_fits(f->h, N, ldx)) {
     swm_log("spmm M=%lld K=%lld N=%lld: on-chip prefill (128x256 blocks)", (long long)f->h.m, (long long)f->h.k,
@@ -457,17 +481,14 @@ static bool expand_route(const swm::Header& h, int64_t N) {
   return 2 * blocks <= cus || blocks > cus;
 }
 
-// The sparse-matrix-core route (compact W into a 2:4 layer, plus a residual
-// layer where the mask needs one, then v_smfmac), taken where the expansion
-// route would be, for handles compressed with SWM_CFG_SMFMAC (or every
-// handle with SWM_SMFMAC = 1; SWM_SMFMAC = 0 turns it off; read once).  It
-// is opt-in because on this chip it does not beat the expansion route: on
-// q_proj 4096x4096 with a 2:4 mask the SMFMAC kernel issues half the matrix
-// instructions of the dense kernel but is bound by the activation side (each
-// step loads and reads the same activation tile in half the matrix time);
-// with the compaction (21 us) the route took 144 us at N = 4096 against
-// 134 us for the expansion route and 119 us dense, and it is slower at
-// N = 1024-2048.  With a residual layer it runs twice the instructions.
+// The sparse-matrix-core route: for handles compressed with SWM_CFG_SMFMAC,
+// whose 2:4 layer (plus a residual layer where the mask needs one) was
+// compacted once at compress time, swm_spmm and swm_spmm_ws multiply with
+// v_smfmac where the expansion route would run (same token counts), with no
+// workspace.  SWM_SMFMAC = 0 turns it off (read once).  It is opt-in because
+// it needs the layers resident beside the tiled format and only pays with a
+// 2:4 mask at full block occupancy (q_proj 4096x4096 at N = 4096); a residual
+// layer doubles its matrix instructions.
 static int smfmac_mode() {
   static const int v = [] {
     const char* e = getenv("SWM_SMFMAC");
@@ -477,15 +498,25 @@ static int smfmac_mode() {
 }
 
 static bool smf_route(const swm_format* f, int64_t N) {
-  if (f->h.tm != 16 || f->h.tk != 64 || !expand_route(f->h, N)) return false;
-  const int mode = smfmac_mode();
-  if (mode == 0) return false;
-  return mode == 1 || f->smf_force;
+  if (!f->smf_mem || f->h.tm != 16 || f->h.tk != 64 || smfmac_mode() == 0) return false;
+  return expand_route(f->h, N);
+}
+
+// The cached layers through v_smfmac; false when the operands do not fit the
+// kernel's 32-bit offsets or alignment (then the caller takes another route).
+static bool run_smf(const swm_format* f, const void* X, int64_t ldx, void* Y, int64_t ldy, int64_t N,
+                    hipStream_t s, swm_status* st) {
+  if (!smf_route(f, N) || !swm::prefill_supported(f->h.k, ldx, X) || !swm::smf_fits(f->h, N, ldx)) return false;
+  swm_log("spmm M=%lld K=%lld N=%lld: resident 2:4 layers + SMFMAC (%s)", (long long)f->h.m, (long long)f->h.k,
+          (long long)N, f->res24 ? "with residual layer" : "no residual");
+  const hipError_t e = swm::launch_smf(f->h, f->smf_layout, f->res24, f->smf_mem, static_cast<const uint16_t*>(X),
+                                       ldx, static_cast<uint16_t*>(Y), ldy, N, s);
+  *st = e == hipSuccess ? SWM_OK : hip_fail(e);
+  return true;
 }
 
 size_t swm_spmm_workspace_bytes(const swm_format* f, int64_t N) {
-  if (!f || !expand_route(f->h, N)) return 0;
-  if (smf_route(f, N)) return swm::sparse24_layout(f->h, f->res24).bytes;
+  if (!f || !expand_route(f->h, N) || smf_route(f, N)) return 0;
   return align_up(size_t(f->h.m) * size_t(f->h.k) * 2, 256);
 }
 
@@ -494,8 +525,8 @@ swm_status swm_spmm_ws(const swm_format* f, const void* X, int64_t ldx, void* Y,
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (!f || !X || !Y) return SWM_ERR_INVALID_ARG;
   if (!workspace && ws_bytes == 0) return run_products(f, X, ldx, Y, ldy, N, false, s);
-  if (!workspace) return SWM_ERR_INVALID_ARG;
   if (reinterpret_cast<uintptr_t>(workspace) & 15) return SWM_ERR_ALIGN;
+  if (!workspace) return SWM_ERR_INVALID_ARG;
   const size_t need = swm_spmm_workspace_bytes(f, N);
   if (need == 0 || !swm::prefill_supported(f->h.k, ldx, X)) return run_products(f, X, ldx, Y, ldy, N, false, s);
   if (ws_bytes < need) return SWM_ERR_INVALID_ARG;
@@ -503,15 +534,6 @@ swm_status swm_spmm_ws(const swm_format* f, const void* X, int64_t ldx, void* Y,
   swm_status st = check_tile_supported(f->h);
   if (st != SWM_OK) return st;
   if (!on_current_device(f)) return SWM_ERR_INVALID_ARG;
-  if (smf_route(f, N) && swm::smf_fits(f->h, N, ldx)) {
-    swm_log("spmm_ws M=%lld K=%lld N=%lld: 2:4 compaction + SMFMAC (%s)", (long long)f->h.m, (long long)f->h.k,
-            (long long)N, f->res24 ? "with residual layer" : "no residual");
-    const swm::Sparse24Layout L = swm::sparse24_layout(f->h, f->res24);
-    SWM_HIP(swm::launch_compact24(f->d, L, f->res24, workspace, s));
-    SWM_HIP(swm::launch_smf(f->h, L, f->res24, workspace, static_cast<const uint16_t*>(X), ldx,
-                            static_cast<uint16_t*>(Y), ldy, N, s));
-    return SWM_OK;
-  }
   swm_log("spmm_ws M=%lld K=%lld N=%lld: expand into the workspace + dense MFMA", (long long)f->h.m,
           (long long)f->h.k, (long long)N);
   uint16_t* w = static_cast<uint16_t*>(workspace);

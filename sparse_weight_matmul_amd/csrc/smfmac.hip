@@ -309,33 +309,33 @@ __global__ __launch_bounds__(256) void smf_kernel(SmfArgs a) {
     xcol[i] = 8 * ((lane & 7) ^ ((r >> 1) & 7));
     xoff[i] = 2u * uint32_t(min(n0 + r, a.N - 1)) * uint32_t(a.ldx) + 2u * uint32_t(xcol[i]);
   }
-  auto issue = [&](int kq) {
-    // past the end: a reload of the last step into the stage of step kq,
-    // which no later step reads
+  // load o of step kq: values 0-3, indices 4-5, [residual values 6-9,
+  // residual indices 10-11,] activations last (8).  Past the end: a reload of
+  // the last step into the stage of step kq, which no later step reads.
+  auto issue_op = [&](int kq, int o) {
     const int st = kq % S::kStages;
     const int ks = min(kq, nsteps - 1);
     const uint32_t vk = 64u * uint32_t(ks), mk = 8u * uint32_t(ks);
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      lds_dma16(vb + (voff[i] + vk), smem + oV(st) + (4 * wave + i) * 1024);
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-      lds_dma4(mb + (ioff[i] + mk), smem + oI(st) + (2 * wave + i) * 256);
-    if constexpr (kRes) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        lds_dma16(vrb + (voff[i] + vk), smem + oVr(st) + (4 * wave + i) * 1024);
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-        lds_dma4(mrb + (ioff[i] + mk), smem + oIr(st) + (2 * wave + i) * 256);
-    }
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    constexpr int kB0 = kRes ? 12 : 6;  // first activation load
+    if (o < 4) {
+      lds_dma16(vb + (voff[o] + vk), smem + oV(st) + (4 * wave + o) * 1024);
+    } else if (o < 6) {
+      lds_dma4(mb + (ioff[o - 4] + mk), smem + oI(st) + (2 * wave + o - 4) * 256);
+    } else if (kRes && o < 10) {
+      lds_dma16(vrb + (voff[o - 6] + vk), smem + oVr(st) + (4 * wave + o - 6) * 1024);
+    } else if (kRes && o < 12) {
+      lds_dma4(mrb + (ioff[o - 10] + mk), smem + oIr(st) + (2 * wave + o - 10) * 256);
+    } else {
+      const int i = o - kB0;
       const bool in = ks * SBK + xcol[i] < a.K;  // K % 8 == 0: a chunk is wholly inside or outside
       const void* src = in ? static_cast<const void*>(xb + (xoff[i] + 128u * uint32_t(ks)))
                            : static_cast<const void*>(g_smf_zero);
       lds_dma16(src, smem + oB(st) + (8 * wave + i) * 1024);
     }
+  };
+  auto issue = [&](int kq) {
+#pragma unroll
+    for (int o = 0; o < S::kOps; ++o) issue_op(kq, o);
   };
 
   f32x16 acc[4][4];
@@ -346,108 +346,145 @@ __global__ __launch_bounds__(256) void smf_kernel(SmfArgs a) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
-#pragma unroll
-  for (int p = 0; p < S::kStages - 1; ++p) issue(p);
-
   const int q = lane >> 5, lr = lane & 31;
+  // Fragments by slice (slot s = slice s of a step): compressed A values of
+  // both layers, B as two 16-byte halves, and one 8-byte index read per row
+  // holding both slices' index words.
+  half8 fa[2][4], far_[2][4];
+  half16 fb[2][4];
+  u32x2 iv[4], ivr[4];
+  auto read_a = [&](int st, int s, int i) {
+    const int row = (wm * 4 + i) * 32 + lr;
+    fa[s][i] = __builtin_bit_cast(half8, lds_load16(base + oV(st) + swz_a(row, 2 * s + q)));
+    if constexpr (kRes) far_[s][i] = __builtin_bit_cast(half8, lds_load16(base + oVr(st) + swz_a(row, 2 * s + q)));
+  };
+  auto read_b = [&](int st, int s, int j) {
+    // tokens (wn*4 + j)*32 + lr, slice rows 8q .. +7 and 16 + 8q .. +7
+    const int tok = (wn * 4 + j) * 32 + lr;
+    const u32x4 lo = lds_load16(base + oB(st) + swz_b(tok, 4 * s + q));
+    const u32x4 hi = lds_load16(base + oB(st) + swz_b(tok, 4 * s + 2 + q));
+    fb[s][j] = __builtin_bit_cast(half16, u32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
+  };
+  auto read_i = [&](int st, int i) {
+    const int row = (wm * 4 + i) * 32 + lr;
+    iv[i] = *reinterpret_cast<const lds_u32x2*>(static_cast<uintptr_t>(base + oI(st) + row * 8));
+    if constexpr (kRes) ivr[i] = *reinterpret_cast<const lds_u32x2*>(static_cast<uintptr_t>(base + oIr(st) + row * 8));
+  };
+  // read unit u of a slice: A rows i = u (u < 4), else B tokens j = u - 4
+  auto read_unit = [&](int st, int s, int u) {
+    if (u < 4) read_a(st, s, u);
+    else read_b(st, s, u - 4);
+  };
+  // index word of slice s for lane half q: uint16 number 2s + q of the row
+  auto idx = [&](const u32x2& v, int s) { return int((v[s] >> (16 * q)) & 0xFFFFu); };
+  int x1[4], x1r[4];  // slice 1's index words, kept while the next step's are read
+  auto product = [&](int s, int m, const int* xi, const int* xr) {
+    const int i = m >> 2, j = m & 3;
+    acc[i][j] = __builtin_amdgcn_smfmac_f32_32x32x32_f16(fa[s][i], fb[s][j], acc[i][j], xi[i], 0, 0);
+    if constexpr (kRes)
+      acc[i][j] = __builtin_amdgcn_smfmac_f32_32x32x32_f16(far_[s][i], fb[s][j], acc[i][j], xr[i], 0, 0);
+  };
+  constexpr int kRead = 8;                 // read units per slice (4 A, 4 B)
+  constexpr int kNext = 4 + kRead;         // step ks + 1: 4 index units, then slice 0's read units
+
+  // Steps 0 .. kStages-1 fill every stage; step ks + kStages is requested in
+  // step ks once every wave holds its last fragments of step ks.
+#pragma unroll
+  for (int p = 0; p < S::kStages; ++p) issue(p);
+  wait_vm_lgkm0<(S::kStages - 1) * S::kOps>();
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) read_i(0, i);
+#pragma unroll
+  for (int u = 0; u < kRead; ++u) read_unit(0, 0, u);
+  __builtin_amdgcn_sched_barrier(0);
+
+  // Per step: slice 0's 16 products with slice 1's reads in their first half;
+  // slice 1's first product, the step's barrier (slice 1's fragments are in
+  // registers, this wave's loads of step ks + 1 are in LDS; after it both
+  // hold for every wave), then step ks + 1's index and slice-0 reads and the
+  // loads of step ks + kStages (into the stage just released) between the
+  // remaining 15 products.  sched_barrier pins the order.
   for (int ks = 0; ks < nsteps; ++ks) {
-    const int st = ks % S::kStages;
-    // step ks's tiles are in (this wave's later requests may still be in
-    // flight), every wave is done with the stage the next request refills
+    const int st = ks % S::kStages, nst = (ks + 1) % S::kStages;
+    int x0[4], x0r[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      x0[i] = idx(iv[i], 0);
+      x1[i] = idx(iv[i], 1);
+      if constexpr (kRes) {
+        x0r[i] = idx(ivr[i], 0);
+        x1r[i] = idx(ivr[i], 1);
+      }
+    }
+#pragma unroll
+    for (int m = 0; m < 16; ++m) {
+      product(0, m, x0, x0r);
+#pragma unroll
+      for (int u = m * kRead / 8; u < (m + 1) * kRead / 8 && u < kRead; ++u) read_unit(st, 1, u);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    product(1, 0, x1, x1r);
     __builtin_amdgcn_sched_barrier(0);
     wait_vm_lgkm0<(S::kStages - 2) * S::kOps>();
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
-    issue(ks + S::kStages - 1);
-    __builtin_amdgcn_sched_barrier(0);
-    // Fragments, double buffered by slice.  One 8-byte read per row brings
-    // the index words of both slices; slice 0's operands are read first,
-    // slice 1's are spread between slice 0's products (at most 12 LDS reads
-    // in flight: the LDS counter has 4 bits).
-    half8 fa[2][4], far_[2][4];
-    half16 fb[2][4];
-    u32x2 iv[4], ivr[4];
-    auto load_a = [&](int s) {
+    // reads first, then the loads; none after the last two products
+    constexpr int kE = kNext + S::kOps;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int row = (wm * 4 + i) * 32 + lr;
-        fa[s][i] = __builtin_bit_cast(half8, lds_load16(base + oV(st) + swz_a(row, 2 * s + q)));
-        if constexpr (kRes) far_[s][i] = __builtin_bit_cast(half8, lds_load16(base + oVr(st) + swz_a(row, 2 * s + q)));
+    for (int m = 1; m < 16; ++m) {
+#pragma unroll
+      for (int e = (m - 1) * kE / 14; e < m * kE / 14 && e < kE; ++e) {
+        if (e < 4)
+          read_i(nst, e);  // unused after the last step
+        else if (e < kNext)
+          read_unit(nst, 0, e - 4);
+        else
+          issue_op(ks + S::kStages, e - kNext);
       }
-    };
-    auto load_b = [&](int s) {
-      // tokens (wn*4 + j)*32 + lr, slice rows 8q .. +7 and 16 + 8q .. +7
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int tok = (wn * 4 + j) * 32 + lr;
-        const u32x4 lo = lds_load16(base + oB(st) + swz_b(tok, 4 * s + q));
-        const u32x4 hi = lds_load16(base + oB(st) + swz_b(tok, 4 * s + 2 + q));
-        fb[s][j] = __builtin_bit_cast(half16, u32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
-      }
-    };
-    // index word of slice s for lane half q: uint16 number 2s + q of the row
-    auto idx = [&](const u32x2& v, int s) { return int((v[s] >> (16 * q)) & 0xFFFFu); };
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = (wm * 4 + i) * 32 + lr;
-      iv[i] = *reinterpret_cast<const lds_u32x2*>(static_cast<uintptr_t>(base + oI(st) + row * 8));
-      if constexpr (kRes) ivr[i] = *reinterpret_cast<const lds_u32x2*>(static_cast<uintptr_t>(base + oIr(st) + row * 8));
+      product(1, m, x1, x1r);
+      __builtin_amdgcn_sched_barrier(0);
     }
-    load_a(0);
-    load_b(0);
-    __builtin_amdgcn_sched_barrier(0);
-    load_a(1);
-    load_b(1);
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        acc[i][j] = __builtin_amdgcn_smfmac_f32_32x32x32_f16(fa[0][i], fb[0][j], acc[i][j], idx(iv[i], 0), 0, 0);
-        if constexpr (kRes)
-          acc[i][j] = __builtin_amdgcn_smfmac_f32_32x32x32_f16(far_[0][i], fb[0][j], acc[i][j], idx(ivr[i], 0), 0, 0);
-      }
-    // slice 0's products with slice 1's reads between them
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      __builtin_amdgcn_sched_group_barrier(0x100, kRes ? 4 : 3, 0);  // DS read
-      __builtin_amdgcn_sched_group_barrier(0x008, kRes ? 8 : 4, 0);  // MFMA
-    }
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        acc[i][j] = __builtin_amdgcn_smfmac_f32_32x32x32_f16(fa[1][i], fb[1][j], acc[i][j], idx(iv[i], 1), 0, 0);
-        if constexpr (kRes)
-          acc[i][j] = __builtin_amdgcn_smfmac_f32_32x32x32_f16(far_[1][i], fb[1][j], acc[i][j], idx(ivr[i], 1), 0, 0);
-      }
   }
-  // drain the trailing (never read) requests before the wave ends
-  wait_vm_lgkm0<0>();
 
-  // epilogue: fp16 round-to-nearest-even, 4 consecutive rows per 8-byte store
+  // Epilogue: fp16 round-to-nearest-even.  Each wave transposes its 128 x 128
+  // quadrant through its own LDS region (a row per token, padded by 8 bytes)
+  // so that the stores are 16 contiguous bytes per lane; every wave's loads
+  // must have landed before any region is written.
+  wait_vm_lgkm0<0>();
+  __builtin_amdgcn_s_barrier();
+  constexpr int kRS = 2 * 128 + 8;
+  const uint32_t reg = base + wave * (128 * kRS);
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int n = n0 + (wn * 4 + j) * 32 + (lane & 31);
-      if (n >= a.N) continue;
+    for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int qq = 0; qq < 4; ++qq) {
-        const int m = m0 + (wm * 4 + i) * 32 + qq * 8 + (lane >> 5) * 4;
+        const int n = j * 32 + (lane & 31), m = i * 32 + qq * 8 + (lane >> 5) * 4;
         uint16_t h[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) h[e] = __builtin_bit_cast(uint16_t, _Float16(acc[i][j][qq * 4 + e]));
-        uint16_t* dst = a.Y + int64_t(n) * a.ldy + m;
-        if (m + 3 < a.M && ((reinterpret_cast<uintptr_t>(dst) & 7) == 0)) {
-          *reinterpret_cast<u32x2*>(dst) =
-              u32x2{uint32_t(h[0]) | (uint32_t(h[1]) << 16), uint32_t(h[2]) | (uint32_t(h[3]) << 16)};
-        } else {
-          for (int e = 0; e < 4; ++e)
-            if (m + e < a.M) dst[e] = h[e];
-        }
+        *reinterpret_cast<lds_u32x2*>(static_cast<uintptr_t>(reg + n * kRS + 2 * m)) =
+            u32x2{uint32_t(h[0]) | (uint32_t(h[1]) << 16), uint32_t(h[2]) | (uint32_t(h[3]) << 16)};
       }
+  const int gm = m0 + wm * 128 + (lane & 15) * 8;
+  const bool vec = (a.ldy % 8 == 0) && ((reinterpret_cast<uintptr_t>(a.Y) & 15) == 0) && gm + 8 <= a.M;
+#pragma unroll
+  for (int r = 0; r < 128; r += 4) {
+    const int nl = r + (lane >> 4);
+    const int n = n0 + wn * 128 + nl;
+    const u32x4 v = lds_load16(reg + nl * kRS + (lane & 15) * 16);
+    if (n >= a.N) continue;
+    uint16_t* dst = a.Y + int64_t(n) * a.ldy + gm;
+    if (vec) {
+      *reinterpret_cast<u32x4*>(dst) = v;
+    } else {
+      for (int e = 0; e < 8; ++e)
+        if (gm + e < a.M) dst[e] = uint16_t(v[e / 2] >> (16 * (e % 2)));
     }
+  }
 }
 
 }  // namespace
@@ -488,8 +525,10 @@ hipError_t launch_compact24(const DevFormat& f, const Sparse24Layout& L, bool re
 }
 
 size_t smf_lds(bool residual) {
-  return residual ? size_t(SmfShape<true>::kStages) * SmfShape<true>::kStage
-                  : size_t(SmfShape<false>::kStages) * SmfShape<false>::kStage;
+  // the stages, or the epilogue's four transposing regions if larger
+  const size_t stages = residual ? size_t(SmfShape<true>::kStages) * SmfShape<true>::kStage
+                                 : size_t(SmfShape<false>::kStages) * SmfShape<false>::kStage;
+  return std::max<size_t>(stages, size_t(4) * 128 * (2 * 128 + 8));
 }
 
 bool smf_fits(const Header& h, int64_t N, int64_t ldx) {

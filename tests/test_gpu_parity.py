@@ -743,18 +743,21 @@ def _layer24_bytes(M, K, residual):
 @pytest.mark.parametrize("N", [1024, 2048, 4096])
 def test_smfmac_route_2_4_qproj(gpu_lib, N):
     """q_proj 4096x4096 with a 2:4 magnitude mask on the sparse-matrix-core
-    route: no residual layer, so spmm_ws compacts W into the 2:4 operand
-    layout (workspace 1.125 bytes per position) and runs v_smfmac; full
-    outputs against the oracle.  Without the option the handle expands."""
+    route: no residual layer; the handle keeps the 2:4 layer compacted at
+    compress time, so spmm_ws needs no workspace and spmm takes the same
+    kernel (bitwise equal); full outputs against the oracle.  Without the
+    option the handle expands."""
     swm = gpu_lib
     W, mask, _ = wl.decode_qproj_2_4(1)
     X = wl.activations(wl.CFG_WIDE, 13, N, 4096)
     assert swm.spmm_workspace_bytes(swm.sparse_compress(W, mask), N) == 2 * 4096 * 4096
     f = swm.sparse_compress(W, mask, smfmac=True)
-    ws, nb = _workspace(swm, f, N)
-    assert nb == _layer24_bytes(4096, 4096, False)
-    Y = _np(swm.spmm_ws(f, _t(X), ws))
+    ws, nb = _workspace(swm, f, N, extra=256)
+    assert nb == 0
+    Xd = _t(X)
+    Y = _np(swm.spmm_ws(f, Xd, ws))
     assert_close(Y, oracle.masked_matmul(W, mask, X), f"2:4 q_proj N={N}")
+    assert np.array_equal(Y.view(np.uint16), _np(swm.spmm(f, Xd)).view(np.uint16))
 
 
 @pytest.mark.parametrize("M,K,N,s", [(520, 392, 1100, 0.5), (300, 4104, 1024, 0.7), (1000, 1024, 1031, 0.6),
@@ -768,9 +771,8 @@ def test_smfmac_route_with_residual(gpu_lib, M, K, N, s):
     W, mask = wl.pruned_weight(105, M + K + N, M, K, s)
     X = wl.activations(105, M + N, N, K)
     f = swm.sparse_compress(W, mask, smfmac=True)
-    ws, nb = _workspace(swm, f, N)
-    assert nb == _layer24_bytes(M, K, s < 1.0)
-    Y = _np(swm.spmm_ws(f, _t(X), ws))
+    assert swm.spmm_workspace_bytes(f, N) == 0
+    Y = _np(swm.spmm(f, _t(X)))
     assert_close(Y, oracle.masked_matmul(W, mask, X), f"smfmac {M}x{K}x{N} s={s}")
     if s == 1.0:
         assert np.all(Y.view(np.uint16) == 0)
@@ -778,12 +780,13 @@ def test_smfmac_route_with_residual(gpu_lib, M, K, N, s):
 
 def test_smfmac_route_upgate_70_full(gpu_lib):
     """up/gate 11008x4096 at 70% (the config's highest sparsity) forced onto
-    the sparse matrix cores with its residual layer, N = 2048, full outputs."""
+    the sparse matrix cores with its residual layer, N = 2048, full outputs;
+    below the route's token counts the same handle decodes as usual."""
     swm = gpu_lib
     W, mask, X = wl.prefill_upgate(0.7, 2048)
     f = swm.sparse_compress(W, mask, smfmac=True)
-    ws, _ = _workspace(swm, f, 2048)
-    assert_close(_np(swm.spmm_ws(f, _t(X), ws)), oracle.masked_matmul(W, mask, X), "up/gate 70% smfmac")
+    assert_close(_np(swm.spmm(f, _t(X))), oracle.masked_matmul(W, mask, X), "up/gate 70% smfmac")
+    assert_close(_np(swm.spmm(f, _t(X[:16]))), oracle.masked_matmul(W, mask, X[:16]), "up/gate 70% decode")
 
 
 def test_spmm_ws_errors(gpu_lib):
