@@ -509,8 +509,11 @@ static bool run_smf(const swm_format* f, const void* X, int64_t ldx, void* Y, in
   if (!smf_route(f, N) || !swm::prefill_supported(f->h.k, ldx, X) || !swm::smf_fits(f->h, N, ldx)) return false;
   swm_log("spmm M=%lld K=%lld N=%lld: resident 2:4 layers + SMFMAC (%s)", (long long)f->h.m, (long long)f->h.k,
           (long long)N, f->res24 ? "with residual layer" : "no residual");
-  const hipError_t e = swm::launch_smf(f->h, f->smf_layout, f->res24, f->smf_mem, static_cast<const uint16_t*>(X),
-                                       ldx, static_cast<uint16_t*>(Y), ldy, N, s);
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess)
+    e = swm::launch_smf(f->h, f->smf_layout, f->res24, f->smf_mem, static_cast<const uint16_t*>(X), ldx,
+                        static_cast<uint16_t*>(Y), ldy, N, num_cus(dev), s);
   *st = e == hipSuccess ? SWM_OK : hip_fail(e);
   return true;
 }

@@ -107,8 +107,7 @@ struct Sparse24Layout {
 Sparse24Layout sparse24_layout(const Header& h, bool residual);
 hipError_t launch_compact24(const DevFormat& f, const Sparse24Layout& L, bool residual, void* ws, hipStream_t s);
 hipError_t launch_smf(const Header& h, const Sparse24Layout& L, bool residual, const void* ws, const uint16_t* X,
-                      int64_t ldx, uint16_t* Y, int64_t ldy, int64_t N, hipStream_t s);
-size_t smf_lds(bool residual);
+                      int64_t ldx, uint16_t* Y, int64_t ldy, int64_t N, int num_cus, hipStream_t s);
 // The SMFMAC kernel addresses the compacted layers and X with 32-bit byte offsets.
 bool smf_fits(const Header& h, int64_t N, int64_t ldx);
 

@@ -211,15 +211,23 @@ __device__ __forceinline__ uint32_t swz_a(int row, int chunk) {
   return uint32_t(row * 64 + ((chunk ^ ((row >> 2) & 3)) << 4));
 }
 
-constexpr int SBM = 256, SBN = 256, SBK = 64;
+constexpr int SBM = 256, SBK = 64;
 constexpr int kSA = SBM * SBK;       // values bytes per stage (32 halves per row)
 constexpr int kSM = SBM * 8;         // index bytes per stage (4 uint16 per row)
-constexpr int kSB = SBN * SBK * 2;   // activation bytes per stage
-template <bool kRes>
+// Block of 256 rows x 64 kWJ tokens: waves 2 x 2, each 4 x kWJ accumulators
+// of 32 x 32.  kWJ = 4 (256 x 256) or 2 (256 x 128, for token counts that
+// leave 256 x 256 blocks short of the CUs).
+template <bool kRes, int kWJ>
 struct SmfShape {
-  static constexpr int kStages = kRes ? 2 : 3;  // LDS stages (3 x 50 KiB, or 2 x 68 KiB with the residual)
+  static constexpr int kBN = 64 * kWJ;          // tokens per block
+  static constexpr int kSB = kBN * SBK * 2;     // activation bytes per stage
+  static constexpr int kIB = kSB / 4096;        // activation loads per wave per step
   static constexpr int kStage = kSA + kSM + (kRes ? kSA + kSM : 0) + kSB;
-  static constexpr int kOps = 14 + (kRes ? 6 : 0);  // LDS-direct loads per wave per step
+  static constexpr int kStages = 3 * kStage <= 160 * 1024 ? 3 : 2;  // LDS stages
+  static constexpr int kOps = 6 + (kRes ? 6 : 0) + kIB;  // LDS-direct loads per wave per step
+  static constexpr int kEpi = 4 * (32 * kWJ) * (2 * 128 + 8);  // epilogue: four transposing regions
+  static constexpr int kLds = kStages * kStage > kEpi ? kStages * kStage : kEpi;
+  static_assert(kLds <= 160 * 1024, "LDS");
 };
 
 // Sixteen zero bytes: the source of activation chunks past K.
@@ -254,9 +262,9 @@ __device__ __forceinline__ void wait_vm_lgkm0() {
 // the wait before that barrier is explicit: at most the later steps' loads
 // may still be in flight.  kRes: the residual layer is staged and multiplied
 // too, into the same accumulators.
-template <bool kRes>
+template <bool kRes, int kWJ>
 __global__ __launch_bounds__(256) void smf_kernel(SmfArgs a) {
-  using S = SmfShape<kRes>;
+  using S = SmfShape<kRes, kWJ>;
   constexpr int kStage = S::kStage;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   int tm, tn;
@@ -265,7 +273,7 @@ __global__ __launch_bounds__(256) void smf_kernel(SmfArgs a) {
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
-  const int m0 = tm * SBM, n0 = tn * SBN;
+  const int m0 = tm * SBM, n0 = tn * S::kBN;
   // stage layout: values | indices | [residual values | residual indices] | activations
   auto oV = [&](int st) { return uint32_t(st * kStage); };
   auto oI = [&](int st) { return uint32_t(st * kStage + kSA); };
@@ -290,8 +298,8 @@ __global__ __launch_bounds__(256) void smf_kernel(SmfArgs a) {
   const uint8_t* vrb = reinterpret_cast<const uint8_t*>(a.vres);
   const uint8_t* mb = reinterpret_cast<const uint8_t*>(a.m24);
   const uint8_t* mrb = reinterpret_cast<const uint8_t*>(a.mres);
-  uint32_t voff[4], ioff[2], xoff[8];
-  int xcol[8];
+  uint32_t voff[4], ioff[2], xoff[S::kIB];
+  int xcol[S::kIB];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int r = 16 * (4 * wave + i) + (lane >> 2);
@@ -304,8 +312,8 @@ __global__ __launch_bounds__(256) void smf_kernel(SmfArgs a) {
     ioff[i] = 2u * uint32_t(min(m0 + r, a.M - 1)) * uint32_t(a.ldm) + 4u * uint32_t(lane & 1);
   }
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int r = 8 * (8 * wave + i) + (lane >> 3);
+  for (int i = 0; i < S::kIB; ++i) {
+    const int r = 8 * (S::kIB * wave + i) + (lane >> 3);
     xcol[i] = 8 * ((lane & 7) ^ ((r >> 1) & 7));
     xoff[i] = 2u * uint32_t(min(n0 + r, a.N - 1)) * uint32_t(a.ldx) + 2u * uint32_t(xcol[i]);
   }
@@ -330,7 +338,7 @@ __global__ __launch_bounds__(256) void smf_kernel(SmfArgs a) {
       const bool in = ks * SBK + xcol[i] < a.K;  // K % 8 == 0: a chunk is wholly inside or outside
       const void* src = in ? static_cast<const void*>(xb + (xoff[i] + 128u * uint32_t(ks)))
                            : static_cast<const void*>(g_smf_zero);
-      lds_dma16(src, smem + oB(st) + (8 * wave + i) * 1024);
+      lds_dma16(src, smem + oB(st) + (S::kIB * wave + i) * 1024);
     }
   };
   auto issue = [&](int kq) {
@@ -338,11 +346,11 @@ __global__ __launch_bounds__(256) void smf_kernel(SmfArgs a) {
     for (int o = 0; o < S::kOps; ++o) issue_op(kq, o);
   };
 
-  f32x16 acc[4][4];
+  f32x16 acc[4][kWJ];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < kWJ; ++j)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
@@ -351,7 +359,7 @@ __global__ __launch_bounds__(256) void smf_kernel(SmfArgs a) {
   // both layers, B as two 16-byte halves, and one 8-byte index read per row
   // holding both slices' index words.
   half8 fa[2][4], far_[2][4];
-  half16 fb[2][4];
+  half16 fb[2][kWJ];
   u32x2 iv[4], ivr[4];
   auto read_a = [&](int st, int s, int i) {
     const int row = (wm * 4 + i) * 32 + lr;
@@ -360,7 +368,7 @@ __global__ __launch_bounds__(256) void smf_kernel(SmfArgs a) {
   };
   auto read_b = [&](int st, int s, int j) {
     // tokens (wn*4 + j)*32 + lr, slice rows 8q .. +7 and 16 + 8q .. +7
-    const int tok = (wn * 4 + j) * 32 + lr;
+    const int tok = (wn * kWJ + j) * 32 + lr;
     const u32x4 lo = lds_load16(base + oB(st) + swz_b(tok, 4 * s + q));
     const u32x4 hi = lds_load16(base + oB(st) + swz_b(tok, 4 * s + 2 + q));
     fb[s][j] = __builtin_bit_cast(half16, u32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
@@ -379,12 +387,13 @@ __global__ __launch_bounds__(256) void smf_kernel(SmfArgs a) {
   auto idx = [&](const u32x2& v, int s) { return int((v[s] >> (16 * q)) & 0xFFFFu); };
   int x1[4], x1r[4];  // slice 1's index words, kept while the next step's are read
   auto product = [&](int s, int m, const int* xi, const int* xr) {
-    const int i = m >> 2, j = m & 3;
+    const int i = m / kWJ, j = m % kWJ;
     acc[i][j] = __builtin_amdgcn_smfmac_f32_32x32x32_f16(fa[s][i], fb[s][j], acc[i][j], xi[i], 0, 0);
     if constexpr (kRes)
       acc[i][j] = __builtin_amdgcn_smfmac_f32_32x32x32_f16(far_[s][i], fb[s][j], acc[i][j], xr[i], 0, 0);
   };
-  constexpr int kRead = 8;                 // read units per slice (4 A, 4 B)
+  constexpr int kRead = 4 + kWJ;           // read units per slice (4 A, kWJ B)
+  constexpr int kM = 4 * kWJ;              // products per slice
   constexpr int kNext = 4 + kRead;         // step ks + 1: 4 index units, then slice 0's read units
 
   // Steps 0 .. kStages-1 fill every stage; step ks + kStages is requested in
@@ -400,12 +409,12 @@ __global__ __launch_bounds__(256) void smf_kernel(SmfArgs a) {
   for (int u = 0; u < kRead; ++u) read_unit(0, 0, u);
   __builtin_amdgcn_sched_barrier(0);
 
-  // Per step: slice 0's 16 products with slice 1's reads in their first half;
+  // Per step: slice 0's products with slice 1's reads in their first half;
   // slice 1's first product, the step's barrier (slice 1's fragments are in
   // registers, this wave's loads of step ks + 1 are in LDS; after it both
   // hold for every wave), then step ks + 1's index and slice-0 reads and the
   // loads of step ks + kStages (into the stage just released) between the
-  // remaining 15 products.  sched_barrier pins the order.
+  // remaining products.  sched_barrier pins the order.
   for (int ks = 0; ks < nsteps; ++ks) {
     const int st = ks % S::kStages, nst = (ks + 1) % S::kStages;
     int x0[4], x0r[4];
@@ -419,10 +428,11 @@ __global__ __launch_bounds__(256) void smf_kernel(SmfArgs a) {
       }
     }
 #pragma unroll
-    for (int m = 0; m < 16; ++m) {
+    for (int m = 0; m < kM; ++m) {
       product(0, m, x0, x0r);
+      // all reads in the first half: they land before slice 1 starts
 #pragma unroll
-      for (int u = m * kRead / 8; u < (m + 1) * kRead / 8 && u < kRead; ++u) read_unit(st, 1, u);
+      for (int u = m * kRead / (kM / 2); u < (m + 1) * kRead / (kM / 2) && u < kRead; ++u) read_unit(st, 1, u);
       __builtin_amdgcn_sched_barrier(0);
     }
     product(1, 0, x1, x1r);
@@ -433,9 +443,9 @@ __global__ __launch_bounds__(256) void smf_kernel(SmfArgs a) {
     // reads first, then the loads; none after the last two products
     constexpr int kE = kNext + S::kOps;
 #pragma unroll
-    for (int m = 1; m < 16; ++m) {
+    for (int m = 1; m < kM; ++m) {
 #pragma unroll
-      for (int e = (m - 1) * kE / 14; e < m * kE / 14 && e < kE; ++e) {
+      for (int e = (m - 1) * kE / (kM - 2); e < m * kE / (kM - 2) && e < kE; ++e) {
         if (e < 4)
           read_i(nst, e);  // unused after the last step
         else if (e < kNext)
@@ -454,12 +464,12 @@ __global__ __launch_bounds__(256) void smf_kernel(SmfArgs a) {
   // must have landed before any region is written.
   wait_vm_lgkm0<0>();
   __builtin_amdgcn_s_barrier();
-  constexpr int kRS = 2 * 128 + 8;
-  const uint32_t reg = base + wave * (128 * kRS);
+  constexpr int kRS = 2 * 128 + 8, kTN = 32 * kWJ;
+  const uint32_t reg = base + wave * (kTN * kRS);
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < kWJ; ++j)
 #pragma unroll
       for (int qq = 0; qq < 4; ++qq) {
         const int n = j * 32 + (lane & 31), m = i * 32 + qq * 8 + (lane >> 5) * 4;
@@ -472,9 +482,9 @@ __global__ __launch_bounds__(256) void smf_kernel(SmfArgs a) {
   const int gm = m0 + wm * 128 + (lane & 15) * 8;
   const bool vec = (a.ldy % 8 == 0) && ((reinterpret_cast<uintptr_t>(a.Y) & 15) == 0) && gm + 8 <= a.M;
 #pragma unroll
-  for (int r = 0; r < 128; r += 4) {
+  for (int r = 0; r < kTN; r += 4) {
     const int nl = r + (lane >> 4);
-    const int n = n0 + wn * 128 + nl;
+    const int n = n0 + wn * kTN + nl;
     const u32x4 v = lds_load16(reg + nl * kRS + (lane & 15) * 16);
     if (n >= a.N) continue;
     uint16_t* dst = a.Y + int64_t(n) * a.ldy + gm;
@@ -524,20 +534,13 @@ hipError_t launch_compact24(const DevFormat& f, const Sparse24Layout& L, bool re
   return hipGetLastError();
 }
 
-size_t smf_lds(bool residual) {
-  // the stages, or the epilogue's four transposing regions if larger
-  const size_t stages = residual ? size_t(SmfShape<true>::kStages) * SmfShape<true>::kStage
-                                 : size_t(SmfShape<false>::kStages) * SmfShape<false>::kStage;
-  return std::max<size_t>(stages, size_t(4) * 128 * (2 * 128 + 8));
-}
-
 bool smf_fits(const Header& h, int64_t N, int64_t ldx) {
   const int64_t kp = (h.k + 63) / 64 * 64;
   return 2 * ((N - 1) * ldx + h.k) < (int64_t(1) << 32) && h.m * kp < (int64_t(1) << 32);
 }
 
 hipError_t launch_smf(const Header& h, const Sparse24Layout& L, bool residual, const void* ws, const uint16_t* X,
-                      int64_t ldx, uint16_t* Y, int64_t ldy, int64_t N, hipStream_t s) {
+                      int64_t ldx, uint16_t* Y, int64_t ldy, int64_t N, int num_cus, hipStream_t s) {
   if (h.k < 8 || h.k % 8 != 0 || N < 1 || !smf_fits(h, N, ldx)) return hipErrorInvalidValue;
   SmfArgs a;
   const uint8_t* w = static_cast<const uint8_t*>(ws);
@@ -556,14 +559,27 @@ hipError_t launch_smf(const Header& h, const Sparse24Layout& L, bool residual, c
   a.K = int(h.k);
   a.Kp = int(L.kp);
   a.tiles_m = int((h.m + SBM - 1) / SBM);
-  a.tiles_n = int((N + SBN - 1) / SBN);
   a.group_m = 8;
   if (a.tiles_m == 0) return hipSuccess;
+  // 256 x 256 blocks when they give every CU one (or more than a round),
+  // else 256 x 128 (twice the blocks)
+  const int64_t big = int64_t(a.tiles_m) * ((N + 255) / 256);
+  const bool wide = big >= num_cus;
+  a.tiles_n = int(wide ? (N + 255) / 256 : (N + 127) / 128);
   const unsigned grid = unsigned((a.tiles_m * a.tiles_n + 7) / 8 * 8);
-  if (residual)
-    hipLaunchKernelGGL(smf_kernel<true>, dim3(grid), dim3(256), smf_lds(true), s, a);
-  else
-    hipLaunchKernelGGL(smf_kernel<false>, dim3(grid), dim3(256), smf_lds(false), s, a);
+  constexpr size_t kL04 = SmfShape<false, 4>::kLds, kL02 = SmfShape<false, 2>::kLds;
+  constexpr size_t kL14 = SmfShape<true, 4>::kLds, kL12 = SmfShape<true, 2>::kLds;
+  if (residual) {
+    if (wide)
+      hipLaunchKernelGGL((smf_kernel<true, 4>), dim3(grid), dim3(256), kL14, s, a);
+    else
+      hipLaunchKernelGGL((smf_kernel<true, 2>), dim3(grid), dim3(256), kL12, s, a);
+  } else {
+    if (wide)
+      hipLaunchKernelGGL((smf_kernel<false, 4>), dim3(grid), dim3(256), kL04, s, a);
+    else
+      hipLaunchKernelGGL((smf_kernel<false, 2>), dim3(grid), dim3(256), kL02, s, a);
+  }
   return hipGetLastError();
 }
 
