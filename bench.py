@@ -366,16 +366,20 @@ def prefill_block(args, torch, swm, wl, G):
     return blk
 
 
-def layer_copies(swm, torch, parts, min_sparse=5, min_dense=3):
+def layer_copies(swm, torch, parts, min_sparse=5, min_dense=3, smfmac=False):
     """Linears given as (W, mask, X): >= min_sparse compressed copies and
     >= min_dense dense copies of each (rotated so that each layer pass streams
     its weights from HBM: 5 x 228 MB and 3 x 405 MB are above 4x the 256 MB
-    Infinity Cache)."""
+    Infinity Cache).  smfmac: every copy also keeps the 2:4 layers."""
     fmts, dens, xs, shapes, alg = [], [], [], [], 0
     for W, mask, X in parts:
-        f0 = swm.sparse_compress(W, mask)
+        f0 = swm.sparse_compress(W, mask, smfmac=smfmac)
         blob = f0.export()
-        fmts.append([f0] + [swm.format_import(blob) for _ in range(min_sparse - 1)])
+        copies = [swm.format_import(blob) for _ in range(min_sparse - 1)]
+        if smfmac:
+            for c in copies:
+                c.enable_smfmac()
+        fmts.append([f0] + copies)
         Wd = torch.from_numpy(W).cuda()
         dens.append([Wd] + [Wd.clone() for _ in range(min_dense - 1)])
         xs.append(torch.from_numpy(X).cuda())
@@ -384,10 +388,10 @@ def layer_copies(swm, torch, parts, min_sparse=5, min_dense=3):
     return fmts, dens, xs, shapes, alg
 
 
-def layer_pass(args, torch, swm, G, parts, CS, CD):
+def layer_pass(args, torch, swm, G, parts, CS, CD, smfmac=False):
     """One layer pass = each of `parts` once, back to back on one stream,
     sparse through spmm_ws and dense through dense_gemm, at N = 16 and 4096."""
-    fmts, dens, xs, shapes, fa = layer_copies(swm, torch, parts, CS, CD)
+    fmts, dens, xs, shapes, fa = layer_copies(swm, torch, parts, CS, CD, smfmac)
     ws = torch.empty(max(max(swm.spmm_workspace_bytes(f[0], 4096) for f in fmts), 256), dtype=torch.uint8,
                      device="cuda")
     L = len(parts)
@@ -410,7 +414,9 @@ def layer_pass(args, torch, swm, G, parts, CS, CD):
         ds, dd = pct(G.samples(gs, reps, CS)), pct(G.samples(gd, reps, CD))
         alg = fa + sum(2 * (shp[0] + shp[1]) * n for shp in shapes)
         e = {"sparse_layer": ds, "dense_layer": dd, "speedup_vs_dense": dd["median_us"] / ds["median_us"],
-             "route": "decode kernels" if n <= 32 else "swm_spmm_ws (expand + dense MFMA; one shared workspace)"}
+             "route": "decode kernels" if n <= 32 else
+                      ("swm_spmm_ws (resident 2:4 layers, v_smfmac)" if smfmac else
+                       "swm_spmm_ws (expand + dense MFMA; one shared workspace)")}
         if n == 16:
             e["alg_bytes"] = alg
             e["GBps_alg"] = alg / (ds["median_us"] * 1e-6) / 1e9
@@ -442,6 +448,12 @@ def layer_block(args, torch, swm, wl, G):
     fb = layer_pass(args, torch, swm, G, fused, CS, CD)
     fb["workload"] = "the same layer as qkv 12288x4096, o 4096x4096, gate_up 22016x4096, down 4096x11008"
     blk["stacked_projections"] = fb
+    _log("layer block: the same seven linears pruned 2:4, sparse-matrix-core route")
+    parts = [wl.layer_linear_2_4(i, 4096) for i in range(7)]
+    b24 = layer_pass(args, torch, swm, G, parts, CS, CD, smfmac=True)
+    b24["workload"] = ("the seven linears pruned 2:4 along K; handles keep the 2:4 layers (SWM_CFG_SMFMAC): "
+                       "decode kernels at N = 16, v_smfmac at N = 4096")
+    blk["pruned_2_4"] = b24
     return blk
 
 

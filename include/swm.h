@@ -353,6 +353,20 @@ swm_status swm_spmspv_threshold(const swm_format* f, const void* x, int64_t ldx,
  *  SWM_ERR_OVERFLOW, SWM_ERR_UNSUPPORTED (M or K too large), SWM_ERR_HIP. */
 swm_status swm_format_enable_skipping(swm_format* f, void* stream, uint64_t* bytes);
 
+/* format_enable_smfmac: attach to f the 2:4 layers of the sparse-matrix-core
+ * prefill route (see swm_spmm_ws) and keep them on f's device, as
+ * SWM_CFG_SMFMAC does at compress time; also for handles from
+ * swm_format_import, whose blob does not carry them.  Source: the
+ * moderate-sparsity page, abstract and Sec. 1 (a sparse-tensor-core layer
+ * plus a residual layer).  The layers hold the same kept entries as f:
+ * values [M][Kp/2] fp16 and 2-bit positions [M][Kp/16] uint16 per layer (Kp
+ * = K rounded up to 64), a residual layer only when some row keeps 3 or 4 of
+ * an aligned group of 4 columns.  Synchronous; idempotent; call it before f
+ * is used by other threads or streams.  *bytes (nullable) receives the
+ * layers' size.  Errors: SWM_ERR_INVALID_ARG (null f, f on another device),
+ * SWM_ERR_UNSUPPORTED (tiles other than 16 x 64), SWM_ERR_OOM, SWM_ERR_HIP. */
+swm_status swm_format_enable_smfmac(swm_format* f, void* stream, uint64_t* bytes);
+
 /* colruns_encode_blob: host-only derivation of the SWM-CR v2 blob (32-byte
  * header b"SWMC", u32 version 2, i64 M, i64 K, u32 rows per block = 256,
  * u32 row blocks; then ptr, bits, values as described above) from a SWM-TCB v2

@@ -67,6 +67,7 @@ SIGNATURES = {
     "swm_spmspv_threshold": (_i32, [_vp, _vp, _i64, _vp, _i64, _i32, ctypes.c_float, _vp]),
     "swm_gate_up_silu": (_i32, [_vp, _vp, _vp, _i64, _vp, _i64, _i32, ctypes.c_float, _vp]),
     "swm_format_enable_skipping": (_i32, [_vp, _vp, ctypes.POINTER(_u64)]),
+    "swm_format_enable_smfmac": (_i32, [_vp, _vp, ctypes.POINTER(_u64)]),
     "swm_colruns_encode_blob": (_i32, [_vp, _sz, _vp, _sz, ctypes.POINTER(_sz)]),
     "swm_dense_gemm": (_i32, [_vp, _i64, _vp, _i64, _vp, _i64, _i64, _i64, _i64, _vp]),
     "swm_hbm_stream": (_i32, [_vp, _sz, _i32, _i32, _vp, _vp]),
@@ -189,6 +190,14 @@ class Format:
         nbytes = _u64(0)
         _check(lib.swm_format_enable_skipping(self._h, _stream_ptr(stream), ctypes.byref(nbytes)),
                "swm_format_enable_skipping")
+        return int(nbytes.value)
+
+    def enable_smfmac(self, stream=None) -> int:
+        """Attach the 2:4 layers of the sparse-matrix-core prefill route; returns their bytes."""
+        lib = load()
+        nbytes = _u64(0)
+        _check(lib.swm_format_enable_smfmac(self._h, _stream_ptr(stream), ctypes.byref(nbytes)),
+               "swm_format_enable_smfmac")
         return int(nbytes.value)
 
     def close(self):

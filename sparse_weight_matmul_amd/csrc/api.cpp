@@ -216,16 +216,11 @@ swm_status swm_sparse_compress(const uint16_t* W, int64_t ldw, const uint8_t* ma
   swm_format* f = nullptr;
   st = upload(std::move(blob), h, static_cast<hipStream_t>(stream), &f);
   if (st != SWM_OK) return st;
-  if (cfg && (cfg->flags & SWM_CFG_SMFMAC) && h.tm == 16 && h.tk == 64 && h.m > 0) {
-    // compact once into the sparse-matrix-core layers; they stay with the handle
-    f->smf_layout = swm::sparse24_layout(h, f->res24);
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    hipError_t e = hipMalloc(&f->smf_mem, f->smf_layout.bytes);
-    if (e == hipSuccess) e = swm::launch_compact24(f->d, f->smf_layout, f->res24, f->smf_mem, s);
-    if (e == hipSuccess) e = hipStreamSynchronize(s);
-    if (e != hipSuccess) {
+  if (cfg && (cfg->flags & SWM_CFG_SMFMAC)) {
+    st = swm_format_enable_smfmac(f, stream, nullptr);
+    if (st != SWM_OK) {
       (void)swm_format_destroy(f);
-      return e == hipErrorOutOfMemory ? SWM_ERR_OOM : hip_fail(e);
+      return st;
     }
   }
   swm_log("sparse_compress M=%lld K=%lld nnz=%llu blob=%zu B flags=%d: decode split %d / %d tiles per wave "
@@ -233,9 +228,7 @@ swm_status swm_sparse_compress(const uint16_t* W, int64_t ldw, const uint8_t* ma
           (long long)h.m, (long long)h.k, (unsigned long long)h.nnz, f->blob.size(), cfg ? cfg->flags : 0,
           f->plan.tiles_per_wave, f->plan_wide.tiles_per_wave,
           f->res24 ? "mask exceeds 2:4 (SMFMAC needs a residual layer)" : "mask within 2:4");
-  if (f->smf_mem)
-    swm_log("sparse_compress: 2:4 layers resident, %zu B (%s)", f->smf_layout.bytes,
-            f->res24 ? "2:4 layer + residual layer" : "2:4 layer only");
+
   if (cfg && (cfg->flags & SWM_CFG_SKIPPING)) {
     st = swm_format_enable_skipping(f, stream, nullptr);
     if (st != SWM_OK) {
@@ -333,6 +326,31 @@ swm_status swm_colruns_encode_blob(const void* tcb_blob, size_t size, void* out,
   if (!out) return SWM_OK;
   if (cap < need) return SWM_ERR_INVALID_ARG;
   swm::colruns_write_blob(c, static_cast<uint8_t*>(out));
+  return SWM_OK;
+}
+
+swm_status swm_format_enable_smfmac(swm_format* f, void* stream, uint64_t* bytes) {
+  if (!f) return SWM_ERR_INVALID_ARG;
+  if (!on_current_device(f)) return SWM_ERR_INVALID_ARG;
+  if (f->h.tm != 16 || f->h.tk != 64) return SWM_ERR_UNSUPPORTED;
+  if (!f->smf_mem && f->h.m > 0) {
+    // compact once into the sparse-matrix-core layers; they stay with the handle
+    const swm::Sparse24Layout L = swm::sparse24_layout(f->h, f->res24);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    void* mem = nullptr;
+    if (hipMalloc(&mem, L.bytes) != hipSuccess) return SWM_ERR_OOM;
+    hipError_t e = swm::launch_compact24(f->d, L, f->res24, mem, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (e != hipSuccess) {
+      (void)hipFree(mem);
+      return hip_fail(e);
+    }
+    f->smf_layout = L;
+    f->smf_mem = mem;
+    swm_log("enable_smfmac M=%lld K=%lld: 2:4 layers resident, %zu B (%s)", (long long)f->h.m, (long long)f->h.k,
+            L.bytes, f->res24 ? "2:4 layer + residual layer" : "2:4 layer only");
+  }
+  if (bytes) *bytes = f->smf_mem ? f->smf_layout.bytes : 0;
   return SWM_OK;
 }
 

@@ -199,6 +199,15 @@ def layer_linear(i: int, n_max: int):
     return W, mask, activations(CFG_LAYER, i, n_max, K)
 
 
+def layer_linear_2_4(i: int, n_max: int):
+    """Linear i of the same layer pruned 2:4 along K instead (the same dense
+    weights, the two largest |w| of every 4 columns kept)."""
+    _, M, K = LLAMA7B_LINEARS[i]
+    W = normal_fp16(rng(CFG_LAYER, ROLE_W, i), (M, K), 0.02)
+    mask = prune_2_4_mask(W)
+    return apply_mask(W, mask), mask, activations(CFG_LAYER, i, n_max, K)
+
+
 # The layer's projections as an inference engine launches them: q, k, v read
 # the same input and are stacked by rows into one 12288x4096 matrix, gate and
 # up likewise into one 22016x4096 matrix.

@@ -206,3 +206,4 @@ def test_colruns_encoder_rejects_bad_input():
     bad = ctypes.create_string_buffer(bytes(tcb), len(tcb))
     assert lib.swm_colruns_encode_blob(bad, len(tcb), None, 0, ctypes.byref(size)) == 6
     assert lib.swm_format_enable_skipping(None, None, None) == 1
+    assert lib.swm_format_enable_smfmac(None, None, None) == 1

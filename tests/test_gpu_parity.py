@@ -789,6 +789,23 @@ def test_smfmac_route_upgate_70_full(gpu_lib):
     assert_close(_np(swm.spmm(f, _t(X[:16]))), oracle.masked_matmul(W, mask, X[:16]), "up/gate 70% decode")
 
 
+@pytest.mark.parametrize("i", [4, 6])   # gate_proj 11008x4096 (688 blocks), down_proj 4096x11008
+def test_smfmac_layer_2_4_as_benchmarked(gpu_lib, i):
+    """The layer's 2:4-pruned linears as the layer bench runs them: a handle
+    imported from the export blob gets its layers by enable_smfmac and gives
+    the compressed handle's bits; full outputs at N = 4096 against the oracle."""
+    swm = gpu_lib
+    W, mask, X = wl.layer_linear_2_4(i, 4096)
+    f = swm.sparse_compress(W, mask, smfmac=True)
+    g = swm.format_import(f.export())
+    nb = g.enable_smfmac()
+    assert nb == f.enable_smfmac() > 0       # idempotent, same layers
+    Xd = _t(X)
+    Y = _np(swm.spmm(f, Xd))
+    assert_close(Y, oracle.masked_matmul(W, mask, X), f"2:4 linear {i}")
+    assert np.array_equal(Y.view(np.uint16), _np(swm.spmm(g, Xd)).view(np.uint16))
+
+
 def test_spmm_ws_errors(gpu_lib):
     import ctypes
     import torch
