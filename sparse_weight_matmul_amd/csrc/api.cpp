@@ -23,7 +23,8 @@ struct swm_format {
   int device = 0;
   void* dev_mem = nullptr;     // one allocation for every device section
   swm::DevFormat d;
-  swm::DecodePlan plan;       // decode split for N <= 8
+  swm::DecodePlan plan;       // decode split for N <= 4
+  swm::DecodePlan plan8;      // 4 < N <= 8
   swm::DecodePlan plan_wide;  // 8 < N <= 16
   swm::DecodePlan plan_pair;  // 16 < N <= 32 (two token groups, looped kernel)
   void* cr_mem = nullptr;  // column-run encoding for activation skipping (optional)
@@ -106,14 +107,13 @@ swm_status upload(std::vector<uint8_t>&& blob, const swm::Header& h, hipStream_t
     delete f;
     return hip_fail(hipErrorNoDevice);
   }
-  // Decode splits, measured on the layer shapes: up to 8 tokens, more and
-  // shorter waves (about 64 per CU; up 11008x4096 at N = 1: 15.4 us against
-  // 17.1 at 16 per CU); beyond 8 tokens each wave stages 16 activation rows
-  // and about 32 waves per CU is best (up at N = 16: 19.3 against 20.2).
-  // Shapes whose slabs are short (q_proj, down) get the same split from both.
+  // Decode splits, one per size of the activation rows a wave stages (4, 8
+  // or 16 tokens): the split with the most waves resident per CU.  The
+  // looped kernel's split (17-32 tokens) targets about 32 waves per CU.
   const uint32_t* tp = reinterpret_cast<const uint32_t*>(f->blob.data() + h.off_tile_ptr());
-  f->plan = swm::plan_decode(h, tp, num_cus(f->device), 64, true);
-  f->plan_wide = swm::plan_decode(h, tp, num_cus(f->device), 32, true);
+  f->plan = swm::plan_decode(h, tp, num_cus(f->device), 64, true, 1);
+  f->plan8 = swm::plan_decode(h, tp, num_cus(f->device), 32, true, 2);
+  f->plan_wide = swm::plan_decode(h, tp, num_cus(f->device), 32, true, 4);
   f->plan_pair = swm::plan_decode(h, tp, num_cus(f->device), 32, false);
   f->res24 = swm::mask_exceeds_2_of_4(h, f->blob.data());
   const size_t T = h.tiles();
@@ -223,10 +223,10 @@ swm_status swm_sparse_compress(const uint16_t* W, int64_t ldw, const uint8_t* ma
       return st;
     }
   }
-  swm_log("sparse_compress M=%lld K=%lld nnz=%llu blob=%zu B flags=%d: decode split %d / %d tiles per wave "
-          "(N <= 8 / <= 16), %s",
+  swm_log("sparse_compress M=%lld K=%lld nnz=%llu blob=%zu B flags=%d: decode split %d / %d / %d tiles per wave "
+          "(N <= 4 / <= 8 / <= 16), %s",
           (long long)h.m, (long long)h.k, (unsigned long long)h.nnz, f->blob.size(), cfg ? cfg->flags : 0,
-          f->plan.tiles_per_wave, f->plan_wide.tiles_per_wave,
+          f->plan.tiles_per_wave, f->plan8.tiles_per_wave, f->plan_wide.tiles_per_wave,
           f->res24 ? "mask exceeds 2:4 (SMFMAC needs a residual layer)" : "mask within 2:4");
 
   if (cfg && (cfg->flags & SWM_CFG_SKIPPING)) {
@@ -416,7 +416,7 @@ swm_status swm_decompress(const swm_format* f, void* W_dev, int64_t ldw, void* s
 }
 
 static const swm::DecodePlan& decode_plan(const swm_format* f, int64_t n) {
-  return n <= 8 ? f->plan : n <= 16 ? f->plan_wide : f->plan_pair;
+  return n <= 4 ? f->plan : n <= 8 ? f->plan8 : n <= 16 ? f->plan_wide : f->plan_pair;
 }
 
 static bool run_smf(const swm_format* f, const void* X, int64_t ldx, void* Y, int64_t ldy, int64_t N,

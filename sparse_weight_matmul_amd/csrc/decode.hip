@@ -824,29 +824,76 @@ int env_int(const char* name, int dflt) {
 }  // namespace
 
 // ------------------------------------------------------------------ host launchers
-DecodePlan plan_decode(const Header& h, const uint32_t* tp, int num_cus, int waves_per_cu, bool straight_line) {
+// Largest two-tile segment of ranges of `tpw` tiles, in 1 KiB loads.
+static int seq_chunks_for(const Header& h, const uint32_t* tp, int64_t tpw) {
+  uint64_t max2 = 0;
+  for (uint64_t i = 0; i < h.mt; ++i)
+    for (int64_t ja = 0; ja < int64_t(h.kt); ja += tpw)
+      for (int64_t js = ja; js < std::min<int64_t>(ja + tpw, h.kt); js += 2) {
+        const int64_t je = std::min<int64_t>({js + 2, ja + tpw, int64_t(h.kt)});
+        const uint64_t b = 2ull * (tp[i * h.kt + je] - tp[i * h.kt + js]);
+        if (b > max2) max2 = b;
+      }
+  const int c = int((max2 + 1023) / 1024);
+  return c < 1 ? 1 : c;
+}
+
+DecodePlan plan_decode(const Header& h, const uint32_t* tp, int num_cus, int waves_per_cu, bool straight_line,
+                       int kxi) {
   DecodePlan p;
-  // One workgroup per slab.  Enough tiles per wave that the whole call is
-  // about `waves_per_cu` waves per CU, and at most 16 waves per workgroup
-  // (SWM_DECODE_WAVES_PER_CU / SWM_DECODE_TPW override for tuning).  When
-  // that leaves more tiles per wave than the straight-line kernel holds, it
-  // runs with its largest instance (16 tiles per wave) if a slab row fits 16
-  // such waves and the split is for token counts it serves (on the
-  // 65536x16384 shape: 339 / 363 us at N = 1 / 16 against 368 / 373 us for
-  // one round of 16 waves per CU of the looped kernel, and 414 us at N = 16
-  // for 128 tiles per wave); else the looped kernel runs one round of 16
-  // waves per CU (at N = 32 on that shape: 581 us, against 666 us with 16
-  // tiles per wave).
   const int64_t tiles = int64_t(h.mt) * h.kt;
   const int64_t min_tpw = (int64_t(h.kt) + 15) / 16;
-  auto split = [&](int64_t wpc) {
-    const int64_t t = (tiles + int64_t(num_cus) * wpc - 1) / (int64_t(num_cus) * wpc);
-    return t < min_tpw ? min_tpw : t;
-  };
-  int64_t tpw = split(env_int("SWM_DECODE_WAVES_PER_CU", waves_per_cu));
-  if (seq_instance(int((tpw + 1) / 2)) == 0) tpw = straight_line && min_tpw <= 16 ? 16 : split(16);
+  const int64_t cus = num_cus > 0 ? num_cus : 256;
+  int64_t tpw = 0;
+  if (straight_line && kxi > 0 && min_tpw <= 16) {
+    // Straight-line kernel: the split with the most waves resident per CU.
+    // A workgroup (one slab) of w waves holds w * (value chunks + kxi * 4
+    // staged activation rows) of LDS; a CU runs as many workgroups as its
+    // 160 KiB of LDS, its 32 wave slots and the slab count allow.  Ranges
+    // are whole two-tile segments (an even tile count, or the least count
+    // that covers a slab row with 16 waves); ties go to fewer tiles per
+    // wave.  Measured on the layer shapes at N = 8 / 16 (one box, us): q/k/v
+    // stacked 12288x4096 N = 8: 22.9 / 18.4 / 16.7 / 18.6 / 19.7 at 4 / 6 /
+    // 8 / 11 / 16 tiles per wave (this rule: 8); gate/up stacked 22016x4096
+    // N = 16: 41.4 / 35.1 / 37.2 / 38.7 / 36.8 (this rule: 6; the earlier
+    // rule, about 32 waves per CU, took 11).  An odd count that leaves the
+    // slab's last wave one tile measured slower (7 at N = 8 on gate/up:
+    // 33.9 us against 30.3 for 6).
+    int64_t best = -1;
+    for (int64_t t = min_tpw; t <= 16; t = (t + 2) & ~int64_t(1)) {
+      const int64_t w = (int64_t(h.kt) + t - 1) / t;
+      if (w > 16 || seq_instance(int((t + 1) / 2)) == 0) continue;
+      const int chunks = seq_chunks_for(h, tp, t);
+      if (chunks > 4) continue;
+      const int64_t lds = 16 + w * (int64_t(chunks) * 1024 + int64_t(4 * kxi) * kXRow);
+      if (lds > 160 * 1024) continue;
+      const int64_t per_cu =
+          std::min<int64_t>({int64_t(160 * 1024) / lds, 32 / w, (int64_t(h.mt) + cus - 1) / cus});
+      if (per_cu * w > best) {
+        best = per_cu * w;
+        tpw = t;
+      }
+    }
+  }
+  if (tpw == 0) {
+    // About `waves_per_cu` waves per CU (SWM_DECODE_WAVES_PER_CU overrides).
+    // When that leaves more tiles per wave than the straight-line kernel
+    // holds, it runs with its largest instance (16 tiles per wave) if a slab
+    // row fits 16 such waves and the split is for token counts it serves (on
+    // the 65536x16384 shape: 339 / 363 us at N = 1 / 16 against 368 / 373 us
+    // for one round of 16 waves per CU of the looped kernel, and 414 us at
+    // N = 16 for 128 tiles per wave); else the looped kernel runs one round
+    // of 16 waves per CU (at N = 32 on that shape: 581 us, against 666 us
+    // with 16 tiles per wave).
+    auto split = [&](int64_t wpc) {
+      const int64_t t = (tiles + cus * wpc - 1) / (cus * wpc);
+      return t < min_tpw ? min_tpw : t;
+    };
+    tpw = split(env_int("SWM_DECODE_WAVES_PER_CU", waves_per_cu));
+    if (seq_instance(int((tpw + 1) / 2)) == 0) tpw = straight_line && min_tpw <= 16 ? 16 : split(16);
+  }
   if (tpw < 1) tpw = 1;
-  tpw = env_int("SWM_DECODE_TPW", int(tpw));
+  tpw = env_int("SWM_DECODE_TPW", int(tpw));  // tuning override
   if (tpw < min_tpw) tpw = min_tpw;
   p.tiles_per_wave = int(tpw);
   p.waves = int((int64_t(h.kt) + tpw - 1) / tpw);
@@ -865,16 +912,7 @@ DecodePlan plan_decode(const Header& h, const uint32_t* tp, int num_cus, int wav
   if (p.seg_chunks < 1) p.seg_chunks = 1;
   // Straight-line schedule: two-tile segments aligned to each wave's range.
   p.seq_segs = seq_instance(int((tpw + 1) / 2));
-  uint64_t max2 = 0;
-  for (uint64_t i = 0; i < h.mt; ++i)
-    for (int64_t ja = 0; ja < int64_t(h.kt); ja += tpw)
-      for (int64_t js = ja; js < std::min<int64_t>(ja + tpw, h.kt); js += 2) {
-        const int64_t je = std::min<int64_t>({js + 2, ja + tpw, int64_t(h.kt)});
-        const uint64_t b = 2ull * (tp[i * h.kt + je] - tp[i * h.kt + js]);
-        if (b > max2) max2 = b;
-      }
-  p.seq_chunks = int((max2 + 1023) / 1024);
-  if (p.seq_chunks < 1) p.seq_chunks = 1;
+  p.seq_chunks = seq_chunks_for(h, tp, tpw);
   if (p.seq_chunks > 4) p.seq_segs = 0;  // cannot happen: two tiles hold at most 4 KiB
   // ablation: the looped kernel everywhere (SWM_DECODE_PATH=loop, or SWM_DECODE_LOOP set)
   const char* path = getenv("SWM_DECODE_PATH");
