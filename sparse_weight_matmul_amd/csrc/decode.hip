@@ -1042,20 +1042,38 @@ hipError_t launch_dense_small(const DensePlan& p, const uint16_t* W, int64_t ldw
 DecodePlan plan_decode_glu(const Header& g, const Header& u, int num_cus, int n) {
   // Both formats' tiles in one launch, at most 8 waves per format (16 per
   // workgroup) and at most 16 tiles per wave (the largest straight-line
-  // instance).  Up to 8 tokens: as many waves as that allows (measured on
-  // gate/up 11008x4096: 26.3 us at 8 tiles per wave against 28.1 at 16).
-  // More tokens stage 16 activation rows per wave, and 16 such waves fill
-  // a CU's LDS: then enough tiles per wave for about one round of 16 waves
-  // per CU (35.5 us at 16 tiles per wave against 37.0 at 8).
+  // instance).  As for the ungated kernel, the split (an even tile count,
+  // or the least that fits 8 waves per format) with the most waves resident
+  // per CU, counting the LDS a workgroup needs for its staged activation
+  // rows (4, 8 or 16 tokens), the 32 wave slots and the slab count.  On
+  // gate/up 11008x4096 that is 8 tiles per wave up to 4 tokens (26.3 us at
+  // N = 1 against 28.1 at 16) and 14 from 5 tokens (two A/B runs on one
+  // box: 34.8 / 33.7 / 36.8 us at N = 6 / 8 / 16 against 37.1 / 35.5 / 37.9
+  // for the earlier split of 8 tiles per wave up to 8 tokens, where a
+  // workgroup's staged rows left room for one workgroup per CU, and 16
+  // above).
   DecodePlan p;
   const int64_t kt = g.kt;
   const int64_t min_tpw = (kt + 7) / 8;
-  int64_t tpw = (2 * int64_t(g.mt) * kt + int64_t(num_cus) * 16 - 1) / (int64_t(num_cus) * 16);
-  if (n <= 8) tpw = min_tpw;
-  tpw = std::min<int64_t>(std::max<int64_t>(tpw, min_tpw), 16);
+  const int kxi = n <= 4 ? 1 : n <= 8 ? 2 : 4;
+  // Two tiles hold at most 2 * max_tile values: a bound on every segment.
+  const uint64_t max2 = 4ull * std::max(g.max_tile, u.max_tile);
+  p.seq_chunks = int(std::max<uint64_t>((max2 + 1023) / 1024, 1));
+  const int64_t cus = num_cus > 0 ? num_cus : 256;
+  int64_t tpw = 0, best = -1;
+  for (int64_t t = min_tpw; t <= 16; t = (t + 2) & ~int64_t(1)) {
+    const int64_t w = 2 * ((kt + t - 1) / t);
+    const int64_t lds = 16 + w * (int64_t(p.seq_chunks) * 1024 + int64_t(4 * kxi) * kXRow);
+    if (w > 16 || lds > 160 * 1024) continue;
+    const int64_t per_cu = std::min<int64_t>({int64_t(160 * 1024) / lds, 32 / w, (int64_t(g.mt) + cus - 1) / cus});
+    if (per_cu * w > best) {
+      best = per_cu * w;
+      tpw = t;
+    }
+  }
   static const int env_tpw = env_int("SWM_GLU_TPW", 0);
   if (env_tpw > 0) tpw = env_tpw;
-  if (tpw < min_tpw || tpw > 16 || kt < 1) {
+  if (tpw < min_tpw || tpw > 16 || kt < 1 || p.seq_chunks > 4) {
     p.seq_segs = 0;  // no instance covers this shape
     return p;
   }
@@ -1064,10 +1082,6 @@ DecodePlan plan_decode_glu(const Header& g, const Header& u, int num_cus, int n)
   // gated instances exist for 1, 2, 4 and 8 two-tile segments per wave
   const int segs = int((tpw + 1) / 2);
   p.seq_segs = segs <= 1 ? 1 : segs <= 2 ? 2 : segs <= 4 ? 4 : 8;
-  // Two tiles hold at most 2 * max_tile values: a bound on every segment.
-  const uint64_t max2 = 4ull * std::max(g.max_tile, u.max_tile);
-  p.seq_chunks = int(std::max<uint64_t>((max2 + 1023) / 1024, 1));
-  if (p.seq_chunks > 4) p.seq_segs = 0;
   return p;
 }
 
