@@ -53,8 +53,9 @@
  *    created), SWM_SKIP = off / on (swm_spmspv never / for every n <= 4 takes
  *    the column-run skipping kernel on a handle that carries it; default up
  *    to 2 tokens; read once), SWM_DENSE_DMA=0 (the register-staged tiled
- *    dense kernel; read once), SWM_DECODE_TPW / SWM_DECODE_WAVES_PER_CU
- *    (decode tiles per wave / waves per CU, read when a handle is created),
+ *    dense kernel; read once), SWM_DECODE_TPW (decode tiles per wave, read
+ *    when a handle is created), SWM_DECODE_WAVES_PER_CU (waves per CU of the
+ *    17-32-token decode split, read when a handle is created),
  *    SWM_DENSE_WAVES_PER_CU (streaming dense kernel), SWM_DENSE_BLOCK = 1 / 2
  *    / 3 (tiled dense block 256x256 / 256x128 / 128x128), SWM_EXPAND_MIN_N
  *    (tokens from which swm_spmm_ws expands W, at least 33; read once),
