@@ -431,24 +431,34 @@ __global__ __launch_bounds__(1024) void decode_kernel(DecodeArgs a) {
 //   * at a segment's start its activations go to the wave's LDS (B operands
 //     are then read with ds_read_b128); its chunks are copied tile by tile,
 //     each as soon as the chunks that hold it have arrived, so decoding
-//     overlaps the rest of the stream.
+//     overlaps the rest of the stream;
+//   * kDB (16 token rows only): the activations are loaded straight in the B
+//     operand layout instead, one 1 KiB load per 32-column step (lane l:
+//     token l%16, columns 8(l/16) .. +7), and used from registers; the wave
+//     needs no LDS for them, so more workgroups fit a CU, at the price of
+//     loads that touch 16 token rows each.
 constexpr int kXRow = 272;  // LDS bytes per token row of a segment's activations (256 + pad)
+// LDS bytes per wave for a segment's staged activations (kxi 1 KiB loads;
+// none when the B operands are loaded straight into registers).
+constexpr int seq_x_bytes(int kxi, bool direct) { return direct ? 0 : 4 * kxi * kXRow; }
 
-template <int NS, int kC, int kXI, bool kGlu = false>
+template <int NS, int kC, int kXI, bool kGlu = false, bool kDB = false>
 __global__ __launch_bounds__(1024) void decode_seq_kernel(typename SeqArgs<kGlu>::type a) {
+  static_assert(!kDB || kXI == 4, "B operands straight from memory only with 16 staged token rows");
   constexpr int kT = 2 * NS;      // tile slots per wave
   constexpr int kSteps = 2 * kT;  // 32-column steps
   constexpr int kTouch = (kT * 128 + 1023) / 1024;
   constexpr int kXRows = 4 * kXI;  // token rows of the activation buffer
-  constexpr uint32_t kWaveLds = kC * 1024 + kXRows * kXRow;
+  constexpr uint32_t kWaveLds = kC * 1024 + (kDB ? 0 : kXRows * kXRow);
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   const int lane = lane_id();
   const int wave = __builtin_amdgcn_readfirstlane(int(threadIdx.x >> 6));
   const int nwaves = int(blockDim.x >> 6);
   const int slab = int(blockIdx.x);
 
-  // LDS: [0,16) zeros | per wave: kC KiB of value chunks, then the segment's
-  // activations [kXRows][kXRow]; the reduction area reuses it after a barrier.
+  // LDS: [0,16) zeros | per wave: kC KiB of value chunks, then (unless kDB)
+  // the segment's activations [kXRows][kXRow]; the reduction area reuses it
+  // after a barrier.
   if (threadIdx.x < 4) reinterpret_cast<uint32_t*>(smem)[threadIdx.x] = 0u;
   __syncthreads();
   const uint32_t zero_addr = lds_addr(smem);
@@ -499,15 +509,23 @@ __global__ __launch_bounds__(1024) void decode_seq_kernel(typename SeqArgs<kGlu>
     }
 
     // Activation pieces: piece p = 64 i + lane is token p/16 (rows past N
-    // repeat token N-1), columns 8 (p%16) .. +7 of the segment.  Byte offsets
-    // fit 32 bits (16 tokens of at most 2^27 halves).
+    // repeat token N-1), columns 8 (p%16) .. +7 of the segment; with kDB,
+    // load i is step i's B operand (token lane%16, rows past N repeating
+    // token N-1, columns 32 i + 8 (lane/16) .. +7).  Byte offsets fit 32 bits
+    // (16 tokens of at most 2^27 halves).
     uint32_t xrow_off[kXI], xcol[kXI], xl[kXI];
 #pragma unroll
     for (int i = 0; i < kXI; ++i) {
       const int pce = i * 64 + lane;
-      xrow_off[i] = 2u * uint32_t(min(pce >> 4, a.N - 1)) * uint32_t(a.ldx);
-      xcol[i] = 8u * uint32_t(pce & 15);
-      xl[i] = xbuf + uint32_t(pce >> 4) * kXRow + 16u * uint32_t(pce & 15);
+      if constexpr (kDB) {
+        xrow_off[i] = 2u * uint32_t(min(lane & 15, a.N - 1)) * uint32_t(a.ldx);
+        xcol[i] = 32u * uint32_t(i) + 8u * uint32_t(lane >> 4);
+        xl[i] = 0;
+      } else {
+        xrow_off[i] = 2u * uint32_t(min(pce >> 4, a.N - 1)) * uint32_t(a.ldx);
+        xcol[i] = 8u * uint32_t(pce & 15);
+        xl[i] = xbuf + uint32_t(pce >> 4) * kXRow + 16u * uint32_t(pce & 15);
+      }
     }
     // B operand: lane l carries token l%16 (rows past kXRows repeat a valid
     // row; their accumulator columns are never stored), columns 8(l/16) .. +7.
@@ -548,9 +566,11 @@ __global__ __launch_bounds__(1024) void decode_seq_kernel(typename SeqArgs<kGlu>
       if (2 * g < nt) {
         // The segment's activations and all its value chunks (chunks past the
         // segment hold clamped duplicates and are never read).
+        if constexpr (!kDB) {
 #pragma unroll
-        for (int i = 0; i < kXI; ++i)
-          *reinterpret_cast<lds_u32x4*>(static_cast<uintptr_t>(xl[i])) = xr[g][i];
+          for (int i = 0; i < kXI; ++i)
+            *reinterpret_cast<lds_u32x4*>(static_cast<uintptr_t>(xl[i])) = xr[g][i];
+        }
 #pragma unroll
         for (int c = 0; c < kC; ++c)
           *reinterpret_cast<lds_u32x4*>(static_cast<uintptr_t>(buf + c * 1024 + lane * 16)) = r[g][c];
@@ -576,8 +596,12 @@ __global__ __launch_bounds__(1024) void decode_seq_kernel(typename SeqArgs<kGlu>
             asm volatile("" ::"s"(wk));
             if (t + 1 < kSteps) load_w(t + 1);
             __builtin_amdgcn_sched_barrier(0);
-            const half8 bop = __builtin_bit_cast(
-                half8, *reinterpret_cast<const lds_u32x4*>(static_cast<uintptr_t>(xb + tt * 128 + s * 64)));
+            half8 bop;
+            if constexpr (kDB)
+              bop = __builtin_bit_cast(half8, xr[g][2 * tt + s]);
+            else
+              bop = __builtin_bit_cast(
+                  half8, *reinterpret_cast<const lds_u32x4*>(static_cast<uintptr_t>(xb + tt * 128 + s * 64)));
             const half8 aop = decode_step(w, base);
             acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(aop, bop, acc, 0, 0, 0);
           }
@@ -783,21 +807,22 @@ __global__ __launch_bounds__(256) void decompress_kernel(DecompArgs a) {
   }
 }
 
-template <int NS, int kXI, bool kGlu>
+template <int NS, int kXI, bool kGlu, bool kDB = false>
 void launch_seq_x(int kc, dim3 grid, dim3 block, size_t lds, hipStream_t s, const typename SeqArgs<kGlu>::type& a) {
   switch (kc) {
-    case 1: hipLaunchKernelGGL((decode_seq_kernel<NS, 1, kXI, kGlu>), grid, block, lds, s, a); break;
-    case 2: hipLaunchKernelGGL((decode_seq_kernel<NS, 2, kXI, kGlu>), grid, block, lds, s, a); break;
-    case 3: hipLaunchKernelGGL((decode_seq_kernel<NS, 3, kXI, kGlu>), grid, block, lds, s, a); break;
-    default: hipLaunchKernelGGL((decode_seq_kernel<NS, 4, kXI, kGlu>), grid, block, lds, s, a); break;
+    case 1: hipLaunchKernelGGL((decode_seq_kernel<NS, 1, kXI, kGlu, kDB>), grid, block, lds, s, a); break;
+    case 2: hipLaunchKernelGGL((decode_seq_kernel<NS, 2, kXI, kGlu, kDB>), grid, block, lds, s, a); break;
+    case 3: hipLaunchKernelGGL((decode_seq_kernel<NS, 3, kXI, kGlu, kDB>), grid, block, lds, s, a); break;
+    default: hipLaunchKernelGGL((decode_seq_kernel<NS, 4, kXI, kGlu, kDB>), grid, block, lds, s, a); break;
   }
 }
 
 template <int NS, bool kGlu = false>
-void launch_seq_ns(int kc, int kxi, dim3 grid, dim3 block, size_t lds, hipStream_t s,
+void launch_seq_ns(int kc, int kxi, bool direct, dim3 grid, dim3 block, size_t lds, hipStream_t s,
                    const typename SeqArgs<kGlu>::type& a) {
   if (kxi == 1) launch_seq_x<NS, 1, kGlu>(kc, grid, block, lds, s, a);
   else if (kxi == 2) launch_seq_x<NS, 2, kGlu>(kc, grid, block, lds, s, a);
+  else if (direct) launch_seq_x<NS, 4, kGlu, true>(kc, grid, block, lds, s, a);
   else launch_seq_x<NS, 4, kGlu>(kc, grid, block, lds, s, a);
 }
 
@@ -859,19 +884,39 @@ DecodePlan plan_decode(const Header& h, const uint32_t* tp, int num_cus, int wav
     // rule, about 32 waves per CU, took 11).  An odd count that leaves the
     // slab's last wave one tile measured slower (7 at N = 8 on gate/up:
     // 33.9 us against 30.3 for 6).
-    int64_t best = -1;
-    for (int64_t t = min_tpw; t <= 16; t = (t + 2) & ~int64_t(1)) {
-      const int64_t w = (int64_t(h.kt) + t - 1) / t;
-      if (w > 16 || seq_instance(int((t + 1) / 2)) == 0) continue;
-      const int chunks = seq_chunks_for(h, tp, t);
-      if (chunks > 4) continue;
-      const int64_t lds = 16 + w * (int64_t(chunks) * 1024 + int64_t(4 * kxi) * kXRow);
-      if (lds > 160 * 1024) continue;
-      const int64_t per_cu =
-          std::min<int64_t>({int64_t(160 * 1024) / lds, 32 / w, (int64_t(h.mt) + cus - 1) / cus});
-      if (per_cu * w > best) {
-        best = per_cu * w;
-        tpw = t;
+    auto best_split = [&](bool direct, int64_t& score) {
+      int64_t best_t = 0;
+      score = -1;
+      for (int64_t t = min_tpw; t <= 16; t = (t + 2) & ~int64_t(1)) {
+        const int64_t w = (int64_t(h.kt) + t - 1) / t;
+        if (w > 16 || seq_instance(int((t + 1) / 2)) == 0) continue;
+        const int chunks = seq_chunks_for(h, tp, t);
+        if (chunks > 4) continue;
+        const int64_t lds = 16 + w * (int64_t(chunks) * 1024 + seq_x_bytes(kxi, direct));
+        if (lds > 160 * 1024) continue;
+        const int64_t per_cu =
+            std::min<int64_t>({int64_t(160 * 1024) / lds, 32 / w, (int64_t(h.mt) + cus - 1) / cus});
+        if (per_cu * w > score) {
+          score = per_cu * w;
+          best_t = t;
+        }
+      }
+      return best_t;
+    };
+    // With 16 token rows the B operands can instead be loaded straight into
+    // registers (no activation staging in LDS).  Those loads touch 16 rows
+    // per instruction instead of 4, which costs 11-15% on shapes whose
+    // workgroups fill the CUs either way (q_proj, down at N = 16); taken only
+    // where the freed LDS gives at least 1.25x the resident waves (up
+    // 11008x4096 N = 12 / 16: 17.36 / 18.08 us against 18.13 / 18.88;
+    // gate/up stacked 22016x4096: 30.36 / 32.42 against 32.93 / 34.58).
+    int64_t score = 0, score_d = 0;
+    tpw = best_split(false, score);
+    if (kxi == 4) {
+      const int64_t td = best_split(true, score_d);
+      if (td > 0 && 4 * score_d >= 5 * score) {
+        tpw = td;
+        p.direct_b = true;
       }
     }
   }
@@ -954,15 +999,16 @@ hipError_t launch_decode(const DevFormat& f, const DecodePlan& p, const uint16_t
   // profitably; the product is computed in full (same result).
   if (vec && p.seq_segs > 0 && a.K >= 8 && x32 && n <= 16) {
     const int kxi = n <= 4 ? 1 : n <= 8 ? 2 : 4;
-    const size_t per_wave = size_t(p.seq_chunks) * 1024 + size_t(4 * kxi) * kXRow;
+    const bool direct = p.direct_b && kxi == 4;
+    const size_t per_wave = size_t(p.seq_chunks) * 1024 + size_t(seq_x_bytes(kxi, direct));
     const size_t seq_lds = 16 + size_t(p.waves) * per_wave;
     switch (p.seq_segs) {
-      case 1: launch_seq_ns<1>(p.seq_chunks, kxi, grid, block, seq_lds, s, a); break;
-      case 2: launch_seq_ns<2>(p.seq_chunks, kxi, grid, block, seq_lds, s, a); break;
-      case 3: launch_seq_ns<3>(p.seq_chunks, kxi, grid, block, seq_lds, s, a); break;
-      case 4: launch_seq_ns<4>(p.seq_chunks, kxi, grid, block, seq_lds, s, a); break;
-      case 6: launch_seq_ns<6>(p.seq_chunks, kxi, grid, block, seq_lds, s, a); break;
-      default: launch_seq_ns<8>(p.seq_chunks, kxi, grid, block, seq_lds, s, a); break;
+      case 1: launch_seq_ns<1>(p.seq_chunks, kxi, direct, grid, block, seq_lds, s, a); break;
+      case 2: launch_seq_ns<2>(p.seq_chunks, kxi, direct, grid, block, seq_lds, s, a); break;
+      case 3: launch_seq_ns<3>(p.seq_chunks, kxi, direct, grid, block, seq_lds, s, a); break;
+      case 4: launch_seq_ns<4>(p.seq_chunks, kxi, direct, grid, block, seq_lds, s, a); break;
+      case 6: launch_seq_ns<6>(p.seq_chunks, kxi, direct, grid, block, seq_lds, s, a); break;
+      default: launch_seq_ns<8>(p.seq_chunks, kxi, direct, grid, block, seq_lds, s, a); break;
     }
     return hipGetLastError();
   }
@@ -1060,15 +1106,31 @@ DecodePlan plan_decode_glu(const Header& g, const Header& u, int num_cus, int n)
   const uint64_t max2 = 4ull * std::max(g.max_tile, u.max_tile);
   p.seq_chunks = int(std::max<uint64_t>((max2 + 1023) / 1024, 1));
   const int64_t cus = num_cus > 0 ? num_cus : 256;
-  int64_t tpw = 0, best = -1;
-  for (int64_t t = min_tpw; t <= 16; t = (t + 2) & ~int64_t(1)) {
-    const int64_t w = 2 * ((kt + t - 1) / t);
-    const int64_t lds = 16 + w * (int64_t(p.seq_chunks) * 1024 + int64_t(4 * kxi) * kXRow);
-    if (w > 16 || lds > 160 * 1024) continue;
-    const int64_t per_cu = std::min<int64_t>({int64_t(160 * 1024) / lds, 32 / w, (int64_t(g.mt) + cus - 1) / cus});
-    if (per_cu * w > best) {
-      best = per_cu * w;
-      tpw = t;
+  auto best_split = [&](bool direct, int64_t& score) {
+    int64_t best_t = 0;
+    score = -1;
+    for (int64_t t = min_tpw; t <= 16; t = (t + 2) & ~int64_t(1)) {
+      const int64_t w = 2 * ((kt + t - 1) / t);
+      const int64_t lds = 16 + w * (int64_t(p.seq_chunks) * 1024 + seq_x_bytes(kxi, direct));
+      if (w > 16 || lds > 160 * 1024) continue;
+      const int64_t per_cu =
+          std::min<int64_t>({int64_t(160 * 1024) / lds, 32 / w, (int64_t(g.mt) + cus - 1) / cus});
+      if (per_cu * w > score) {
+        score = per_cu * w;
+        best_t = t;
+      }
+    }
+    return best_t;
+  };
+  // B operands straight into registers where that gives 1.25x the resident
+  // waves (as for the ungated kernel)
+  int64_t score = 0, score_d = 0;
+  int64_t tpw = best_split(false, score);
+  if (kxi == 4) {
+    const int64_t td = best_split(true, score_d);
+    if (td > 0 && 4 * score_d >= 5 * score) {
+      tpw = td;
+      p.direct_b = true;
     }
   }
   static const int env_tpw = env_int("SWM_GLU_TPW", 0);
@@ -1116,13 +1178,14 @@ hipError_t launch_decode_glu(const DevFormat& g, const DevFormat& u, const Decod
   if (g.h.mt == 0) return hipSuccess;
   const dim3 grid{unsigned(g.h.mt), 1, 1}, block{unsigned(p.waves * 64), 1, 1};
   const int kxi = n <= 4 ? 1 : n <= 8 ? 2 : 4;
-  const size_t per_wave = size_t(p.seq_chunks) * 1024 + size_t(4 * kxi) * kXRow;
+  const bool direct = p.direct_b && kxi == 4;
+  const size_t per_wave = size_t(p.seq_chunks) * 1024 + size_t(seq_x_bytes(kxi, direct));
   const size_t lds = 16 + size_t(p.waves) * per_wave;
   switch (p.seq_segs) {
-    case 1: launch_seq_ns<1, true>(p.seq_chunks, kxi, grid, block, lds, s, a); break;
-    case 2: launch_seq_ns<2, true>(p.seq_chunks, kxi, grid, block, lds, s, a); break;
-    case 4: launch_seq_ns<4, true>(p.seq_chunks, kxi, grid, block, lds, s, a); break;
-    default: launch_seq_ns<8, true>(p.seq_chunks, kxi, grid, block, lds, s, a); break;
+    case 1: launch_seq_ns<1, true>(p.seq_chunks, kxi, direct, grid, block, lds, s, a); break;
+    case 2: launch_seq_ns<2, true>(p.seq_chunks, kxi, direct, grid, block, lds, s, a); break;
+    case 4: launch_seq_ns<4, true>(p.seq_chunks, kxi, direct, grid, block, lds, s, a); break;
+    default: launch_seq_ns<8, true>(p.seq_chunks, kxi, direct, grid, block, lds, s, a); break;
   }
   return hipGetLastError();
 }

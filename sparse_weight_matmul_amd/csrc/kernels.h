@@ -26,6 +26,7 @@ struct DecodePlan {
   int seg_chunks = 1;      // 1 KiB loads per segment (covers the largest segment)
   int seq_segs = 0;        // straight-line kernel: two-tile segments per wave (0 = not used)
   int seq_chunks = 1;      // 1 KiB loads per two-tile segment
+  bool direct_b = false;   // 9-16 tokens: B operands loaded straight into registers
 };
 
 // Work split of the decode kernel (at least one wave per 16 tiles of a slab
