@@ -285,6 +285,9 @@ def bench_decode(args, torch, swm, wl, G):
     ach = alg[dom] / (per_n[dom] * 1e-3) / 1e9
     _log("stream calibration at the decode launch's byte count")
     st = stream_achievable(torch, swm, G, alg[dom])
+    _log("stream calibration at the dense baseline launch's byte count")
+    st_d = stream_achievable(torch, swm, G, dense_b[dom])
+    dense_ach = dense_b[dom] / (per_n_d[dom] * 1e-3) / 1e9
     out = {
         "metric": "decode SpMM HBM throughput on compressed bytes (q_proj 4096x4096, 50%)",
         "value": value, "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
@@ -295,6 +298,9 @@ def bench_decode(args, torch, swm, wl, G):
                    "format_alg_bytes": fa, "rotating_copies": C},
         "speedup_vs_dense": ms_dense / ms_total,
         "dense_ms_per_step": ms_dense / args.steps,
+        "dense_baseline": {"kernel": "dense_small_kernel, N=16", "bytes_per_launch": dense_b[dom],
+                           "GBps": dense_ach, "frac_hbm": dense_ach / HBM_PEAK_GBS,
+                           "achievable": st_d["GBps"], "frac_of_achievable": dense_ach / st_d["GBps"]},
         "detail": detail,
         "roofline": {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": ach / HBM_PEAK_GBS,

@@ -642,7 +642,15 @@ __device__ __attribute__((aligned(16))) uint16_t g_zero_chunk[8];
 // run seven steps ahead through an eight-slot register ring; loads past the
 // wave's columns read g_zero_chunk.  Rows past M read row M-1 and tokens past
 // N read token N-1: their accumulator entries are never stored.
-template <bool kVec>
+//
+// kXI > 0 (5-16 tokens): the activations are staged through LDS as in the
+// sparse kernel instead of loaded in the B operand layout, whose loads touch
+// 16 token rows of 64 bytes each: per 128-column segment kXI loads of 4 token
+// rows x 256 contiguous bytes (whole cache lines), two segments ahead, stored
+// into the wave's LDS rows and read back as B operands with ds_read_b128.
+constexpr int kDXRow = 272;  // LDS bytes per staged token row (256 + pad)
+
+template <bool kVec, int kXI = 0>
 __global__ __launch_bounds__(1024) void dense_small_kernel(DenseArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   const int lane = lane_id();
@@ -659,7 +667,65 @@ __global__ __launch_bounds__(1024) void dense_small_kernel(DenseArgs a) {
 
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   if (kb < ke) {
-    if constexpr (kVec) {
+    if constexpr (kVec && kXI > 0) {
+      constexpr int kXRows = 4 * kXI;
+      const int nsteps = int((ke - kb + 31) / 32);  // a multiple of 8 but for the last wave
+      const uint32_t xs = lds_addr(smem) + uint32_t(wave) * (kXRows * kDXRow);
+      // staged piece p = 64 i + lane: token p/16 (rows past N repeat token
+      // N-1), 16-byte chunk p%16 of the segment's 256 bytes
+      const uint16_t* xsrc[kXI];
+      uint32_t xdst[kXI];
+      int xch[kXI];
+#pragma unroll
+      for (int i = 0; i < kXI; ++i) {
+        const int pce = 64 * i + lane;
+        xsrc[i] = a.X + int64_t(min(pce >> 4, a.N - 1)) * a.ldx;
+        xch[i] = 8 * (pce & 15);
+        xdst[i] = xs + uint32_t(pce >> 4) * kDXRow + 16u * uint32_t(pce & 15);
+      }
+      // B operand: token lane%16 (rows past kXRows repeat a staged row; their
+      // accumulator columns are never stored), columns 8(lane/16) .. +7
+      const uint32_t xb = xs + uint32_t(min(lane & 15, kXRows - 1)) * kDXRow + 16u * uint32_t(lane >> 4);
+      half8 A[8];
+      u32x4 xr[2][kXI];
+      auto issueA = [&](int st, int slot) {
+        const int64_t k = kb + int64_t(st) * 32 + kq;
+        A[slot] = __builtin_bit_cast(half8, *reinterpret_cast<const u32x4*>(k < ke ? wrow + k : g_zero_chunk));
+      };
+      auto issueX = [&](int g, int slot) {
+#pragma unroll
+        for (int i = 0; i < kXI; ++i) {
+          const int64_t k = kb + int64_t(g) * 128 + xch[i];
+          xr[slot][i] = *reinterpret_cast<const u32x4*>(k < ke ? xsrc[i] + k : g_zero_chunk);
+        }
+      };
+      issueX(0, 0);
+      issueX(1, 1);
+#pragma unroll
+      for (int u = 0; u < 7; ++u) issueA(u, u);
+      for (int s0 = 0; s0 < nsteps; s0 += 8) {
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          if ((u & 3) == 0) {
+            // segment (s0 + u) / 4 into the wave's LDS rows (its previous
+            // segment's B reads were issued before these writes), then the
+            // segment two ahead into the freed registers
+            const int slot = u >> 2;
+#pragma unroll
+            for (int i = 0; i < kXI; ++i)
+              *reinterpret_cast<lds_u32x4*>(static_cast<uintptr_t>(xdst[i])) = xr[slot][i];
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            issueX((s0 + u) / 4 + 2, slot);
+          }
+          issueA(s0 + u + 7, (u + 7) & 7);
+          const half8 B = __builtin_bit_cast(
+              half8, *reinterpret_cast<const lds_u32x4*>(static_cast<uintptr_t>(xb + 64u * uint32_t(u & 3))));
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[u], B, acc, 0, 0, 0);
+        }
+      }
+    } else if constexpr (kVec) {
       const int nsteps = int((ke - kb + 31) / 32);
       half8 A[8], B[8];
       auto issue = [&](int s, int slot) {
@@ -685,6 +751,7 @@ __global__ __launch_bounds__(1024) void dense_small_kernel(DenseArgs a) {
       }
     }
   }
+  if constexpr (kXI > 0) __syncthreads();  // every wave is done with its staged rows
   slab_reduce_store(reinterpret_cast<float*>(smem), nwaves, wave, lane, acc, slab, a.M, a.N, a.Y, a.ldy);
 }
 
@@ -1079,9 +1146,15 @@ hipError_t launch_dense_small(const DensePlan& p, const uint16_t* W, int64_t ldw
   if (slabs == 0) return hipSuccess;
   if (n < 1 || n > 16) return hipErrorInvalidValue;
   const dim3 grid{unsigned(slabs), 1, 1}, block{unsigned(p.waves * 64), 1, 1};
-  const size_t lds = size_t(p.waves) * 256 * 4;
-  if (vec) hipLaunchKernelGGL((dense_small_kernel<true>), grid, block, lds, s, a);
-  else hipLaunchKernelGGL((dense_small_kernel<false>), grid, block, lds, s, a);
+  const size_t red = size_t(p.waves) * 256 * 4;
+  // 5-16 tokens: activations staged through LDS (4 or 8 KiB-ish per wave)
+  const int kxi = n <= 4 ? 0 : n <= 8 ? 2 : 4;
+  const size_t stage = size_t(p.waves) * size_t(4 * kxi) * kDXRow;
+  const size_t lds = std::max(red, stage);
+  if (vec && kxi == 4) hipLaunchKernelGGL((dense_small_kernel<true, 4>), grid, block, lds, s, a);
+  else if (vec && kxi == 2) hipLaunchKernelGGL((dense_small_kernel<true, 2>), grid, block, lds, s, a);
+  else if (vec) hipLaunchKernelGGL((dense_small_kernel<true>), grid, block, red, s, a);
+  else hipLaunchKernelGGL((dense_small_kernel<false>), grid, block, red, s, a);
   return hipGetLastError();
 }
 

@@ -413,7 +413,9 @@ def test_spmspv_skip_strided(gpu_lib):
 
 # ------------------------------------------------------------------ dense baseline, ragged
 @pytest.mark.parametrize("M,K,N", [(1, 1, 1), (65, 129, 3), (300, 1000, 16), (100, 64, 20), (1000, 512, 32),
-                                   (3000, 256, 30), (20000, 64, 32), (257, 4104, 17)])
+                                   (3000, 256, 30), (20000, 64, 32), (257, 4104, 17),
+                                   # 5-16 tokens: activations staged through LDS, ragged K per wave
+                                   (300, 1000, 5), (77, 2056, 8), (513, 4104, 9), (40, 8, 12), (1040, 11008, 15)])
 def test_dense_gemm_ragged(gpu_lib, M, K, N):
     g = np.random.default_rng(M * K)
     W = (0.02 * g.standard_normal((M, K))).astype(np.float16)
