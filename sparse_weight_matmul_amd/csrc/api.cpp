@@ -224,9 +224,10 @@ swm_status swm_sparse_compress(const uint16_t* W, int64_t ldw, const uint8_t* ma
     }
   }
   swm_log("sparse_compress M=%lld K=%lld nnz=%llu blob=%zu B flags=%d: decode split %d / %d / %d tiles per wave "
-          "(N <= 4 / <= 8 / <= 16), %s",
+          "(N <= 4 / <= 8 / <= 16%s), %s",
           (long long)h.m, (long long)h.k, (unsigned long long)h.nnz, f->blob.size(), cfg ? cfg->flags : 0,
           f->plan.tiles_per_wave, f->plan8.tiles_per_wave, f->plan_wide.tiles_per_wave,
+          f->plan_wide.direct_b ? ", B operands from memory" : "",
           f->res24 ? "mask exceeds 2:4 (SMFMAC needs a residual layer)" : "mask within 2:4");
 
   if (cfg && (cfg->flags & SWM_CFG_SKIPPING)) {

@@ -497,6 +497,54 @@ print("ok", flush=True)
 """
 
 
+_DIRECT_B_CHECK = r"""
+import sys
+import numpy as np
+sys.path.insert(0, sys.argv[1])
+sys.path.insert(0, sys.argv[2])
+import torch
+import sparse_weight_matmul_amd as swm
+import oracle
+g = np.random.default_rng(8208)
+M, K = 8208, 4040                      # 513 slabs, 64 tiles per slab row (the last one 8 columns wide)
+W = (0.02 * g.standard_normal((M, K))).astype(np.float16)
+mask = g.random((M, K)) < 0.5
+Wu = (0.02 * g.standard_normal((M, K))).astype(np.float16)
+mu = g.random((M, K)) < 0.5
+X = g.standard_normal((16, K)).astype(np.float16)
+f, fu = swm.sparse_compress(W, mask), swm.sparse_compress(Wu, mu)
+Xd = torch.from_numpy(X).cuda()
+for n in (9, 13, 16):
+    y = swm.spmm(f, Xd[:n]).float().cpu().numpy()
+    ref = oracle.masked_matmul(W, mask, X[:n])
+    err = np.abs(y - ref).max()
+    rel = np.linalg.norm(y - ref) / np.linalg.norm(ref)
+    assert err <= 1e-2 and rel <= 1e-3, (n, err, rel)
+h = swm.gate_up_silu(f, fu, Xd[:16], 0.0).float().cpu().numpy()
+want = oracle.gate_up_silu(W, mask, Wu, mu, X[:16], 0.0)
+assert np.abs(h - want).max() <= 1e-2, np.abs(h - want).max()
+torch.cuda.synchronize()
+print("ok", flush=True)
+"""
+
+
+def test_decode_b_operands_from_memory_tall_ragged():
+    """A tall matrix (513 slabs, a ragged last tile column) makes the decode
+    plan load the B operands straight into registers at 9-16 tokens (the
+    dispatch log says so); spmm at N = 9, 13, 16 and the gated step at 16
+    tokens match the oracle.  A child process, because SWM_LOG is read once."""
+    import os
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    env = dict(os.environ, SWM_LOG="1")
+    r = subprocess.run([sys.executable, "-c", _DIRECT_B_CHECK, root, os.path.join(root, "tests")], env=env,
+                       capture_output=True, text=True, timeout=110)
+    assert r.returncode == 0 and r.stdout.strip().endswith("ok"), r.stdout[-2000:] + r.stderr[-2000:]
+    log = [ln for ln in r.stderr.splitlines() if ln.startswith("[swm] sparse_compress M=8208")]
+    assert log and all("B operands from memory" in ln for ln in log), log
+
+
 @pytest.mark.parametrize("mode", ["off", "on"])
 def test_dispatch_log_and_skip_switch(mode):
     """SWM_LOG=1 names every dispatch decision on stderr; SWM_SKIP forces the
