@@ -162,16 +162,17 @@ def rotating_dense(torch, W, min_bytes=ROTATE_BYTES):
 
 def profiled_traffic(profile_md):
     """HBM bytes per launch from a committed counter summary, if the kernel
-    source it was taken on is the one built now; else None."""
+    sources it was taken on are the ones built now; else None."""
     import hashlib
     import re
     try:
         text = open(os.path.join(ROOT, "profiles", profile_md)).read()
         meta = json.loads(re.search(r"<!-- bench-traffic: (\{.*\}) -->", text).group(1))
-        src = open(os.path.join(ROOT, meta["source"]), "rb").read()
-    except (OSError, AttributeError, ValueError, KeyError):
-        return None
-    if hashlib.sha256(src).hexdigest() != meta["source_sha256"]:
+        sources = meta.get("sources") or [[meta["source"], meta["source_sha256"]]]
+        for path, sha in sources:
+            if hashlib.sha256(open(os.path.join(ROOT, path), "rb").read()).hexdigest() != sha:
+                return None
+    except (OSError, AttributeError, ValueError, KeyError, TypeError):
         return None
     return int(meta["traffic_bytes_per_launch"])
 
@@ -358,7 +359,8 @@ def prefill_block(args, torch, swm, wl, G):
                      "achieved": useful / t_ws / 1e12, "frac": useful / t_ws / 1e12 / MFMA_F16_PEAK_TFLOPS,
                      "executed_TFLOPs": executed / t_ws / 1e12,
                      "frac_executed": executed / t_ws / 1e12 / MFMA_F16_PEAK_TFLOPS,
-                     "useful_flops_per_launch": useful, "executed_flops_per_launch": executed, "traffic": None},
+                     "useful_flops_per_launch": useful, "executed_flops_per_launch": executed,
+                     "traffic": profiled_traffic("prefill_upgate_n4096_traffic.md")},
     }
     if not args.no_cpu:
         _log("timing the CPU oracle on a 512-token slice")
