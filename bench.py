@@ -341,11 +341,17 @@ def prefill_block(args, torch, swm, wl, G):
     swm.dense_gemm(Wd, Xd, y)
     torch.cuda.synchronize()
     reps = 4
-    d_ws = pct(G.samples(G.capture([lambda: swm.spmm_ws(f, Xd, ws, y)] * reps), 10, reps))
-    d_on = pct(G.samples(G.capture([lambda: swm.spmm(f, Xd, y)] * reps), 10, reps))
-    d_de = pct(G.samples(G.capture([lambda: swm.dense_gemm(Wd, Xd, y)] * reps), 10, reps))
-    d_dc = pct(G.samples(G.capture([lambda: swm.decompress(f, ws.view(torch.float16)[:M * K].view(M, K))] * reps),
-                         10, reps))
+
+    def timed(fn):
+        # a few untimed replays first: the block follows host-side work (the
+        # oracle's timing), during which the GPU's clocks drop
+        g = G.capture([fn] * reps)
+        G.time(g, 3)
+        return pct(G.samples(g, 10, reps))
+    d_ws = timed(lambda: swm.spmm_ws(f, Xd, ws, y))
+    d_on = timed(lambda: swm.spmm(f, Xd, y))
+    d_de = timed(lambda: swm.dense_gemm(Wd, Xd, y))
+    d_dc = timed(lambda: swm.decompress(f, ws.view(torch.float16)[:M * K].view(M, K)))
     useful, executed = 2.0 * nnz * n, 2.0 * M * K * n
     t_ws, t_on, t_de = d_ws["median_us"] * 1e-6, d_on["median_us"] * 1e-6, d_de["median_us"] * 1e-6
     blk = {
