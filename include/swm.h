@@ -61,7 +61,8 @@
  *    (tokens from which swm_spmm_ws expands W, at least 33; read once),
  *    SWM_GLU_TPW (tiles per wave of swm_gate_up_silu; read once), SWM_SMFMAC
  *    (0: the sparse-matrix-core route of SWM_CFG_SMFMAC handles off;
- *    read once).
+ *    read once), SWM_SMF_WAVES=4 (that route's 2:4 kernel with four waves
+ *    per block instead of eight; read once).
  */
 #ifndef SWM_H_
 #define SWM_H_

@@ -34,6 +34,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cstdlib>
 
 #include "kernels.h"
 
@@ -214,18 +215,26 @@ __device__ __forceinline__ uint32_t swz_a(int row, int chunk) {
 constexpr int SBM = 256, SBK = 64;
 constexpr int kSA = SBM * SBK;       // values bytes per stage (32 halves per row)
 constexpr int kSM = SBM * 8;         // index bytes per stage (4 uint16 per row)
-// Block of 256 rows x 64 kWJ tokens: waves 2 x 2, each 4 x kWJ accumulators
-// of 32 x 32.  kWJ = 4 (256 x 256) or 2 (256 x 128, for token counts that
-// leave 256 x 256 blocks short of the CUs).
-template <bool kRes, int kWJ>
+// Block of 256 rows x 64 kWJ tokens: waves 2 x kWN, each 4 x kJ accumulators
+// of 32 x 32 (kJ = 2 kWJ / kWN).  kWJ = 4 (256 x 256) or 2 (256 x 128, for
+// token counts that leave 256 x 256 blocks short of the CUs).  kWN = 2: four
+// waves of 128 x 32 kWJ; kWN = 4 (256 x 256 only): eight waves of 128 x 64,
+// two per SIMD.
+template <bool kRes, int kWJ, int kWN = 2>
 struct SmfShape {
+  static constexpr int kNW = 2 * kWN;           // waves
+  static constexpr int kJ = 2 * kWJ / kWN;      // accumulator columns per wave
   static constexpr int kBN = 64 * kWJ;          // tokens per block
   static constexpr int kSB = kBN * SBK * 2;     // activation bytes per stage
-  static constexpr int kIB = kSB / 4096;        // activation loads per wave per step
+  static constexpr int kIV = kSA / (1024 * kNW);  // value loads per wave per step (per layer)
+  static constexpr int kII = kSM / (256 * kNW);   // index loads per wave per step (per layer)
+  static constexpr int kIB = kSB / (1024 * kNW);  // activation loads per wave per step
+  static_assert(kIV * 1024 * kNW == kSA && kII * 256 * kNW == kSM && kIB * 1024 * kNW == kSB && kJ >= 1,
+                "whole loads per wave");
   static constexpr int kStage = kSA + kSM + (kRes ? kSA + kSM : 0) + kSB;
   static constexpr int kStages = 3 * kStage <= 160 * 1024 ? 3 : 2;  // LDS stages
-  static constexpr int kOps = 6 + (kRes ? 6 : 0) + kIB;  // LDS-direct loads per wave per step
-  static constexpr int kEpi = 4 * (32 * kWJ) * (2 * 128 + 8);  // epilogue: four transposing regions
+  static constexpr int kOps = (kIV + kII) * (kRes ? 2 : 1) + kIB;  // LDS-direct loads per wave per step
+  static constexpr int kEpi = kNW * (32 * kJ) * (2 * 128 + 8);  // epilogue: one transposing region per wave
   static constexpr int kLds = kStages * kStage > kEpi ? kStages * kStage : kEpi;
   static_assert(kLds <= 160 * 1024, "LDS");
 };
@@ -251,9 +260,9 @@ __device__ __forceinline__ void wait_vm_lgkm0() {
   __builtin_amdgcn_s_waitcnt((n & 15) | (7 << 4) | (((n >> 4) & 3) << 14));
 }
 
-// 256 threads, waves in a 2 x 2 layout, each owning 4 x 4 accumulators of
-// 32 x 32 (a 128 x 128 quarter of the 256 x 256 output block); 64-column
-// K steps in two 32-column slices.  The tiles go from global memory straight
+// Waves in a 2 x kWN layout (SmfShape), each owning 4 x kJ accumulators of
+// 32 x 32 (a 128-row x 32 kJ-token part of the output block); 64-column K
+// steps in two 32-column slices.  The tiles go from global memory straight
 // into LDS (global_load_lds_dwordx4 / _dword: lane l of an instruction writes
 // 16 or 4 bytes at LDS base + 16l or 4l, so each lane loads the chunk that
 // the swizzled layout places there) and need no staging registers.  The
@@ -262,9 +271,10 @@ __device__ __forceinline__ void wait_vm_lgkm0() {
 // the wait before that barrier is explicit: at most the later steps' loads
 // may still be in flight.  kRes: the residual layer is staged and multiplied
 // too, into the same accumulators.
-template <bool kRes, int kWJ>
-__global__ __launch_bounds__(256) void smf_kernel(SmfArgs a) {
-  using S = SmfShape<kRes, kWJ>;
+template <bool kRes, int kWJ, int kWN = 2>
+__global__ __launch_bounds__(128 * kWN) void smf_kernel(SmfArgs a) {
+  using S = SmfShape<kRes, kWJ, kWN>;
+  constexpr int kJ = S::kJ, kIV = S::kIV, kII = S::kII;
   constexpr int kStage = S::kStage;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   int tm, tn;
@@ -272,7 +282,7 @@ __global__ __launch_bounds__(256) void smf_kernel(SmfArgs a) {
   const int tid = int(threadIdx.x);
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / kWN, wn = wave % kWN;
   const int m0 = tm * SBM, n0 = tn * S::kBN;
   // stage layout: values | indices | [residual values | residual indices] | activations
   auto oV = [&](int st) { return uint32_t(st * kStage); };
@@ -285,11 +295,11 @@ __global__ __launch_bounds__(256) void smf_kernel(SmfArgs a) {
 
   // Per-lane sources of the LDS-direct loads (32-bit byte offsets; the
   // launcher checks that every operand fits 4 GiB).
-  //  values: instruction i of wave w fills LDS bytes (4w + i) KiB + 16 lane:
-  //    row r = 16 (4w + i) + lane/4, stored chunk lane%4 = logical chunk
-  //    (lane%4) ^ ((r >> 2) & 3);
-  //  indices: instruction i fills (2w + i) * 256 + 4 lane: row 32 (2w + i) +
-  //    lane/2, dword lane%2 of the row's 8 bytes;
+  //  values: instruction i of wave w fills LDS bytes (kIV w + i) KiB + 16
+  //    lane: row r = 16 (kIV w + i) + lane/4, stored chunk lane%4 = logical
+  //    chunk (lane%4) ^ ((r >> 2) & 3);
+  //  indices: instruction i fills (kII w + i) * 256 + 4 lane: row
+  //    32 (kII w + i) + lane/2, dword lane%2 of the row's 8 bytes;
   //  activations: instruction i fills (8w + i) KiB + 16 lane: token
   //    r = 8 (8w + i) + lane/8, stored chunk lane%8 = logical chunk
   //    (lane%8) ^ ((r >> 1) & 7).
@@ -298,17 +308,17 @@ __global__ __launch_bounds__(256) void smf_kernel(SmfArgs a) {
   const uint8_t* vrb = reinterpret_cast<const uint8_t*>(a.vres);
   const uint8_t* mb = reinterpret_cast<const uint8_t*>(a.m24);
   const uint8_t* mrb = reinterpret_cast<const uint8_t*>(a.mres);
-  uint32_t voff[4], ioff[2], xoff[S::kIB];
+  uint32_t voff[kIV], ioff[kII], xoff[S::kIB];
   int xcol[S::kIB];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int r = 16 * (4 * wave + i) + (lane >> 2);
+  for (int i = 0; i < kIV; ++i) {
+    const int r = 16 * (kIV * wave + i) + (lane >> 2);
     const int c = (lane & 3) ^ ((r >> 2) & 3);
     voff[i] = 2u * uint32_t(min(m0 + r, a.M - 1)) * uint32_t(a.ldv) + 16u * uint32_t(c);
   }
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int r = 32 * (2 * wave + i) + (lane >> 1);
+  for (int i = 0; i < kII; ++i) {
+    const int r = 32 * (kII * wave + i) + (lane >> 1);
     ioff[i] = 2u * uint32_t(min(m0 + r, a.M - 1)) * uint32_t(a.ldm) + 4u * uint32_t(lane & 1);
   }
 #pragma unroll
@@ -317,22 +327,23 @@ __global__ __launch_bounds__(256) void smf_kernel(SmfArgs a) {
     xcol[i] = 8 * ((lane & 7) ^ ((r >> 1) & 7));
     xoff[i] = 2u * uint32_t(min(n0 + r, a.N - 1)) * uint32_t(a.ldx) + 2u * uint32_t(xcol[i]);
   }
-  // load o of step kq: values 0-3, indices 4-5, [residual values 6-9,
-  // residual indices 10-11,] activations last (8).  Past the end: a reload of
-  // the last step into the stage of step kq, which no later step reads.
+  // load o of step kq: values, indices, [residual values, residual
+  // indices,] activations last.  Past the end: a reload of the last step
+  // into the stage of step kq, which no later step reads.
   auto issue_op = [&](int kq, int o) {
     const int st = kq % S::kStages;
     const int ks = min(kq, nsteps - 1);
     const uint32_t vk = 64u * uint32_t(ks), mk = 8u * uint32_t(ks);
-    constexpr int kB0 = kRes ? 12 : 6;  // first activation load
-    if (o < 4) {
-      lds_dma16(vb + (voff[o] + vk), smem + oV(st) + (4 * wave + o) * 1024);
-    } else if (o < 6) {
-      lds_dma4(mb + (ioff[o - 4] + mk), smem + oI(st) + (2 * wave + o - 4) * 256);
-    } else if (kRes && o < 10) {
-      lds_dma16(vrb + (voff[o - 6] + vk), smem + oVr(st) + (4 * wave + o - 6) * 1024);
-    } else if (kRes && o < 12) {
-      lds_dma4(mrb + (ioff[o - 10] + mk), smem + oIr(st) + (2 * wave + o - 10) * 256);
+    constexpr int kL = kIV + kII;            // loads of one layer
+    constexpr int kB0 = kRes ? 2 * kL : kL;  // first activation load
+    if (o < kIV) {
+      lds_dma16(vb + (voff[o] + vk), smem + oV(st) + (kIV * wave + o) * 1024);
+    } else if (o < kL) {
+      lds_dma4(mb + (ioff[o - kIV] + mk), smem + oI(st) + (kII * wave + o - kIV) * 256);
+    } else if (kRes && o < kL + kIV) {
+      lds_dma16(vrb + (voff[o - kL] + vk), smem + oVr(st) + (kIV * wave + o - kL) * 1024);
+    } else if (kRes && o < 2 * kL) {
+      lds_dma4(mrb + (ioff[o - kL - kIV] + mk), smem + oIr(st) + (kII * wave + o - kL - kIV) * 256);
     } else {
       const int i = o - kB0;
       const bool in = ks * SBK + xcol[i] < a.K;  // K % 8 == 0: a chunk is wholly inside or outside
@@ -346,11 +357,11 @@ __global__ __launch_bounds__(256) void smf_kernel(SmfArgs a) {
     for (int o = 0; o < S::kOps; ++o) issue_op(kq, o);
   };
 
-  f32x16 acc[4][kWJ];
+  f32x16 acc[4][kJ];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < kWJ; ++j)
+    for (int j = 0; j < kJ; ++j)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
@@ -359,7 +370,7 @@ __global__ __launch_bounds__(256) void smf_kernel(SmfArgs a) {
   // both layers, B as two 16-byte halves, and one 8-byte index read per row
   // holding both slices' index words.
   half8 fa[2][4], far_[2][4];
-  half16 fb[2][kWJ];
+  half16 fb[2][kJ];
   u32x2 iv[4], ivr[4];
   auto read_a = [&](int st, int s, int i) {
     const int row = (wm * 4 + i) * 32 + lr;
@@ -368,7 +379,7 @@ __global__ __launch_bounds__(256) void smf_kernel(SmfArgs a) {
   };
   auto read_b = [&](int st, int s, int j) {
     // tokens (wn*4 + j)*32 + lr, slice rows 8q .. +7 and 16 + 8q .. +7
-    const int tok = (wn * kWJ + j) * 32 + lr;
+    const int tok = (wn * kJ + j) * 32 + lr;
     const u32x4 lo = lds_load16(base + oB(st) + swz_b(tok, 4 * s + q));
     const u32x4 hi = lds_load16(base + oB(st) + swz_b(tok, 4 * s + 2 + q));
     fb[s][j] = __builtin_bit_cast(half16, u32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
@@ -387,13 +398,13 @@ __global__ __launch_bounds__(256) void smf_kernel(SmfArgs a) {
   auto idx = [&](const u32x2& v, int s) { return int((v[s] >> (16 * q)) & 0xFFFFu); };
   int x1[4], x1r[4];  // slice 1's index words, kept while the next step's are read
   auto product = [&](int s, int m, const int* xi, const int* xr) {
-    const int i = m / kWJ, j = m % kWJ;
+    const int i = m / kJ, j = m % kJ;
     acc[i][j] = __builtin_amdgcn_smfmac_f32_32x32x32_f16(fa[s][i], fb[s][j], acc[i][j], xi[i], 0, 0);
     if constexpr (kRes)
       acc[i][j] = __builtin_amdgcn_smfmac_f32_32x32x32_f16(far_[s][i], fb[s][j], acc[i][j], xr[i], 0, 0);
   };
-  constexpr int kRead = 4 + kWJ;           // read units per slice (4 A, kWJ B)
-  constexpr int kM = 4 * kWJ;              // products per slice
+  constexpr int kRead = 4 + kJ;            // read units per slice (4 A, kJ B)
+  constexpr int kM = 4 * kJ;               // products per slice
   constexpr int kNext = 4 + kRead;         // step ks + 1: 4 index units, then slice 0's read units
 
   // Steps 0 .. kStages-1 fill every stage; step ks + kStages is requested in
@@ -458,18 +469,18 @@ __global__ __launch_bounds__(256) void smf_kernel(SmfArgs a) {
     }
   }
 
-  // Epilogue: fp16 round-to-nearest-even.  Each wave transposes its 128 x 128
-  // quadrant through its own LDS region (a row per token, padded by 8 bytes)
+  // Epilogue: fp16 round-to-nearest-even.  Each wave transposes its 128 x
+  // 32 kJ part through its own LDS region (a row per token, padded by 8 bytes)
   // so that the stores are 16 contiguous bytes per lane; every wave's loads
   // must have landed before any region is written.
   wait_vm_lgkm0<0>();
   __builtin_amdgcn_s_barrier();
-  constexpr int kRS = 2 * 128 + 8, kTN = 32 * kWJ;
+  constexpr int kRS = 2 * 128 + 8, kTN = 32 * kJ;
   const uint32_t reg = base + wave * (kTN * kRS);
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < kWJ; ++j)
+    for (int j = 0; j < kJ; ++j)
 #pragma unroll
       for (int qq = 0; qq < 4; ++qq) {
         const int n = j * 32 + (lane & 31), m = i * 32 + qq * 8 + (lane >> 5) * 4;
@@ -569,14 +580,29 @@ hipError_t launch_smf(const Header& h, const Sparse24Layout& L, bool residual, c
   const unsigned grid = unsigned((a.tiles_m * a.tiles_n + 7) / 8 * 8);
   constexpr size_t kL04 = SmfShape<false, 4>::kLds, kL02 = SmfShape<false, 2>::kLds;
   constexpr size_t kL14 = SmfShape<true, 4>::kLds, kL12 = SmfShape<true, 2>::kLds;
+  constexpr size_t kL04w = SmfShape<false, 4, 4>::kLds, kL02w = SmfShape<false, 2, 4>::kLds;
+  // Blocks of a 2:4 mask with eight waves (two per SIMD) unless
+  // SWM_SMF_WAVES=4 (read once).  Two A/B runs, us, q_proj 2:4: N = 4096
+  // (256 x 256 blocks) 109.8 / 111.0 with four waves against 92.9 / 92.9
+  // with eight; N = 1024 / 2048 (256 x 128 blocks) 57.5 / 68.7 against
+  // 54.8 / 65.4.  With a residual layer the 256 x 256 eight-wave instance
+  // would spill its A fragments, so that route keeps four waves.
+  static const bool eight = [] {
+    const char* e = getenv("SWM_SMF_WAVES");
+    return !(e && atoi(e) == 4);
+  }();
   if (residual) {
     if (wide)
       hipLaunchKernelGGL((smf_kernel<true, 4>), dim3(grid), dim3(256), kL14, s, a);
     else
       hipLaunchKernelGGL((smf_kernel<true, 2>), dim3(grid), dim3(256), kL12, s, a);
   } else {
-    if (wide)
+    if (wide && eight)
+      hipLaunchKernelGGL((smf_kernel<false, 4, 4>), dim3(grid), dim3(512), kL04w, s, a);
+    else if (wide)
       hipLaunchKernelGGL((smf_kernel<false, 4>), dim3(grid), dim3(256), kL04, s, a);
+    else if (eight)
+      hipLaunchKernelGGL((smf_kernel<false, 2, 4>), dim3(grid), dim3(512), kL02w, s, a);
     else
       hipLaunchKernelGGL((smf_kernel<false, 2>), dim3(grid), dim3(256), kL02, s, a);
   }
