@@ -269,6 +269,41 @@ swm_status swm_spmm_ws(const swm_format* f, const void* X, int64_t ldx, void* Y,
 swm_status swm_gate_up_silu(const swm_format* g, const swm_format* u, const void* X, int64_t ldx, void* H,
                             int64_t ldh, int32_t n, float tau, void* stream);
 
+/* Bytes of device workspace swm_gate_up_silu_ws uses for n tokens: 0 below
+ * 33 tokens (the decode launches of swm_gate_up_silu), else 2*M*K*2 rounded
+ * up to 256 (the gate and up weights expanded side by side); 0 for NULL or
+ * mismatched handles. */
+size_t swm_gate_up_silu_workspace_bytes(const swm_format* g, const swm_format* u, int64_t n);
+
+/* gate_up_silu_ws: swm_gate_up_silu for any token count n >= 1, the same
+ * hidden activation H = SiLU(X W_g^T) (.) (X W_u^T) with |H| < tau (after
+ * rounding to fp16) stored as +0 ("Reduced Matrix Multiplication" blog page,
+ * Secs. 3.2 and 4.1-4.2; the FFN of the prefill input, moderate-sparsity
+ * page Sec. 2.1).  Below 33 tokens it is swm_gate_up_silu (the workspace is
+ * not touched).  From 33 tokens both weights are expanded into the workspace
+ * as one matrix of interleaved rows (gate row m at row 2m, up row m at row
+ * 2m + 1) and one dense MFMA product computes both, its epilogue forming
+ * h = SiLU(g) * u from the fp32 accumulators of the two rows, rounded once
+ * to fp16: no g or u buffer and no separate element-wise pass.  The result
+ * equals SiLU(g) * u of two swm_spmm_ws calls up to fp32 summation order.
+ *  g, u: handles of the gate and up weights, same M and K.  X: DEVICE fp16
+ *  token-major n x K (ldx >= K).  H: DEVICE fp16 n x M (ldh >= M),
+ *  overwritten.  tau: 0 <= tau <= 65504 (0 keeps every entry).
+ *  workspace: DEVICE, 16-byte aligned, ws_bytes >=
+ *  swm_gate_up_silu_workspace_bytes(g, u, n), owned by the caller, contents
+ *  undefined afterwards (calls sharing it must be ordered on one stream).
+ *  SWM_ERR_INVALID_ARG: NULL handles, X or H; n < 1; tau outside its range
+ *  or NaN; shapes that differ; leading dimensions too small; a workspace
+ *  that is NULL or too small when n >= 33; a handle on another device.
+ *  SWM_ERR_ALIGN: X not 16-byte aligned or ldx % 8 != 0, or a workspace that
+ *  is not 16-byte aligned.  SWM_ERR_UNSUPPORTED: K < 8 or K % 8 != 0, tiles
+ *  other than 16 x 64, or (from 33 tokens) 2*M*K or (n-1)*ldx + K beyond the
+ *  product kernel's 32-bit byte offsets; below 33 tokens swm_gate_up_silu's
+ *  errors.  Asynchronous on stream. */
+swm_status swm_gate_up_silu_ws(const swm_format* g, const swm_format* u, const void* X, int64_t ldx, void* H,
+                               int64_t ldh, int64_t n, float tau, void* workspace, size_t ws_bytes,
+                               void* stream);
+
 /* spmspv: as swm_spmm for 1 <= n <= 16 tokens, for activations with zero
  * input channels (x[t][k] == +0 or -0 for all tokens t).  Such channels
  * contribute exact zeros, so the result equals swm_spmm's up to fp32

@@ -66,6 +66,8 @@ SIGNATURES = {
     "swm_spmspv_noalloc": (_i32, [_vp, _vp, _i64, _vp, _i64, _i32, _vp]),
     "swm_spmspv_threshold": (_i32, [_vp, _vp, _i64, _vp, _i64, _i32, ctypes.c_float, _vp]),
     "swm_gate_up_silu": (_i32, [_vp, _vp, _vp, _i64, _vp, _i64, _i32, ctypes.c_float, _vp]),
+    "swm_gate_up_silu_workspace_bytes": (_sz, [_vp, _vp, _i64]),
+    "swm_gate_up_silu_ws": (_i32, [_vp, _vp, _vp, _i64, _vp, _i64, _i64, ctypes.c_float, _vp, _sz, _vp]),
     "swm_format_enable_skipping": (_i32, [_vp, _vp, ctypes.POINTER(_u64)]),
     "swm_format_enable_smfmac": (_i32, [_vp, _vp, ctypes.POINTER(_u64)]),
     "swm_colruns_encode_blob": (_i32, [_vp, _sz, _vp, _sz, ctypes.POINTER(_sz)]),
@@ -338,6 +340,32 @@ def gate_up_silu(gate: Format, up: Format, X, tau: float = 0.0, H=None, stream=N
     hp, ldh = _dev2d(H, "H", rows=n, cols=gate.M)
     _check(lib.swm_gate_up_silu(gate._h, up._h, xp, ldx, hp, ldh, n, float(tau), _stream_ptr(stream)),
            "swm_gate_up_silu")
+    return H
+
+
+def gate_up_silu_workspace_bytes(gate: Format, up: Format, n: int) -> int:
+    """Device workspace bytes gate_up_silu_ws uses for n tokens (0: none)."""
+    return int(load().swm_gate_up_silu_workspace_bytes(gate._h, up._h, int(n)))
+
+
+def gate_up_silu_ws(gate: Format, up: Format, X, workspace, tau: float = 0.0, H=None, stream=None):
+    """gate_up_silu for any token count: from 33 tokens the gate and up
+    weights are expanded into `workspace` (a contiguous CUDA uint8 tensor of at
+    least gate_up_silu_workspace_bytes(gate, up, n) bytes; None below 33
+    tokens) and one dense MFMA product forms H with the gated epilogue."""
+    lib = load()
+    n = X.shape[0]
+    xp, ldx = _dev2d(X, "X", cols=gate.K)
+    H = _out(H, n, gate.M, X)
+    hp, ldh = _dev2d(H, "H", rows=n, cols=gate.M)
+    if workspace is None:
+        wp, wb = None, 0
+    else:
+        if not workspace.is_cuda or not workspace.is_contiguous():
+            raise ValueError("workspace must be a contiguous CUDA tensor")
+        wp, wb = ctypes.c_void_p(workspace.data_ptr()), workspace.numel() * workspace.element_size()
+    _check(lib.swm_gate_up_silu_ws(gate._h, up._h, xp, ldx, hp, ldh, n, float(tau), wp, wb, _stream_ptr(stream)),
+           "swm_gate_up_silu_ws")
     return H
 
 

@@ -658,6 +658,52 @@ swm_status swm_gate_up_silu(const swm_format* g, const swm_format* u, const void
   return SWM_OK;
 }
 
+// Prefill sizes of the gated FFN step: from this token count the gate and up
+// weights are expanded into the workspace and multiplied by the dense MFMA
+// kernel with the gated epilogue; below it, swm_gate_up_silu's decode
+// launches.
+constexpr int64_t kGluExpandMinN = 33;
+
+size_t swm_gate_up_silu_workspace_bytes(const swm_format* g, const swm_format* u, int64_t n) {
+  if (!g || !u || n < kGluExpandMinN || g->h.m != u->h.m || g->h.k != u->h.k) return 0;
+  return align_up(size_t(2) * size_t(g->h.m) * size_t(g->h.k) * 2, 256);
+}
+
+swm_status swm_gate_up_silu_ws(const swm_format* g, const swm_format* u, const void* X, int64_t ldx, void* H,
+                               int64_t ldh, int64_t n, float tau, void* workspace, size_t ws_bytes,
+                               void* stream) {
+  if (!g || !u || !X || !H) return SWM_ERR_INVALID_ARG;
+  if (n < 1 || !(tau >= 0.f) || !(tau <= 65504.f)) return SWM_ERR_INVALID_ARG;
+  if (n < kGluExpandMinN) return swm_gate_up_silu(g, u, X, ldx, H, ldh, int32_t(n), tau, stream);
+  if (g->h.m != u->h.m || g->h.k != u->h.k) return SWM_ERR_INVALID_ARG;
+  if (ldx < g->h.k || ldh < g->h.m || ldx <= 0 || ldh <= 0) return SWM_ERR_INVALID_ARG;
+  if (!workspace || ws_bytes < swm_gate_up_silu_workspace_bytes(g, u, n)) return SWM_ERR_INVALID_ARG;
+  if (reinterpret_cast<uintptr_t>(workspace) & 15) return SWM_ERR_ALIGN;
+  swm_status st = check_tile_supported(g->h);
+  if (st == SWM_OK) st = check_tile_supported(u->h);
+  if (st != SWM_OK) return st;
+  if (!on_current_device(g) || !on_current_device(u)) return SWM_ERR_INVALID_ARG;
+  if (g->h.k < 8 || g->h.k % 8 != 0) return SWM_ERR_UNSUPPORTED;
+  if (ldx % 8 != 0 || (reinterpret_cast<uintptr_t>(X) & 15) != 0) return SWM_ERR_ALIGN;
+  const int64_t M = int64_t(g->h.m), K = int64_t(g->h.k);
+  if (M == 0) return SWM_OK;
+  if (2 * M > (int64_t(1) << 31) - 64 || !swm::prefill_dense_dma_fits(2 * M, K, K, n, ldx))
+    return SWM_ERR_UNSUPPORTED;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  int dev = 0;
+  SWM_HIP(hipGetDevice(&dev));
+  swm_log("gate_up_silu_ws M=%lld K=%lld n=%lld: gate and up expanded as interleaved rows + dense MFMA with the "
+          "gated epilogue",
+          (long long)M, (long long)K, (long long)n);
+  // gate row m -> workspace row 2m, up row m -> row 2m + 1 (row stride K)
+  uint16_t* w = static_cast<uint16_t*>(workspace);
+  SWM_HIP(swm::launch_decompress(g->d, w, 2 * K, s));
+  SWM_HIP(swm::launch_decompress(u->d, w + K, 2 * K, s));
+  SWM_HIP(swm::launch_prefill_dense_glu(w, K, static_cast<const uint16_t*>(X), ldx, static_cast<uint16_t*>(H), ldh,
+                                        2 * M, K, n, tau, num_cus(dev), s));
+  return SWM_OK;
+}
+
 swm_status swm_hbm_stream(const void* buf, size_t bytes, int32_t unroll, int32_t blocks,
                           uint32_t* out, void* stream) {
   if (!buf || !out || bytes % 16 || blocks <= 0) return SWM_ERR_INVALID_ARG;

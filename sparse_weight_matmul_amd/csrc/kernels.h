@@ -93,6 +93,14 @@ hipError_t launch_dense_small(const DensePlan& p, const uint16_t* W, int64_t ldw
 hipError_t launch_prefill_dense(const uint16_t* W, int64_t ldw, const uint16_t* X, int64_t ldx,
                                 uint16_t* Y, int64_t ldy, int64_t M, int64_t K, int64_t N, int num_cus,
                                 hipStream_t s);
+// The same kernel with the gated-FFN epilogue: W is M2 = 2 x channels rows
+// with gate and up rows interleaved (2c, 2c+1), H (N x M2/2) receives
+// SiLU(g) * u rounded to fp16, +0 where |h| < tau.  Needs the LDS-direct
+// kernel's 32-bit byte offsets (prefill_dense_dma_fits).
+hipError_t launch_prefill_dense_glu(const uint16_t* W, int64_t ldw, const uint16_t* X, int64_t ldx,
+                                    uint16_t* H, int64_t ldh, int64_t M2, int64_t K, int64_t N, float tau,
+                                    int num_cus, hipStream_t s);
+bool prefill_dense_dma_fits(int64_t M, int64_t ldw, int64_t K, int64_t N, int64_t ldx);
 hipError_t launch_prefill_sparse(const DevFormat& f, const uint16_t* X, int64_t ldx, uint16_t* Y,
                                  int64_t ldy, int64_t N, hipStream_t s);
 // The prefill kernels need K >= 8, K % 8 == 0, ldx % 8 == 0 and a 16-byte aligned X.

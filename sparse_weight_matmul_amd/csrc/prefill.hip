@@ -77,6 +77,7 @@ struct PrefillArgs {
   int tiles_m, tiles_n, kt, mt;
   int group_m;     // output-tile rows per L2 group
   int run_chunks;  // 512-byte run chunks per tile (1..4), sparse variant
+  float tau;       // gated epilogue: |h| below tau (after fp16 rounding) is stored as +0
 };
 
 // Map the workgroup id to an output tile: regroup ids so that each XCD (id % 8)
@@ -312,7 +313,13 @@ struct DmaShape {
 // loads of step ks + kStages (into the stage just released) are spread
 // between the slice's products, so a load has kStages - 1 steps to arrive
 // and the matrix cores do not wait for the first fragments of a step.
-template <int kWI, int kWJ, int kWM, int kWN>
+//
+// kGlu: W holds the gate and up rows of a gated FFN interleaved (row 2c =
+// gate channel c, row 2c+1 = up channel c; M = 2 x channels) and Y receives
+// H (N x M/2), h = SiLU(g) * u rounded once to fp16, +0 where |h| < tau.  A
+// lane's accumulator holds four consecutive rows of one token, so each
+// gate / up pair meets in the same lane's registers.
+template <int kWI, int kWJ, int kWM, int kWN, bool kGlu = false>
 __global__ __launch_bounds__(64 * kWM * kWN) void dense_dma_kernel(PrefillArgs a) {
   using S = DmaShape<kWI, kWJ, kWM, kWN>;
   constexpr int kAT = S::kAT, kStage = kAT + S::kBTB;
@@ -452,7 +459,8 @@ __global__ __launch_bounds__(64 * kWM * kWN) void dense_dma_kernel(PrefillArgs a
   // every wave's loads must have landed before any region is written.
   wait_vm_lgkm0<0>();
   __builtin_amdgcn_s_barrier();
-  constexpr int kTM = 32 * kWI, kTN = 32 * kWJ, kRS = 2 * kTM + 8;
+  // output rows per wave quadrant: 32 kWI, or half as many gated channels
+  constexpr int kTM = kGlu ? 16 * kWI : 32 * kWI, kTN = 32 * kWJ, kRS = 2 * kTM + 8;
   const uint32_t reg = base + wave * (kTN * kRS);
 #pragma unroll
   for (int i = 0; i < kWI; ++i)
@@ -461,16 +469,31 @@ __global__ __launch_bounds__(64 * kWM * kWN) void dense_dma_kernel(PrefillArgs a
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int n = j * 32 + (lane & 31), m = i * 32 + q * 8 + (lane >> 5) * 4;
-        uint16_t h[4];
+        if constexpr (kGlu) {
+          // rows m, m+1 are gate / up of channel m/2, rows m+2, m+3 of m/2+1
+          uint16_t h[2];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) h[e] = __builtin_bit_cast(uint16_t, _Float16(acc[i][j][q * 4 + e]));
-        const u32x2 pk = {uint32_t(h[0]) | (uint32_t(h[1]) << 16), uint32_t(h[2]) | (uint32_t(h[3]) << 16)};
-        *reinterpret_cast<lds_u32x2*>(static_cast<uintptr_t>(reg + n * kRS + 2 * m)) = pk;
+          for (int e = 0; e < 2; ++e) {
+            const float g = acc[i][j][q * 4 + 2 * e], u = acc[i][j][q * 4 + 2 * e + 1];
+            _Float16 v = _Float16(g / (1.f + expf(-g)) * u);
+            if (!(fabsf(float(v)) >= a.tau)) v = _Float16(0.f);
+            h[e] = __builtin_bit_cast(uint16_t, v);
+          }
+          *reinterpret_cast<__attribute__((address_space(3))) uint32_t*>(
+              static_cast<uintptr_t>(reg + n * kRS + m)) = uint32_t(h[0]) | (uint32_t(h[1]) << 16);
+        } else {
+          uint16_t h[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) h[e] = __builtin_bit_cast(uint16_t, _Float16(acc[i][j][q * 4 + e]));
+          const u32x2 pk = {uint32_t(h[0]) | (uint32_t(h[1]) << 16), uint32_t(h[2]) | (uint32_t(h[3]) << 16)};
+          *reinterpret_cast<lds_u32x2*>(static_cast<uintptr_t>(reg + n * kRS + 2 * m)) = pk;
+        }
       }
   constexpr int kLPR = kTM / 8;    // lanes per token row
   constexpr int kRPI = 64 / kLPR;  // rows per instruction
-  const int gm = m0 + wm * kTM + (lane % kLPR) * 8;
-  const bool vec = (a.ldy % 8 == 0) && ((reinterpret_cast<uintptr_t>(a.Y) & 15) == 0) && gm + 8 <= a.M;
+  const int Mo = kGlu ? a.M / 2 : a.M;  // rows (or gated channels) of Y
+  const int gm = (kGlu ? m0 / 2 : m0) + wm * kTM + (lane % kLPR) * 8;
+  const bool vec = (a.ldy % 8 == 0) && ((reinterpret_cast<uintptr_t>(a.Y) & 15) == 0) && gm + 8 <= Mo;
 #pragma unroll
   for (int r = 0; r < kTN; r += kRPI) {
     const int nl = r + lane / kLPR;
@@ -482,7 +505,7 @@ __global__ __launch_bounds__(64 * kWM * kWN) void dense_dma_kernel(PrefillArgs a
       *reinterpret_cast<u32x4*>(dst) = v;
     } else {
       for (int e = 0; e < 8; ++e)
-        if (gm + e < a.M) dst[e] = uint16_t(v[e / 2] >> (16 * (e % 2)));
+        if (gm + e < Mo) dst[e] = uint16_t(v[e / 2] >> (16 * (e % 2)));
     }
   }
 }
@@ -768,7 +791,7 @@ bool prefill_sparse_fits(const Header& h, int64_t N, int64_t ldx) {
 }
 
 namespace {
-template <int kWI, int kWJ>
+template <int kWI, int kWJ, bool kGlu = false>
 hipError_t launch_dense(PrefillArgs a, hipStream_t s) {
   a.tiles_m = int((a.M + 64 * kWI - 1) / (64 * kWI));
   a.tiles_n = int((a.N + 64 * kWJ - 1) / (64 * kWJ));
@@ -780,13 +803,15 @@ hipError_t launch_dense(PrefillArgs a, hipStream_t s) {
   }();
   const bool fits = 2 * (int64_t(a.M - 1) * a.ldw + a.K) < (int64_t(1) << 32) &&
                     2 * (int64_t(a.N - 1) * a.ldx + a.K) < (int64_t(1) << 32);
-  if (dma && fits) {
+  if (kGlu && !fits) return hipErrorInvalidValue;  // the gated epilogue exists in this kernel only
+  if (kGlu || (dma && fits)) {
     // 256 x 256 with eight waves (two per SIMD, 128 x 64 each); the smaller
     // blocks with four
     constexpr int kWN = kWI == 4 && kWJ == 4 ? 4 : 2;
     constexpr int kJ = kWI == 4 && kWJ == 4 ? 2 : kWJ;
     using S = DmaShape<kWI, kJ, 2, kWN>;
-    hipLaunchKernelGGL((dense_dma_kernel<kWI, kJ, 2, kWN>), dim3(grid_size(a)), dim3(64 * S::kNW), S::kLds, s, a);
+    hipLaunchKernelGGL((dense_dma_kernel<kWI, kJ, 2, kWN, kGlu>), dim3(grid_size(a)), dim3(64 * S::kNW), S::kLds,
+                       s, a);
     return hipGetLastError();
   }
   const size_t lds = size_t(2) * (64 * kWI + 64 * kWJ) * BK * 2;
@@ -795,12 +820,15 @@ hipError_t launch_dense(PrefillArgs a, hipStream_t s) {
 }
 }  // namespace
 
-hipError_t launch_prefill_dense(const uint16_t* W, int64_t ldw, const uint16_t* X, int64_t ldx,
-                                uint16_t* Y, int64_t ldy, int64_t M, int64_t K, int64_t N, int num_cus,
-                                hipStream_t s) {
+namespace {
+hipError_t launch_dense_any(const uint16_t* W, int64_t ldw, const uint16_t* X, int64_t ldx, uint16_t* Y,
+                            int64_t ldy, int64_t M, int64_t K, int64_t N, int num_cus, bool glu, float tau,
+                            hipStream_t s) {
   PrefillArgs a = make_args(M, N, K, X, ldx, Y, ldy);
   a.W = W;
   a.ldw = ldw;
+  a.tau = tau;
+  if (glu && M % 2 != 0) return hipErrorInvalidValue;
   if (a.tiles_m == 0 || a.tiles_n == 0) return hipSuccess;
   if (K < 8 || K % 8 != 0) return hipErrorInvalidValue;
   // Block shape 256 x 256, 256 x 128 or 128 x 128: the one with the fewest
@@ -825,9 +853,31 @@ hipError_t launch_prefill_dense(const uint16_t* W, int64_t ldw, const uint16_t* 
   if (const char* e = getenv("SWM_DENSE_BLOCK")) {
     if (*e >= '1' && *e <= '3') shape = *e - '0';
   }
+  if (glu) {
+    if (shape == 1) return launch_dense<4, 4, true>(a, s);
+    if (shape == 2) return launch_dense<4, 2, true>(a, s);
+    return launch_dense<2, 2, true>(a, s);
+  }
   if (shape == 1) return launch_dense<4, 4>(a, s);
   if (shape == 2) return launch_dense<4, 2>(a, s);
   return launch_dense<2, 2>(a, s);
+}
+}  // namespace
+
+hipError_t launch_prefill_dense(const uint16_t* W, int64_t ldw, const uint16_t* X, int64_t ldx,
+                                uint16_t* Y, int64_t ldy, int64_t M, int64_t K, int64_t N, int num_cus,
+                                hipStream_t s) {
+  return launch_dense_any(W, ldw, X, ldx, Y, ldy, M, K, N, num_cus, false, 0.f, s);
+}
+
+hipError_t launch_prefill_dense_glu(const uint16_t* W, int64_t ldw, const uint16_t* X, int64_t ldx,
+                                    uint16_t* H, int64_t ldh, int64_t M2, int64_t K, int64_t N, float tau,
+                                    int num_cus, hipStream_t s) {
+  return launch_dense_any(W, ldw, X, ldx, H, ldh, M2, K, N, num_cus, true, tau, s);
+}
+
+bool prefill_dense_dma_fits(int64_t M, int64_t ldw, int64_t K, int64_t N, int64_t ldx) {
+  return 2 * ((M - 1) * ldw + K) < (int64_t(1) << 32) && 2 * ((N - 1) * ldx + K) < (int64_t(1) << 32);
 }
 
 size_t prefill_sparse_lds(const Header& h) {

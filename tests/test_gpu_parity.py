@@ -1071,6 +1071,145 @@ def test_gate_up_silu_errors(gpu_lib):
     torch.cuda.synchronize()
 
 
+# ------------------------------------------------------------------ gated FFN hidden activation (prefill)
+def _glu_ws(swm, fg, fu, X, tau, extra=0):
+    """gate_up_silu_ws with a fresh workspace of exactly the bytes it asks for (+ extra)."""
+    import torch
+    n = X.shape[0]
+    nb = swm.gate_up_silu_workspace_bytes(fg, fu, n)
+    ws = torch.empty(nb + extra, dtype=torch.uint8, device="cuda") if nb + extra > 0 else None
+    return swm.gate_up_silu_ws(fg, fu, _t(X), ws, tau), nb
+
+
+@pytest.fixture(scope="module")
+def gate_up_prefill(gpu_lib):
+    """gate/up 11008x4096 at 50% (the Llama-2-7B layer's), 640 prefill tokens."""
+    Wg, mg, X = wl.layer_linear(4, 640)
+    Wu, mu, _ = wl.layer_linear(5, 640)
+    fg, fu = gpu_lib.sparse_compress(Wg, mg), gpu_lib.sparse_compress(Wu, mu)
+    full = oracle.gate_up_silu(Wg, mg, Wu, mu, X, 0.0)
+    return Wg, mg, Wu, mu, X, fg, fu, full
+
+
+@pytest.mark.parametrize("N", [33, 640])
+@pytest.mark.parametrize("tau", [0.0, 0.3])
+def test_gate_up_silu_ws_llama_shape(gpu_lib, gate_up_prefill, N, tau):
+    """The prefill route (both weights expanded as interleaved rows, one dense
+    MFMA product with the gated epilogue) against the oracle, every output;
+    640 tokens span three 256-token blocks with a ragged last one."""
+    Wg, mg, Wu, mu, X, fg, fu, full = gate_up_prefill
+    H, nb = _glu_ws(gpu_lib, fg, fu, X[:N], tau)
+    assert nb == 2 * Wg.shape[0] * Wg.shape[1] * 2
+    assert_glu_close(_np(H), full[:N], tau, f"gate/up prefill N={N} tau={tau}")
+
+
+@pytest.mark.parametrize("M,K,N,tau", [(1000, 1032, 33, 0.1), (520, 392, 300, 0.0), (300, 8192, 100, 0.2),
+                                       (17, 136, 257, 0.05), (4096, 4096, 1100, 0.3), (131, 520, 70, 0.0)])
+def test_gate_up_silu_ws_ragged(gpu_lib, M, K, N, tau):
+    """Ragged channel and token counts (partial row and token blocks, the 128-
+    and 256-row block shapes) against the oracle."""
+    swm = gpu_lib
+    Wg, mg = wl.pruned_weight(104, M + K, M, K, 0.5)
+    Wu, mu = wl.pruned_weight(104, M + K + 1, M, K, 0.6)
+    X = wl.activations(104, M + N, N, K)
+    fg, fu = swm.sparse_compress(Wg, mg), swm.sparse_compress(Wu, mu)
+    H, _ = _glu_ws(swm, fg, fu, X, tau, extra=256)
+    assert_glu_close(_np(H), oracle.gate_up_silu(Wg, mg, Wu, mu, X, 0.0), tau, f"glu ws {M}x{K} N={N} tau={tau}")
+
+
+def test_gate_up_silu_ws_small_n_is_decode_path(gpu_lib, gate_up_prefill):
+    """Below 33 tokens the call is swm_gate_up_silu (no workspace): bit for bit."""
+    Wg, mg, Wu, mu, X, fg, fu, full = gate_up_prefill
+    for n in (1, 16, 32):
+        assert gpu_lib.gate_up_silu_workspace_bytes(fg, fu, n) == 0
+        H = gpu_lib.gate_up_silu_ws(fg, fu, _t(X[:n]), None, 0.3)
+        ref = gpu_lib.gate_up_silu(fg, fu, _t(X[:n]), 0.3)
+        assert np.array_equal(_np(H).view(np.uint16), _np(ref).view(np.uint16)), n
+
+
+def test_gate_up_silu_ws_degenerate_cases(gpu_lib):
+    """Zero activations give exact +0; the largest tau drops every entry; the
+    same handle as gate and up gives SiLU(g) * g; an all-pruned gate gives
+    SiLU(0) * u = 0."""
+    swm = gpu_lib
+    M, K, N = 520, 392, 96
+    Wg, mg = wl.pruned_weight(105, 0, M, K, 0.5)
+    Wu, mu = wl.pruned_weight(105, 1, M, K, 0.5)
+    fg, fu = swm.sparse_compress(Wg, mg), swm.sparse_compress(Wu, mu)
+    X = wl.activations(105, 0, N, K)
+    Z = np.zeros((N, K), dtype=np.float16)
+    assert np.all(_np(_glu_ws(swm, fg, fu, Z, 0.0)[0]).view(np.uint16) == 0)
+    assert np.all(_np(_glu_ws(swm, fg, fu, X, 65504.0)[0]).view(np.uint16) == 0)
+    H = _np(_glu_ws(swm, fg, fg, X, 0.0)[0])
+    assert_glu_close(H, oracle.gate_up_silu(Wg, mg, Wg, mg, X, 0.0), 0.0, "gate == up")
+    f0 = swm.sparse_compress(Wg, np.zeros_like(mg))
+    assert np.all(_np(_glu_ws(swm, f0, fu, X, 0.0)[0]) == 0)
+
+
+def test_gate_up_silu_ws_graph_replays(gpu_lib):
+    """Both expansions and the gated product captured in one graph: replays
+    with new activations (eager calls in between) equal eager calls bit for bit."""
+    import torch
+    swm = gpu_lib
+    M, K, N, tau = 520, 392, 300, 0.1
+    Wg, mg = wl.pruned_weight(106, 0, M, K, 0.5)
+    Wu, mu = wl.pruned_weight(106, 1, M, K, 0.5)
+    fg, fu = swm.sparse_compress(Wg, mg), swm.sparse_compress(Wu, mu)
+    ws = torch.empty(swm.gate_up_silu_workspace_bytes(fg, fu, N), dtype=torch.uint8, device="cuda")
+    xb = torch.empty((N, K), dtype=torch.float16, device="cuda")
+    hb = torch.empty((N, M), dtype=torch.float16, device="cuda")
+    xb.copy_(_t(wl.activations(106, 0, N, K)))
+    swm.gate_up_silu_ws(fg, fu, xb, ws, tau, hb)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        swm.gate_up_silu_ws(fg, fu, xb, ws, tau, hb)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        X = wl.activations(106, rep + 1, N, K)
+        xb.copy_(_t(X))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        h_graph = hb.cpu().numpy().copy()
+        h_eager = _np(_glu_ws(swm, fg, fu, X, tau)[0])
+        assert np.array_equal(h_graph.view(np.uint16), h_eager.view(np.uint16)), f"replay {rep}"
+        assert_glu_close(h_graph, oracle.gate_up_silu(Wg, mg, Wu, mu, X, 0.0), tau, f"replay {rep}")
+
+
+def test_gate_up_silu_ws_errors(gpu_lib):
+    import ctypes
+    import torch
+    swm = gpu_lib
+    lib = swm.load()
+    M, K, N = 64, 128, 40
+    Wg, mg = wl.pruned_weight(107, 0, M, K, 0.5)
+    fg, fu = swm.sparse_compress(Wg, mg), swm.sparse_compress(Wg, mg)
+    fo = swm.sparse_compress(*wl.pruned_weight(107, 1, M + 16, K, 0.5))
+    need = swm.gate_up_silu_workspace_bytes(fg, fu, N)
+    assert need == 2 * M * K * 2 and swm.gate_up_silu_workspace_bytes(fg, fo, N) == 0
+    X = torch.zeros((N, K + 8), dtype=torch.float16, device="cuda")
+    H = torch.empty((N, M), dtype=torch.float16, device="cuda")
+    ws = torch.empty(need + 256, dtype=torch.uint8, device="cuda")
+    xp, hp, wp = ctypes.c_void_p(X.data_ptr()), ctypes.c_void_p(H.data_ptr()), ctypes.c_void_p(ws.data_ptr())
+    s = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    f = lambda a, b, ldx, n, tau, w=wp, nb=need, x=xp: lib.swm_gate_up_silu_ws(a, b, x, ldx, hp, M, n, tau, w, nb, s)
+    assert f(fg._h, fu._h, K, N, 0.0) == 0
+    assert f(fg._h, fo._h, K, N, 0.0) == 1                # shapes differ
+    assert f(fg._h, None, K, N, 0.0) == 1
+    assert f(fg._h, fu._h, K, 0, 0.0) == 1                # n < 1
+    assert f(fg._h, fu._h, K, N, float("nan")) == 1
+    assert f(fg._h, fu._h, K, N, -1.0) == 1
+    assert f(fg._h, fu._h, K - 8, N, 0.0) == 1            # ldx < K
+    assert f(fg._h, fu._h, K, N, 0.0, nb=need - 1) == 1   # workspace too small
+    assert f(fg._h, fu._h, K, N, 0.0, w=None) == 1        # NULL workspace
+    assert f(fg._h, fu._h, K, N, 0.0, w=ctypes.c_void_p(ws.data_ptr() + 8)) == 3  # misaligned workspace
+    assert f(fg._h, fu._h, K + 4, N, 0.0) == 3            # ldx % 8 != 0: SWM_ERR_ALIGN
+    assert f(fg._h, fu._h, K, N, 0.0, x=ctypes.c_void_p(X.data_ptr() + 2)) == 3  # misaligned X
+    assert f(fg._h, fu._h, K, 4, 0.0, w=None, nb=0) == 0  # decode path: no workspace needed
+    torch.cuda.synchronize()
+
+
 # ------------------------------------------------------------------ wider workloads
 @pytest.mark.parametrize("s", [0.6, 0.7])
 @pytest.mark.parametrize("N", [1, 16])
