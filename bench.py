@@ -623,6 +623,7 @@ def bench_mlp(args, torch, swm, wl, G):
             "speedup_vs_unfused": t["unfused_chain"] / best, "speedup_vs_dense": t["dense_chain"] / best}
         _log(f"n={n}: fused {t['fused_chain']:.2f} / {t['fused_full_chain']:.2f} us (skipping / full down), "
              f"unfused {t['unfused_chain']:.2f} us, dense {t['dense_chain']:.2f} us")
+    out["prefill"] = mlp_prefill(args, torch, swm, wl, G)
     out["value"] = out["detail"]["1"]["best_fused_chain_us"]
     d1 = out["detail"]["1"]
     out["roofline"] = {"bound": "hbm", "achieved": d1["fused_glu_GBps_alg"], "peak": 8000.0, "unit": "GB/s",
@@ -630,6 +631,83 @@ def bench_mlp(args, torch, swm, wl, G):
                        "kernel": "decode_seq_kernel (gated), gate+up, n=1",
                        "alg_bytes_per_launch": fbg + fbu + 2 * K + 2 * M, "avg_launch_us": d1["fused_glu_us"]}
     return out
+
+
+def mlp_prefill(args, torch, swm, wl, G, Ns=(512, 2048, 4096)):
+    """The same FFN block at prefill token counts: gate and up through
+    swm_gate_up_silu_ws (both expanded as interleaved rows, one dense MFMA
+    product with the gated epilogue), then the down projection through
+    swm_spmm_ws; against the dense baseline with the same gated epilogue
+    (swm_dense_gate_up_silu on the interleaved masked weights, then
+    swm_dense_gemm), and against both unfused (two products, SiLU * mul and
+    the threshold as torch element-wise ops).  One call per graph replay,
+    median of 10."""
+    F = torch.nn.functional
+    tau = args.tau
+    nmax = max(Ns)
+    _log(f"FFN block at prefill sizes (N = {', '.join(map(str, Ns))})")
+    Wg, mg, X = wl.layer_linear(4, nmax)
+    Wu, mu, _ = wl.layer_linear(5, nmax)
+    Wd, md, _ = wl.layer_linear(6, 1)
+    fg, fu, fd = swm.sparse_compress(Wg, mg), swm.sparse_compress(Wu, mu), swm.sparse_compress(Wd, md)
+    dg, du, dd = (torch.from_numpy(w).cuda() for w in (Wg, Wu, Wd))
+    M, K = Wg.shape
+    W2 = np.empty((2 * M, K), dtype=np.float16)
+    W2[0::2], W2[1::2] = Wg, Wu  # gate row m at 2m, up row m at 2m + 1
+    d2 = torch.from_numpy(W2).cuda()
+    del W2
+    nnz = int(mg.sum()) + int(mu.sum())
+    Xd = torch.from_numpy(X).cuda()
+    wsb = max(swm.gate_up_silu_workspace_bytes(fg, fu, nmax), swm.spmm_workspace_bytes(fd, nmax), 256)
+    ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
+    res = {"workload": "Llama-2-7B FFN block, gate/up 11008x4096 + down 4096x11008, 50%, prefill", "tau": tau}
+    for n in Ns:
+        x = Xd[:n]
+        H = torch.empty((n, M), dtype=torch.float16, device="cuda")
+        g = torch.empty((n, M), dtype=torch.float16, device="cuda")
+        u = torch.empty((n, M), dtype=torch.float16, device="cuda")
+        y = torch.empty((n, K), dtype=torch.float16, device="cuda")
+
+        def epilogue():
+            h = (F.silu(g.float()) * u.float()).half()
+            return torch.where(h.abs() >= tau, h, torch.zeros_like(h))
+
+        fns = {
+            "fused_glu": lambda: swm.gate_up_silu_ws(fg, fu, x, ws, tau, H),
+            "two_spmm_ws_eltwise": lambda: (swm.spmm_ws(fg, x, ws, g), swm.spmm_ws(fu, x, ws, u), epilogue()),
+            "dense_fused_glu": lambda: swm.dense_gate_up_silu(d2, x, tau, H),
+            "dense_two_eltwise": lambda: (swm.dense_gemm(dg, x, g), swm.dense_gemm(du, x, u), epilogue()),
+            "fused_chain": lambda: (swm.gate_up_silu_ws(fg, fu, x, ws, tau, H), swm.spmm_ws(fd, H, ws, y)),
+            "unfused_chain": lambda: (swm.spmm_ws(fg, x, ws, g), swm.spmm_ws(fu, x, ws, u),
+                                      swm.spmm_ws(fd, epilogue(), ws, y)),
+            "dense_fused_chain": lambda: (swm.dense_gate_up_silu(d2, x, tau, H), swm.dense_gemm(dd, H, y)),
+            "dense_chain": lambda: (swm.dense_gemm(dg, x, g), swm.dense_gemm(du, x, u),
+                                    swm.dense_gemm(dd, epilogue(), y)),
+        }
+        for fn in fns.values():
+            fn()
+        torch.cuda.synchronize()
+        d = {}
+        for name, fn in fns.items():
+            gr = G.capture([fn])
+            G.time(gr, 3)
+            d[name] = pct(G.samples(gr, 10, 1))
+        t = {k: v["median_us"] for k, v in d.items()}
+        res[str(n)] = {**{k + "_us": v for k, v in t.items()},
+                       "glu_useful_TFLOPs": 2.0 * nnz * n / (t["fused_glu"] * 1e-6) / 1e12,
+                       "glu_speedup_vs_unfused": t["two_spmm_ws_eltwise"] / t["fused_glu"],
+                       "glu_speedup_vs_dense_fused": t["dense_fused_glu"] / t["fused_glu"],
+                       "chain_speedup_vs_unfused": t["unfused_chain"] / t["fused_chain"],
+                       "chain_speedup_vs_dense_fused": t["dense_fused_chain"] / t["fused_chain"]}
+        _log(f"prefill n={n}: gate/up fused {t['fused_glu']:.1f} us (dense fused {t['dense_fused_glu']:.1f}), "
+             f"two spmm_ws + eltwise {t['two_spmm_ws_eltwise']:.1f}, two dense + eltwise "
+             f"{t['dense_two_eltwise']:.1f}; chain fused {t['fused_chain']:.1f} (dense fused "
+             f"{t['dense_fused_chain']:.1f}) / unfused {t['unfused_chain']:.1f} / dense unfused "
+             f"{t['dense_chain']:.1f} us")
+        del H, g, u, y
+    del ws, d2
+    torch.cuda.empty_cache()
+    return res
 
 
 # ------------------------------------------------------------------ prefill

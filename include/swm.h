@@ -304,6 +304,26 @@ swm_status swm_gate_up_silu_ws(const swm_format* g, const swm_format* u, const v
                                int64_t ldh, int64_t n, float tau, void* workspace, size_t ws_bytes,
                                void* stream);
 
+/* dense_gate_up_silu: the dense counterpart of swm_gate_up_silu_ws, the
+ * in-house dense baseline of the gated FFN step (the full-matmul fallback
+ * the "Reduced Matrix Multiplication" blog page keeps beside its reduced
+ * product): H = SiLU(X Wg^T) (.) (X Wu^T) with |H| < tau (after rounding to
+ * fp16) stored as +0, by the dense MFMA kernel with the gated epilogue for
+ * every N.  Given the masked weights (W (.) mask, pruned entries +0) it
+ * returns the same bits as swm_gate_up_silu_ws from 33 tokens.
+ *  W2: DEVICE fp16, 2M x K row-major (ldw >= K), the gate and up weights
+ *  interleaved by row: row 2m is gate row m, row 2m + 1 is up row m.
+ *  X: DEVICE fp16 token-major N x K (ldx >= K).  H: DEVICE fp16 N x M
+ *  (ldh >= M), overwritten.  tau: 0 <= tau <= 65504.
+ *  SWM_ERR_INVALID_ARG: NULL pointers, M < 0, K < 0, N <= 0, leading
+ *  dimensions too small, tau outside its range or NaN.  SWM_ERR_ALIGN: W2 or
+ *  X not 16-byte aligned, ldw % 8 != 0 or ldx % 8 != 0.  SWM_ERR_UNSUPPORTED:
+ *  K < 8 or K % 8 != 0, or 2M rows of W2 or the activations beyond the
+ *  kernel's 32-bit byte offsets.  M == 0 returns SWM_OK.  Asynchronous on
+ *  stream. */
+swm_status swm_dense_gate_up_silu(const void* W2, int64_t ldw, const void* X, int64_t ldx, void* H, int64_t ldh,
+                                  int64_t M, int64_t K, int64_t N, float tau, void* stream);
+
 /* spmspv: as swm_spmm for 1 <= n <= 16 tokens, for activations with zero
  * input channels (x[t][k] == +0 or -0 for all tokens t).  Such channels
  * contribute exact zeros, so the result equals swm_spmm's up to fp32

@@ -68,6 +68,7 @@ SIGNATURES = {
     "swm_gate_up_silu": (_i32, [_vp, _vp, _vp, _i64, _vp, _i64, _i32, ctypes.c_float, _vp]),
     "swm_gate_up_silu_workspace_bytes": (_sz, [_vp, _vp, _i64]),
     "swm_gate_up_silu_ws": (_i32, [_vp, _vp, _vp, _i64, _vp, _i64, _i64, ctypes.c_float, _vp, _sz, _vp]),
+    "swm_dense_gate_up_silu": (_i32, [_vp, _i64, _vp, _i64, _vp, _i64, _i64, _i64, _i64, ctypes.c_float, _vp]),
     "swm_format_enable_skipping": (_i32, [_vp, _vp, ctypes.POINTER(_u64)]),
     "swm_format_enable_smfmac": (_i32, [_vp, _vp, ctypes.POINTER(_u64)]),
     "swm_colruns_encode_blob": (_i32, [_vp, _sz, _vp, _sz, ctypes.POINTER(_sz)]),
@@ -366,6 +367,24 @@ def gate_up_silu_ws(gate: Format, up: Format, X, workspace, tau: float = 0.0, H=
         wp, wb = ctypes.c_void_p(workspace.data_ptr()), workspace.numel() * workspace.element_size()
     _check(lib.swm_gate_up_silu_ws(gate._h, up._h, xp, ldx, hp, ldh, n, float(tau), wp, wb, _stream_ptr(stream)),
            "swm_gate_up_silu_ws")
+    return H
+
+
+def dense_gate_up_silu(W2, X, tau: float = 0.0, H=None, stream=None):
+    """Dense gated FFN step: W2 (2M, K) holds the gate and up weights
+    interleaved by row (2m: gate row m, 2m+1: up row m); H (N, M) =
+    SiLU(X @ Wg.T) * (X @ Wu.T), |H| < tau stored as +0."""
+    lib = load()
+    N = X.shape[0]
+    if W2.shape[0] % 2:
+        raise ValueError("W2 must hold an even number of rows (gate / up interleaved)")
+    M, K = W2.shape[0] // 2, W2.shape[1]
+    wp, ldw = _dev2d(W2, "W2", cols=K)
+    xp, ldx = _dev2d(X, "X", cols=K)
+    H = _out(H, N, M, X)
+    hp, ldh = _dev2d(H, "H", rows=N, cols=M)
+    _check(lib.swm_dense_gate_up_silu(wp, ldw, xp, ldx, hp, ldh, M, K, N, float(tau), _stream_ptr(stream)),
+           "swm_dense_gate_up_silu")
     return H
 
 

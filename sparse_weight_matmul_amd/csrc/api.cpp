@@ -704,6 +704,29 @@ swm_status swm_gate_up_silu_ws(const swm_format* g, const swm_format* u, const v
   return SWM_OK;
 }
 
+swm_status swm_dense_gate_up_silu(const void* W2, int64_t ldw, const void* X, int64_t ldx, void* H, int64_t ldh,
+                                  int64_t M, int64_t K, int64_t N, float tau, void* stream) {
+  if (!W2 || !X || !H) return SWM_ERR_INVALID_ARG;
+  if (M < 0 || K < 0 || N <= 0 || ldw < K || ldx < K || ldh < M || ldw <= 0 || ldx <= 0 || ldh <= 0)
+    return SWM_ERR_INVALID_ARG;
+  if (!(tau >= 0.f) || !(tau <= 65504.f)) return SWM_ERR_INVALID_ARG;
+  if (M == 0) return SWM_OK;
+  if (K < 8 || K % 8 != 0) return SWM_ERR_UNSUPPORTED;
+  if (ldx % 8 != 0 || ldw % 8 != 0 || (reinterpret_cast<uintptr_t>(X) & 15) != 0 ||
+      (reinterpret_cast<uintptr_t>(W2) & 15) != 0)
+    return SWM_ERR_ALIGN;
+  if (2 * M > (int64_t(1) << 31) - 64 || !swm::prefill_dense_dma_fits(2 * M, ldw, K, N, ldx))
+    return SWM_ERR_UNSUPPORTED;
+  int dev = 0;
+  SWM_HIP(hipGetDevice(&dev));
+  swm_log("dense_gate_up_silu M=%lld K=%lld N=%lld: dense MFMA with the gated epilogue", (long long)M,
+          (long long)K, (long long)N);
+  SWM_HIP(swm::launch_prefill_dense_glu(static_cast<const uint16_t*>(W2), ldw, static_cast<const uint16_t*>(X), ldx,
+                                        static_cast<uint16_t*>(H), ldh, 2 * M, K, N, tau, num_cus(dev),
+                                        static_cast<hipStream_t>(stream)));
+  return SWM_OK;
+}
+
 swm_status swm_hbm_stream(const void* buf, size_t bytes, int32_t unroll, int32_t blocks,
                           uint32_t* out, void* stream) {
   if (!buf || !out || bytes % 16 || blocks <= 0) return SWM_ERR_INVALID_ARG;

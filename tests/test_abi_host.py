@@ -177,6 +177,7 @@ def test_null_handle_calls_are_rejected():
     assert lib.swm_gate_up_silu(None, None, None, 1, None, 1, 1, 0.0, None) == 1
     assert lib.swm_gate_up_silu_ws(None, None, None, 1, None, 1, 4096, 0.0, None, 0, None) == 1
     assert lib.swm_gate_up_silu_workspace_bytes(None, None, 4096) == 0
+    assert lib.swm_dense_gate_up_silu(None, 8, None, 8, None, 8, 8, 8, 64, 0.0, None) == 1
     assert lib.swm_format_destroy(None) == 0
     assert lib.swm_format_validate_blob(None, 0) == 1
 

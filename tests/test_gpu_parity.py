@@ -1210,6 +1210,59 @@ def test_gate_up_silu_ws_errors(gpu_lib):
     torch.cuda.synchronize()
 
 
+def _interleave(Wg, Wu):
+    """2M x K: gate row m at 2m, up row m at 2m + 1."""
+    W2 = np.empty((2 * Wg.shape[0], Wg.shape[1]), dtype=np.float16)
+    W2[0::2], W2[1::2] = Wg, Wu
+    return W2
+
+
+def test_dense_gate_up_silu_equals_sparse_route_bitwise(gpu_lib, gate_up_prefill):
+    """The dense gated product on W (.) mask returns the bits of the sparse
+    prefill route (the expansion reproduces W (.) mask exactly, and both run
+    one kernel), and both match the oracle."""
+    Wg, mg, Wu, mu, X, fg, fu, full = gate_up_prefill
+    W2 = _t(_interleave(Wg, Wu))  # the workload's W has +0 at every pruned entry
+    for n, tau in ((640, 0.3), (100, 0.0)):
+        Hd = _np(gpu_lib.dense_gate_up_silu(W2, _t(X[:n]), tau))
+        Hs = _np(_glu_ws(gpu_lib, fg, fu, X[:n], tau)[0])
+        assert np.array_equal(Hd.view(np.uint16), Hs.view(np.uint16)), n
+        assert_glu_close(Hd, full[:n], tau, f"dense gate/up n={n}")
+
+
+@pytest.mark.parametrize("M,K,N,tau", [(520, 392, 5, 0.1), (17, 136, 40, 0.0), (1000, 1032, 300, 0.2)])
+def test_dense_gate_up_silu_ragged(gpu_lib, M, K, N, tau):
+    swm = gpu_lib
+    Wg, mg = wl.pruned_weight(108, M + K, M, K, 0.5)
+    Wu, mu = wl.pruned_weight(108, M + K + 1, M, K, 0.6)
+    X = wl.activations(108, M + N, N, K)
+    H = _np(swm.dense_gate_up_silu(_t(_interleave(Wg, Wu)), _t(X), tau))
+    assert_glu_close(H, oracle.gate_up_silu(Wg, mg, Wu, mu, X, 0.0), tau, f"dense glu {M}x{K} N={N} tau={tau}")
+
+
+def test_dense_gate_up_silu_errors(gpu_lib):
+    import ctypes
+    import torch
+    lib = gpu_lib.load()
+    M, K, N = 64, 128, 40
+    W2 = torch.zeros((2 * M, K + 8), dtype=torch.float16, device="cuda")
+    X = torch.zeros((N, K + 8), dtype=torch.float16, device="cuda")
+    H = torch.empty((N, M), dtype=torch.float16, device="cuda")
+    wp, xp, hp = (ctypes.c_void_p(t.data_ptr()) for t in (W2, X, H))
+    s = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    f = lambda ldw, ldx, m, k, n, tau, w=wp, x=xp: lib.swm_dense_gate_up_silu(w, ldw, x, ldx, hp, M, m, k, n, tau, s)
+    assert f(K, K, M, K, N, 0.0) == 0
+    assert f(K, K, M, K, 0, 0.0) == 1                     # N <= 0
+    assert f(K - 8, K, M, K, N, 0.0) == 1                 # ldw < K
+    assert f(K, K, M, K, N, float("nan")) == 1
+    assert f(K + 4, K, M, K, N, 0.0) == 3                 # ldw % 8 != 0
+    assert f(K, K, M, K, N, 0.0, w=ctypes.c_void_p(W2.data_ptr() + 2)) == 3
+    assert f(K, K, M, K, N, 0.0, x=ctypes.c_void_p(X.data_ptr() + 2)) == 3
+    assert f(K, K, M, 12, N, 0.0) == 8                    # K % 8 != 0
+    assert f(K, K, 0, K, N, 0.0) == 0                     # M == 0: nothing to do
+    torch.cuda.synchronize()
+
+
 # ------------------------------------------------------------------ wider workloads
 @pytest.mark.parametrize("s", [0.6, 0.7])
 @pytest.mark.parametrize("N", [1, 16])
