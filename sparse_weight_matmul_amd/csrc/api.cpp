@@ -677,6 +677,7 @@ swm_status swm_gate_up_silu_ws(const swm_format* g, const swm_format* u, const v
   if (n < kGluExpandMinN) return swm_gate_up_silu(g, u, X, ldx, H, ldh, int32_t(n), tau, stream);
   if (g->h.m != u->h.m || g->h.k != u->h.k) return SWM_ERR_INVALID_ARG;
   if (ldx < g->h.k || ldh < g->h.m || ldx <= 0 || ldh <= 0) return SWM_ERR_INVALID_ARG;
+  if (g->h.m == 0) return SWM_OK;  // nothing to compute, no workspace needed
   if (!workspace || ws_bytes < swm_gate_up_silu_workspace_bytes(g, u, n)) return SWM_ERR_INVALID_ARG;
   if (reinterpret_cast<uintptr_t>(workspace) & 15) return SWM_ERR_ALIGN;
   swm_status st = check_tile_supported(g->h);
@@ -686,7 +687,6 @@ swm_status swm_gate_up_silu_ws(const swm_format* g, const swm_format* u, const v
   if (g->h.k < 8 || g->h.k % 8 != 0) return SWM_ERR_UNSUPPORTED;
   if (ldx % 8 != 0 || (reinterpret_cast<uintptr_t>(X) & 15) != 0) return SWM_ERR_ALIGN;
   const int64_t M = int64_t(g->h.m), K = int64_t(g->h.k);
-  if (M == 0) return SWM_OK;
   if (2 * M > (int64_t(1) << 31) - 64 || !swm::prefill_dense_dma_fits(2 * M, K, K, n, ldx))
     return SWM_ERR_UNSUPPORTED;
   hipStream_t s = static_cast<hipStream_t>(stream);
