@@ -1103,6 +1103,19 @@ def test_gate_up_silu_ws_llama_shape(gpu_lib, gate_up_prefill, N, tau):
     assert_glu_close(_np(H), full[:N], tau, f"gate/up prefill N={N} tau={tau}")
 
 
+def test_gate_up_silu_ws_full_size(gpu_lib):
+    """gate/up 11008x4096 at 50% and N = 4096, the size the FFN bench times:
+    every output against the oracle (tau = 0.3), and the dense gated step on
+    W (.) mask returns the same bits."""
+    Wg, mg, X = wl.layer_linear(4, 4096)
+    Wu, mu, _ = wl.layer_linear(5, 4096)
+    fg, fu = gpu_lib.sparse_compress(Wg, mg), gpu_lib.sparse_compress(Wu, mu)
+    H = _np(_glu_ws(gpu_lib, fg, fu, X, 0.3)[0])
+    Hd = _np(gpu_lib.dense_gate_up_silu(_t(_interleave(Wg, Wu)), _t(X), 0.3))
+    assert np.array_equal(H.view(np.uint16), Hd.view(np.uint16))
+    assert_glu_close(H, oracle.gate_up_silu(Wg, mg, Wu, mu, X, 0.0), 0.3, "gate/up prefill N=4096")
+
+
 @pytest.mark.parametrize("M,K,N,tau", [(1000, 1032, 33, 0.1), (520, 392, 300, 0.0), (300, 8192, 100, 0.2),
                                        (17, 136, 257, 0.05), (4096, 4096, 1100, 0.3), (131, 520, 70, 0.0)])
 def test_gate_up_silu_ws_ragged(gpu_lib, M, K, N, tau):
