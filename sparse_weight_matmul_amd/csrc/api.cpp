@@ -186,7 +186,7 @@ const char* swm_status_str(swm_status s) {
 
 int32_t swm_last_hip_error(void) { return g_last_hip.load(); }
 
-int32_t swm_version(void) { return 100; }
+int32_t swm_version(void) { return 200; }  // 0.2.0: the gated steps at prefill sizes
 
 swm_status swm_encode_blob(const uint16_t* W, int64_t ldw, const uint8_t* mask, int64_t ldm,
                            int64_t M, int64_t K, const swm_tile_cfg* cfg, void* buf, size_t cap,
