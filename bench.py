@@ -144,6 +144,28 @@ class Graphs:
         ev[-1].synchronize()
         return [ev[r].elapsed_time(ev[r + 1]) / per for r in range(reps)]
 
+    def interleaved(self, graphs, reps, pers, warm=3):
+        """ms per launch of `reps` replays of each graph (`pers[i]` launches in
+        graph i), sampled in turn: one replay of every graph per round, after
+        `warm` untimed rounds, so that all of them run in the same clock and
+        power state (a route timed alone right after host-side work runs on a
+        cooler, slower chip)."""
+        torch = self.torch
+        s = torch.cuda.current_stream()
+        for _ in range(warm):
+            for g in graphs:
+                g.replay()
+        torch.cuda.synchronize()
+        ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+              for _ in graphs]
+        for r in range(reps):
+            for i, g in enumerate(graphs):
+                ev[i][r][0].record(s)
+                g.replay()
+                ev[i][r][1].record(s)
+        torch.cuda.synchronize()
+        return [[ev[i][r][0].elapsed_time(ev[i][r][1]) / pers[i] for r in range(reps)] for i in range(len(graphs))]
+
 
 def rotating_formats(swm, W, mask, min_bytes=ROTATE_BYTES):
     """Copies of the compressed W whose resident bytes add up to >= min_bytes;
@@ -342,16 +364,13 @@ def prefill_block(args, torch, swm, wl, G):
     torch.cuda.synchronize()
     reps = 4
 
-    def timed(fn):
-        # a few untimed replays first: the block follows host-side work (the
-        # oracle's timing), during which the GPU's clocks drop
-        g = G.capture([fn] * reps)
-        G.time(g, 3)
-        return pct(G.samples(g, 10, reps))
-    d_ws = timed(lambda: swm.spmm_ws(f, Xd, ws, y))
-    d_on = timed(lambda: swm.spmm(f, Xd, y))
-    d_de = timed(lambda: swm.dense_gemm(Wd, Xd, y))
-    d_dc = timed(lambda: swm.decompress(f, ws.view(torch.float16)[:M * K].view(M, K)))
+    # The block follows host-side work (the oracle's timing), during which
+    # the GPU's clocks drop: the routes are sampled in turn after common
+    # warm-up rounds, so that none of them is timed on a cooler chip.
+    gr = [G.capture([fn] * reps) for fn in (lambda: swm.spmm_ws(f, Xd, ws, y), lambda: swm.spmm(f, Xd, y),
+                                            lambda: swm.dense_gemm(Wd, Xd, y),
+                                            lambda: swm.decompress(f, ws.view(torch.float16)[:M * K].view(M, K)))]
+    d_ws, d_on, d_de, d_dc = (pct(t) for t in G.interleaved(gr, 10, [reps] * 4, warm=5))
     useful, executed = 2.0 * nnz * n, 2.0 * M * K * n
     t_ws, t_on, t_de = d_ws["median_us"] * 1e-6, d_on["median_us"] * 1e-6, d_de["median_us"] * 1e-6
     blk = {
@@ -425,7 +444,8 @@ def layer_pass(args, torch, swm, G, parts, CS, CD, smfmac=False):
         gs = G.capture([sp(c, i) for c in range(CS) for i in range(L)])
         gd = G.capture([de(c, i) for c in range(CD) for i in range(L)])
         reps = 10 if n == 16 else 3
-        ds, dd = pct(G.samples(gs, reps, CS)), pct(G.samples(gd, reps, CD))
+        ts, td = G.interleaved([gs, gd], reps, [CS, CD], warm=3 if n == 16 else 1)
+        ds, dd = pct(ts), pct(td)
         alg = fa + sum(2 * (shp[0] + shp[1]) * n for shp in shapes)
         e = {"sparse_layer": ds, "dense_layer": dd, "speedup_vs_dense": dd["median_us"] / ds["median_us"],
              "route": "decode kernels" if n <= 32 else
@@ -687,11 +707,8 @@ def mlp_prefill(args, torch, swm, wl, G, Ns=(512, 2048, 4096)):
         for fn in fns.values():
             fn()
         torch.cuda.synchronize()
-        d = {}
-        for name, fn in fns.items():
-            gr = G.capture([fn])
-            G.time(gr, 3)
-            d[name] = pct(G.samples(gr, 10, 1))
+        graphs = [G.capture([fn]) for fn in fns.values()]
+        d = {name: pct(t) for name, t in zip(fns, G.interleaved(graphs, 10, [1] * len(graphs)))}
         t = {k: v["median_us"] for k, v in d.items()}
         res[str(n)] = {**{k + "_us": v for k, v in t.items()},
                        "glu_useful_TFLOPs": 2.0 * nnz * n / (t["fused_glu"] * 1e-6) / 1e12,
