@@ -106,6 +106,11 @@ __device__ __forceinline__ _Float16 lds_half(uint32_t addr) {
   return *reinterpret_cast<const lds_f16*>(static_cast<uintptr_t>(addr));
 }
 
+// Global -> LDS without registers: lane l writes 16 bytes at lds + 16 l.
+__device__ __forceinline__ void lds_dma16(const void* src, uint8_t* lds) {
+  __builtin_amdgcn_global_load_lds(src, lds, 16, 0, 0);
+}
+
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p));
 }
@@ -418,9 +423,12 @@ __global__ __launch_bounds__(1024) void decode_kernel(DecodeArgs a) {
 //     (scalar), then the bitmap words of the range are touched into L2 so
 //     that the per-step scalar loads hit there;
 //   * per segment of two tiles, the activations of its 128 columns for the N
-//     tokens are loaded first (kXI loads of 1 KiB: 256 contiguous bytes per
-//     token, whole cache lines), then its value chunks; using the
-//     activations never waits for value bytes;
+//     tokens are loaded first, straight into the wave's LDS
+//     (global_load_lds_dwordx4: kXI loads of 1 KiB, four token rows of 256
+//     contiguous bytes each, whole cache lines; no registers and no LDS
+//     stores), then its value chunks; using the activations never waits for
+//     value bytes (measured 1.7% / 3.3% faster at N = 16 on q_proj / down
+//     than loading them into registers and storing them to LDS);
 //   * one segment is requested ahead: segment g+1 is issued when segment g
 //     has been decoded.  With every wave's whole range in flight at once, the
 //     memory system served the waves of a SIMD in launch order and the last
@@ -428,16 +436,19 @@ __global__ __launch_bounds__(1024) void decode_kernel(DecodeArgs a) {
 //     ahead interleaves the waves' requests, so each wave has at most one
 //     segment left when the last bytes arrive (measured 5-9% faster on the
 //     q_proj, down and up shapes);
-//   * at a segment's start its activations go to the wave's LDS (B operands
-//     are then read with ds_read_b128); its chunks are copied tile by tile,
-//     each as soon as the chunks that hold it have arrived, so decoding
-//     overlaps the rest of the stream;
+//   * at a segment's start its value chunks go to the wave's LDS, and the B
+//     operands are read with ds_read_b128 from the staged rows (chunk k of
+//     row t at position k ^ t, so the 16 rows of one read meet no bank
+//     twice);
 //   * kDB (16 token rows only): the activations are loaded straight in the B
 //     operand layout instead, one 1 KiB load per 32-column step (lane l:
 //     token l%16, columns 8(l/16) .. +7), and used from registers; the wave
 //     needs no LDS for them, so more workgroups fit a CU, at the price of
 //     loads that touch 16 token rows each.
-constexpr int kXRow = 272;  // LDS bytes per token row of a segment's activations (256 + pad)
+// LDS bytes reserved per staged token row (the rows are 256 bytes; the
+// reserve, from an earlier padded layout, keeps the work splits below as
+// measured).
+constexpr int kXRow = 272;
 // LDS bytes per wave for a segment's staged activations (kxi 1 KiB loads;
 // none when the B operands are loaded straight into registers).
 constexpr int seq_x_bytes(int kxi, bool direct) { return direct ? 0 : 4 * kxi * kXRow; }
@@ -457,7 +468,7 @@ __global__ __launch_bounds__(1024) void decode_seq_kernel(typename SeqArgs<kGlu>
   const int slab = int(blockIdx.x);
 
   // LDS: [0,16) unused | per wave: kC KiB of value chunks, then (unless kDB)
-  // the segment's activations [kXRows][kXRow]; the reduction area reuses it
+  // the segment's activations [kXRows][256 bytes, swizzled]; the reduction area reuses it
   // after a barrier.  No barrier at the start: each wave issues its first
   // loads as soon as it runs (lanes whose bit is clear read a neighbouring
   // value, not a zero slot; 1-2% faster than zeroing a slot and waiting for
@@ -513,25 +524,33 @@ __global__ __launch_bounds__(1024) void decode_seq_kernel(typename SeqArgs<kGlu>
     // load i is step i's B operand (token lane%16, rows past N repeating
     // token N-1, columns 32 i + 8 (lane/16) .. +7).  Byte offsets fit 32 bits
     // (16 tokens of at most 2^27 halves).
-    uint32_t xrow_off[kXI], xcol[kXI], xl[kXI];
+    uint32_t xrow_off[kXI], xcol[kXI];
 #pragma unroll
     for (int i = 0; i < kXI; ++i) {
       const int pce = i * 64 + lane;
       if constexpr (kDB) {
         xrow_off[i] = 2u * uint32_t(min(lane & 15, a.N - 1)) * uint32_t(a.ldx);
         xcol[i] = 32u * uint32_t(i) + 8u * uint32_t(lane >> 4);
-        xl[i] = 0;
       } else {
+        // LDS-direct staging: load i fills rows 4i .. 4i+3 of 256 bytes
+        // (lane l at row 4i + l/16, position l%16; rows past N repeat token
+        // N-1); the lane fetches chunk (l%16) ^ row, so chunk k of row t sits
+        // at position k ^ t and the B reads of one instruction (16 rows, one
+        // chunk) meet no LDS bank twice
         xrow_off[i] = 2u * uint32_t(min(pce >> 4, a.N - 1)) * uint32_t(a.ldx);
-        xcol[i] = 8u * uint32_t(pce & 15);
-        xl[i] = xbuf + uint32_t(pce >> 4) * kXRow + 16u * uint32_t(pce & 15);
+        xcol[i] = 8u * uint32_t((pce & 15) ^ ((pce >> 4) & 15));
       }
     }
     // B operand: lane l carries token l%16 (rows past kXRows repeat a valid
-    // row; their accumulator columns are never stored), columns 8(l/16) .. +7.
-    const uint32_t xb = xbuf + uint32_t(min(lane & 15, kXRows - 1)) * kXRow + 16u * uint32_t(lane >> 4);
+    // row; their accumulator columns are never stored), columns 8(l/16) .. +7
+    // of the step: chunk 4q + l/16 of the segment for step q = 2 tt + s
+    const uint32_t xrow = uint32_t(min(lane & 15, kXRows - 1));
+    uint32_t xsw[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      xsw[q] = xbuf + xrow * 256u + 16u * ((uint32_t(4 * q) + uint32_t(lane >> 4)) ^ xrow);
 
-    u32x4 xr[NS][kXI];
+    u32x4 xr[NS][kDB ? kXI : 1];  // B operands in registers (kDB only)
     u32x4 r[NS][kC];
     // Segment g: its activations, then its value chunks.  For g = 0 the first
     // step's bitmap is folded into the first tile pointer with a mask that is
@@ -540,11 +559,25 @@ __global__ __launch_bounds__(1024) void decode_seq_kernel(typename SeqArgs<kGlu>
     // branches and be waited for there.
     auto issue_seg = [&](int g) {
       const int c0 = (j0 + 2 * g) * kTK;
+      if constexpr (!kDB) {
+        // the previous segment's B reads must have returned before its rows
+        // are overwritten
+        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt and expcnt not waited for
+        __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int i = 0; i < kXI; ++i) {
-        const uint32_t col = uint32_t(min(c0 + int(xcol[i]), kmax8));
-        xr[g][i] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint8_t*>(a.X) + xrow_off[i] +
-                                                   2u * col);
+        for (int i = 0; i < kXI; ++i) {
+          const uint32_t col = uint32_t(min(c0 + int(xcol[i]), kmax8));
+          const uint32_t off = xrow_off[i] + 2u * col;  // one 32-bit offset from the uniform base
+          lds_dma16(reinterpret_cast<const uint8_t*>(a.X) + off, smem + (xbuf - lds_addr(smem)) + i * 1024);
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < kXI; ++i) {
+          const uint32_t col = uint32_t(min(c0 + int(xcol[i]), kmax8));
+          xr[g][i] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint8_t*>(a.X) + xrow_off[i] +
+                                                     2u * col);
+        }
       }
       __builtin_amdgcn_sched_barrier(0);
       if (g == 0) tp[0] += wv[0][0] & uint32_t(a.N >> 31);
@@ -566,14 +599,15 @@ __global__ __launch_bounds__(1024) void decode_seq_kernel(typename SeqArgs<kGlu>
       if (2 * g < nt) {
         // The segment's activations and all its value chunks (chunks past the
         // segment hold clamped duplicates and are never read).
-        if constexpr (!kDB) {
-#pragma unroll
-          for (int i = 0; i < kXI; ++i)
-            *reinterpret_cast<lds_u32x4*>(static_cast<uintptr_t>(xl[i])) = xr[g][i];
-        }
 #pragma unroll
         for (int c = 0; c < kC; ++c)
           *reinterpret_cast<lds_u32x4*>(static_cast<uintptr_t>(buf + c * 1024 + lane * 16)) = r[g][c];
+        if constexpr (!kDB) {
+          // the segment's LDS-direct activation rows have landed (they were
+          // requested before its value chunks, and loads return in order)
+          __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+          __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+        }
       }
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt) {
@@ -600,8 +634,8 @@ __global__ __launch_bounds__(1024) void decode_seq_kernel(typename SeqArgs<kGlu>
             if constexpr (kDB)
               bop = __builtin_bit_cast(half8, xr[g][2 * tt + s]);
             else
-              bop = __builtin_bit_cast(
-                  half8, *reinterpret_cast<const lds_u32x4*>(static_cast<uintptr_t>(xb + tt * 128 + s * 64)));
+              bop = __builtin_bit_cast(half8,
+                                       *reinterpret_cast<const lds_u32x4*>(static_cast<uintptr_t>(xsw[2 * tt + s])));
             const half8 aop = decode_step(w, base);
             acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(aop, bop, acc, 0, 0, 0);
           }
@@ -611,6 +645,9 @@ __global__ __launch_bounds__(1024) void decode_seq_kernel(typename SeqArgs<kGlu>
     }
   }
   if (keep == 0x9E3779B9u && a.N < 0) a.Y[0] = 0;  // never true: keeps the L2 touch loads
+  // LDS-direct rows requested for segments past a short range are never
+  // read; they must have landed before the area is reused
+  if constexpr (!kDB) __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
 
   __syncthreads();  // all wave buffers are free: reuse them as the reduction area
   if constexpr (kGlu)
