@@ -110,6 +110,10 @@ __device__ __forceinline__ _Float16 lds_half(uint32_t addr) {
 __device__ __forceinline__ void lds_dma16(const void* src, uint8_t* lds) {
   __builtin_amdgcn_global_load_lds(src, lds, 16, 0, 0);
 }
+// The same with the non-temporal hint (streamed once, not kept in L2).
+__device__ __forceinline__ void lds_dma16_nt(const void* src, uint8_t* lds) {
+  __builtin_amdgcn_global_load_lds(src, lds, 16, 0, 2);
+}
 
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p));
@@ -423,12 +427,14 @@ __global__ __launch_bounds__(1024) void decode_kernel(DecodeArgs a) {
 //     (scalar), then the bitmap words of the range are touched into L2 so
 //     that the per-step scalar loads hit there;
 //   * per segment of two tiles, the activations of its 128 columns for the N
-//     tokens are loaded first, straight into the wave's LDS
-//     (global_load_lds_dwordx4: kXI loads of 1 KiB, four token rows of 256
-//     contiguous bytes each, whole cache lines; no registers and no LDS
-//     stores), then its value chunks; using the activations never waits for
-//     value bytes (measured 1.7% / 3.3% faster at N = 16 on q_proj / down
-//     than loading them into registers and storing them to LDS);
+//     tokens are loaded first, then its value chunks (kC 1 KiB loads, with
+//     the non-temporal hint), both straight into the wave's LDS
+//     (global_load_lds_dwordx4: four token rows of 256 contiguous bytes, or
+//     1 KiB of the run stream, per load; no staging registers and no LDS
+//     stores).  Against loads into registers stored to LDS, measured in
+//     alternating runs on one box: activations 1.7% / 3.3% faster at N = 16
+//     on q_proj / down, values a further 3.9% / 9.5% at N = 16 and 1.9-3.3%
+//     at N = 1;
 //   * one segment is requested ahead: segment g+1 is issued when segment g
 //     has been decoded.  With every wave's whole range in flight at once, the
 //     memory system served the waves of a SIMD in launch order and the last
@@ -436,15 +442,25 @@ __global__ __launch_bounds__(1024) void decode_kernel(DecodeArgs a) {
 //     ahead interleaves the waves' requests, so each wave has at most one
 //     segment left when the last bytes arrive (measured 5-9% faster on the
 //     q_proj, down and up shapes);
-//   * at a segment's start its value chunks go to the wave's LDS, and the B
-//     operands are read with ds_read_b128 from the staged rows (chunk k of
-//     row t at position k ^ t, so the 16 rows of one read meet no bank
-//     twice);
+//   * a segment's decode starts once its loads have landed (vmcnt(0)), and
+//     the next segment is requested only after every LDS read of the
+//     current one has returned (lgkmcnt(0)), so one LDS region per wave
+//     serves all segments; the B operands are read with ds_read_b128 from
+//     the staged rows (chunk k of row t at position k ^ t, so the 16 rows of
+//     one read meet no bank twice);
+//   * the gated instances (kGlu) keep the earlier form: activations and value
+//     chunks through registers into a padded row layout, and an opening
+//     zero slot and workgroup barrier (with the direct loads and no barrier
+//     their launch measured 22% slower, 26.9 against 32.8 us at n = 1 on the
+//     gate/up shape, both builds alternating on one box; neither change
+//     alone recovered it);
 //   * kDB (16 token rows only): the activations are loaded straight in the B
 //     operand layout instead, one 1 KiB load per 32-column step (lane l:
 //     token l%16, columns 8(l/16) .. +7), and used from registers; the wave
 //     needs no LDS for them, so more workgroups fit a CU, at the price of
-//     loads that touch 16 token rows each.
+//     loads that touch 16 token rows each.  Its value chunks go through
+//     registers (loaded straight into LDS they measured 1.3% slower: the
+//     wait for the LDS reads before each request is then pure cost).
 // LDS bytes reserved per staged token row (the rows are 256 bytes; the
 // reserve, from an earlier padded layout, keeps the work splits below as
 // measured).
@@ -473,6 +489,13 @@ __global__ __launch_bounds__(1024) void decode_seq_kernel(typename SeqArgs<kGlu>
   // loads as soon as it runs (lanes whose bit is clear read a neighbouring
   // value, not a zero slot; 1-2% faster than zeroing a slot and waiting for
   // the whole workgroup first).
+  if constexpr (kGlu) {
+    // the gated instances keep the zero slot and the opening barrier: their
+    // two wave halves measured 22% slower without them and with LDS-direct
+    // staging (alternating runs of both builds on one box)
+    if (threadIdx.x < 4) reinterpret_cast<uint32_t*>(smem)[threadIdx.x] = 0u;
+    __syncthreads();
+  }
   const uint32_t buf = lds_addr(smem + 16 + size_t(wave) * kWaveLds);
   const uint32_t xbuf = buf + kC * 1024;
 
@@ -524,13 +547,21 @@ __global__ __launch_bounds__(1024) void decode_seq_kernel(typename SeqArgs<kGlu>
     // load i is step i's B operand (token lane%16, rows past N repeating
     // token N-1, columns 32 i + 8 (lane/16) .. +7).  Byte offsets fit 32 bits
     // (16 tokens of at most 2^27 halves).
-    uint32_t xrow_off[kXI], xcol[kXI];
+    // direct: activations and value chunks go straight into LDS; otherwise
+    // (the B-operand instances, and gated ones unless switched) through
+    // registers
+    constexpr bool direct = !kDB && !kGlu;
+    uint32_t xrow_off[kXI], xcol[kXI], xl[kXI];
 #pragma unroll
     for (int i = 0; i < kXI; ++i) {
       const int pce = i * 64 + lane;
+      xl[i] = xbuf + uint32_t(pce >> 4) * kXRow + 16u * uint32_t(pce & 15);
       if constexpr (kDB) {
         xrow_off[i] = 2u * uint32_t(min(lane & 15, a.N - 1)) * uint32_t(a.ldx);
         xcol[i] = 32u * uint32_t(i) + 8u * uint32_t(lane >> 4);
+      } else if (!direct) {
+        xrow_off[i] = 2u * uint32_t(min(pce >> 4, a.N - 1)) * uint32_t(a.ldx);
+        xcol[i] = 8u * uint32_t(pce & 15);
       } else {
         // LDS-direct staging: load i fills rows 4i .. 4i+3 of 256 bytes
         // (lane l at row 4i + l/16, position l%16; rows past N repeat token
@@ -545,13 +576,14 @@ __global__ __launch_bounds__(1024) void decode_seq_kernel(typename SeqArgs<kGlu>
     // row; their accumulator columns are never stored), columns 8(l/16) .. +7
     // of the step: chunk 4q + l/16 of the segment for step q = 2 tt + s
     const uint32_t xrow = uint32_t(min(lane & 15, kXRows - 1));
+    const uint32_t xb = xbuf + xrow * kXRow + 16u * uint32_t(lane >> 4);  // register-staged layout
     uint32_t xsw[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q)
       xsw[q] = xbuf + xrow * 256u + 16u * ((uint32_t(4 * q) + uint32_t(lane >> 4)) ^ xrow);
 
-    u32x4 xr[NS][kDB ? kXI : 1];  // B operands in registers (kDB only)
-    u32x4 r[NS][kC];
+    u32x4 xr[NS][(kDB || kGlu) ? kXI : 1];  // activations in registers (kDB, gated)
+    u32x4 r[NS][(kDB || kGlu) ? kC : 1];  // value chunks in registers
     // Segment g: its activations, then its value chunks.  For g = 0 the first
     // step's bitmap is folded into the first tile pointer with a mask that is
     // always zero (N >= 1), so the wait for the pointers also covers that
@@ -559,9 +591,9 @@ __global__ __launch_bounds__(1024) void decode_seq_kernel(typename SeqArgs<kGlu>
     // branches and be waited for there.
     auto issue_seg = [&](int g) {
       const int c0 = (j0 + 2 * g) * kTK;
-      if constexpr (!kDB) {
-        // the previous segment's B reads must have returned before its rows
-        // are overwritten
+      if (direct) {
+        // the previous segment's B and value reads must have returned before
+        // its rows and chunks are overwritten
         __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt and expcnt not waited for
         __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
         __builtin_amdgcn_sched_barrier(0);
@@ -571,7 +603,7 @@ __global__ __launch_bounds__(1024) void decode_seq_kernel(typename SeqArgs<kGlu>
           const uint32_t off = xrow_off[i] + 2u * col;  // one 32-bit offset from the uniform base
           lds_dma16(reinterpret_cast<const uint8_t*>(a.X) + off, smem + (xbuf - lds_addr(smem)) + i * 1024);
         }
-      } else {
+      } else if constexpr (kDB || kGlu) {
 #pragma unroll
         for (int i = 0; i < kXI; ++i) {
           const uint32_t col = uint32_t(min(c0 + int(xcol[i]), kmax8));
@@ -586,7 +618,14 @@ __global__ __launch_bounds__(1024) void decode_seq_kernel(typename SeqArgs<kGlu>
 #pragma unroll
       for (int c = 0; c < kC; ++c) {
         const uint32_t off = min(p0 + uint32_t(c * 512 + lane * 8), last);
-        r[g][c] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vals + off));
+        if constexpr (kDB || kGlu) {
+          if (!direct)
+            r[g][c] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vals + off));
+          else
+            lds_dma16_nt(vals + off, smem + (buf - lds_addr(smem)) + c * 1024);
+        } else {
+          lds_dma16_nt(vals + off, smem + (buf - lds_addr(smem)) + c * 1024);
+        }
       }
       __builtin_amdgcn_sched_barrier(0);
     };
@@ -599,12 +638,20 @@ __global__ __launch_bounds__(1024) void decode_seq_kernel(typename SeqArgs<kGlu>
       if (2 * g < nt) {
         // The segment's activations and all its value chunks (chunks past the
         // segment hold clamped duplicates and are never read).
+        if constexpr (kDB || kGlu) {
+          if (!direct) {
+            if constexpr (!kDB) {
 #pragma unroll
-        for (int c = 0; c < kC; ++c)
-          *reinterpret_cast<lds_u32x4*>(static_cast<uintptr_t>(buf + c * 1024 + lane * 16)) = r[g][c];
-        if constexpr (!kDB) {
-          // the segment's LDS-direct activation rows have landed (they were
-          // requested before its value chunks, and loads return in order)
+              for (int i = 0; i < kXI; ++i)
+                *reinterpret_cast<lds_u32x4*>(static_cast<uintptr_t>(xl[i])) = xr[g][i];
+            }
+#pragma unroll
+            for (int c = 0; c < kC; ++c)
+              *reinterpret_cast<lds_u32x4*>(static_cast<uintptr_t>(buf + c * 1024 + lane * 16)) = r[g][c];
+          }
+        }
+        if (direct) {
+          // the segment's LDS-direct rows and chunks have landed
           __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
           __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
         }
@@ -633,9 +680,12 @@ __global__ __launch_bounds__(1024) void decode_seq_kernel(typename SeqArgs<kGlu>
             half8 bop;
             if constexpr (kDB)
               bop = __builtin_bit_cast(half8, xr[g][2 * tt + s]);
-            else
+            else if (direct)
               bop = __builtin_bit_cast(half8,
                                        *reinterpret_cast<const lds_u32x4*>(static_cast<uintptr_t>(xsw[2 * tt + s])));
+            else
+              bop = __builtin_bit_cast(
+                  half8, *reinterpret_cast<const lds_u32x4*>(static_cast<uintptr_t>(xb + tt * 128 + s * 64)));
             const half8 aop = decode_step(w, base);
             acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(aop, bop, acc, 0, 0, 0);
           }
@@ -647,7 +697,7 @@ __global__ __launch_bounds__(1024) void decode_seq_kernel(typename SeqArgs<kGlu>
   if (keep == 0x9E3779B9u && a.N < 0) a.Y[0] = 0;  // never true: keeps the L2 touch loads
   // LDS-direct rows requested for segments past a short range are never
   // read; they must have landed before the area is reused
-  if constexpr (!kDB) __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+  if constexpr (!kDB && !kGlu) __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
 
   __syncthreads();  // all wave buffers are free: reuse them as the reduction area
   if constexpr (kGlu)
